@@ -1,0 +1,419 @@
+/*
+ * tiletask.h -- C ABI of libtiletask: a GPT2 training step written as tile
+ * tasks on one AMD Instinct MI355X (gfx950).
+ *
+ * Method. The pith.science review of NNTile ("What carries the argument")
+ * describes the mechanism this library implements: every tensor is split
+ * into tiles along all of its axes; every layer (embedding, linear, layer
+ * norm, softmax, attention, cross-entropy, Adam update) becomes tasks that
+ * read and write a few tiles, forward and backward; tasks are submitted in
+ * program order (sequential task flow) and a runtime infers the ordering
+ * between them from the tiles they touch, then maps ready tasks onto the
+ * hardware and moves tiles between GPU and CPU memory on its own. The NNTile
+ * arXiv index page ("Abstract") adds that the runtime, not the user, decides
+ * where each task runs and when data moves. The NNTile README ("Minimal
+ * working GPT example") gives the tile flags (batch, seq, embd, inner and
+ * head tiles; seq, head and batch tiles must divide their axis, embd and
+ * inner tiles need not) and the optimiser settings (fused AdamW, eps 1e-8,
+ * weight decay 0.1, lr 3e-4, mean loss over the batch's tokens).
+ *
+ * Three layers of entry points:
+ *   1. tile ops   -- tile_* : one kernel launch on raw device pointers;
+ *   2. tasks      -- tt_ctx / tt_tensor / tt_submit_* : tiled tensors and the
+ *                    sequential-task-flow executor;
+ *   3. the model  -- tt_gpt2_* : the whole fwd + bwd + AdamW step.
+ *
+ * Conventions (all entry points):
+ *   - Every function returns int: TT_OK (0) or a negative TT_ERR_* code;
+ *     tt_last_error() returns a thread-local message for the last failure.
+ *     Nothing throws across the ABI.
+ *   - All floating point is IEEE fp32 (no TF32/xf32/bf16 anywhere).
+ *   - "device" pointers are HIP device memory on the current device;
+ *     "host" pointers are ordinary host memory. Streams are hipStream_t
+ *     passed as void* (NULL = the default stream).
+ *   - Tile ops are asynchronous on their stream; they validate arguments on
+ *     the host (TT_ERR_ARG / TT_ERR_SHAPE) before launching and return
+ *     TT_ERR_HIP if the launch fails. Size 0 problems are no-ops.
+ *   - Matrices are row-major with an explicit leading dimension (elements).
+ */
+#ifndef TILETASK_H
+#define TILETASK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- errors */
+#define TT_OK             0
+#define TT_ERR_ARG       -1  /* null pointer, bad enum, negative size       */
+#define TT_ERR_SHAPE     -2  /* tile/shape rule violated                     */
+#define TT_ERR_OOM       -3  /* device or pinned-host allocation failed      */
+#define TT_ERR_HIP       -4  /* a HIP call failed (launch, copy, event)      */
+#define TT_ERR_STATE     -5  /* use after destroy, or a latched async fault  */
+#define TT_ERR_UNSUPPORTED -6
+
+const char* tt_last_error(void);
+/* Library version string, e.g. "tiletask 0.1 gfx950". */
+const char* tt_version(void);
+
+/* ============================================================ 1. tile ops */
+
+/* tile_gemm -- the linear layer's tile task (forward Y = X W + b and its
+ * backward dX = dY W^T, dW += X^T dY), and the tied LM head's z = n wte^T.
+ * Layer list: pith.science review of NNTile, "What carries the argument".
+ *
+ *   acc = alpha * op(A) * op(B) + beta * S          (S = C, or aux for GELU)
+ *   op(A) is m x k: A[i*lda + p] (transA = 0) or A[p*lda + i] (transA = 1)
+ *   op(B) is k x n: B[p*ldb + j] (transB = 0) or B[j*ldb + p] (transB = 1)
+ * Epilogue flags (bitwise or):
+ *   TT_EPI_BIAS     acc += bias[j]                  (bias: n floats)
+ *   TT_EPI_RES      acc += res[i*ldr + j]           (residual add)
+ *   TT_EPI_GELU     S = aux; aux[i*ldaux+j] = acc; C = gelu_tanh(acc)
+ *                   (the MLP activation, stored with its pre-activation)
+ *   TT_EPI_GELU_BWD C = acc * gelu_tanh'(aux[i*ldaux+j])
+ * When beta == 0, S is not read (it may hold NaNs). C, A, B must not alias
+ * except that res may equal C (each element is read before it is written).
+ * Arbitrary (ragged) m, n, k; any leading dimensions >= the row length.
+ * Accumulation is fp32 on the matrix cores (MFMA). Deterministic.
+ */
+#define TT_EPI_NONE      0
+#define TT_EPI_BIAS      1
+#define TT_EPI_RES       2
+#define TT_EPI_GELU      4
+#define TT_EPI_GELU_BWD  8
+int tile_gemm(void* stream, int transA, int transB, int64_t m, int64_t n, int64_t k,
+              float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
+              float beta, float* C, int64_t ldc, int epilogue, const float* bias,
+              const float* res, int64_t ldr, float* aux, int64_t ldaux);
+
+/* tile_layernorm_fwd -- layer norm over the embedding axis, split into
+ * feature tiles (layer list: pith.science review, "What carries the
+ * argument"; definition after the "Layer Normalization" paper the arXiv
+ * index page lists under "Builds on"): y = (x - mean) * rstd * gamma + beta,
+ * rstd = 1/sqrt(var + eps), var biased. Rows are tokens, columns a feature
+ * tile of width cols starting at feature col_offset of a row of n_total.
+ * Phases:
+ *   TT_LN_PARTIAL  parts[r*3 + {0,1,2}] = (count, mean, M2) of this tile's row r
+ *   TT_LN_MERGE    merges n_parts partial buffers (part i at parts + i*part_stride)
+ *                  pairwise in order (Chan et al. update) -> stats[r*2 + {0,1}] =
+ *                  (mean, rstd). x, gamma, beta, y unused.
+ *   TT_LN_APPLY    y = (x - mean) * rstd * gamma + beta using stats
+ *   TT_LN_FUSED    the row fits this tile (cols == n_total): computes stats
+ *                  and y in one pass.
+ * gamma/beta point at this tile's cols entries. x/y: rows x cols, ld ldx/ldy.
+ */
+#define TT_LN_PARTIAL 0
+#define TT_LN_MERGE   1
+#define TT_LN_APPLY   2
+#define TT_LN_FUSED   3
+int tile_layernorm_fwd(void* stream, int phase, int64_t rows, int64_t cols,
+                       const float* x, int64_t ldx, const float* gamma, const float* beta,
+                       float* parts, int64_t n_parts, int64_t part_stride,
+                       float* stats, float* y, int64_t ldy, float eps);
+
+/* tile_layernorm_bwd -- gradient of tile_layernorm_fwd.
+ * With xhat = (x - mean) * rstd and dxhat = dy * gamma:
+ *   TT_LN_PARTIAL  parts[r*2 + {0,1}] = (sum dxhat, sum dxhat*xhat) over this tile
+ *   TT_LN_APPLY    sums the n_parts partials (part i at parts + i*part_stride) in
+ *                  order and writes dx = rstd*(dxhat - S1/n_total - xhat*S2/n_total);
+ *                  if dx_acc != 0, dx is added to the existing contents of dx
+ *                  (the residual-stream gradient).
+ *   TT_LN_FUSED    cols == n_total: PARTIAL and APPLY in one pass.
+ * APPLY and FUSED also accumulate dgamma[c] += sum_r dy*xhat and
+ * dbeta[c] += sum_r dy (deterministic two-stage column sums through
+ * `workspace`, which must hold tile_layernorm_bwd_workspace(rows, cols)
+ * bytes and must not be used concurrently by another launch).
+ */
+int tile_layernorm_bwd(void* stream, int phase, int64_t rows, int64_t cols, int64_t n_total,
+                       const float* dy, int64_t lddy, const float* x, int64_t ldx,
+                       const float* gamma, const float* stats,
+                       float* parts, int64_t n_parts, int64_t part_stride,
+                       float* dx, int64_t lddx, int dx_acc, float* dgamma, float* dbeta,
+                       void* workspace);
+size_t tile_layernorm_bwd_workspace(int64_t rows, int64_t cols);
+
+/* tile_softmax -- row softmax of a tile whose columns are one tile of a
+ * longer row (layer list: pith.science review, "What carries the argument").
+ * Element (r, c) of the tile is logit x = scale * X[r*ldx + c] at global
+ * column col_offset + c; with causal != 0 it is masked (-inf) when
+ * col_offset + c > row_offset + r.
+ *   TT_SM_STATS  parts[r*3 + {0,1,2}] = (row max, sum exp(x - max), picked)
+ *                where picked = x at column labels[r] if labels != NULL and the
+ *                label falls in this tile, else 0. Fully masked rows give
+ *                (-inf, 0, 0).
+ *   TT_SM_MERGE  lse[r] = logsumexp over the n_parts partials (part i at
+ *                parts + i*part_stride), merged in order by rescaling to the
+ *                larger max; if row_loss != NULL also row_loss[r] =
+ *                lse[r] - sum_i picked_i (the cross-entropy of row r).
+ *   TT_SM_APPLY  Y = (exp(x - lse[r]) - [labels && col == labels[r]]) * grad_scale;
+ *                Y may equal X (in place).
+ */
+#define TT_SM_STATS 0
+#define TT_SM_MERGE 1
+#define TT_SM_APPLY 2
+int tile_softmax(void* stream, int phase, int64_t rows, int64_t cols,
+                 int64_t row_offset, int64_t col_offset, float scale, int causal,
+                 const float* X, int64_t ldx, const int32_t* labels,
+                 float* parts, int64_t n_parts, int64_t part_stride,
+                 float* lse, float* row_loss, float* Y, int64_t ldy, float grad_scale);
+
+/* tile_xentropy -- mean cross-entropy over all tokens of the batch (NNTile
+ * README, "Minimal working GPT example": the reported loss is the mean over
+ * the batch's tokens). Builds on tile_softmax's STATS/MERGE/APPLY:
+ *   TT_XE_LOSS  loss[0] = (accumulate ? loss[0] : 0) + inv_n * sum_r row_loss[r]
+ *               over `rows` rows, summed in a fixed order (deterministic).
+ *   TT_XE_GRAD  logits (rows x v_len tile at vocab offset v_off, ld ldz) are
+ *               replaced in place by dz = (softmax - onehot(labels)) * inv_n.
+ */
+#define TT_XE_LOSS 0
+#define TT_XE_GRAD 1
+int tile_xentropy(void* stream, int phase, int64_t rows, int64_t v_len, int64_t v_off,
+                  const int32_t* labels, float* logits, int64_t ldz, const float* lse,
+                  const float* row_loss, float* loss, int accumulate, float inv_n);
+
+/* tile_attention_fwd -- causal multi-head scaled dot-product attention for
+ * one (query tile, key tile) pair (layer list: pith.science review; the
+ * "Attention Is All You Need" paper listed under "Builds on"; the README's
+ * flash-attention flag reorders work to save memory, which this online
+ * softmax does). Q/O tiles hold batch x q_len tokens x heads x hd, K/V
+ * tiles batch x k_len x heads x hd, token-major:
+ *   Q[((b*q_len + t)*heads + h)*hd + e]       (row stride heads*hd)
+ * Query t has global position q_off + t, key s position k_off + s; keys
+ * with k_off + s > q_off + t are masked. scale is usually 1/sqrt(hd).
+ * State carried across the key tiles of one query tile:
+ *   O   unnormalised accumulator (same layout as Q),
+ *   ml  running (max, sum) per (b, h, t): ml[((b*heads + h)*q_len + t)*2 + {0,1}],
+ *   lse logsumexp per (b, h, t):          lse[(b*heads + h)*q_len + t].
+ * first != 0 starts from (max = -inf, sum = 0, O = 0); last != 0 finishes:
+ * O /= sum and lse = max + log(sum). A single key tile uses first = last = 1.
+ * hd must be 16, 32, 64 or 128.
+ */
+int tile_attention_fwd(void* stream, int64_t batch, int64_t heads, int64_t q_len, int64_t k_len,
+                       int64_t hd, int64_t q_off, int64_t k_off, const float* Q, const float* K,
+                       const float* V, float* O, float* ml, float* lse, int first, int last,
+                       float scale);
+
+/* tile_attention_bwd -- gradient of tile_attention_fwd for one tile pair.
+ *   TT_ATT_PREP  Dvec[(b*heads+h)*q_len + t] = sum_e dO*O over the query tile
+ *                (K, V, dQ, dK, dV unused).
+ *   TT_ATT_GRAD  with P = exp(scale*Q K^T - lse) (masked causally):
+ *                dV += P^T dO; dS = P * (dO V^T - Dvec); dQ += scale * dS K;
+ *                dK += scale * dS^T Q.
+ *                acc_dq / acc_dkv = 0 overwrite dQ / (dK, dV) instead of adding.
+ * Layouts as tile_attention_fwd. Deterministic (no atomics).
+ */
+#define TT_ATT_PREP 0
+#define TT_ATT_GRAD 1
+int tile_attention_bwd(void* stream, int phase, int64_t batch, int64_t heads, int64_t q_len,
+                       int64_t k_len, int64_t hd, int64_t q_off, int64_t k_off,
+                       const float* Q, const float* K, const float* V, const float* O,
+                       const float* dO, const float* lse, float* Dvec,
+                       float* dQ, float* dK, float* dV, int acc_dq, int acc_dkv, float scale);
+
+/* tile_fused_adamw -- one decoupled-weight-decay Adam step over one
+ * parameter tile, one pass over p, g, m, v (NNTile README, "Minimal working
+ * GPT example": fused AdamW; the "Decoupled Weight Decay Regularization"
+ * paper listed on the arXiv index page under "Builds on"):
+ *   p *= 1 - lr*wd;  m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;
+ *   p -= lr * (m / bc[0]) / (sqrt(v / bc[1]) + eps)
+ * bias_corr is DEVICE memory holding bc = {1 - b1^t, 1 - b2^t} (so a
+ * captured step stays valid as t advances; see tile_adamw_advance).
+ */
+int tile_fused_adamw(void* stream, int64_t n, float* p, const float* g, float* m, float* v,
+                     float lr, float beta1, float beta2, float eps, float weight_decay,
+                     const float* bias_corr);
+/* tile_adamw_advance -- device-side step counter: t = ++(*step) and
+ * bias_corr = {1 - beta1^t, 1 - beta2^t} (step: device int32, bias_corr: device
+ * float[2]). One tiny launch per optimiser step. */
+int tile_adamw_advance(void* stream, int32_t* step, float* bias_corr, float beta1, float beta2);
+
+/* ---- auxiliary tile ops of the embedding layer and the linear backward ---- */
+
+/* tile_embedding_fwd -- token + position embedding for one (token tile, embd
+ * tile): out[r*ldo + c] = wte[ids[r]*ld_wte + c] + wpe[pos_r*ld_wpe + c] with
+ * pos_r = pos_offset + (r % seq_len). wte and wpe point at contiguous
+ * [vocab x cols] and [positions x cols] slabs (one embd tile column of the
+ * tiled tables). ids must lie in [0, vocab) -- checked on the device: an
+ * out-of-range id writes NaN to its row and never reads out of bounds. */
+int tile_embedding_fwd(void* stream, int64_t rows, int64_t cols, const int32_t* ids, int64_t vocab,
+                       const float* wte, int64_t ld_wte, const float* wpe, int64_t ld_wpe,
+                       int64_t seq_len, int64_t pos_offset, float* out, int64_t ldo);
+
+/* tile_embedding_index -- stable sort of one token tile's ids: sorted_ids
+ * ascending and perm (original row of each sorted entry), ties in row order.
+ * rows <= 65536. Used by tile_embedding_bwd for a deterministic scatter-add. */
+int tile_embedding_index(void* stream, int64_t rows, const int32_t* ids, int32_t* sorted_ids,
+                         int32_t* perm);
+
+/* tile_embedding_bwd -- dwte rows of one vocab tile [v_off, v_off + v_len):
+ * dwte[(id - v_off)*ld_dwte + c] += sum of dh[r*lddh + c] over rows r with
+ * ids[r] == id, added in row order (from tile_embedding_index's output).
+ * TT_EMB_POS phase instead accumulates the position gradient of one
+ * (batch tile x seq tile) token tile: dwpe[t*ld + c] += sum_b dh[(b*seq_len + t)*lddh + c]
+ * for batch = rows / seq_len. */
+#define TT_EMB_TOKEN 0
+#define TT_EMB_POS   1
+int tile_embedding_bwd(void* stream, int phase, int64_t rows, int64_t cols,
+                       const int32_t* sorted_ids, const int32_t* perm,
+                       int64_t v_off, int64_t v_len, int64_t seq_len,
+                       const float* dh, int64_t lddh, float* dst, int64_t ld_dst);
+
+/* tile_reduce_rows -- bias gradient of the linear layer:
+ * out[c] = (beta ? out[c] : 0) + sum_r X[r*ldx + c], in a fixed order
+ * (two-stage through `workspace` of tile_reduce_rows_workspace(rows, cols)
+ * bytes). */
+int tile_reduce_rows(void* stream, int64_t rows, int64_t cols, const float* X, int64_t ldx,
+                     float* out, int beta, void* workspace);
+size_t tile_reduce_rows_workspace(int64_t rows, int64_t cols);
+
+/* tile_fill -- dst[i] = value for i < n. tile_split_tokens -- from a window
+ * array tokens[b*(seq+1) + t] (int32), ids[b*seq + t] = tokens[b*(seq+1)+t]
+ * and labels[b*seq + t] = tokens[b*(seq+1)+t+1] for b < batch, t < seq. */
+int tile_fill(void* stream, int64_t n, float* dst, float value);
+int tile_split_tokens(void* stream, int64_t batch, int64_t seq, const int32_t* tokens,
+                      int32_t* ids, int32_t* labels);
+
+/* ================================================= 2. tensors and tasks */
+
+typedef struct tt_ctx tt_ctx;
+typedef struct tt_tensor tt_tensor;
+
+#define TT_MAX_DIMS 6
+#define TT_F32 0
+#define TT_I32 1
+#define TT_HOME_DEVICE      0   /* tiles live in HBM */
+#define TT_HOME_PINNED_HOST 1   /* tiles live in pinned host RAM, staged on use */
+#define TT_DEVICE_DRYRUN   -1   /* tt_ctx_create: no GPU, tasks recorded only */
+
+/* Context: owns n_streams HIP streams (default priority), their events and
+ * per-stream workspaces, and the device arena of its tensors. device =
+ * TT_DEVICE_DRYRUN builds a context that runs nothing: tensors get no
+ * memory, submitted tasks are recorded with their inferred dependencies and
+ * stream choice and can be dumped (tt_dump_dag); this is how the executor's
+ * dependency inference is tested without a GPU. device_budget_bytes caps
+ * the device memory used for tiles whose home is pinned host (0 = no cap).
+ * window = number of submitted tasks held before they are launched
+ * (0 = default 512); a larger window gives the stream assignment more
+ * look-ahead. One submitting thread per context. */
+int tt_ctx_create(int device, int n_streams, int window, size_t device_budget_bytes, tt_ctx** out);
+int tt_ctx_destroy(tt_ctx* ctx);
+/* hipStream_t of executor stream i (for callers that want to order their own
+ * work after the context's). */
+int tt_ctx_stream(tt_ctx* ctx, int i, void** stream);
+/* Keep (on != 0) or drop the per-task records tt_dump_dag writes; dry-run
+ * contexts record by default, device contexts do not. */
+int tt_ctx_record(tt_ctx* ctx, int on);
+
+/* Tiled tensor: shape[d] split into tiles of tile_shape[d] (the last tile of
+ * an axis is ragged when tile_shape[d] does not divide shape[d]). Storage is
+ * tile-major: each tile is one contiguous row-major block of its own extent;
+ * tiles are laid out in grid order with the FIRST grid axis varying fastest,
+ * so for a matrix all tiles of one tile-column form one contiguous row-major
+ * slab. Memory is owned by the tensor (home = TT_HOME_*). */
+int tt_tensor_create(tt_ctx* ctx, int ndim, const int64_t* shape, const int64_t* tile_shape,
+                     int dtype, int home, tt_tensor** out);
+/* Same, over caller-owned device memory of tt_tensor_bytes() bytes laid out
+ * as above; the memory must outlive the tensor. */
+int tt_tensor_wrap(tt_ctx* ctx, int ndim, const int64_t* shape, const int64_t* tile_shape,
+                   int dtype, void* device_base, tt_tensor** out);
+int tt_tensor_destroy(tt_tensor* t);
+int64_t tt_tensor_bytes(const tt_tensor* t);
+/* Number of tiles along axis d, and the total. */
+int tt_tensor_grid(const tt_tensor* t, int64_t* grid_out /* ndim */, int64_t* ntiles);
+/* Device pointer and extent of one tile (waits for pending tasks that write
+ * it and makes it resident when its home is pinned host). */
+int tt_tensor_tile(tt_tensor* t, const int64_t* tile_idx, void** dev_ptr, int64_t* extent);
+/* Dense row-major host array <-> tiled tensor (synchronous; waits for the
+ * tensor's pending tasks). */
+int tt_tensor_copy_in(tt_tensor* t, const void* dense_host);
+int tt_tensor_copy_out(tt_tensor* t, void* dense_host);
+
+/* Task submission in sequential task flow order. Each call records the
+ * task's tile accesses, derives read-after-write, write-after-read and
+ * write-after-write edges against earlier tasks, and queues the task; tasks
+ * are launched in submission order onto the context's streams, with event
+ * waits for edges that cross streams. */
+#define TT_R  1
+#define TT_W  2
+#define TT_RW 3
+typedef struct {
+    tt_tensor* tensor;
+    int64_t tile[TT_MAX_DIMS];
+    int mode;            /* TT_R, TT_W or TT_RW */
+} tt_access;
+/* A task that only declares accesses (runs nothing); label <= 31 chars. */
+int tt_submit_nop(tt_ctx* ctx, const char* label, const tt_access* acc, int n_acc);
+/* C(ic) = alpha op(A(ia)) op(B(ib)) + beta C(ic) on 2-D tiles (extents must
+ * agree after transposition; TT_ERR_SHAPE otherwise). Accesses: A R, B R,
+ * C W when beta == 0 else RW. */
+int tt_submit_gemm(tt_ctx* ctx, int transA, int transB, float alpha,
+                   tt_tensor* A, const int64_t* ia, tt_tensor* B, const int64_t* ib,
+                   float beta, tt_tensor* C, const int64_t* ic);
+/* Every element of tile idx = value (access W). */
+int tt_submit_fill(tt_ctx* ctx, tt_tensor* t, const int64_t* idx, float value);
+/* Launch everything queued and wait for the GPU; returns the first latched
+ * error, if any. */
+int tt_wait(tt_ctx* ctx);
+/* Write the recorded task graph as JSON lines: one object per task with
+ * id, label, stream, deps and accesses (dry-run and real contexts). */
+int tt_dump_dag(tt_ctx* ctx, const char* path);
+
+typedef struct {
+    int64_t tasks;            /* tasks submitted since creation / reset     */
+    int64_t edges;            /* dependency edges inferred                  */
+    int64_t cross_stream_waits;
+    int64_t events_recorded;
+    double  submit_seconds;   /* host time spent in submit + launch         */
+    int64_t h2d_bytes, d2h_bytes;  /* residency traffic                      */
+    int64_t evictions, prefetches;
+} tt_stats;
+int tt_get_stats(tt_ctx* ctx, tt_stats* out);
+int tt_reset_stats(tt_ctx* ctx);
+
+/* ====================================================== 3. the GPT2 step */
+
+typedef struct tt_gpt2 tt_gpt2;
+typedef struct {
+    int n_layer, vocab, n_embd, n_head, n_inner, seq, batch;
+    float ln_eps;             /* 1e-5 */
+} tt_gpt2_config;
+typedef struct {              /* README tile flags; vocab has no flag there */
+    int batch, seq, embd, inner, head, vocab;
+} tt_gpt2_tiles;
+typedef struct {
+    float lr, beta1, beta2, eps, weight_decay;
+} tt_adamw_hparams;
+
+/* Allocates parameters, gradients, AdamW moments (zeroed) and activations
+ * as tiled tensors. Parameters are in the order: wte [V,d], wpe [T,d], then
+ * per block ln1_g, ln1_b, w_qkv [d,3d], b_qkv, w_o [d,d], b_o, ln2_g, ln2_b,
+ * w_fc [d,I], b_fc, w_p [I,d], b_p, then lnf_g, lnf_b (GPT2 with a tied
+ * head). TT_ERR_SHAPE if seq, head or batch tiles do not divide their axis
+ * or n_embd % n_head != 0. param_home = TT_HOME_PINNED_HOST keeps
+ * parameters, gradients and moments in pinned host RAM (out-of-core). */
+int tt_gpt2_create(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_gpt2_tiles* tiles,
+                   int param_home, tt_gpt2** out);
+int tt_gpt2_destroy(tt_gpt2* g);
+int tt_gpt2_num_params(tt_gpt2* g, int* n);
+/* Tensors of parameter `index`: value, gradient, first and second moment
+ * (any output may be NULL). Dense layouts match the shapes listed above. */
+int tt_gpt2_param(tt_gpt2* g, int index, tt_tensor** param, tt_tensor** grad,
+                  tt_tensor** m, tt_tensor** v);
+/* One training step, submitted as tile tasks: embedding, blocks, final
+ * LayerNorm, tied head, cross-entropy, the backward of each, and (if
+ * do_update) one AdamW step on every parameter tile. tokens: DEVICE int32
+ * [batch, seq+1] windows (inputs = tokens[:, :seq], labels = tokens[:, 1:]),
+ * ids in [0, vocab). The step is queued; tt_gpt2_loss waits and returns
+ * the mean loss. */
+int tt_gpt2_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams* hp, int do_update);
+int tt_gpt2_loss(tt_gpt2* g, float* loss_host);
+/* Number of tasks the last step submitted. */
+int tt_gpt2_task_count(tt_gpt2* g, int64_t* n);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TILETASK_H */

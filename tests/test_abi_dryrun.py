@@ -1,0 +1,162 @@
+"""CPU tests of the C ABI: the library loads and exports every symbol the
+header declares, argument errors are reported, and the sequential-task-flow
+executor infers exactly the read-after-write, write-after-read and
+write-after-write edges (dry-run contexts launch nothing and need no GPU)."""
+import os
+import re
+
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tiletask.h")
+
+tt = pytest.importorskip("tile_task_transformer_amd")
+from tile_task_transformer_amd import _lib as L  # noqa: E402
+from tile_task_transformer_amd.runtime import Context, GPT2  # noqa: E402
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**\s*((?:tt|tile)_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    names = declared_functions()
+    assert len(names) >= 40, names
+    for n in names:
+        assert hasattr(L.lib, n), n
+        assert n in L.SIGNATURES, f"{n} has no ctypes signature"
+    assert L.lib.tt_version().decode().startswith("tiletask")
+
+
+def test_argument_errors_without_gpu():
+    # validation happens on the host before any launch
+    with pytest.raises(L.TTError) as e:
+        tt.tile_gemm(None, 0, 0, -1, 4, 4, 1.0, 0, 4, 0, 4, 0.0, 0, 4)
+    assert e.value.code == L.TT_ERR_ARG
+    with pytest.raises(L.TTError) as e:
+        tt.tile_attention_fwd(None, 1, 1, 8, 8, 48, 0, 0, 16, 16, 16, 16, 16, 16, 1, 1, 1.0)
+    assert e.value.code == L.TT_ERR_UNSUPPORTED
+    with pytest.raises(L.TTError) as e:
+        tt.tile_layernorm_fwd(None, L.TT_LN_FUSED, 4, 4096, 16, 4096, 16, 16, None, 0, 0, 16, 16, 4096, 1e-5)
+    assert e.value.code == L.TT_ERR_SHAPE
+    # zero-size problems are no-ops
+    tt.tile_gemm(None, 0, 0, 0, 4, 4, 1.0, None, 4, None, 4, 0.0, None, 4)
+    tt.tile_fill(None, 0, None, 0.0)
+
+
+def _edges(dag):
+    return {r["id"]: sorted(r["deps"]) for r in dag}
+
+
+def test_stf_hazard_edges(tmp_path):
+    with Context(L.TT_DEVICE_DRYRUN, n_streams=2) as ctx:
+        a = ctx.tensor((4, 4), (2, 2))
+        b = ctx.tensor((4, 4), (2, 2))
+        R, W, RW = L.TT_R, L.TT_W, L.TT_RW
+        ctx.submit_nop("w0", [(a, (0, 0), W)])                      # 0
+        ctx.submit_nop("r1", [(a, (0, 0), R)])                      # 1: RAW on 0
+        ctx.submit_nop("r2", [(a, (0, 0), R), (b, (1, 0), W)])      # 2: RAW on 0
+        ctx.submit_nop("w3", [(a, (0, 0), W)])                      # 3: WAW 0, WAR 1, 2
+        ctx.submit_nop("r4", [(a, (1, 1), R)])                      # 4: independent tile
+        ctx.submit_nop("rw5", [(a, (0, 0), RW), (a, (1, 1), R)])    # 5: RAW/WAW on 3; R-R with 4 is free
+        ctx.submit_nop("w6", [(a, (1, 1), W)])                      # 6: WAR on 4 and 5
+        ctx.submit_nop("r7", [(b, (1, 0), R), (b, (1, 0), W)])      # 7: duplicate access merges to RW: on 2
+        ctx.submit_nop("none", [])                                  # 8: no accesses
+        dag = ctx.dump_dag(str(tmp_path / "dag.jsonl"))
+    e = _edges(dag)
+    assert e == {0: [], 1: [0], 2: [0], 3: [0, 1, 2], 4: [], 5: [3], 6: [4, 5], 7: [2], 8: []}
+    labels = [r["label"] for r in dag]
+    assert labels[:3] == ["w0", "r1", "r2"]
+
+
+def test_stream_assignment_keeps_chains_and_spreads_independent_work(tmp_path):
+    with Context(L.TT_DEVICE_DRYRUN, n_streams=4) as ctx:
+        a = ctx.tensor((8,), (1,))
+        W, RW, R = L.TT_W, L.TT_RW, L.TT_R
+        for i in range(4):                     # 4 independent writers
+            ctx.submit_nop("w", [(a, (i,), W)])
+        for i in range(4):                     # each continues its own chain
+            ctx.submit_nop("rw", [(a, (i,), RW)])
+        ctx.submit_nop("join", [(a, (i,), R) for i in range(4)] + [(a, (7,), W)])
+        dag = ctx.dump_dag(str(tmp_path / "dag.jsonl"))
+        st = ctx.stats()
+    s = [r["stream"] for r in dag]
+    assert sorted(s[:4]) == [0, 1, 2, 3]
+    assert s[4:8] == s[:4]                     # chain continuation stays on its stream
+    assert st["cross_stream_waits"] == 3       # the join waits on the three other streams
+    assert st["tasks"] == 9 and st["edges"] == 4 + 4
+
+
+def test_ksplit_gemm_chain_edges(tmp_path):
+    with Context(L.TT_DEVICE_DRYRUN, n_streams=2) as ctx:
+        A = ctx.tensor((64, 96), (64, 32))    # 3 K tiles
+        B = ctx.tensor((96, 64), (32, 64))
+        Cc = ctx.tensor((64, 64), (64, 64))
+        for kt in range(3):
+            ctx.submit_gemm(0, 0, 1.0, A, (0, kt), B, (kt, 0), 0.0 if kt == 0 else 1.0, Cc, (0, 0))
+        ctx.submit_fill(A, (0, 1), 0.0)       # overwrites a tile the second GEMM read
+        with pytest.raises(L.TTError) as e:   # shape mismatch is rejected at submit time
+            ctx.submit_gemm(0, 0, 1.0, A, (0, 0), A, (0, 1), 0.0, Cc, (0, 0))
+        assert e.value.code == L.TT_ERR_SHAPE
+        dag = ctx.dump_dag(str(tmp_path / "dag.jsonl"))
+    assert _edges(dag) == {0: [], 1: [0], 2: [1], 3: [1]}
+
+
+def _check_races(dag):
+    """Every pair of accesses to one tile where at least one writes must be
+    ordered by a path of dependency edges (STF as the race model)."""
+    n = len(dag)
+    ids = [r["id"] for r in dag]
+    pos = {t: i for i, t in enumerate(ids)}
+    reach = [0] * n   # bitset of ancestors
+    for i, r in enumerate(dag):
+        m = 0
+        for d in r["deps"]:
+            assert d < r["id"], "edge must point to an earlier task"
+            j = pos[d]
+            m |= reach[j] | (1 << j)
+        reach[i] = m
+    last = {}
+    for i, r in enumerate(dag):
+        for tid, lin, mode in r["acc"]:
+            key = (tid, lin)
+            for j, m2 in last.get(key, []):
+                if (mode & 2) or (m2 & 2):
+                    assert (reach[i] >> j) & 1, f"race on tile {key} between {dag[j]['label']} and {r['label']}"
+            last.setdefault(key, []).append((i, mode))
+
+
+@pytest.mark.parametrize("tiles", [
+    synth.Tiles(2, 32, 32, 32, 4, 32),     # the tiny workload's tiles
+    synth.Tiles(1, 8, 16, 24, 1, 40),      # ragged embd/inner/vocab, split seq/head/batch
+    synth.Tiles(2, 16, 64, 256, 2, 256),   # untiled embd/inner/vocab
+])
+def test_gpt2_step_dag_is_race_free(tiles, tmp_path):
+    shape = synth.GPT2Shape(2, 100, 64, 4, 96, 32, 2)
+    with Context(L.TT_DEVICE_DRYRUN, n_streams=4, window=100000) as ctx:
+        model = GPT2(ctx, shape, tiles)
+        model.step(None)
+        n = model.task_count()
+        dag = ctx.dump_dag(str(tmp_path / "dag.jsonl"))
+        model.close()
+    assert n == len(dag) > 0
+    _check_races(dag)
+    labels = {r["label"] for r in dag}
+    for need in ("emb_fwd", "qkv", "attn_fwd", "attn_proj", "fc", "mlp_proj", "head", "ce_stats", "ce_merge",
+                 "ce_loss", "ce_grad", "head_dw", "head_dx", "attn_bwd", "adamw", "emb_dw", "emb_dpos"):
+        assert need in labels, need
+
+
+def test_gpt2_rejects_bad_tiles():
+    shape = synth.GPT2Shape(1, 100, 64, 4, 96, 32, 2)
+    with Context(L.TT_DEVICE_DRYRUN) as ctx:
+        for bad in (synth.Tiles(2, 12, 32, 32, 4, 32),   # seq tile does not divide seq
+                    synth.Tiles(2, 32, 32, 32, 3, 32),   # head tile does not divide heads
+                    synth.Tiles(3, 32, 32, 32, 4, 32)):  # batch tile does not divide batch
+            with pytest.raises(L.TTError) as e:
+                GPT2(ctx, shape, bad)
+            assert e.value.code == L.TT_ERR_SHAPE

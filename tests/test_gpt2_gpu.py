@@ -1,0 +1,125 @@
+"""End-to-end parity of the tiled GPT2 step (HIP) with the untiled fp64 oracle.
+
+Bar (fp32 path vs fp64 oracle, same seeded inputs):
+  * loss: relative error <= 1e-4;
+  * every gradient tensor: normwise relative error <= 1e-3 and
+    max |g - g_ref| <= 1e-3 * max |g_ref|;
+  * every updated parameter: normwise relative error <= 1e-3;
+  * AdamW itself: the GPU's updated parameters equal the oracle's AdamW fed
+    with the GPU's own fp32 gradients, elementwise within 1e-3 relative with
+    an absolute floor of 1e-3 * lr (the first step moves each weight by
+    about lr * sign(g), so tiny gradients whose sign differs between fp32
+    and fp64 would otherwise fail spuriously).
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import synth  # noqa: E402
+from oracle import gpt2 as og  # noqa: E402
+from tile_task_transformer_amd.runtime import Context, GPT2  # noqa: E402
+from tests.gpu_util import normwise  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(shape, tiles, params, tokens, n_streams=4, steps=1):
+    specs = synth.param_specs(shape)
+    with Context(0, n_streams=n_streams) as ctx:
+        model = GPT2(ctx, shape, tiles)
+        model.set_params(params, specs)
+        tok = torch.from_numpy(tokens.astype(np.int32)).cuda()
+        losses = []
+        for _ in range(steps):
+            model.step(tok)
+            losses.append(model.loss())
+        out = dict(loss=losses, grads=model.get(specs, 1), params=model.get(specs, 0),
+                   m=model.get(specs, 2), v=model.get(specs, 3), tasks=model.task_count())
+        model.close()
+    return out
+
+
+def check_against_oracle(shape, gpu, params, tokens, w):
+    loss, grads, newp, _ = og.step(params, tokens, shape.n_layer, shape.n_head, lr=w.lr, beta1=w.beta1,
+                                   beta2=w.beta2, eps=w.eps, wd=w.weight_decay)
+    assert abs(gpu["loss"][0] - loss) <= 1e-4 * abs(loss), (gpu["loss"][0], loss)
+    for name, ref in grads.items():
+        got = gpu["grads"][name].astype(np.float64)
+        assert normwise(got, ref) <= 1e-3, (name, normwise(got, ref))
+        assert np.abs(got - ref).max() <= 1e-3 * np.abs(ref).max() + 1e-30, name
+    for name, ref in newp.items():
+        got = gpu["params"][name].astype(np.float64)
+        assert normwise(got, ref) <= 1e-3, (name, normwise(got, ref))
+        # AdamW fed with the GPU's own gradients
+        p1, _, _ = og.adamw(np.asarray(params[name], np.float64), gpu["grads"][name].astype(np.float64), 0, 0, 1,
+                            w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)
+        err = np.abs(got - p1)
+        assert (err <= 1e-3 * np.abs(p1) + 1e-3 * w.lr).all(), (name, err.max())
+    return loss
+
+
+TINY = synth.WORKLOADS["tiny"]
+
+
+@pytest.mark.parametrize("tiles", [
+    TINY.tiles,                                  # 32 on every axis, clamped
+    synth.Tiles(2, 32, 64, 256, 4, 256),         # untiled
+    synth.Tiles(1, 16, 16, 48, 2, 40),           # split batch/seq/head, ragged inner and vocab
+    synth.Tiles(2, 8, 24, 40, 1, 100),           # ragged embd, one head per tile, seq tile 8
+])
+def test_tiny_step_matches_oracle(tiles):
+    shape = TINY.shape
+    params = synth.init_params(shape, seed=0)
+    tokens = synth.token_stream(shape, seed=1)
+    gpu = run_gpu(shape, tiles, params, tokens)
+    check_against_oracle(shape, gpu, params, tokens, TINY)
+
+
+def test_tiny_step_with_rich_params_two_layers():
+    """Larger weights, random LayerNorm gains/biases and two blocks, so every
+    gradient term is far from zero."""
+    shape = synth.GPT2Shape(2, 256, 64, 4, 256, 32, 2)
+    rng = np.random.default_rng(9)
+    params = {}
+    for name, shp, kind in synth.param_specs(shape):
+        base = 1.0 if kind == "ones" else 0.0
+        params[name] = (base + rng.standard_normal(shp) * 0.1).astype(np.float32)
+    tokens = synth.token_stream(shape, seed=2)
+    gpu = run_gpu(shape, synth.Tiles(1, 16, 32, 96, 2, 64), params, tokens)
+    check_against_oracle(shape, gpu, params, tokens, TINY)
+
+
+def test_uniform_logits_loss_is_ln_vocab():
+    shape = TINY.shape
+    params = synth.init_params(shape, seed=0)
+    params["wte"] = np.zeros_like(params["wte"])
+    gpu = run_gpu(shape, TINY.tiles, params, synth.token_stream(shape, seed=1))
+    assert abs(gpu["loss"][0] - np.log(256)) <= 1e-6 * np.log(256)
+
+
+def test_tile_shapes_agree_and_steps_are_deterministic():
+    shape = TINY.shape
+    params = synth.init_params(shape, seed=0)
+    tokens = synth.token_stream(shape, seed=1)
+    a = run_gpu(shape, TINY.tiles, params, tokens, steps=2)
+    b = run_gpu(shape, synth.Tiles(1, 8, 16, 64, 1, 48), params, tokens, steps=2)
+    c = run_gpu(shape, TINY.tiles, params, tokens, steps=2, n_streams=1)
+    assert abs(a["loss"][1] - b["loss"][1]) <= 1e-5 * abs(a["loss"][1])
+    for name in a["grads"]:
+        assert normwise(a["grads"][name], b["grads"][name]) <= 1e-4, name
+    # same tiles, different stream counts: bitwise equal (no atomics anywhere)
+    assert a["loss"] == c["loss"]
+    for name in a["params"]:
+        assert np.array_equal(a["params"][name], c["params"][name]), name
+        assert np.array_equal(a["grads"][name], c["grads"][name]), name
+
+
+def test_gpt2_small_full_size_step_matches_oracle():
+    """The GPT2-small workload at its full size and README tiles, checked
+    against the full fp64 oracle step."""
+    w = synth.WORKLOADS["gpt2_small"]
+    params = synth.init_params(w.shape, seed=0)
+    tokens = synth.token_stream(w.shape, seed=1)
+    gpu = run_gpu(w.shape, w.tiles, params, tokens)
+    check_against_oracle(w.shape, gpu, params, tokens, w)

@@ -1,0 +1,386 @@
+"""Parity of every HIP tile op with the fp64 oracle (GPU).
+
+Inputs are seeded (synth.rand_*); sizes span several kernel tiles and a
+ragged tail; every call goes through the C ABI. Float tolerances follow the
+fp32 arithmetic: a length-k dot product in fp32 is within ~k*2^-24 of the
+fp64 value relative to the sum of |terms| (worst case), the memory-bound
+ops within a few units of 2^-24 of their inputs' scale.
+"""
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import synth  # noqa: E402
+import tile_task_transformer_amd as tt  # noqa: E402
+from oracle import gpt2 as og  # noqa: E402
+from oracle import tiled as otl  # noqa: E402
+from tests.gpu_util import EPS32, assert_close_bound, assert_rel, dev, empty, host  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------ GEMM
+
+def _op(a, t):
+    return a.T if t else a
+
+
+@pytest.mark.parametrize("ta,tb", [(0, 0), (0, 1), (1, 0), (1, 1)])
+@pytest.mark.parametrize("m,n,k", [(257, 130, 70), (128, 128, 16), (300, 513, 337), (1, 1, 1), (64, 200, 1),
+                                   (1100, 700, 256)])
+def test_gemm_parity(ta, tb, m, n, k):
+    seed = m * 7 + n * 3 + k + 10 * ta + 20 * tb
+    a = synth.rand_normal((k, m) if ta else (m, k), seed)
+    b = synth.rand_normal((n, k) if tb else (k, n), seed + 1)
+    c0 = synth.rand_normal((m, n), seed + 2)
+    ref = 0.75 * _op(a.astype(np.float64), ta) @ _op(b.astype(np.float64), tb) + 0.5 * c0
+    C = dev(c0)
+    tt.tile_gemm(None, ta, tb, m, n, k, 0.75, dev(a), a.shape[1], dev(b), b.shape[1], 0.5, C, n)
+    bound = 0.75 * (np.abs(_op(a, ta)).astype(np.float64) @ np.abs(_op(b, tb)).astype(np.float64)) * (k + 2) * EPS32
+    assert_close_bound(host(C), ref, bound + 4 * EPS32 * np.abs(ref) + 1e-30, f"gemm {ta}{tb} {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("ld_pad", [0, 1, 4])
+def test_gemm_leading_dims_and_views(ld_pad):
+    m, n, k = 96, 72, 40
+    a = synth.rand_normal((m, k + ld_pad), 1)
+    b = synth.rand_normal((k, n + ld_pad), 2)
+    C = empty((m, n + ld_pad))
+    tt.tile_gemm(None, 0, 0, m, n, k, 1.0, dev(a), k + ld_pad, dev(b), n + ld_pad, 0.0, C, n + ld_pad)
+    ref = a[:, :k].astype(np.float64) @ b[:, :n].astype(np.float64)
+    got = host(C)
+    assert_rel(got[:, :n], ref, 1e-5, 1e-5, "gemm ld")
+    if ld_pad:
+        assert np.isnan(got[:, n:]).all(), "wrote outside the m x n block"
+
+
+def test_gemm_epilogues():
+    m, n, k = 200, 150, 64
+    x = synth.rand_normal((m, k), 3)
+    w = synth.rand_normal((k, n), 4, std=0.2)
+    bias = synth.rand_normal((n,), 5)
+    res = synth.rand_normal((m, n), 6)
+    acc0 = synth.rand_normal((m, n), 7)
+    base = x.astype(np.float64) @ w.astype(np.float64)
+    # BIAS | RES, beta 0
+    C = empty((m, n))
+    tt.tile_gemm(None, 0, 0, m, n, k, 1.0, dev(x), k, dev(w), n, 0.0, C, n, tt.TT_EPI_BIAS | tt.TT_EPI_RES,
+                 dev(bias), dev(res), n)
+    assert_rel(host(C), base + bias + res, 2e-5, 2e-5, "bias+res")
+    # GELU with beta 1: pre = AB + aux + bias; aux <- pre; C <- gelu(pre)
+    aux = dev(acc0)
+    C = empty((m, n))
+    tt.tile_gemm(None, 0, 0, m, n, k, 1.0, dev(x), k, dev(w), n, 1.0, C, n, tt.TT_EPI_GELU | tt.TT_EPI_BIAS,
+                 dev(bias), None, 0, aux, n)
+    pre = base + acc0 + bias
+    assert_rel(host(aux), pre, 2e-5, 2e-5, "gelu pre-activation")
+    assert_rel(host(C), og.gelu(pre), 2e-5, 2e-5, "gelu")
+    # GELU_BWD: C <- (AB + beta C) * gelu'(aux)
+    u = synth.rand_normal((m, n), 8, std=2.0)
+    C = dev(acc0)
+    tt.tile_gemm(None, 0, 0, m, n, k, 1.0, dev(x), k, dev(w), n, 1.0, C, n, tt.TT_EPI_GELU_BWD, None, None, 0,
+                 dev(u), n)
+    assert_rel(host(C), (base + acc0) * og.gelu_grad(u.astype(np.float64)), 2e-5, 2e-5, "gelu_bwd")
+
+
+# ------------------------------------------------------------- LayerNorm
+
+@pytest.mark.parametrize("rows,cols", [(1, 32), (37, 768), (300, 2048), (64, 33), (130, 512)])
+def test_layernorm_fwd_fused(rows, cols):
+    x = synth.rand_normal((rows, cols), rows + cols, std=3.0) + 1.5
+    g = synth.rand_normal((cols,), 1) + 1
+    b = synth.rand_normal((cols,), 2)
+    y, stats = empty((rows, cols)), empty((rows, 2))
+    tt.tile_layernorm_fwd(None, tt.TT_LN_FUSED, rows, cols, dev(x), cols, dev(g), dev(b), None, 0, 0, stats, y,
+                          cols, 1e-5)
+    ry, (mu, rs) = og.layernorm_fwd(x.astype(np.float64), g.astype(np.float64), b.astype(np.float64))
+    assert_rel(host(y), ry, 1e-5, 1e-5, "ln y")
+    assert_rel(host(stats)[:, 0], mu, 1e-5, 1e-6, "ln mean")
+    assert_rel(host(stats)[:, 1], rs, 1e-5, 0, "ln rstd")
+
+
+@pytest.mark.parametrize("rows,cols,et", [(40, 64, 32), (129, 2000, 512), (16, 100, 24)])
+def test_layernorm_three_phase_and_bwd(rows, cols, et):
+    x = synth.rand_normal((rows, cols), 11, std=2.0) - 0.7
+    g = synth.rand_normal((cols,), 12) + 1
+    b = synth.rand_normal((cols,), 13)
+    dy = synth.rand_normal((rows, cols), 14)
+    X, G, Bb, DY = dev(x), dev(g), dev(b), dev(dy)
+    tiles = otl.tiles(cols, et)
+    ne = len(tiles)
+    parts = empty((ne, rows, 3))
+    stats = empty((rows, 2))
+    y = empty((rows, cols))
+    for i, (c0, c1) in enumerate(tiles):
+        xt = X[:, c0:c1].contiguous()
+        tt.tile_layernorm_fwd(None, tt.TT_LN_PARTIAL, rows, c1 - c0, xt, c1 - c0, None, None, parts[i], 0, 0, None,
+                              None, 0, 1e-5)
+    tt.tile_layernorm_fwd(None, tt.TT_LN_MERGE, rows, 0, None, 0, None, None, parts, ne, rows * 3, stats, None, 0,
+                          1e-5)
+    for c0, c1 in tiles:
+        yt = empty((rows, c1 - c0))
+        tt.tile_layernorm_fwd(None, tt.TT_LN_APPLY, rows, c1 - c0, X[:, c0:c1].contiguous(), c1 - c0,
+                              G[c0:c1].contiguous(), Bb[c0:c1].contiguous(), None, 0, 0, stats, yt, c1 - c0, 1e-5)
+        y[:, c0:c1] = yt
+    x64, g64 = x.astype(np.float64), g.astype(np.float64)
+    ry, (mu, rs) = og.layernorm_fwd(x64, g64, b.astype(np.float64))
+    assert_rel(host(y), ry, 2e-5, 2e-5, "ln 3-phase y")
+    # backward: PARTIAL per tile, APPLY per tile (dx accumulates onto an existing gradient)
+    rdx, rdg, rdb = og.layernorm_bwd(dy.astype(np.float64), x64, g64, mu, rs)
+    dx0 = synth.rand_normal((rows, cols), 15)
+    dx = dev(dx0)
+    dgam, dbet = dev(np.full(cols, 0.25, np.float32)), dev(np.zeros(cols, np.float32))
+    bparts = empty((ne, rows, 2))
+    for i, (c0, c1) in enumerate(tiles):
+        w = c1 - c0
+        tt.tile_layernorm_bwd(None, tt.TT_LN_PARTIAL, rows, w, cols, DY[:, c0:c1].contiguous(), w,
+                              X[:, c0:c1].contiguous(), w, G[c0:c1].contiguous(), stats, bparts[i], 0, 0, None, 0, 0,
+                              None, None, None)
+    for i, (c0, c1) in enumerate(tiles):
+        w = c1 - c0
+        ws = torch.empty(tt.tile_layernorm_bwd_workspace(rows, w) // 4 + 1, device="cuda")
+        dxt = dx[:, c0:c1].contiguous()
+        dgt, dbt = dgam[c0:c1].contiguous(), dbet[c0:c1].contiguous()
+        tt.tile_layernorm_bwd(None, tt.TT_LN_APPLY, rows, w, cols, DY[:, c0:c1].contiguous(), w,
+                              X[:, c0:c1].contiguous(), w, G[c0:c1].contiguous(), stats, bparts, ne, rows * 2, dxt,
+                              w, 1, dgt, dbt, ws)
+        dx[:, c0:c1] = dxt
+        dgam[c0:c1] = dgt
+        dbet[c0:c1] = dbt
+    assert_rel(host(dx), dx0 + rdx, 1e-4, 1e-5, "ln dx")
+    assert_rel(host(dgam), 0.25 + rdg, 1e-4, 1e-4, "ln dgamma")
+    assert_rel(host(dbet), rdb, 1e-4, 1e-4, "ln dbeta")
+
+
+@pytest.mark.parametrize("rows,cols", [(5, 64), (1000, 768), (64, 33)])
+def test_layernorm_bwd_fused(rows, cols):
+    x = synth.rand_normal((rows, cols), 21, std=2.0)
+    g = synth.rand_normal((cols,), 22) + 1
+    dy = synth.rand_normal((rows, cols), 23)
+    ry, (mu, rs) = og.layernorm_fwd(x.astype(np.float64), g.astype(np.float64), np.zeros(cols))
+    stats = dev(np.stack([mu, rs], 1).astype(np.float32))
+    dx = empty((rows, cols))
+    dgam, dbet = dev(np.zeros(cols, np.float32)), dev(np.zeros(cols, np.float32))
+    ws = torch.empty(tt.tile_layernorm_bwd_workspace(rows, cols) // 4 + 1, device="cuda")
+    tt.tile_layernorm_bwd(None, tt.TT_LN_FUSED, rows, cols, cols, dev(dy), cols, dev(x), cols, dev(g), stats, None,
+                          0, 0, dx, cols, 0, dgam, dbet, ws)
+    rdx, rdg, rdb = og.layernorm_bwd(dy.astype(np.float64), x.astype(np.float64), g.astype(np.float64), mu, rs)
+    assert_rel(host(dx), rdx, 1e-4, 1e-5, "ln dx")
+    assert_rel(host(dgam), rdg, 1e-4, 1e-4, "dgamma")
+    assert_rel(host(dbet), rdb, 1e-4, 1e-4, "dbeta")
+
+
+# ------------------------------------------------------- softmax / CE
+
+@pytest.mark.parametrize("rows,cols,vt", [(64, 256, 32), (300, 5000, 768), (7, 2049, 2048), (33, 100, 100)])
+def test_cross_entropy_tiles(rows, cols, vt):
+    z = synth.rand_normal((rows, cols), 31, std=3.0)
+    y = np.random.default_rng(32).integers(0, cols, rows).astype(np.int32)
+    Z, Y = dev(z), dev(y)
+    tiles = otl.tiles(cols, vt)
+    parts = empty((len(tiles), rows, 3))
+    for i, (c0, c1) in enumerate(tiles):
+        tt.tile_softmax(None, tt.TT_SM_STATS, rows, c1 - c0, 0, c0, 1.0, 0, Z[:, c0:c1].contiguous(), c1 - c0, Y,
+                        parts[i], 0, 0, None, None, None, 0, 1.0)
+    lse, rl = empty((rows,)), empty((rows,))
+    tt.tile_softmax(None, tt.TT_SM_MERGE, rows, 0, 0, 0, 1.0, 0, None, 0, None, parts, len(tiles), rows * 3, lse, rl,
+                    None, 0, 1.0)
+    loss = empty((1,))
+    half = rows // 2
+    tt.tile_xentropy(None, tt.TT_XE_LOSS, half, 0, 0, None, None, 0, None, rl, loss, 0, 1.0 / rows)
+    tt.tile_xentropy(None, tt.TT_XE_LOSS, rows - half, 0, 0, None, None, 0, None, rl[half:], loss, 1, 1.0 / rows)
+    rloss, rdz, rlse = og.cross_entropy(z.astype(np.float64), y)
+    assert_rel(host(lse), rlse, 1e-6, 1e-6, "lse")
+    assert abs(host(loss)[0] - rloss) <= 1e-5 * abs(rloss)
+    dz = Z.clone()
+    for c0, c1 in tiles:
+        blk = dz[:, c0:c1].contiguous()
+        tt.tile_xentropy(None, tt.TT_XE_GRAD, rows, c1 - c0, c0, Y, blk, c1 - c0, lse, None, None, 0, 1.0 / rows)
+        dz[:, c0:c1] = blk
+    assert_rel(host(dz), rdz, 1e-5, 1e-7 / rows, "dz")
+
+
+def test_softmax_causal_apply():
+    rows, cols, roff, coff, scale = 40, 96, 50, 30, 0.7
+    x = synth.rand_normal((rows, cols), 41)
+    X = dev(x)
+    parts, lse, Y = empty((1, rows, 3)), empty((rows,)), empty((rows, cols))
+    tt.tile_softmax(None, tt.TT_SM_STATS, rows, cols, roff, coff, scale, 1, X, cols, None, parts, 0, 0, None, None,
+                    None, 0, 1.0)
+    tt.tile_softmax(None, tt.TT_SM_MERGE, rows, 0, 0, 0, 1.0, 0, None, 0, None, parts, 1, rows * 3, lse, None, None,
+                    0, 1.0)
+    tt.tile_softmax(None, tt.TT_SM_APPLY, rows, cols, roff, coff, scale, 1, X, cols, None, None, 0, 0, lse, None, Y,
+                    cols, 1.0)
+    s = x.astype(np.float64) * scale
+    mask = (coff + np.arange(cols))[None, :] > (roff + np.arange(rows))[:, None]
+    s[mask] = -np.inf
+    assert_rel(host(Y), og.softmax(s), 1e-5, 1e-7, "causal softmax")
+
+
+# ------------------------------------------------------------ attention
+
+def _attn_inputs(b, t, h, hd, seed):
+    q = synth.rand_normal((b, t, h, hd), seed)
+    k = synth.rand_normal((b, t, h, hd), seed + 1)
+    v = synth.rand_normal((b, t, h, hd), seed + 2)
+    return q, k, v
+
+
+def _attn_ref(q, k, v):
+    f = lambda a: a.astype(np.float64).transpose(0, 2, 1, 3)  # noqa: E731
+    o, p = og.causal_attention_fwd(f(q), f(k), f(v))
+    hd = q.shape[-1]
+    s = f(q) @ np.swapaxes(f(k), -1, -2) / math.sqrt(hd)
+    t = q.shape[1]
+    s = np.where(np.triu(np.ones((t, t), bool), 1), -np.inf, s)
+    return o, p, og.logsumexp(s)
+
+
+@pytest.mark.parametrize("b,t,h,hd", [(2, 32, 4, 16), (1, 200, 3, 64), (2, 256, 2, 128), (1, 130, 1, 32)])
+def test_attention_fwd_single_tile(b, t, h, hd):
+    q, k, v = _attn_inputs(b, t, h, hd, 51 + hd)
+    O, lse = empty((b, t, h, hd)), empty((b, h, t))
+    tt.tile_attention_fwd(None, b, h, t, t, hd, 0, 0, dev(q), dev(k), dev(v), O, None, lse, 1, 1, 1 / math.sqrt(hd))
+    ro, _, rlse = _attn_ref(q, k, v)
+    assert_rel(host(O).transpose(0, 2, 1, 3), ro, 1e-4, 2e-5, "attn O")
+    assert_rel(host(lse), rlse, 1e-5, 1e-5, "attn lse")
+
+
+@pytest.mark.parametrize("hd,st", [(64, 64), (128, 96), (16, 8)])
+def test_attention_fwd_bwd_tile_pairs(hd, st):
+    b, h, t = 2, 2, 3 * st
+    q, k, v = _attn_inputs(b, t, h, hd, 61)
+    do = synth.rand_normal((b, t, h, hd), 64)
+    scale = 1 / math.sqrt(hd)
+    seq = lambda a, i: dev(np.ascontiguousarray(a[:, i * st:(i + 1) * st]))  # noqa: E731
+    n = t // st
+    Q = [seq(q, i) for i in range(n)]
+    K = [seq(k, i) for i in range(n)]
+    V = [seq(v, i) for i in range(n)]
+    dO = [seq(do, i) for i in range(n)]
+    O = [empty((b, st, h, hd)) for _ in range(n)]
+    lse = [empty((b, h, st)) for _ in range(n)]
+    ml = empty((b, h, st, 2))
+    for qi in range(n):
+        for ki in range(qi + 1):
+            tt.tile_attention_fwd(None, b, h, st, st, hd, qi * st, ki * st, Q[qi], K[ki], V[ki], O[qi], ml, lse[qi],
+                                  int(ki == 0), int(ki == qi), scale)
+    ro, rp, rlse = _attn_ref(q, k, v)
+    got_o = np.concatenate([host(x) for x in O], axis=1).transpose(0, 2, 1, 3)
+    assert_rel(got_o, ro, 1e-4, 2e-5, "tiled attn O")
+    assert_rel(np.concatenate([host(x) for x in lse], axis=2), rlse, 1e-5, 1e-5, "tiled lse")
+    # backward by tile pairs
+    Dv = [empty((b, h, st)) for _ in range(n)]
+    dQ = [empty((b, st, h, hd)) for _ in range(n)]
+    dK = [empty((b, st, h, hd)) for _ in range(n)]
+    dV = [empty((b, st, h, hd)) for _ in range(n)]
+    for qi in range(n):
+        tt.tile_attention_bwd(None, tt.TT_ATT_PREP, b, h, st, st, hd, 0, 0, None, None, None, O[qi], dO[qi], None,
+                              Dv[qi], None, None, None, 0, 0, scale)
+    for qi in range(n):
+        for ki in range(qi + 1):
+            tt.tile_attention_bwd(None, tt.TT_ATT_GRAD, b, h, st, st, hd, qi * st, ki * st, Q[qi], K[ki], V[ki], None,
+                                  dO[qi], lse[qi], Dv[qi], dQ[qi], dK[ki], dV[ki], int(ki > 0), int(qi > ki), scale)
+    f = lambda a: a.astype(np.float64).transpose(0, 2, 1, 3)  # noqa: E731
+    rdq, rdk, rdv = og.causal_attention_bwd(f(do), f(q), f(k), f(v), rp)
+    cat = lambda xs: np.concatenate([host(x) for x in xs], axis=1).transpose(0, 2, 1, 3)  # noqa: E731
+    for got, ref, name in ((cat(dQ), rdq, "dQ"), (cat(dK), rdk, "dK"), (cat(dV), rdv, "dV")):
+        assert_rel(got, ref, 2e-4, 2e-4 * np.abs(ref).max(), name)
+
+
+# ---------------------------------------------------------------- AdamW
+
+@pytest.mark.parametrize("n", [1, 1000, 4096 + 3, 1 << 20])
+def test_fused_adamw(n):
+    p = synth.rand_normal((n,), 71)
+    g = synth.rand_normal((n,), 72) * np.logspace(-6, 0, n).astype(np.float32)
+    P, G = dev(p), dev(g)
+    M, V = dev(np.zeros(n, np.float32)), dev(np.zeros(n, np.float32))
+    step = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bc = empty((2,))
+    rp, rm, rv = p.astype(np.float64), np.zeros(n), np.zeros(n)
+    for t in (1, 2, 3):
+        tt.tile_adamw_advance(None, step, bc, 0.9, 0.999)
+        tt.tile_fused_adamw(None, n, P, G, M, V, 3e-4, 0.9, 0.999, 1e-8, 0.1, bc)
+        rp, rm, rv = og.adamw(rp, g.astype(np.float64), rm, rv, t, 3e-4, 0.9, 0.999, 1e-8, 0.1)
+    assert int(step.item()) == 3
+    assert_rel(host(bc), [1 - 0.9 ** 3, 1 - 0.999 ** 3], 1e-6)
+    assert_rel(host(M), rm, 1e-5, 1e-12, "m")
+    assert_rel(host(V), rv, 1e-5, 1e-20, "v")
+    # parameter: abs floor well below one lr step
+    assert_close_bound(host(P), rp, 1e-6 * np.abs(rp) + 1e-3 * 3e-4, "p")
+
+
+# ----------------------------------------------------- embedding / misc
+
+def test_embedding_fwd_bwd():
+    vocab, d, bt, st = 300, 96, 3, 40
+    rows = bt * st
+    wte = synth.rand_normal((vocab, d), 81)
+    wpe = synth.rand_normal((st, d), 82)
+    rng = np.random.default_rng(83)
+    ids = rng.integers(0, vocab, rows).astype(np.int32)
+    ids[:10] = 7  # repeated ids
+    out = empty((rows, d))
+    IDS = dev(ids)
+    tt.tile_embedding_fwd(None, rows, d, IDS, vocab, dev(wte), d, dev(wpe), d, st, 0, out, d)
+    ref = wte[ids] + wpe[np.arange(rows) % st]
+    assert np.array_equal(host(out), ref.astype(np.float32).astype(np.float64))
+    srt = torch.empty(rows, dtype=torch.int32, device="cuda")
+    perm = torch.empty(rows, dtype=torch.int32, device="cuda")
+    tt.tile_embedding_index(None, rows, IDS, srt, perm)
+    order = np.argsort(ids, kind="stable")
+    assert np.array_equal(perm.cpu().numpy(), order) and np.array_equal(srt.cpu().numpy(), ids[order])
+    dh = synth.rand_normal((rows, d), 84)
+    dw0 = synth.rand_normal((vocab, d), 85)
+    DW = dev(dw0)
+    vt = 128
+    for v0, v1 in otl.tiles(vocab, vt):
+        blk = DW[v0:v1].contiguous()
+        tt.tile_embedding_bwd(None, tt.TT_EMB_TOKEN, rows, d, srt, perm, v0, v1 - v0, st, dev(dh), d, blk, d)
+        DW[v0:v1] = blk
+    rdw = dw0 + otl.embedding_bwd_tiled(dh.astype(np.float64), ids, vocab, vt, d, rows)
+    assert_rel(host(DW), rdw, 1e-6, 1e-6, "dwte")
+    dp = dev(np.zeros((st, d), np.float32))
+    tt.tile_embedding_bwd(None, tt.TT_EMB_POS, rows, d, None, None, 0, 0, st, dev(dh), d, dp, d)
+    assert_rel(host(dp), dh.astype(np.float64).reshape(bt, st, d).sum(0), 1e-6, 1e-6, "dwpe")
+
+
+def test_embedding_out_of_range_id_gives_nan_row():
+    ids = np.array([0, 5, 99, -1], np.int32)
+    wte = synth.rand_normal((5, 8), 1)
+    wpe = synth.rand_normal((4, 8), 2)
+    out = empty((4, 8), fill=0.0)
+    tt.tile_embedding_fwd(None, 4, 8, dev(ids), 5, dev(wte), 8, dev(wpe), 8, 4, 0, out, 8)
+    got = host(out)
+    assert np.isfinite(got[0]).all() and np.isnan(got[1]).all() and np.isnan(got[2]).all() and np.isnan(got[3]).all()
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 5), (4096, 768), (300, 3072), (1000, 33)])
+def test_reduce_rows(rows, cols):
+    x = synth.rand_normal((rows, cols), 91)
+    out = dev(np.full(cols, 2.0, np.float32))
+    ws = torch.empty(tt.tile_reduce_rows_workspace(rows, cols) // 4 + 1, device="cuda")
+    tt.tile_reduce_rows(None, rows, cols, dev(x), cols, out, 1, ws)
+    ref = 2.0 + x.astype(np.float64).sum(0)
+    bound = (np.abs(x).astype(np.float64).sum(0) + 2) * rows * EPS32
+    assert_close_bound(host(out), ref, bound, "reduce_rows")
+    # deterministic: same bits on a second run
+    out2 = dev(np.full(cols, 2.0, np.float32))
+    tt.tile_reduce_rows(None, rows, cols, dev(x), cols, out2, 1, ws)
+    assert torch.equal(out, out2)
+
+
+def test_fill_and_split_tokens():
+    f = empty((1000,))
+    tt.tile_fill(None, 1000, f, 3.5)
+    assert (host(f) == 3.5).all()
+    tok = np.random.default_rng(1).integers(0, 50257, (3, 9)).astype(np.int32)
+    ids = torch.empty(24, dtype=torch.int32, device="cuda")
+    lab = torch.empty(24, dtype=torch.int32, device="cuda")
+    tt.tile_split_tokens(None, 3, 8, dev(tok), ids, lab)
+    assert np.array_equal(ids.cpu().numpy().reshape(3, 8), tok[:, :8])
+    assert np.array_equal(lab.cpu().numpy().reshape(3, 8), tok[:, 1:])

@@ -1,0 +1,166 @@
+"""ctypes binding of libtiletask (include/tiletask.h), same names as the C ABI.
+
+Argument marshalling only: device buffers may be passed as torch tensors
+(their data_ptr() is used), integers (raw addresses) or None; streams as
+torch.cuda.Stream, integers (hipStream_t) or None (default stream). Every
+call checks the return code and raises TTError with tt_last_error().
+There is no fallback: if libtiletask.so is missing the import fails.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("TILETASK_LIB", os.path.join(_HERE, "libtiletask.so"))
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libtiletask.so not found at {LIB_PATH}: build it with "
+                      "`python -m tile_task_transformer_amd.build` (hipcc, gfx950)")
+lib = C.CDLL(LIB_PATH)
+
+# ---- constants (mirror include/tiletask.h)
+TT_OK, TT_ERR_ARG, TT_ERR_SHAPE, TT_ERR_OOM, TT_ERR_HIP, TT_ERR_STATE, TT_ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
+TT_EPI_NONE, TT_EPI_BIAS, TT_EPI_RES, TT_EPI_GELU, TT_EPI_GELU_BWD = 0, 1, 2, 4, 8
+TT_LN_PARTIAL, TT_LN_MERGE, TT_LN_APPLY, TT_LN_FUSED = 0, 1, 2, 3
+TT_SM_STATS, TT_SM_MERGE, TT_SM_APPLY = 0, 1, 2
+TT_XE_LOSS, TT_XE_GRAD = 0, 1
+TT_ATT_PREP, TT_ATT_GRAD = 0, 1
+TT_EMB_TOKEN, TT_EMB_POS = 0, 1
+TT_MAX_DIMS = 6
+TT_F32, TT_I32 = 0, 1
+TT_HOME_DEVICE, TT_HOME_PINNED_HOST = 0, 1
+TT_DEVICE_DRYRUN = -1
+TT_R, TT_W, TT_RW = 1, 2, 3
+
+_ERRNAMES = {-1: "TT_ERR_ARG", -2: "TT_ERR_SHAPE", -3: "TT_ERR_OOM", -4: "TT_ERR_HIP", -5: "TT_ERR_STATE",
+             -6: "TT_ERR_UNSUPPORTED"}
+
+
+class TTError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_ERRNAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+class tt_access(C.Structure):
+    _fields_ = [("tensor", C.c_void_p), ("tile", C.c_int64 * TT_MAX_DIMS), ("mode", C.c_int)]
+
+
+class tt_stats(C.Structure):
+    _fields_ = [("tasks", C.c_int64), ("edges", C.c_int64), ("cross_stream_waits", C.c_int64),
+                ("events_recorded", C.c_int64), ("submit_seconds", C.c_double), ("h2d_bytes", C.c_int64),
+                ("d2h_bytes", C.c_int64), ("evictions", C.c_int64), ("prefetches", C.c_int64)]
+
+
+class tt_gpt2_config(C.Structure):
+    _fields_ = [("n_layer", C.c_int), ("vocab", C.c_int), ("n_embd", C.c_int), ("n_head", C.c_int),
+                ("n_inner", C.c_int), ("seq", C.c_int), ("batch", C.c_int), ("ln_eps", C.c_float)]
+
+
+class tt_gpt2_tiles(C.Structure):
+    _fields_ = [("batch", C.c_int), ("seq", C.c_int), ("embd", C.c_int), ("inner", C.c_int), ("head", C.c_int),
+                ("vocab", C.c_int)]
+
+
+class tt_adamw_hparams(C.Structure):
+    _fields_ = [("lr", C.c_float), ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float),
+                ("weight_decay", C.c_float)]
+
+
+P, I, I64, F, SZ = C.c_void_p, C.c_int, C.c_int64, C.c_float, C.c_size_t
+PP = C.POINTER(C.c_void_p)
+
+# name -> (restype, argtypes)
+SIGNATURES = {
+    "tt_last_error": (C.c_char_p, []),
+    "tt_version": (C.c_char_p, []),
+    "tile_gemm": (I, [P, I, I, I64, I64, I64, F, P, I64, P, I64, F, P, I64, I, P, P, I64, P, I64]),
+    "tile_layernorm_fwd": (I, [P, I, I64, I64, P, I64, P, P, P, I64, I64, P, P, I64, F]),
+    "tile_layernorm_bwd": (I, [P, I, I64, I64, I64, P, I64, P, I64, P, P, P, I64, I64, P, I64, I, P, P, P]),
+    "tile_layernorm_bwd_workspace": (SZ, [I64, I64]),
+    "tile_softmax": (I, [P, I, I64, I64, I64, I64, F, I, P, I64, P, P, I64, I64, P, P, P, I64, F]),
+    "tile_xentropy": (I, [P, I, I64, I64, I64, P, P, I64, P, P, P, I, F]),
+    "tile_attention_fwd": (I, [P, I64, I64, I64, I64, I64, I64, I64, P, P, P, P, P, P, I, I, F]),
+    "tile_attention_bwd": (I, [P, I, I64, I64, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P, I, I, F]),
+    "tile_fused_adamw": (I, [P, I64, P, P, P, P, F, F, F, F, F, P]),
+    "tile_adamw_advance": (I, [P, P, P, F, F]),
+    "tile_embedding_fwd": (I, [P, I64, I64, P, I64, P, I64, P, I64, I64, I64, P, I64]),
+    "tile_embedding_index": (I, [P, I64, P, P, P]),
+    "tile_embedding_bwd": (I, [P, I, I64, I64, P, P, I64, I64, I64, P, I64, P, I64]),
+    "tile_reduce_rows": (I, [P, I64, I64, P, I64, P, I, P]),
+    "tile_reduce_rows_workspace": (SZ, [I64, I64]),
+    "tile_fill": (I, [P, I64, P, F]),
+    "tile_split_tokens": (I, [P, I64, I64, P, P, P]),
+    "tt_ctx_create": (I, [I, I, I, SZ, PP]),
+    "tt_ctx_destroy": (I, [P]),
+    "tt_ctx_stream": (I, [P, I, PP]),
+    "tt_ctx_record": (I, [P, I]),
+    "tt_tensor_create": (I, [P, I, C.POINTER(I64), C.POINTER(I64), I, I, PP]),
+    "tt_tensor_wrap": (I, [P, I, C.POINTER(I64), C.POINTER(I64), I, P, PP]),
+    "tt_tensor_destroy": (I, [P]),
+    "tt_tensor_bytes": (I64, [P]),
+    "tt_tensor_grid": (I, [P, C.POINTER(I64), C.POINTER(I64)]),
+    "tt_tensor_tile": (I, [P, C.POINTER(I64), PP, C.POINTER(I64)]),
+    "tt_tensor_copy_in": (I, [P, P]),
+    "tt_tensor_copy_out": (I, [P, P]),
+    "tt_submit_nop": (I, [P, C.c_char_p, C.POINTER(tt_access), I]),
+    "tt_submit_gemm": (I, [P, I, I, F, P, C.POINTER(I64), P, C.POINTER(I64), F, P, C.POINTER(I64)]),
+    "tt_submit_fill": (I, [P, P, C.POINTER(I64), F]),
+    "tt_wait": (I, [P]),
+    "tt_dump_dag": (I, [P, C.c_char_p]),
+    "tt_get_stats": (I, [P, C.POINTER(tt_stats)]),
+    "tt_reset_stats": (I, [P]),
+    "tt_gpt2_create": (I, [P, C.POINTER(tt_gpt2_config), C.POINTER(tt_gpt2_tiles), I, PP]),
+    "tt_gpt2_destroy": (I, [P]),
+    "tt_gpt2_num_params": (I, [P, C.POINTER(I)]),
+    "tt_gpt2_param": (I, [P, I, PP, PP, PP, PP]),
+    "tt_gpt2_step": (I, [P, P, C.POINTER(tt_adamw_hparams), I]),
+    "tt_gpt2_loss": (I, [P, C.POINTER(F)]),
+    "tt_gpt2_task_count": (I, [P, C.POINTER(I64)]),
+}
+
+for _name, (_res, _args) in SIGNATURES.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+def last_error() -> str:
+    return lib.tt_last_error().decode()
+
+
+def check(rc: int) -> int:
+    if rc != TT_OK:
+        raise TTError(rc, last_error())
+    return rc
+
+
+def ptr(x) -> int | None:
+    """Device/host address of a torch tensor, numpy array, int or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    if hasattr(x, "ctypes"):
+        return x.ctypes.data
+    raise TypeError(f"cannot take the address of {type(x)}")
+
+
+def stream_handle(s) -> int | None:
+    if s is None:
+        return None
+    if isinstance(s, int):
+        return s
+    if hasattr(s, "cuda_stream"):
+        return s.cuda_stream
+    raise TypeError(f"not a stream: {type(s)}")
+
+
+def i64_array(vals):
+    arr = (C.c_int64 * TT_MAX_DIMS)()
+    for i, v in enumerate(vals):
+        arr[i] = int(v)
+    return arr

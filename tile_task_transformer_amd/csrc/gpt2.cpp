@@ -1,0 +1,914 @@
+// The GPT2 training step as tile tasks (model level of the C ABI).
+//
+// The pith.science review of NNTile ("What carries the argument") states the
+// recipe this file follows: split every tensor into tiles along all axes and
+// express every layer -- embedding, linear, layer norm, softmax/attention,
+// cross-entropy and the Adam update -- as tasks on a few tiles, forward and
+// backward, so that one training iteration is a single graph of small tasks.
+// The NNTile README ("Minimal working GPT example") supplies the tile flags
+// (batch/minibatch, seq, embd, inner and head tiles; seq, head and batch
+// tiles divide their axis, embd and inner tiles need not) and the optimiser
+// (fused AdamW, eps 1e-8, weight decay 0.1, lr 3e-4, mean loss).
+//
+// Model form (readings of what the pages leave open): pre-LN GPT2 blocks,
+// GELU (tanh) MLP, LayerNorm eps 1e-5 with biased variance, biases on every
+// linear layer, causal attention scaled by 1/sqrt(head_dim), LM head tied to
+// the token embedding, no dropout, one AdamW group with decay on every
+// parameter.
+//
+// Every task below names the tiles it reads and writes; the executor infers
+// the ordering. Submission order is the program order of the untiled step:
+// embedding, blocks, final LN, head, loss, then the backward in reverse and
+// AdamW.
+#include <cmath>
+#include <cstring>
+#include <memory>
+
+#include "runtime.hpp"
+
+using namespace tt;
+
+namespace {
+
+struct BlockT {
+  tt_tensor *h_in, *ln1, *n1, *q, *k, *v, *o, *lse, *h_mid, *ln2, *n2, *u, *g;
+};
+
+}  // namespace
+
+struct tt_gpt2 {
+  tt_ctx* ctx = nullptr;
+  tt_gpt2_config c{};
+  tt_gpt2_tiles t{};
+  int param_home = TT_HOME_DEVICE;
+  // tile grid sizes
+  int64_t nb = 0, ns = 0, ntok = 0, NE = 0, NI = 0, NH = 0, NV = 0, rows = 0, hd = 0;
+  std::vector<tt_tensor*> P, G, M, Vv;  // parameter, gradient, moments (param_specs order)
+  std::vector<tt_tensor*> owned;        // every tensor to destroy
+  // activations
+  tt_tensor *tokens = nullptr, *ids = nullptr, *labels = nullptr, *sorted = nullptr, *perm = nullptr;
+  std::vector<BlockT> blk;
+  tt_tensor *h_last = nullptr, *lnf = nullptr, *nf = nullptr, *z = nullptr;
+  tt_tensor *ml = nullptr, *ln_parts = nullptr, *lnb_parts = nullptr, *ce_parts = nullptr;
+  tt_tensor *ce_lse = nullptr, *row_loss = nullptr, *loss = nullptr;
+  tt_tensor *dnf = nullptr, *dh = nullptr, *dgu = nullptr, *dn = nullptr, *dO = nullptr, *dq = nullptr,
+            *dk = nullptr, *dv = nullptr, *Dv = nullptr;
+  tt_tensor *step = nullptr, *bc = nullptr;
+  int64_t last_tasks = 0;
+
+  enum { WTE = 0, WPE = 1 };
+  int pidx(int layer, int which) const { return 2 + 12 * layer + which; }
+  int lnf_g() const { return 2 + 12 * c.n_layer; }
+};
+
+namespace {
+
+enum { LN1G, LN1B, WQKV, BQKV, WO, BO, LN2G, LN2B, WFC, BFC, WP, BP };
+
+int mk(tt_gpt2* g, tt_tensor** out, const char* name, std::initializer_list<int64_t> shape,
+       std::initializer_list<int64_t> tile, int split, int dtype = TT_F32, int home = TT_HOME_DEVICE) {
+  std::vector<int64_t> s(shape), t(tile);
+  int rc = tensor_create(g->ctx, (int)s.size(), s.data(), t.data(), dtype, home, split, name, out);
+  if (rc == TT_OK) g->owned.push_back(*out);
+  return rc;
+}
+
+// tile lin helpers
+int64_t L(tt_tensor* t, std::initializer_list<int64_t> idx) {
+  int64_t a[TT_MAX_DIMS] = {};
+  int i = 0;
+  for (int64_t v : idx) a[i++] = v;
+  return t->lin(a);
+}
+float* F(tt_tensor* t, int64_t lin) { return (float*)t->dev(lin); }
+const int32_t* I32(tt_tensor* t, int64_t lin) { return (const int32_t*)t->dev(lin); }
+
+struct Gemm {
+  int ta = 0, tb = 0;
+  float alpha = 1.f, beta = 0.f;
+  TileRef A, B, C;
+  int epi = TT_EPI_NONE;
+  TileRef bias, res, aux;
+};
+
+int submit_gemm(tt_ctx* ctx, const char* label, const Gemm& q) {
+  int64_t ar, ac, br, bc, cr, cc;
+  q.A.t->mat(q.A.lin, &ar, &ac);
+  q.B.t->mat(q.B.lin, &br, &bc);
+  q.C.t->mat(q.C.lin, &cr, &cc);
+  const int64_t m = q.ta ? ac : ar, k = q.ta ? ar : ac;
+  const int64_t kb = q.tb ? bc : br, n = q.tb ? br : bc;
+  if (k != kb || m != cr || n != cc)
+    return fail(TT_ERR_SHAPE, "%s: op(A) %lldx%lld op(B) %lldx%lld C %lldx%lld", label, (long long)m, (long long)k,
+                (long long)kb, (long long)n, (long long)cr, (long long)cc);
+  std::vector<Access> acc = {R(q.A.t, q.A.lin), R(q.B.t, q.B.lin)};
+  const bool gelu = q.epi & TT_EPI_GELU;
+  acc.push_back((q.beta == 0.f || gelu) ? (gelu ? R(q.C.t, q.C.lin) : W(q.C.t, q.C.lin)) : RW(q.C.t, q.C.lin));
+  if (gelu) acc.back().mode = TT_W;
+  if (q.bias.valid()) acc.push_back(R(q.bias.t, q.bias.lin));
+  if (q.res.valid()) acc.push_back(R(q.res.t, q.res.lin));
+  if (q.aux.valid()) acc.push_back(gelu ? RW(q.aux.t, q.aux.lin) : R(q.aux.t, q.aux.lin));
+  Gemm p = q;
+  return ctx->submit(label, std::move(acc), [p, m, n, k, ac, bc, cc](hipStream_t s, void*) {
+    int64_t ldr = 0, ldaux = 0, rr, rc_;
+    if (p.res.valid()) p.res.t->mat(p.res.lin, &rr, &ldr);
+    if (p.aux.valid()) p.aux.t->mat(p.aux.lin, &rr, &ldaux);
+    (void)rc_;
+    return tile_gemm(s, p.ta, p.tb, m, n, k, p.alpha, F(p.A.t, p.A.lin), ac, F(p.B.t, p.B.lin), bc, p.beta,
+                     F(p.C.t, p.C.lin), cc, p.epi, p.bias.valid() ? F(p.bias.t, p.bias.lin) : nullptr,
+                     p.res.valid() ? F(p.res.t, p.res.lin) : nullptr, ldr,
+                     p.aux.valid() ? F(p.aux.t, p.aux.lin) : nullptr, ldaux);
+  });
+}
+
+int fill_task(tt_ctx* ctx, tt_tensor* t, int64_t lin, float v) {
+  const int64_t n = t->tile_elems(lin);
+  return ctx->submit("fill", {W(t, lin)}, [t, lin, n, v](hipStream_t s, void*) { return tile_fill(s, n, F(t, lin), v); });
+}
+
+#define TRY(x)                 \
+  do {                         \
+    int rc_ = (x);             \
+    if (rc_ != TT_OK) return rc_; \
+  } while (0)
+
+// ------------------------------------------------------------ LayerNorm
+
+// y = LN(x) over the embd tiles of token tile ti
+int ln_forward(tt_gpt2* g, tt_tensor* x, tt_tensor* gam, tt_tensor* bet, tt_tensor* stats, tt_tensor* y, int64_t ti,
+               int64_t bi, int64_t si) {
+  tt_ctx* ctx = g->ctx;
+  const float eps = g->c.ln_eps;
+  const int64_t rows = g->rows;
+  const int64_t st = L(stats, {bi, si, 0});
+  if (g->NE == 1) {
+    const int64_t lx = L(x, {bi, si, 0}), ly = L(y, {bi, si, 0});
+    const int64_t cols = g->c.n_embd;
+    return ctx->submit("ln_fwd", {R(x, lx), R(gam, 0), R(bet, 0), W(stats, st), W(y, ly)},
+                       [=](hipStream_t s, void*) {
+                         return tile_layernorm_fwd(s, TT_LN_FUSED, rows, cols, F(x, lx), cols, F(gam, 0), F(bet, 0),
+                                                   nullptr, 0, 0, F(stats, st), F(y, ly), cols, eps);
+                       });
+  }
+  tt_tensor* parts = g->ln_parts;
+  std::vector<Access> merge_acc;
+  for (int64_t e = 0; e < g->NE; ++e) {
+    const int64_t lx = L(x, {bi, si, e}), lp = L(parts, {e, ti, 0});
+    int64_t r, cols;
+    x->mat(lx, &r, &cols);
+    TRY(ctx->submit("ln_part", {R(x, lx), W(parts, lp)}, [=](hipStream_t s, void*) {
+      return tile_layernorm_fwd(s, TT_LN_PARTIAL, rows, cols, F(x, lx), cols, nullptr, nullptr, F(parts, lp), 0, 0,
+                                nullptr, nullptr, 0, eps);
+    }));
+    merge_acc.push_back(R(parts, lp));
+  }
+  merge_acc.push_back(W(stats, st));
+  const int64_t lp0 = L(parts, {0, ti, 0});
+  const int64_t stride = rows * 3, ne = g->NE;
+  TRY(ctx->submit("ln_merge", merge_acc, [=](hipStream_t s, void*) {
+    return tile_layernorm_fwd(s, TT_LN_MERGE, rows, 0, nullptr, 0, nullptr, nullptr, F(parts, lp0), ne, stride,
+                              F(stats, st), nullptr, 0, eps);
+  }));
+  for (int64_t e = 0; e < g->NE; ++e) {
+    const int64_t lx = L(x, {bi, si, e}), ly = L(y, {bi, si, e});
+    int64_t r, cols;
+    x->mat(lx, &r, &cols);
+    TRY(ctx->submit("ln_apply", {R(x, lx), R(gam, e), R(bet, e), R(stats, st), W(y, ly)}, [=](hipStream_t s, void*) {
+      return tile_layernorm_fwd(s, TT_LN_APPLY, rows, cols, F(x, lx), cols, F(gam, e), F(bet, e), nullptr, 0, 0,
+                                F(stats, st), F(y, ly), cols, eps);
+    }));
+  }
+  return TT_OK;
+}
+
+// dx (+)= LN_bwd(dy) for token tile ti; dgamma/dbeta accumulate
+int ln_backward(tt_gpt2* g, tt_tensor* dy, tt_tensor* x, tt_tensor* gam, tt_tensor* stats, tt_tensor* dx,
+                int dx_acc, tt_tensor* dgam, tt_tensor* dbet, int64_t ti, int64_t bi, int64_t si) {
+  tt_ctx* ctx = g->ctx;
+  const int64_t rows = g->rows, n_total = g->c.n_embd;
+  const int64_t st = L(stats, {bi, si, 0});
+  if (g->NE == 1) {
+    const int64_t ly = L(dy, {bi, si, 0}), lx = L(x, {bi, si, 0}), ld = L(dx, {bi, si, 0});
+    const int64_t cols = n_total;
+    return ctx->submit("ln_bwd",
+                       {R(dy, ly), R(x, lx), R(gam, 0), R(stats, st), dx_acc ? RW(dx, ld) : W(dx, ld), RW(dgam, 0),
+                        RW(dbet, 0)},
+                       [=](hipStream_t s, void* ws) {
+                         return tile_layernorm_bwd(s, TT_LN_FUSED, rows, cols, n_total, F(dy, ly), cols, F(x, lx),
+                                                   cols, F(gam, 0), F(stats, st), nullptr, 0, 0, F(dx, ld), cols,
+                                                   dx_acc, F(dgam, 0), F(dbet, 0), ws);
+                       });
+  }
+  tt_tensor* parts = g->lnb_parts;
+  std::vector<Access> part_reads;
+  for (int64_t e = 0; e < g->NE; ++e) {
+    const int64_t ly = L(dy, {bi, si, e}), lx = L(x, {bi, si, e}), lp = L(parts, {e, ti, 0});
+    int64_t r, cols;
+    x->mat(lx, &r, &cols);
+    TRY(ctx->submit("lnb_part", {R(dy, ly), R(x, lx), R(gam, e), R(stats, st), W(parts, lp)},
+                    [=](hipStream_t s, void*) {
+                      return tile_layernorm_bwd(s, TT_LN_PARTIAL, rows, cols, n_total, F(dy, ly), cols, F(x, lx),
+                                                cols, F(gam, e), F(stats, st), F(parts, lp), 0, 0, nullptr, 0, 0,
+                                                nullptr, nullptr, nullptr);
+                    }));
+    part_reads.push_back(R(parts, lp));
+  }
+  const int64_t lp0 = L(parts, {0, ti, 0}), stride = rows * 2, ne = g->NE;
+  for (int64_t e = 0; e < g->NE; ++e) {
+    const int64_t ly = L(dy, {bi, si, e}), lx = L(x, {bi, si, e}), ld = L(dx, {bi, si, e});
+    int64_t r, cols;
+    x->mat(lx, &r, &cols);
+    std::vector<Access> acc = part_reads;
+    acc.insert(acc.end(), {R(dy, ly), R(x, lx), R(gam, e), R(stats, st), dx_acc ? RW(dx, ld) : W(dx, ld),
+                           RW(dgam, e), RW(dbet, e)});
+    TRY(ctx->submit("lnb_apply", acc, [=](hipStream_t s, void* ws) {
+      return tile_layernorm_bwd(s, TT_LN_APPLY, rows, cols, n_total, F(dy, ly), cols, F(x, lx), cols, F(gam, e),
+                                F(stats, st), F(parts, lp0), ne, stride, F(dx, ld), cols, dx_acc, F(dgam, e),
+                                F(dbet, e), ws);
+    }));
+  }
+  return TT_OK;
+}
+
+int colsum_task(tt_ctx* ctx, tt_tensor* x, int64_t lx, tt_tensor* out, int64_t lo, int beta) {
+  int64_t r, c;
+  x->mat(lx, &r, &c);
+  return ctx->submit("colsum", {R(x, lx), beta ? RW(out, lo) : W(out, lo)}, [=](hipStream_t s, void* ws) {
+    return tile_reduce_rows(s, r, c, F(x, lx), c, F(out, lo), beta, ws);
+  });
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ create
+
+extern "C" int tt_gpt2_destroy(tt_gpt2* g) {
+  if (!g) return fail(TT_ERR_ARG, "tt_gpt2_destroy: null");
+  int rc = g->ctx->dryrun ? TT_OK : g->ctx->wait_all();
+  for (auto it = g->owned.rbegin(); it != g->owned.rend(); ++it) tt_tensor_destroy(*it);
+  delete g;
+  return rc;
+}
+
+extern "C" int tt_gpt2_create(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_gpt2_tiles* tiles, int param_home,
+                              tt_gpt2** out) {
+  clear_error();
+  if (!ctx || !cfg || !tiles || !out) return fail(TT_ERR_ARG, "tt_gpt2_create: null argument");
+  const tt_gpt2_config& c = *cfg;
+  const tt_gpt2_tiles& t = *tiles;
+  if (c.n_layer < 0 || c.vocab < 1 || c.n_embd < 1 || c.n_head < 1 || c.n_inner < 1 || c.seq < 1 || c.batch < 1)
+    return fail(TT_ERR_ARG, "tt_gpt2_create: sizes must be positive");
+  if (t.batch < 1 || t.seq < 1 || t.embd < 1 || t.inner < 1 || t.head < 1 || t.vocab < 1)
+    return fail(TT_ERR_ARG, "tt_gpt2_create: tiles must be positive");
+  if (c.n_embd % c.n_head) return fail(TT_ERR_SHAPE, "tt_gpt2_create: n_embd %% n_head != 0");
+  if (c.seq % t.seq) return fail(TT_ERR_SHAPE, "tt_gpt2_create: seq tile must divide seq");
+  if (c.n_head % t.head) return fail(TT_ERR_SHAPE, "tt_gpt2_create: head tile must divide n_head");
+  if (c.batch % t.batch) return fail(TT_ERR_SHAPE, "tt_gpt2_create: batch tile must divide batch");
+  const int64_t hd = c.n_embd / c.n_head;
+  if (hd != 16 && hd != 32 && hd != 64 && hd != 128)
+    return fail(TT_ERR_UNSUPPORTED, "tt_gpt2_create: head dim %lld not in {16,32,64,128}", (long long)hd);
+  const int64_t et = std::min(t.embd, c.n_embd), vt = std::min(t.vocab, c.vocab);
+  if (et > 2048 || vt > 2048) return fail(TT_ERR_UNSUPPORTED, "tt_gpt2_create: embd and vocab tiles must be <= 2048");
+  if (param_home != TT_HOME_DEVICE && param_home != TT_HOME_PINNED_HOST)
+    return fail(TT_ERR_ARG, "tt_gpt2_create: bad param_home");
+
+  std::unique_ptr<tt_gpt2> g(new tt_gpt2());
+  g->ctx = ctx;
+  g->c = c;
+  g->t = t;
+  g->param_home = param_home;
+  g->nb = c.batch / t.batch;
+  g->ns = c.seq / t.seq;
+  g->ntok = g->nb * g->ns;
+  g->rows = (int64_t)t.batch * t.seq;
+  g->NE = ceil_div(c.n_embd, et);
+  g->NI = ceil_div(c.n_inner, std::min(t.inner, c.n_inner));
+  g->NH = c.n_head / t.head;
+  g->NV = ceil_div(c.vocab, vt);
+  g->hd = hd;
+  const int64_t B = c.batch, T = c.seq, d = c.n_embd, H = c.n_head, I = c.n_inner, V = c.vocab;
+  const int64_t bt = t.batch, sq = t.seq, it = t.inner, ht = t.head;
+  const int ph = param_home;
+  tt_gpt2* G = g.get();
+  auto fail_clean = [&](int rc) {
+    for (auto p = G->owned.rbegin(); p != G->owned.rend(); ++p) tt_tensor_destroy(*p);
+    G->owned.clear();
+    return rc;
+  };
+#define MK(...)                          \
+  do {                                   \
+    int rc_ = mk(G, __VA_ARGS__);        \
+    if (rc_) return fail_clean(rc_);     \
+  } while (0)
+  // parameters, gradients and moments in param_specs order
+  struct Spec {
+    const char* name;
+    std::vector<int64_t> shape, tile;
+    int split;
+  };
+  std::vector<Spec> specs;
+  specs.push_back({"wte", {V, d}, {vt, et}, 1});
+  specs.push_back({"wpe", {T, d}, {sq, et}, 1});
+  for (int l = 0; l < c.n_layer; ++l) {
+    specs.push_back({"ln1_g", {d}, {et}, 0});
+    specs.push_back({"ln1_b", {d}, {et}, 0});
+    specs.push_back({"w_qkv", {d, 3, H, hd}, {et, 1, ht, hd}, 1});
+    specs.push_back({"b_qkv", {3, H, hd}, {1, ht, hd}, 0});
+    specs.push_back({"w_o", {H, hd, d}, {ht, hd, et}, 2});
+    specs.push_back({"b_o", {d}, {et}, 0});
+    specs.push_back({"ln2_g", {d}, {et}, 0});
+    specs.push_back({"ln2_b", {d}, {et}, 0});
+    specs.push_back({"w_fc", {d, I}, {et, it}, 1});
+    specs.push_back({"b_fc", {I}, {it}, 0});
+    specs.push_back({"w_p", {I, d}, {it, et}, 1});
+    specs.push_back({"b_p", {d}, {et}, 0});
+  }
+  specs.push_back({"lnf_g", {d}, {et}, 0});
+  specs.push_back({"lnf_b", {d}, {et}, 0});
+  for (auto& s : specs) {
+    tt_tensor* ts[4];
+    const char* suffix[4] = {"", ".grad", ".m", ".v"};
+    for (int j = 0; j < 4; ++j) {
+      std::string nm = std::string(s.name) + suffix[j];
+      int rc = tensor_create(ctx, (int)s.shape.size(), s.shape.data(), s.tile.data(), TT_F32, ph, s.split,
+                             nm.c_str(), &ts[j]);
+      if (rc) return fail_clean(rc);
+      G->owned.push_back(ts[j]);
+    }
+    G->P.push_back(ts[0]);
+    G->G.push_back(ts[1]);
+    G->M.push_back(ts[2]);
+    G->Vv.push_back(ts[3]);
+  }
+  // tokens and per-token-tile index tensors
+  MK(&G->tokens, "tokens", {B, T + 1}, {B, T + 1}, 1, TT_I32);
+  MK(&G->ids, "ids", {B, T}, {bt, sq}, 2, TT_I32);
+  MK(&G->labels, "labels", {B, T}, {bt, sq}, 2, TT_I32);
+  MK(&G->sorted, "sorted_ids", {B, T}, {bt, sq}, 2, TT_I32);
+  MK(&G->perm, "perm", {B, T}, {bt, sq}, 2, TT_I32);
+  // activations
+  G->blk.resize(c.n_layer);
+  MK(&(G->blk.empty() ? G->h_last : G->blk[0].h_in), "h0", {B, T, d}, {bt, sq, et}, 2);
+  for (int l = 0; l < c.n_layer; ++l) {
+    BlockT& b = G->blk[l];
+    MK(&b.ln1, "ln1_stats", {B, T, 2}, {bt, sq, 2}, 2);
+    MK(&b.n1, "n1", {B, T, d}, {bt, sq, et}, 2);
+    MK(&b.q, "q", {B, T, H, hd}, {bt, sq, ht, hd}, 2);
+    MK(&b.k, "k", {B, T, H, hd}, {bt, sq, ht, hd}, 2);
+    MK(&b.v, "v", {B, T, H, hd}, {bt, sq, ht, hd}, 2);
+    MK(&b.o, "o", {B, T, H, hd}, {bt, sq, ht, hd}, 2);
+    MK(&b.lse, "attn_lse", {B / bt, T / sq, H / ht, bt * sq * ht}, {1, 1, 1, bt * sq * ht}, 3);
+    MK(&b.h_mid, "h_mid", {B, T, d}, {bt, sq, et}, 2);
+    MK(&b.ln2, "ln2_stats", {B, T, 2}, {bt, sq, 2}, 2);
+    MK(&b.n2, "n2", {B, T, d}, {bt, sq, et}, 2);
+    MK(&b.u, "u", {B, T, I}, {bt, sq, it}, 2);
+    MK(&b.g, "gelu", {B, T, I}, {bt, sq, it}, 2);
+    tt_tensor** next = (l + 1 < c.n_layer) ? &G->blk[l + 1].h_in : &G->h_last;
+    MK(next, "h", {B, T, d}, {bt, sq, et}, 2);
+  }
+  MK(&G->lnf, "lnf_stats", {B, T, 2}, {bt, sq, 2}, 2);
+  MK(&G->nf, "nf", {B, T, d}, {bt, sq, et}, 2);
+  MK(&G->z, "logits", {B, T, V}, {bt, sq, vt}, 2);
+  MK(&G->ml, "attn_ml", {B / bt, T / sq, H / ht, bt * sq * ht * 2}, {1, 1, 1, bt * sq * ht * 2}, 3);
+  MK(&G->ln_parts, "ln_parts", {G->NE, G->ntok, G->rows * 3}, {1, 1, G->rows * 3}, 2);
+  MK(&G->lnb_parts, "lnb_parts", {G->NE, G->ntok, G->rows * 2}, {1, 1, G->rows * 2}, 2);
+  MK(&G->ce_parts, "ce_parts", {G->NV, G->ntok, G->rows * 3}, {1, 1, G->rows * 3}, 2);
+  MK(&G->ce_lse, "ce_lse", {G->ntok, G->rows}, {1, G->rows}, 1);
+  MK(&G->row_loss, "row_loss", {G->ntok, G->rows}, {1, G->rows}, 1);
+  MK(&G->loss, "loss", {1}, {1}, 0);
+  MK(&G->dnf, "dnf", {B, T, d}, {bt, sq, et}, 2);
+  MK(&G->dh, "dh", {B, T, d}, {bt, sq, et}, 2);
+  MK(&G->dgu, "dgu", {B, T, I}, {bt, sq, it}, 2);
+  MK(&G->dn, "dn", {B, T, d}, {bt, sq, et}, 2);
+  MK(&G->dO, "do", {B, T, H, hd}, {bt, sq, ht, hd}, 2);
+  MK(&G->dq, "dq", {B, T, H, hd}, {bt, sq, ht, hd}, 2);
+  MK(&G->dk, "dk", {B, T, H, hd}, {bt, sq, ht, hd}, 2);
+  MK(&G->dv, "dv", {B, T, H, hd}, {bt, sq, ht, hd}, 2);
+  MK(&G->Dv, "attn_D", {B / bt, T / sq, H / ht, bt * sq * ht}, {1, 1, 1, bt * sq * ht}, 3);
+  MK(&G->step, "adam_step", {1}, {1}, 0, TT_I32);
+  MK(&G->bc, "adam_bias_corr", {2}, {2}, 0);
+#undef MK
+  // per-stream workspace for the deterministic column sums
+  const int64_t widest = std::max<int64_t>({et, std::min<int64_t>(it, I), ht * hd});
+  size_t ws = std::max(tile_layernorm_bwd_workspace(G->rows, et), tile_reduce_rows_workspace(G->rows, widest));
+  if (int rc = ctx->ensure_workspace(ws)) return fail_clean(rc);
+  // zero gradients' home state, moments and the step counter
+  if (!ctx->dryrun) {
+    for (size_t i = 0; i < G->P.size(); ++i)
+      for (tt_tensor* x : {G->M[i], G->Vv[i]})
+        if (x->home == TT_HOME_DEVICE) {
+          hipError_t e = hipMemset(x->base, 0, x->bytes());
+          if (e != hipSuccess) return fail_clean(fail(TT_ERR_HIP, "hipMemset: %s", hipGetErrorString(e)));
+        }
+    if (hipMemset(G->step->base, 0, 4) != hipSuccess) return fail_clean(fail(TT_ERR_HIP, "hipMemset(step)"));
+  }
+  *out = g.release();
+  return TT_OK;
+}
+
+extern "C" int tt_gpt2_num_params(tt_gpt2* g, int* n) {
+  if (!g || !n) return fail(TT_ERR_ARG, "tt_gpt2_num_params: null");
+  *n = (int)g->P.size();
+  return TT_OK;
+}
+
+extern "C" int tt_gpt2_param(tt_gpt2* g, int index, tt_tensor** p, tt_tensor** gr, tt_tensor** m, tt_tensor** v) {
+  if (!g) return fail(TT_ERR_ARG, "tt_gpt2_param: null");
+  if (index < 0 || index >= (int)g->P.size()) return fail(TT_ERR_ARG, "tt_gpt2_param: index %d out of range", index);
+  if (p) *p = g->P[index];
+  if (gr) *gr = g->G[index];
+  if (m) *m = g->M[index];
+  if (v) *v = g->Vv[index];
+  return TT_OK;
+}
+
+extern "C" int tt_gpt2_task_count(tt_gpt2* g, int64_t* n) {
+  if (!g || !n) return fail(TT_ERR_ARG, "tt_gpt2_task_count: null");
+  *n = g->last_tasks;
+  return TT_OK;
+}
+
+extern "C" int tt_gpt2_loss(tt_gpt2* g, float* loss) {
+  clear_error();
+  if (!g || !loss) return fail(TT_ERR_ARG, "tt_gpt2_loss: null");
+  if (g->ctx->dryrun) {
+    *loss = NAN;
+    return g->ctx->wait_all();
+  }
+  TRY(g->ctx->wait_all());
+  TT_HIP_TRY(hipMemcpy(loss, g->loss->base, 4, hipMemcpyDeviceToHost));
+  return TT_OK;
+}
+
+// -------------------------------------------------------------------- step
+
+extern "C" int tt_gpt2_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams* hp, int do_update) {
+  clear_error();
+  if (!g || !hp) return fail(TT_ERR_ARG, "tt_gpt2_step: null argument");
+  tt_ctx* ctx = g->ctx;
+  if (!tokens && !ctx->dryrun) return fail(TT_ERR_ARG, "tt_gpt2_step: null tokens");
+  const int64_t t0 = ctx->next_id;
+  const tt_gpt2_config& c = g->c;
+  const int64_t B = c.batch, T = c.seq, hd = g->hd, V = c.vocab;
+  const int64_t bt = g->t.batch, sq = g->t.seq, ht = g->t.head, rows = g->rows;
+  const int64_t NE = g->NE, NI = g->NI, NH = g->NH, NV = g->NV;
+  const float scale = 1.f / std::sqrt((float)hd);
+  const float inv_n = 1.f / (float)(B * T);
+
+  // ---- inputs: copy the token windows, split into ids/labels, index for the embedding backward
+  {
+    tt_tensor* tok = g->tokens;
+    const size_t bytes = (size_t)B * (T + 1) * 4;
+    TRY(ctx->submit("tokens", {W(tok, 0)}, [tok, tokens, bytes](hipStream_t s, void*) {
+      TT_HIP_TRY(hipMemcpyAsync(tok->dev(0), tokens, bytes, hipMemcpyDeviceToDevice, s));
+      return TT_OK;
+    }));
+  }
+  for (int64_t bi = 0; bi < g->nb; ++bi)
+    for (int64_t si = 0; si < g->ns; ++si) {
+      tt_tensor *tok = g->tokens, *ids = g->ids, *lab = g->labels, *so = g->sorted, *pe = g->perm;
+      const int64_t li = L(ids, {bi, si});
+      // split: rows of this tile start at window bi*bt, position si*sq; one launch per batch row
+      TRY(ctx->submit("split", {R(tok, 0), W(ids, li), W(lab, li)}, [=](hipStream_t s, void*) {
+        for (int64_t b = 0; b < bt; ++b) {
+          const int32_t* src = (const int32_t*)tok->dev(0) + (bi * bt + b) * (T + 1) + si * sq;
+          int rc = tile_split_tokens(s, 1, sq, src, (int32_t*)ids->dev(li) + b * sq, (int32_t*)lab->dev(li) + b * sq);
+          if (rc) return rc;
+        }
+        return TT_OK;
+      }));
+      TRY(ctx->submit("emb_index", {R(ids, li), W(so, li), W(pe, li)}, [=](hipStream_t s, void*) {
+        return tile_embedding_index(s, rows, I32(ids, li), (int32_t*)so->dev(li), (int32_t*)pe->dev(li));
+      }));
+    }
+
+  // ---- embedding forward
+  tt_tensor* h0 = c.n_layer ? g->blk[0].h_in : g->h_last;
+  for (int64_t bi = 0; bi < g->nb; ++bi)
+    for (int64_t si = 0; si < g->ns; ++si)
+      for (int64_t e = 0; e < NE; ++e) {
+        tt_tensor *wte = g->P[0], *wpe = g->P[1], *ids = g->ids;
+        const int64_t li = L(ids, {bi, si}), lo = L(h0, {bi, si, e}), lp = L(wpe, {si, e});
+        int64_t r, cols;
+        h0->mat(lo, &r, &cols);
+        std::vector<Access> acc = {R(ids, li), R(wpe, lp), W(h0, lo)};
+        for (int64_t v = 0; v < NV; ++v) acc.push_back(R(wte, L(wte, {v, e})));
+        const int64_t lw = L(wte, {0, e});
+        TRY(ctx->submit("emb_fwd", acc, [=](hipStream_t s, void*) {
+          return tile_embedding_fwd(s, rows, cols, I32(ids, li), V, F(wte, lw), cols, F(wpe, lp), cols, sq, 0,
+                                    F(h0, lo), cols);
+        }));
+      }
+
+  // ---- blocks forward
+  for (int l = 0; l < c.n_layer; ++l) {
+    BlockT& b = g->blk[l];
+    tt_tensor* hout = (l + 1 < c.n_layer) ? g->blk[l + 1].h_in : g->h_last;
+    tt_tensor *ln1g = g->P[g->pidx(l, LN1G)], *ln1b = g->P[g->pidx(l, LN1B)];
+    tt_tensor *wqkv = g->P[g->pidx(l, WQKV)], *bqkv = g->P[g->pidx(l, BQKV)];
+    tt_tensor *wo = g->P[g->pidx(l, WO)], *bo = g->P[g->pidx(l, BO)];
+    tt_tensor *ln2g = g->P[g->pidx(l, LN2G)], *ln2b = g->P[g->pidx(l, LN2B)];
+    tt_tensor *wfc = g->P[g->pidx(l, WFC)], *bfc = g->P[g->pidx(l, BFC)];
+    tt_tensor *wp = g->P[g->pidx(l, WP)], *bp = g->P[g->pidx(l, BP)];
+    tt_tensor* qkv[3] = {b.q, b.k, b.v};
+    for (int64_t bi = 0; bi < g->nb; ++bi)
+      for (int64_t si = 0; si < g->ns; ++si) {
+        const int64_t ti = bi + g->nb * si;
+        TRY(ln_forward(g, b.h_in, ln1g, ln1b, b.ln1, b.n1, ti, bi, si));
+        for (int cq = 0; cq < 3; ++cq)
+          for (int64_t hj = 0; hj < NH; ++hj)
+            for (int64_t ek = 0; ek < NE; ++ek) {
+              Gemm q;
+              q.A = {b.n1, L(b.n1, {bi, si, ek})};
+              q.B = {wqkv, L(wqkv, {ek, cq, hj, 0})};
+              q.C = {qkv[cq], L(qkv[cq], {bi, si, hj, 0})};
+              q.beta = ek > 0 ? 1.f : 0.f;
+              if (ek == NE - 1) {
+                q.epi = TT_EPI_BIAS;
+                q.bias = {bqkv, L(bqkv, {cq, hj, 0})};
+              }
+              TRY(submit_gemm(ctx, "qkv", q));
+            }
+      }
+    // attention: (query tile, key tile) pairs, key tiles in order
+    for (int64_t bi = 0; bi < g->nb; ++bi)
+      for (int64_t hj = 0; hj < NH; ++hj)
+        for (int64_t qi = 0; qi < g->ns; ++qi)
+          for (int64_t ki = 0; ki <= qi; ++ki) {
+            tt_tensor *Q = b.q, *K = b.k, *Vt = b.v, *O = b.o, *ml = g->ml, *lse = b.lse;
+            const int64_t lq = L(Q, {bi, qi, hj, 0}), lk = L(K, {bi, ki, hj, 0});
+            const int64_t ls = L(lse, {bi, qi, hj, 0}), lm = L(ml, {bi, qi, hj, 0});
+            const int first = ki == 0, last = ki == qi;
+            std::vector<Access> acc = {R(Q, lq), R(K, lk), R(Vt, lk), first ? W(O, lq) : RW(O, lq)};
+            if (!(first && last)) acc.push_back(first ? W(ml, lm) : RW(ml, lm));
+            if (last) acc.push_back(W(lse, ls));
+            TRY(ctx->submit("attn_fwd", acc, [=](hipStream_t s, void*) {
+              return tile_attention_fwd(s, bt, ht, sq, sq, hd, qi * sq, ki * sq, F(Q, lq), F(K, lk), F(Vt, lk),
+                                        F(O, lq), F(ml, lm), F(lse, ls), first, last, scale);
+            }));
+          }
+    for (int64_t bi = 0; bi < g->nb; ++bi)
+      for (int64_t si = 0; si < g->ns; ++si) {
+        const int64_t ti = bi + g->nb * si;
+        // h_mid = h_in + O W_o + b_o
+        for (int64_t ej = 0; ej < NE; ++ej)
+          for (int64_t hk = 0; hk < NH; ++hk) {
+            Gemm q;
+            q.A = {b.o, L(b.o, {bi, si, hk, 0})};
+            q.B = {wo, L(wo, {hk, 0, ej})};
+            q.C = {b.h_mid, L(b.h_mid, {bi, si, ej})};
+            q.beta = hk > 0 ? 1.f : 0.f;
+            if (hk == 0) {
+              q.epi |= TT_EPI_RES;
+              q.res = {b.h_in, L(b.h_in, {bi, si, ej})};
+            }
+            if (hk == NH - 1) {
+              q.epi |= TT_EPI_BIAS;
+              q.bias = {bo, ej};
+            }
+            TRY(submit_gemm(ctx, "attn_proj", q));
+          }
+        TRY(ln_forward(g, b.h_mid, ln2g, ln2b, b.ln2, b.n2, ti, bi, si));
+        // g = gelu(n2 W_fc + b_fc), pre-activation kept in u
+        for (int64_t ij = 0; ij < NI; ++ij)
+          for (int64_t ek = 0; ek < NE; ++ek) {
+            Gemm q;
+            q.A = {b.n2, L(b.n2, {bi, si, ek})};
+            q.B = {wfc, L(wfc, {ek, ij})};
+            q.beta = ek > 0 ? 1.f : 0.f;
+            if (ek == NE - 1) {
+              q.C = {b.g, L(b.g, {bi, si, ij})};
+              q.epi = TT_EPI_GELU | TT_EPI_BIAS;
+              q.bias = {bfc, ij};
+              q.aux = {b.u, L(b.u, {bi, si, ij})};
+            } else {
+              q.C = {b.u, L(b.u, {bi, si, ij})};
+            }
+            TRY(submit_gemm(ctx, "fc", q));
+          }
+        // h_out = h_mid + g W_p + b_p
+        for (int64_t ej = 0; ej < NE; ++ej)
+          for (int64_t ik = 0; ik < NI; ++ik) {
+            Gemm q;
+            q.A = {b.g, L(b.g, {bi, si, ik})};
+            q.B = {wp, L(wp, {ik, ej})};
+            q.C = {hout, L(hout, {bi, si, ej})};
+            q.beta = ik > 0 ? 1.f : 0.f;
+            if (ik == 0) {
+              q.epi |= TT_EPI_RES;
+              q.res = {b.h_mid, L(b.h_mid, {bi, si, ej})};
+            }
+            if (ik == NI - 1) {
+              q.epi |= TT_EPI_BIAS;
+              q.bias = {bp, ej};
+            }
+            TRY(submit_gemm(ctx, "mlp_proj", q));
+          }
+      }
+  }
+
+  // ---- final LayerNorm, tied head, cross-entropy
+  tt_tensor *lnfg = g->P[g->lnf_g()], *lnfb = g->P[g->lnf_g() + 1], *wte = g->P[0];
+  for (int64_t bi = 0; bi < g->nb; ++bi)
+    for (int64_t si = 0; si < g->ns; ++si) {
+      const int64_t ti = bi + g->nb * si;
+      TRY(ln_forward(g, g->h_last, lnfg, lnfb, g->lnf, g->nf, ti, bi, si));
+      for (int64_t vj = 0; vj < NV; ++vj) {
+        for (int64_t ek = 0; ek < NE; ++ek) {
+          Gemm q;
+          q.tb = 1;
+          q.A = {g->nf, L(g->nf, {bi, si, ek})};
+          q.B = {wte, L(wte, {vj, ek})};
+          q.C = {g->z, L(g->z, {bi, si, vj})};
+          q.beta = ek > 0 ? 1.f : 0.f;
+          TRY(submit_gemm(ctx, "head", q));
+        }
+        tt_tensor *z = g->z, *lab = g->labels, *parts = g->ce_parts;
+        const int64_t lz = L(z, {bi, si, vj}), ll = L(lab, {bi, si}), lp = L(parts, {vj, ti, 0});
+        int64_t r, cols;
+        z->mat(lz, &r, &cols);
+        const int64_t voff = vj * std::min<int64_t>(g->t.vocab, V);
+        TRY(ctx->submit("ce_stats", {R(z, lz), R(lab, ll), W(parts, lp)}, [=](hipStream_t s, void*) {
+          return tile_softmax(s, TT_SM_STATS, rows, cols, 0, voff, 1.f, 0, F(z, lz), cols, I32(lab, ll), F(parts, lp),
+                              0, 0, nullptr, nullptr, nullptr, 0, 1.f);
+        }));
+      }
+      {
+        tt_tensor *parts = g->ce_parts, *lse = g->ce_lse, *rl = g->row_loss;
+        std::vector<Access> acc;
+        for (int64_t vj = 0; vj < NV; ++vj) acc.push_back(R(parts, L(parts, {vj, ti, 0})));
+        acc.push_back(W(lse, ti));
+        acc.push_back(W(rl, ti));
+        const int64_t lp0 = L(parts, {0, ti, 0});
+        TRY(ctx->submit("ce_merge", acc, [=](hipStream_t s, void*) {
+          return tile_softmax(s, TT_SM_MERGE, rows, 0, 0, 0, 1.f, 0, nullptr, 0, nullptr, F(parts, lp0), NV, rows * 3,
+                              F(lse, ti), F(rl, ti), nullptr, 0, 1.f);
+        }));
+        tt_tensor* loss = g->loss;
+        const int accumulate = ti > 0;
+        TRY(ctx->submit("ce_loss", {R(rl, ti), accumulate ? RW(loss, 0) : W(loss, 0)}, [=](hipStream_t s, void*) {
+          return tile_xentropy(s, TT_XE_LOSS, rows, 0, 0, nullptr, nullptr, 0, nullptr, F(rl, ti), F(loss, 0),
+                               accumulate, inv_n);
+        }));
+        for (int64_t vj = 0; vj < NV; ++vj) {
+          tt_tensor *z = g->z, *lab = g->labels;
+          const int64_t lz = L(z, {bi, si, vj}), ll = L(lab, {bi, si});
+          int64_t r, cols;
+          z->mat(lz, &r, &cols);
+          const int64_t voff = vj * std::min<int64_t>(g->t.vocab, V);
+          TRY(ctx->submit("ce_grad", {RW(z, lz), R(lab, ll), R(lse, ti)}, [=](hipStream_t s, void*) {
+            return tile_xentropy(s, TT_XE_GRAD, rows, cols, voff, I32(lab, ll), F(z, lz), cols, F(lse, ti), nullptr,
+                                 nullptr, 0, inv_n);
+          }));
+        }
+      }
+    }
+
+  // ---- backward: head (dz is in place of the logits)
+  tt_tensor* gwte = g->G[0];
+  for (int64_t vj = 0; vj < NV; ++vj)
+    for (int64_t ek = 0; ek < NE; ++ek) {
+      // dwte (head part) = sum over token tiles of dz^T nf
+      for (int64_t si = 0; si < g->ns; ++si)
+        for (int64_t bi = 0; bi < g->nb; ++bi) {
+          const int64_t ti = bi + g->nb * si;
+          Gemm q;
+          q.ta = 1;
+          q.A = {g->z, L(g->z, {bi, si, vj})};
+          q.B = {g->nf, L(g->nf, {bi, si, ek})};
+          q.C = {gwte, L(gwte, {vj, ek})};
+          q.beta = ti > 0 ? 1.f : 0.f;
+          TRY(submit_gemm(ctx, "head_dw", q));
+        }
+      // dnf = sum over vocab tiles of dz wte
+      for (int64_t si = 0; si < g->ns; ++si)
+        for (int64_t bi = 0; bi < g->nb; ++bi) {
+          Gemm q;
+          q.A = {g->z, L(g->z, {bi, si, vj})};
+          q.B = {wte, L(wte, {vj, ek})};
+          q.C = {g->dnf, L(g->dnf, {bi, si, ek})};
+          q.beta = vj > 0 ? 1.f : 0.f;
+          TRY(submit_gemm(ctx, "head_dx", q));
+        }
+    }
+  // zero the LayerNorm and position gradients, which accumulate
+  for (int l = 0; l < c.n_layer; ++l)
+    for (int w : {LN1G, LN1B, LN2G, LN2B})
+      for (int64_t e = 0; e < NE; ++e) TRY(fill_task(ctx, g->G[g->pidx(l, w)], e, 0.f));
+  for (int64_t e = 0; e < NE; ++e) {
+    TRY(fill_task(ctx, g->G[g->lnf_g()], e, 0.f));
+    TRY(fill_task(ctx, g->G[g->lnf_g() + 1], e, 0.f));
+  }
+  for (int64_t lt = 0; lt < g->G[1]->ntiles; ++lt) TRY(fill_task(ctx, g->G[1], lt, 0.f));
+  for (int64_t bi = 0; bi < g->nb; ++bi)
+    for (int64_t si = 0; si < g->ns; ++si)
+      TRY(ln_backward(g, g->dnf, g->h_last, lnfg, g->lnf, g->dh, 0, g->G[g->lnf_g()], g->G[g->lnf_g() + 1],
+                      bi + g->nb * si, bi, si));
+
+  // ---- blocks backward
+  for (int l = c.n_layer - 1; l >= 0; --l) {
+    BlockT& b = g->blk[l];
+    tt_tensor *ln1g = g->P[g->pidx(l, LN1G)], *wqkv = g->P[g->pidx(l, WQKV)], *wo = g->P[g->pidx(l, WO)];
+    tt_tensor *ln2g = g->P[g->pidx(l, LN2G)], *wfc = g->P[g->pidx(l, WFC)], *wp = g->P[g->pidx(l, WP)];
+    tt_tensor *gwqkv = g->G[g->pidx(l, WQKV)], *gbqkv = g->G[g->pidx(l, BQKV)];
+    tt_tensor *gwo = g->G[g->pidx(l, WO)], *gbo = g->G[g->pidx(l, BO)];
+    tt_tensor *gwfc = g->G[g->pidx(l, WFC)], *gbfc = g->G[g->pidx(l, BFC)];
+    tt_tensor *gwp = g->G[g->pidx(l, WP)], *gbp = g->G[g->pidx(l, BP)];
+    tt_tensor* dqkv[3] = {g->dq, g->dk, g->dv};
+    tt_tensor* qkv[3] = {b.q, b.k, b.v};
+    // MLP: h_out = h_mid + gelu(u) W_p + b_p
+    for (int64_t si = 0; si < g->ns; ++si)
+      for (int64_t bi = 0; bi < g->nb; ++bi) {
+        const int64_t ti = bi + g->nb * si;
+        for (int64_t ej = 0; ej < NE; ++ej) {
+          for (int64_t ik = 0; ik < NI; ++ik) {
+            Gemm q;
+            q.ta = 1;
+            q.A = {b.g, L(b.g, {bi, si, ik})};
+            q.B = {g->dh, L(g->dh, {bi, si, ej})};
+            q.C = {gwp, L(gwp, {ik, ej})};
+            q.beta = ti > 0 ? 1.f : 0.f;
+            TRY(submit_gemm(ctx, "mlp_proj_dw", q));
+          }
+          TRY(colsum_task(ctx, g->dh, L(g->dh, {bi, si, ej}), gbp, ej, ti > 0));
+        }
+        for (int64_t ik = 0; ik < NI; ++ik)
+          for (int64_t ej = 0; ej < NE; ++ej) {
+            Gemm q;
+            q.tb = 1;
+            q.A = {g->dh, L(g->dh, {bi, si, ej})};
+            q.B = {wp, L(wp, {ik, ej})};
+            q.C = {g->dgu, L(g->dgu, {bi, si, ik})};
+            q.beta = ej > 0 ? 1.f : 0.f;
+            if (ej == NE - 1) {
+              q.epi = TT_EPI_GELU_BWD;
+              q.aux = {b.u, L(b.u, {bi, si, ik})};
+            }
+            TRY(submit_gemm(ctx, "mlp_proj_dx", q));
+          }
+        for (int64_t ik = 0; ik < NI; ++ik) {
+          for (int64_t ek = 0; ek < NE; ++ek) {
+            Gemm q;
+            q.ta = 1;
+            q.A = {b.n2, L(b.n2, {bi, si, ek})};
+            q.B = {g->dgu, L(g->dgu, {bi, si, ik})};
+            q.C = {gwfc, L(gwfc, {ek, ik})};
+            q.beta = ti > 0 ? 1.f : 0.f;
+            TRY(submit_gemm(ctx, "fc_dw", q));
+          }
+          TRY(colsum_task(ctx, g->dgu, L(g->dgu, {bi, si, ik}), gbfc, ik, ti > 0));
+        }
+        for (int64_t ek = 0; ek < NE; ++ek)
+          for (int64_t ik = 0; ik < NI; ++ik) {
+            Gemm q;
+            q.tb = 1;
+            q.A = {g->dgu, L(g->dgu, {bi, si, ik})};
+            q.B = {wfc, L(wfc, {ek, ik})};
+            q.C = {g->dn, L(g->dn, {bi, si, ek})};
+            q.beta = ik > 0 ? 1.f : 0.f;
+            TRY(submit_gemm(ctx, "fc_dx", q));
+          }
+        TRY(ln_backward(g, g->dn, b.h_mid, ln2g, b.ln2, g->dh, 1, g->G[g->pidx(l, LN2G)], g->G[g->pidx(l, LN2B)], ti,
+                        bi, si));
+        // attention projection: h_mid = h_in + O W_o + b_o
+        for (int64_t ej = 0; ej < NE; ++ej) {
+          for (int64_t hk = 0; hk < NH; ++hk) {
+            Gemm q;
+            q.ta = 1;
+            q.A = {b.o, L(b.o, {bi, si, hk, 0})};
+            q.B = {g->dh, L(g->dh, {bi, si, ej})};
+            q.C = {gwo, L(gwo, {hk, 0, ej})};
+            q.beta = ti > 0 ? 1.f : 0.f;
+            TRY(submit_gemm(ctx, "attn_proj_dw", q));
+          }
+          TRY(colsum_task(ctx, g->dh, L(g->dh, {bi, si, ej}), gbo, ej, ti > 0));
+        }
+        for (int64_t hk = 0; hk < NH; ++hk)
+          for (int64_t ej = 0; ej < NE; ++ej) {
+            Gemm q;
+            q.tb = 1;
+            q.A = {g->dh, L(g->dh, {bi, si, ej})};
+            q.B = {wo, L(wo, {hk, 0, ej})};
+            q.C = {g->dO, L(g->dO, {bi, si, hk, 0})};
+            q.beta = ej > 0 ? 1.f : 0.f;
+            TRY(submit_gemm(ctx, "attn_proj_dx", q));
+          }
+      }
+    // attention backward
+    for (int64_t bi = 0; bi < g->nb; ++bi)
+      for (int64_t hj = 0; hj < NH; ++hj) {
+        for (int64_t qi = 0; qi < g->ns; ++qi) {
+          tt_tensor *O = b.o, *dO = g->dO, *Dv = g->Dv;
+          const int64_t lq = L(O, {bi, qi, hj, 0}), ld = L(Dv, {bi, qi, hj, 0});
+          TRY(ctx->submit("attn_prep", {R(O, lq), R(dO, lq), W(Dv, ld)}, [=](hipStream_t s, void*) {
+            return tile_attention_bwd(s, TT_ATT_PREP, bt, ht, sq, sq, hd, 0, 0, nullptr, nullptr, nullptr, F(O, lq),
+                                      F(dO, lq), nullptr, F(Dv, ld), nullptr, nullptr, nullptr, 0, 0, scale);
+          }));
+        }
+        for (int64_t qi = 0; qi < g->ns; ++qi)
+          for (int64_t ki = 0; ki <= qi; ++ki) {
+            tt_tensor *Q = b.q, *K = b.k, *Vt = b.v, *dO = g->dO, *lse = b.lse, *Dv = g->Dv;
+            tt_tensor *dq = g->dq, *dk = g->dk, *dv = g->dv;
+            const int64_t lq = L(Q, {bi, qi, hj, 0}), lk = L(K, {bi, ki, hj, 0});
+            const int64_t ls = L(lse, {bi, qi, hj, 0});
+            const int acc_q = ki > 0, acc_kv = qi > ki;
+            TRY(ctx->submit("attn_bwd",
+                            {R(Q, lq), R(K, lk), R(Vt, lk), R(dO, lq), R(lse, ls), R(Dv, ls),
+                             acc_q ? RW(dq, lq) : W(dq, lq), acc_kv ? RW(dk, lk) : W(dk, lk),
+                             acc_kv ? RW(dv, lk) : W(dv, lk)},
+                            [=](hipStream_t s, void*) {
+                              return tile_attention_bwd(s, TT_ATT_GRAD, bt, ht, sq, sq, hd, qi * sq, ki * sq, F(Q, lq),
+                                                        F(K, lk), F(Vt, lk), nullptr, F(dO, lq), F(lse, ls),
+                                                        F(Dv, ls), F(dq, lq), F(dk, lk), F(dv, lk), acc_q, acc_kv,
+                                                        scale);
+                            }));
+          }
+      }
+    // QKV projection backward
+    for (int64_t si = 0; si < g->ns; ++si)
+      for (int64_t bi = 0; bi < g->nb; ++bi) {
+        const int64_t ti = bi + g->nb * si;
+        for (int cq = 0; cq < 3; ++cq)
+          for (int64_t hj = 0; hj < NH; ++hj) {
+            for (int64_t ek = 0; ek < NE; ++ek) {
+              Gemm q;
+              q.ta = 1;
+              q.A = {b.n1, L(b.n1, {bi, si, ek})};
+              q.B = {dqkv[cq], L(dqkv[cq], {bi, si, hj, 0})};
+              q.C = {gwqkv, L(gwqkv, {ek, cq, hj, 0})};
+              q.beta = ti > 0 ? 1.f : 0.f;
+              TRY(submit_gemm(ctx, "qkv_dw", q));
+            }
+            TRY(colsum_task(ctx, dqkv[cq], L(dqkv[cq], {bi, si, hj, 0}), gbqkv, L(gbqkv, {cq, hj, 0}), ti > 0));
+          }
+        for (int64_t ek = 0; ek < NE; ++ek) {
+          bool firstk = true;
+          for (int cq = 0; cq < 3; ++cq)
+            for (int64_t hj = 0; hj < NH; ++hj) {
+              Gemm q;
+              q.tb = 1;
+              q.A = {dqkv[cq], L(dqkv[cq], {bi, si, hj, 0})};
+              q.B = {wqkv, L(wqkv, {ek, cq, hj, 0})};
+              q.C = {g->dn, L(g->dn, {bi, si, ek})};
+              q.beta = firstk ? 0.f : 1.f;
+              firstk = false;
+              TRY(submit_gemm(ctx, "qkv_dx", q));
+            }
+        }
+        TRY(ln_backward(g, g->dn, b.h_in, ln1g, b.ln1, g->dh, 1, g->G[g->pidx(l, LN1G)], g->G[g->pidx(l, LN1B)], ti,
+                        bi, si));
+      }
+    (void)qkv;
+  }
+
+  // ---- embedding backward: token rows into dwte (after its head part), positions into dwpe
+  for (int64_t vj = 0; vj < NV; ++vj)
+    for (int64_t ek = 0; ek < NE; ++ek)
+      for (int64_t si = 0; si < g->ns; ++si)
+        for (int64_t bi = 0; bi < g->nb; ++bi) {
+          tt_tensor *dh = g->dh, *so = g->sorted, *pe = g->perm;
+          const int64_t ld = L(dh, {bi, si, ek}), li = L(so, {bi, si}), lw = L(gwte, {vj, ek});
+          int64_t r, cols, vr, vc;
+          dh->mat(ld, &r, &cols);
+          gwte->mat(lw, &vr, &vc);
+          const int64_t voff = vj * std::min<int64_t>(g->t.vocab, V);
+          TRY(ctx->submit("emb_dw", {R(dh, ld), R(so, li), R(pe, li), RW(gwte, lw)}, [=](hipStream_t s, void*) {
+            return tile_embedding_bwd(s, TT_EMB_TOKEN, rows, cols, I32(so, li), I32(pe, li), voff, vr, sq, F(dh, ld),
+                                      cols, F(gwte, lw), cols);
+          }));
+        }
+  for (int64_t si = 0; si < g->ns; ++si)
+    for (int64_t ek = 0; ek < NE; ++ek)
+      for (int64_t bi = 0; bi < g->nb; ++bi) {
+        tt_tensor *dh = g->dh, *gwpe = g->G[1];
+        const int64_t ld = L(dh, {bi, si, ek}), lw = L(gwpe, {si, ek});
+        int64_t r, cols;
+        dh->mat(ld, &r, &cols);
+        TRY(ctx->submit("emb_dpos", {R(dh, ld), RW(gwpe, lw)}, [=](hipStream_t s, void*) {
+          return tile_embedding_bwd(s, TT_EMB_POS, rows, cols, nullptr, nullptr, 0, 0, sq, F(dh, ld), cols,
+                                    F(gwpe, lw), cols);
+        }));
+      }
+
+  // ---- AdamW on every parameter tile
+  if (do_update) {
+    tt_tensor *stp = g->step, *bc = g->bc;
+    const float b1 = hp->beta1, b2 = hp->beta2;
+    TRY(ctx->submit("adam_step", {RW(stp, 0), W(bc, 0)}, [=](hipStream_t s, void*) {
+      return tile_adamw_advance(s, (int32_t*)stp->dev(0), F(bc, 0), b1, b2);
+    }));
+    const tt_adamw_hparams h = *hp;
+    for (size_t i = 0; i < g->P.size(); ++i) {
+      tt_tensor *p = g->P[i], *gr = g->G[i], *m = g->M[i], *v = g->Vv[i];
+      for (int64_t lt = 0; lt < p->ntiles; ++lt) {
+        const int64_t n = p->tile_elems(lt);
+        TRY(ctx->submit("adamw", {RW(p, lt), R(gr, lt), RW(m, lt), RW(v, lt), R(bc, 0)}, [=](hipStream_t s, void*) {
+          return tile_fused_adamw(s, n, F(p, lt), F(gr, lt), F(m, lt), F(v, lt), h.lr, h.beta1, h.beta2, h.eps,
+                                  h.weight_decay, F(bc, 0));
+        }));
+      }
+    }
+  }
+  g->last_tasks = ctx->next_id - t0;
+  return ctx->flush();
+}

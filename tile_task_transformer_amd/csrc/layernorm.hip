@@ -1,0 +1,438 @@
+// LayerNorm tile tasks (forward, backward) and the deterministic column sums
+// they and the linear-layer bias gradient use.
+//
+// LayerNorm is HBM-bound: each row (token) is read once, reduced with one
+// wave64 butterfly and written once. One wave owns one row at a time; a row
+// tile of up to 2048 features stays in registers (NV float4 per lane), so
+// the two-pass mean / squared-deviation statistics cost no second read.
+// When the embedding axis is split into several feature tiles, each tile
+// contributes (count, mean, M2) and the partials are merged in tile order
+// with the parallel-variance update of Chan, Golub and LeVeque.
+#include "rowops.hpp"
+
+using tt::f32x4;
+
+namespace {
+
+constexpr int kWaves = 4;  // waves per workgroup
+
+// ------------------------------------------------------------- forward
+
+// phase FUSED: stats + y; phase PARTIAL: (count, mean, M2) only
+template <int NV, bool VEC>
+__global__ __launch_bounds__(256) void ln_fwd_rows(int phase, int rows, int cols, const float* __restrict__ x,
+                                                   int64_t ldx, const float* __restrict__ gamma,
+                                                   const float* __restrict__ beta, float* __restrict__ parts,
+                                                   float* __restrict__ stats, float* __restrict__ y, int64_t ldy,
+                                                   float eps) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  f32x4 v[NV];
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int c = (j * 64 + lane) * 4;
+    v[j] = c < cols ? tt::ld4<VEC>(x, ldx, row, c, cols) : f32x4{0.f, 0.f, 0.f, 0.f};
+    sum += (v[j][0] + v[j][1]) + (v[j][2] + v[j][3]);
+  }
+  const float mean = tt::wave_sum(sum) / (float)cols;
+  float m2 = 0.f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int c = (j * 64 + lane) * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (c + i < cols) {
+        const float d = v[j][i] - mean;
+        m2 += d * d;
+      }
+  }
+  m2 = tt::wave_sum(m2);
+  if (phase == TT_LN_PARTIAL) {
+    if (lane == 0) {
+      parts[(int64_t)row * 3 + 0] = (float)cols;
+      parts[(int64_t)row * 3 + 1] = mean;
+      parts[(int64_t)row * 3 + 2] = m2;
+    }
+    return;
+  }
+  const float rstd = 1.f / sqrtf(m2 / (float)cols + eps);
+  if (lane == 0) {
+    stats[(int64_t)row * 2 + 0] = mean;
+    stats[(int64_t)row * 2 + 1] = rstd;
+  }
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int c = (j * 64 + lane) * 4;
+    if (c >= cols) continue;
+    const f32x4 g = tt::ldv4<VEC>(gamma, c, cols), b = tt::ldv4<VEC>(beta, c, cols);
+    f32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = (v[j][i] - mean) * rstd * g[i] + b[i];
+    tt::st4<VEC>(y, ldy, row, c, cols, o);
+  }
+}
+
+__global__ void ln_fwd_merge(int rows, int n_parts, const float* __restrict__ parts, int64_t stride,
+                             float* __restrict__ stats, float eps) {
+  const int row = blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= rows) return;
+  float n = parts[(int64_t)row * 3], mean = parts[(int64_t)row * 3 + 1], m2 = parts[(int64_t)row * 3 + 2];
+  for (int p = 1; p < n_parts; ++p) {
+    const float* q = parts + p * stride + (int64_t)row * 3;
+    const float nb = q[0], mb = q[1], m2b = q[2];
+    const float nn = n + nb, delta = mb - mean;
+    mean += delta * (nb / nn);
+    m2 += m2b + delta * delta * (n * nb / nn);
+    n = nn;
+  }
+  stats[(int64_t)row * 2] = mean;
+  stats[(int64_t)row * 2 + 1] = 1.f / sqrtf(m2 / n + eps);
+}
+
+template <bool VEC>
+__global__ void ln_fwd_apply(int rows, int cols, const float* __restrict__ x, int64_t ldx,
+                             const float* __restrict__ gamma, const float* __restrict__ beta,
+                             const float* __restrict__ stats, float* __restrict__ y, int64_t ldy) {
+  const int c4 = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  const int row = blockIdx.y;
+  if (c4 >= cols) return;
+  const float mean = stats[(int64_t)row * 2], rstd = stats[(int64_t)row * 2 + 1];
+  const f32x4 v = tt::ld4<VEC>(x, ldx, row, c4, cols);
+  const f32x4 g = tt::ldv4<VEC>(gamma, c4, cols), b = tt::ldv4<VEC>(beta, c4, cols);
+  f32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = (v[i] - mean) * rstd * g[i] + b[i];
+  tt::st4<VEC>(y, ldy, row, c4, cols, o);
+}
+
+// ------------------------------------------------------------- backward
+
+// Rows of one workgroup; each wave takes kRowsPerWave consecutive rows.
+constexpr int kRowsPerWave = 4;
+constexpr int kRowsPerBlock = kWaves * kRowsPerWave;
+
+// phase PARTIAL: parts = (sum dxhat, sum dxhat*xhat); FUSED / APPLY: dx and
+// per-block column partials of dy*xhat and dy into ws[block][2][cols].
+template <int NV, bool VEC>
+__global__ __launch_bounds__(256) void ln_bwd_rows(int phase, int rows, int cols, float n_total,
+                                                   const float* __restrict__ dy, int64_t lddy,
+                                                   const float* __restrict__ x, int64_t ldx,
+                                                   const float* __restrict__ gamma, const float* __restrict__ stats,
+                                                   float* __restrict__ parts, int n_parts, int64_t part_stride,
+                                                   float* __restrict__ dx, int64_t lddx, int dx_acc,
+                                                   float* __restrict__ ws) {
+  __shared__ f32x4 red[kWaves][2][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  f32x4 g[NV], dg[NV], db[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int c = (j * 64 + lane) * 4;
+    g[j] = c < cols ? tt::ldv4<VEC>(gamma, c, cols) : f32x4{0.f, 0.f, 0.f, 0.f};
+    dg[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    db[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float inv_n = 1.f / n_total;
+  for (int rr = 0; rr < kRowsPerWave; ++rr) {
+    const int row = blockIdx.x * kRowsPerBlock + wave * kRowsPerWave + rr;
+    if (row >= rows) break;
+    const float mean = stats[(int64_t)row * 2], rstd = stats[(int64_t)row * 2 + 1];
+    f32x4 xh[NV], dxh[NV];
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int c = (j * 64 + lane) * 4;
+      f32x4 xv = f32x4{0.f, 0.f, 0.f, 0.f}, dv = xv;
+      if (c < cols) {
+        xv = tt::ld4<VEC>(x, ldx, row, c, cols);
+        dv = tt::ld4<VEC>(dy, lddy, row, c, cols);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = c + i < cols;
+        xh[j][i] = ok ? (xv[i] - mean) * rstd : 0.f;
+        dxh[j][i] = dv[i] * g[j][i];
+        s1 += dxh[j][i];
+        s2 += dxh[j][i] * xh[j][i];
+        dg[j][i] += dv[i] * xh[j][i];
+        db[j][i] += dv[i];
+      }
+    }
+    if (phase == TT_LN_PARTIAL) {
+      s1 = tt::wave_sum(s1);
+      s2 = tt::wave_sum(s2);
+      if (lane == 0) {
+        parts[(int64_t)row * 2] = s1;
+        parts[(int64_t)row * 2 + 1] = s2;
+      }
+      continue;
+    }
+    if (phase == TT_LN_FUSED) {
+      s1 = tt::wave_sum(s1);
+      s2 = tt::wave_sum(s2);
+    } else {  // APPLY: merge the per-tile partial sums in tile order
+      s1 = 0.f;
+      s2 = 0.f;
+      for (int p = 0; p < n_parts; ++p) {
+        s1 += parts[p * part_stride + (int64_t)row * 2];
+        s2 += parts[p * part_stride + (int64_t)row * 2 + 1];
+      }
+    }
+    const float a1 = s1 * inv_n, a2 = s2 * inv_n;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int c = (j * 64 + lane) * 4;
+      if (c >= cols) continue;
+      f32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = rstd * (dxh[j][i] - a1 - xh[j][i] * a2);
+      if (dx_acc) {
+        const f32x4 old = tt::ld4<VEC>(dx, lddx, row, c, cols);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] += old[i];
+      }
+      tt::st4<VEC>(dx, lddx, row, c, cols, o);
+    }
+  }
+  if (phase == TT_LN_PARTIAL) return;
+  // combine the 4 waves' column partials in wave order, one 256-column chunk at a time
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    red[wave][0][lane] = dg[j];
+    red[wave][1][lane] = db[j];
+    __syncthreads();
+    if (wave == 0) {
+      const int c = (j * 64 + lane) * 4;
+      f32x4 a = red[0][0][lane], b = red[0][1][lane];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) {
+        a += red[w][0][lane];
+        b += red[w][1][lane];
+      }
+      float* out = ws + (int64_t)blockIdx.x * 2 * cols;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (c + i < cols) {
+          out[c + i] = a[i];
+          out[cols + c + i] = b[i];
+        }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+// Column sums of nblk partial rows -> out[c] (+)= sum_b ws[b*ws_ld + c], in
+// block order. One workgroup: 64 columns x 16 row groups, combined in order.
+__global__ __launch_bounds__(256) void colsum_finish(int nblk, int cols, const float* __restrict__ ws,
+                                                     int64_t ws_ld, int64_t ws_off, float* __restrict__ out,
+                                                     int accumulate) {
+  __shared__ float red[16][64];
+  const int cl = threadIdx.x & 63, grp = threadIdx.x >> 6;  // 4 groups of 64 threads
+  const int c = blockIdx.x * 64 + cl;
+  float s[4] = {0.f, 0.f, 0.f, 0.f};
+  if (c < cols) {
+    // group grp sums partial rows b = grp*4 + q (mod 16 lanes of order)
+    for (int b = grp; b < nblk; b += 4) s[b / 4 % 4] += ws[(int64_t)b * ws_ld + ws_off + c];
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) red[grp * 4 + q][cl] = s[q];
+  __syncthreads();
+  if (grp == 0 && c < cols) {
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t += red[i][cl];
+    out[c] = accumulate ? out[c] + t : t;
+  }
+}
+
+namespace {
+
+template <int NV>
+int launch_ln_fwd_rows(bool vec, int phase, int rows, int cols, const float* x, int64_t ldx, const float* gamma,
+                       const float* beta, float* parts, float* stats, float* y, int64_t ldy, float eps,
+                       hipStream_t s) {
+  dim3 grid((rows + kWaves - 1) / kWaves), block(256);
+  if (vec)
+    hipLaunchKernelGGL((ln_fwd_rows<NV, true>), grid, block, 0, s, phase, rows, cols, x, ldx, gamma, beta, parts,
+                       stats, y, ldy, eps);
+  else
+    hipLaunchKernelGGL((ln_fwd_rows<NV, false>), grid, block, 0, s, phase, rows, cols, x, ldx, gamma, beta, parts,
+                       stats, y, ldy, eps);
+  return tt::launch_status("tile_layernorm_fwd");
+}
+
+template <int NV>
+int launch_ln_bwd_rows(bool vec, int phase, int rows, int cols, float n_total, const float* dy, int64_t lddy,
+                       const float* x, int64_t ldx, const float* gamma, const float* stats, float* parts,
+                       int n_parts, int64_t part_stride, float* dx, int64_t lddx, int dx_acc, float* ws,
+                       hipStream_t s) {
+  dim3 grid((rows + kRowsPerBlock - 1) / kRowsPerBlock), block(256);
+  if (vec)
+    hipLaunchKernelGGL((ln_bwd_rows<NV, true>), grid, block, 0, s, phase, rows, cols, n_total, dy, lddy, x, ldx,
+                       gamma, stats, parts, n_parts, part_stride, dx, lddx, dx_acc, ws);
+  else
+    hipLaunchKernelGGL((ln_bwd_rows<NV, false>), grid, block, 0, s, phase, rows, cols, n_total, dy, lddy, x, ldx,
+                       gamma, stats, parts, n_parts, part_stride, dx, lddx, dx_acc, ws);
+  return tt::launch_status("tile_layernorm_bwd");
+}
+
+constexpr int kMaxCols = 2048;  // 8 float4 per lane
+
+}  // namespace
+
+extern "C" int tile_layernorm_fwd(void* stream, int phase, int64_t rows, int64_t cols, const float* x, int64_t ldx,
+                                  const float* gamma, const float* beta, float* parts, int64_t n_parts,
+                                  int64_t part_stride, float* stats, float* y, int64_t ldy, float eps) {
+  using tt::fail;
+  hipStream_t s = tt::as_stream(stream);
+  if (rows < 0 || cols < 0) return fail(TT_ERR_ARG, "tile_layernorm_fwd: negative size");
+  if (rows == 0) return TT_OK;
+  if (rows > INT32_MAX) return fail(TT_ERR_ARG, "tile_layernorm_fwd: too many rows");
+  if (phase == TT_LN_MERGE) {
+    if (!parts || !stats || n_parts < 1) return fail(TT_ERR_ARG, "tile_layernorm_fwd(MERGE): bad argument");
+    hipLaunchKernelGGL(ln_fwd_merge, dim3((rows + 255) / 256), dim3(256), 0, s, (int)rows, (int)n_parts, parts,
+                       part_stride, stats, eps);
+    return tt::launch_status("tile_layernorm_fwd(MERGE)");
+  }
+  if (cols < 1 || cols > kMaxCols) return fail(TT_ERR_SHAPE, "tile_layernorm_fwd: cols %lld not in [1, %d]",
+                                               (long long)cols, kMaxCols);
+  if (!x || ldx < cols) return fail(TT_ERR_ARG, "tile_layernorm_fwd: bad x");
+  const bool vec = ldx % 4 == 0 && tt::aligned16(x);
+  if (phase == TT_LN_APPLY) {
+    if (!stats || !y || !gamma || !beta || ldy < cols) return fail(TT_ERR_ARG, "tile_layernorm_fwd(APPLY): bad argument");
+    const bool v2 = vec && ldy % 4 == 0 && tt::aligned16(y) && tt::aligned16(gamma) && tt::aligned16(beta);
+    dim3 grid((unsigned)((cols / 4 + 1 + 63) / 64), (unsigned)rows), block(64);
+    if (v2) hipLaunchKernelGGL(ln_fwd_apply<true>, grid, block, 0, s, (int)rows, (int)cols, x, ldx, gamma, beta, stats, y, ldy);
+    else hipLaunchKernelGGL(ln_fwd_apply<false>, grid, block, 0, s, (int)rows, (int)cols, x, ldx, gamma, beta, stats, y, ldy);
+    return tt::launch_status("tile_layernorm_fwd(APPLY)");
+  }
+  if (phase == TT_LN_PARTIAL) {
+    if (!parts) return fail(TT_ERR_ARG, "tile_layernorm_fwd(PARTIAL): null parts");
+  } else if (phase == TT_LN_FUSED) {
+    if (!stats || !y || !gamma || !beta || ldy < cols) return fail(TT_ERR_ARG, "tile_layernorm_fwd(FUSED): bad argument");
+  } else {
+    return fail(TT_ERR_ARG, "tile_layernorm_fwd: bad phase %d", phase);
+  }
+  const bool v2 = vec && (phase == TT_LN_PARTIAL ||
+                          (ldy % 4 == 0 && tt::aligned16(y) && tt::aligned16(gamma) && tt::aligned16(beta)));
+  const int nv = (int)((cols + 255) / 256);
+  const int r = (int)rows, c = (int)cols;
+  switch (nv) {
+    case 1: return launch_ln_fwd_rows<1>(v2, phase, r, c, x, ldx, gamma, beta, parts, stats, y, ldy, eps, s);
+    case 2: return launch_ln_fwd_rows<2>(v2, phase, r, c, x, ldx, gamma, beta, parts, stats, y, ldy, eps, s);
+    case 3: return launch_ln_fwd_rows<3>(v2, phase, r, c, x, ldx, gamma, beta, parts, stats, y, ldy, eps, s);
+    case 4: return launch_ln_fwd_rows<4>(v2, phase, r, c, x, ldx, gamma, beta, parts, stats, y, ldy, eps, s);
+    case 5: case 6: return launch_ln_fwd_rows<6>(v2, phase, r, c, x, ldx, gamma, beta, parts, stats, y, ldy, eps, s);
+    default: return launch_ln_fwd_rows<8>(v2, phase, r, c, x, ldx, gamma, beta, parts, stats, y, ldy, eps, s);
+  }
+}
+
+extern "C" size_t tile_layernorm_bwd_workspace(int64_t rows, int64_t cols) {
+  const int64_t nblk = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  return (size_t)(nblk * 2 * cols * sizeof(float));
+}
+
+extern "C" int tile_layernorm_bwd(void* stream, int phase, int64_t rows, int64_t cols, int64_t n_total,
+                                  const float* dy, int64_t lddy, const float* x, int64_t ldx, const float* gamma,
+                                  const float* stats, float* parts, int64_t n_parts, int64_t part_stride, float* dx,
+                                  int64_t lddx, int dx_acc, float* dgamma, float* dbeta, void* workspace) {
+  using tt::fail;
+  hipStream_t s = tt::as_stream(stream);
+  if (rows < 0 || cols < 0) return fail(TT_ERR_ARG, "tile_layernorm_bwd: negative size");
+  if (rows == 0) return TT_OK;
+  if (rows > INT32_MAX) return fail(TT_ERR_ARG, "tile_layernorm_bwd: too many rows");
+  if (cols < 1 || cols > kMaxCols) return fail(TT_ERR_SHAPE, "tile_layernorm_bwd: cols %lld not in [1, %d]",
+                                               (long long)cols, kMaxCols);
+  if (phase != TT_LN_PARTIAL && phase != TT_LN_APPLY && phase != TT_LN_FUSED)
+    return fail(TT_ERR_ARG, "tile_layernorm_bwd: bad phase %d", phase);
+  if (!dy || !x || !gamma || !stats || lddy < cols || ldx < cols) return fail(TT_ERR_ARG, "tile_layernorm_bwd: bad input");
+  if (phase == TT_LN_FUSED && n_total != cols) return fail(TT_ERR_SHAPE, "tile_layernorm_bwd(FUSED): n_total != cols");
+  if (n_total < cols) return fail(TT_ERR_SHAPE, "tile_layernorm_bwd: n_total < cols");
+  if (phase != TT_LN_FUSED && !parts) return fail(TT_ERR_ARG, "tile_layernorm_bwd: null parts");
+  if (phase == TT_LN_APPLY && n_parts < 1) return fail(TT_ERR_ARG, "tile_layernorm_bwd(APPLY): n_parts < 1");
+  if (phase != TT_LN_PARTIAL && (!dx || lddx < cols || !dgamma || !dbeta || !workspace))
+    return fail(TT_ERR_ARG, "tile_layernorm_bwd: bad output");
+  const bool vec = lddy % 4 == 0 && ldx % 4 == 0 && tt::aligned16(dy) && tt::aligned16(x) && tt::aligned16(gamma) &&
+                   (phase == TT_LN_PARTIAL || (lddx % 4 == 0 && tt::aligned16(dx)));
+  const int nv = (int)((cols + 255) / 256);
+  const int r = (int)rows, c = (int)cols;
+  float* ws = (float*)workspace;
+  int rc;
+#define TT_LNB(NV)                                                                                              \
+  launch_ln_bwd_rows<NV>(vec, phase, r, c, (float)n_total, dy, lddy, x, ldx, gamma, stats, parts, (int)n_parts, \
+                         part_stride, dx, lddx, dx_acc, ws, s)
+  switch (nv) {
+    case 1: rc = TT_LNB(1); break;
+    case 2: rc = TT_LNB(2); break;
+    case 3: rc = TT_LNB(3); break;
+    case 4: rc = TT_LNB(4); break;
+    case 5: case 6: rc = TT_LNB(6); break;
+    default: rc = TT_LNB(8); break;
+  }
+#undef TT_LNB
+  if (rc || phase == TT_LN_PARTIAL) return rc;
+  const int nblk = (r + kRowsPerBlock - 1) / kRowsPerBlock;
+  dim3 grid((c + 63) / 64), block(256);
+  hipLaunchKernelGGL(colsum_finish, grid, block, 0, s, nblk, c, ws, (int64_t)2 * c, (int64_t)0, dgamma, 1);
+  hipLaunchKernelGGL(colsum_finish, grid, block, 0, s, nblk, c, ws, (int64_t)2 * c, (int64_t)c, dbeta, 1);
+  return tt::launch_status("tile_layernorm_bwd(colsum)");
+}
+
+// ------------------------------------------------------------ reduce_rows
+
+namespace {
+constexpr int kReduceRows = 64;  // rows per stage-1 block
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void reduce_rows_stage1(int rows, int cols, const float* __restrict__ X,
+                                                          int64_t ldx, float* __restrict__ ws) {
+  __shared__ f32x4 red[4][64];
+  const int cl = threadIdx.x & 63, grp = threadIdx.x >> 6;
+  const int c = (blockIdx.y * 64 + cl) * 4;
+  const int r0 = blockIdx.x * kReduceRows + grp * (kReduceRows / 4);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (c < cols)
+    for (int r = r0; r < min(rows, r0 + kReduceRows / 4); ++r) acc += tt::ld4<VEC>(X, ldx, r, c, cols);
+  red[grp][cl] = acc;
+  __syncthreads();
+  if (grp == 0 && c < cols) {
+    f32x4 t = red[0][cl];
+#pragma unroll
+    for (int g = 1; g < 4; ++g) t += red[g][cl];
+    float* out = ws + (int64_t)blockIdx.x * cols;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (c + i < cols) out[c + i] = t[i];
+  }
+}
+}  // namespace
+
+extern "C" size_t tile_reduce_rows_workspace(int64_t rows, int64_t cols) {
+  return (size_t)(((rows + kReduceRows - 1) / kReduceRows) * cols * sizeof(float));
+}
+
+extern "C" int tile_reduce_rows(void* stream, int64_t rows, int64_t cols, const float* X, int64_t ldx, float* out,
+                                int beta, void* workspace) {
+  using tt::fail;
+  hipStream_t s = tt::as_stream(stream);
+  if (rows < 0 || cols < 0) return fail(TT_ERR_ARG, "tile_reduce_rows: negative size");
+  if (cols == 0) return TT_OK;
+  if (!out || !workspace) return fail(TT_ERR_ARG, "tile_reduce_rows: null output/workspace");
+  if (rows > INT32_MAX || cols > INT32_MAX) return fail(TT_ERR_ARG, "tile_reduce_rows: size exceeds int32");
+  const int r = (int)rows, c = (int)cols;
+  const int nblk = (r + kReduceRows - 1) / kReduceRows;
+  float* ws = (float*)workspace;
+  if (rows > 0) {
+    if (!X || ldx < cols) return fail(TT_ERR_ARG, "tile_reduce_rows: bad X");
+    dim3 grid(nblk, (c + 255) / 256), block(256);
+    if (ldx % 4 == 0 && tt::aligned16(X)) hipLaunchKernelGGL(reduce_rows_stage1<true>, grid, block, 0, s, r, c, X, ldx, ws);
+    else hipLaunchKernelGGL(reduce_rows_stage1<false>, grid, block, 0, s, r, c, X, ldx, ws);
+    if (int rc = tt::launch_status("tile_reduce_rows")) return rc;
+  }
+  hipLaunchKernelGGL(colsum_finish, dim3((c + 63) / 64), dim3(256), 0, s, nblk, c, ws, (int64_t)c, (int64_t)0, out,
+                     beta);
+  return tt::launch_status("tile_reduce_rows(finish)");
+}

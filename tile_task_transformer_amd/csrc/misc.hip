@@ -1,0 +1,274 @@
+// Fused AdamW, the embedding layer's tile tasks, and small helpers.
+//
+// All of these are HBM-bound streams: AdamW reads p, g, m, v and writes p,
+// m, v (28 bytes per parameter) in one pass of 16-byte accesses; the
+// embedding gather reads one wte row and one wpe row per token.
+#include "rowops.hpp"
+
+using tt::f32x4;
+
+namespace {
+
+__device__ __forceinline__ float adamw1(float& p, float g, float& m, float& v, float lr, float b1, float b2, float eps,
+                                        float decay, float bc1, float bc2) {
+  p *= decay;
+  m = b1 * m + (1.f - b1) * g;
+  v = b2 * v + (1.f - b2) * g * g;
+  p -= lr * (m / bc1) / (sqrtf(v / bc2) + eps);
+  return p;
+}
+
+__global__ __launch_bounds__(256) void adamw_vec(int64_t n4, f32x4* __restrict__ p, const f32x4* __restrict__ g,
+                                                 f32x4* __restrict__ m, f32x4* __restrict__ v, float lr, float b1,
+                                                 float b2, float eps, float decay, const float* __restrict__ bc) {
+  const float bc1 = bc[0], bc2 = bc[1];
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+    f32x4 pp = p[i], gg = g[i], mm = m[i], vv = v[i];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float a = pp[k], c = mm[k], e = vv[k];
+      adamw1(a, gg[k], c, e, lr, b1, b2, eps, decay, bc1, bc2);
+      pp[k] = a;
+      mm[k] = c;
+      vv[k] = e;
+    }
+    p[i] = pp;
+    m[i] = mm;
+    v[i] = vv;
+  }
+}
+
+__global__ void adamw_scalar(int64_t n, float* __restrict__ p, const float* __restrict__ g, float* __restrict__ m,
+                             float* __restrict__ v, float lr, float b1, float b2, float eps, float decay,
+                             const float* __restrict__ bc) {
+  const float bc1 = bc[0], bc2 = bc[1];
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    adamw1(p[i], g[i], m[i], v[i], lr, b1, b2, eps, decay, bc1, bc2);
+}
+
+__global__ void adamw_advance_k(int32_t* step, float* bc, float b1, float b2) {
+  const int t = ++step[0];
+  // 1 - beta^t by repeated multiplication in double (t is small)
+  double p1 = 1.0, p2 = 1.0;
+  for (int i = 0; i < t; ++i) {
+    p1 *= (double)b1;
+    p2 *= (double)b2;
+  }
+  bc[0] = (float)(1.0 - p1);
+  bc[1] = (float)(1.0 - p2);
+}
+
+unsigned grid_for(int64_t work, int per_block = 256) {
+  int64_t b = (work + per_block - 1) / per_block;
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(b, 256 * 64));
+}
+
+// -------------------------------------------------------------- embedding
+
+template <bool VEC>
+__global__ void emb_fwd(int rows, int cols, const int32_t* __restrict__ ids, int64_t vocab, const float* __restrict__ wte,
+                        int64_t ld_wte, const float* __restrict__ wpe, int64_t ld_wpe, int64_t seq_len,
+                        int64_t pos_off, float* __restrict__ out, int64_t ldo) {
+  const int64_t cpr = (cols + 3) / 4;
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= (int64_t)rows * cpr) return;
+  const int64_t r = i / cpr;
+  const int c = (int)(i % cpr) * 4;
+  const int32_t id = ids[r];
+  f32x4 o;
+  if (id < 0 || id >= vocab) {
+    o = f32x4{NAN, NAN, NAN, NAN};
+  } else {
+    const int64_t pos = pos_off + r % seq_len;
+    o = tt::ld4<VEC>(wte, ld_wte, id, c, cols) + tt::ld4<VEC>(wpe, ld_wpe, pos, c, cols);
+  }
+  tt::st4<VEC>(out, ldo, r, c, cols, o);
+}
+
+// stable rank of each id: number of ids that are smaller, or equal and earlier
+__global__ __launch_bounds__(256) void emb_index(int rows, const int32_t* __restrict__ ids, int32_t* __restrict__ sorted,
+                                                 int32_t* __restrict__ perm) {
+  __shared__ int32_t chunk[2048];
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  const int32_t me = r < rows ? ids[r] : 0;
+  int rank = 0;
+  for (int base = 0; base < rows; base += 2048) {
+    const int n = min(2048, rows - base);
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += 256) chunk[i] = ids[base + i];
+    __syncthreads();
+    if (r < rows)
+      for (int i = 0; i < n; ++i) {
+        const int32_t o = chunk[i];
+        rank += (o < me) || (o == me && base + i < r);
+      }
+  }
+  if (r < rows) {
+    sorted[rank] = me;
+    perm[rank] = r;
+  }
+}
+
+// one wave per sorted position that starts a run of equal ids inside the vocab tile
+template <bool VEC>
+__global__ __launch_bounds__(256) void emb_bwd_token(int rows, int cols, const int32_t* __restrict__ sorted,
+                                                     const int32_t* __restrict__ perm, int64_t v_off, int64_t v_len,
+                                                     const float* __restrict__ dh, int64_t lddh,
+                                                     float* __restrict__ dst, int64_t ld) {
+  const int lane = threadIdx.x & 63;
+  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (p >= rows) return;
+  const int32_t id = sorted[p];
+  if (id < v_off || id >= v_off + v_len) return;
+  if (p > 0 && sorted[p - 1] == id) return;
+  int end = p + 1;
+  while (end < rows && sorted[end] == id) ++end;
+  const int64_t drow = id - v_off;
+  for (int c = lane * 4; c < cols; c += 256) {
+    f32x4 acc = tt::ld4<VEC>(dst, ld, drow, c, cols);
+    for (int q = p; q < end; ++q) acc += tt::ld4<VEC>(dh, lddh, perm[q], c, cols);
+    tt::st4<VEC>(dst, ld, drow, c, cols, acc);
+  }
+}
+
+template <bool VEC>
+__global__ void emb_bwd_pos(int seq_len, int batch, int cols, const float* __restrict__ dh, int64_t lddh,
+                            float* __restrict__ dst, int64_t ld) {
+  const int64_t cpr = (cols + 3) / 4;
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= (int64_t)seq_len * cpr) return;
+  const int64_t t = i / cpr;
+  const int c = (int)(i % cpr) * 4;
+  f32x4 acc = tt::ld4<VEC>(dst, ld, t, c, cols);
+  for (int b = 0; b < batch; ++b) acc += tt::ld4<VEC>(dh, lddh, (int64_t)b * seq_len + t, c, cols);
+  tt::st4<VEC>(dst, ld, t, c, cols, acc);
+}
+
+__global__ void fill_k(int64_t n, float* __restrict__ dst, float value) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = value;
+}
+
+__global__ void split_tokens_k(int64_t batch, int64_t seq, const int32_t* __restrict__ tokens, int32_t* __restrict__ ids,
+                               int32_t* __restrict__ labels) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= batch * seq) return;
+  const int64_t b = i / seq, t = i % seq;
+  ids[i] = tokens[b * (seq + 1) + t];
+  labels[i] = tokens[b * (seq + 1) + t + 1];
+}
+
+}  // namespace
+
+extern "C" int tile_fused_adamw(void* stream, int64_t n, float* p, const float* g, float* m, float* v, float lr,
+                                float beta1, float beta2, float eps, float weight_decay, const float* bias_corr) {
+  using tt::fail;
+  if (n < 0) return fail(TT_ERR_ARG, "tile_fused_adamw: negative size");
+  if (n == 0) return TT_OK;
+  if (!p || !g || !m || !v || !bias_corr) return fail(TT_ERR_ARG, "tile_fused_adamw: null pointer");
+  hipStream_t s = tt::as_stream(stream);
+  const float decay = 1.f - lr * weight_decay;
+  if (n % 4 == 0 && tt::aligned16(p) && tt::aligned16(g) && tt::aligned16(m) && tt::aligned16(v)) {
+    hipLaunchKernelGGL(adamw_vec, dim3(grid_for(n / 4)), dim3(256), 0, s, n / 4, (f32x4*)p, (const f32x4*)g,
+                       (f32x4*)m, (f32x4*)v, lr, beta1, beta2, eps, decay, bias_corr);
+  } else {
+    hipLaunchKernelGGL(adamw_scalar, dim3(grid_for(n)), dim3(256), 0, s, n, p, g, m, v, lr, beta1, beta2, eps, decay,
+                       bias_corr);
+  }
+  return tt::launch_status("tile_fused_adamw");
+}
+
+extern "C" int tile_adamw_advance(void* stream, int32_t* step, float* bias_corr, float beta1, float beta2) {
+  if (!step || !bias_corr) return tt::fail(TT_ERR_ARG, "tile_adamw_advance: null pointer");
+  hipLaunchKernelGGL(adamw_advance_k, dim3(1), dim3(1), 0, tt::as_stream(stream), step, bias_corr, beta1, beta2);
+  return tt::launch_status("tile_adamw_advance");
+}
+
+extern "C" int tile_embedding_fwd(void* stream, int64_t rows, int64_t cols, const int32_t* ids, int64_t vocab,
+                                  const float* wte, int64_t ld_wte, const float* wpe, int64_t ld_wpe, int64_t seq_len,
+                                  int64_t pos_offset, float* out, int64_t ldo) {
+  using tt::fail;
+  if (rows < 0 || cols < 0 || seq_len <= 0 || vocab <= 0) return fail(TT_ERR_ARG, "tile_embedding_fwd: bad size");
+  if (rows == 0 || cols == 0) return TT_OK;
+  if (!ids || !wte || !wpe || !out || ld_wte < cols || ld_wpe < cols || ldo < cols)
+    return fail(TT_ERR_ARG, "tile_embedding_fwd: bad argument");
+  if (rows > INT32_MAX || cols > INT32_MAX) return fail(TT_ERR_ARG, "tile_embedding_fwd: size exceeds int32");
+  const bool vec = ld_wte % 4 == 0 && ld_wpe % 4 == 0 && ldo % 4 == 0 && tt::aligned16(wte) && tt::aligned16(wpe) &&
+                   tt::aligned16(out);
+  const int64_t work = rows * ((cols + 3) / 4);
+  dim3 grid((unsigned)((work + 255) / 256)), block(256);
+  hipStream_t s = tt::as_stream(stream);
+  if (vec)
+    hipLaunchKernelGGL(emb_fwd<true>, grid, block, 0, s, (int)rows, (int)cols, ids, vocab, wte, ld_wte, wpe, ld_wpe,
+                       seq_len, pos_offset, out, ldo);
+  else
+    hipLaunchKernelGGL(emb_fwd<false>, grid, block, 0, s, (int)rows, (int)cols, ids, vocab, wte, ld_wte, wpe, ld_wpe,
+                       seq_len, pos_offset, out, ldo);
+  return tt::launch_status("tile_embedding_fwd");
+}
+
+extern "C" int tile_embedding_index(void* stream, int64_t rows, const int32_t* ids, int32_t* sorted_ids,
+                                    int32_t* perm) {
+  using tt::fail;
+  if (rows < 0 || rows > 65536) return fail(TT_ERR_ARG, "tile_embedding_index: rows must be in [0, 65536]");
+  if (rows == 0) return TT_OK;
+  if (!ids || !sorted_ids || !perm) return fail(TT_ERR_ARG, "tile_embedding_index: null pointer");
+  hipLaunchKernelGGL(emb_index, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, tt::as_stream(stream), (int)rows,
+                     ids, sorted_ids, perm);
+  return tt::launch_status("tile_embedding_index");
+}
+
+extern "C" int tile_embedding_bwd(void* stream, int phase, int64_t rows, int64_t cols, const int32_t* sorted_ids,
+                                  const int32_t* perm, int64_t v_off, int64_t v_len, int64_t seq_len, const float* dh,
+                                  int64_t lddh, float* dst, int64_t ld_dst) {
+  using tt::fail;
+  if (rows < 0 || cols < 0) return fail(TT_ERR_ARG, "tile_embedding_bwd: negative size");
+  if (rows == 0 || cols == 0) return TT_OK;
+  if (!dh || !dst || lddh < cols || ld_dst < cols) return fail(TT_ERR_ARG, "tile_embedding_bwd: bad argument");
+  if (rows > INT32_MAX || cols > INT32_MAX) return fail(TT_ERR_ARG, "tile_embedding_bwd: size exceeds int32");
+  const bool vec = lddh % 4 == 0 && ld_dst % 4 == 0 && tt::aligned16(dh) && tt::aligned16(dst);
+  hipStream_t s = tt::as_stream(stream);
+  if (phase == TT_EMB_TOKEN) {
+    if (!sorted_ids || !perm || v_len < 0) return fail(TT_ERR_ARG, "tile_embedding_bwd(TOKEN): bad argument");
+    dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    if (vec)
+      hipLaunchKernelGGL(emb_bwd_token<true>, grid, block, 0, s, (int)rows, (int)cols, sorted_ids, perm, v_off, v_len,
+                         dh, lddh, dst, ld_dst);
+    else
+      hipLaunchKernelGGL(emb_bwd_token<false>, grid, block, 0, s, (int)rows, (int)cols, sorted_ids, perm, v_off, v_len,
+                         dh, lddh, dst, ld_dst);
+    return tt::launch_status("tile_embedding_bwd(TOKEN)");
+  }
+  if (phase == TT_EMB_POS) {
+    if (seq_len <= 0 || rows % seq_len != 0) return fail(TT_ERR_SHAPE, "tile_embedding_bwd(POS): rows not a multiple of seq_len");
+    const int64_t work = seq_len * ((cols + 3) / 4);
+    dim3 grid((unsigned)((work + 255) / 256)), block(256);
+    if (vec)
+      hipLaunchKernelGGL(emb_bwd_pos<true>, grid, block, 0, s, (int)seq_len, (int)(rows / seq_len), (int)cols, dh, lddh,
+                         dst, ld_dst);
+    else
+      hipLaunchKernelGGL(emb_bwd_pos<false>, grid, block, 0, s, (int)seq_len, (int)(rows / seq_len), (int)cols, dh,
+                         lddh, dst, ld_dst);
+    return tt::launch_status("tile_embedding_bwd(POS)");
+  }
+  return fail(TT_ERR_ARG, "tile_embedding_bwd: bad phase %d", phase);
+}
+
+extern "C" int tile_fill(void* stream, int64_t n, float* dst, float value) {
+  if (n < 0) return tt::fail(TT_ERR_ARG, "tile_fill: negative size");
+  if (n == 0) return TT_OK;
+  if (!dst) return tt::fail(TT_ERR_ARG, "tile_fill: null pointer");
+  hipLaunchKernelGGL(fill_k, dim3(grid_for(n)), dim3(256), 0, tt::as_stream(stream), n, dst, value);
+  return tt::launch_status("tile_fill");
+}
+
+extern "C" int tile_split_tokens(void* stream, int64_t batch, int64_t seq, const int32_t* tokens, int32_t* ids,
+                                 int32_t* labels) {
+  if (batch < 0 || seq < 0) return tt::fail(TT_ERR_ARG, "tile_split_tokens: negative size");
+  if (batch == 0 || seq == 0) return TT_OK;
+  if (!tokens || !ids || !labels) return tt::fail(TT_ERR_ARG, "tile_split_tokens: null pointer");
+  const int64_t n = batch * seq;
+  hipLaunchKernelGGL(split_tokens_k, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, tt::as_stream(stream), batch, seq,
+                     tokens, ids, labels);
+  return tt::launch_status("tile_split_tokens");
+}

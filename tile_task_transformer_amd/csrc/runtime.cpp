@@ -1,0 +1,628 @@
+// Tiled tensors, the sequential-task-flow executor, and their C ABI.
+#include "runtime.hpp"
+
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <fstream>
+
+namespace tt {
+
+static thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[1024];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+void clear_error() { g_err.clear(); }
+
+}  // namespace tt
+
+extern "C" const char* tt_last_error(void) { return tt::g_err.c_str(); }
+extern "C" const char* tt_version(void) { return "tiletask 0.1 gfx950"; }
+
+using namespace tt;
+
+// ------------------------------------------------------------------ tensors
+
+void tt_tensor::extent(int64_t l, int64_t* ext) const {
+  for (int d = 0; d < ndim; ++d) {
+    int64_t i = l % grid[d];
+    l /= grid[d];
+    ext[d] = std::min(tshape[d], shape[d] - i * tshape[d]);
+  }
+}
+
+int64_t tt_tensor::tile_elems(int64_t l) const {
+  int64_t ext[TT_MAX_DIMS];
+  extent(l, ext);
+  int64_t n = 1;
+  for (int d = 0; d < ndim; ++d) n *= ext[d];
+  return n;
+}
+
+int64_t tt_tensor::lin(const int64_t* idx) const {
+  int64_t l = 0;
+  for (int d = ndim - 1; d >= 0; --d) l = l * grid[d] + idx[d];
+  return l;
+}
+
+void tt_tensor::mat(int64_t l, int64_t* rows, int64_t* cols) const {
+  int64_t ext[TT_MAX_DIMS];
+  extent(l, ext);
+  int64_t r = 1, c = 1;
+  for (int d = 0; d < ndim; ++d) (d < mat_split ? r : c) *= ext[d];
+  *rows = r;
+  *cols = c;
+}
+
+void* tt_tensor::dev(int64_t l) const {
+  if (home == TT_HOME_PINNED_HOST) return res[l].dev;
+  if (!base) return nullptr;
+  return base + tile_off[l] * (int64_t)esize();
+}
+
+namespace tt {
+
+int tensor_create(tt_ctx* ctx, int ndim, const int64_t* shape, const int64_t* tshape, int dtype,
+                  int home, int mat_split, const char* name, tt_tensor** out) {
+  if (!ctx || !out || !shape || !tshape) return fail(TT_ERR_ARG, "tensor_create: null argument");
+  if (ndim < 1 || ndim > TT_MAX_DIMS) return fail(TT_ERR_ARG, "tensor_create: ndim %d out of range", ndim);
+  if (dtype != TT_F32 && dtype != TT_I32) return fail(TT_ERR_ARG, "tensor_create: bad dtype");
+  if (home != TT_HOME_DEVICE && home != TT_HOME_PINNED_HOST) return fail(TT_ERR_ARG, "tensor_create: bad home");
+  std::unique_ptr<tt_tensor> t(new tt_tensor());
+  t->ctx = ctx;
+  t->id = ctx->next_tensor_id++;
+  t->ndim = ndim;
+  t->dtype = dtype;
+  t->home = home;
+  t->mat_split = std::max(0, std::min(mat_split, ndim));
+  t->name = name ? name : "";
+  t->ntiles = 1;
+  t->elems = 1;
+  for (int d = 0; d < ndim; ++d) {
+    if (shape[d] <= 0 || tshape[d] <= 0)
+      return fail(TT_ERR_SHAPE, "tensor %s: axis %d has shape %lld tile %lld", t->name.c_str(), d,
+                  (long long)shape[d], (long long)tshape[d]);
+    t->shape[d] = shape[d];
+    t->tshape[d] = std::min(tshape[d], shape[d]);
+    t->grid[d] = ceil_div(shape[d], t->tshape[d]);
+    t->ntiles *= t->grid[d];
+    t->elems *= shape[d];
+  }
+  t->tile_off.resize(t->ntiles);
+  int64_t off = 0;
+  for (int64_t l = 0; l < t->ntiles; ++l) {
+    t->tile_off[l] = off;
+    off += t->tile_elems(l);
+  }
+  t->state.resize(t->ntiles);
+  if (!ctx->dryrun) {
+    if (home == TT_HOME_DEVICE) {
+      hipError_t e = hipMalloc(&t->base, std::max<int64_t>(t->bytes(), 256));
+      if (e != hipSuccess)
+        return fail(TT_ERR_OOM, "tensor %s: hipMalloc(%lld) failed: %s", t->name.c_str(),
+                    (long long)t->bytes(), hipGetErrorString(e));
+    } else {
+      hipError_t e = hipHostMalloc(&t->host, std::max<int64_t>(t->bytes(), 256), hipHostMallocDefault);
+      if (e != hipSuccess)
+        return fail(TT_ERR_OOM, "tensor %s: hipHostMalloc(%lld) failed: %s", t->name.c_str(),
+                    (long long)t->bytes(), hipGetErrorString(e));
+      memset(t->host, 0, t->bytes());
+      t->res.resize(t->ntiles);
+    }
+    t->owned = true;
+  }
+  ctx->tensors.push_back(t.get());
+  *out = t.release();
+  return TT_OK;
+}
+
+}  // namespace tt
+
+// ----------------------------------------------------------------- executor
+
+tt::Launched* tt_ctx::info(int64_t id) {
+  if (id < launched_base || id - launched_base >= (int64_t)launched.size()) return nullptr;
+  return &launched[id - launched_base];
+}
+
+int tt_ctx::acquire_event(int* idx) {
+  if (events_used == (int)events.size()) {
+    hipEvent_t e;
+    TT_HIP_TRY(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    events.push_back(e);
+  }
+  *idx = events_used++;
+  stats.events_recorded++;
+  return TT_OK;
+}
+
+int tt_ctx::ensure_workspace(size_t bytes) {
+  if (bytes <= workspace_bytes || dryrun) {
+    workspace_bytes = std::max(workspace_bytes, bytes);
+    return TT_OK;
+  }
+  int rc = wait_all();
+  if (rc) return rc;
+  for (void* p : workspace)
+    if (p) (void)hipFree(p);
+  workspace.assign(n_streams, nullptr);
+  for (int s = 0; s < n_streams; ++s) {
+    hipError_t e = hipMalloc(&workspace[s], bytes);
+    if (e != hipSuccess) return fail(TT_ERR_OOM, "workspace hipMalloc(%zu) failed", bytes);
+  }
+  workspace_bytes = bytes;
+  return TT_OK;
+}
+
+int tt_ctx::submit(const char* label, std::vector<tt::Access> acc, tt::LaunchFn run) {
+  if (latched) return fail(TT_ERR_STATE, "context has a latched error: %s", latched_msg.c_str());
+  auto t0 = std::chrono::steady_clock::now();
+  tt::Task task;
+  task.id = next_id++;
+  snprintf(task.label, sizeof(task.label), "%s", label ? label : "");
+  // merge duplicate accesses to the same tile: any write makes it a write
+  for (size_t i = 0; i < acc.size(); ++i) {
+    if (!acc[i].ref.t) return fail(TT_ERR_ARG, "task %s: null tensor in access %zu", task.label, i);
+    if (acc[i].ref.t->ctx != this) return fail(TT_ERR_ARG, "task %s: tensor from another context", task.label);
+    if (acc[i].ref.lin < 0 || acc[i].ref.lin >= acc[i].ref.t->ntiles)
+      return fail(TT_ERR_ARG, "task %s: tile index out of range", task.label);
+  }
+  std::vector<tt::Access> merged;
+  for (auto& a : acc) {
+    bool found = false;
+    for (auto& m : merged)
+      if (m.ref.t == a.ref.t && m.ref.lin == a.ref.lin) {
+        m.mode |= a.mode;
+        found = true;
+      }
+    if (!found) merged.push_back(a);
+  }
+  // dependency inference (sequential task flow)
+  for (auto& a : merged) {
+    tt::TileState& st = a.ref.t->state[a.ref.lin];
+    if (st.last_writer >= done_below) task.deps.push_back(st.last_writer);
+    if (a.mode & TT_W) {
+      for (int64_t r : st.readers)
+        if (r >= done_below) task.deps.push_back(r);
+      st.readers.clear();
+      st.last_writer = task.id;
+    } else {
+      st.readers.push_back(task.id);
+    }
+  }
+  std::sort(task.deps.begin(), task.deps.end());
+  task.deps.erase(std::unique(task.deps.begin(), task.deps.end()), task.deps.end());
+  stats.tasks++;
+  stats.edges += (int64_t)task.deps.size();
+  task.acc = std::move(merged);
+  task.run = std::move(run);
+  if (pending.empty()) window_base = task.id;
+  pending.push_back(std::move(task));
+  int rc = TT_OK;
+  if ((int)pending.size() >= window) rc = flush();
+  stats.submit_seconds += std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+  return rc;
+}
+
+int tt_ctx::flush() {
+  if (pending.empty()) return latched;
+  // 1. stream assignment: continue the chain of a dependency that is still the
+  //    tail of its stream, else spread independent work round-robin.
+  for (auto& task : pending) {
+    int best = -1;
+    int64_t best_id = -1;
+    for (int64_t d : task.deps) {
+      int ds = -1;
+      if (d >= window_base) ds = pending[d - window_base].stream;
+      else if (auto* li = info(d)) ds = li->stream;
+      if (ds >= 0 && last_assigned[ds] == d && d > best_id) {
+        best = ds;
+        best_id = d;
+      }
+    }
+    if (best < 0) {
+      best = rr;
+      rr = (rr + 1) % n_streams;
+    }
+    task.stream = best;
+    last_assigned[best] = task.id;
+  }
+  // 2. events only where a successor in this window sits on another stream
+  for (auto& task : pending)
+    for (int64_t d : task.deps)
+      if (d >= window_base && pending[d - window_base].stream != task.stream)
+        pending[d - window_base].need_event = true;
+  // 3. launch in submission order
+  if (launched.empty()) launched_base = window_base;
+  for (auto& task : pending) {
+    const int s = task.stream;
+    for (int64_t d : task.deps) {
+      if (d < done_below) continue;
+      tt::Launched* li = info(d);
+      if (!li || li->stream == s) continue;
+      if (waited[s][li->stream] >= li->seq) continue;
+      if (!dryrun) {
+        if (li->event < 0) {
+          // dependency launched in an earlier window without an event: record
+          // one now on its stream (covers it and whatever followed it there)
+          int ev;
+          if (int rc = acquire_event(&ev)) return rc;
+          TT_HIP_TRY(hipEventRecord(events[ev], streams[li->stream]));
+          li->event = ev;
+          li->seq = stream_seq[li->stream];
+        }
+        TT_HIP_TRY(hipStreamWaitEvent(streams[s], events[li->event], 0));
+      }
+      waited[s][li->stream] = li->seq;
+      stats.cross_stream_waits++;
+    }
+    if (record) {
+      tt::TaskRecord r;
+      r.id = task.id;
+      r.label = task.label;
+      r.stream = s;
+      r.deps = task.deps;
+      for (auto& a : task.acc) r.acc.push_back({a.ref.t->id, {a.ref.lin, a.mode}});
+      records.push_back(std::move(r));
+    }
+    tt::Launched li;
+    li.stream = s;
+    li.seq = ++stream_seq[s];
+    if (!dryrun && !latched) {
+      int rc = make_resident(task, streams[s]);
+      if (rc == TT_OK && task.run) rc = task.run(streams[s], workspace.empty() ? nullptr : workspace[s]);
+      if (rc != TT_OK) {
+        latched = rc;
+        latched_msg = std::string(task.label) + ": " + tt_last_error();
+      }
+      if (task.need_event && !latched) {
+        int ev;
+        if (int rc2 = acquire_event(&ev)) return rc2;
+        TT_HIP_TRY(hipEventRecord(events[ev], streams[s]));
+        li.event = ev;
+      }
+    }
+    launched.push_back(li);
+  }
+  pending.clear();
+  if (latched) return fail(latched, "%s", latched_msg.c_str());
+  return TT_OK;
+}
+
+int tt_ctx::make_resident(tt::Task& task, hipStream_t s) {
+  (void)s;
+  for (auto& a : task.acc)
+    if (a.ref.t->home == TT_HOME_PINNED_HOST)
+      return fail(TT_ERR_UNSUPPORTED, "pinned-host tiles are not resident-managed yet");
+  return TT_OK;
+}
+
+int tt_ctx::wait_all() {
+  int rc = flush();
+  if (!dryrun) {
+    for (auto s : streams) {
+      hipError_t e = hipStreamSynchronize(s);
+      if (e != hipSuccess && !latched) {
+        latched = TT_ERR_HIP;
+        latched_msg = std::string("asynchronous fault: ") + hipGetErrorString(e);
+      }
+    }
+  }
+  // everything submitted so far has completed
+  done_below = next_id;
+  launched.clear();
+  launched_base = next_id;
+  events_used = 0;
+  for (auto& w : waited) std::fill(w.begin(), w.end(), 0);
+  for (int s = 0; s < n_streams; ++s) {
+    stream_seq[s] = 0;
+    last_assigned[s] = -1;
+  }
+  if (latched) return fail(latched, "%s", latched_msg.c_str());
+  return rc;
+}
+
+// -------------------------------------------------------------------- C ABI
+
+extern "C" {
+
+int tt_ctx_create(int device, int n_streams, int window, size_t device_budget_bytes, tt_ctx** out) {
+  clear_error();
+  if (!out) return fail(TT_ERR_ARG, "tt_ctx_create: out is null");
+  if (n_streams < 1 || n_streams > 16) return fail(TT_ERR_ARG, "tt_ctx_create: n_streams must be 1..16");
+  if (window < 0) return fail(TT_ERR_ARG, "tt_ctx_create: negative window");
+  std::unique_ptr<tt_ctx> c(new tt_ctx());
+  c->dryrun = device == TT_DEVICE_DRYRUN;
+  c->device = c->dryrun ? -1 : device;
+  c->n_streams = n_streams;
+  c->window = window ? window : 512;
+  c->budget = device_budget_bytes;
+  c->record = c->dryrun;
+  if (const char* e = getenv("TT_RECORD_DAG")) c->record = c->record || atoi(e) != 0;
+  c->stream_seq.assign(n_streams, 0);
+  c->last_assigned.assign(n_streams, -1);
+  c->waited.assign(n_streams, std::vector<int64_t>(n_streams, 0));
+  if (!c->dryrun) {
+    if (device < 0) return fail(TT_ERR_ARG, "tt_ctx_create: bad device %d", device);
+    TT_HIP_TRY(hipSetDevice(device));
+    c->streams.resize(n_streams);
+    for (int s = 0; s < n_streams; ++s)
+      TT_HIP_TRY(hipStreamCreateWithFlags(&c->streams[s], hipStreamNonBlocking));
+    TT_HIP_TRY(hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking));
+  }
+  *out = c.release();
+  return TT_OK;
+}
+
+int tt_ctx_destroy(tt_ctx* c) {
+  clear_error();
+  if (!c) return fail(TT_ERR_ARG, "tt_ctx_destroy: null");
+  int rc = c->dryrun ? TT_OK : c->wait_all();
+  while (!c->tensors.empty()) tt_tensor_destroy(c->tensors.back());
+  if (!c->dryrun) {
+    for (void* p : c->workspace)
+      if (p) (void)hipFree(p);
+    for (auto e : c->events) (void)hipEventDestroy(e);
+    for (auto s : c->streams) (void)hipStreamDestroy(s);
+    if (c->copy_stream) (void)hipStreamDestroy(c->copy_stream);
+  }
+  delete c;
+  return rc;
+}
+
+int tt_ctx_stream(tt_ctx* c, int i, void** stream) {
+  if (!c || !stream || i < 0 || i >= c->n_streams) return fail(TT_ERR_ARG, "tt_ctx_stream: bad argument");
+  *stream = c->dryrun ? nullptr : (void*)c->streams[i];
+  return TT_OK;
+}
+
+int tt_ctx_record(tt_ctx* c, int on) {
+  if (!c) return fail(TT_ERR_ARG, "tt_ctx_record: null");
+  c->record = on != 0;
+  return TT_OK;
+}
+
+int tt_tensor_create(tt_ctx* ctx, int ndim, const int64_t* shape, const int64_t* tile_shape, int dtype,
+                     int home, tt_tensor** out) {
+  clear_error();
+  return tt::tensor_create(ctx, ndim, shape, tile_shape, dtype, home, ndim - 1, nullptr, out);
+}
+
+int tt_tensor_wrap(tt_ctx* ctx, int ndim, const int64_t* shape, const int64_t* tile_shape, int dtype,
+                   void* device_base, tt_tensor** out) {
+  clear_error();
+  if (!ctx || ctx->dryrun) return fail(TT_ERR_ARG, "tt_tensor_wrap: needs a device context");
+  if (!device_base) return fail(TT_ERR_ARG, "tt_tensor_wrap: null base");
+  // create a dry descriptor then attach the caller's memory
+  bool dr = ctx->dryrun;
+  ctx->dryrun = true;
+  int rc = tt::tensor_create(ctx, ndim, shape, tile_shape, dtype, TT_HOME_DEVICE, ndim - 1, nullptr, out);
+  ctx->dryrun = dr;
+  if (rc) return rc;
+  (*out)->base = (char*)device_base;
+  (*out)->owned = false;
+  return TT_OK;
+}
+
+int tt_tensor_destroy(tt_tensor* t) {
+  if (!t) return fail(TT_ERR_ARG, "tt_tensor_destroy: null");
+  tt_ctx* c = t->ctx;
+  if (!c->dryrun) {
+    int rc = c->wait_all();
+    (void)rc;
+  }
+  if (t->owned) {
+    if (t->base) (void)hipFree(t->base);
+    if (t->host) (void)hipHostFree(t->host);
+    for (auto& r : t->res)
+      if (r.dev) (void)hipFree(r.dev);
+  }
+  auto it = std::find(c->tensors.begin(), c->tensors.end(), t);
+  if (it != c->tensors.end()) c->tensors.erase(it);
+  delete t;
+  return TT_OK;
+}
+
+int64_t tt_tensor_bytes(const tt_tensor* t) { return t ? t->bytes() : -1; }
+
+int tt_tensor_grid(const tt_tensor* t, int64_t* grid_out, int64_t* ntiles) {
+  if (!t) return fail(TT_ERR_ARG, "tt_tensor_grid: null");
+  if (grid_out)
+    for (int d = 0; d < t->ndim; ++d) grid_out[d] = t->grid[d];
+  if (ntiles) *ntiles = t->ntiles;
+  return TT_OK;
+}
+
+static int check_idx(const tt_tensor* t, const int64_t* idx) {
+  if (!idx) return fail(TT_ERR_ARG, "null tile index");
+  for (int d = 0; d < t->ndim; ++d)
+    if (idx[d] < 0 || idx[d] >= t->grid[d])
+      return fail(TT_ERR_ARG, "tile index %lld out of range on axis %d", (long long)idx[d], d);
+  return TT_OK;
+}
+
+int tt_tensor_tile(tt_tensor* t, const int64_t* idx, void** dev_ptr, int64_t* extent) {
+  clear_error();
+  if (!t) return fail(TT_ERR_ARG, "tt_tensor_tile: null");
+  if (int rc = check_idx(t, idx)) return rc;
+  int64_t l = t->lin(idx);
+  if (!t->ctx->dryrun)
+    if (int rc = t->ctx->wait_all()) return rc;
+  if (t->home == TT_HOME_PINNED_HOST)
+    return fail(TT_ERR_UNSUPPORTED, "tt_tensor_tile: pinned-host tile access not supported");
+  if (dev_ptr) *dev_ptr = t->dev(l);
+  if (extent) t->extent(l, extent);
+  return TT_OK;
+}
+
+// dense row-major <-> tile-major permutation on the host
+static void permute(const tt_tensor* t, const char* src, char* dst, bool to_tiles) {
+  const size_t es = t->esize();
+  int64_t dstride[TT_MAX_DIMS];
+  dstride[t->ndim - 1] = 1;
+  for (int d = t->ndim - 2; d >= 0; --d) dstride[d] = dstride[d + 1] * t->shape[d + 1];
+  for (int64_t l = 0; l < t->ntiles; ++l) {
+    int64_t ext[TT_MAX_DIMS], org[TT_MAX_DIMS];
+    t->extent(l, ext);
+    int64_t rem = l;
+    for (int d = 0; d < t->ndim; ++d) {
+      org[d] = (rem % t->grid[d]) * t->tshape[d];
+      rem /= t->grid[d];
+    }
+    int64_t tile_base = t->tile_off[l];
+    const int last = t->ndim - 1;
+    int64_t nrows = 1;
+    for (int d = 0; d < last; ++d) nrows *= ext[d];
+    int64_t cnt[TT_MAX_DIMS] = {};
+    for (int64_t r = 0; r < nrows; ++r) {
+      int64_t doff = org[last];
+      for (int d = 0; d < last; ++d) doff += (org[d] + cnt[d]) * dstride[d];
+      int64_t toff = tile_base + r * ext[last];
+      if (to_tiles) memcpy(dst + toff * es, src + doff * es, ext[last] * es);
+      else memcpy(dst + doff * es, src + toff * es, ext[last] * es);
+      for (int d = last - 1; d >= 0; --d) {
+        if (++cnt[d] < ext[d]) break;
+        cnt[d] = 0;
+      }
+    }
+  }
+}
+
+int tt_tensor_copy_in(tt_tensor* t, const void* dense) {
+  clear_error();
+  if (!t || !dense) return fail(TT_ERR_ARG, "tt_tensor_copy_in: null");
+  tt_ctx* c = t->ctx;
+  if (c->dryrun) return fail(TT_ERR_STATE, "tt_tensor_copy_in: dry-run context");
+  if (int rc = c->wait_all()) return rc;
+  std::vector<char> buf(t->bytes());
+  permute(t, (const char*)dense, buf.data(), true);
+  if (t->home == TT_HOME_PINNED_HOST) {
+    memcpy(t->host, buf.data(), t->bytes());
+    for (auto& r : t->res) {
+      r.host_valid = true;
+      r.dev_valid = false;
+    }
+    return TT_OK;
+  }
+  TT_HIP_TRY(hipMemcpy(t->base, buf.data(), t->bytes(), hipMemcpyHostToDevice));
+  return TT_OK;
+}
+
+int tt_tensor_copy_out(tt_tensor* t, void* dense) {
+  clear_error();
+  if (!t || !dense) return fail(TT_ERR_ARG, "tt_tensor_copy_out: null");
+  tt_ctx* c = t->ctx;
+  if (c->dryrun) return fail(TT_ERR_STATE, "tt_tensor_copy_out: dry-run context");
+  if (int rc = c->wait_all()) return rc;
+  std::vector<char> buf(t->bytes());
+  if (t->home == TT_HOME_PINNED_HOST) {
+    for (int64_t l = 0; l < t->ntiles; ++l) {
+      auto& r = t->res[l];
+      if (!r.host_valid && r.dev_valid)
+        TT_HIP_TRY(hipMemcpy(t->host + t->tile_off[l] * 4, r.dev, t->tile_elems(l) * 4, hipMemcpyDeviceToHost));
+      r.host_valid = true;
+    }
+    memcpy(buf.data(), t->host, t->bytes());
+  } else {
+    TT_HIP_TRY(hipMemcpy(buf.data(), t->base, t->bytes(), hipMemcpyDeviceToHost));
+  }
+  permute(t, buf.data(), (char*)dense, false);
+  return TT_OK;
+}
+
+int tt_submit_nop(tt_ctx* c, const char* label, const tt_access* acc, int n) {
+  clear_error();
+  if (!c || (n > 0 && !acc) || n < 0) return fail(TT_ERR_ARG, "tt_submit_nop: bad argument");
+  std::vector<tt::Access> a;
+  for (int i = 0; i < n; ++i) {
+    if (!acc[i].tensor) return fail(TT_ERR_ARG, "tt_submit_nop: null tensor");
+    if (acc[i].mode < TT_R || acc[i].mode > TT_RW) return fail(TT_ERR_ARG, "tt_submit_nop: bad mode");
+    if (int rc = check_idx(acc[i].tensor, acc[i].tile)) return rc;
+    a.push_back(tt::Access{tt::TileRef{acc[i].tensor, acc[i].tensor->lin(acc[i].tile)}, acc[i].mode});
+  }
+  return c->submit(label, std::move(a), nullptr);
+}
+
+int tt_submit_gemm(tt_ctx* c, int transA, int transB, float alpha, tt_tensor* A, const int64_t* ia,
+                   tt_tensor* B, const int64_t* ib, float beta, tt_tensor* C, const int64_t* ic) {
+  clear_error();
+  if (!c || !A || !B || !C) return fail(TT_ERR_ARG, "tt_submit_gemm: null");
+  if (A->ndim != 2 || B->ndim != 2 || C->ndim != 2) return fail(TT_ERR_SHAPE, "tt_submit_gemm: 2-D tensors only");
+  if (A->dtype != TT_F32 || B->dtype != TT_F32 || C->dtype != TT_F32)
+    return fail(TT_ERR_ARG, "tt_submit_gemm: f32 tensors only");
+  for (auto p : {std::make_pair((const tt_tensor*)A, ia), std::make_pair((const tt_tensor*)B, ib),
+                  std::make_pair((const tt_tensor*)C, ic)})
+    if (int rc = check_idx(p.first, p.second)) return rc;
+  int64_t la = A->lin(ia), lb = B->lin(ib), lc = C->lin(ic);
+  int64_t ar, ac, br, bc, cr, cc;
+  A->mat(la, &ar, &ac);
+  B->mat(lb, &br, &bc);
+  C->mat(lc, &cr, &cc);
+  int64_t m = transA ? ac : ar, k = transA ? ar : ac;
+  int64_t kb = transB ? bc : br, n = transB ? br : bc;
+  if (k != kb || m != cr || n != cc)
+    return fail(TT_ERR_SHAPE, "tt_submit_gemm: op(A) %lldx%lld, op(B) %lldx%lld, C %lldx%lld", (long long)m,
+                (long long)k, (long long)kb, (long long)n, (long long)cr, (long long)cc);
+  std::vector<tt::Access> acc = {tt::R(A, la), tt::R(B, lb), beta == 0.f ? tt::W(C, lc) : tt::RW(C, lc)};
+  return c->submit("gemm", std::move(acc), [=](hipStream_t s, void*) {
+    return tile_gemm(s, transA, transB, m, n, k, alpha, (const float*)A->dev(la), ac, (const float*)B->dev(lb), bc,
+                     beta, (float*)C->dev(lc), cc, TT_EPI_NONE, nullptr, nullptr, 0, nullptr, 0);
+  });
+}
+
+int tt_submit_fill(tt_ctx* c, tt_tensor* t, const int64_t* idx, float value) {
+  clear_error();
+  if (!c || !t) return fail(TT_ERR_ARG, "tt_submit_fill: null");
+  if (int rc = check_idx(t, idx)) return rc;
+  int64_t l = t->lin(idx);
+  int64_t n = t->tile_elems(l);
+  return c->submit("fill", {tt::W(t, l)}, [=](hipStream_t s, void*) {
+    return tile_fill(s, n, (float*)t->dev(l), value);
+  });
+}
+
+int tt_wait(tt_ctx* c) {
+  clear_error();
+  if (!c) return fail(TT_ERR_ARG, "tt_wait: null");
+  return c->wait_all();
+}
+
+int tt_dump_dag(tt_ctx* c, const char* path) {
+  clear_error();
+  if (!c || !path) return fail(TT_ERR_ARG, "tt_dump_dag: null");
+  if (int rc = c->flush()) return rc;
+  std::ofstream f(path);
+  if (!f) return fail(TT_ERR_ARG, "tt_dump_dag: cannot open %s", path);
+  for (auto& r : c->records) {
+    f << "{\"id\":" << r.id << ",\"label\":\"" << r.label << "\",\"stream\":" << r.stream << ",\"deps\":[";
+    for (size_t i = 0; i < r.deps.size(); ++i) f << (i ? "," : "") << r.deps[i];
+    f << "],\"acc\":[";
+    for (size_t i = 0; i < r.acc.size(); ++i)
+      f << (i ? "," : "") << "[" << r.acc[i].first << "," << r.acc[i].second.first << ","
+        << r.acc[i].second.second << "]";
+    f << "]}\n";
+  }
+  return TT_OK;
+}
+
+int tt_get_stats(tt_ctx* c, tt_stats* out) {
+  if (!c || !out) return fail(TT_ERR_ARG, "tt_get_stats: null");
+  *out = c->stats;
+  return TT_OK;
+}
+
+int tt_reset_stats(tt_ctx* c) {
+  if (!c) return fail(TT_ERR_ARG, "tt_reset_stats: null");
+  c->stats = tt_stats{};
+  c->records.clear();
+  return TT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,175 @@
+// Tiled tensors and the sequential-task-flow executor (internal C++ API).
+//
+// The executor implements the runtime side of the method described in the
+// pith.science review of NNTile ("What carries the argument"): tasks are
+// submitted in program order, each names the tiles it reads and writes, and
+// the ordering between tasks is inferred from those accesses alone:
+//   read  after write  (RAW): a reader waits for the tile's last writer;
+//   write after read   (WAR): a writer waits for every reader since then;
+//   write after write  (WAW): a writer waits for the previous writer.
+// Ready tasks are mapped onto a small set of HIP streams (one GPU); an edge
+// between tasks on the same stream is free (streams are FIFO), an edge that
+// crosses streams becomes an event record + hipStreamWaitEvent.
+#pragma once
+
+#include <chrono>
+#include <functional>
+#include <memory>
+#include <string>
+#include <vector>
+
+#include "common.hpp"
+
+struct tt_ctx;
+
+namespace tt {
+
+struct TileState {
+  int64_t last_writer = -1;        // task id of the last writer
+  std::vector<int64_t> readers;    // task ids that read since that write
+};
+
+// Residency of one tile whose home is pinned host memory.
+struct Residency {
+  float* dev = nullptr;            // device copy (null if not resident)
+  bool dev_valid = false;          // device copy holds the latest value
+  bool host_valid = true;          // host copy holds the latest value
+  int64_t last_use = -1;           // task id of the last task using it
+  int64_t ready_seq = -1;          // copy-stream sequence of its H2D, if any
+};
+
+}  // namespace tt
+
+struct tt_tensor {
+  tt_ctx* ctx = nullptr;
+  int64_t id = 0;
+  int ndim = 0;
+  int64_t shape[TT_MAX_DIMS] = {};
+  int64_t tshape[TT_MAX_DIMS] = {};
+  int64_t grid[TT_MAX_DIMS] = {};
+  int dtype = TT_F32;
+  int home = TT_HOME_DEVICE;
+  int mat_split = 1;               // leading dims that form the rows of a tile's matrix view
+  int64_t ntiles = 0;
+  int64_t elems = 0;
+  std::vector<int64_t> tile_off;   // element offset of each tile (tile-major)
+  std::vector<tt::TileState> state;
+  char* base = nullptr;            // device base (device home)
+  char* host = nullptr;            // pinned host base (pinned home)
+  bool owned = false;
+  std::vector<tt::Residency> res;  // pinned home only
+  std::string name;
+
+  size_t esize() const { return 4; }
+  int64_t bytes() const { return elems * (int64_t)esize(); }
+  // extents of tile `lin`
+  void extent(int64_t lin, int64_t* ext) const;
+  int64_t tile_elems(int64_t lin) const;
+  int64_t lin(const int64_t* idx) const;
+  // rows/cols of the matrix view of tile `lin`
+  void mat(int64_t lin, int64_t* rows, int64_t* cols) const;
+  // device pointer of tile `lin` (valid at launch time; residency handled by the executor)
+  void* dev(int64_t lin) const;
+};
+
+namespace tt {
+
+struct TileRef {
+  tt_tensor* t = nullptr;
+  int64_t lin = -1;
+  bool valid() const { return t != nullptr; }
+};
+
+struct Access {
+  TileRef ref;
+  int mode;  // TT_R, TT_W, TT_RW
+};
+
+using LaunchFn = std::function<int(hipStream_t stream, void* workspace)>;
+
+struct Task {
+  int64_t id = 0;
+  char label[32] = {};
+  std::vector<int64_t> deps;
+  std::vector<Access> acc;
+  LaunchFn run;
+  int stream = -1;
+  bool need_event = false;
+};
+
+struct Launched {
+  int stream = -1;
+  int64_t seq = -1;        // position on its stream (1-based)
+  int event = -1;          // index into the event pool, -1 = none recorded
+};
+
+struct TaskRecord {        // kept for tt_dump_dag
+  int64_t id;
+  std::string label;
+  int stream;
+  std::vector<int64_t> deps;
+  std::vector<std::pair<int64_t, std::pair<int64_t, int>>> acc;  // tensor id, tile lin, mode
+};
+
+}  // namespace tt
+
+struct tt_ctx {
+  int device = 0;
+  bool dryrun = false;
+  int n_streams = 1;
+  int window = 512;
+  size_t budget = 0;
+  bool record = false;
+  int latched = TT_OK;             // first asynchronous/launch error
+  std::string latched_msg;
+
+  std::vector<hipStream_t> streams;
+  hipStream_t copy_stream = nullptr;   // residency H2D/D2H
+  std::vector<void*> workspace;        // per stream
+  size_t workspace_bytes = 0;
+
+  // task ids
+  int64_t next_id = 0;
+  int64_t done_below = 0;              // tasks with id < done_below are complete
+  int64_t window_base = 0;             // id of pending[0]
+  std::vector<tt::Task> pending;
+  std::vector<tt::Launched> launched;  // index id - launched_base
+  int64_t launched_base = 0;
+
+  // per-stream bookkeeping
+  std::vector<int64_t> stream_seq;     // tasks launched on each stream
+  std::vector<int64_t> last_assigned;  // id of the last task assigned to each stream
+  std::vector<std::vector<int64_t>> waited;  // waited[s][t] = highest seq of t waited by s
+  int rr = 0;
+
+  // events
+  std::vector<hipEvent_t> events;
+  int events_used = 0;
+
+  // residency
+  size_t resident_bytes = 0;
+  int64_t copy_seq = 0;
+  std::vector<hipEvent_t> copy_events; // index by copy seq % ring
+
+  int64_t next_tensor_id = 0;
+  std::vector<tt_tensor*> tensors;     // live tensors
+  std::vector<tt::TaskRecord> records;
+  tt_stats stats = {};
+
+  // ---- internal API
+  int submit(const char* label, std::vector<tt::Access> acc, tt::LaunchFn run);
+  int flush();
+  int wait_all();
+  int ensure_workspace(size_t bytes);
+  tt::Launched* info(int64_t id);
+  int acquire_event(int* idx);
+  int make_resident(tt::Task& task, hipStream_t s);
+};
+
+namespace tt {
+int tensor_create(tt_ctx* ctx, int ndim, const int64_t* shape, const int64_t* tshape, int dtype,
+                  int home, int mat_split, const char* name, tt_tensor** out);
+inline Access R(tt_tensor* t, int64_t lin) { return Access{TileRef{t, lin}, TT_R}; }
+inline Access W(tt_tensor* t, int64_t lin) { return Access{TileRef{t, lin}, TT_W}; }
+inline Access RW(tt_tensor* t, int64_t lin) { return Access{TileRef{t, lin}, TT_RW}; }
+}  // namespace tt

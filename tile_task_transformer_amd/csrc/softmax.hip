@@ -1,0 +1,206 @@
+// Row softmax and cross-entropy tile tasks.
+//
+// The tied LM head's logits are split into vocab tiles, so the softmax over
+// a row is assembled from per-tile partials (row max, sum of exp(x - max))
+// merged by rescaling to the larger max. The same per-tile pass picks the
+// target logit when a row's label falls in the tile, so the loss needs no
+// extra read of the logits. All kernels are HBM-bound row sweeps: one wave
+// per row, the row held in registers between its max and sum passes.
+#include "rowops.hpp"
+
+using tt::f32x4;
+
+namespace {
+
+constexpr int kWaves = 4;
+
+template <int NV, bool VEC>
+__global__ __launch_bounds__(256) void sm_stats(int rows, int cols, int64_t row_off, int64_t col_off, float scale,
+                                                int causal, const float* __restrict__ X, int64_t ldx,
+                                                const int32_t* __restrict__ labels, float* __restrict__ parts) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  // valid columns of this row: c < lim
+  int lim = cols;
+  if (causal) {
+    const int64_t l = row_off + row - col_off + 1;
+    lim = (int)max((int64_t)0, min((int64_t)cols, l));
+  }
+  f32x4 v[NV];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int c = (j * 64 + lane) * 4;
+    v[j] = c < cols ? tt::ld4<VEC>(X, ldx, row, c, cols) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[j][i] = c + i < lim ? v[j][i] * scale : -INFINITY;
+      mx = fmaxf(mx, v[j][i]);
+    }
+  }
+  mx = tt::wave_max(mx);
+  float se = 0.f;
+  if (mx > -INFINITY) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) se += expf(v[j][i] - mx);
+  }
+  se = tt::wave_sum(se);
+  if (lane == 0) {
+    float picked = 0.f;
+    if (labels) {
+      const int64_t lab = labels[row] - col_off;
+      if (lab >= 0 && lab < lim) picked = X[(int64_t)row * ldx + lab] * scale;
+    }
+    parts[(int64_t)row * 3 + 0] = mx;
+    parts[(int64_t)row * 3 + 1] = se;
+    parts[(int64_t)row * 3 + 2] = picked;
+  }
+}
+
+__global__ void sm_merge(int rows, int n_parts, const float* __restrict__ parts, int64_t stride,
+                         float* __restrict__ lse, float* __restrict__ row_loss) {
+  const int row = blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= rows) return;
+  float m = -INFINITY, s = 0.f, picked = 0.f;
+  for (int p = 0; p < n_parts; ++p) {
+    const float* q = parts + p * stride + (int64_t)row * 3;
+    const float mb = q[0], sb = q[1];
+    picked += q[2];
+    const float mn = fmaxf(m, mb);
+    if (mn > -INFINITY) s = (m > -INFINITY ? s * expf(m - mn) : 0.f) + (mb > -INFINITY ? sb * expf(mb - mn) : 0.f);
+    m = mn;
+  }
+  const float l = m + logf(s);
+  lse[row] = l;
+  if (row_loss) row_loss[row] = l - picked;
+}
+
+template <bool VEC>
+__global__ void sm_apply(int rows, int cols, int64_t row_off, int64_t col_off, float scale, int causal,
+                         const float* X, int64_t ldx, const int32_t* __restrict__ labels,
+                         const float* __restrict__ lse, float* Y, int64_t ldy, float grad_scale) {
+  const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  const int row = blockIdx.y;
+  if (c >= cols) return;
+  const float l = lse[row];
+  const int64_t lab = labels ? labels[row] - col_off : -1;
+  const int64_t lim = causal ? row_off + row - col_off + 1 : (int64_t)cols;
+  const f32x4 x = tt::ld4<VEC>(X, ldx, row, c, cols);
+  f32x4 y;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float p = (c + i < lim) ? expf(x[i] * scale - l) : 0.f;
+    if (c + i == lab) p -= 1.f;
+    y[i] = p * grad_scale;
+  }
+  tt::st4<VEC>(Y, ldy, row, c, cols, y);
+}
+
+__global__ __launch_bounds__(256) void xe_loss(int rows, const float* __restrict__ row_loss, float* loss,
+                                               int accumulate, float inv_n) {
+  __shared__ float red[256];
+  float s = 0.f;
+  for (int r = threadIdx.x; r < rows; r += 256) s += row_loss[r];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) loss[0] = (accumulate ? loss[0] : 0.f) + inv_n * red[0];
+}
+
+template <int NV>
+int launch_stats(bool vec, int rows, int cols, int64_t row_off, int64_t col_off, float scale, int causal,
+                 const float* X, int64_t ldx, const int32_t* labels, float* parts, hipStream_t s) {
+  dim3 grid((rows + kWaves - 1) / kWaves), block(256);
+  if (vec)
+    hipLaunchKernelGGL((sm_stats<NV, true>), grid, block, 0, s, rows, cols, row_off, col_off, scale, causal, X, ldx,
+                       labels, parts);
+  else
+    hipLaunchKernelGGL((sm_stats<NV, false>), grid, block, 0, s, rows, cols, row_off, col_off, scale, causal, X, ldx,
+                       labels, parts);
+  return tt::launch_status("tile_softmax(STATS)");
+}
+
+int launch_apply(int rows, int cols, int64_t row_off, int64_t col_off, float scale, int causal, const float* X,
+                 int64_t ldx, const int32_t* labels, const float* lse, float* Y, int64_t ldy, float grad_scale,
+                 hipStream_t s) {
+  const bool vec = ldx % 4 == 0 && ldy % 4 == 0 && tt::aligned16(X) && tt::aligned16(Y);
+  dim3 grid((unsigned)((cols / 4 + 1 + 255) / 256), (unsigned)rows), block(256);
+  if (vec)
+    hipLaunchKernelGGL(sm_apply<true>, grid, block, 0, s, rows, cols, row_off, col_off, scale, causal, X, ldx, labels,
+                       lse, Y, ldy, grad_scale);
+  else
+    hipLaunchKernelGGL(sm_apply<false>, grid, block, 0, s, rows, cols, row_off, col_off, scale, causal, X, ldx, labels,
+                       lse, Y, ldy, grad_scale);
+  return tt::launch_status("tile_softmax(APPLY)");
+}
+
+constexpr int kMaxCols = 2048;
+constexpr int64_t kMaxRows = 65535;
+
+}  // namespace
+
+extern "C" int tile_softmax(void* stream, int phase, int64_t rows, int64_t cols, int64_t row_offset,
+                            int64_t col_offset, float scale, int causal, const float* X, int64_t ldx,
+                            const int32_t* labels, float* parts, int64_t n_parts, int64_t part_stride, float* lse,
+                            float* row_loss, float* Y, int64_t ldy, float grad_scale) {
+  using tt::fail;
+  hipStream_t s = tt::as_stream(stream);
+  if (rows < 0 || cols < 0) return fail(TT_ERR_ARG, "tile_softmax: negative size");
+  if (rows == 0) return TT_OK;
+  if (phase == TT_SM_MERGE) {
+    if (!parts || !lse || n_parts < 1 || rows > INT32_MAX) return fail(TT_ERR_ARG, "tile_softmax(MERGE): bad argument");
+    hipLaunchKernelGGL(sm_merge, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, (int)rows, (int)n_parts, parts,
+                       part_stride, lse, row_loss);
+    return tt::launch_status("tile_softmax(MERGE)");
+  }
+  if (cols < 1 || cols > kMaxCols) return fail(TT_ERR_SHAPE, "tile_softmax: cols %lld not in [1, %d]", (long long)cols, kMaxCols);
+  if (rows > kMaxRows) return fail(TT_ERR_SHAPE, "tile_softmax: rows %lld > %lld", (long long)rows, (long long)kMaxRows);
+  if (!X || ldx < cols) return fail(TT_ERR_ARG, "tile_softmax: bad X");
+  if (phase == TT_SM_STATS) {
+    if (!parts) return fail(TT_ERR_ARG, "tile_softmax(STATS): null parts");
+    const bool vec = ldx % 4 == 0 && tt::aligned16(X);
+    const int nv = (int)((cols + 255) / 256);
+    const int r = (int)rows, c = (int)cols;
+    switch (nv) {
+      case 1: return launch_stats<1>(vec, r, c, row_offset, col_offset, scale, causal, X, ldx, labels, parts, s);
+      case 2: return launch_stats<2>(vec, r, c, row_offset, col_offset, scale, causal, X, ldx, labels, parts, s);
+      case 3: return launch_stats<3>(vec, r, c, row_offset, col_offset, scale, causal, X, ldx, labels, parts, s);
+      case 4: return launch_stats<4>(vec, r, c, row_offset, col_offset, scale, causal, X, ldx, labels, parts, s);
+      case 5: case 6: return launch_stats<6>(vec, r, c, row_offset, col_offset, scale, causal, X, ldx, labels, parts, s);
+      default: return launch_stats<8>(vec, r, c, row_offset, col_offset, scale, causal, X, ldx, labels, parts, s);
+    }
+  }
+  if (phase == TT_SM_APPLY) {
+    if (!lse || !Y || ldy < cols) return fail(TT_ERR_ARG, "tile_softmax(APPLY): bad argument");
+    return launch_apply((int)rows, (int)cols, row_offset, col_offset, scale, causal, X, ldx, labels, lse, Y, ldy,
+                        grad_scale, s);
+  }
+  return fail(TT_ERR_ARG, "tile_softmax: bad phase %d", phase);
+}
+
+extern "C" int tile_xentropy(void* stream, int phase, int64_t rows, int64_t v_len, int64_t v_off,
+                             const int32_t* labels, float* logits, int64_t ldz, const float* lse,
+                             const float* row_loss, float* loss, int accumulate, float inv_n) {
+  using tt::fail;
+  hipStream_t s = tt::as_stream(stream);
+  if (rows < 0 || v_len < 0) return fail(TT_ERR_ARG, "tile_xentropy: negative size");
+  if (phase == TT_XE_LOSS) {
+    if (!loss || (rows > 0 && !row_loss) || rows > INT32_MAX) return fail(TT_ERR_ARG, "tile_xentropy(LOSS): bad argument");
+    hipLaunchKernelGGL(xe_loss, dim3(1), dim3(256), 0, s, (int)rows, row_loss, loss, accumulate, inv_n);
+    return tt::launch_status("tile_xentropy(LOSS)");
+  }
+  if (phase == TT_XE_GRAD) {
+    if (rows == 0 || v_len == 0) return TT_OK;
+    if (!labels || !logits || !lse || ldz < v_len) return fail(TT_ERR_ARG, "tile_xentropy(GRAD): bad argument");
+    if (v_len > kMaxCols) return fail(TT_ERR_SHAPE, "tile_xentropy: v_len > %d", kMaxCols);
+    if (rows > kMaxRows) return fail(TT_ERR_SHAPE, "tile_xentropy: rows > %lld", (long long)kMaxRows);
+    return launch_apply((int)rows, (int)v_len, 0, v_off, 1.f, 0, logits, ldz, labels, lse, logits, ldz, inv_n, s);
+  }
+  return fail(TT_ERR_ARG, "tile_xentropy: bad phase %d", phase);
+}

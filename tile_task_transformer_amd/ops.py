@@ -1,0 +1,110 @@
+"""Tile ops of libtiletask with the C names; arguments marshalled only.
+
+Buffers: torch tensors on the GPU (or raw device addresses). Streams:
+torch.cuda.Stream, a raw hipStream_t, or None for the default stream. See
+include/tiletask.h for the meaning, layout and error behaviour of every
+argument; each call raises TTError on a non-zero return code.
+"""
+from __future__ import annotations
+
+from ._lib import (TT_EPI_NONE, check, lib, ptr, stream_handle, TT_EPI_BIAS, TT_EPI_RES, TT_EPI_GELU,  # noqa: F401
+                   TT_EPI_GELU_BWD, TT_LN_PARTIAL, TT_LN_MERGE, TT_LN_APPLY, TT_LN_FUSED, TT_SM_STATS,
+                   TT_SM_MERGE, TT_SM_APPLY, TT_XE_LOSS, TT_XE_GRAD, TT_ATT_PREP, TT_ATT_GRAD, TT_EMB_TOKEN,
+                   TT_EMB_POS)
+
+__all__ = [
+    "tile_gemm", "tile_layernorm_fwd", "tile_layernorm_bwd", "tile_layernorm_bwd_workspace", "tile_softmax",
+    "tile_xentropy", "tile_attention_fwd", "tile_attention_bwd", "tile_fused_adamw", "tile_adamw_advance",
+    "tile_embedding_fwd", "tile_embedding_index", "tile_embedding_bwd", "tile_reduce_rows",
+    "tile_reduce_rows_workspace", "tile_fill", "tile_split_tokens",
+    "TT_EPI_NONE", "TT_EPI_BIAS", "TT_EPI_RES", "TT_EPI_GELU", "TT_EPI_GELU_BWD", "TT_LN_PARTIAL",
+    "TT_LN_MERGE", "TT_LN_APPLY", "TT_LN_FUSED", "TT_SM_STATS", "TT_SM_MERGE", "TT_SM_APPLY", "TT_XE_LOSS",
+    "TT_XE_GRAD", "TT_ATT_PREP", "TT_ATT_GRAD", "TT_EMB_TOKEN", "TT_EMB_POS",
+]
+
+
+def tile_gemm(stream, transA, transB, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, epilogue=TT_EPI_NONE,
+              bias=None, res=None, ldr=0, aux=None, ldaux=0):
+    return check(lib.tile_gemm(stream_handle(stream), transA, transB, m, n, k, alpha, ptr(A), lda, ptr(B), ldb,
+                               beta, ptr(C), ldc, epilogue, ptr(bias), ptr(res), ldr, ptr(aux), ldaux))
+
+
+def tile_layernorm_fwd(stream, phase, rows, cols, x, ldx, gamma, beta, parts, n_parts, part_stride, stats, y,
+                       ldy, eps):
+    return check(lib.tile_layernorm_fwd(stream_handle(stream), phase, rows, cols, ptr(x), ldx, ptr(gamma),
+                                        ptr(beta), ptr(parts), n_parts, part_stride, ptr(stats), ptr(y), ldy, eps))
+
+
+def tile_layernorm_bwd(stream, phase, rows, cols, n_total, dy, lddy, x, ldx, gamma, stats, parts, n_parts,
+                       part_stride, dx, lddx, dx_acc, dgamma, dbeta, workspace):
+    return check(lib.tile_layernorm_bwd(stream_handle(stream), phase, rows, cols, n_total, ptr(dy), lddy, ptr(x),
+                                        ldx, ptr(gamma), ptr(stats), ptr(parts), n_parts, part_stride, ptr(dx),
+                                        lddx, dx_acc, ptr(dgamma), ptr(dbeta), ptr(workspace)))
+
+
+def tile_layernorm_bwd_workspace(rows, cols):
+    return lib.tile_layernorm_bwd_workspace(rows, cols)
+
+
+def tile_softmax(stream, phase, rows, cols, row_offset, col_offset, scale, causal, X, ldx, labels, parts,
+                 n_parts, part_stride, lse, row_loss, Y, ldy, grad_scale):
+    return check(lib.tile_softmax(stream_handle(stream), phase, rows, cols, row_offset, col_offset, scale, causal,
+                                  ptr(X), ldx, ptr(labels), ptr(parts), n_parts, part_stride, ptr(lse),
+                                  ptr(row_loss), ptr(Y), ldy, grad_scale))
+
+
+def tile_xentropy(stream, phase, rows, v_len, v_off, labels, logits, ldz, lse, row_loss, loss, accumulate, inv_n):
+    return check(lib.tile_xentropy(stream_handle(stream), phase, rows, v_len, v_off, ptr(labels), ptr(logits), ldz,
+                                   ptr(lse), ptr(row_loss), ptr(loss), accumulate, inv_n))
+
+
+def tile_attention_fwd(stream, batch, heads, q_len, k_len, hd, q_off, k_off, Q, K, V, O, ml, lse, first, last,
+                       scale):
+    return check(lib.tile_attention_fwd(stream_handle(stream), batch, heads, q_len, k_len, hd, q_off, k_off, ptr(Q),
+                                        ptr(K), ptr(V), ptr(O), ptr(ml), ptr(lse), first, last, scale))
+
+
+def tile_attention_bwd(stream, phase, batch, heads, q_len, k_len, hd, q_off, k_off, Q, K, V, O, dO, lse, Dvec, dQ,
+                       dK, dV, acc_dq, acc_dkv, scale):
+    return check(lib.tile_attention_bwd(stream_handle(stream), phase, batch, heads, q_len, k_len, hd, q_off, k_off,
+                                        ptr(Q), ptr(K), ptr(V), ptr(O), ptr(dO), ptr(lse), ptr(Dvec), ptr(dQ),
+                                        ptr(dK), ptr(dV), acc_dq, acc_dkv, scale))
+
+
+def tile_fused_adamw(stream, n, p, g, m, v, lr, beta1, beta2, eps, weight_decay, bias_corr):
+    return check(lib.tile_fused_adamw(stream_handle(stream), n, ptr(p), ptr(g), ptr(m), ptr(v), lr, beta1, beta2,
+                                      eps, weight_decay, ptr(bias_corr)))
+
+
+def tile_adamw_advance(stream, step, bias_corr, beta1, beta2):
+    return check(lib.tile_adamw_advance(stream_handle(stream), ptr(step), ptr(bias_corr), beta1, beta2))
+
+
+def tile_embedding_fwd(stream, rows, cols, ids, vocab, wte, ld_wte, wpe, ld_wpe, seq_len, pos_offset, out, ldo):
+    return check(lib.tile_embedding_fwd(stream_handle(stream), rows, cols, ptr(ids), vocab, ptr(wte), ld_wte,
+                                        ptr(wpe), ld_wpe, seq_len, pos_offset, ptr(out), ldo))
+
+
+def tile_embedding_index(stream, rows, ids, sorted_ids, perm):
+    return check(lib.tile_embedding_index(stream_handle(stream), rows, ptr(ids), ptr(sorted_ids), ptr(perm)))
+
+
+def tile_embedding_bwd(stream, phase, rows, cols, sorted_ids, perm, v_off, v_len, seq_len, dh, lddh, dst, ld_dst):
+    return check(lib.tile_embedding_bwd(stream_handle(stream), phase, rows, cols, ptr(sorted_ids), ptr(perm), v_off,
+                                        v_len, seq_len, ptr(dh), lddh, ptr(dst), ld_dst))
+
+
+def tile_reduce_rows(stream, rows, cols, X, ldx, out, beta, workspace):
+    return check(lib.tile_reduce_rows(stream_handle(stream), rows, cols, ptr(X), ldx, ptr(out), beta, ptr(workspace)))
+
+
+def tile_reduce_rows_workspace(rows, cols):
+    return lib.tile_reduce_rows_workspace(rows, cols)
+
+
+def tile_fill(stream, n, dst, value):
+    return check(lib.tile_fill(stream_handle(stream), n, ptr(dst), value))
+
+
+def tile_split_tokens(stream, batch, seq, tokens, ids, labels):
+    return check(lib.tile_split_tokens(stream_handle(stream), batch, seq, ptr(tokens), ptr(ids), ptr(labels)))

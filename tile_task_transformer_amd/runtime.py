@@ -1,0 +1,196 @@
+"""Tiled tensors, the task executor and the GPT2 step: thin object wrappers
+over the C ABI (tt_ctx_*, tt_tensor_*, tt_submit_*, tt_gpt2_*)."""
+from __future__ import annotations
+
+import ctypes as C
+import json
+from typing import Dict, List, Sequence
+
+import numpy as np
+
+from . import _lib as L
+from ._lib import check, lib
+
+
+class Context:
+    """Executor context: `device` = GPU ordinal, or L.TT_DEVICE_DRYRUN to
+    record tasks without a GPU."""
+
+    def __init__(self, device: int = 0, n_streams: int = 4, window: int = 0, device_budget: int = 0):
+        h = C.c_void_p()
+        check(lib.tt_ctx_create(device, n_streams, window, device_budget, C.byref(h)))
+        self.h = h
+        self.dryrun = device == L.TT_DEVICE_DRYRUN
+        self._tensors: List["Tensor"] = []
+
+    def close(self):
+        if self.h:
+            for t in self._tensors:
+                t.h = None  # destroyed with the context
+            check(lib.tt_ctx_destroy(self.h))
+            self.h = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def stream(self, i: int = 0) -> int:
+        s = C.c_void_p()
+        check(lib.tt_ctx_stream(self.h, i, C.byref(s)))
+        return s.value or 0
+
+    def record(self, on: bool = True):
+        check(lib.tt_ctx_record(self.h, int(on)))
+
+    def tensor(self, shape: Sequence[int], tile: Sequence[int], dtype: int = L.TT_F32,
+               home: int = L.TT_HOME_DEVICE) -> "Tensor":
+        t = Tensor(self, shape, tile, dtype, home)
+        self._tensors.append(t)
+        return t
+
+    def submit_nop(self, label: str, accesses):
+        """accesses: iterable of (Tensor, tile index tuple, mode)."""
+        acc = list(accesses)
+        arr = (L.tt_access * max(1, len(acc)))()
+        for i, (t, idx, mode) in enumerate(acc):
+            arr[i].tensor = t.h
+            for j, v in enumerate(idx):
+                arr[i].tile[j] = v
+            arr[i].mode = mode
+        check(lib.tt_submit_nop(self.h, label.encode(), arr, len(acc)))
+
+    def submit_gemm(self, transA, transB, alpha, A, ia, B, ib, beta, Cc, ic):
+        check(lib.tt_submit_gemm(self.h, transA, transB, alpha, A.h, L.i64_array(ia), B.h, L.i64_array(ib), beta,
+                                 Cc.h, L.i64_array(ic)))
+
+    def submit_fill(self, t, idx, value: float):
+        check(lib.tt_submit_fill(self.h, t.h, L.i64_array(idx), value))
+
+    def wait(self):
+        check(lib.tt_wait(self.h))
+
+    def dump_dag(self, path: str) -> List[dict]:
+        check(lib.tt_dump_dag(self.h, path.encode()))
+        with open(path) as f:
+            return [json.loads(line) for line in f if line.strip()]
+
+    def stats(self) -> Dict[str, float]:
+        s = L.tt_stats()
+        check(lib.tt_get_stats(self.h, C.byref(s)))
+        return {k: getattr(s, k) for k, _ in L.tt_stats._fields_}
+
+    def reset_stats(self):
+        check(lib.tt_reset_stats(self.h))
+
+
+class Tensor:
+    def __init__(self, ctx: Context, shape, tile, dtype=L.TT_F32, home=L.TT_HOME_DEVICE, handle=None):
+        self.ctx = ctx
+        self.shape = tuple(int(s) for s in shape)
+        self.tile = tuple(int(s) for s in tile)
+        self.dtype = dtype
+        if handle is None:
+            h = C.c_void_p()
+            check(lib.tt_tensor_create(ctx.h, len(self.shape), L.i64_array(self.shape), L.i64_array(self.tile),
+                                       dtype, home, C.byref(h)))
+            self.h = h
+        else:
+            self.h = handle
+
+    @property
+    def np_dtype(self):
+        return np.float32 if self.dtype == L.TT_F32 else np.int32
+
+    def grid(self):
+        g = L.i64_array([0] * L.TT_MAX_DIMS)
+        n = C.c_int64()
+        check(lib.tt_tensor_grid(self.h, g, C.byref(n)))
+        return tuple(g[i] for i in range(len(self.shape))), n.value
+
+    def nbytes(self) -> int:
+        return lib.tt_tensor_bytes(self.h)
+
+    def tile_ptr(self, idx):
+        p = C.c_void_p()
+        ext = L.i64_array([0] * L.TT_MAX_DIMS)
+        check(lib.tt_tensor_tile(self.h, L.i64_array(idx), C.byref(p), ext))
+        return p.value, tuple(ext[i] for i in range(len(self.shape)))
+
+    def copy_in(self, dense: np.ndarray):
+        a = np.ascontiguousarray(dense, dtype=self.np_dtype)
+        if a.size != int(np.prod(self.shape)):
+            raise ValueError(f"copy_in: {a.shape} does not match {self.shape}")
+        check(lib.tt_tensor_copy_in(self.h, a.ctypes.data))
+
+    def copy_out(self) -> np.ndarray:
+        a = np.empty(self.shape, dtype=self.np_dtype)
+        check(lib.tt_tensor_copy_out(self.h, a.ctypes.data))
+        return a
+
+    def destroy(self):
+        if self.h:
+            check(lib.tt_tensor_destroy(self.h))
+            self.h = None
+
+
+class GPT2:
+    """The GPT2 training step of libtiletask. `shape`/`tiles` are synth.GPT2Shape
+    / synth.Tiles-like objects (attribute access)."""
+
+    def __init__(self, ctx: Context, shape, tiles, param_home: int = L.TT_HOME_DEVICE, ln_eps: float = 1e-5):
+        self.ctx = ctx
+        self.shape = shape
+        cfg = L.tt_gpt2_config(shape.n_layer, shape.vocab, shape.n_embd, shape.n_head, shape.n_inner, shape.seq,
+                               shape.batch, ln_eps)
+        tl = L.tt_gpt2_tiles(tiles.batch, tiles.seq, tiles.embd, tiles.inner, tiles.head, tiles.vocab)
+        h = C.c_void_p()
+        check(lib.tt_gpt2_create(ctx.h, C.byref(cfg), C.byref(tl), param_home, C.byref(h)))
+        self.h = h
+        n = C.c_int()
+        check(lib.tt_gpt2_num_params(self.h, C.byref(n)))
+        self.n_params = n.value
+
+    def tensors(self, index: int):
+        """(param, grad, m, v) Tensor wrappers of parameter `index`."""
+        hs = [C.c_void_p() for _ in range(4)]
+        check(lib.tt_gpt2_param(self.h, index, *[C.byref(x) for x in hs]))
+        return [Tensor(self.ctx, (), (), L.TT_F32, handle=x) for x in hs]
+
+    def _wrap(self, index: int, which: int, shape) -> Tensor:
+        t = self.tensors(index)[which]
+        t.shape = tuple(shape)
+        return t
+
+    def set_params(self, params: Dict[str, np.ndarray], specs):
+        for i, (name, shp, _) in enumerate(specs):
+            self._wrap(i, 0, shp).copy_in(params[name])
+
+    def get(self, specs, which: int) -> Dict[str, np.ndarray]:
+        """which: 0 params, 1 grads, 2 first moments, 3 second moments."""
+        return {name: self._wrap(i, which, shp).copy_out() for i, (name, shp, _) in enumerate(specs)}
+
+    def step(self, tokens_dev, lr=3e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1, update=True):
+        if hasattr(tokens_dev, "device") and getattr(tokens_dev.device, "type", "") == "cuda":
+            # the executor's streams do not order after torch's: the token
+            # buffer must be complete before the step's first task reads it
+            import torch
+            torch.cuda.current_stream(tokens_dev.device).synchronize()
+        hp = L.tt_adamw_hparams(lr, beta1, beta2, eps, weight_decay)
+        check(lib.tt_gpt2_step(self.h, L.ptr(tokens_dev), C.byref(hp), int(update)))
+
+    def loss(self) -> float:
+        f = C.c_float()
+        check(lib.tt_gpt2_loss(self.h, C.byref(f)))
+        return f.value
+
+    def task_count(self) -> int:
+        n = C.c_int64()
+        check(lib.tt_gpt2_task_count(self.h, C.byref(n)))
+        return n.value
+
+    def close(self):
+        if self.h:
+            check(lib.tt_gpt2_destroy(self.h))
+            self.h = None
