@@ -361,6 +361,21 @@ int tt_wait(tt_ctx* ctx);
  * id, label, stream, deps and accesses (dry-run and real contexts). */
 int tt_dump_dag(tt_ctx* ctx, const char* path);
 
+/* Per-task GPU timing. Tasks whose label equals label_filter ("*" = every
+ * task, NULL = off) are bracketed by a pair of timing events on their
+ * stream; the durations are aggregated per label when the context drains.
+ * tt_profile_read waits, fills up to max_entries entries (one per label,
+ * *n_entries = number of labels seen) and clears the aggregate. Timing
+ * events add a little GPU time per bracketed task, so narrow filters are
+ * the ones to use inside a timed region. */
+typedef struct {
+    char label[32];
+    int64_t count;            /* launches timed                             */
+    double total_ms, min_ms, max_ms;
+} tt_profile_entry;
+int tt_ctx_profile(tt_ctx* ctx, const char* label_filter);
+int tt_profile_read(tt_ctx* ctx, tt_profile_entry* out, int max_entries, int* n_entries);
+
 typedef struct {
     int64_t tasks;            /* tasks submitted since creation / reset     */
     int64_t edges;            /* dependency edges inferred                  */

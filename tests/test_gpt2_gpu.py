@@ -4,12 +4,18 @@ Bar (fp32 path vs fp64 oracle, same seeded inputs):
   * loss: relative error <= 1e-4;
   * every gradient tensor: normwise relative error <= 1e-3 and
     max |g - g_ref| <= 1e-3 * max |g_ref|;
-  * every updated parameter: normwise relative error <= 1e-3;
   * AdamW itself: the GPU's updated parameters equal the oracle's AdamW fed
     with the GPU's own fp32 gradients, elementwise within 1e-3 relative with
-    an absolute floor of 1e-3 * lr (the first step moves each weight by
-    about lr * sign(g), so tiny gradients whose sign differs between fp32
-    and fp64 would otherwise fail spuriously).
+    an absolute floor of 1e-3 * lr;
+  * every updated parameter vs the full oracle step: normwise relative error
+    <= 1e-3 over the elements whose update direction the arithmetic decides,
+    and |p - p_ref| <= 2 lr (1 + 1e-3) everywhere.
+The first decoupled-Adam step moves each weight by about lr * sign(g). Where
+the fp64 gradient is below the gradient tolerance (1e-3 * max|g_ref| of its
+tensor) its sign is not fixed by fp32 arithmetic -- e.g. the key bias,
+whose exact gradient is zero because a per-query constant added to every
+score leaves the softmax unchanged -- so both results are valid there and
+only the step-size bound applies.
 """
 import numpy as np
 import pytest
@@ -50,12 +56,17 @@ def check_against_oracle(shape, gpu, params, tokens, w):
         assert np.abs(got - ref).max() <= 1e-3 * np.abs(ref).max() + 1e-30, name
     for name, ref in newp.items():
         got = gpu["params"][name].astype(np.float64)
-        assert normwise(got, ref) <= 1e-3, (name, normwise(got, ref))
         # AdamW fed with the GPU's own gradients
         p1, _, _ = og.adamw(np.asarray(params[name], np.float64), gpu["grads"][name].astype(np.float64), 0, 0, 1,
                             w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)
         err = np.abs(got - p1)
         assert (err <= 1e-3 * np.abs(p1) + 1e-3 * w.lr).all(), (name, err.max())
+        # against the full oracle step
+        assert np.abs(got - ref).max() <= 2 * w.lr * (1 + 1e-3) + 1e-6 * np.abs(ref).max(), name
+        g_ref = grads[name]
+        decided = np.abs(g_ref) > 1e-3 * np.abs(g_ref).max()
+        if decided.any():
+            assert normwise(got[decided], ref[decided]) <= 1e-3, (name, normwise(got[decided], ref[decided]))
     return loss
 
 

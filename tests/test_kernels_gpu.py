@@ -301,13 +301,15 @@ def test_fused_adamw(n):
     M, V = dev(np.zeros(n, np.float32)), dev(np.zeros(n, np.float32))
     step = torch.zeros(1, dtype=torch.int32, device="cuda")
     bc = empty((2,))
+    # the kernel receives its hyperparameters as fp32: feed the oracle the same values
+    b1, b2, lr, eps, wd = (float(np.float32(x)) for x in (0.9, 0.999, 3e-4, 1e-8, 0.1))
     rp, rm, rv = p.astype(np.float64), np.zeros(n), np.zeros(n)
     for t in (1, 2, 3):
-        tt.tile_adamw_advance(None, step, bc, 0.9, 0.999)
-        tt.tile_fused_adamw(None, n, P, G, M, V, 3e-4, 0.9, 0.999, 1e-8, 0.1, bc)
-        rp, rm, rv = og.adamw(rp, g.astype(np.float64), rm, rv, t, 3e-4, 0.9, 0.999, 1e-8, 0.1)
+        tt.tile_adamw_advance(None, step, bc, b1, b2)
+        tt.tile_fused_adamw(None, n, P, G, M, V, lr, b1, b2, eps, wd, bc)
+        rp, rm, rv = og.adamw(rp, g.astype(np.float64), rm, rv, t, lr, b1, b2, eps, wd)
     assert int(step.item()) == 3
-    assert_rel(host(bc), [1 - 0.9 ** 3, 1 - 0.999 ** 3], 1e-6)
+    assert_rel(host(bc), np.array([1 - b1 ** 3, 1 - b2 ** 3]), 1e-6)
     assert_rel(host(M), rm, 1e-5, 1e-12, "m")
     assert_rel(host(V), rv, 1e-5, 1e-20, "v")
     # parameter: abs floor well below one lr step

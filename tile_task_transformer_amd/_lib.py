@@ -16,7 +16,7 @@ LIB_PATH = os.environ.get("TILETASK_LIB", os.path.join(_HERE, "libtiletask.so"))
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"libtiletask.so not found at {LIB_PATH}: build it with "
-                      "`python -m tile_task_transformer_amd.build` (hipcc, gfx950)")
+                      "`python tile_task_transformer_amd/build.py` (hipcc, gfx950)")
 lib = C.CDLL(LIB_PATH)
 
 # ---- constants (mirror include/tiletask.h)
@@ -51,6 +51,11 @@ class tt_stats(C.Structure):
     _fields_ = [("tasks", C.c_int64), ("edges", C.c_int64), ("cross_stream_waits", C.c_int64),
                 ("events_recorded", C.c_int64), ("submit_seconds", C.c_double), ("h2d_bytes", C.c_int64),
                 ("d2h_bytes", C.c_int64), ("evictions", C.c_int64), ("prefetches", C.c_int64)]
+
+
+class tt_profile_entry(C.Structure):
+    _fields_ = [("label", C.c_char * 32), ("count", C.c_int64), ("total_ms", C.c_double), ("min_ms", C.c_double),
+                ("max_ms", C.c_double)]
 
 
 class tt_gpt2_config(C.Structure):
@@ -110,6 +115,8 @@ SIGNATURES = {
     "tt_wait": (I, [P]),
     "tt_dump_dag": (I, [P, C.c_char_p]),
     "tt_get_stats": (I, [P, C.POINTER(tt_stats)]),
+    "tt_ctx_profile": (I, [P, C.c_char_p]),
+    "tt_profile_read": (I, [P, C.POINTER(tt_profile_entry), I, C.POINTER(I)]),
     "tt_reset_stats": (I, [P]),
     "tt_gpt2_create": (I, [P, C.POINTER(tt_gpt2_config), C.POINTER(tt_gpt2_tiles), I, PP]),
     "tt_gpt2_destroy": (I, [P]),

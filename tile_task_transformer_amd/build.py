@@ -1,6 +1,6 @@
 """Builds libtiletask.so for gfx950 in-tree with hipcc.
 
-Usage: python -m tile_task_transformer_amd.build [--jobs N] [--debug]
+Usage: python tile_task_transformer_amd/build.py [--jobs N] [--debug]
 
 Each source under csrc/ compiles to an object (in parallel), then hipcc
 links the shared library next to this file. Every compile disables packed

@@ -277,7 +277,20 @@ int tt_ctx::flush() {
     li.seq = ++stream_seq[s];
     if (!dryrun && !latched) {
       int rc = make_resident(task, streams[s]);
+      const bool prof = prof_on && (prof_filter == "*" || prof_filter == task.label);
+      if (prof && rc == TT_OK) {
+        for (int k = 0; k < 2; ++k)
+          if (prof_used + k >= (int)prof_events.size()) {
+            hipEvent_t e;
+            TT_HIP_TRY(hipEventCreate(&e));
+            prof_events.push_back(e);
+          }
+        prof_pending.push_back({task.label, prof_used, prof_used + 1});
+        prof_used += 2;
+        TT_HIP_TRY(hipEventRecord(prof_events[prof_pending.back().ev0], streams[s]));
+      }
       if (rc == TT_OK && task.run) rc = task.run(streams[s], workspace.empty() ? nullptr : workspace[s]);
+      if (prof && rc == TT_OK) TT_HIP_TRY(hipEventRecord(prof_events[prof_pending.back().ev1], streams[s]));
       if (rc != TT_OK) {
         latched = rc;
         latched_msg = std::string(task.label) + ": " + tt_last_error();
@@ -315,6 +328,7 @@ int tt_ctx::wait_all() {
       }
     }
   }
+  if (!latched && !dryrun) prof_collect();
   // everything submitted so far has completed
   done_below = next_id;
   launched.clear();
@@ -327,6 +341,27 @@ int tt_ctx::wait_all() {
   }
   if (latched) return fail(latched, "%s", latched_msg.c_str());
   return rc;
+}
+
+int tt_ctx::prof_collect() {
+  for (auto& r : prof_pending) {
+    float ms = 0.f;
+    TT_HIP_TRY(hipEventElapsedTime(&ms, prof_events[r.ev0], prof_events[r.ev1]));
+    ProfAgg* a = nullptr;
+    for (auto& p : prof_agg)
+      if (p.first == r.label) a = &p.second;
+    if (!a) {
+      prof_agg.push_back({r.label, ProfAgg{}});
+      a = &prof_agg.back().second;
+    }
+    a->count++;
+    a->total += ms;
+    a->mn = std::min(a->mn, (double)ms);
+    a->mx = std::max(a->mx, (double)ms);
+  }
+  prof_pending.clear();
+  prof_used = 0;
+  return TT_OK;
 }
 
 // -------------------------------------------------------------------- C ABI
@@ -386,6 +421,36 @@ int tt_ctx_stream(tt_ctx* c, int i, void** stream) {
 int tt_ctx_record(tt_ctx* c, int on) {
   if (!c) return fail(TT_ERR_ARG, "tt_ctx_record: null");
   c->record = on != 0;
+  return TT_OK;
+}
+
+int tt_ctx_profile(tt_ctx* c, const char* label_filter) {
+  if (!c) return fail(TT_ERR_ARG, "tt_ctx_profile: null");
+  if (int rc = c->flush()) return rc;
+  c->prof_on = label_filter != nullptr;
+  c->prof_filter = label_filter ? label_filter : "";
+  return TT_OK;
+}
+
+int tt_profile_read(tt_ctx* c, tt_profile_entry* out, int max_entries, int* n_entries) {
+  clear_error();
+  if (!c || !n_entries || (max_entries > 0 && !out)) return fail(TT_ERR_ARG, "tt_profile_read: bad argument");
+  if (int rc = c->wait_all()) return rc;
+  int n = 0;
+  for (auto& p : c->prof_agg) {
+    if (n < max_entries) {
+      tt_profile_entry& e = out[n];
+      memset(&e, 0, sizeof(e));
+      snprintf(e.label, sizeof(e.label), "%s", p.first.c_str());
+      e.count = p.second.count;
+      e.total_ms = p.second.total;
+      e.min_ms = p.second.count ? p.second.mn : 0;
+      e.max_ms = p.second.mx;
+    }
+    ++n;
+  }
+  *n_entries = n;
+  c->prof_agg.clear();
   return TT_OK;
 }
 

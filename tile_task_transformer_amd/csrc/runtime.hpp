@@ -151,6 +151,23 @@ struct tt_ctx {
   int64_t copy_seq = 0;
   std::vector<hipEvent_t> copy_events; // index by copy seq % ring
 
+  // per-task GPU timing (tt_ctx_profile): event pairs around matching launches
+  bool prof_on = false;
+  std::string prof_filter;             // "*" = every task
+  struct ProfRec {
+    std::string label;
+    int ev0, ev1;
+  };
+  std::vector<ProfRec> prof_pending;
+  std::vector<hipEvent_t> prof_events;
+  int prof_used = 0;
+  struct ProfAgg {
+    int64_t count = 0;
+    double total = 0, mn = 1e30, mx = 0;
+  };
+  std::vector<std::pair<std::string, ProfAgg>> prof_agg;
+  int prof_collect();
+
   int64_t next_tensor_id = 0;
   std::vector<tt_tensor*> tensors;     // live tensors
   std::vector<tt::TaskRecord> records;

@@ -84,6 +84,18 @@ class Context:
     def reset_stats(self):
         check(lib.tt_reset_stats(self.h))
 
+    def profile(self, label_filter):
+        """Time tasks with this label ("*" = all, None = off) with event pairs."""
+        check(lib.tt_ctx_profile(self.h, None if label_filter is None else label_filter.encode()))
+
+    def profile_take(self) -> Dict[str, dict]:
+        """Wait, return {label: {count, total_ms, min_ms, max_ms}} and clear."""
+        buf = (L.tt_profile_entry * 256)()
+        n = C.c_int()
+        check(lib.tt_profile_read(self.h, buf, 256, C.byref(n)))
+        return {buf[i].label.decode(): dict(count=buf[i].count, total_ms=buf[i].total_ms, min_ms=buf[i].min_ms,
+                                            max_ms=buf[i].max_ms) for i in range(min(n.value, 256))}
+
 
 class Tensor:
     def __init__(self, ctx: Context, shape, tile, dtype=L.TT_F32, home=L.TT_HOME_DEVICE, handle=None):
