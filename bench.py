@@ -57,6 +57,111 @@ def gemm_launch_flops(label, s, t) -> float:
     return 2.0 * m * n * k
 
 
+GEMM_SHAPES = {  # label -> (transA, transB, m, n, k, epilogue, beta) in tile terms
+    "qkv": lambda r, e, i, h, v: (0, 0, r, h, e, 1, 0.0), "attn_proj": lambda r, e, i, h, v: (0, 0, r, e, h, 3, 0.0),
+    "fc": lambda r, e, i, h, v: (0, 0, r, i, e, 5, 0.0), "mlp_proj": lambda r, e, i, h, v: (0, 0, r, e, i, 3, 0.0),
+    "head": lambda r, e, i, h, v: (0, 1, r, v, e, 0, 0.0), "head_dw": lambda r, e, i, h, v: (1, 0, v, e, r, 0, 1.0),
+    "head_dx": lambda r, e, i, h, v: (0, 0, r, e, v, 0, 1.0),
+    "mlp_proj_dw": lambda r, e, i, h, v: (1, 0, i, e, r, 0, 0.0),
+    "mlp_proj_dx": lambda r, e, i, h, v: (0, 1, r, i, e, 8, 0.0),
+    "fc_dw": lambda r, e, i, h, v: (1, 0, e, i, r, 0, 0.0), "fc_dx": lambda r, e, i, h, v: (0, 1, r, e, i, 0, 0.0),
+    "attn_proj_dw": lambda r, e, i, h, v: (1, 0, h, e, r, 0, 0.0),
+    "attn_proj_dx": lambda r, e, i, h, v: (0, 1, r, h, e, 0, 0.0),
+    "qkv_dw": lambda r, e, i, h, v: (1, 0, e, h, r, 0, 0.0), "qkv_dx": lambda r, e, i, h, v: (0, 1, r, e, h, 0, 1.0),
+}
+
+
+def tile_classes(w, reps=20):
+    """Each tile-op class of the workload, launched alone on one stream at its
+    task shape; HIP-event time per launch against its roofline."""
+    import math
+
+    import torch
+
+    import tile_task_transformer_amd as tt
+    s, t = w.shape, w.tiles
+    r = t.batch * t.seq
+    e, i, v = min(t.embd, s.n_embd), min(t.inner, s.n_inner), min(t.vocab, s.vocab)
+    hd = s.n_embd // s.n_head
+    h = t.head * hd
+    st = torch.cuda.current_stream()
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    rnd = lambda *shape: torch.randn(*shape, device="cuda", generator=gen)  # noqa: E731
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        for _ in range(reps):
+            fn()
+        b.record(st)
+        b.synchronize()
+        return a.elapsed_time(b) / reps
+
+    out = {}
+    for label, f in GEMM_SHAPES.items():
+        ta, tb, m, n, k, epi, beta = f(r, e, i, h, v)
+        A = rnd(k, m) if ta else rnd(m, k)
+        B = rnd(n, k) if tb else rnd(k, n)
+        C, aux, bias = rnd(m, n), rnd(m, n), rnd(n)
+        res = rnd(m, n) if epi & 2 else None
+        nws = tt.tile_gemm_workspace(m, n, k)
+        ws = torch.empty(max(nws // 4, 1), device="cuda")
+        ms = timed(lambda: tt.tile_gemm_ws(st, ta, tb, m, n, k, 1.0, A, A.shape[1], B, B.shape[1], beta, C, n, epi,
+                                           bias, res, n if res is not None else 0, aux, n, ws, nws))
+        tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+        out[label] = {"bound": "mfma", "shape": [m, n, k, ta, tb], "us": round(ms * 1e3, 1),
+                      "achieved": round(tf, 2), "unit": "TFLOP/s", "frac": round(tf / MFMA_FP32_PEAK, 4)}
+    # attention (per (batch tile, head tile) pair of the workload's seq tile)
+    Q, K, V = rnd(t.batch, t.seq, t.head, hd), rnd(t.batch, t.seq, t.head, hd), rnd(t.batch, t.seq, t.head, hd)
+    O, dO = torch.empty_like(Q), rnd(t.batch, t.seq, t.head, hd)
+    lse, Dv = torch.empty(t.batch * t.head * t.seq, device="cuda"), torch.empty(t.batch * t.head * t.seq, device="cuda")
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(Q), torch.empty_like(Q)
+    sc = 1 / math.sqrt(hd)
+    fl = 2 * 2 * t.batch * t.head * hd * (t.seq * (t.seq + 1) // 2)
+    ms = timed(lambda: tt.tile_attention_fwd(st, t.batch, t.head, t.seq, t.seq, hd, 0, 0, Q, K, V, O, None, lse, 1, 1,
+                                             sc))
+    out["attn_fwd"] = {"bound": "mfma", "us": round(ms * 1e3, 1), "achieved": round(fl / ms / 1e9, 2),
+                       "unit": "TFLOP/s (model)", "frac": round(fl / ms / 1e9 / MFMA_FP32_PEAK, 4)}
+    ms = timed(lambda: tt.tile_attention_bwd(st, tt.TT_ATT_GRAD, t.batch, t.head, t.seq, t.seq, hd, 0, 0, Q, K, V,
+                                             None, dO, lse, Dv, dQ, dK, dV, 0, 0, sc))
+    out["attn_bwd"] = {"bound": "mfma", "us": round(ms * 1e3, 1), "achieved": round(2.5 * fl / ms / 1e9, 2),
+                       "unit": "TFLOP/s (model)", "frac": round(2.5 * fl / ms / 1e9 / MFMA_FP32_PEAK, 4)}
+
+    def hbm(label, nbytes, fn):
+        ms = timed(fn)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[label] = {"bound": "hbm", "us": round(ms * 1e3, 1), "bytes": nbytes, "achieved": round(gbs, 1),
+                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK, 4)}
+
+    x, y, g_, b_ = rnd(r, e), torch.empty(r, e, device="cuda"), rnd(e), rnd(e)
+    stats = torch.empty(r, 2, device="cuda")
+    hbm("ln_fwd", 8 * r * e, lambda: tt.tile_layernorm_fwd(st, tt.TT_LN_FUSED, r, e, x, e, g_, b_, None, 0, 0, stats,
+                                                           y, e, 1e-5))
+    dx, dg, db = rnd(r, e), torch.zeros(e, device="cuda"), torch.zeros(e, device="cuda")
+    lws = torch.empty(tt.tile_layernorm_bwd_workspace(r, e) // 4 + 1, device="cuda")
+    hbm("ln_bwd", 16 * r * e, lambda: tt.tile_layernorm_bwd(st, tt.TT_LN_FUSED, r, e, e, y, e, x, e, g_, stats, None,
+                                                            0, 0, dx, e, 1, dg, db, lws))
+    z = rnd(r, v)
+    lab = torch.randint(0, v, (r,), device="cuda", dtype=torch.int32)
+    parts = torch.empty(r, 3, device="cuda")
+    hbm("ce_stats", 4 * r * v, lambda: tt.tile_softmax(st, tt.TT_SM_STATS, r, v, 0, 0, 1.0, 0, z, v, lab, parts, 0, 0,
+                                                       None, None, None, 0, 1.0))
+    lse_r = torch.zeros(r, device="cuda") + 10.0
+    hbm("ce_grad", 8 * r * v, lambda: tt.tile_xentropy(st, tt.TT_XE_GRAD, r, v, 0, lab, z, v, lse_r, None, None, 0,
+                                                       1.0 / r))
+    n_ad = i * e
+    p, gr, m_, v_ = rnd(n_ad), rnd(n_ad), torch.zeros(n_ad, device="cuda"), torch.zeros(n_ad, device="cuda")
+    bc = torch.tensor([0.1, 0.001], device="cuda")
+    hbm("adamw", 28 * n_ad, lambda: tt.tile_fused_adamw(st, n_ad, p, gr, m_, v_, 3e-4, 0.9, 0.999, 1e-8, 0.1, bc))
+    xr = rnd(r, i)
+    outc = torch.zeros(i, device="cuda")
+    rws = torch.empty(tt.tile_reduce_rows_workspace(r, i) // 4 + 1, device="cuda")
+    hbm("colsum", 4 * r * i, lambda: tt.tile_reduce_rows(st, r, i, xr, i, outc, 1, rws))
+    return out
+
+
 def cpu_baseline(w, params, tokens):
     """The fp64 oracle on the host, one sequence of the batch (bounded sample)."""
     import numpy as np
@@ -85,6 +190,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", default=os.path.join("gpurun_out", "bench_breakdown.json"),
                     help="per-task-class GPU times of one extra profiled step ('' = skip)")
+    ap.add_argument("--tile-classes", default="",
+                    help="instead of the step: time each tile-op class alone and write this JSON file")
     a = ap.parse_args(argv)
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
@@ -97,6 +204,15 @@ def main(argv=None):
     from tile_task_transformer_amd.runtime import Context, GPT2
 
     w = synth.WORKLOADS[a.workload]
+    if a.tile_classes:
+        res = tile_classes(w)
+        os.makedirs(os.path.dirname(a.tile_classes) or ".", exist_ok=True)
+        with open(a.tile_classes, "w") as f:
+            json.dump(res, f, indent=1)
+        for k, v in res.items():
+            print(f"{k:14s} {v['us']:9.1f} us  {v['achieved']:8.1f} {v['unit']:16s} {100 * v['frac']:5.1f}%",
+                  file=sys.stderr)
+        return 0
     s, t = w.shape, w.tiles
     specs = synth.param_specs(s)
     params = synth.init_params(s, seed=0)

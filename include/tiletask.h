@@ -88,6 +88,18 @@ int tile_gemm(void* stream, int transA, int transB, int64_t m, int64_t n, int64_
               float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
               float beta, float* C, int64_t ldc, int epilogue, const float* bias,
               const float* res, int64_t ldr, float* aux, int64_t ldaux);
+/* tile_gemm with a device workspace (caller-owned, not used concurrently by
+ * another launch). When C has too few 128x128 blocks to fill the GPU and K
+ * is long, the K range is split over workgroups that write partial sums to
+ * the workspace; a second kernel adds them in a fixed order (same result
+ * on every run). tile_gemm_workspace(m, n, k) is the size that enables the
+ * full split; smaller workspaces split less (0 bytes = no split). */
+int tile_gemm_ws(void* stream, int transA, int transB, int64_t m, int64_t n, int64_t k,
+                 float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
+                 float beta, float* C, int64_t ldc, int epilogue, const float* bias,
+                 const float* res, int64_t ldr, float* aux, int64_t ldaux,
+                 void* workspace, size_t workspace_bytes);
+size_t tile_gemm_workspace(int64_t m, int64_t n, int64_t k);
 
 /* tile_layernorm_fwd -- layer norm over the embedding axis, split into
  * feature tiles (layer list: pith.science review, "What carries the

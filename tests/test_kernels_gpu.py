@@ -43,6 +43,31 @@ def test_gemm_parity(ta, tb, m, n, k):
     assert_close_bound(host(C), ref, bound + 4 * EPS32 * np.abs(ref) + 1e-30, f"gemm {ta}{tb} {m}x{n}x{k}")
 
 
+@pytest.mark.parametrize("ta,tb,m,n,k", [(1, 0, 768, 768, 4096), (1, 0, 700, 300, 5000), (0, 1, 1536, 768, 4096),
+                                         (0, 0, 1000, 200, 2049), (1, 1, 3072, 768, 4096)])
+def test_gemm_split_k_workspace(ta, tb, m, n, k):
+    """Tall-K shapes take the split-K path when given a workspace: same result
+    within the fp32 bound, bitwise equal across runs, epilogue applied once."""
+    seed = m + n + k
+    a = synth.rand_normal((k, m) if ta else (m, k), seed)
+    b = synth.rand_normal((n, k) if tb else (k, n), seed + 1)
+    c0 = synth.rand_normal((m, n), seed + 2)
+    bias = synth.rand_normal((n,), seed + 3)
+    need = tt.tile_gemm_workspace(m, n, k)
+    assert need > 0, "shape expected to split"
+    ws = torch.empty(need // 4, device="cuda")
+    outs = []
+    for _ in range(2):
+        C = dev(c0)
+        tt.tile_gemm_ws(None, ta, tb, m, n, k, 1.0, dev(a), a.shape[1], dev(b), b.shape[1], 1.0, C, n,
+                        tt.TT_EPI_BIAS, dev(bias), None, 0, None, 0, ws, need)
+        outs.append(C)
+    ref = _op(a.astype(np.float64), ta) @ _op(b.astype(np.float64), tb) + c0 + bias
+    bound = (np.abs(_op(a, ta)).astype(np.float64) @ np.abs(_op(b, tb)).astype(np.float64)) * (k + 2) * EPS32
+    assert_close_bound(host(outs[0]), ref, bound + 4 * EPS32 * np.abs(ref), "split-K gemm")
+    assert torch.equal(outs[0], outs[1])
+
+
 @pytest.mark.parametrize("ld_pad", [0, 1, 4])
 def test_gemm_leading_dims_and_views(ld_pad):
     m, n, k = 96, 72, 40

@@ -7,29 +7,42 @@
 //   * a workgroup of 256 threads (4 wave64s, 2x2) computes a BM x BN block of
 //     C; each wave owns a (BM/2) x (BN/2) sub-block made of 32x32 MFMA tiles
 //     whose fp32 accumulators stay in registers for the whole K loop;
-//   * K advances in steps of BK through two LDS buffers: the next step's
+//   * K advances in steps of BK = 32 through two LDS buffers: the next step's
 //     global loads are issued before the current step's MFMAs and written to
-//     the other buffer afterwards, so one barrier per step suffices;
+//     the other buffer afterwards, so one barrier per step suffices; 32
+//     floats of K are 128 bytes, one full cache line per row of a
+//     K-contiguous operand;
 //   * each operand is staged in LDS in the orientation it has in HBM, so the
 //     global->LDS path is always 16-byte vector loads/stores:
 //       K-contiguous operands (A, or B^T)  -> LDS [rows][BK + 4]
-//       row-contiguous operands (A^T, B)   -> LDS [BK][rows + 4]
+//       row-contiguous operands (A^T, B)   -> LDS [BK][rows + 8]
+//     (paddings chosen so 16-byte reads of the first and 4-byte reads of
+//     the second are free of bank conflicts);
 //   * the summation order inside each group of 8 k values is permuted so a
 //     lane's 4 consecutive MFMA steps use 4 consecutive k of its half-wave:
 //     k = 8*kb + 4*(lane/32) + s. A K-contiguous operand then feeds 4 MFMAs
 //     from one 16-byte LDS read;
 //   * blockIdx is remapped so consecutive C blocks land on the same XCD
 //     (workgroups are dispatched round-robin over the 8 XCDs, each with its
-//     own L2), then grouped along M for L2 reuse of the B panel.
+//     own L2), then grouped along M for L2 reuse of the B panel;
+//   * split-K: when C has too few blocks to fill 256 CUs and K is long (the
+//     weight-gradient GEMMs, K = tokens), S workgroups share a C block, each
+//     reducing a K range into its own slice of a workspace; a second kernel
+//     adds the slices in slice order and applies the epilogue (deterministic:
+//     no atomics).
 // Ragged M, N, K are handled by zero-filling out-of-range loads and
 // predicating stores; leading dimensions that are not multiples of 4 (or
 // unaligned pointers) select a scalar-load instantiation.
+#include <cstdlib>
+
 #include "common.hpp"
 
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kSplitAlign = 32;  // split-K chunks are multiples of every BK used
 
 struct GemmArgs {
   int m, n, k;
@@ -44,6 +57,9 @@ struct GemmArgs {
   int64_t ldr;
   float* aux;
   int64_t ldaux;
+  float* ws;       // split-K partials [splits][m][n], or null
+  int splits;      // K ranges (1 = no split)
+  int kchunk;      // K per split (multiple of kSplitAlign)
 };
 
 __device__ __forceinline__ float gelu_tanh(float u) {
@@ -59,11 +75,26 @@ __device__ __forceinline__ float gelu_tanh_grad(float u) {
   return 0.5f * (1.f + t) + 0.5f * u * (1.f - t * t) * c * (1.f + 3.f * 0.044715f * u * u);
 }
 
-// Loads a float4 of an operand at (r, c) of a matrix with `rows` x `cols`
-// valid elements (row-major, leading dimension ld), zero-filling outside.
+// acc (already alpha-scaled) -> C, with beta source, bias, residual, GELU
+__device__ __forceinline__ void epilogue_store(const GemmArgs& g, int row, int col, float v) {
+  const bool gelu = g.epi & TT_EPI_GELU;
+  if (g.beta != 0.f)
+    v += g.beta * (gelu ? g.aux[(int64_t)row * g.ldaux + col] : g.C[(int64_t)row * g.ldc + col]);
+  if (g.epi & TT_EPI_BIAS) v += g.bias[col];
+  if (g.epi & TT_EPI_RES) v += g.res[(int64_t)row * g.ldr + col];
+  if (gelu) {
+    g.aux[(int64_t)row * g.ldaux + col] = v;
+    v = gelu_tanh(v);
+  } else if (g.epi & TT_EPI_GELU_BWD) {
+    v *= gelu_tanh_grad(g.aux[(int64_t)row * g.ldaux + col]);
+  }
+  g.C[(int64_t)row * g.ldc + col] = v;
+}
+
+// float4 of an operand at (r, c) of a `rows` x `cols` row-major matrix with
+// leading dimension ld; zero outside.
 template <bool VEC>
-__device__ __forceinline__ f32x4 load4(const float* __restrict__ p, int64_t ld, int r, int c, int rows,
-                                       int cols) {
+__device__ __forceinline__ f32x4 load4(const float* __restrict__ p, int64_t ld, int r, int c, int rows, int cols) {
   f32x4 v = {0.f, 0.f, 0.f, 0.f};
   if (r >= rows) return v;
   const float* q = p + (int64_t)r * ld + c;
@@ -74,17 +105,15 @@ __device__ __forceinline__ f32x4 load4(const float* __restrict__ p, int64_t ld, 
   return v;
 }
 
-template <int BM, int BN, int BK, bool TA, bool TB, bool VA, bool VB>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
+template <int BM, int BN, int BK, bool TA, bool TB, bool VA, bool VB, bool SPLIT>
+__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   constexpr int WM = BM / 2, WN = BN / 2;      // wave sub-block
   constexpr int FM = WM / 32, FN = WN / 32;    // 32x32 MFMA tiles per wave
-  // LDS geometry per operand: "KC" = [rows][BK+4], "RC" = [BK][rows+4]
   constexpr int A_KC = !TA, B_KC = TB;
-  constexpr int A_LD = A_KC ? BK + 4 : BM + 4;
-  constexpr int B_LD = B_KC ? BK + 4 : BN + 4;
+  constexpr int A_LD = A_KC ? BK + 4 : BM + 8;
+  constexpr int B_LD = B_KC ? BK + 4 : BN + 8;
   constexpr int A_SZ = A_KC ? BM * A_LD : BK * A_LD;
   constexpr int B_SZ = B_KC ? BN * B_LD : BK * B_LD;
-  // float4 slots per operand tile and per thread
   constexpr int A_V4 = BM * BK / 4, B_V4 = BN * BK / 4;
   constexpr int A_PT = A_V4 / 256, B_PT = B_V4 / 256;
   static_assert(A_V4 % 256 == 0 && B_V4 % 256 == 0, "tile must split evenly over 256 threads");
@@ -96,14 +125,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   const int wm = wave >> 1, wn = wave & 1;
   const int half = lane >> 5, l32 = lane & 31;
 
-  // ---- block -> C tile: XCD-contiguous, then grouped along M
+  // ---- block -> (C tile, K range): XCD-contiguous, then grouped along M
   const int grid_m = (g.m + BM - 1) / BM, grid_n = (g.n + BN - 1) / BN;
-  const int nb = grid_m * grid_n;
+  const int ntile = grid_m * grid_n;
+  const int nb = ntile * g.splits;
   int b = blockIdx.x;
   {
     const int per = nb / 8, rem = nb % 8, x = b % 8;
     b = x * per + min(x, rem) + b / 8;
   }
+  const int split = b / ntile;
+  b -= split * ntile;
   constexpr int GROUP = 8;
   const int in_group = GROUP * grid_n;
   const int first_m = (b / in_group) * GROUP;
@@ -111,30 +143,31 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   const int tm = first_m + (b % in_group) % gsz;
   const int tn = (b % in_group) / gsz;
   const int m0 = tm * BM, n0 = tn * BN;
+  const int kbeg = split * g.kchunk;
+  const int kend = min(g.k, kbeg + g.kchunk);
 
-  // ---- global -> register staging
   f32x4 ra[A_PT], rb[B_PT];
   auto gload = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < A_PT; ++i) {
-      int idx = tid + 256 * i;
-      if (A_KC) {  // A[m][k]: rows m, 4-wide along k
-        int r = idx / (BK / 4), c = (idx % (BK / 4)) * 4;
-        ra[i] = load4<VA>(g.A, g.lda, m0 + r, k0 + c, g.m, g.k);
-      } else {     // A^T stored [k][m]: rows k, 4-wide along m
-        int r = idx / (BM / 4), c = (idx % (BM / 4)) * 4;
-        ra[i] = load4<VA>(g.A, g.lda, k0 + r, m0 + c, g.k, g.m);
+      const int idx = tid + 256 * i;
+      if (A_KC) {
+        const int r = idx / (BK / 4), c = (idx % (BK / 4)) * 4;
+        ra[i] = load4<VA>(g.A, g.lda, m0 + r, k0 + c, g.m, kend);
+      } else {
+        const int r = idx / (BM / 4), c = (idx % (BM / 4)) * 4;
+        ra[i] = load4<VA>(g.A, g.lda, k0 + r, m0 + c, kend, g.m);
       }
     }
 #pragma unroll
     for (int i = 0; i < B_PT; ++i) {
-      int idx = tid + 256 * i;
-      if (B_KC) {  // B^T stored [n][k]
-        int r = idx / (BK / 4), c = (idx % (BK / 4)) * 4;
-        rb[i] = load4<VB>(g.B, g.ldb, n0 + r, k0 + c, g.n, g.k);
-      } else {     // B stored [k][n]
-        int r = idx / (BN / 4), c = (idx % (BN / 4)) * 4;
-        rb[i] = load4<VB>(g.B, g.ldb, k0 + r, n0 + c, g.k, g.n);
+      const int idx = tid + 256 * i;
+      if (B_KC) {
+        const int r = idx / (BK / 4), c = (idx % (BK / 4)) * 4;
+        rb[i] = load4<VB>(g.B, g.ldb, n0 + r, k0 + c, g.n, kend);
+      } else {
+        const int r = idx / (BN / 4), c = (idx % (BN / 4)) * 4;
+        rb[i] = load4<VB>(g.B, g.ldb, k0 + r, n0 + c, kend, g.n);
       }
     }
   };
@@ -143,16 +176,16 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     float* Bs = As + A_SZ;
 #pragma unroll
     for (int i = 0; i < A_PT; ++i) {
-      int idx = tid + 256 * i;
-      int r = A_KC ? idx / (BK / 4) : idx / (BM / 4);
-      int c = A_KC ? (idx % (BK / 4)) * 4 : (idx % (BM / 4)) * 4;
+      const int idx = tid + 256 * i;
+      const int r = A_KC ? idx / (BK / 4) : idx / (BM / 4);
+      const int c = A_KC ? (idx % (BK / 4)) * 4 : (idx % (BM / 4)) * 4;
       *reinterpret_cast<f32x4*>(As + r * A_LD + c) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < B_PT; ++i) {
-      int idx = tid + 256 * i;
-      int r = B_KC ? idx / (BK / 4) : idx / (BN / 4);
-      int c = B_KC ? (idx % (BK / 4)) * 4 : (idx % (BN / 4)) * 4;
+      const int idx = tid + 256 * i;
+      const int r = B_KC ? idx / (BK / 4) : idx / (BN / 4);
+      const int c = B_KC ? (idx % (BK / 4)) * 4 : (idx % (BN / 4)) * 4;
       *reinterpret_cast<f32x4*>(Bs + r * B_LD + c) = rb[i];
     }
   };
@@ -165,18 +198,20 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = (g.k + BK - 1) / BK;
-  gload(0);
-  sstore(0);
+  const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+  if (nk > 0) {
+    gload(kbeg);
+    sstore(0);
+  }
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+    if (kt + 1 < nk) gload(kbeg + (kt + 1) * BK);
     const float* As = lds + cur * (A_SZ + B_SZ);
     const float* Bs = As + A_SZ;
 #pragma unroll
     for (int kb = 0; kb < BK / 8; ++kb) {
-      const int kk = kb * 8 + half * 4;   // this half-wave's 4 consecutive k
+      const int kk = kb * 8 + half * 4;
       f32x4 fa[FM], fb[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
@@ -212,63 +247,138 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 
   // ---- epilogue: accumulator register r of lane l holds
   //      row 8*(r/4) + 4*(l/32) + (r%4), column l%32 of its 32x32 tile
-  const bool gelu = g.epi & TT_EPI_GELU, gelu_bwd = g.epi & TT_EPI_GELU_BWD;
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int col = n0 + wn * WN + j * 32 + l32;
       if (col >= g.n) continue;
-      const float bcol = (g.epi & TT_EPI_BIAS) ? g.bias[col] : 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
         if (row >= g.m) continue;
-        float v = g.alpha * acc[i][j][r];
-        if (g.beta != 0.f) {
-          const float src = gelu ? g.aux[(int64_t)row * g.ldaux + col] : g.C[(int64_t)row * g.ldc + col];
-          v += g.beta * src;
-        }
-        v += bcol;
-        if (g.epi & TT_EPI_RES) v += g.res[(int64_t)row * g.ldr + col];
-        if (gelu) {
-          g.aux[(int64_t)row * g.ldaux + col] = v;
-          v = gelu_tanh(v);
-        } else if (gelu_bwd) {
-          v *= gelu_tanh_grad(g.aux[(int64_t)row * g.ldaux + col]);
-        }
-        g.C[(int64_t)row * g.ldc + col] = v;
+        if (SPLIT)
+          g.ws[((int64_t)split * g.m + row) * g.n + col] = acc[i][j][r];
+        else
+          epilogue_store(g, row, col, g.alpha * acc[i][j][r]);
       }
     }
 }
 
-template <int BM, int BN, int BK, bool TA, bool TB>
-int launch_v(const GemmArgs& g, bool va, bool vb, hipStream_t s) {
-  const int nb = ((g.m + BM - 1) / BM) * ((g.n + BN - 1) / BN);
+// Sum of the split-K slices in slice order, then the epilogue.
+__global__ __launch_bounds__(256) void gemm_split_finish(GemmArgs g) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const int64_t mn = (int64_t)g.m * g.n;
+  if (i >= mn) return;
+  float s = 0.f;
+  for (int z = 0; z < g.splits; ++z) s += g.ws[z * mn + i];
+  epilogue_store(g, (int)(i / g.n), (int)(i % g.n), g.alpha * s);
+}
+
+template <int BM, int BN, int BK, bool TA, bool TB, bool SPLIT>
+void launch_v(const GemmArgs& g, bool va, bool vb, hipStream_t s) {
+  const int nb = ((g.m + BM - 1) / BM) * ((g.n + BN - 1) / BN) * g.splits;
   dim3 grid(nb), block(256);
-  if (va && vb) hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, TA, TB, true, true>), grid, block, 0, s, g);
-  else if (va) hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, TA, TB, true, false>), grid, block, 0, s, g);
-  else if (vb) hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, TA, TB, false, true>), grid, block, 0, s, g);
-  else hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, TA, TB, false, false>), grid, block, 0, s, g);
-  return tt::launch_status("tile_gemm");
+  if (va && vb) hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, TA, TB, true, true, SPLIT>), grid, block, 0, s, g);
+  else if (va) hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, TA, TB, true, false, SPLIT>), grid, block, 0, s, g);
+  else if (vb) hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, TA, TB, false, true, SPLIT>), grid, block, 0, s, g);
+  else hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, TA, TB, false, false, SPLIT>), grid, block, 0, s, g);
+}
+
+struct Plan {
+  int bm, bn, bk, splits, kchunk;
+};
+
+// Tuning override "bm,bn,bk,splits" (e.g. "128,128,16,1") read once from
+// TT_GEMM_PLAN; only configurations this file instantiates are accepted.
+bool plan_override(Plan* p, int64_t k) {
+  static int parsed = 0;
+  static Plan forced{0, 0, 0, 1, 0};
+  if (!parsed) {
+    parsed = -1;
+    if (const char* e = getenv("TT_GEMM_PLAN")) {
+      Plan q{0, 0, 0, 1, 0};
+      if (sscanf(e, "%d,%d,%d,%d", &q.bm, &q.bn, &q.bk, &q.splits) == 4 && (q.bk == 16 || q.bk == 32) &&
+          q.splits >= 1 && ((q.bm == 128 && (q.bn == 128 || q.bn == 64)) || (q.bm == 64 && q.bn == 64))) {
+        forced = q;
+        parsed = 1;
+      }
+    }
+  }
+  if (parsed != 1) return false;
+  *p = forced;
+  int64_t chunk = (k + p->splits - 1) / p->splits;
+  chunk = (chunk + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
+  p->kchunk = (int)std::max<int64_t>(chunk, kSplitAlign);
+  p->splits = (int)std::max<int64_t>(1, (k + p->kchunk - 1) / p->kchunk);
+  if (p->splits == 1) p->kchunk = (int)k;
+  return true;
+}
+
+// Block shape and split count: fill at least ~2 workgroups per CU.
+Plan plan_for(int64_t m, int64_t n, int64_t k, size_t ws_bytes) {
+  const int64_t want = 512;
+  auto blocks = [&](int bm, int bn) { return ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
+  // Choices measured per tile-op class on MI355X (isolated launches): 128x128
+  // with BK 16 when it gives >= 2 blocks per CU; split-K only when C is small
+  // (<= 144 such blocks) and K long; otherwise 64x64 blocks, whose larger
+  // block count beats the bigger tile's reuse at these sizes.
+  Plan p{128, 128, 16, 1, (int)k};
+  if (plan_override(&p, k)) return p;
+  if (blocks(128, 128) >= want) return p;
+  const int64_t b128 = blocks(128, 128);
+  if (k >= 2048 && b128 <= 144 && ws_bytes > 0) {
+    int s = (int)std::min<int64_t>((want + b128 - 1) / b128, k / 512);
+    while (s > 1 && (size_t)s * m * n * sizeof(float) > ws_bytes) --s;
+    if (s > 1) {
+      int64_t chunk = (k + s - 1) / s;
+      chunk = (chunk + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
+      s = (int)((k + chunk - 1) / chunk);
+      if (s > 1) return Plan{128, 128, 32, s, (int)chunk};
+    }
+  }
+  return Plan{64, 64, 32, 1, (int)k};
 }
 
 template <bool TA, bool TB>
-int launch_t(const GemmArgs& g, bool va, bool vb, hipStream_t s) {
-  // 128x128 blocks when they give at least ~2 blocks per CU, else 64x64
-  const int64_t big = ((int64_t)(g.m + 127) / 128) * ((g.n + 127) / 128);
-  if (big >= 512) return launch_v<128, 128, 16, TA, TB>(g, va, vb, s);
-  return launch_v<64, 64, 16, TA, TB>(g, va, vb, s);
+int launch_t(GemmArgs g, bool va, bool vb, size_t ws_bytes, hipStream_t s) {
+  const Plan p = plan_for(g.m, g.n, g.k, ws_bytes);
+  g.splits = p.splits;
+  g.kchunk = p.kchunk;
+  if (p.splits > 1) {
+    if (p.bk == 16) launch_v<128, 128, 16, TA, TB, true>(g, va, vb, s);
+    else launch_v<128, 128, 32, TA, TB, true>(g, va, vb, s);
+    if (int rc = tt::launch_status("tile_gemm(split)")) return rc;
+    const int64_t mn = (int64_t)g.m * g.n;
+    hipLaunchKernelGGL(gemm_split_finish, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, s, g);
+    return tt::launch_status("tile_gemm(split finish)");
+  }
+  if (p.bk == 16) {
+    if (p.bm == 128 && p.bn == 128) launch_v<128, 128, 16, TA, TB, false>(g, va, vb, s);
+    else if (p.bm == 128) launch_v<128, 64, 16, TA, TB, false>(g, va, vb, s);
+    else launch_v<64, 64, 16, TA, TB, false>(g, va, vb, s);
+  } else {
+    if (p.bm == 128 && p.bn == 128) launch_v<128, 128, 32, TA, TB, false>(g, va, vb, s);
+    else if (p.bm == 128) launch_v<128, 64, 32, TA, TB, false>(g, va, vb, s);
+    else launch_v<64, 64, 32, TA, TB, false>(g, va, vb, s);
+  }
+  return tt::launch_status("tile_gemm");
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 }  // namespace
 
-extern "C" int tile_gemm(void* stream, int transA, int transB, int64_t m, int64_t n, int64_t k, float alpha,
-                         const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
-                         int64_t ldc, int epilogue, const float* bias, const float* res, int64_t ldr,
-                         float* aux, int64_t ldaux) {
+extern "C" size_t tile_gemm_workspace(int64_t m, int64_t n, int64_t k) {
+  if (m <= 0 || n <= 0 || k <= 0) return 0;
+  const Plan p = plan_for(m, n, k, (size_t)-1);
+  return p.splits > 1 ? (size_t)p.splits * m * n * sizeof(float) : 0;
+}
+
+extern "C" int tile_gemm_ws(void* stream, int transA, int transB, int64_t m, int64_t n, int64_t k, float alpha,
+                            const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
+                            int64_t ldc, int epilogue, const float* bias, const float* res, int64_t ldr, float* aux,
+                            int64_t ldaux, void* workspace, size_t workspace_bytes) {
   using tt::fail;
   if (m < 0 || n < 0 || k < 0) return fail(TT_ERR_ARG, "tile_gemm: negative size");
   if (m == 0 || n == 0) return TT_OK;
@@ -285,15 +395,22 @@ extern "C" int tile_gemm(void* stream, int transA, int transB, int64_t m, int64_
   if ((epilogue & TT_EPI_RES) && (!res || ldr < n)) return fail(TT_ERR_ARG, "tile_gemm: bad residual");
   if ((epilogue & (TT_EPI_GELU | TT_EPI_GELU_BWD)) && (!aux || ldaux < n))
     return fail(TT_ERR_ARG, "tile_gemm: GELU epilogue needs aux");
-  GemmArgs g{(int)m, (int)n, (int)k, alpha, beta, A, B, C, lda, ldb, ldc, epilogue, bias, res, ldr, aux, ldaux};
-  if (k == 0) {  // C = beta*S (+epilogue): run the kernel with an empty K loop
-    g.k = 0;
-  }
+  if (workspace_bytes > 0 && !workspace) return fail(TT_ERR_ARG, "tile_gemm: null workspace");
+  GemmArgs g{(int)m, (int)n, (int)k, alpha, beta, A, B, C, lda, ldb, ldc, epilogue, bias, res, ldr, aux, ldaux,
+             (float*)workspace, 1, (int)k};
   const bool va = k > 0 && aligned16(A) && lda % 4 == 0;
   const bool vb = k > 0 && aligned16(B) && ldb % 4 == 0;
+  const size_t wsb = workspace ? workspace_bytes : 0;
   hipStream_t s = tt::as_stream(stream);
-  if (!transA && !transB) return launch_t<false, false>(g, va, vb, s);
-  if (!transA && transB) return launch_t<false, true>(g, va, vb, s);
-  if (transA && !transB) return launch_t<true, false>(g, va, vb, s);
-  return launch_t<true, true>(g, va, vb, s);
+  if (!transA && !transB) return launch_t<false, false>(g, va, vb, wsb, s);
+  if (!transA && transB) return launch_t<false, true>(g, va, vb, wsb, s);
+  if (transA && !transB) return launch_t<true, false>(g, va, vb, wsb, s);
+  return launch_t<true, true>(g, va, vb, wsb, s);
+}
+
+extern "C" int tile_gemm(void* stream, int transA, int transB, int64_t m, int64_t n, int64_t k, float alpha,
+                         const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C, int64_t ldc,
+                         int epilogue, const float* bias, const float* res, int64_t ldr, float* aux, int64_t ldaux) {
+  return tile_gemm_ws(stream, transA, transB, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, epilogue, bias, res, ldr,
+                      aux, ldaux, nullptr, 0);
 }

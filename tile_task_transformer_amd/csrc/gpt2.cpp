@@ -103,21 +103,20 @@ int submit_gemm(tt_ctx* ctx, const char* label, const Gemm& q) {
                 (long long)kb, (long long)n, (long long)cr, (long long)cc);
   std::vector<Access> acc = {R(q.A.t, q.A.lin), R(q.B.t, q.B.lin)};
   const bool gelu = q.epi & TT_EPI_GELU;
-  acc.push_back((q.beta == 0.f || gelu) ? (gelu ? R(q.C.t, q.C.lin) : W(q.C.t, q.C.lin)) : RW(q.C.t, q.C.lin));
-  if (gelu) acc.back().mode = TT_W;
+  // C is only written when beta == 0 or when the GELU epilogue accumulates in aux
+  acc.push_back((q.beta == 0.f || gelu) ? W(q.C.t, q.C.lin) : RW(q.C.t, q.C.lin));
   if (q.bias.valid()) acc.push_back(R(q.bias.t, q.bias.lin));
   if (q.res.valid()) acc.push_back(R(q.res.t, q.res.lin));
   if (q.aux.valid()) acc.push_back(gelu ? RW(q.aux.t, q.aux.lin) : R(q.aux.t, q.aux.lin));
   Gemm p = q;
-  return ctx->submit(label, std::move(acc), [p, m, n, k, ac, bc, cc](hipStream_t s, void*) {
-    int64_t ldr = 0, ldaux = 0, rr, rc_;
+  return ctx->submit(label, std::move(acc), [p, m, n, k, ac, bc, cc, ctx](hipStream_t s, void* ws) {
+    int64_t ldr = 0, ldaux = 0, rr;
     if (p.res.valid()) p.res.t->mat(p.res.lin, &rr, &ldr);
     if (p.aux.valid()) p.aux.t->mat(p.aux.lin, &rr, &ldaux);
-    (void)rc_;
-    return tile_gemm(s, p.ta, p.tb, m, n, k, p.alpha, F(p.A.t, p.A.lin), ac, F(p.B.t, p.B.lin), bc, p.beta,
-                     F(p.C.t, p.C.lin), cc, p.epi, p.bias.valid() ? F(p.bias.t, p.bias.lin) : nullptr,
-                     p.res.valid() ? F(p.res.t, p.res.lin) : nullptr, ldr,
-                     p.aux.valid() ? F(p.aux.t, p.aux.lin) : nullptr, ldaux);
+    return tile_gemm_ws(s, p.ta, p.tb, m, n, k, p.alpha, F(p.A.t, p.A.lin), ac, F(p.B.t, p.B.lin), bc, p.beta,
+                        F(p.C.t, p.C.lin), cc, p.epi, p.bias.valid() ? F(p.bias.t, p.bias.lin) : nullptr,
+                        p.res.valid() ? F(p.res.t, p.res.lin) : nullptr, ldr,
+                        p.aux.valid() ? F(p.aux.t, p.aux.lin) : nullptr, ldaux, ws, ws ? ctx->workspace_bytes : 0);
   });
 }
 
@@ -391,6 +390,15 @@ extern "C" int tt_gpt2_create(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_g
   // per-stream workspace for the deterministic column sums
   const int64_t widest = std::max<int64_t>({et, std::min<int64_t>(it, I), ht * hd});
   size_t ws = std::max(tile_layernorm_bwd_workspace(G->rows, et), tile_reduce_rows_workspace(G->rows, widest));
+  {
+    // split-K slices of the step's GEMM shapes (m, n, k), capped at 256 MiB per stream
+    const int64_t r = G->rows, e = et, in = std::min<int64_t>(it, I), hw = ht * hd, vv = vt;
+    const int64_t shapes[][3] = {{r, hw, e}, {r, e, hw}, {r, in, e}, {r, e, in}, {r, vv, e}, {vv, e, r}, {r, e, vv},
+                                 {in, e, r}, {e, in, r}, {hw, e, r}, {e, hw, r}};
+    size_t g = 0;
+    for (auto& s : shapes) g = std::max(g, tile_gemm_workspace(s[0], s[1], s[2]));
+    ws = std::max(ws, std::min<size_t>(g, (size_t)256 << 20));
+  }
   if (int rc = ctx->ensure_workspace(ws)) return fail_clean(rc);
   // zero gradients' home state, moments and the step counter
   if (!ctx->dryrun) {

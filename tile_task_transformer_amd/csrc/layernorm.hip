@@ -109,20 +109,22 @@ __global__ void ln_fwd_apply(int rows, int cols, const float* __restrict__ x, in
 
 // ------------------------------------------------------------- backward
 
-// Rows of one workgroup; each wave takes kRowsPerWave consecutive rows.
-constexpr int kRowsPerWave = 4;
-constexpr int kRowsPerBlock = kWaves * kRowsPerWave;
+// Each wave takes kRowsPerWave consecutive rows; a workgroup has bwd_waves(NV)
+// waves (as many as the row's registers allow), so one block covers
+// kRowsPerWave * waves rows and few per-block column partials remain.
+constexpr int kRowsPerWave = 2;
+__host__ __device__ constexpr int bwd_waves(int nv) { return nv <= 2 ? 16 : (nv <= 4 ? 8 : 4); }
 
 // phase PARTIAL: parts = (sum dxhat, sum dxhat*xhat); FUSED / APPLY: dx and
 // per-block column partials of dy*xhat and dy into ws[block][2][cols].
 template <int NV, bool VEC>
-__global__ __launch_bounds__(256) void ln_bwd_rows(int phase, int rows, int cols, float n_total,
-                                                   const float* __restrict__ dy, int64_t lddy,
-                                                   const float* __restrict__ x, int64_t ldx,
-                                                   const float* __restrict__ gamma, const float* __restrict__ stats,
-                                                   float* __restrict__ parts, int n_parts, int64_t part_stride,
-                                                   float* __restrict__ dx, int64_t lddx, int dx_acc,
-                                                   float* __restrict__ ws) {
+__global__ __launch_bounds__(64 * bwd_waves(NV)) void ln_bwd_rows(
+    int phase, int rows, int cols, float n_total, const float* __restrict__ dy, int64_t lddy,
+    const float* __restrict__ x, int64_t ldx, const float* __restrict__ gamma, const float* __restrict__ stats,
+    float* __restrict__ parts, int n_parts, int64_t part_stride, float* __restrict__ dx, int64_t lddx, int dx_acc,
+    float* __restrict__ ws) {
+  constexpr int kWaves = bwd_waves(NV);
+  constexpr int kRowsPerBlock = kWaves * kRowsPerWave;
   __shared__ f32x4 red[kWaves][2][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   f32x4 g[NV], dg[NV], db[NV];
@@ -224,21 +226,31 @@ __global__ __launch_bounds__(256) void ln_bwd_rows(int phase, int rows, int cols
 
 }  // namespace
 
-// Column sums of nblk partial rows -> out[c] (+)= sum_b ws[b*ws_ld + c], in
-// block order. One workgroup: 64 columns x 16 row groups, combined in order.
-__global__ __launch_bounds__(256) void colsum_finish(int nblk, int cols, const float* __restrict__ ws,
-                                                     int64_t ws_ld, int64_t ws_off, float* __restrict__ out,
-                                                     int accumulate) {
+// Column sums of nblk partial rows -> out[c] (+)= sum_b ws[b*ws_ld + c], in a
+// fixed order. One workgroup: 64 columns x 16 row groups; group g sums rows
+// g, g+16, ... (loads issued 4 at a time), then the 16 group sums are added
+// in group order.
+__global__ __launch_bounds__(1024) void colsum_finish(int nblk, int cols, const float* __restrict__ ws,
+                                                      int64_t ws_ld, int64_t ws_off, float* __restrict__ out,
+                                                      int accumulate) {
   __shared__ float red[16][64];
-  const int cl = threadIdx.x & 63, grp = threadIdx.x >> 6;  // 4 groups of 64 threads
+  const int cl = threadIdx.x & 63, grp = threadIdx.x >> 6;
   const int c = blockIdx.x * 64 + cl;
-  float s[4] = {0.f, 0.f, 0.f, 0.f};
+  float s = 0.f;
   if (c < cols) {
-    // group grp sums partial rows b = grp*4 + q (mod 16 lanes of order)
-    for (int b = grp; b < nblk; b += 4) s[b / 4 % 4] += ws[(int64_t)b * ws_ld + ws_off + c];
+    const float* src = ws + ws_off + c;
+    int b = grp;
+    for (; b + 48 < nblk; b += 64) {
+      const float v0 = src[(int64_t)b * ws_ld], v1 = src[(int64_t)(b + 16) * ws_ld];
+      const float v2 = src[(int64_t)(b + 32) * ws_ld], v3 = src[(int64_t)(b + 48) * ws_ld];
+      s += v0;
+      s += v1;
+      s += v2;
+      s += v3;
+    }
+    for (; b < nblk; b += 16) s += src[(int64_t)b * ws_ld];
   }
-#pragma unroll
-  for (int q = 0; q < 4; ++q) red[grp * 4 + q][cl] = s[q];
+  red[grp][cl] = s;
   __syncthreads();
   if (grp == 0 && c < cols) {
     float t = 0.f;
@@ -269,7 +281,8 @@ int launch_ln_bwd_rows(bool vec, int phase, int rows, int cols, float n_total, c
                        const float* x, int64_t ldx, const float* gamma, const float* stats, float* parts,
                        int n_parts, int64_t part_stride, float* dx, int64_t lddx, int dx_acc, float* ws,
                        hipStream_t s) {
-  dim3 grid((rows + kRowsPerBlock - 1) / kRowsPerBlock), block(256);
+  constexpr int rpb = bwd_waves(NV) * kRowsPerWave;
+  dim3 grid((rows + rpb - 1) / rpb), block(64 * bwd_waves(NV));
   if (vec)
     hipLaunchKernelGGL((ln_bwd_rows<NV, true>), grid, block, 0, s, phase, rows, cols, n_total, dy, lddy, x, ldx,
                        gamma, stats, parts, n_parts, part_stride, dx, lddx, dx_acc, ws);
@@ -280,6 +293,13 @@ int launch_ln_bwd_rows(bool vec, int phase, int rows, int cols, float n_total, c
 }
 
 constexpr int kMaxCols = 2048;  // 8 float4 per lane
+
+// instantiated float4-per-lane counts and the rows one backward block covers
+int nv_for(int64_t cols) {
+  const int nv = (int)((cols + 255) / 256);
+  return nv <= 4 ? nv : (nv <= 6 ? 6 : 8);
+}
+int64_t bwd_rows_per_block(int64_t cols) { return (int64_t)bwd_waves(nv_for(cols)) * kRowsPerWave; }
 
 }  // namespace
 
@@ -331,7 +351,8 @@ extern "C" int tile_layernorm_fwd(void* stream, int phase, int64_t rows, int64_t
 }
 
 extern "C" size_t tile_layernorm_bwd_workspace(int64_t rows, int64_t cols) {
-  const int64_t nblk = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int64_t rpb = bwd_rows_per_block(cols);
+  const int64_t nblk = (rows + rpb - 1) / rpb;
   return (size_t)(nblk * 2 * cols * sizeof(float));
 }
 
@@ -374,8 +395,8 @@ extern "C" int tile_layernorm_bwd(void* stream, int phase, int64_t rows, int64_t
   }
 #undef TT_LNB
   if (rc || phase == TT_LN_PARTIAL) return rc;
-  const int nblk = (r + kRowsPerBlock - 1) / kRowsPerBlock;
-  dim3 grid((c + 63) / 64), block(256);
+  const int nblk = (int)((r + bwd_rows_per_block(c) - 1) / bwd_rows_per_block(c));
+  dim3 grid((c + 63) / 64), block(1024);
   hipLaunchKernelGGL(colsum_finish, grid, block, 0, s, nblk, c, ws, (int64_t)2 * c, (int64_t)0, dgamma, 1);
   hipLaunchKernelGGL(colsum_finish, grid, block, 0, s, nblk, c, ws, (int64_t)2 * c, (int64_t)c, dbeta, 1);
   return tt::launch_status("tile_layernorm_bwd(colsum)");
@@ -394,8 +415,16 @@ __global__ __launch_bounds__(256) void reduce_rows_stage1(int rows, int cols, co
   const int c = (blockIdx.y * 64 + cl) * 4;
   const int r0 = blockIdx.x * kReduceRows + grp * (kReduceRows / 4);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (c < cols)
-    for (int r = r0; r < min(rows, r0 + kReduceRows / 4); ++r) acc += tt::ld4<VEC>(X, ldx, r, c, cols);
+  if (c < cols) {
+    // all loads of the thread's rows in flight before the (ordered) sum
+    constexpr int R = kReduceRows / 4;
+    f32x4 v[R];
+#pragma unroll
+    for (int q = 0; q < R; ++q)
+      v[q] = r0 + q < rows ? tt::ld4<VEC>(X, ldx, r0 + q, c, cols) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < R; ++q) acc += v[q];
+  }
   red[grp][cl] = acc;
   __syncthreads();
   if (grp == 0 && c < cols) {
@@ -432,7 +461,7 @@ extern "C" int tile_reduce_rows(void* stream, int64_t rows, int64_t cols, const 
     else hipLaunchKernelGGL(reduce_rows_stage1<false>, grid, block, 0, s, r, c, X, ldx, ws);
     if (int rc = tt::launch_status("tile_reduce_rows")) return rc;
   }
-  hipLaunchKernelGGL(colsum_finish, dim3((c + 63) / 64), dim3(256), 0, s, nblk, c, ws, (int64_t)c, (int64_t)0, out,
+  hipLaunchKernelGGL(colsum_finish, dim3((c + 63) / 64), dim3(1024), 0, s, nblk, c, ws, (int64_t)c, (int64_t)0, out,
                      beta);
   return tt::launch_status("tile_reduce_rows(finish)");
 }

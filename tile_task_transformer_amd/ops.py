@@ -13,7 +13,7 @@ from ._lib import (TT_EPI_NONE, check, lib, ptr, stream_handle, TT_EPI_BIAS, TT_
                    TT_EMB_POS)
 
 __all__ = [
-    "tile_gemm", "tile_layernorm_fwd", "tile_layernorm_bwd", "tile_layernorm_bwd_workspace", "tile_softmax",
+    "tile_gemm", "tile_gemm_ws", "tile_gemm_workspace", "tile_layernorm_fwd", "tile_layernorm_bwd", "tile_layernorm_bwd_workspace", "tile_softmax",
     "tile_xentropy", "tile_attention_fwd", "tile_attention_bwd", "tile_fused_adamw", "tile_adamw_advance",
     "tile_embedding_fwd", "tile_embedding_index", "tile_embedding_bwd", "tile_reduce_rows",
     "tile_reduce_rows_workspace", "tile_fill", "tile_split_tokens",
@@ -27,6 +27,17 @@ def tile_gemm(stream, transA, transB, m, n, k, alpha, A, lda, B, ldb, beta, C, l
               bias=None, res=None, ldr=0, aux=None, ldaux=0):
     return check(lib.tile_gemm(stream_handle(stream), transA, transB, m, n, k, alpha, ptr(A), lda, ptr(B), ldb,
                                beta, ptr(C), ldc, epilogue, ptr(bias), ptr(res), ldr, ptr(aux), ldaux))
+
+
+def tile_gemm_ws(stream, transA, transB, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, epilogue=TT_EPI_NONE,
+                 bias=None, res=None, ldr=0, aux=None, ldaux=0, workspace=None, workspace_bytes=0):
+    return check(lib.tile_gemm_ws(stream_handle(stream), transA, transB, m, n, k, alpha, ptr(A), lda, ptr(B), ldb,
+                                  beta, ptr(C), ldc, epilogue, ptr(bias), ptr(res), ldr, ptr(aux), ldaux,
+                                  ptr(workspace), workspace_bytes))
+
+
+def tile_gemm_workspace(m, n, k):
+    return lib.tile_gemm_workspace(m, n, k)
 
 
 def tile_layernorm_fwd(stream, phase, rows, cols, x, ldx, gamma, beta, parts, n_parts, part_stride, stats, y,
