@@ -16,6 +16,20 @@
 // The backward uses the same trick twice: one kernel owns queries (dQ), the
 // other owns keys (dK, dV); neither needs atomics, so results are bitwise
 // reproducible.
+//
+// Work split. A workgroup has 4 waves and owns 64 queries (dK/dV: 64 keys)
+// as 2 groups of 32. Each group's row of work (all visible keys; dK/dV: all
+// queries that see the key) is shared by 2 waves: the streamed operand
+// arrives in LDS stages of 64 rows and wave `part` takes the 32-row half
+// `part` of every stage. At the end the two partial results are merged in a
+// fixed order (online-softmax states by rescaling to the larger max,
+// gradient partials by addition), so the result does not depend on timing.
+// Splitting the rows halves the longest wave of a causal tile (the last
+// query block sees every key), which bounds the kernel's critical path.
+// The next stage's global loads are in flight (in registers) while the
+// current stage's MFMAs run. Per-element causal masking is applied only to
+// sub-blocks that straddle the diagonal; sub-blocks wholly above it are
+// skipped per wave.
 #include "common.hpp"
 
 namespace {
@@ -25,8 +39,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kBQ = 128;   // queries per workgroup (4 waves x 32)
-constexpr int kBK = 64;    // keys per LDS stage
+constexpr int kNT = 256;          // threads per workgroup (4 waves)
+constexpr int kBQ = 64;           // queries (dK/dV kernel: keys) owned per workgroup
+constexpr int kBS = 64;           // streamed rows per LDS stage (2 halves of 32)
 
 __device__ __forceinline__ f32x16 mfma(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -46,45 +61,73 @@ __device__ __forceinline__ int64_t row_off(int b, int t, int h, int len, int hea
   return (((int64_t)b * len + t) * heads + h) * hd;
 }
 
-// Stage `n` rows (of `len` valid) x HD floats of one (b, h) into LDS [kBK][ld],
-// zero-filling rows >= len and columns HD..ld-4.
+// Streams blocks of kBS rows x HD floats of one (b, h) through registers into
+// an LDS buffer [kBS][LD]; rows >= len read as zero.
 template <int HD, int LD>
-__device__ __forceinline__ void stage_rows(float* __restrict__ dst, const float* __restrict__ src, int b, int h,
-                                           int r0, int len, int heads) {
-  constexpr int V4 = kBK * HD / 4;
-  for (int i = threadIdx.x; i < V4; i += 256) {
-    const int r = i / (HD / 4), c = (i % (HD / 4)) * 4;
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (r0 + r < len) v = *reinterpret_cast<const f32x4*>(src + row_off(b, r0 + r, h, len, heads, HD) + c);
-    *reinterpret_cast<f32x4*>(dst + r * LD + c) = v;
-  }
-  if (LD - 4 > HD) {  // pad columns HD..LD-5 (used when HD < 32)
-    for (int i = threadIdx.x; i < kBK * (LD - 4 - HD); i += 256) {
-      const int r = i / (LD - 4 - HD), c = HD + i % (LD - 4 - HD);
-      dst[r * LD + c] = 0.f;
+struct Stager {
+  static constexpr int V4 = kBS * HD / 4;
+  static constexpr int PT = (V4 + kNT - 1) / kNT;
+  f32x4 r[PT];
+  __device__ __forceinline__ void load(const float* __restrict__ src, int b, int h, int r0, int len, int heads) {
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int idx = threadIdx.x + kNT * i;
+      const int row = idx / (HD / 4), c = (idx % (HD / 4)) * 4;
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (idx < V4 && r0 + row < len)
+        v = *reinterpret_cast<const f32x4*>(src + row_off(b, r0 + row, h, len, heads, HD) + c);
+      r[i] = v;
     }
   }
+  __device__ __forceinline__ void store(float* dst) const {
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int idx = threadIdx.x + kNT * i;
+      if (idx < V4) {
+        const int row = idx / (HD / 4), c = (idx % (HD / 4)) * 4;
+        *reinterpret_cast<f32x4*>(dst + row * LD + c) = r[i];
+      }
+    }
+  }
+};
+
+// zero the pad columns HD..LD-5 of an LDS block (used when HD < 32)
+template <int HD, int LD>
+__device__ __forceinline__ void zero_pad(float* dst) {
+  constexpr int W = LD - 4 - HD;
+  if (W > 0)
+    for (int i = threadIdx.x; i < kBS * W; i += kNT) dst[(i / W) * LD + HD + i % W] = 0.f;
 }
+
+template <int HD>
+struct Cfg {
+  static constexpr int HDP = HD < 32 ? 32 : HD;   // MFMA output rows padded to 32
+  static constexpr int LD = HDP + 4;              // LDS row stride
+  static constexpr int NKB = HD / 8;              // 8-wide head-dim groups (4 per half-wave)
+  static constexpr int NEB = HDP / 32;            // 32-row blocks of the head dim
+  static constexpr int MINW = HD <= 64 ? 2 : 1;   // waves per SIMD the registers must allow
+};
 
 // ------------------------------------------------------------------ forward
 
 template <int HD>
-__global__ __launch_bounds__(256) void attn_fwd(AttnGeom g, const float* __restrict__ Q, const float* __restrict__ K,
-                                                const float* __restrict__ V, float* __restrict__ O,
-                                                float* __restrict__ ml, float* __restrict__ lse, int first, int last) {
-  constexpr int HDP = HD < 32 ? 32 : HD;   // output rows padded to the 32-row MFMA tile
-  constexpr int LDK = HD + 4, LDV = HDP + 4;
-  constexpr int NKB = HD / 8;              // float4 groups of the head dim per half-wave
-  constexpr int NEB = HDP / 32;
-  __shared__ __attribute__((aligned(16))) float Ks[kBK * LDK];
-  __shared__ __attribute__((aligned(16))) float Vs[kBK * LDV];
+__global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_fwd(AttnGeom g, const float* __restrict__ Q,
+                                                              const float* __restrict__ K,
+                                                              const float* __restrict__ V, float* __restrict__ O,
+                                                              float* __restrict__ ml, float* __restrict__ lse,
+                                                              int first, int last) {
+  using C = Cfg<HD>;
+  constexpr int LD = C::LD, NKB = C::NKB, NEB = C::NEB;
+  __shared__ __attribute__((aligned(16))) float Ks[kBS * LD];
+  __shared__ __attribute__((aligned(16))) float Vs[kBS * LD];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = wave & 1, part = wave >> 1;
   const int half = lane >> 5, l32 = lane & 31;
   const int qblk = gridDim.x - 1 - blockIdx.x;  // heavy (late) query blocks first
   const int bh = blockIdx.y, b = bh / g.heads, h = bh % g.heads;
-  const int q0 = qblk * kBQ + wave * 32;        // this wave's first query
-  const int q = q0 + l32;                       // this lane's query
+  const int q0 = qblk * kBQ + grp * 32;
+  const int q = q0 + l32;
   const bool qvalid = q < g.q_len;
   const int64_t qpos = g.q_off + q;
 
@@ -98,10 +141,12 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnGeom g, const float* __restr
       qf[kb] = v * qs;
     }
   }
+  // running state; the previous key tiles' state enters through part 0 only
   f32x16 oacc[NEB];
   float m = -INFINITY, l = 0.f;
   const int64_t st = ((int64_t)b * g.heads + h) * g.q_len + q;
-  if (!first && qvalid) {
+  const bool carry = !first && qvalid && part == 0;
+  if (carry) {
     m = ml[st * 2];
     l = ml[st * 2 + 1];
   }
@@ -110,39 +155,53 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnGeom g, const float* __restr
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int e = eb * 32 + kidx(r, half);
-      oacc[eb][r] = (!first && qvalid && e < HD) ? O[row_off(b, q, h, g.q_len, g.heads, HD) + e] : 0.f;
+      oacc[eb][r] = (carry && e < HD) ? O[row_off(b, q, h, g.q_len, g.heads, HD) + e] : 0.f;
     }
 
-  // keys that any query of this workgroup may see
   const int64_t qmax = g.q_off + min(g.q_len, qblk * kBQ + kBQ) - 1;
   const int kend = (int)max((int64_t)0, min((int64_t)g.k_len, qmax - g.k_off + 1));
+  const int64_t wave_qmin = g.q_off + q0;
   const int64_t wave_qmax = g.q_off + min(g.q_len - 1, q0 + 31);
+  const bool wave_live = q0 < g.q_len;
 
-  for (int k0 = 0; k0 < kend; k0 += kBK) {
-    __syncthreads();
-    stage_rows<HD, LDK>(Ks, K, b, h, k0, g.k_len, g.heads);
-    stage_rows<HD, LDV>(Vs, V, b, h, k0, g.k_len, g.heads);
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < kBK / 32; ++kk) {
-      const int kb0 = k0 + kk * 32;
-      if (kb0 >= g.k_len || q0 >= g.q_len || g.k_off + kb0 > wave_qmax) continue;  // wave-uniform skip
+  zero_pad<HD, LD>(Vs);
+  Stager<HD, LD> sk, sv;
+  if (kend > 0) {
+    sk.load(K, b, h, 0, g.k_len, g.heads);
+    sv.load(V, b, h, 0, g.k_len, g.heads);
+    sk.store(Ks);
+    sv.store(Vs);
+  }
+  __syncthreads();
+  for (int k0 = 0; k0 < kend; k0 += kBS) {
+    const bool more = k0 + kBS < kend;
+    if (more) {
+      sk.load(K, b, h, k0 + kBS, g.k_len, g.heads);
+      sv.load(V, b, h, k0 + kBS, g.k_len, g.heads);
+    }
+    const int kb0 = k0 + part * 32;
+    const float* ks = Ks + part * 32 * LD;
+    const float* vs = Vs + part * 32 * LD;
+    if (wave_live && kb0 < g.k_len && g.k_off + kb0 <= wave_qmax) {  // wave-uniform
       f32x16 s;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const f32x4 kf = *reinterpret_cast<const f32x4*>(Ks + (kk * 32 + l32) * LDK + 8 * kb + 4 * half);
+        const f32x4 kf = *reinterpret_cast<const f32x4*>(ks + l32 * LD + 8 * kb + 4 * half);
 #pragma unroll
         for (int i = 0; i < 4; ++i) s = mfma(kf[i], qf[kb][i], s);
       }
-      float mloc = -INFINITY;
+      if (kb0 + 31 >= g.k_len || g.k_off + kb0 + 31 > wave_qmin) {  // straddles the diagonal or the end
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kb0 + kidx(r, half);
-        if (key >= g.k_len || g.k_off + key > qpos) s[r] = -INFINITY;
-        mloc = fmaxf(mloc, s[r]);
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb0 + kidx(r, half);
+          if (key >= g.k_len || g.k_off + key > qpos) s[r] = -INFINITY;
+        }
       }
+      float mloc = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, s[r]);
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
       const float mnew = fmaxf(m, mloc);
       const float alpha = mnew == -INFINITY ? 1.f : exp2f(m - mnew);
@@ -159,13 +218,43 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnGeom g, const float* __restr
       for (int eb = 0; eb < NEB; ++eb) {
         oacc[eb] *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          oacc[eb] = mfma(Vs[(kk * 32 + kidx(r, half)) * LDV + eb * 32 + l32], s[r], oacc[eb]);
+        for (int r = 0; r < 16; ++r) oacc[eb] = mfma(vs[kidx(r, half) * LD + eb * 32 + l32], s[r], oacc[eb]);
       }
     }
+    __syncthreads();
+    if (more) {
+      sk.store(Ks);
+      sv.store(Vs);
+    }
+    __syncthreads();
   }
 
-  if (!qvalid) return;
+  // merge part 1 into part 0 (LDS reused; the loop ended on a barrier)
+  constexpr int STR = 2 + 16 * NEB;
+  float* xb = Ks;  // kBS*LD floats >= 2 groups x 64 lanes x STR
+  if (part == 1) {
+    float* p = xb + (grp * 64 + lane) * STR;
+    p[0] = m;
+    p[1] = l;
+#pragma unroll
+    for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[2 + 16 * eb + r] = oacc[eb][r];
+  }
+  __syncthreads();
+  if (part == 1 || !qvalid) return;
+  {
+    const float* p = xb + (grp * 64 + lane) * STR;
+    const float m1 = p[0], l1 = p[1];
+    const float mm = fmaxf(m, m1);
+    const float a0 = m == -INFINITY ? 0.f : exp2f(m - mm), a1 = m1 == -INFINITY ? 0.f : exp2f(m1 - mm);
+    l = l * a0 + l1 * a1;
+    m = mm;
+#pragma unroll
+    for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[eb][r] = oacc[eb][r] * a0 + p[2 + 16 * eb + r] * a1;
+  }
   const float inv = last ? 1.f / l : 1.f;
   float* orow = O + row_off(b, q, h, g.q_len, g.heads, HD);
 #pragma unroll
@@ -207,23 +296,43 @@ __global__ void attn_prep(int batch, int heads, int q_len, int hd, const float* 
   Dv[((int64_t)b * heads + h) * q_len + t] = s;
 }
 
-// dQ: each wave owns 32 queries; loops over key blocks.
+// sum of the two parts' register blocks, part 0 + part 1, through LDS
+template <int N>
+__device__ __forceinline__ void merge_add(float* xb, int grp, int part, int lane, f32x16 (&a)[N]) {
+  float* p = xb + (grp * 64 + lane) * (16 * N);
+  if (part == 1)
+#pragma unroll
+    for (int n = 0; n < N; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[16 * n + r] = a[n][r];
+  __syncthreads();
+  if (part == 0)
+#pragma unroll
+    for (int n = 0; n < N; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) a[n][r] += p[16 * n + r];
+}
+
+// dQ: a group of 32 queries per wave pair; streams key blocks.
 template <int HD>
-__global__ __launch_bounds__(256) void attn_bwd_dq(AttnGeom g, const float* __restrict__ Q,
-                                                   const float* __restrict__ K, const float* __restrict__ V,
-                                                   const float* __restrict__ dO, const float* __restrict__ lse,
-                                                   const float* __restrict__ Dv, float* __restrict__ dQ, int acc) {
-  constexpr int HDP = HD < 32 ? 32 : HD;
-  constexpr int LD = HDP + 4;
-  constexpr int NKB = HD / 8, NEB = HDP / 32;
-  __shared__ __attribute__((aligned(16))) float Ks[kBK * LD];
-  __shared__ __attribute__((aligned(16))) float Vs[kBK * LD];
+__global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_bwd_dq(AttnGeom g, const float* __restrict__ Q,
+                                                                 const float* __restrict__ K,
+                                                                 const float* __restrict__ V,
+                                                                 const float* __restrict__ dO,
+                                                                 const float* __restrict__ lse,
+                                                                 const float* __restrict__ Dv, float* __restrict__ dQ,
+                                                                 int acc) {
+  using C = Cfg<HD>;
+  constexpr int LD = C::LD, NKB = C::NKB, NEB = C::NEB;
+  __shared__ __attribute__((aligned(16))) float Ks[kBS * LD];
+  __shared__ __attribute__((aligned(16))) float Vs[kBS * LD];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = wave & 1, part = wave >> 1;
   const int half = lane >> 5, l32 = lane & 31;
   const int qblk = gridDim.x - 1 - blockIdx.x;
   const int bh = blockIdx.y, b = bh / g.heads, h = bh % g.heads;
-  const int q0 = qblk * kBQ + wave * 32;
+  const int q0 = qblk * kBQ + grp * 32;
   const int q = q0 + l32;
   const bool qvalid = q < g.q_len;
   const int64_t qpos = g.q_off + q;
@@ -251,17 +360,29 @@ __global__ __launch_bounds__(256) void attn_bwd_dq(AttnGeom g, const float* __re
 
   const int64_t qmax = g.q_off + min(g.q_len, qblk * kBQ + kBQ) - 1;
   const int kend = (int)max((int64_t)0, min((int64_t)g.k_len, qmax - g.k_off + 1));
+  const int64_t wave_qmin = g.q_off + q0;
   const int64_t wave_qmax = g.q_off + min(g.q_len - 1, q0 + 31);
+  const bool wave_live = q0 < g.q_len;
 
-  for (int k0 = 0; k0 < kend; k0 += kBK) {
-    __syncthreads();
-    stage_rows<HD, LD>(Ks, K, b, h, k0, g.k_len, g.heads);
-    stage_rows<HD, LD>(Vs, V, b, h, k0, g.k_len, g.heads);
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < kBK / 32; ++kk) {
-      const int kb0 = k0 + kk * 32;
-      if (kb0 >= g.k_len || q0 >= g.q_len || g.k_off + kb0 > wave_qmax) continue;
+  zero_pad<HD, LD>(Ks);
+  Stager<HD, LD> sk, sv;
+  if (kend > 0) {
+    sk.load(K, b, h, 0, g.k_len, g.heads);
+    sv.load(V, b, h, 0, g.k_len, g.heads);
+    sk.store(Ks);
+    sv.store(Vs);
+  }
+  __syncthreads();
+  for (int k0 = 0; k0 < kend; k0 += kBS) {
+    const bool more = k0 + kBS < kend;
+    if (more) {
+      sk.load(K, b, h, k0 + kBS, g.k_len, g.heads);
+      sv.load(V, b, h, k0 + kBS, g.k_len, g.heads);
+    }
+    const int kb0 = k0 + part * 32;
+    const float* ks = Ks + part * 32 * LD;
+    const float* vs = Vs + part * 32 * LD;
+    if (wave_live && kb0 < g.k_len && g.k_off + kb0 <= wave_qmax) {
       f32x16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -270,29 +391,36 @@ __global__ __launch_bounds__(256) void attn_bwd_dq(AttnGeom g, const float* __re
       }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const f32x4 kf = *reinterpret_cast<const f32x4*>(Ks + (kk * 32 + l32) * LD + 8 * kb + 4 * half);
-        const f32x4 vf = *reinterpret_cast<const f32x4*>(Vs + (kk * 32 + l32) * LD + 8 * kb + 4 * half);
+        const f32x4 kf = *reinterpret_cast<const f32x4*>(ks + l32 * LD + 8 * kb + 4 * half);
+        const f32x4 vf = *reinterpret_cast<const f32x4*>(vs + l32 * LD + 8 * kb + 4 * half);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           s = mfma(kf[i], qf[kb][i], s);     // S^T = K Q^T (log2 units)
           dp = mfma(vf[i], df[kb][i], dp);   // dP^T = V dO^T
         }
       }
+      const bool edge = kb0 + 31 >= g.k_len || g.k_off + kb0 + 31 > wave_qmin;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kb0 + kidx(r, half);
-        const bool ok = qvalid && key < g.k_len && g.k_off + key <= qpos;
+        const bool ok = qvalid && (!edge || (key < g.k_len && g.k_off + key <= qpos));
         const float p = ok ? exp2f(s[r] - lse2) : 0.f;
         s[r] = p * (dp[r] - dq_d);           // dS^T
       }
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          dacc[eb] = mfma(Ks[(kk * 32 + kidx(r, half)) * LD + eb * 32 + l32], s[r], dacc[eb]);
+        for (int r = 0; r < 16; ++r) dacc[eb] = mfma(ks[kidx(r, half) * LD + eb * 32 + l32], s[r], dacc[eb]);
     }
+    __syncthreads();
+    if (more) {
+      sk.store(Ks);
+      sv.store(Vs);
+    }
+    __syncthreads();
   }
-  if (!qvalid) return;
+  merge_add<NEB>(Ks, grp, part, lane, dacc);
+  if (part == 1 || !qvalid) return;
   float* drow = dQ + row_off(b, q, h, g.q_len, g.heads, HD);
 #pragma unroll
   for (int eb = 0; eb < NEB; ++eb)
@@ -308,26 +436,26 @@ __global__ __launch_bounds__(256) void attn_bwd_dq(AttnGeom g, const float* __re
     }
 }
 
-// dK, dV: each wave owns 32 keys; loops over query blocks.
+// dK, dV: a group of 32 keys per wave pair; streams query blocks (Q, dO, lse, D).
 template <int HD>
-__global__ __launch_bounds__(256) void attn_bwd_dkv(AttnGeom g, const float* __restrict__ Q,
-                                                    const float* __restrict__ K, const float* __restrict__ V,
-                                                    const float* __restrict__ dO, const float* __restrict__ lse,
-                                                    const float* __restrict__ Dv, float* __restrict__ dK,
-                                                    float* __restrict__ dV, int acc) {
-  constexpr int HDP = HD < 32 ? 32 : HD;
-  constexpr int LD = HDP + 4;
-  constexpr int NKB = HD / 8, NEB = HDP / 32;
-  __shared__ __attribute__((aligned(16))) float Qs[kBK * LD];
-  __shared__ __attribute__((aligned(16))) float Ds[kBK * LD];
-  __shared__ float Ls[kBK], Dd[kBK];
+__global__ __launch_bounds__(kNT, 1) void attn_bwd_dkv(AttnGeom g, const float* __restrict__ Q,
+                                                      const float* __restrict__ K, const float* __restrict__ V,
+                                                      const float* __restrict__ dO, const float* __restrict__ lse,
+                                                      const float* __restrict__ Dv, float* __restrict__ dK,
+                                                      float* __restrict__ dV, int acc) {
+  using C = Cfg<HD>;
+  constexpr int LD = C::LD, NKB = C::NKB, NEB = C::NEB;
+  __shared__ __attribute__((aligned(16))) float Qs[2 * kBS * LD];   // Q stage, then dO stage
+  __shared__ float Ls[kBS], Dd[kBS];
+  float* Ds = Qs + kBS * LD;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = wave & 1, part = wave >> 1;
   const int half = lane >> 5, l32 = lane & 31;
-  const int kblk = blockIdx.x;
+  const int kblk = blockIdx.x;   // early keys see the most queries: launched first
   const int bh = blockIdx.y, b = bh / g.heads, h = bh % g.heads;
-  const int k0w = kblk * kBQ + wave * 32;     // this wave's first key
-  const int key = k0w + l32;                  // this lane's key
+  const int k0w = kblk * kBQ + grp * 32;
+  const int key = k0w + l32;
   const bool kvalid = key < g.k_len;
   const int64_t kpos = g.k_off + key;
 
@@ -343,37 +471,56 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv(AttnGeom g, const float* __r
     kf[kb] = v * qs;
     vf[kb] = w;
   }
-  f32x16 dk[NEB], dv[NEB];
+  f32x16 dkv[2 * NEB];  // dK blocks, then dV blocks
 #pragma unroll
-  for (int eb = 0; eb < NEB; ++eb)
+  for (int n = 0; n < 2 * NEB; ++n)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dk[eb][r] = 0.f;
-      dv[eb][r] = 0.f;
-    }
+    for (int r = 0; r < 16; ++r) dkv[n][r] = 0.f;
 
-  // first query (tile-local) that can see the workgroup's first key
+  // first (tile-local) query that can see the workgroup's first key
   const int64_t kmin = g.k_off + (int64_t)kblk * kBQ;
   int qstart = (int)max((int64_t)0, kmin - g.q_off);
-  qstart = (qstart / kBK) * kBK;
+  qstart = (qstart / kBS) * kBS;
   const bool wave_live = k0w < g.k_len;
+  const int64_t wave_kmin = g.k_off + k0w;
+  const int64_t wave_kmax = g.k_off + min(g.k_len - 1, k0w + 31);
 
-  for (int qb = qstart; qb < g.q_len; qb += kBK) {
-    __syncthreads();
-    stage_rows<HD, LD>(Qs, Q, b, h, qb, g.q_len, g.heads);
-    stage_rows<HD, LD>(Ds, dO, b, h, qb, g.q_len, g.heads);
-    for (int i = threadIdx.x; i < kBK; i += 256) {
-      const int qq = qb + i;
-      const int64_t st = ((int64_t)b * g.heads + h) * g.q_len + qq;
-      Ls[i] = qq < g.q_len ? lse[st] * kLog2e : 0.f;
-      Dd[i] = qq < g.q_len ? Dv[st] : 0.f;
+  zero_pad<HD, LD>(Qs);
+  zero_pad<HD, LD>(Ds);
+  Stager<HD, LD> sq, sd;
+  float pl = 0.f, pd = 0.f;  // lse / D prefetch (threads < kBS)
+  auto load_rows = [&](int qb) {
+    sq.load(Q, b, h, qb, g.q_len, g.heads);
+    sd.load(dO, b, h, qb, g.q_len, g.heads);
+    if ((int)threadIdx.x < kBS) {
+      const int qq = qb + threadIdx.x;
+      const int64_t s2 = ((int64_t)b * g.heads + h) * g.q_len + qq;
+      pl = qq < g.q_len ? lse[s2] * kLog2e : 0.f;
+      pd = qq < g.q_len ? Dv[s2] : 0.f;
     }
-    __syncthreads();
-    if (!wave_live) continue;
-#pragma unroll
-    for (int qq = 0; qq < kBK / 32; ++qq) {
-      const int qb0 = qb + qq * 32;
-      if (qb0 >= g.q_len || g.q_off + qb0 + 31 < g.k_off + k0w) continue;  // all masked for this wave
+  };
+  auto store_rows = [&]() {
+    sq.store(Qs);
+    sd.store(Ds);
+    if ((int)threadIdx.x < kBS) {
+      Ls[threadIdx.x] = pl;
+      Dd[threadIdx.x] = pd;
+    }
+  };
+  if (qstart < g.q_len) {
+    load_rows(qstart);
+    store_rows();
+  }
+  __syncthreads();
+  for (int qb = qstart; qb < g.q_len; qb += kBS) {
+    const bool more = qb + kBS < g.q_len;
+    if (more) load_rows(qb + kBS);
+    const int qb0 = qb + part * 32;
+    const float* qsb = Qs + part * 32 * LD;
+    const float* dsb = Ds + part * 32 * LD;
+    const float* lsb = Ls + part * 32;
+    const float* ddb = Dd + part * 32;
+    if (wave_live && qb0 < g.q_len && g.q_off + qb0 + 31 >= wave_kmin) {  // not all masked
       f32x16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -382,34 +529,40 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv(AttnGeom g, const float* __r
       }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const f32x4 qf = *reinterpret_cast<const f32x4*>(Qs + (qq * 32 + l32) * LD + 8 * kb + 4 * half);
-        const f32x4 df = *reinterpret_cast<const f32x4*>(Ds + (qq * 32 + l32) * LD + 8 * kb + 4 * half);
+        const f32x4 qf = *reinterpret_cast<const f32x4*>(qsb + l32 * LD + 8 * kb + 4 * half);
+        const f32x4 df = *reinterpret_cast<const f32x4*>(dsb + l32 * LD + 8 * kb + 4 * half);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          s = mfma(qf[i], kf[kb][i], s);     // S = Q K^T (log2 units); lane owns key column
+          s = mfma(qf[i], kf[kb][i], s);     // S = Q K^T (log2 units); lane owns a key column
           dp = mfma(df[i], vf[kb][i], dp);   // dP = dO V^T
         }
       }
-      f32x16 p;
+      const bool edge = qb0 + 31 >= g.q_len || g.q_off + qb0 < wave_kmax;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ql = qq * 32 + kidx(r, half);
-        const int qg = qb + ql;
-        const bool ok = kvalid && qg < g.q_len && kpos <= g.q_off + qg;
-        p[r] = ok ? exp2f(s[r] - Ls[ql]) : 0.f;
-        s[r] = p[r] * (dp[r] - Dd[ql]);      // dS
+      for (int r = 0; r < 16; ++r) {         // P, in place of S
+        const int ql = kidx(r, half);
+        const bool ok = kvalid && (!edge || (qb0 + ql < g.q_len && kpos <= g.q_off + qb0 + ql));
+        s[r] = ok ? exp2f(s[r] - lsb[ql]) : 0.f;
       }
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ql = qq * 32 + kidx(r, half);
-          dv[eb] = mfma(Ds[ql * LD + eb * 32 + l32], p[r], dv[eb]);   // dV^T += dO^T P
-          dk[eb] = mfma(Qs[ql * LD + eb * 32 + l32], s[r], dk[eb]);   // dK^T += Q^T dS
-        }
+        for (int r = 0; r < 16; ++r)
+          dkv[NEB + eb] = mfma(dsb[kidx(r, half) * LD + eb * 32 + l32], s[r], dkv[NEB + eb]);  // dV^T += dO^T P
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] *= dp[r] - ddb[kidx(r, half)];  // dS, in place of P
+#pragma unroll
+      for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          dkv[eb] = mfma(qsb[kidx(r, half) * LD + eb * 32 + l32], s[r], dkv[eb]);  // dK^T += Q^T dS
     }
+    __syncthreads();
+    if (more) store_rows();
+    __syncthreads();
   }
-  if (!kvalid) return;
+  merge_add<2 * NEB>(Qs, grp, part, lane, dkv);
+  if (part == 1 || !kvalid) return;
   float* krow = dK + row_off(b, key, h, g.k_len, g.heads, HD);
   float* vrow = dV + row_off(b, key, h, g.k_len, g.heads, HD);
 #pragma unroll
@@ -418,8 +571,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv(AttnGeom g, const float* __r
     for (int gq = 0; gq < 4; ++gq) {
       const int e = eb * 32 + 8 * gq + 4 * half;
       if (e < HD) {
-        f32x4 a = {dk[eb][4 * gq], dk[eb][4 * gq + 1], dk[eb][4 * gq + 2], dk[eb][4 * gq + 3]};
-        f32x4 c = {dv[eb][4 * gq], dv[eb][4 * gq + 1], dv[eb][4 * gq + 2], dv[eb][4 * gq + 3]};
+        f32x4 a = {dkv[eb][4 * gq], dkv[eb][4 * gq + 1], dkv[eb][4 * gq + 2], dkv[eb][4 * gq + 3]};
+        f32x4 c = {dkv[NEB + eb][4 * gq], dkv[NEB + eb][4 * gq + 1], dkv[NEB + eb][4 * gq + 2],
+                   dkv[NEB + eb][4 * gq + 3]};
         a *= g.scale;
         if (acc) {
           a += *reinterpret_cast<const f32x4*>(krow + e);
@@ -454,7 +608,7 @@ extern "C" int tile_attention_fwd(void* stream, int64_t batch, int64_t heads, in
   if (!aligned16(Q) || !aligned16(O) || (k_len > 0 && (!aligned16(K) || !aligned16(V))))
     return tt::fail(TT_ERR_ARG, "tile_attention_fwd: tensors must be 16-byte aligned");
   AttnGeom g{(int)batch, (int)heads, (int)q_len, (int)k_len, q_off, k_off, scale};
-  dim3 grid((unsigned)((q_len + kBQ - 1) / kBQ), (unsigned)(batch * heads)), block(256);
+  dim3 grid((unsigned)((q_len + kBQ - 1) / kBQ), (unsigned)(batch * heads)), block(kNT);
   hipStream_t s = tt::as_stream(stream);
   switch (hd) {
     case 16: hipLaunchKernelGGL(attn_fwd<16>, grid, block, 0, s, g, Q, K, V, O, ml, lse, first, last); break;
@@ -491,7 +645,7 @@ extern "C" int tile_attention_bwd(void* stream, int phase, int64_t batch, int64_
   AttnGeom g{(int)batch, (int)heads, (int)q_len, (int)k_len, q_off, k_off, scale};
   dim3 gq((unsigned)((q_len + kBQ - 1) / kBQ), (unsigned)(batch * heads));
   dim3 gk((unsigned)((k_len + kBQ - 1) / kBQ), (unsigned)(batch * heads));
-  dim3 block(256);
+  dim3 block(kNT);
 #define TT_ATT_BWD(HD)                                                                                   \
   hipLaunchKernelGGL(attn_bwd_dq<HD>, gq, block, 0, s, g, Q, K, V, dO, lse, Dvec, dQ, acc_dq);          \
   hipLaunchKernelGGL(attn_bwd_dkv<HD>, gk, block, 0, s, g, Q, K, V, dO, lse, Dvec, dK, dV, acc_dkv)
