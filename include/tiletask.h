@@ -245,14 +245,17 @@ int tile_adamw_advance(void* stream, int32_t* step, float* bias_corr, float beta
 /* ---- auxiliary tile ops of the embedding layer and the linear backward ---- */
 
 /* tile_embedding_fwd -- token + position embedding for one (token tile, embd
- * tile): out[r*ldo + c] = wte[ids[r]*ld_wte + c] + wpe[pos_r*ld_wpe + c] with
- * pos_r = pos_offset + (r % seq_len). wte and wpe point at contiguous
- * [vocab x cols] and [positions x cols] slabs (one embd tile column of the
- * tiled tables). ids must lie in [0, vocab) -- checked on the device: an
- * out-of-range id writes NaN to its row and never reads out of bounds. */
+ * tile): out[r*ldo + c] = wte[(ids[r] - v_off)*ld_wte + c] + wpe[pos_r*ld_wpe + c]
+ * with pos_r = pos_offset + (r % seq_len), for the rows whose id lies in
+ * [v_off, v_off + v_len); wte points at that [v_len x cols] slab of the table
+ * (one vocab tile, or with v_off = 0 and v_len = vocab a whole embd tile
+ * column of the tiled table, which is contiguous) and wpe at a
+ * [positions x cols] slab. Other rows are left untouched, except that rows
+ * whose id is outside [0, vocab) get NaN when v_off == 0 -- ids are checked
+ * on the device and never read out of bounds. */
 int tile_embedding_fwd(void* stream, int64_t rows, int64_t cols, const int32_t* ids, int64_t vocab,
-                       const float* wte, int64_t ld_wte, const float* wpe, int64_t ld_wpe,
-                       int64_t seq_len, int64_t pos_offset, float* out, int64_t ldo);
+                       int64_t v_off, int64_t v_len, const float* wte, int64_t ld_wte, const float* wpe,
+                       int64_t ld_wpe, int64_t seq_len, int64_t pos_offset, float* out, int64_t ldo);
 
 /* tile_embedding_index -- stable sort of one token tile's ids: sorted_ids
  * ascending and perm (original row of each sorted entry), ties in row order.
@@ -305,8 +308,15 @@ typedef struct tt_tensor tt_tensor;
  * TT_DEVICE_DRYRUN builds a context that runs nothing: tensors get no
  * memory, submitted tasks are recorded with their inferred dependencies and
  * stream choice and can be dumped (tt_dump_dag); this is how the executor's
- * dependency inference is tested without a GPU. device_budget_bytes caps
- * the device memory used for tiles whose home is pinned host (0 = no cap).
+ * dependency inference is tested without a GPU. device_budget_bytes is the
+ * size of the device arena that holds copies of tiles whose home is pinned
+ * host (0 = half of the free device memory at first use). Such a tile is
+ * copied in (copy stream, H2D) before a task that reads it runs, and the
+ * tiles the next 4 tasks read are prefetched; when the arena is full the
+ * least recently used tile that the launching task does not access is
+ * evicted, written back first if a task changed it. Results do not depend
+ * on the budget. TT_ERR_OOM (latched, reported by the submit or wait that
+ * launches it) when the tiles of one task do not fit.
  * window = number of submitted tasks held before they are launched
  * (0 = default 512); a larger window gives the stream assignment more
  * look-ahead. One submitting thread per context. */
@@ -335,8 +345,9 @@ int tt_tensor_destroy(tt_tensor* t);
 int64_t tt_tensor_bytes(const tt_tensor* t);
 /* Number of tiles along axis d, and the total. */
 int tt_tensor_grid(const tt_tensor* t, int64_t* grid_out /* ndim */, int64_t* ntiles);
-/* Device pointer and extent of one tile (waits for pending tasks that write
- * it and makes it resident when its home is pinned host). */
+/* Device pointer and extent of one tile, after waiting for every submitted
+ * task. TT_ERR_UNSUPPORTED for a tensor whose home is pinned host: its
+ * device copy lives in the context's arena only while tasks use it. */
 int tt_tensor_tile(tt_tensor* t, const int64_t* tile_idx, void** dev_ptr, int64_t* extent);
 /* Dense row-major host array <-> tiled tensor (synchronous; waits for the
  * tensor's pending tasks). */
@@ -356,6 +367,10 @@ typedef struct {
     int64_t tile[TT_MAX_DIMS];
     int mode;            /* TT_R, TT_W or TT_RW */
 } tt_access;
+/* TT_W promises that the task overwrites EVERY element of the tile: for a
+ * pinned-host tile no copy-in precedes it. A task that updates part of a
+ * tile declares TT_RW. Accesses of one task to the same tile merge (any
+ * write makes the merged access a write). */
 /* A task that only declares accesses (runs nothing); label <= 31 chars. */
 int tt_submit_nop(tt_ctx* ctx, const char* label, const tt_access* acc, int n_acc);
 /* C(ic) = alpha op(A(ia)) op(B(ib)) + beta C(ic) on 2-D tiles (extents must

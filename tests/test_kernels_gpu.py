@@ -353,7 +353,7 @@ def test_embedding_fwd_bwd():
     ids[:10] = 7  # repeated ids
     out = empty((rows, d))
     IDS = dev(ids)
-    tt.tile_embedding_fwd(None, rows, d, IDS, vocab, dev(wte), d, dev(wpe), d, st, 0, out, d)
+    tt.tile_embedding_fwd(None, rows, d, IDS, vocab, 0, vocab, dev(wte), d, dev(wpe), d, st, 0, out, d)
     ref = wte[ids] + wpe[np.arange(rows) % st]
     assert np.array_equal(host(out), ref.astype(np.float32).astype(np.float64))
     srt = torch.empty(rows, dtype=torch.int32, device="cuda")
@@ -381,7 +381,7 @@ def test_embedding_out_of_range_id_gives_nan_row():
     wte = synth.rand_normal((5, 8), 1)
     wpe = synth.rand_normal((4, 8), 2)
     out = empty((4, 8), fill=0.0)
-    tt.tile_embedding_fwd(None, 4, 8, dev(ids), 5, dev(wte), 8, dev(wpe), 8, 4, 0, out, 8)
+    tt.tile_embedding_fwd(None, 4, 8, dev(ids), 5, 0, 5, dev(wte), 8, dev(wpe), 8, 4, 0, out, 8)
     got = host(out)
     assert np.isfinite(got[0]).all() and np.isnan(got[1]).all() and np.isnan(got[2]).all() and np.isnan(got[3]).all()
 

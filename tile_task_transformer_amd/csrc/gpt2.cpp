@@ -501,10 +501,18 @@ extern "C" int tt_gpt2_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hp
         h0->mat(lo, &r, &cols);
         std::vector<Access> acc = {R(ids, li), R(wpe, lp), W(h0, lo)};
         for (int64_t v = 0; v < NV; ++v) acc.push_back(R(wte, L(wte, {v, e})));
-        const int64_t lw = L(wte, {0, e});
+        const int64_t lw = L(wte, {0, e}), vt = std::min<int64_t>(g->t.vocab, V), nv = NV;
         TRY(ctx->submit("emb_fwd", acc, [=](hipStream_t s, void*) {
-          return tile_embedding_fwd(s, rows, cols, I32(ids, li), V, F(wte, lw), cols, F(wpe, lp), cols, sq, 0,
-                                    F(h0, lo), cols);
+          if (wte->home == TT_HOME_DEVICE)  // the vocab tiles of one embd column form one contiguous slab
+            return tile_embedding_fwd(s, rows, cols, I32(ids, li), V, 0, V, F(wte, lw), cols, F(wpe, lp), cols, sq, 0,
+                                      F(h0, lo), cols);
+          for (int64_t v = 0; v < nv; ++v) {  // staged tiles are separate: one gather per vocab tile
+            const int64_t lv = L(wte, {v, e}), v_off = v * vt;
+            int rc = tile_embedding_fwd(s, rows, cols, I32(ids, li), V, v_off, std::min(vt, V - v_off), F(wte, lv),
+                                        cols, F(wpe, lp), cols, sq, 0, F(h0, lo), cols);
+            if (rc) return rc;
+          }
+          return TT_OK;
         }));
       }
 

@@ -66,21 +66,23 @@ unsigned grid_for(int64_t work, int per_block = 256) {
 // -------------------------------------------------------------- embedding
 
 template <bool VEC>
-__global__ void emb_fwd(int rows, int cols, const int32_t* __restrict__ ids, int64_t vocab, const float* __restrict__ wte,
-                        int64_t ld_wte, const float* __restrict__ wpe, int64_t ld_wpe, int64_t seq_len,
-                        int64_t pos_off, float* __restrict__ out, int64_t ldo) {
+__global__ void emb_fwd(int rows, int cols, const int32_t* __restrict__ ids, int64_t vocab, int64_t v_off,
+                        int64_t v_len, const float* __restrict__ wte, int64_t ld_wte, const float* __restrict__ wpe,
+                        int64_t ld_wpe, int64_t seq_len, int64_t pos_off, float* __restrict__ out, int64_t ldo) {
   const int64_t cpr = (cols + 3) / 4;
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i >= (int64_t)rows * cpr) return;
   const int64_t r = i / cpr;
   const int c = (int)(i % cpr) * 4;
-  const int32_t id = ids[r];
+  const int64_t id = ids[r];
   f32x4 o;
   if (id < 0 || id >= vocab) {
+    if (v_off != 0) return;
     o = f32x4{NAN, NAN, NAN, NAN};
   } else {
+    if (id < v_off || id >= v_off + v_len) return;
     const int64_t pos = pos_off + r % seq_len;
-    o = tt::ld4<VEC>(wte, ld_wte, id, c, cols) + tt::ld4<VEC>(wpe, ld_wpe, pos, c, cols);
+    o = tt::ld4<VEC>(wte, ld_wte, id - v_off, c, cols) + tt::ld4<VEC>(wpe, ld_wpe, pos, c, cols);
   }
   tt::st4<VEC>(out, ldo, r, c, cols, o);
 }
@@ -185,10 +187,11 @@ extern "C" int tile_adamw_advance(void* stream, int32_t* step, float* bias_corr,
 }
 
 extern "C" int tile_embedding_fwd(void* stream, int64_t rows, int64_t cols, const int32_t* ids, int64_t vocab,
-                                  const float* wte, int64_t ld_wte, const float* wpe, int64_t ld_wpe, int64_t seq_len,
-                                  int64_t pos_offset, float* out, int64_t ldo) {
+                                  int64_t v_off, int64_t v_len, const float* wte, int64_t ld_wte, const float* wpe,
+                                  int64_t ld_wpe, int64_t seq_len, int64_t pos_offset, float* out, int64_t ldo) {
   using tt::fail;
   if (rows < 0 || cols < 0 || seq_len <= 0 || vocab <= 0) return fail(TT_ERR_ARG, "tile_embedding_fwd: bad size");
+  if (v_off < 0 || v_len < 0 || v_off + v_len > vocab) return fail(TT_ERR_ARG, "tile_embedding_fwd: bad vocab range");
   if (rows == 0 || cols == 0) return TT_OK;
   if (!ids || !wte || !wpe || !out || ld_wte < cols || ld_wpe < cols || ldo < cols)
     return fail(TT_ERR_ARG, "tile_embedding_fwd: bad argument");
@@ -199,11 +202,11 @@ extern "C" int tile_embedding_fwd(void* stream, int64_t rows, int64_t cols, cons
   dim3 grid((unsigned)((work + 255) / 256)), block(256);
   hipStream_t s = tt::as_stream(stream);
   if (vec)
-    hipLaunchKernelGGL(emb_fwd<true>, grid, block, 0, s, (int)rows, (int)cols, ids, vocab, wte, ld_wte, wpe, ld_wpe,
-                       seq_len, pos_offset, out, ldo);
+    hipLaunchKernelGGL(emb_fwd<true>, grid, block, 0, s, (int)rows, (int)cols, ids, vocab, v_off, v_len, wte, ld_wte,
+                       wpe, ld_wpe, seq_len, pos_offset, out, ldo);
   else
-    hipLaunchKernelGGL(emb_fwd<false>, grid, block, 0, s, (int)rows, (int)cols, ids, vocab, wte, ld_wte, wpe, ld_wpe,
-                       seq_len, pos_offset, out, ldo);
+    hipLaunchKernelGGL(emb_fwd<false>, grid, block, 0, s, (int)rows, (int)cols, ids, vocab, v_off, v_len, wte, ld_wte,
+                       wpe, ld_wpe, seq_len, pos_offset, out, ldo);
   return tt::launch_status("tile_embedding_fwd");
 }
 

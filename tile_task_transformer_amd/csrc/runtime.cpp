@@ -241,8 +241,10 @@ int tt_ctx::flush() {
         pending[d - window_base].need_event = true;
   // 3. launch in submission order
   if (launched.empty()) launched_base = window_base;
-  for (auto& task : pending) {
+  for (size_t ti = 0; ti < pending.size(); ++ti) {
+    tt::Task& task = pending[ti];
     const int s = task.stream;
+    cur_task = task.id;
     for (int64_t d : task.deps) {
       if (d < done_below) continue;
       tt::Launched* li = info(d);
@@ -303,24 +305,263 @@ int tt_ctx::flush() {
       }
     }
     launched.push_back(li);
+    if (!dryrun && !latched && arena) {
+      int rc = prefetch(ti);
+      if (rc != TT_OK && !latched) {
+        latched = rc;
+        latched_msg = std::string("prefetch: ") + tt_last_error();
+      }
+    }
   }
   pending.clear();
   if (latched) return fail(latched, "%s", latched_msg.c_str());
   return TT_OK;
 }
 
-int tt_ctx::make_resident(tt::Task& task, hipStream_t s) {
-  (void)s;
-  for (auto& a : task.acc)
-    if (a.ref.t->home == TT_HOME_PINNED_HOST)
-      return fail(TT_ERR_UNSUPPORTED, "pinned-host tiles are not resident-managed yet");
+// ---------------------------------------------------------------- residency
+//
+// Tiles whose home is pinned host RAM are staged into a device arena of
+// `budget` bytes before a task touches them: H2D copies on the copy stream,
+// and a task's stream waits for the copy stream before it runs. When the
+// arena is full, the least recently used tile that the task being launched
+// does not access is evicted (tiles prefetched for the next few tasks last):
+// the copy stream first waits for every launched task that used the device
+// copy, writes it back if the device copy is newer, then the space is
+// reused. A task writing a tile (TT_W) overwrites all of it, so no copy-in
+// is needed for it.
+
+int tt_ctx::arena_init() {
+  if (arena) return TT_OK;
+  size_t bytes = budget;
+  if (!bytes) {
+    size_t fr = 0, tot = 0;
+    TT_HIP_TRY(hipMemGetInfo(&fr, &tot));
+    bytes = fr / 2;
+  }
+  bytes &= ~(size_t)255;
+  hipError_t e = hipMalloc(&arena, bytes);
+  if (e != hipSuccess) return fail(TT_ERR_OOM, "residency arena hipMalloc(%zu) failed", bytes);
+  arena_bytes = bytes;
+  arena_free.clear();
+  arena_free[0] = bytes;
   return TT_OK;
+}
+
+void tt_ctx::arena_release(size_t off, size_t bytes) {
+  auto it = arena_free.emplace(off, bytes).first;
+  auto nx = std::next(it);
+  if (nx != arena_free.end() && it->first + it->second == nx->first) {
+    it->second += nx->second;
+    arena_free.erase(nx);
+  }
+  if (it != arena_free.begin()) {
+    auto pv = std::prev(it);
+    if (pv->first + pv->second == it->first) {
+      pv->second += it->second;
+      arena_free.erase(it);
+    }
+  }
+}
+
+// First-fit allocation of `bytes` (rounded to 256) in the arena, evicting
+// least recently used tiles until a hole fits. Tiles of the task being
+// launched are never evicted; tiles prefetched for the next tasks only when
+// nothing else frees room. With `soft` (a prefetch) the prefetched tiles are
+// spared and 1 is returned, with no error set, when no room can be made.
+int tt_ctx::arena_alloc(size_t bytes, size_t* off, bool soft) {
+  bytes = (bytes + 255) & ~(size_t)255;
+  if (bytes > arena_bytes)
+    return fail(TT_ERR_OOM, "tile of %zu bytes exceeds the device budget of %zu bytes", bytes, arena_bytes);
+  for (;;) {
+    for (auto it = arena_free.begin(); it != arena_free.end(); ++it)
+      if (it->second >= bytes) {
+        *off = it->first;
+        const size_t rest = it->second - bytes, at = it->first + bytes;
+        arena_free.erase(it);
+        if (rest) arena_free[at] = rest;
+        return TT_OK;
+      }
+    int rc = evict_one(true);
+    if (rc == 1 && !soft) rc = evict_one(false);
+    if (rc == 1) {
+      if (soft) return 1;
+      return fail(TT_ERR_OOM, "device budget of %zu bytes cannot hold the tiles one task needs", arena_bytes);
+    }
+    if (rc) return rc;
+  }
+}
+
+int tt_ctx::wait_users(tt_tensor* t, int64_t lin, hipStream_t s) {
+  for (int64_t u : t->res[lin].users) {
+    if (u < done_below || u >= cur_task) continue;
+    tt::Launched* li = info(u);
+    if (!li) continue;
+    if (li->event < 0) {
+      int ev;
+      if (int rc = acquire_event(&ev)) return rc;
+      TT_HIP_TRY(hipEventRecord(events[ev], streams[li->stream]));
+      li->event = ev;
+      li->seq = stream_seq[li->stream];
+    }
+    TT_HIP_TRY(hipStreamWaitEvent(s, events[li->event], 0));
+  }
+  return TT_OK;
+}
+
+// Evict the least recently used tile that the task being launched does not
+// access (and, with `spare_prefetched`, that no upcoming task was prefetched
+// for). Returns 1, with no error set, when there is no such tile.
+int tt_ctx::evict_one(bool spare_prefetched) {
+  int best = -1;
+  for (size_t i = 0; i < resident.size(); ++i) {
+    const tt::Residency& r = resident[i].t->res[resident[i].lin];
+    if (r.need >= cur_task) continue;
+    if (spare_prefetched && r.protect >= cur_task) continue;
+    if (best < 0 || r.last_use < resident[best].t->res[resident[best].lin].last_use) best = (int)i;
+  }
+  if (best < 0) return 1;
+  tt::TileRef v = resident[best];
+  tt::Residency& r = v.t->res[v.lin];
+  if (int rc = wait_users(v.t, v.lin, copy_stream)) return rc;
+  if (r.dev_valid && !r.host_valid) {
+    TT_HIP_TRY(hipMemcpyAsync(v.t->host + v.t->tile_off[v.lin] * 4, r.dev, v.t->tile_elems(v.lin) * 4,
+                              hipMemcpyDeviceToHost, copy_stream));
+    stats.d2h_bytes += v.t->tile_elems(v.lin) * 4;
+    r.host_valid = true;
+  }
+  arena_release(r.off, r.bytes);
+  r.dev = nullptr;
+  r.dev_valid = false;
+  r.users.clear();
+  resident[best] = resident.back();
+  resident.pop_back();
+  stats.evictions++;
+  copy_pending = true;
+  return TT_OK;
+}
+
+// device copy for tile (t, lin), allocated and (if `load`) filled from host;
+// `soft` as for arena_alloc (returns 1 when a prefetch finds no room)
+static int stage_tile(tt_ctx* c, tt_tensor* t, int64_t lin, bool load, bool soft) {
+  tt::Residency& r = t->res[lin];
+  if (!r.dev) {
+    size_t off;
+    const size_t bytes = (size_t)t->tile_elems(lin) * 4;
+    if (int rc = c->arena_alloc(bytes, &off, soft)) return rc;
+    r.dev = (float*)(c->arena + off);
+    r.off = off;
+    r.bytes = (bytes + 255) & ~(size_t)255;
+    r.dev_valid = false;
+    c->resident.push_back(tt::TileRef{t, lin});
+    c->copy_pending = true;
+  }
+  if (load && !r.dev_valid) {
+    if (!r.host_valid) return fail(TT_ERR_STATE, "tile has neither a valid host nor device copy");
+    TT_HIP_TRY(hipMemcpyAsync(r.dev, t->host + t->tile_off[lin] * 4, t->tile_elems(lin) * 4, hipMemcpyHostToDevice,
+                              c->copy_stream));
+    c->stats.h2d_bytes += t->tile_elems(lin) * 4;
+    r.dev_valid = true;
+    c->copy_pending = true;
+  }
+  return TT_OK;
+}
+
+int tt_ctx::make_resident(tt::Task& task, hipStream_t s) {
+  bool any = false;
+  for (auto& a : task.acc)
+    if (a.ref.t->home == TT_HOME_PINNED_HOST) {
+      any = true;
+      a.ref.t->res[a.ref.lin].need = task.id;
+    }
+  if (!any) return TT_OK;
+  if (int rc = arena_init()) return rc;
+  for (auto& a : task.acc) {
+    tt_tensor* t = a.ref.t;
+    if (t->home != TT_HOME_PINNED_HOST) continue;
+    if (int rc = stage_tile(this, t, a.ref.lin, (a.mode & TT_R) != 0, false)) return rc;
+  }
+  // the task's stream runs after every copy (and eviction) queued so far
+  if (copy_pending) {
+    int ev;
+    if (int rc = acquire_event(&ev)) return rc;
+    TT_HIP_TRY(hipEventRecord(events[ev], copy_stream));
+    copy_event = ev;
+    copy_pending = false;
+  }
+  if (copy_event >= 0) {
+    const int si = (int)(std::find(streams.begin(), streams.end(), s) - streams.begin());
+    if (si < n_streams && waited_copy[si] != copy_event) {
+      TT_HIP_TRY(hipStreamWaitEvent(s, events[copy_event], 0));
+      waited_copy[si] = copy_event;
+    }
+  }
+  for (auto& a : task.acc) {
+    tt_tensor* t = a.ref.t;
+    if (t->home != TT_HOME_PINNED_HOST) continue;
+    tt::Residency& r = t->res[a.ref.lin];
+    if (a.mode & TT_W) {
+      r.dev_valid = true;
+      r.host_valid = false;
+      r.users.clear();
+    }
+    r.users.push_back(task.id);
+    r.last_use = task.id;
+  }
+  return TT_OK;
+}
+
+// stage the pinned tiles that the next few tasks read, so their copies
+// overlap the current task (a tile written by an earlier one of those tasks
+// is not prefetched: its host copy would be stale)
+int tt_ctx::prefetch(size_t i) {
+  constexpr size_t kAhead = 4;
+  const size_t end = std::min(pending.size(), i + 1 + kAhead);
+  // task i has been launched: an eviction from here on must wait for it too
+  cur_task = pending[i].id + 1;
+  for (size_t j = i + 1; j < end; ++j)
+    for (auto& a : pending[j].acc)
+      if (a.ref.t->home == TT_HOME_PINNED_HOST) {
+        tt::Residency& r = a.ref.t->res[a.ref.lin];
+        r.protect = std::max(r.protect, pending[j].id);
+      }
+  for (size_t j = i + 1; j < end; ++j)
+    for (auto& a : pending[j].acc) {
+      tt_tensor* t = a.ref.t;
+      if (t->home != TT_HOME_PINNED_HOST || !(a.mode & TT_R)) continue;
+      tt::Residency& r = t->res[a.ref.lin];
+      if (r.dev_valid) continue;
+      bool written_before = false;
+      for (size_t k = i + 1; k < j && !written_before; ++k)
+        for (auto& b : pending[k].acc)
+          if (b.ref.t == t && b.ref.lin == a.ref.lin && (b.mode & TT_W)) written_before = true;
+      if (written_before) continue;
+      const int rc = stage_tile(this, t, a.ref.lin, true, true);
+      if (rc == 1) return TT_OK;  // no room without evicting what is needed next: stop here
+      if (rc) return rc;
+      stats.prefetches++;
+    }
+  return TT_OK;
+}
+
+void tt_ctx::drop_resident(tt_tensor* t) {
+  for (size_t i = 0; i < resident.size();)
+    if (resident[i].t == t) {
+      tt::Residency& r = t->res[resident[i].lin];
+      arena_release(r.off, r.bytes);
+      r.dev = nullptr;
+      resident[i] = resident.back();
+      resident.pop_back();
+    } else {
+      ++i;
+    }
 }
 
 int tt_ctx::wait_all() {
   int rc = flush();
   if (!dryrun) {
-    for (auto s : streams) {
+    std::vector<hipStream_t> all(streams);
+    if (copy_stream) all.push_back(copy_stream);
+    for (auto s : all) {
       hipError_t e = hipStreamSynchronize(s);
       if (e != hipSuccess && !latched) {
         latched = TT_ERR_HIP;
@@ -334,6 +575,9 @@ int tt_ctx::wait_all() {
   launched.clear();
   launched_base = next_id;
   events_used = 0;
+  copy_event = -1;
+  copy_pending = false;
+  std::fill(waited_copy.begin(), waited_copy.end(), -1);
   for (auto& w : waited) std::fill(w.begin(), w.end(), 0);
   for (int s = 0; s < n_streams; ++s) {
     stream_seq[s] = 0;
@@ -384,6 +628,7 @@ int tt_ctx_create(int device, int n_streams, int window, size_t device_budget_by
   c->stream_seq.assign(n_streams, 0);
   c->last_assigned.assign(n_streams, -1);
   c->waited.assign(n_streams, std::vector<int64_t>(n_streams, 0));
+  c->waited_copy.assign(n_streams, -1);
   if (!c->dryrun) {
     if (device < 0) return fail(TT_ERR_ARG, "tt_ctx_create: bad device %d", device);
     TT_HIP_TRY(hipSetDevice(device));
@@ -405,8 +650,10 @@ int tt_ctx_destroy(tt_ctx* c) {
     for (void* p : c->workspace)
       if (p) (void)hipFree(p);
     for (auto e : c->events) (void)hipEventDestroy(e);
+    for (auto e : c->prof_events) (void)hipEventDestroy(e);
     for (auto s : c->streams) (void)hipStreamDestroy(s);
     if (c->copy_stream) (void)hipStreamDestroy(c->copy_stream);
+    if (c->arena) (void)hipFree(c->arena);
   }
   delete c;
   return rc;
@@ -483,11 +730,10 @@ int tt_tensor_destroy(tt_tensor* t) {
     int rc = c->wait_all();
     (void)rc;
   }
+  c->drop_resident(t);  // device copies live in the context's arena
   if (t->owned) {
     if (t->base) (void)hipFree(t->base);
     if (t->host) (void)hipHostFree(t->host);
-    for (auto& r : t->res)
-      if (r.dev) (void)hipFree(r.dev);
   }
   auto it = std::find(c->tensors.begin(), c->tensors.end(), t);
   if (it != c->tensors.end()) c->tensors.erase(it);

@@ -14,6 +14,7 @@
 
 #include <chrono>
 #include <functional>
+#include <map>
 #include <memory>
 #include <string>
 #include <vector>
@@ -31,11 +32,14 @@ struct TileState {
 
 // Residency of one tile whose home is pinned host memory.
 struct Residency {
-  float* dev = nullptr;            // device copy (null if not resident)
+  float* dev = nullptr;            // device copy in the context's arena (null if not resident)
+  size_t off = 0, bytes = 0;       // its arena offset and size
   bool dev_valid = false;          // device copy holds the latest value
   bool host_valid = true;          // host copy holds the latest value
-  int64_t last_use = -1;           // task id of the last task using it
-  int64_t ready_seq = -1;          // copy-stream sequence of its H2D, if any
+  int64_t last_use = -1;           // id of the last task that used it (LRU order)
+  int64_t need = -1;               // id of the latest task being launched that accesses it
+  int64_t protect = -1;            // prefetched for tasks with id <= protect (evicted only under pressure)
+  std::vector<int64_t> users;      // launched tasks that touched the device copy since its last launched writer
 };
 
 }  // namespace tt
@@ -146,10 +150,24 @@ struct tt_ctx {
   std::vector<hipEvent_t> events;
   int events_used = 0;
 
-  // residency
-  size_t resident_bytes = 0;
-  int64_t copy_seq = 0;
-  std::vector<hipEvent_t> copy_events; // index by copy seq % ring
+  // residency of pinned-host tiles: device copies live in one arena of
+  // `budget` bytes (first-fit with coalescing); LRU eviction writes dirty
+  // tiles back on the copy stream
+  char* arena = nullptr;
+  size_t arena_bytes = 0;
+  std::map<size_t, size_t> arena_free;  // offset -> size
+  std::vector<tt::TileRef> resident;    // tiles with a device copy
+  int64_t cur_task = -1;                // id of the task being launched
+  bool copy_pending = false;            // copy-stream work not yet covered by copy_event
+  int copy_event = -1;                  // event after the latest copy-stream work
+  std::vector<int> waited_copy;         // per stream: copy_event it already waited on
+  int arena_init();
+  int arena_alloc(size_t bytes, size_t* off, bool soft);
+  void arena_release(size_t off, size_t bytes);
+  int evict_one(bool spare_prefetched);
+  int wait_users(tt_tensor* t, int64_t lin, hipStream_t s);
+  int prefetch(size_t i);
+  void drop_resident(tt_tensor* t);
 
   // per-task GPU timing (tt_ctx_profile): event pairs around matching launches
   bool prof_on = false;

@@ -91,8 +91,9 @@ def tile_adamw_advance(stream, step, bias_corr, beta1, beta2):
     return check(lib.tile_adamw_advance(stream_handle(stream), ptr(step), ptr(bias_corr), beta1, beta2))
 
 
-def tile_embedding_fwd(stream, rows, cols, ids, vocab, wte, ld_wte, wpe, ld_wpe, seq_len, pos_offset, out, ldo):
-    return check(lib.tile_embedding_fwd(stream_handle(stream), rows, cols, ptr(ids), vocab, ptr(wte), ld_wte,
+def tile_embedding_fwd(stream, rows, cols, ids, vocab, v_off, v_len, wte, ld_wte, wpe, ld_wpe, seq_len, pos_offset,
+                       out, ldo):
+    return check(lib.tile_embedding_fwd(stream_handle(stream), rows, cols, ptr(ids), vocab, v_off, v_len, ptr(wte), ld_wte,
                                         ptr(wpe), ld_wpe, seq_len, pos_offset, ptr(out), ldo))
 
 
