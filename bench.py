@@ -7,12 +7,17 @@ Prints ONE JSON line:
   value        tokens/s of the whole step (inputs resident in HBM)
   tflops       model TFLOP/s = 3 x forward matmul flops (causal attention
                counted over T(T+1)/2 pairs) / step time; mfma_frac = / 157.3
-  roofline     the dominant tile kernel: algorithmic flops per launch /
-               its average launch duration, timed with HIP events on the
+  roofline     the dominant GEMM task class (largest share of a step run
+               on one stream): its algorithmic flops per launch / its
+               average launch duration, timed with HIP events on the
                executor stream that launches it, during the timed steps
+  classes      every task class's achieved throughput against its roofline
+               (MFMA fp32 or HBM), from one extra step run on one stream
+               with each task timed, so no kernel shares the GPU
   cpu_baseline the fp64 oracle step timed on this host's cores on a bounded
                sample (one of the batch's sequences), scaled to tokens/s
-Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3]
+Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload NAME]
+       [--streams 4] [--pinned --budget-gb G]
 """
 from __future__ import annotations
 
@@ -22,15 +27,17 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+import synth  # noqa: E402
+
 METRIC = "GPT2 train tokens/sec + TFLOP/s (% fp32 MFMA peak) per fwd+bwd+AdamW step, 1 GPU"
 MFMA_FP32_PEAK = 157.3  # TFLOP/s, MI355X dense fp32 matrix
 HBM_PEAK = 8000.0       # GB/s
-GEMM_LABELS = ("qkv", "attn_proj", "fc", "mlp_proj", "head", "head_dw", "head_dx", "mlp_proj_dw", "mlp_proj_dx",
-               "fc_dw", "fc_dx", "attn_proj_dw", "attn_proj_dx", "qkv_dw", "qkv_dx")
 
 
 def model_flops(s) -> float:
@@ -41,20 +48,53 @@ def model_flops(s) -> float:
     return 3.0 * (s.n_layer * (per_block + attn) + head)
 
 
-def gemm_launch_flops(label, s, t) -> float:
-    """Algorithmic flops of one launch of a GEMM task class (2*m*n*k)."""
-    rows = t.batch * t.seq
-    et, it, vt = min(t.embd, s.n_embd), min(t.inner, s.n_inner), min(t.vocab, s.vocab)
-    hw = t.head * (s.n_embd // s.n_head)
-    table = {
-        "qkv": (rows, hw, et), "attn_proj": (rows, et, hw), "fc": (rows, it, et), "mlp_proj": (rows, et, it),
-        "head": (rows, vt, et), "head_dx": (rows, et, vt), "head_dw": (vt, et, rows),
-        "mlp_proj_dw": (it, et, rows), "mlp_proj_dx": (rows, it, et), "fc_dw": (et, it, rows),
-        "fc_dx": (rows, et, it), "attn_proj_dw": (hw, et, rows), "attn_proj_dx": (rows, hw, et),
-        "qkv_dw": (et, hw, rows), "qkv_dx": (rows, et, hw),
-    }
-    m, n, k = table[label]
-    return 2.0 * m * n * k
+def class_work(s) -> dict:
+    """Algorithmic work of each task class over one step: label -> (bound,
+    amount, unit). GEMM classes count 2*m*n*k over all their tiles (ragged
+    tiles included, so dividing by the launch count gives the exact mean per
+    launch); attention counts causal pairs T(T+1)/2, the backward as 5
+    products against the forward's 2 (its recompute of P included); memory
+    classes count the bytes each kernel must move at least."""
+    n, d, i, v, L = s.batch * s.seq, s.n_embd, s.n_inner, s.vocab, s.n_layer
+    f = {"qkv": 2.0 * n * d * 3 * d * L, "attn_proj": 2.0 * n * d * d * L, "fc": 2.0 * n * d * i * L,
+         "mlp_proj": 2.0 * n * i * d * L, "head": 2.0 * n * d * v}
+    out = {}
+    for k, x in f.items():
+        for suf in ("", "_dx", "_dw"):
+            out[k + suf] = ("mfma", x, "flop")
+    att = 2 * 2 * s.batch * d * (s.seq * (s.seq + 1) // 2) * L
+    out["attn_fwd"] = ("mfma", float(att), "flop")
+    out["attn_bwd"] = ("mfma", 2.5 * att, "flop")
+    out["ln_fwd"] = ("hbm", 8.0 * n * d * (2 * L + 1), "B")
+    out["ln_bwd"] = ("hbm", 16.0 * n * d * (2 * L + 1), "B")
+    out["ce_stats"] = ("hbm", 4.0 * n * v, "B")
+    out["ce_grad"] = ("hbm", 8.0 * n * v, "B")
+    out["colsum"] = ("hbm", 4.0 * n * (3 * d + d + i + d) * L, "B")
+    n_params = sum(int(np.prod(shp)) for _, shp, _ in synth.param_specs(s))
+    out["adamw"] = ("hbm", 28.0 * n_params, "B")
+    return out
+
+
+# task labels whose kernels together do one class's work (LayerNorm over
+# several embd tiles runs as partial statistics, merge and apply tasks)
+CLASS_LABELS = {"ln_fwd": ("ln_fwd", "ln_part", "ln_merge", "ln_apply"), "ln_bwd": ("ln_bwd", "lnb_part", "lnb_apply")}
+
+
+def class_rooflines(breakdown: dict, s) -> dict:
+    """Per-class achieved throughput from a serialized profiled step."""
+    res = {}
+    for label, (bound, amount, unit) in class_work(s).items():
+        parts = [breakdown[x] for x in CLASS_LABELS.get(label, (label,)) if x in breakdown]
+        b = {"count": sum(x["count"] for x in parts), "total_ms": sum(x["total_ms"] for x in parts)}
+        if not b["count"]:
+            continue
+        sec = b["total_ms"] * 1e-3
+        peak = MFMA_FP32_PEAK if bound == "mfma" else HBM_PEAK
+        ach = amount / sec / (1e12 if bound == "mfma" else 1e9)
+        res[label] = {"bound": bound, "launches": b["count"], "ms": round(b["total_ms"], 3),
+                      "per_launch": amount / b["count"], "unit_per_launch": unit, "achieved": round(ach, 2),
+                      "unit": "TFLOP/s" if bound == "mfma" else "GB/s", "frac": round(ach / peak, 4)}
+    return res
 
 
 GEMM_SHAPES = {  # label -> (transA, transB, m, n, k, epilogue, beta) in tile terms
@@ -185,11 +225,14 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="gpt2_small")
+    ap.add_argument("--workload", default="gpt2_small", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--streams", type=int, default=4)
+    ap.add_argument("--pinned", action="store_true",
+                    help="parameters, gradients and moments live in pinned host RAM (out-of-core residency)")
+    ap.add_argument("--budget-gb", type=float, default=0.0, help="device arena for pinned tiles (0 = half of free)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", default=os.path.join("gpurun_out", "bench_breakdown.json"),
-                    help="per-task-class GPU times of one extra profiled step ('' = skip)")
+                    help="per-task-class GPU times of one extra step run on one stream ('' = skip)")
     ap.add_argument("--tile-classes", default="",
                     help="instead of the step: time each tile-op class alone and write this JSON file")
     a = ap.parse_args(argv)
@@ -197,10 +240,9 @@ def main(argv=None):
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
-    import synth
+    from tile_task_transformer_amd import _lib as L
     from tile_task_transformer_amd.runtime import Context, GPT2
 
     w = synth.WORKLOADS[a.workload]
@@ -215,32 +257,49 @@ def main(argv=None):
         return 0
     s, t = w.shape, w.tiles
     specs = synth.param_specs(s)
-    params = synth.init_params(s, seed=0)
+    t0 = time.perf_counter()
+    params = synth.init_params(s, seed=0, threads=min(16, os.cpu_count() or 1))
     tokens = synth.token_stream(s, seed=1)
-    ctx = Context(0, n_streams=a.streams, window=4096)
-    model = GPT2(ctx, s, t)
+    home = L.TT_HOME_PINNED_HOST if a.pinned else L.TT_HOME_DEVICE
+    ctx = Context(0, n_streams=a.streams, window=4096, device_budget=int(a.budget_gb * 2 ** 30))
+    model = GPT2(ctx, s, t, param_home=home)
     model.set_params(params, specs)
+    if a.no_cpu_baseline:
+        params = None  # the oracle sample is not needed: free the host copy
     tok = torch.from_numpy(tokens.astype(np.int32)).cuda()
     hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
+    print(f"[bench] {a.workload}: parameters ready in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
 
-    for _ in range(a.warmup):
+    for k in range(a.warmup):
         model.step(tok, **hp)
-    loss0 = model.loss()
-    print(f"[bench] warmup done, loss {loss0:.4f}, {model.task_count()} tasks/step", file=sys.stderr, flush=True)
+        print(f"[bench] warmup step {k + 1}/{a.warmup} loss {model.loss():.4f}", file=sys.stderr, flush=True)
+    print(f"[bench] {model.task_count()} tasks/step", file=sys.stderr, flush=True)
 
-    breakdown = {}
+    # one step on a single stream with every task timed: each kernel has the
+    # GPU to itself, which gives the per-class rooflines
+    breakdown, classes = {}, {}
     if a.breakdown:
+        ctx.streams_active(1)
         ctx.profile("*")
         model.step(tok, **hp)
         breakdown = ctx.profile_take()
         ctx.profile(None)
+        ctx.streams_active(a.streams)
+        classes = class_rooflines(breakdown, s)
         os.makedirs(os.path.dirname(a.breakdown) or ".", exist_ok=True)
         with open(a.breakdown, "w") as f:
-            json.dump(breakdown, f, indent=1, sort_keys=True)
-    gemm_times = {k: v["total_ms"] for k, v in breakdown.items() if k in GEMM_LABELS}
-    dominant = max(gemm_times, key=gemm_times.get) if gemm_times else "fc"
+            json.dump({"workload": a.workload, "tasks": breakdown, "classes": classes}, f, indent=1, sort_keys=True)
+        print("[bench] serialized step by class (ms, achieved, % of roofline):", file=sys.stderr)
+        for k, v in sorted(classes.items(), key=lambda kv: -kv[1]["ms"]):
+            print(f"  {k:14s} {v['ms']:9.2f} ms  {v['achieved']:9.1f} {v['unit']:8s} {100 * v['frac']:5.1f}%",
+                  file=sys.stderr)
+        print(f"  serialized total {sum(b['total_ms'] for b in breakdown.values()):.2f} ms", file=sys.stderr,
+              flush=True)
+    work = class_work(s)
+    mfma_ms = {k: v["ms"] for k, v in classes.items() if v["bound"] == "mfma" and not k.startswith("attn")}
+    dominant = max(mfma_ms, key=mfma_ms.get) if mfma_ms else "fc"
 
-    # timed region: K steps back to back, the dominant GEMM class bracketed by events
+    # timed region: K steps back to back, the dominant class bracketed by events
     ctx.profile(dominant)
     ctx.reset_stats()
     torch.cuda.synchronize()
@@ -259,25 +318,34 @@ def main(argv=None):
     ms = 1e3 * elapsed / a.steps
     tok_s = s.batch * s.seq / (elapsed / a.steps)
     tflops = model_flops(s) / (elapsed / a.steps) / 1e12
-    per_launch = gemm_launch_flops(dominant, s, t)
-    avg_ms = prof["total_ms"] / prof["count"] if prof.get("count") else float("nan")
+    launches = prof.get("count", 0)
+    per_launch = work[dominant][1] / (launches / a.steps) if launches else float("nan")
+    avg_ms = prof["total_ms"] / launches if launches else float("nan")
     achieved = per_launch / (avg_ms * 1e-3) / 1e12
     out = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": a.workload, "global_batch": s.batch, "seq_len": s.seq, "n_layer": s.n_layer,
-                   "n_embd": s.n_embd, "vocab": s.vocab,
+                   "n_embd": s.n_embd, "n_inner": s.n_inner, "n_head": s.n_head, "vocab": s.vocab,
                    "tiles": {"batch": t.batch, "seq": t.seq, "embd": t.embd, "inner": t.inner, "head": t.head,
-                             "vocab": t.vocab}, "streams": a.streams},
+                             "vocab": t.vocab}, "streams": a.streams,
+                   "param_home": "pinned_host" if a.pinned else "device"},
         "tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_FP32_PEAK, 4),
         "tasks_per_step": model.task_count(), "loss": round(loss, 5),
         "host_submit_ms_per_step": round(1e3 * st["submit_seconds"] / a.steps, 3),
         "roofline": {"bound": "mfma", "kernel": f"tile_gemm[{dominant}]", "achieved": round(achieved, 2),
                      "peak": MFMA_FP32_PEAK, "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP32_PEAK, 4),
                      "traffic": None, "flops_per_launch": per_launch, "avg_launch_ms": round(avg_ms, 4),
-                     "launches": prof.get("count", 0)},
+                     "launches": launches},
     }
+    if a.pinned:
+        out["residency"] = {k: st[k] / a.steps for k in ("h2d_bytes", "d2h_bytes", "evictions", "prefetches")}
+        out["residency"]["link_GBps"] = round((st["h2d_bytes"] + st["d2h_bytes"]) / elapsed / 1e9, 2)
+        out["residency"]["budget_gb"] = a.budget_gb
+    if classes:
+        out["classes"] = {k: {"frac": v["frac"], "achieved": v["achieved"], "unit": v["unit"], "ms": v["ms"]}
+                          for k, v in classes.items()}
     print(f"[bench] timed {a.steps} steps: {ms:.2f} ms/step, {tok_s:.0f} tokens/s, {tflops:.1f} TFLOP/s",
           file=sys.stderr, flush=True)
     model.close()

@@ -325,6 +325,11 @@ int tt_ctx_destroy(tt_ctx* ctx);
 /* hipStream_t of executor stream i (for callers that want to order their own
  * work after the context's). */
 int tt_ctx_stream(tt_ctx* ctx, int i, void** stream);
+/* Launch the tasks submitted from now on on streams 0..n-1 only (1 <= n <=
+ * n_streams; TT_ERR_ARG otherwise). n = 1 runs the task graph in submission
+ * order on one stream, so every kernel has the GPU to itself (per-task
+ * timing); results do not depend on n. */
+int tt_ctx_streams_active(tt_ctx* ctx, int n);
 /* Keep (on != 0) or drop the per-task records tt_dump_dag writes; dry-run
  * contexts record by default, device contexts do not. */
 int tt_ctx_record(tt_ctx* ctx, int on);
@@ -452,6 +457,12 @@ int tt_gpt2_param(tt_gpt2* g, int index, tt_tensor** param, tt_tensor** grad,
  * the mean loss. */
 int tt_gpt2_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams* hp, int do_update);
 int tt_gpt2_loss(tt_gpt2* g, float* loss_host);
+/* Per-token losses of the last step's forward, lse - z[label] for every
+ * (b, t), written to host memory as float [batch, seq] row-major (the
+ * caller owns out_host, batch*seq floats). Waits for the step. Their mean
+ * is the loss. Position t depends only on tokens 0..t of its window
+ * (causal attention), so a prefix of the window reproduces it. */
+int tt_gpt2_row_losses(tt_gpt2* g, float* out_host);
 /* Number of tasks the last step submitted. */
 int tt_gpt2_task_count(tt_gpt2* g, int64_t* n);
 

@@ -192,6 +192,15 @@ def forward(params: Dict[str, np.ndarray], x: np.ndarray, y: np.ndarray, n_layer
     return loss, cache
 
 
+def row_losses(params: Dict[str, np.ndarray], x: np.ndarray, y: np.ndarray, n_layer: int, n_head: int,
+               ln_eps: float = 1e-5) -> np.ndarray:
+    """Per-token next-token losses [B, T]: logsumexp of the row's logits
+    minus its label's logit, i.e. the terms whose mean is the loss (R7)."""
+    _, cache = forward(params, x, y, n_layer, n_head, ln_eps)
+    z, lse = cache["z"], cache["lse"]
+    return (lse - z[np.arange(z.shape[0]), y.reshape(-1)]).reshape(x.shape)
+
+
 def backward(cache, n_layer: int, n_head: int) -> Dict[str, np.ndarray]:
     """Analytic gradients of the mean loss w.r.t. every parameter (float64)."""
     P, x = cache["P"], cache["x"]

@@ -135,8 +135,17 @@ def init_param(spec: Tuple[str, Tuple[int, ...], str], index: int, seed: int = 0
     return (rng.standard_normal(shape) * std).astype(np.float32)
 
 
-def init_params(s: GPT2Shape, seed: int = 0, std: float = 0.02) -> Dict[str, np.ndarray]:
-    return {spec[0]: init_param(spec, i, seed, std) for i, spec in enumerate(param_specs(s))}
+def init_params(s: GPT2Shape, seed: int = 0, std: float = 0.02, threads: int = 1) -> Dict[str, np.ndarray]:
+    """Every parameter, in param_specs order. Each tensor has its own seeded
+    stream, so `threads` (drawing several tensors at once) changes nothing
+    but the wall time."""
+    specs = param_specs(s)
+    if threads <= 1:
+        return {spec[0]: init_param(spec, i, seed, std) for i, spec in enumerate(specs)}
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(threads) as ex:
+        arrs = list(ex.map(lambda a: init_param(a[1], a[0], seed, std), enumerate(specs)))
+    return {spec[0]: arr for spec, arr in zip(specs, arrs)}
 
 
 def token_stream(s: GPT2Shape, seed: int = 1) -> np.ndarray:

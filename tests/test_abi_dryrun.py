@@ -91,6 +91,28 @@ def test_stream_assignment_keeps_chains_and_spreads_independent_work(tmp_path):
     assert st["tasks"] == 9 and st["edges"] == 4 + 4
 
 
+def test_streams_active_narrows_the_assignment(tmp_path):
+    with Context(L.TT_DEVICE_DRYRUN, n_streams=4) as ctx:
+        a = ctx.tensor((8,), (1,))
+        for i in range(4):
+            ctx.submit_nop("w", [(a, (i,), L.TT_W)])
+        ctx.streams_active(1)
+        for i in range(4):                     # chains from streams 1..3 cannot continue there
+            ctx.submit_nop("rw", [(a, (i,), L.TT_RW)])
+        ctx.streams_active(2)
+        for i in range(4, 8):
+            ctx.submit_nop("w2", [(a, (i,), L.TT_W)])
+        with pytest.raises(L.TTError):
+            ctx.streams_active(5)
+        with pytest.raises(L.TTError):
+            ctx.streams_active(0)
+        dag = ctx.dump_dag(str(tmp_path / "dag.jsonl"))
+    s = [r["stream"] for r in dag]
+    assert sorted(s[:4]) == [0, 1, 2, 3]
+    assert s[4:8] == [0, 0, 0, 0]
+    assert sorted(s[8:]) == [0, 0, 1, 1]
+
+
 def test_ksplit_gemm_chain_edges(tmp_path):
     with Context(L.TT_DEVICE_DRYRUN, n_streams=2) as ctx:
         A = ctx.tensor((64, 96), (64, 32))    # 3 K tiles

@@ -88,6 +88,27 @@ def test_softmax_rows_and_causality():
     assert np.abs(og.logsumexp(s) - np.log(np.exp(s).sum(-1))).max() <= 1e-12
 
 
+def test_row_losses_depend_on_the_prefix_only():
+    """Causal attention: the loss at position t is fixed by tokens 0..t, so a
+    window cut after t reproduces it, and changing a later token does not
+    move it; the per-token losses average to the loss."""
+    params = _rich_params(TINY)
+    rng = np.random.default_rng(5)
+    tok = rng.integers(0, TINY.vocab, size=(TINY.batch, TINY.seq + 1))
+    x, y = tok[:, :-1], tok[:, 1:]
+    full = og.row_losses(params, x, y, TINY.n_layer, TINY.n_head)
+    loss, _ = og.forward(params, x, y, TINY.n_layer, TINY.n_head)
+    assert abs(full.mean() - loss) <= 1e-13
+    for p in range(1, TINY.seq):
+        pre = og.row_losses(params, x[:, :p], y[:, :p], TINY.n_layer, TINY.n_head)
+        assert np.abs(pre - full[:, :p]).max() <= 1e-13
+    x2 = x.copy()
+    x2[:, -1] = (x2[:, -1] + 1) % TINY.vocab
+    moved = og.row_losses(params, x2, y, TINY.n_layer, TINY.n_head)
+    assert np.abs(moved[:, :-1] - full[:, :-1]).max() <= 1e-13
+    assert np.abs(moved[:, -1] - full[:, -1]).max() > 1e-6
+
+
 def test_layernorm_statistics():
     rng = np.random.default_rng(1)
     x = rng.standard_normal((6, 33)) * 3 + 2

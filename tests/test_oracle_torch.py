@@ -120,6 +120,9 @@ def test_gpt2_matches_transformers_fp64():
     assert np.abs(logits.detach().numpy().reshape(-1, shape.vocab) - cache["z"]).max() <= 1e-11
     lt = F.cross_entropy(logits.reshape(-1, shape.vocab), torch.tensor(y).reshape(-1))
     assert abs(lt.item() - loss) <= 1e-12
+    per_tok = F.cross_entropy(logits.reshape(-1, shape.vocab), torch.tensor(y).reshape(-1), reduction="none")
+    rl = og.row_losses(params, x, y, shape.n_layer, shape.n_head)
+    assert np.abs(rl - per_tok.detach().numpy().reshape(x.shape)).max() <= 1e-11
     lt.backward()
     own = dict(model.transformer.named_parameters())
     names = {"wte.weight": "wte", "wpe.weight": "wpe", "ln_f.weight": "lnf_g", "ln_f.bias": "lnf_b"}

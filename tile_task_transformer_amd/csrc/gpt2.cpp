@@ -448,6 +448,23 @@ extern "C" int tt_gpt2_loss(tt_gpt2* g, float* loss) {
   return TT_OK;
 }
 
+extern "C" int tt_gpt2_row_losses(tt_gpt2* g, float* out) {
+  clear_error();
+  if (!g || !out) return fail(TT_ERR_ARG, "tt_gpt2_row_losses: null");
+  if (g->ctx->dryrun) return fail(TT_ERR_STATE, "tt_gpt2_row_losses: dry-run context");
+  // row_loss is [token tile, row]: token tile bi + nb*si holds rows (b in the
+  // batch tile) * seq_tile + (t in the seq tile)
+  std::vector<float> tiles((size_t)(g->ntok * g->rows));
+  TRY(tt_tensor_copy_out(g->row_loss, tiles.data()));
+  const int64_t T = g->c.seq, bt = g->t.batch, sq = g->t.seq;
+  for (int64_t b = 0; b < g->c.batch; ++b)
+    for (int64_t t = 0; t < T; ++t) {
+      const int64_t ti = b / bt + g->nb * (t / sq), r = (b % bt) * sq + t % sq;
+      out[b * T + t] = tiles[ti * g->rows + r];
+    }
+  return TT_OK;
+}
+
 // -------------------------------------------------------------------- step
 
 extern "C" int tt_gpt2_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams* hp, int do_update) {

@@ -222,14 +222,14 @@ int tt_ctx::flush() {
       int ds = -1;
       if (d >= window_base) ds = pending[d - window_base].stream;
       else if (auto* li = info(d)) ds = li->stream;
-      if (ds >= 0 && last_assigned[ds] == d && d > best_id) {
+      if (ds >= 0 && ds < active_streams && last_assigned[ds] == d && d > best_id) {
         best = ds;
         best_id = d;
       }
     }
     if (best < 0) {
-      best = rr;
-      rr = (rr + 1) % n_streams;
+      best = rr % active_streams;
+      rr = (best + 1) % active_streams;
     }
     task.stream = best;
     last_assigned[best] = task.id;
@@ -621,6 +621,7 @@ int tt_ctx_create(int device, int n_streams, int window, size_t device_budget_by
   c->dryrun = device == TT_DEVICE_DRYRUN;
   c->device = c->dryrun ? -1 : device;
   c->n_streams = n_streams;
+  c->active_streams = n_streams;
   c->window = window ? window : 512;
   c->budget = device_budget_bytes;
   c->record = c->dryrun;
@@ -662,6 +663,13 @@ int tt_ctx_destroy(tt_ctx* c) {
 int tt_ctx_stream(tt_ctx* c, int i, void** stream) {
   if (!c || !stream || i < 0 || i >= c->n_streams) return fail(TT_ERR_ARG, "tt_ctx_stream: bad argument");
   *stream = c->dryrun ? nullptr : (void*)c->streams[i];
+  return TT_OK;
+}
+
+int tt_ctx_streams_active(tt_ctx* c, int n) {
+  if (!c || n < 1 || n > c->n_streams) return fail(TT_ERR_ARG, "tt_ctx_streams_active: n must be 1..n_streams");
+  if (int rc = c->flush()) return rc;
+  c->active_streams = n;
   return TT_OK;
 }
 

@@ -121,6 +121,7 @@ struct tt_ctx {
   int device = 0;
   bool dryrun = false;
   int n_streams = 1;
+  int active_streams = 1;  // tasks go to streams 0..active_streams-1
   int window = 512;
   size_t budget = 0;
   bool record = false;

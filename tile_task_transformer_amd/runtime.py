@@ -41,6 +41,10 @@ class Context:
         check(lib.tt_ctx_stream(self.h, i, C.byref(s)))
         return s.value or 0
 
+    def streams_active(self, n: int):
+        """Launch later tasks on streams 0..n-1 only (1 = one stream, in order)."""
+        check(lib.tt_ctx_streams_active(self.h, n))
+
     def record(self, on: bool = True):
         check(lib.tt_ctx_record(self.h, int(on)))
 
@@ -196,6 +200,12 @@ class GPT2:
         f = C.c_float()
         check(lib.tt_gpt2_loss(self.h, C.byref(f)))
         return f.value
+
+    def row_losses(self) -> np.ndarray:
+        """Per-token losses [batch, seq] of the last step's forward."""
+        out = np.empty((self.shape.batch, self.shape.seq), np.float32)
+        check(lib.tt_gpt2_row_losses(self.h, out.ctypes.data_as(C.POINTER(C.c_float))))
+        return out
 
     def task_count(self) -> int:
         n = C.c_int64()
