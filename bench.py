@@ -40,6 +40,30 @@ MFMA_FP32_PEAK = 157.3  # TFLOP/s, MI355X dense fp32 matrix
 HBM_PEAK = 8000.0       # GB/s
 
 
+# HBM bytes per launch of a task class, from two rocprofv3 --pmc runs of the
+# class alone at its task shape (FETCH_SIZE, then WRITE_SIZE, KiB per
+# dispatch, summed over the dispatches one task makes), each scaled by what
+# the counter reads for a 1 GiB device copy (FETCH_SIZE reads half the bytes
+# on gfx950: factor 2.0; WRITE_SIZE: 1.0). Valid only for the kernel source
+# the counters were taken on (sha256 prefix of the file); else null.
+TRAFFIC = {
+    ("gpt2_small", "head_dw"): {"source": "tile_task_transformer_amd/csrc/gemm.hip", "sha256": "257fe531472aa611",
+                                "fetch_kib": 12391.29 + 10393.53, "fetch_factor": 2.0,
+                                "write_kib": 18432.0 + 2304.0, "write_factor": 1.0},
+}
+
+
+def traffic_bytes(workload: str, label: str):
+    import hashlib
+    t = TRAFFIC.get((workload, label))
+    if not t:
+        return None
+    with open(os.path.join(ROOT, t["source"]), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest()[:16] != t["sha256"]:
+            return None
+    return 1024.0 * (t["fetch_kib"] * t["fetch_factor"] + t["write_kib"] * t["write_factor"])
+
+
 def model_flops(s) -> float:
     n = s.batch * s.seq
     per_block = 2 * n * s.n_embd * (3 * s.n_embd + s.n_embd + 2 * s.n_inner)
@@ -111,9 +135,10 @@ GEMM_SHAPES = {  # label -> (transA, transB, m, n, k, epilogue, beta) in tile te
 }
 
 
-def tile_classes(w, reps=20):
-    """Each tile-op class of the workload, launched alone on one stream at its
-    task shape; HIP-event time per launch against its roofline."""
+def tile_classes(w, reps=20, only=None):
+    """Each tile-op class of the workload (or just `only`), launched alone on
+    one stream at its task shape; HIP-event time per launch against its
+    roofline."""
     import math
 
     import torch
@@ -141,6 +166,8 @@ def tile_classes(w, reps=20):
 
     out = {}
     for label, f in GEMM_SHAPES.items():
+        if only and label != only:
+            continue
         ta, tb, m, n, k, epi, beta = f(r, e, i, h, v)
         A = rnd(k, m) if ta else rnd(m, k)
         B = rnd(n, k) if tb else rnd(k, n)
@@ -153,6 +180,8 @@ def tile_classes(w, reps=20):
         tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
         out[label] = {"bound": "mfma", "shape": [m, n, k, ta, tb], "us": round(ms * 1e3, 1),
                       "achieved": round(tf, 2), "unit": "TFLOP/s", "frac": round(tf / MFMA_FP32_PEAK, 4)}
+    if only:
+        return out
     # attention (per (batch tile, head tile) pair of the workload's seq tile)
     Q, K, V = rnd(t.batch, t.seq, t.head, hd), rnd(t.batch, t.seq, t.head, hd), rnd(t.batch, t.seq, t.head, hd)
     O, dO = torch.empty_like(Q), rnd(t.batch, t.seq, t.head, hd)
@@ -202,6 +231,56 @@ def tile_classes(w, reps=20):
     return out
 
 
+def copy_probe(mib: int):
+    """A plain device-to-device copy of `mib` MiB (torch's copy kernel), three
+    times: the known byte count calibrates the profiler's memory counters."""
+    import torch
+    n = mib * 2 ** 20 // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty(n, device="cuda")
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def pmc_summary(paths, copy_mib: int) -> dict:
+    """Mean FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per (kernel, grid) from
+    rocprofv3 counter_collection.csv files, and the factor that maps each
+    counter to bytes: the known size of the copy probe over what the counter
+    reads for it."""
+    import csv
+    from collections import defaultdict
+    acc = defaultdict(lambda: [0.0, 0])
+    durations = defaultdict(list)
+    for p in paths:
+        with open(p) as f:
+            for row in csv.DictReader(f):
+                if "Counter_Name" in row:
+                    key = (row["Counter_Name"], row["Kernel_Name"], int(row["Grid_Size"]))
+                    acc[key][0] += float(row["Counter_Value"])
+                    acc[key][1] += 1
+                else:  # a kernel trace: durations per (kernel, grid)
+                    grid = 1
+                    for ax in ("X", "Y", "Z"):
+                        grid *= int(row.get("Grid_Size_" + ax, 1) or 1)
+                    durations[(row["Kernel_Name"], grid)].append(
+                        (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) * 1e-3)
+    out = {"kernels": [], "copy_bytes": copy_mib * 2 ** 20}
+    for (ctr, name, grid), (tot, cnt) in sorted(acc.items()):
+        out["kernels"].append({"counter": ctr, "kernel": name[:160], "grid": grid, "dispatches": cnt,
+                               "mean_kib": tot / cnt})
+    for (name, grid), us in sorted(durations.items(), key=lambda kv: -sum(kv[1])):
+        out["kernels"].append({"kernel": name[:160], "grid": grid, "dispatches": len(us),
+                               "mean_us": sum(us) / len(us), "total_ms": sum(us) * 1e-3})
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        copies = [k for k in out["kernels"] if k.get("counter") == ctr and "copy" in k["kernel"].lower()
+                  and k["mean_kib"] * 1024 > 0.5 * out["copy_bytes"]]
+        if copies:
+            c = max(copies, key=lambda k: k["mean_kib"])
+            out[ctr + "_factor"] = out["copy_bytes"] / (c["mean_kib"] * 1024)
+    return out
+
+
 def cpu_baseline(w, params, tokens):
     """The fp64 oracle on the host, one sequence of the batch (bounded sample)."""
     import numpy as np
@@ -235,7 +314,16 @@ def main(argv=None):
                     help="per-task-class GPU times of one extra step run on one stream ('' = skip)")
     ap.add_argument("--tile-classes", default="",
                     help="instead of the step: time each tile-op class alone and write this JSON file")
+    ap.add_argument("--only", default=None, help="with --tile-classes: just this GEMM class")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the run, copy this many MiB three times (counter calibration)")
+    ap.add_argument("--pmc-summary", nargs="+", default=None,
+                    help="instead of running: summarise rocprofv3 counter_collection.csv files")
     a = ap.parse_args(argv)
+    if a.pmc_summary:
+        res = pmc_summary(a.pmc_summary, a.copy_probe_mib)
+        print(json.dumps(res, indent=1))
+        return 0
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
         return 2
@@ -247,7 +335,9 @@ def main(argv=None):
 
     w = synth.WORKLOADS[a.workload]
     if a.tile_classes:
-        res = tile_classes(w)
+        res = tile_classes(w, only=a.only)
+        if a.copy_probe_mib:
+            copy_probe(a.copy_probe_mib)
         os.makedirs(os.path.dirname(a.tile_classes) or ".", exist_ok=True)
         with open(a.tile_classes, "w") as f:
             json.dump(res, f, indent=1)
@@ -336,7 +426,8 @@ def main(argv=None):
         "host_submit_ms_per_step": round(1e3 * st["submit_seconds"] / a.steps, 3),
         "roofline": {"bound": "mfma", "kernel": f"tile_gemm[{dominant}]", "achieved": round(achieved, 2),
                      "peak": MFMA_FP32_PEAK, "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP32_PEAK, 4),
-                     "traffic": None, "flops_per_launch": per_launch, "avg_launch_ms": round(avg_ms, 4),
+                     "traffic": traffic_bytes(a.workload, dominant), "flops_per_launch": per_launch,
+                     "avg_launch_ms": round(avg_ms, 4),
                      "launches": launches},
     }
     if a.pinned:
