@@ -306,6 +306,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gpt2_small", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--streams", type=int, default=4)
+    ap.add_argument("--heavy-gflops", type=float, default=0.0,
+                    help="tasks of at least this many GFLOP run in order on stream 0 (0 = off)")
     ap.add_argument("--pinned", action="store_true",
                     help="parameters, gradients and moments live in pinned host RAM (out-of-core residency)")
     ap.add_argument("--budget-gb", type=float, default=0.0, help="device arena for pinned tiles (0 = half of free)")
@@ -352,6 +354,8 @@ def main(argv=None):
     tokens = synth.token_stream(s, seed=1)
     home = L.TT_HOME_PINNED_HOST if a.pinned else L.TT_HOME_DEVICE
     ctx = Context(0, n_streams=a.streams, window=4096, device_budget=int(a.budget_gb * 2 ** 30))
+    if a.heavy_gflops > 0:
+        ctx.heavy_lane(a.heavy_gflops * 1e9)
     model = GPT2(ctx, s, t, param_home=home)
     model.set_params(params, specs)
     if a.no_cpu_baseline:
@@ -401,9 +405,9 @@ def main(argv=None):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     loss = model.loss()
+    st = ctx.stats()
     prof = ctx.profile_take().get(dominant, {})
     ctx.profile(None)
-    st = ctx.stats()
 
     ms = 1e3 * elapsed / a.steps
     tok_s = s.batch * s.seq / (elapsed / a.steps)
@@ -419,7 +423,7 @@ def main(argv=None):
         "config": {"workload": a.workload, "global_batch": s.batch, "seq_len": s.seq, "n_layer": s.n_layer,
                    "n_embd": s.n_embd, "n_inner": s.n_inner, "n_head": s.n_head, "vocab": s.vocab,
                    "tiles": {"batch": t.batch, "seq": t.seq, "embd": t.embd, "inner": t.inner, "head": t.head,
-                             "vocab": t.vocab}, "streams": a.streams,
+                             "vocab": t.vocab}, "streams": a.streams, "heavy_gflops": a.heavy_gflops,
                    "param_home": "pinned_host" if a.pinned else "device"},
         "tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_FP32_PEAK, 4),
         "tasks_per_step": model.task_count(), "loss": round(loss, 5),

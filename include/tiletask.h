@@ -330,6 +330,13 @@ int tt_ctx_stream(tt_ctx* ctx, int i, void** stream);
  * order on one stream, so every kernel has the GPU to itself (per-task
  * timing); results do not depend on n. */
 int tt_ctx_streams_active(tt_ctx* ctx, int n);
+/* Heavy lane (min_flops > 0, with at least 2 active streams): tasks whose
+ * flop estimate (GEMM 2mnk, attention 4·hd per visible pair forward, 10·hd
+ * backward) is at least min_flops run in submission order on stream 0,
+ * every other task on streams 1..n-1. A kernel that fills every CU gains
+ * nothing from sharing the GPU with another one; the light memory-bound
+ * tasks still overlap with it. 0 = off (default). Results do not change. */
+int tt_ctx_heavy_lane(tt_ctx* ctx, double min_flops);
 /* Keep (on != 0) or drop the per-task records tt_dump_dag writes; dry-run
  * contexts record by default, device contexts do not. */
 int tt_ctx_record(tt_ctx* ctx, int on);
@@ -456,6 +463,20 @@ int tt_gpt2_param(tt_gpt2* g, int index, tt_tensor** param, tt_tensor** grad,
  * ids in [0, vocab). The step is queued; tt_gpt2_loss waits and returns
  * the mean loss. */
 int tt_gpt2_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams* hp, int do_update);
+/* Graph replay (on != 0): the next tt_gpt2_step records its tasks into one
+ * HIP graph (kernels, copies and cross-stream waits; nothing runs while
+ * recording) and launches it; later steps with the same tokens pointer,
+ * hyperparameters and do_update launch that graph again instead of
+ * submitting the tasks one by one. The tokens buffer is read when the graph
+ * runs, so its contents may change between steps; another pointer or other
+ * hyperparameters record a new graph. The AdamW step count lives in device
+ * memory, so replays advance it. Results are bitwise those of the task-by-
+ * task step. TT_ERR_UNSUPPORTED for pinned-host parameters or a dry-run
+ * context; per-task timing (tt_ctx_profile) is refused while recording.
+ * CURRENTLY DISABLED: on != 0 always returns TT_ERR_UNSUPPORTED (the first
+ * GPU run of a recorded step ended in a host-side fault not yet explained);
+ * on = 0 is accepted. */
+int tt_gpt2_set_replay(tt_gpt2* g, int on);
 int tt_gpt2_loss(tt_gpt2* g, float* loss_host);
 /* Per-token losses of the last step's forward, lse - z[label] for every
  * (b, t), written to host memory as float [batch, seq] row-major (the

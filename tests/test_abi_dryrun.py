@@ -113,6 +113,27 @@ def test_streams_active_narrows_the_assignment(tmp_path):
     assert sorted(s[8:]) == [0, 0, 1, 1]
 
 
+def test_heavy_lane_puts_large_tasks_in_order_on_stream_zero(tmp_path):
+    with Context(L.TT_DEVICE_DRYRUN, n_streams=4) as ctx:
+        ctx.heavy_lane(1e6)
+        A = ctx.tensor((256, 256), (128, 128))
+        a = ctx.tensor((8,), (1,))
+        C = ctx.tensor((256, 256), (128, 128))
+        for i in range(2):                     # 2*128^3 flops each: heavy
+            for j in range(2):
+                ctx.submit_gemm(0, 0, 1.0, A, (i, 0), A, (0, j), 0.0, C, (i, j))
+        for i in range(6):                     # light, independent
+            ctx.submit_nop("w", [(a, (i,), L.TT_W)])
+        ctx.submit_nop("rd", [(C, (0, 0), L.TT_R)])  # light reader of a heavy result
+        with pytest.raises(L.TTError):
+            ctx.heavy_lane(-1.0)
+        dag = ctx.dump_dag(str(tmp_path / "dag.jsonl"))
+    s = [r["stream"] for r in dag]
+    assert s[:4] == [0, 0, 0, 0]
+    assert all(x in (1, 2, 3) for x in s[4:])
+    assert sorted(s[4:10]) == [1, 1, 2, 2, 3, 3]
+
+
 def test_ksplit_gemm_chain_edges(tmp_path):
     with Context(L.TT_DEVICE_DRYRUN, n_streams=2) as ctx:
         A = ctx.tensor((64, 96), (64, 32))    # 3 K tiles

@@ -104,6 +104,7 @@ SIGNATURES = {
     "tt_ctx_stream": (I, [P, I, PP]),
     "tt_ctx_record": (I, [P, I]),
     "tt_ctx_streams_active": (I, [P, I]),
+    "tt_ctx_heavy_lane": (I, [P, C.c_double]),
     "tt_tensor_create": (I, [P, I, C.POINTER(I64), C.POINTER(I64), I, I, PP]),
     "tt_tensor_wrap": (I, [P, I, C.POINTER(I64), C.POINTER(I64), I, P, PP]),
     "tt_tensor_destroy": (I, [P]),
@@ -129,6 +130,7 @@ SIGNATURES = {
     "tt_gpt2_loss": (I, [P, C.POINTER(F)]),
     "tt_gpt2_task_count": (I, [P, C.POINTER(I64)]),
     "tt_gpt2_row_losses": (I, [P, C.POINTER(F)]),
+    "tt_gpt2_set_replay": (I, [P, I]),
 }
 
 for _name, (_res, _args) in SIGNATURES.items():

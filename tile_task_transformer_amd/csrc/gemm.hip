@@ -7,11 +7,10 @@
 //   * a workgroup of 256 threads (4 wave64s, 2x2) computes a BM x BN block of
 //     C; each wave owns a (BM/2) x (BN/2) sub-block made of 32x32 MFMA tiles
 //     whose fp32 accumulators stay in registers for the whole K loop;
-//   * K advances in steps of BK = 32 through two LDS buffers: the next step's
-//     global loads are issued before the current step's MFMAs and written to
-//     the other buffer afterwards, so one barrier per step suffices; 32
-//     floats of K are 128 bytes, one full cache line per row of a
-//     K-contiguous operand;
+//   * K advances in steps of BK (16 or 32, per plan) through two LDS
+//     buffers: the next step's global loads are issued before the current
+//     step's MFMAs and written to the other buffer afterwards, so one
+//     barrier per step suffices;
 //   * each operand is staged in LDS in the orientation it has in HBM, so the
 //     global->LDS path is always 16-byte vector loads/stores:
 //       K-contiguous operands (A, or B^T)  -> LDS [rows][BK + 4]
@@ -29,11 +28,13 @@
 //     weight-gradient GEMMs, K = tokens), S workgroups share a C block, each
 //     reducing a K range into its own slice of a workspace; a second kernel
 //     adds the slices in slice order and applies the epilogue (deterministic:
-//     no atomics).
+//     no atomics). S is picked so the workgroup count sits just under a
+//     multiple of the CU count.
 // Ragged M, N, K are handled by zero-filling out-of-range loads and
 // predicating stores; leading dimensions that are not multiples of 4 (or
 // unaligned pointers) select a scalar-load instantiation.
 #include <cstdlib>
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -43,6 +44,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kSplitAlign = 32;  // split-K chunks are multiples of every BK used
+constexpr int64_t kCUs = 256;    // MI355X compute units (8 XCDs x 32)
 
 struct GemmArgs {
   int m, n, k;
@@ -266,13 +268,32 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
 }
 
 // Sum of the split-K slices in slice order, then the epilogue.
+// Each thread sums VEC consecutive elements; the loads of up to 8 slices are
+// issued together, the additions stay in slice order.
+template <int VEC>
 __global__ __launch_bounds__(256) void gemm_split_finish(GemmArgs g) {
-  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  using V = typename std::conditional<VEC == 4, f32x4, float>::type;
+  const int64_t i = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) * VEC;
   const int64_t mn = (int64_t)g.m * g.n;
   if (i >= mn) return;
-  float s = 0.f;
-  for (int z = 0; z < g.splits; ++z) s += g.ws[z * mn + i];
-  epilogue_store(g, (int)(i / g.n), (int)(i % g.n), g.alpha * s);
+  const V* w = reinterpret_cast<const V*>(g.ws + i);
+  const int64_t stride = mn / VEC;
+  V s = {};
+  int z = 0;
+  for (; z + 8 <= g.splits; z += 8) {
+    V v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = w[(z + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; z < g.splits; ++z) s += w[z * stride];
+  if constexpr (VEC == 4) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) epilogue_store(g, (int)((i + e) / g.n), (int)((i + e) % g.n), g.alpha * s[e]);
+  } else {
+    epilogue_store(g, (int)(i / g.n), (int)(i % g.n), g.alpha * s);
+  }
 }
 
 template <int BM, int BN, int BK, bool TA, bool TB, bool SPLIT>
@@ -328,14 +349,26 @@ Plan plan_for(int64_t m, int64_t n, int64_t k, size_t ws_bytes) {
   if (blocks(128, 128) >= want) return p;
   const int64_t b128 = blocks(128, 128);
   if (k >= 2048 && b128 <= 144 && ws_bytes > 0) {
-    int s = (int)std::min<int64_t>((want + b128 - 1) / b128, k / 512);
-    while (s > 1 && (size_t)s * m * n * sizeof(float) > ws_bytes) --s;
-    if (s > 1) {
+    // split count by CU balance: workgroups run in rounds of one per CU, so
+    // b128*s just under a multiple of 256 keeps every CU equally loaded
+    // (measured: 36 tiles x 7 beats x 8 by 1.3x, 144 tiles x 7 beats x 4)
+    int best_s = 1;
+    int64_t best_chunk = k;
+    double best_bal = 0.0;
+    for (int s = 2; s <= 8; ++s) {
       int64_t chunk = (k + s - 1) / s;
       chunk = (chunk + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
-      s = (int)((k + chunk - 1) / chunk);
-      if (s > 1) return Plan{128, 128, 32, s, (int)chunk};
+      const int64_t sa = (k + chunk - 1) / chunk;
+      if (chunk < 256 || (size_t)sa * m * n * sizeof(float) > ws_bytes) continue;
+      const int64_t nwg = b128 * sa;
+      const double bal = (double)nwg / (double)(((nwg + kCUs - 1) / kCUs) * kCUs);
+      if (bal > best_bal + 0.01) {
+        best_bal = bal;
+        best_s = (int)sa;
+        best_chunk = chunk;
+      }
     }
+    if (best_s > 1) return Plan{128, 128, 32, best_s, (int)best_chunk};
   }
   return Plan{64, 64, 32, 1, (int)k};
 }
@@ -346,11 +379,23 @@ int launch_t(GemmArgs g, bool va, bool vb, size_t ws_bytes, hipStream_t s) {
   g.splits = p.splits;
   g.kchunk = p.kchunk;
   if (p.splits > 1) {
-    if (p.bk == 16) launch_v<128, 128, 16, TA, TB, true>(g, va, vb, s);
-    else launch_v<128, 128, 32, TA, TB, true>(g, va, vb, s);
+    if (p.bk == 16) {
+      if (p.bm == 128 && p.bn == 128) launch_v<128, 128, 16, TA, TB, true>(g, va, vb, s);
+      else if (p.bm == 128) launch_v<128, 64, 16, TA, TB, true>(g, va, vb, s);
+      else launch_v<64, 64, 16, TA, TB, true>(g, va, vb, s);
+    } else {
+      if (p.bm == 128 && p.bn == 128) launch_v<128, 128, 32, TA, TB, true>(g, va, vb, s);
+      else if (p.bm == 128) launch_v<128, 64, 32, TA, TB, true>(g, va, vb, s);
+      else launch_v<64, 64, 32, TA, TB, true>(g, va, vb, s);
+    }
     if (int rc = tt::launch_status("tile_gemm(split)")) return rc;
     const int64_t mn = (int64_t)g.m * g.n;
-    hipLaunchKernelGGL(gemm_split_finish, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, s, g);
+    // the workspace comes from hipMalloc (256-byte aligned) and each slice
+    // plane starts at a multiple of mn floats
+    if (mn % 4 == 0 && (reinterpret_cast<uintptr_t>(g.ws) & 15) == 0)
+      hipLaunchKernelGGL(gemm_split_finish<4>, dim3((unsigned)((mn / 4 + 255) / 256)), dim3(256), 0, s, g);
+    else
+      hipLaunchKernelGGL(gemm_split_finish<1>, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, s, g);
     return tt::launch_status("tile_gemm(split finish)");
   }
   if (p.bk == 16) {

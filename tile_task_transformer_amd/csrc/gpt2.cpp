@@ -55,6 +55,15 @@ struct tt_gpt2 {
             *dk = nullptr, *dv = nullptr, *Dv = nullptr;
   tt_tensor *step = nullptr, *bc = nullptr;
   int64_t last_tasks = 0;
+  // graph replay of the whole step (tt_gpt2_set_replay): the captured graph
+  // and the arguments it was captured with
+  bool replay = false;
+  hipGraphExec_t graph = nullptr;
+  const int32_t* graph_tokens = nullptr;
+  tt_adamw_hparams graph_hp{};
+  int graph_update = 0;
+  int64_t graph_tasks = 0;
+  int64_t graph_ws_gen = -1;
 
   enum { WTE = 0, WPE = 1 };
   int pidx(int layer, int which) const { return 2 + 12 * layer + which; }
@@ -117,7 +126,7 @@ int submit_gemm(tt_ctx* ctx, const char* label, const Gemm& q) {
                         F(p.C.t, p.C.lin), cc, p.epi, p.bias.valid() ? F(p.bias.t, p.bias.lin) : nullptr,
                         p.res.valid() ? F(p.res.t, p.res.lin) : nullptr, ldr,
                         p.aux.valid() ? F(p.aux.t, p.aux.lin) : nullptr, ldaux, ws, ws ? ctx->workspace_bytes : 0);
-  });
+  }, 2.0 * m * n * k);
 }
 
 int fill_task(tt_ctx* ctx, tt_tensor* t, int64_t lin, float v) {
@@ -244,9 +253,29 @@ int colsum_task(tt_ctx* ctx, tt_tensor* x, int64_t lx, tt_tensor* out, int64_t l
 extern "C" int tt_gpt2_destroy(tt_gpt2* g) {
   if (!g) return fail(TT_ERR_ARG, "tt_gpt2_destroy: null");
   int rc = g->ctx->dryrun ? TT_OK : g->ctx->wait_all();
+  if (g->graph) (void)hipGraphExecDestroy(g->graph);
   for (auto it = g->owned.rbegin(); it != g->owned.rend(); ++it) tt_tensor_destroy(*it);
   delete g;
   return rc;
+}
+
+extern "C" int tt_gpt2_set_replay(tt_gpt2* g, int on) {
+  clear_error();
+  if (!g) return fail(TT_ERR_ARG, "tt_gpt2_set_replay: null");
+  if (on && g->ctx->dryrun) return fail(TT_ERR_UNSUPPORTED, "tt_gpt2_set_replay: dry-run context");
+  // Switched off: the first GPU run of a recorded step ended in a host-side
+  // segmentation fault whose cause has not been found; the recording path
+  // stays unreachable until it is.
+  if (on) return fail(TT_ERR_UNSUPPORTED, "tt_gpt2_set_replay: graph replay is disabled in this build");
+  if (on && g->param_home != TT_HOME_DEVICE)
+    return fail(TT_ERR_UNSUPPORTED, "tt_gpt2_set_replay: pinned-host parameters are staged at launch time");
+  if (!on && g->graph) {
+    TRY(g->ctx->wait_all());
+    (void)hipGraphExecDestroy(g->graph);
+    g->graph = nullptr;
+  }
+  g->replay = on != 0;
+  return TT_OK;
 }
 
 extern "C" int tt_gpt2_create(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_gpt2_tiles* tiles, int param_home,
@@ -467,11 +496,41 @@ extern "C" int tt_gpt2_row_losses(tt_gpt2* g, float* out) {
 
 // -------------------------------------------------------------------- step
 
+static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams* hp, int do_update);
+
 extern "C" int tt_gpt2_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams* hp, int do_update) {
   clear_error();
   if (!g || !hp) return fail(TT_ERR_ARG, "tt_gpt2_step: null argument");
   tt_ctx* ctx = g->ctx;
   if (!tokens && !ctx->dryrun) return fail(TT_ERR_ARG, "tt_gpt2_step: null tokens");
+  if (!g->replay) return submit_step(g, tokens, hp, do_update);
+  const bool same = g->graph && g->graph_tokens == tokens && g->graph_update == do_update &&
+                    !memcmp(&g->graph_hp, hp, sizeof(*hp)) && g->graph_ws_gen == ctx->workspace_gen;
+  if (!same) {
+    if (g->graph) {
+      TRY(ctx->wait_all());
+      (void)hipGraphExecDestroy(g->graph);
+      g->graph = nullptr;
+    }
+    TRY(ctx->capture_begin());
+    const int rc = submit_step(g, tokens, hp, do_update);
+    hipGraphExec_t exec = nullptr;
+    const int rc2 = ctx->capture_end(rc == TT_OK ? &exec : nullptr);
+    if (rc != TT_OK) return rc;
+    if (rc2 != TT_OK) return rc2;
+    g->graph = exec;
+    g->graph_tokens = tokens;
+    g->graph_hp = *hp;
+    g->graph_update = do_update;
+    g->graph_tasks = g->last_tasks;
+    g->graph_ws_gen = ctx->workspace_gen;
+  }
+  g->last_tasks = g->graph_tasks;
+  return ctx->graph_launch(g->graph);
+}
+
+static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams* hp, int do_update) {
+  tt_ctx* ctx = g->ctx;
   const int64_t t0 = ctx->next_id;
   const tt_gpt2_config& c = g->c;
   const int64_t B = c.batch, T = c.seq, hd = g->hd, V = c.vocab;
@@ -575,10 +634,12 @@ extern "C" int tt_gpt2_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hp
             std::vector<Access> acc = {R(Q, lq), R(K, lk), R(Vt, lk), first ? W(O, lq) : RW(O, lq)};
             if (!(first && last)) acc.push_back(first ? W(ml, lm) : RW(ml, lm));
             if (last) acc.push_back(W(lse, ls));
+            // QK^T and PV over the visible (query, key) pairs of the tile pair
+            const double pairs = last ? sq * (sq + 1) / 2.0 : (double)sq * sq;
             TRY(ctx->submit("attn_fwd", acc, [=](hipStream_t s, void*) {
               return tile_attention_fwd(s, bt, ht, sq, sq, hd, qi * sq, ki * sq, F(Q, lq), F(K, lk), F(Vt, lk),
                                         F(O, lq), F(ml, lm), F(lse, ls), first, last, scale);
-            }));
+            }, 4.0 * bt * ht * hd * pairs));
           }
     for (int64_t bi = 0; bi < g->nb; ++bi)
       for (int64_t si = 0; si < g->ns; ++si) {
@@ -854,7 +915,8 @@ extern "C" int tt_gpt2_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hp
                                                         F(K, lk), F(Vt, lk), nullptr, F(dO, lq), F(lse, ls),
                                                         F(Dv, ls), F(dq, lq), F(dk, lk), F(dv, lk), acc_q, acc_kv,
                                                         scale);
-                            }));
+                            },
+                            10.0 * bt * ht * hd * (qi == ki ? sq * (sq + 1) / 2.0 : (double)sq * sq)));
           }
       }
     // QKV projection backward

@@ -153,6 +153,7 @@ int tt_ctx::ensure_workspace(size_t bytes) {
   for (void* p : workspace)
     if (p) (void)hipFree(p);
   workspace.assign(n_streams, nullptr);
+  ++workspace_gen;
   for (int s = 0; s < n_streams; ++s) {
     hipError_t e = hipMalloc(&workspace[s], bytes);
     if (e != hipSuccess) return fail(TT_ERR_OOM, "workspace hipMalloc(%zu) failed", bytes);
@@ -161,7 +162,7 @@ int tt_ctx::ensure_workspace(size_t bytes) {
   return TT_OK;
 }
 
-int tt_ctx::submit(const char* label, std::vector<tt::Access> acc, tt::LaunchFn run) {
+int tt_ctx::submit(const char* label, std::vector<tt::Access> acc, tt::LaunchFn run, double cost) {
   if (latched) return fail(TT_ERR_STATE, "context has a latched error: %s", latched_msg.c_str());
   auto t0 = std::chrono::steady_clock::now();
   tt::Task task;
@@ -203,6 +204,7 @@ int tt_ctx::submit(const char* label, std::vector<tt::Access> acc, tt::LaunchFn 
   stats.edges += (int64_t)task.deps.size();
   task.acc = std::move(merged);
   task.run = std::move(run);
+  task.cost = cost;
   if (pending.empty()) window_base = task.id;
   pending.push_back(std::move(task));
   int rc = TT_OK;
@@ -214,22 +216,32 @@ int tt_ctx::submit(const char* label, std::vector<tt::Access> acc, tt::LaunchFn 
 int tt_ctx::flush() {
   if (pending.empty()) return latched;
   // 1. stream assignment: continue the chain of a dependency that is still the
-  //    tail of its stream, else spread independent work round-robin.
+  //    tail of its stream, else spread independent work round-robin. With a
+  //    heavy lane, tasks of at least heavy_flops run in order on stream 0
+  //    (a kernel that fills every CU gains nothing from sharing the GPU with
+  //    another such kernel) and the light ones use the other streams, where
+  //    they overlap with it.
+  const bool lane = heavy_flops > 0 && active_streams > 1;
+  const int lo = lane ? 1 : 0;
   for (auto& task : pending) {
     int best = -1;
-    int64_t best_id = -1;
-    for (int64_t d : task.deps) {
-      int ds = -1;
-      if (d >= window_base) ds = pending[d - window_base].stream;
-      else if (auto* li = info(d)) ds = li->stream;
-      if (ds >= 0 && ds < active_streams && last_assigned[ds] == d && d > best_id) {
-        best = ds;
-        best_id = d;
+    if (lane && task.cost >= heavy_flops) {
+      best = 0;
+    } else {
+      int64_t best_id = -1;
+      for (int64_t d : task.deps) {
+        int ds = -1;
+        if (d >= window_base) ds = pending[d - window_base].stream;
+        else if (auto* li = info(d)) ds = li->stream;
+        if (ds >= lo && ds < active_streams && last_assigned[ds] == d && d > best_id) {
+          best = ds;
+          best_id = d;
+        }
       }
-    }
-    if (best < 0) {
-      best = rr % active_streams;
-      rr = (best + 1) % active_streams;
+      if (best < 0) {
+        best = lo + (rr - lo + (active_streams - lo)) % (active_streams - lo);
+        rr = lo + (best - lo + 1) % (active_streams - lo);
+      }
     }
     task.stream = best;
     last_assigned[best] = task.id;
@@ -470,6 +482,7 @@ int tt_ctx::make_resident(tt::Task& task, hipStream_t s) {
   bool any = false;
   for (auto& a : task.acc)
     if (a.ref.t->home == TT_HOME_PINNED_HOST) {
+      if (capturing) return fail(TT_ERR_UNSUPPORTED, "pinned-host tiles cannot be captured into a graph");
       any = true;
       a.ref.t->res[a.ref.lin].need = task.id;
     }
@@ -557,6 +570,7 @@ void tt_ctx::drop_resident(tt_tensor* t) {
 }
 
 int tt_ctx::wait_all() {
+  if (capturing) return fail(TT_ERR_STATE, "cannot wait while a graph is being captured");
   int rc = flush();
   if (!dryrun) {
     std::vector<hipStream_t> all(streams);
@@ -570,7 +584,12 @@ int tt_ctx::wait_all() {
     }
   }
   if (!latched && !dryrun) prof_collect();
-  // everything submitted so far has completed
+  forget_launched();  // everything submitted so far has completed
+  if (latched) return fail(latched, "%s", latched_msg.c_str());
+  return rc;
+}
+
+void tt_ctx::forget_launched() {
   done_below = next_id;
   launched.clear();
   launched_base = next_id;
@@ -583,8 +602,69 @@ int tt_ctx::wait_all() {
     stream_seq[s] = 0;
     last_assigned[s] = -1;
   }
-  if (latched) return fail(latched, "%s", latched_msg.c_str());
+}
+
+// ------------------------------------------------------------ graph capture
+//
+// Stream 0 starts the capture; every other stream joins it by waiting on an
+// event recorded there, so the kernels, copies and event waits the flushes
+// issue on any stream become nodes and edges of one graph. At the end every
+// stream's tail is joined back into stream 0. Per-task timing and
+// pinned-host tiles (whose copies are decided at launch time) are not
+// capturable.
+
+int tt_ctx::capture_begin() {
+  if (dryrun) return fail(TT_ERR_UNSUPPORTED, "graph capture needs a device context");
+  if (capturing) return fail(TT_ERR_STATE, "a capture is already open");
+  if (prof_on) return fail(TT_ERR_STATE, "per-task timing is on: it cannot be captured");
+  if (int rc = wait_all()) return rc;
+  TT_HIP_TRY(hipStreamBeginCapture(streams[0], hipStreamCaptureModeThreadLocal));
+  capturing = true;
+  int ev;
+  if (int rc = acquire_event(&ev)) return rc;
+  TT_HIP_TRY(hipEventRecord(events[ev], streams[0]));
+  for (int s = 1; s < n_streams; ++s) TT_HIP_TRY(hipStreamWaitEvent(streams[s], events[ev], 0));
+  return TT_OK;
+}
+
+int tt_ctx::capture_end(hipGraphExec_t* out) {
+  if (!capturing) return fail(TT_ERR_STATE, "no capture is open");
+  int rc = flush();
+  hipError_t e = hipSuccess;
+  for (int s = 1; s < n_streams && e == hipSuccess; ++s) {
+    int ev;
+    if (acquire_event(&ev)) break;
+    e = hipEventRecord(events[ev], streams[s]);
+    if (e == hipSuccess) e = hipStreamWaitEvent(streams[0], events[ev], 0);
+  }
+  hipGraph_t graph = nullptr;
+  const hipError_t e2 = hipStreamEndCapture(streams[0], &graph);
+  capturing = false;
+  forget_launched();  // the graph carries the order of what was captured
+  if (rc == TT_OK && latched) rc = fail(latched, "%s", latched_msg.c_str());
+  if (rc == TT_OK && e != hipSuccess) rc = fail(TT_ERR_HIP, "capture join: %s", hipGetErrorString(e));
+  if (rc == TT_OK && e2 != hipSuccess) rc = fail(TT_ERR_HIP, "hipStreamEndCapture: %s", hipGetErrorString(e2));
+  if (rc == TT_OK && out) {
+    const hipError_t e3 = hipGraphInstantiate(out, graph, nullptr, nullptr, 0);
+    if (e3 != hipSuccess) rc = fail(TT_ERR_HIP, "hipGraphInstantiate: %s", hipGetErrorString(e3));
+  }
+  if (graph) (void)hipGraphDestroy(graph);
   return rc;
+}
+
+int tt_ctx::graph_launch(hipGraphExec_t exec) {
+  if (latched) return fail(TT_ERR_STATE, "context has a latched error: %s", latched_msg.c_str());
+  if (capturing) return fail(TT_ERR_STATE, "cannot launch a graph while capturing");
+  if (int rc = flush()) return rc;
+  TT_HIP_TRY(hipGraphLaunch(exec, streams[0]));
+  // work submitted later, on any stream, runs after the graph
+  int ev;
+  if (int rc = acquire_event(&ev)) return rc;
+  TT_HIP_TRY(hipEventRecord(events[ev], streams[0]));
+  for (int s = 1; s < n_streams; ++s) TT_HIP_TRY(hipStreamWaitEvent(streams[s], events[ev], 0));
+  forget_launched();
+  events_used = ev + 1;  // keep the join event alive until the next drain
+  return TT_OK;
 }
 
 int tt_ctx::prof_collect() {
@@ -673,6 +753,13 @@ int tt_ctx_streams_active(tt_ctx* c, int n) {
   return TT_OK;
 }
 
+int tt_ctx_heavy_lane(tt_ctx* c, double min_flops) {
+  if (!c || !(min_flops >= 0)) return fail(TT_ERR_ARG, "tt_ctx_heavy_lane: bad argument");
+  if (int rc = c->flush()) return rc;
+  c->heavy_flops = min_flops;
+  return TT_OK;
+}
+
 int tt_ctx_record(tt_ctx* c, int on) {
   if (!c) return fail(TT_ERR_ARG, "tt_ctx_record: null");
   c->record = on != 0;
@@ -681,6 +768,7 @@ int tt_ctx_record(tt_ctx* c, int on) {
 
 int tt_ctx_profile(tt_ctx* c, const char* label_filter) {
   if (!c) return fail(TT_ERR_ARG, "tt_ctx_profile: null");
+  if (c->capturing) return fail(TT_ERR_STATE, "tt_ctx_profile: a graph is being captured");
   if (int rc = c->flush()) return rc;
   c->prof_on = label_filter != nullptr;
   c->prof_filter = label_filter ? label_filter : "";
@@ -893,7 +981,7 @@ int tt_submit_gemm(tt_ctx* c, int transA, int transB, float alpha, tt_tensor* A,
   return c->submit("gemm", std::move(acc), [=](hipStream_t s, void*) {
     return tile_gemm(s, transA, transB, m, n, k, alpha, (const float*)A->dev(la), ac, (const float*)B->dev(lb), bc,
                      beta, (float*)C->dev(lc), cc, TT_EPI_NONE, nullptr, nullptr, 0, nullptr, 0);
-  });
+  }, 2.0 * m * n * k);
 }
 
 int tt_submit_fill(tt_ctx* c, tt_tensor* t, const int64_t* idx, float value) {

@@ -97,6 +97,7 @@ struct Task {
   std::vector<int64_t> deps;
   std::vector<Access> acc;
   LaunchFn run;
+  double cost = 0.0;  // flop estimate (0 = unknown, treated as light)
   int stream = -1;
   bool need_event = false;
 };
@@ -122,6 +123,7 @@ struct tt_ctx {
   bool dryrun = false;
   int n_streams = 1;
   int active_streams = 1;  // tasks go to streams 0..active_streams-1
+  double heavy_flops = 0;  // > 0: tasks of at least this cost run in order on stream 0
   int window = 512;
   size_t budget = 0;
   bool record = false;
@@ -193,9 +195,19 @@ struct tt_ctx {
   tt_stats stats = {};
 
   // ---- internal API
-  int submit(const char* label, std::vector<tt::Access> acc, tt::LaunchFn run);
+  int submit(const char* label, std::vector<tt::Access> acc, tt::LaunchFn run, double cost = 0.0);
   int flush();
   int wait_all();
+  void forget_launched();  // bookkeeping after a drain: nothing submitted so far is pending
+
+  // graph capture: the tasks submitted between capture_begin and capture_end
+  // are recorded (not run) into one executable graph, replayed with
+  // graph_launch
+  bool capturing = false;
+  int64_t workspace_gen = 0;  // bumped when the per-stream workspaces move (recorded graphs go stale)
+  int capture_begin();
+  int capture_end(hipGraphExec_t* out);  // out may be null (discard)
+  int graph_launch(hipGraphExec_t exec);
   int ensure_workspace(size_t bytes);
   tt::Launched* info(int64_t id);
   int acquire_event(int* idx);

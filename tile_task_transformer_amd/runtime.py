@@ -45,6 +45,11 @@ class Context:
         """Launch later tasks on streams 0..n-1 only (1 = one stream, in order)."""
         check(lib.tt_ctx_streams_active(self.h, n))
 
+    def heavy_lane(self, min_flops: float):
+        """Tasks of at least min_flops on stream 0 in order, the rest on the
+        other streams (0 = off)."""
+        check(lib.tt_ctx_heavy_lane(self.h, float(min_flops)))
+
     def record(self, on: bool = True):
         check(lib.tt_ctx_record(self.h, int(on)))
 
@@ -200,6 +205,11 @@ class GPT2:
         f = C.c_float()
         check(lib.tt_gpt2_loss(self.h, C.byref(f)))
         return f.value
+
+    def set_replay(self, on: bool = True):
+        """Record the step into a HIP graph once and replay it (same tokens
+        buffer and hyperparameters)."""
+        check(lib.tt_gpt2_set_replay(self.h, int(on)))
 
     def row_losses(self) -> np.ndarray:
         """Per-token losses [batch, seq] of the last step's forward."""
