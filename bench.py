@@ -47,9 +47,9 @@ HBM_PEAK = 8000.0       # GB/s
 # on gfx950: factor 2.0; WRITE_SIZE: 1.0). Valid only for the kernel source
 # the counters were taken on (sha256 prefix of the file); else null.
 TRAFFIC = {
-    ("gpt2_small", "head_dw"): {"source": "tile_task_transformer_amd/csrc/gemm.hip", "sha256": "257fe531472aa611",
-                                "fetch_kib": 12391.29 + 10393.53, "fetch_factor": 2.0,
-                                "write_kib": 18432.0 + 2304.0, "write_factor": 1.0},
+    ("gpt2_small", "head_dw"): {"source": "tile_task_transformer_amd/csrc/gemm.hip", "sha256": "0b26658bf60b4189",
+                                "fetch_kib": 18990.5 + 9285.5, "fetch_factor": 2.0,
+                                "write_kib": 16128.0 + 2304.0, "write_factor": 1.0},
 }
 
 
@@ -241,6 +241,35 @@ def copy_probe(mib: int):
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
+
+
+def link_probe(mib: int = 1024, reps: int = 5) -> dict:
+    """Pinned host <-> HBM copy rates (GB/s): H2D alone, D2H alone, and both
+    at once on two streams (the link is full duplex)."""
+    import torch
+    n = mib * 2 ** 20 // 4
+    h_src = torch.ones(n, pin_memory=True)
+    h_dst = torch.empty(n, pin_memory=True)
+    d_src = torch.ones(n, device="cuda")
+    d_dst = torch.empty(n, device="cuda")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def timed(fns):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            for st, fn in fns:
+                with torch.cuda.stream(st):
+                    fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / reps
+
+    nbytes = n * 4
+    h2d = nbytes / timed([(s1, lambda: d_dst.copy_(h_src, non_blocking=True))]) / 1e9
+    d2h = nbytes / timed([(s1, lambda: h_dst.copy_(d_src, non_blocking=True))]) / 1e9
+    both = 2 * nbytes / timed([(s1, lambda: d_dst.copy_(h_src, non_blocking=True)),
+                               (s2, lambda: h_dst.copy_(d_src, non_blocking=True))]) / 1e9
+    return {"h2d_GBps": round(h2d, 1), "d2h_GBps": round(d2h, 1), "both_GBps": round(both, 1), "mib": mib}
 
 
 def pmc_summary(paths, copy_mib: int) -> dict:
@@ -438,6 +467,7 @@ def main(argv=None):
         out["residency"] = {k: st[k] / a.steps for k in ("h2d_bytes", "d2h_bytes", "evictions", "prefetches")}
         out["residency"]["link_GBps"] = round((st["h2d_bytes"] + st["d2h_bytes"]) / elapsed / 1e9, 2)
         out["residency"]["budget_gb"] = a.budget_gb
+        out["residency"]["probe"] = link_probe()
     if classes:
         out["classes"] = {k: {"frac": v["frac"], "achieved": v["achieved"], "unit": v["unit"], "ms": v["ms"]}
                           for k, v in classes.items()}

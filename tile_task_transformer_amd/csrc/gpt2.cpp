@@ -18,8 +18,8 @@
 //
 // Every task below names the tiles it reads and writes; the executor infers
 // the ordering. Submission order is the program order of the untiled step:
-// embedding, blocks, final LN, head, loss, then the backward in reverse and
-// AdamW.
+// embedding, blocks, final LN, head, loss, then the backward in reverse,
+// with each parameter's AdamW tasks right after the backward of its layer.
 #include <cmath>
 #include <cstring>
 #include <memory>
@@ -758,6 +758,32 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
       }
     }
 
+  // ---- AdamW, one task per parameter tile, submitted as soon as the
+  // tile's gradient is final (after the backward of the parameter's own
+  // layer): the update overlaps the rest of the backward and finds p and g
+  // still resident; the result is the same as updating at the end, since no
+  // later task of the step reads these parameters
+  tt_tensor *stp = g->step, *bc = g->bc;
+  const tt_adamw_hparams h = *hp;
+  auto adamw_of = [&](size_t i) -> int {
+    if (!do_update) return TT_OK;
+    tt_tensor *p = g->P[i], *gr = g->G[i], *m = g->M[i], *v = g->Vv[i];
+    for (int64_t lt = 0; lt < p->ntiles; ++lt) {
+      const int64_t n = p->tile_elems(lt);
+      TRY(ctx->submit("adamw", {RW(p, lt), R(gr, lt), RW(m, lt), RW(v, lt), R(bc, 0)}, [=](hipStream_t s, void*) {
+        return tile_fused_adamw(s, n, F(p, lt), F(gr, lt), F(m, lt), F(v, lt), h.lr, h.beta1, h.beta2, h.eps,
+                                h.weight_decay, F(bc, 0));
+      }));
+    }
+    return TT_OK;
+  };
+  if (do_update) {
+    const float b1 = hp->beta1, b2 = hp->beta2;
+    TRY(ctx->submit("adam_step", {RW(stp, 0), W(bc, 0)}, [=](hipStream_t s, void*) {
+      return tile_adamw_advance(s, (int32_t*)stp->dev(0), F(bc, 0), b1, b2);
+    }));
+  }
+
   // ---- backward: head (dz is in place of the logits)
   tt_tensor* gwte = g->G[0];
   for (int64_t vj = 0; vj < NV; ++vj)
@@ -798,6 +824,8 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
     for (int64_t si = 0; si < g->ns; ++si)
       TRY(ln_backward(g, g->dnf, g->h_last, lnfg, g->lnf, g->dh, 0, g->G[g->lnf_g()], g->G[g->lnf_g() + 1],
                       bi + g->nb * si, bi, si));
+  TRY(adamw_of(g->lnf_g()));
+  TRY(adamw_of(g->lnf_g() + 1));
 
   // ---- blocks backward
   for (int l = c.n_layer - 1; l >= 0; --l) {
@@ -954,6 +982,7 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
                         bi, si));
       }
     (void)qkv;
+    for (int w = 0; w < 12; ++w) TRY(adamw_of(g->pidx(l, w)));
   }
 
   // ---- embedding backward: token rows into dwte (after its head part), positions into dwpe
@@ -985,25 +1014,9 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
         }));
       }
 
-  // ---- AdamW on every parameter tile
-  if (do_update) {
-    tt_tensor *stp = g->step, *bc = g->bc;
-    const float b1 = hp->beta1, b2 = hp->beta2;
-    TRY(ctx->submit("adam_step", {RW(stp, 0), W(bc, 0)}, [=](hipStream_t s, void*) {
-      return tile_adamw_advance(s, (int32_t*)stp->dev(0), F(bc, 0), b1, b2);
-    }));
-    const tt_adamw_hparams h = *hp;
-    for (size_t i = 0; i < g->P.size(); ++i) {
-      tt_tensor *p = g->P[i], *gr = g->G[i], *m = g->M[i], *v = g->Vv[i];
-      for (int64_t lt = 0; lt < p->ntiles; ++lt) {
-        const int64_t n = p->tile_elems(lt);
-        TRY(ctx->submit("adamw", {RW(p, lt), R(gr, lt), RW(m, lt), RW(v, lt), R(bc, 0)}, [=](hipStream_t s, void*) {
-          return tile_fused_adamw(s, n, F(p, lt), F(gr, lt), F(m, lt), F(v, lt), h.lr, h.beta1, h.beta2, h.eps,
-                                  h.weight_decay, F(bc, 0));
-        }));
-      }
-    }
-  }
+  // ---- AdamW of the embeddings (their gradients are final now)
+  TRY(adamw_of(0));
+  TRY(adamw_of(1));
   g->last_tasks = ctx->next_id - t0;
   return ctx->flush();
 }

@@ -115,6 +115,7 @@ int tensor_create(tt_ctx* ctx, int ndim, const int64_t* shape, const int64_t* ts
                     (long long)t->bytes(), hipGetErrorString(e));
       memset(t->host, 0, t->bytes());
       t->res.resize(t->ntiles);
+      ctx->has_pinned++;
     }
     t->owned = true;
   }
@@ -253,6 +254,7 @@ int tt_ctx::flush() {
         pending[d - window_base].need_event = true;
   // 3. launch in submission order
   if (launched.empty()) launched_base = window_base;
+  if (!dryrun && has_pinned) plan_window();
   for (size_t ti = 0; ti < pending.size(); ++ti) {
     tt::Task& task = pending[ti];
     const int s = task.stream;
@@ -318,7 +320,8 @@ int tt_ctx::flush() {
     }
     launched.push_back(li);
     if (!dryrun && !latched && arena) {
-      int rc = prefetch(ti);
+      int rc = clean_ahead(ti);
+      if (rc == TT_OK) rc = prefetch(ti);
       if (rc != TT_OK && !latched) {
         latched = rc;
         latched_msg = std::string("prefetch: ") + tt_last_error();
@@ -326,6 +329,7 @@ int tt_ctx::flush() {
     }
   }
   pending.clear();
+  unplan_window();
   if (latched) return fail(latched, "%s", latched_msg.c_str());
   return TT_OK;
 }
@@ -335,12 +339,13 @@ int tt_ctx::flush() {
 // Tiles whose home is pinned host RAM are staged into a device arena of
 // `budget` bytes before a task touches them: H2D copies on the copy stream,
 // and a task's stream waits for the copy stream before it runs. When the
-// arena is full, the least recently used tile that the task being launched
-// does not access is evicted (tiles prefetched for the next few tasks last):
-// the copy stream first waits for every launched task that used the device
-// copy, writes it back if the device copy is newer, then the space is
-// reused. A task writing a tile (TT_W) overwrites all of it, so no copy-in
-// is needed for it.
+// arena is full, the tile whose next use in the launching window is
+// farthest is evicted (never one the launching task accesses; tiles
+// prefetched for the next tasks last). A tile a task changed is written
+// back on a second stream (the host link is full duplex) after every
+// launched task that used it; its range is reused, and the tile reloaded,
+// only after that write-back. A task writing a tile (TT_W) overwrites all
+// of it, so no copy-in is needed for it.
 
 int tt_ctx::arena_init() {
   if (arena) return TT_OK;
@@ -376,11 +381,12 @@ void tt_ctx::arena_release(size_t off, size_t bytes) {
 }
 
 // First-fit allocation of `bytes` (rounded to 256) in the arena, evicting
-// least recently used tiles until a hole fits. Tiles of the task being
-// launched are never evicted; tiles prefetched for the next tasks only when
-// nothing else frees room. With `soft` (a prefetch) the prefetched tiles are
-// spared and 1 is returned, with no error set, when no room can be made.
-int tt_ctx::arena_alloc(size_t bytes, size_t* off, bool soft) {
+// until a hole fits. Tiles of the task being launched are never evicted;
+// tiles prefetched for the next tasks only when nothing else frees room.
+// With `soft` (a prefetch for a task with id `use`) the prefetched tiles are
+// spared, only tiles needed later than `use` are evicted, and 1 is
+// returned, with no error set, when no room can be made.
+int tt_ctx::arena_alloc(size_t bytes, size_t* off, bool soft, int64_t use) {
   bytes = (bytes + 255) & ~(size_t)255;
   if (bytes > arena_bytes)
     return fail(TT_ERR_OOM, "tile of %zu bytes exceeds the device budget of %zu bytes", bytes, arena_bytes);
@@ -393,8 +399,8 @@ int tt_ctx::arena_alloc(size_t bytes, size_t* off, bool soft) {
         if (rest) arena_free[at] = rest;
         return TT_OK;
       }
-    int rc = evict_one(true);
-    if (rc == 1 && !soft) rc = evict_one(false);
+    int rc = evict_one(true, soft ? use : -1);
+    if (rc == 1 && !soft) rc = evict_one(false, -1);
     if (rc == 1) {
       if (soft) return 1;
       return fail(TT_ERR_OOM, "device budget of %zu bytes cannot hold the tiles one task needs", arena_bytes);
@@ -403,6 +409,7 @@ int tt_ctx::arena_alloc(size_t bytes, size_t* off, bool soft) {
   }
 }
 
+// `s` waits for every launched task that used the device copy of (t, lin)
 int tt_ctx::wait_users(tt_tensor* t, int64_t lin, hipStream_t s) {
   for (int64_t u : t->res[lin].users) {
     if (u < done_below || u >= cur_task) continue;
@@ -420,26 +427,69 @@ int tt_ctx::wait_users(tt_tensor* t, int64_t lin, hipStream_t s) {
   return TT_OK;
 }
 
-// Evict the least recently used tile that the task being launched does not
-// access (and, with `spare_prefetched`, that no upcoming task was prefetched
-// for). Returns 1, with no error set, when there is no such tile.
-int tt_ctx::evict_one(bool spare_prefetched) {
+// id of the next task in the launching window that accesses the tile
+// (INT64_MAX: none)
+int64_t tt_ctx::next_use(tt::Residency& r) {
+  while (r.fpos < r.future.size() && r.future[r.fpos] < cur_task) ++r.fpos;
+  return r.fpos < r.future.size() ? r.future[r.fpos] : INT64_MAX;
+}
+
+// `s` must not touch arena range [off, off + bytes) before the write-backs
+// that freed any part of it have finished
+int tt_ctx::wait_dirty_free(size_t off, size_t bytes, hipStream_t s) {
+  for (const DirtyFree& d : dirty_free)
+    if (d.off < off + bytes && off < d.off + d.bytes) TT_HIP_TRY(hipStreamWaitEvent(s, events[d.event], 0));
+  return TT_OK;
+}
+
+// Evict the tile whose next use in the launching window is farthest
+// (Belady's rule over the known future; ties: a clean tile, whose eviction
+// costs no write-back, then the least recently used). Never a tile of the
+// task being launched; with `spare_prefetched`, never one prefetched for an
+// upcoming task; with `later_than` >= 0, only a tile next used after that
+// task. Returns 1, with no error set, when there is no such tile.
+int tt_ctx::evict_one(bool spare_prefetched, int64_t later_than) {
   int best = -1;
+  int64_t best_use = -1;
   for (size_t i = 0; i < resident.size(); ++i) {
-    const tt::Residency& r = resident[i].t->res[resident[i].lin];
+    tt::Residency& r = resident[i].t->res[resident[i].lin];
     if (r.need >= cur_task) continue;
     if (spare_prefetched && r.protect >= cur_task) continue;
-    if (best < 0 || r.last_use < resident[best].t->res[resident[best].lin].last_use) best = (int)i;
+    const int64_t u = next_use(r);
+    if (later_than >= 0 && u <= later_than) continue;
+    bool better = best < 0 || u > best_use;
+    if (!better && u == best_use) {
+      const tt::Residency& b = resident[best].t->res[resident[best].lin];
+      const bool rc = r.host_valid || !r.dev_valid, bc = b.host_valid || !b.dev_valid;
+      better = (rc && !bc) || (rc == bc && r.last_use < b.last_use);
+    }
+    if (better) {
+      best = (int)i;
+      best_use = u;
+    }
   }
   if (best < 0) return 1;
   tt::TileRef v = resident[best];
   tt::Residency& r = v.t->res[v.lin];
-  if (int rc = wait_users(v.t, v.lin, copy_stream)) return rc;
   if (r.dev_valid && !r.host_valid) {
+    // write-back on its own stream after every launched user; the range is
+    // reused (and the tile reloaded) only after it
+    if (int rc = wait_users(v.t, v.lin, d2h_stream)) return rc;
     TT_HIP_TRY(hipMemcpyAsync(v.t->host + v.t->tile_off[v.lin] * 4, r.dev, v.t->tile_elems(v.lin) * 4,
-                              hipMemcpyDeviceToHost, copy_stream));
+                              hipMemcpyDeviceToHost, d2h_stream));
+    int ev;
+    if (int rc = acquire_event(&ev)) return rc;
+    TT_HIP_TRY(hipEventRecord(events[ev], d2h_stream));
+    dirty_free.push_back({r.off, r.bytes, ev});
+    r.wb_event = ev;
     stats.d2h_bytes += v.t->tile_elems(v.lin) * 4;
     r.host_valid = true;
+  } else {
+    // the next writer of the range is an H2D copy, or a task ordered after the
+    // copy stream: the copy stream waits for the tile's users, and for an
+    // early write-back still reading the range
+    if (int rc = wait_users(v.t, v.lin, copy_stream)) return rc;
+    if (r.wb_event >= 0) dirty_free.push_back({r.off, r.bytes, r.wb_event});
   }
   arena_release(r.off, r.bytes);
   r.dev = nullptr;
@@ -453,22 +503,26 @@ int tt_ctx::evict_one(bool spare_prefetched) {
 }
 
 // device copy for tile (t, lin), allocated and (if `load`) filled from host;
-// `soft` as for arena_alloc (returns 1 when a prefetch finds no room)
-static int stage_tile(tt_ctx* c, tt_tensor* t, int64_t lin, bool load, bool soft) {
+// `soft`/`use` as for arena_alloc (returns 1 when a prefetch finds no room)
+static int stage_tile(tt_ctx* c, tt_tensor* t, int64_t lin, bool load, bool soft, int64_t use) {
   tt::Residency& r = t->res[lin];
   if (!r.dev) {
     size_t off;
     const size_t bytes = (size_t)t->tile_elems(lin) * 4;
-    if (int rc = c->arena_alloc(bytes, &off, soft)) return rc;
+    if (int rc = c->arena_alloc(bytes, &off, soft, use)) return rc;
     r.dev = (float*)(c->arena + off);
     r.off = off;
     r.bytes = (bytes + 255) & ~(size_t)255;
     r.dev_valid = false;
     c->resident.push_back(tt::TileRef{t, lin});
+    // whoever writes the range next (this copy, or the task through the
+    // copy stream's event) comes after write-backs that freed it
+    if (int rc = c->wait_dirty_free(r.off, r.bytes, c->copy_stream)) return rc;
     c->copy_pending = true;
   }
   if (load && !r.dev_valid) {
     if (!r.host_valid) return fail(TT_ERR_STATE, "tile has neither a valid host nor device copy");
+    if (r.wb_event >= 0) TT_HIP_TRY(hipStreamWaitEvent(c->copy_stream, c->events[r.wb_event], 0));
     TT_HIP_TRY(hipMemcpyAsync(r.dev, t->host + t->tile_off[lin] * 4, t->tile_elems(lin) * 4, hipMemcpyHostToDevice,
                               c->copy_stream));
     c->stats.h2d_bytes += t->tile_elems(lin) * 4;
@@ -491,7 +545,7 @@ int tt_ctx::make_resident(tt::Task& task, hipStream_t s) {
   for (auto& a : task.acc) {
     tt_tensor* t = a.ref.t;
     if (t->home != TT_HOME_PINNED_HOST) continue;
-    if (int rc = stage_tile(this, t, a.ref.lin, (a.mode & TT_R) != 0, false)) return rc;
+    if (int rc = stage_tile(this, t, a.ref.lin, (a.mode & TT_R) != 0, false, task.id)) return rc;
   }
   // the task's stream runs after every copy (and eviction) queued so far
   if (copy_pending) {
@@ -512,6 +566,8 @@ int tt_ctx::make_resident(tt::Task& task, hipStream_t s) {
     tt_tensor* t = a.ref.t;
     if (t->home != TT_HOME_PINNED_HOST) continue;
     tt::Residency& r = t->res[a.ref.lin];
+    // a write-back of this device copy may still be reading it
+    if ((a.mode & TT_W) && r.wb_event >= 0) TT_HIP_TRY(hipStreamWaitEvent(s, events[r.wb_event], 0));
     if (a.mode & TT_W) {
       r.dev_valid = true;
       r.host_valid = false;
@@ -523,21 +579,68 @@ int tt_ctx::make_resident(tt::Task& task, hipStream_t s) {
   return TT_OK;
 }
 
-// stage the pinned tiles that the next few tasks read, so their copies
-// overlap the current task (a tile written by an earlier one of those tasks
-// is not prefetched: its host copy would be stale)
+// Record, for every pinned tile the window's tasks access, the ids of those
+// tasks: the eviction rule looks them up.
+void tt_ctx::plan_window() {
+  for (auto& task : pending)
+    for (auto& a : task.acc)
+      if (a.ref.t->home == TT_HOME_PINNED_HOST) {
+        tt::Residency& r = a.ref.t->res[a.ref.lin];
+        if (r.future.empty()) planned.push_back(&r);
+        if (r.future.empty() || r.future.back() != task.id) r.future.push_back(task.id);
+      }
+}
+
+void tt_ctx::unplan_window() {
+  for (tt::Residency* r : planned) {
+    r->future.clear();
+    r->fpos = 0;
+  }
+  planned.clear();
+}
+
+// A tile the launched task i wrote that no later task of the window
+// accesses is written back now, on the write-back stream after task i: it
+// stays resident but clean, so its eviction later copies nothing. A later
+// writer of the tile waits for this copy (make_resident), and so does any
+// reuse of its range (evict_one).
+int tt_ctx::clean_ahead(size_t i) {
+  const tt::Task& task = pending[i];
+  cur_task = task.id + 1;
+  for (auto& a : task.acc) {
+    tt_tensor* t = a.ref.t;
+    if (t->home != TT_HOME_PINNED_HOST || !(a.mode & TT_W)) continue;
+    tt::Residency& r = t->res[a.ref.lin];
+    if (!r.dev || !r.dev_valid || r.host_valid || next_use(r) != INT64_MAX) continue;
+    if (int rc = wait_users(t, a.ref.lin, d2h_stream)) return rc;
+    TT_HIP_TRY(hipMemcpyAsync(t->host + t->tile_off[a.ref.lin] * 4, r.dev, t->tile_elems(a.ref.lin) * 4,
+                              hipMemcpyDeviceToHost, d2h_stream));
+    int ev;
+    if (int rc = acquire_event(&ev)) return rc;
+    TT_HIP_TRY(hipEventRecord(events[ev], d2h_stream));
+    r.wb_event = ev;
+    r.host_valid = true;
+    stats.d2h_bytes += t->tile_elems(a.ref.lin) * 4;
+  }
+  return TT_OK;
+}
+
+// Stage the pinned tiles that the next tasks read (up to 16 tasks and a
+// quarter of the arena ahead) so their copies overlap the current task; a
+// tile written by an earlier one of those tasks is not prefetched (its host
+// copy would be stale).
 int tt_ctx::prefetch(size_t i) {
-  constexpr size_t kAhead = 4;
+  constexpr size_t kAhead = 16;
   const size_t end = std::min(pending.size(), i + 1 + kAhead);
   // task i has been launched: an eviction from here on must wait for it too
   cur_task = pending[i].id + 1;
-  for (size_t j = i + 1; j < end; ++j)
+  size_t planned_bytes = 0;
+  for (size_t j = i + 1; j < end; ++j) {
     for (auto& a : pending[j].acc)
       if (a.ref.t->home == TT_HOME_PINNED_HOST) {
         tt::Residency& r = a.ref.t->res[a.ref.lin];
         r.protect = std::max(r.protect, pending[j].id);
       }
-  for (size_t j = i + 1; j < end; ++j)
     for (auto& a : pending[j].acc) {
       tt_tensor* t = a.ref.t;
       if (t->home != TT_HOME_PINNED_HOST || !(a.mode & TT_R)) continue;
@@ -548,11 +651,14 @@ int tt_ctx::prefetch(size_t i) {
         for (auto& b : pending[k].acc)
           if (b.ref.t == t && b.ref.lin == a.ref.lin && (b.mode & TT_W)) written_before = true;
       if (written_before) continue;
-      const int rc = stage_tile(this, t, a.ref.lin, true, true);
-      if (rc == 1) return TT_OK;  // no room without evicting what is needed next: stop here
+      planned_bytes += (size_t)t->tile_elems(a.ref.lin) * 4;
+      if (planned_bytes > arena_bytes / 4) return TT_OK;
+      const int rc = stage_tile(this, t, a.ref.lin, true, true, pending[j].id);
+      if (rc == 1) return TT_OK;  // no room without evicting what is needed sooner: stop here
       if (rc) return rc;
       stats.prefetches++;
     }
+  }
   return TT_OK;
 }
 
@@ -575,6 +681,7 @@ int tt_ctx::wait_all() {
   if (!dryrun) {
     std::vector<hipStream_t> all(streams);
     if (copy_stream) all.push_back(copy_stream);
+    if (d2h_stream) all.push_back(d2h_stream);
     for (auto s : all) {
       hipError_t e = hipStreamSynchronize(s);
       if (e != hipSuccess && !latched) {
@@ -590,6 +697,10 @@ int tt_ctx::wait_all() {
 }
 
 void tt_ctx::forget_launched() {
+  // write-back events are recycled with the others
+  for (auto& t : tensors)
+    for (auto& r : t->res) r.wb_event = -1;
+  dirty_free.clear();
   done_below = next_id;
   launched.clear();
   launched_base = next_id;
@@ -717,6 +828,7 @@ int tt_ctx_create(int device, int n_streams, int window, size_t device_budget_by
     for (int s = 0; s < n_streams; ++s)
       TT_HIP_TRY(hipStreamCreateWithFlags(&c->streams[s], hipStreamNonBlocking));
     TT_HIP_TRY(hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking));
+    TT_HIP_TRY(hipStreamCreateWithFlags(&c->d2h_stream, hipStreamNonBlocking));
   }
   *out = c.release();
   return TT_OK;
@@ -734,6 +846,7 @@ int tt_ctx_destroy(tt_ctx* c) {
     for (auto e : c->prof_events) (void)hipEventDestroy(e);
     for (auto s : c->streams) (void)hipStreamDestroy(s);
     if (c->copy_stream) (void)hipStreamDestroy(c->copy_stream);
+    if (c->d2h_stream) (void)hipStreamDestroy(c->d2h_stream);
     if (c->arena) (void)hipFree(c->arena);
   }
   delete c;
@@ -827,6 +940,7 @@ int tt_tensor_destroy(tt_tensor* t) {
     (void)rc;
   }
   c->drop_resident(t);  // device copies live in the context's arena
+  if (!t->res.empty()) c->has_pinned--;
   if (t->owned) {
     if (t->base) (void)hipFree(t->base);
     if (t->host) (void)hipHostFree(t->host);

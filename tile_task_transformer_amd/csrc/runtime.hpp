@@ -40,6 +40,9 @@ struct Residency {
   int64_t need = -1;               // id of the latest task being launched that accesses it
   int64_t protect = -1;            // prefetched for tasks with id <= protect (evicted only under pressure)
   std::vector<int64_t> users;      // launched tasks that touched the device copy since its last launched writer
+  std::vector<int64_t> future;     // ids of the tasks in the launching window that access it (ascending)
+  size_t fpos = 0;                 // first entry of `future` not yet passed
+  int wb_event = -1;               // event after its last write-back (host copy in flight until then)
 };
 
 }  // namespace tt
@@ -131,7 +134,8 @@ struct tt_ctx {
   std::string latched_msg;
 
   std::vector<hipStream_t> streams;
-  hipStream_t copy_stream = nullptr;   // residency H2D/D2H
+  hipStream_t copy_stream = nullptr;   // residency H2D
+  hipStream_t d2h_stream = nullptr;    // residency write-backs (the link is full duplex)
   std::vector<void*> workspace;        // per stream
   size_t workspace_bytes = 0;
 
@@ -165,11 +169,23 @@ struct tt_ctx {
   int copy_event = -1;                  // event after the latest copy-stream work
   std::vector<int> waited_copy;         // per stream: copy_event it already waited on
   int arena_init();
-  int arena_alloc(size_t bytes, size_t* off, bool soft);
+  int arena_alloc(size_t bytes, size_t* off, bool soft, int64_t use);
   void arena_release(size_t off, size_t bytes);
-  int evict_one(bool spare_prefetched);
+  int evict_one(bool spare_prefetched, int64_t use);
+  int64_t next_use(tt::Residency& r);
+  // arena ranges freed by a write-back still in flight: (offset, bytes, event)
+  struct DirtyFree {
+    size_t off, bytes;
+    int event;
+  };
+  std::vector<DirtyFree> dirty_free;
+  std::vector<tt::Residency*> planned;  // tiles whose `future` this window filled
+  int wait_dirty_free(size_t off, size_t bytes, hipStream_t s);
   int wait_users(tt_tensor* t, int64_t lin, hipStream_t s);
   int prefetch(size_t i);
+  int clean_ahead(size_t i);
+  void plan_window();
+  void unplan_window();
   void drop_resident(tt_tensor* t);
 
   // per-task GPU timing (tt_ctx_profile): event pairs around matching launches
@@ -191,6 +207,7 @@ struct tt_ctx {
 
   int64_t next_tensor_id = 0;
   std::vector<tt_tensor*> tensors;     // live tensors
+  int has_pinned = 0;                  // live tensors whose home is pinned host
   std::vector<tt::TaskRecord> records;
   tt_stats stats = {};
 
