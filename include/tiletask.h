@@ -437,8 +437,15 @@ typedef struct {
 typedef struct {              /* README tile flags; vocab has no flag there */
     int batch, seq, embd, inner, head, vocab;
 } tt_gpt2_tiles;
+/* AdamW settings of the NNTile README's GPT example (fused AdamW, eps,
+ * weight decay, lr) plus its warm-up flags: AdamW iteration 1 uses
+ * start_lr, iteration full_lr_iter and later ones lr, linearly in between;
+ * full_lr_iter <= 1 uses lr throughout. Iterations are counted per
+ * tt_gpt2 from its creation. */
 typedef struct {
     float lr, beta1, beta2, eps, weight_decay;
+    float start_lr;
+    int full_lr_iter;
 } tt_adamw_hparams;
 
 /* Allocates parameters, gradients, AdamW moments (zeroed) and activations
@@ -463,6 +470,18 @@ int tt_gpt2_param(tt_gpt2* g, int index, tt_tensor** param, tt_tensor** grad,
  * ids in [0, vocab). The step is queued; tt_gpt2_loss waits and returns
  * the mean loss. */
 int tt_gpt2_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams* hp, int do_update);
+/* One optimiser step over a batch of n_micro minibatches (the README's
+ * batch / minibatch flags: gradients of the whole batch are collected
+ * before the update). tokens: DEVICE int32 [n_micro * batch, seq + 1];
+ * minibatch i is rows i*batch .. (i+1)*batch - 1. Forward and backward run
+ * per minibatch, every gradient accumulating after the first; the loss and
+ * its gradient are scaled by 1 / (n_micro * batch * seq), so the result is
+ * the step on the whole batch with the mean loss. AdamW (if do_update) runs
+ * once, after the last minibatch's backward. tt_gpt2_loss returns the batch
+ * mean, tt_gpt2_row_losses the last minibatch's. n_micro = 1 is
+ * tt_gpt2_step. TT_ERR_ARG for n_micro < 1. */
+int tt_gpt2_step_accum(tt_gpt2* g, const int32_t* tokens, int n_micro, const tt_adamw_hparams* hp,
+                       int do_update);
 /* Graph replay (on != 0): the next tt_gpt2_step records its tasks into one
  * HIP graph (kernels, copies and cross-stream waits; nothing runs while
  * recording) and launches it; later steps with the same tokens pointer,

@@ -245,6 +245,17 @@ def backward(cache, n_layer: int, n_head: int) -> Dict[str, np.ndarray]:
     return G
 
 
+def lr_at(t: int, lr: float, start_lr: float, full_lr_iter: int) -> float:
+    """Learning rate of AdamW iteration t (counted from 1). The NNTile README
+    ("Minimal working GPT example") fixes the ends: the first iteration uses
+    start_lr, iteration full_lr_iter and every later one the full lr, and
+    full_lr_iter = 1 means the full lr throughout. Reading: linear in t
+    between the ends."""
+    if full_lr_iter <= 1 or t >= full_lr_iter:
+        return lr
+    return start_lr + (lr - start_lr) * (t - 1) / (full_lr_iter - 1)
+
+
 def step(params: Dict[str, np.ndarray], tokens: np.ndarray, n_layer: int, n_head: int,
          lr: float = 3e-4, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
          wd: float = 0.1, t: int = 1, ln_eps: float = 1e-5, state=None):

@@ -194,6 +194,33 @@ def test_gpt2_step_dag_is_race_free(tiles, tmp_path):
         assert need in labels, need
 
 
+def test_gpt2_accumulating_step_dag_is_race_free(tmp_path):
+    """Two minibatches into one update: race free, twice the forward and
+    backward tasks, AdamW tasks once, and no gradient is zeroed twice."""
+    shape = synth.GPT2Shape(2, 100, 64, 4, 96, 32, 2)
+    tiles = synth.Tiles(1, 16, 32, 48, 2, 40)
+    counts = []
+    for n_micro in (1, 2):
+        with Context(L.TT_DEVICE_DRYRUN, n_streams=4, window=100000) as ctx:
+            model = GPT2(ctx, shape, tiles)
+            model.step(None, n_micro=n_micro)
+            dag = ctx.dump_dag(str(tmp_path / f"dag{n_micro}.jsonl"))
+            model.close()
+        _check_races(dag)
+        counts.append({lab: sum(r["label"] == lab for r in dag) for lab in ("adamw", "adam_step", "fill", "qkv",
+                                                                            "head_dw", "ce_loss")})
+    one, two = counts
+    assert two["adamw"] == one["adamw"] and two["adam_step"] == one["adam_step"] == 1
+    assert two["fill"] == one["fill"]
+    for lab in ("qkv", "head_dw", "ce_loss"):
+        assert two[lab] == 2 * one[lab], lab
+    with Context(L.TT_DEVICE_DRYRUN, n_streams=2) as ctx:
+        model = GPT2(ctx, shape, tiles)
+        with pytest.raises(L.TTError):
+            model.step(None, n_micro=0)
+        model.close()
+
+
 def test_gpt2_rejects_bad_tiles():
     shape = synth.GPT2Shape(1, 100, 64, 4, 96, 32, 2)
     with Context(L.TT_DEVICE_DRYRUN) as ctx:

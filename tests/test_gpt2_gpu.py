@@ -134,3 +134,63 @@ def test_gpt2_small_full_size_step_matches_oracle():
     tokens = synth.token_stream(w.shape, seed=1)
     gpu = run_gpu(w.shape, w.tiles, params, tokens)
     check_against_oracle(w.shape, gpu, params, tokens, w)
+
+
+def test_two_minibatches_make_the_batch_step():
+    """The README's batch/minibatch flags: a batch of 4 windows processed as
+    2 minibatches of 2 with gradients accumulated, then one update, is the
+    step on the whole batch (mean loss over all its tokens)."""
+    shape = TINY.shape
+    big = synth.GPT2Shape(shape.n_layer, shape.vocab, shape.n_embd, shape.n_head, shape.n_inner, shape.seq,
+                          2 * shape.batch)
+    params = synth.init_params(shape, seed=0)
+    tokens = synth.token_stream(big, seed=1)
+    specs = synth.param_specs(shape)
+    with Context(0, n_streams=4) as ctx:
+        model = GPT2(ctx, shape, synth.Tiles(1, 16, 32, 64, 2, 48))
+        model.set_params(params, specs)
+        model.step(torch.from_numpy(tokens.astype(np.int32)).cuda(), n_micro=2)
+        gpu = dict(loss=[model.loss()], grads=model.get(specs, 1), params=model.get(specs, 0))
+        model.close()
+    check_against_oracle(big, gpu, params, tokens, TINY)
+
+
+def test_lr_warmup_schedule():
+    """start_lr at the first update, lr from update full_lr_iter on, linear in
+    between: with start_lr = 0 the first update leaves every parameter
+    exactly as it was, so the second forward repeats the first bitwise; three
+    steps follow the oracle's schedule."""
+    shape = TINY.shape
+    params = synth.init_params(shape, seed=0)
+    tokens = synth.token_stream(shape, seed=1)
+    specs = synth.param_specs(shape)
+    lr, full = 1e-3, 3
+    with Context(0, n_streams=4) as ctx:
+        model = GPT2(ctx, shape, TINY.tiles)
+        model.set_params(params, specs)
+        tok = torch.from_numpy(tokens.astype(np.int32)).cuda()
+        losses = []
+        for _ in range(3):
+            model.step(tok, lr=lr, start_lr=0.0, full_lr_iter=full)
+            losses.append(model.loss())
+        got = model.get(specs, 0)
+        model.close()
+    assert losses[1] == losses[0]
+    p, state, ref_losses, lrs, decided = params, None, [], [], {}
+    for t in range(1, 4):
+        lr_t = og.lr_at(t, lr, 0.0, full)
+        lrs.append(lr_t)
+        loss, grads, p, state = og.step(p, tokens, shape.n_layer, shape.n_head, lr=lr_t, beta1=TINY.beta1,
+                                        beta2=TINY.beta2, eps=TINY.eps, wd=TINY.weight_decay, t=t, state=state)
+        ref_losses.append(loss)
+        for name, g in grads.items():  # elements whose update direction every step's gradient decides
+            d = np.abs(g) > 1e-3 * np.abs(g).max()
+            decided[name] = d if t == 1 else decided[name] & d
+    assert lrs == [0.0, lr / 2, lr]
+    for a, b in zip(losses, ref_losses):
+        assert abs(a - b) <= 1e-4 * abs(b), (a, b)
+    for name, ref in p.items():
+        g = got[name].astype(np.float64)
+        assert np.abs(g - ref).max() <= 2 * sum(lrs) * (1 + 1e-3) + 1e-6 * np.abs(ref).max(), name
+        if decided[name].any():
+            assert normwise(g[decided[name]], ref[decided[name]]) <= 1e-3, name

@@ -109,6 +109,36 @@ def test_row_losses_depend_on_the_prefix_only():
     assert np.abs(moved[:, -1] - full[:, -1]).max() > 1e-6
 
 
+def test_lr_schedule_ends_and_constant_case():
+    """The README's warm-up flags: iteration 1 uses start_lr, iteration
+    full_lr_iter and later the full lr; full_lr_iter = 1 keeps it constant."""
+    assert og.lr_at(1, 3e-4, 0.0, 10) == 0.0
+    assert og.lr_at(10, 3e-4, 0.0, 10) == 3e-4
+    assert og.lr_at(57, 3e-4, 0.0, 10) == 3e-4
+    assert all(og.lr_at(t, 3e-4, 1e-5, 1) == 3e-4 for t in range(1, 5))
+    ramp = [og.lr_at(t, 1.0, 0.1, 4) for t in range(1, 5)]
+    assert np.allclose(np.diff(ramp), 0.3) and ramp[0] == 0.1 and ramp[-1] == 1.0
+
+
+def test_accumulated_minibatch_gradients_equal_the_batch_gradient():
+    """Mean loss over a batch = average of the minibatch mean losses (equal
+    sizes), so the batch gradient is the average of minibatch gradients --
+    what accumulating over minibatches must reproduce."""
+    params = _rich_params(TINY)
+    rng = np.random.default_rng(11)
+    tok = rng.integers(0, TINY.vocab, size=(4, TINY.seq + 1))
+    x, y = tok[:, :-1], tok[:, 1:]
+    loss, cache = og.forward(params, x, y, TINY.n_layer, TINY.n_head)
+    grads = og.backward(cache, TINY.n_layer, TINY.n_head)
+    parts = []
+    for i in range(2):
+        li, ci = og.forward(params, x[2 * i:2 * i + 2], y[2 * i:2 * i + 2], TINY.n_layer, TINY.n_head)
+        parts.append((li, og.backward(ci, TINY.n_layer, TINY.n_head)))
+    assert abs(loss - (parts[0][0] + parts[1][0]) / 2) <= 1e-13
+    for name, g in grads.items():
+        assert np.abs(g - (parts[0][1][name] + parts[1][1][name]) / 2).max() <= 1e-13 * max(1.0, np.abs(g).max())
+
+
 def test_layernorm_statistics():
     rng = np.random.default_rng(1)
     x = rng.standard_normal((6, 33)) * 3 + 2

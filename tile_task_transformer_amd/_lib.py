@@ -70,7 +70,7 @@ class tt_gpt2_tiles(C.Structure):
 
 class tt_adamw_hparams(C.Structure):
     _fields_ = [("lr", C.c_float), ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float),
-                ("weight_decay", C.c_float)]
+                ("weight_decay", C.c_float), ("start_lr", C.c_float), ("full_lr_iter", C.c_int)]
 
 
 P, I, I64, F, SZ = C.c_void_p, C.c_int, C.c_int64, C.c_float, C.c_size_t
@@ -131,6 +131,7 @@ SIGNATURES = {
     "tt_gpt2_task_count": (I, [P, C.POINTER(I64)]),
     "tt_gpt2_row_losses": (I, [P, C.POINTER(F)]),
     "tt_gpt2_set_replay": (I, [P, I]),
+    "tt_gpt2_step_accum": (I, [P, P, I, C.POINTER(tt_adamw_hparams), I]),
 }
 
 for _name, (_res, _args) in SIGNATURES.items():

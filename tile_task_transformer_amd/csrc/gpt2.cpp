@@ -64,6 +64,7 @@ struct tt_gpt2 {
   int graph_update = 0;
   int64_t graph_tasks = 0;
   int64_t graph_ws_gen = -1;
+  int64_t updates = 0;  // AdamW iterations submitted (warm-up schedule)
 
   enum { WTE = 0, WPE = 1 };
   int pidx(int layer, int which) const { return 2 + 12 * layer + which; }
@@ -496,16 +497,42 @@ extern "C" int tt_gpt2_row_losses(tt_gpt2* g, float* out) {
 
 // -------------------------------------------------------------------- step
 
-static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams* hp, int do_update);
+static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams* hp, int do_update, int micro,
+                       int n_micro);
 
-extern "C" int tt_gpt2_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams* hp, int do_update) {
+// learning rate of AdamW iteration t (from 1): start_lr at 1, lr from
+// full_lr_iter on, linear in between (the README's warm-up flags)
+static float lr_at(int64_t t, const tt_adamw_hparams& h) {
+  if (h.full_lr_iter <= 1 || t >= h.full_lr_iter) return h.lr;
+  return h.start_lr + (h.lr - h.start_lr) * (float)(t - 1) / (float)(h.full_lr_iter - 1);
+}
+
+// every minibatch's tasks; `h` carries the lr of this update
+static int submit_batch(tt_gpt2* g, const int32_t* tokens, int n_micro, const tt_adamw_hparams& h, int do_update) {
+  tt_ctx* ctx = g->ctx;
+  const int64_t t0 = ctx->next_id, win = (int64_t)g->c.batch * (g->c.seq + 1);
+  for (int i = 0; i < n_micro; ++i)
+    TRY(submit_step(g, tokens ? tokens + i * win : nullptr, &h, do_update && i == n_micro - 1, i, n_micro));
+  g->last_tasks = ctx->next_id - t0;
+  return TT_OK;
+}
+
+extern "C" int tt_gpt2_step_accum(tt_gpt2* g, const int32_t* tokens, int n_micro, const tt_adamw_hparams* hp,
+                                  int do_update) {
   clear_error();
   if (!g || !hp) return fail(TT_ERR_ARG, "tt_gpt2_step: null argument");
+  if (n_micro < 1) return fail(TT_ERR_ARG, "tt_gpt2_step_accum: n_micro must be >= 1");
   tt_ctx* ctx = g->ctx;
   if (!tokens && !ctx->dryrun) return fail(TT_ERR_ARG, "tt_gpt2_step: null tokens");
-  if (!g->replay) return submit_step(g, tokens, hp, do_update);
+  tt_adamw_hparams h = *hp;
+  if (do_update) h.lr = lr_at(g->updates + 1, *hp);
+  if (!g->replay || n_micro != 1) {
+    TRY(submit_batch(g, tokens, n_micro, h, do_update));
+    if (do_update) g->updates++;
+    return TT_OK;
+  }
   const bool same = g->graph && g->graph_tokens == tokens && g->graph_update == do_update &&
-                    !memcmp(&g->graph_hp, hp, sizeof(*hp)) && g->graph_ws_gen == ctx->workspace_gen;
+                    !memcmp(&g->graph_hp, &h, sizeof(h)) && g->graph_ws_gen == ctx->workspace_gen;
   if (!same) {
     if (g->graph) {
       TRY(ctx->wait_all());
@@ -513,23 +540,33 @@ extern "C" int tt_gpt2_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hp
       g->graph = nullptr;
     }
     TRY(ctx->capture_begin());
-    const int rc = submit_step(g, tokens, hp, do_update);
+    const int rc = submit_batch(g, tokens, 1, h, do_update);
     hipGraphExec_t exec = nullptr;
     const int rc2 = ctx->capture_end(rc == TT_OK ? &exec : nullptr);
     if (rc != TT_OK) return rc;
     if (rc2 != TT_OK) return rc2;
     g->graph = exec;
     g->graph_tokens = tokens;
-    g->graph_hp = *hp;
+    g->graph_hp = h;
     g->graph_update = do_update;
     g->graph_tasks = g->last_tasks;
     g->graph_ws_gen = ctx->workspace_gen;
   }
   g->last_tasks = g->graph_tasks;
-  return ctx->graph_launch(g->graph);
+  TRY(ctx->graph_launch(g->graph));
+  if (do_update) g->updates++;
+  return TT_OK;
 }
 
-static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams* hp, int do_update) {
+extern "C" int tt_gpt2_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams* hp, int do_update) {
+  return tt_gpt2_step_accum(g, tokens, 1, hp, do_update);
+}
+
+// One minibatch: forward, loss, backward and (if do_update) AdamW. Minibatch
+// `micro` of `n_micro` accumulates into the gradients and the loss of the
+// earlier ones (micro > 0); the loss is scaled for the mean over all of them.
+static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams* hp, int do_update, int micro,
+                       int n_micro) {
   tt_ctx* ctx = g->ctx;
   const int64_t t0 = ctx->next_id;
   const tt_gpt2_config& c = g->c;
@@ -537,7 +574,8 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
   const int64_t bt = g->t.batch, sq = g->t.seq, ht = g->t.head, rows = g->rows;
   const int64_t NE = g->NE, NI = g->NI, NH = g->NH, NV = g->NV;
   const float scale = 1.f / std::sqrt((float)hd);
-  const float inv_n = 1.f / (float)(B * T);
+  const float inv_n = 1.f / (float)(B * T * n_micro);
+  const bool later_mb = micro > 0;  // gradients and loss already hold earlier minibatches
 
   // ---- inputs: copy the token windows, split into ids/labels, index for the embedding backward
   {
@@ -739,7 +777,7 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
                               F(lse, ti), F(rl, ti), nullptr, 0, 1.f);
         }));
         tt_tensor* loss = g->loss;
-        const int accumulate = ti > 0;
+        const int accumulate = ti > 0 || later_mb;
         TRY(ctx->submit("ce_loss", {R(rl, ti), accumulate ? RW(loss, 0) : W(loss, 0)}, [=](hipStream_t s, void*) {
           return tile_xentropy(s, TT_XE_LOSS, rows, 0, 0, nullptr, nullptr, 0, nullptr, F(rl, ti), F(loss, 0),
                                accumulate, inv_n);
@@ -797,7 +835,7 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
           q.A = {g->z, L(g->z, {bi, si, vj})};
           q.B = {g->nf, L(g->nf, {bi, si, ek})};
           q.C = {gwte, L(gwte, {vj, ek})};
-          q.beta = ti > 0 ? 1.f : 0.f;
+          q.beta = (ti > 0 || later_mb) ? 1.f : 0.f;
           TRY(submit_gemm(ctx, "head_dw", q));
         }
       // dnf = sum over vocab tiles of dz wte
@@ -811,15 +849,18 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
           TRY(submit_gemm(ctx, "head_dx", q));
         }
     }
-  // zero the LayerNorm and position gradients, which accumulate
-  for (int l = 0; l < c.n_layer; ++l)
-    for (int w : {LN1G, LN1B, LN2G, LN2B})
-      for (int64_t e = 0; e < NE; ++e) TRY(fill_task(ctx, g->G[g->pidx(l, w)], e, 0.f));
-  for (int64_t e = 0; e < NE; ++e) {
-    TRY(fill_task(ctx, g->G[g->lnf_g()], e, 0.f));
-    TRY(fill_task(ctx, g->G[g->lnf_g() + 1], e, 0.f));
+  // zero the LayerNorm and position gradients, which accumulate (over
+  // token tiles, and over minibatches after the first)
+  if (!later_mb) {
+    for (int l = 0; l < c.n_layer; ++l)
+      for (int w : {LN1G, LN1B, LN2G, LN2B})
+        for (int64_t e = 0; e < NE; ++e) TRY(fill_task(ctx, g->G[g->pidx(l, w)], e, 0.f));
+    for (int64_t e = 0; e < NE; ++e) {
+      TRY(fill_task(ctx, g->G[g->lnf_g()], e, 0.f));
+      TRY(fill_task(ctx, g->G[g->lnf_g() + 1], e, 0.f));
+    }
+    for (int64_t lt = 0; lt < g->G[1]->ntiles; ++lt) TRY(fill_task(ctx, g->G[1], lt, 0.f));
   }
-  for (int64_t lt = 0; lt < g->G[1]->ntiles; ++lt) TRY(fill_task(ctx, g->G[1], lt, 0.f));
   for (int64_t bi = 0; bi < g->nb; ++bi)
     for (int64_t si = 0; si < g->ns; ++si)
       TRY(ln_backward(g, g->dnf, g->h_last, lnfg, g->lnf, g->dh, 0, g->G[g->lnf_g()], g->G[g->lnf_g() + 1],
@@ -849,10 +890,10 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
             q.A = {b.g, L(b.g, {bi, si, ik})};
             q.B = {g->dh, L(g->dh, {bi, si, ej})};
             q.C = {gwp, L(gwp, {ik, ej})};
-            q.beta = ti > 0 ? 1.f : 0.f;
+            q.beta = (ti > 0 || later_mb) ? 1.f : 0.f;
             TRY(submit_gemm(ctx, "mlp_proj_dw", q));
           }
-          TRY(colsum_task(ctx, g->dh, L(g->dh, {bi, si, ej}), gbp, ej, ti > 0));
+          TRY(colsum_task(ctx, g->dh, L(g->dh, {bi, si, ej}), gbp, ej, ti > 0 || later_mb));
         }
         for (int64_t ik = 0; ik < NI; ++ik)
           for (int64_t ej = 0; ej < NE; ++ej) {
@@ -875,10 +916,10 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
             q.A = {b.n2, L(b.n2, {bi, si, ek})};
             q.B = {g->dgu, L(g->dgu, {bi, si, ik})};
             q.C = {gwfc, L(gwfc, {ek, ik})};
-            q.beta = ti > 0 ? 1.f : 0.f;
+            q.beta = (ti > 0 || later_mb) ? 1.f : 0.f;
             TRY(submit_gemm(ctx, "fc_dw", q));
           }
-          TRY(colsum_task(ctx, g->dgu, L(g->dgu, {bi, si, ik}), gbfc, ik, ti > 0));
+          TRY(colsum_task(ctx, g->dgu, L(g->dgu, {bi, si, ik}), gbfc, ik, ti > 0 || later_mb));
         }
         for (int64_t ek = 0; ek < NE; ++ek)
           for (int64_t ik = 0; ik < NI; ++ik) {
@@ -900,10 +941,10 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
             q.A = {b.o, L(b.o, {bi, si, hk, 0})};
             q.B = {g->dh, L(g->dh, {bi, si, ej})};
             q.C = {gwo, L(gwo, {hk, 0, ej})};
-            q.beta = ti > 0 ? 1.f : 0.f;
+            q.beta = (ti > 0 || later_mb) ? 1.f : 0.f;
             TRY(submit_gemm(ctx, "attn_proj_dw", q));
           }
-          TRY(colsum_task(ctx, g->dh, L(g->dh, {bi, si, ej}), gbo, ej, ti > 0));
+          TRY(colsum_task(ctx, g->dh, L(g->dh, {bi, si, ej}), gbo, ej, ti > 0 || later_mb));
         }
         for (int64_t hk = 0; hk < NH; ++hk)
           for (int64_t ej = 0; ej < NE; ++ej) {
@@ -959,10 +1000,10 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
               q.A = {b.n1, L(b.n1, {bi, si, ek})};
               q.B = {dqkv[cq], L(dqkv[cq], {bi, si, hj, 0})};
               q.C = {gwqkv, L(gwqkv, {ek, cq, hj, 0})};
-              q.beta = ti > 0 ? 1.f : 0.f;
+              q.beta = (ti > 0 || later_mb) ? 1.f : 0.f;
               TRY(submit_gemm(ctx, "qkv_dw", q));
             }
-            TRY(colsum_task(ctx, dqkv[cq], L(dqkv[cq], {bi, si, hj, 0}), gbqkv, L(gbqkv, {cq, hj, 0}), ti > 0));
+            TRY(colsum_task(ctx, dqkv[cq], L(dqkv[cq], {bi, si, hj, 0}), gbqkv, L(gbqkv, {cq, hj, 0}), ti > 0 || later_mb));
           }
         for (int64_t ek = 0; ek < NE; ++ek) {
           bool firstk = true;

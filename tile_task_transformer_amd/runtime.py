@@ -192,14 +192,19 @@ class GPT2:
         """which: 0 params, 1 grads, 2 first moments, 3 second moments."""
         return {name: self._wrap(i, which, shp).copy_out() for i, (name, shp, _) in enumerate(specs)}
 
-    def step(self, tokens_dev, lr=3e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1, update=True):
+    def step(self, tokens_dev, lr=3e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1, update=True,
+             n_micro=1, start_lr=None, full_lr_iter=1):
+        """One optimiser step. tokens_dev: int32 [n_micro * batch, seq + 1] on
+        the GPU (n_micro minibatches whose gradients accumulate); warm-up:
+        start_lr at the first update, lr from update full_lr_iter on."""
         if hasattr(tokens_dev, "device") and getattr(tokens_dev.device, "type", "") == "cuda":
             # the executor's streams do not order after torch's: the token
             # buffer must be complete before the step's first task reads it
             import torch
             torch.cuda.current_stream(tokens_dev.device).synchronize()
-        hp = L.tt_adamw_hparams(lr, beta1, beta2, eps, weight_decay)
-        check(lib.tt_gpt2_step(self.h, L.ptr(tokens_dev), C.byref(hp), int(update)))
+        hp = L.tt_adamw_hparams(lr, beta1, beta2, eps, weight_decay, lr if start_lr is None else start_lr,
+                                full_lr_iter)
+        check(lib.tt_gpt2_step_accum(self.h, L.ptr(tokens_dev), n_micro, C.byref(hp), int(update)))
 
     def loss(self) -> float:
         f = C.c_float()
