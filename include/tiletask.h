@@ -237,6 +237,16 @@ int tile_attention_bwd(void* stream, int phase, int64_t batch, int64_t heads, in
 int tile_fused_adamw(void* stream, int64_t n, float* p, const float* g, float* m, float* v,
                      float lr, float beta1, float beta2, float eps, float weight_decay,
                      const float* bias_corr);
+/* tile_fused_adamw_multi -- the same update on `count` tiles (0 <= count <=
+ * TT_ADAMW_MAX_TILES) in one launch: tile i has n[i] elements at p[i],
+ * g[i], m[i], v[i]. The pointer arrays and n are HOST arrays of DEVICE
+ * pointers, read before the call returns. Each element gets exactly the
+ * arithmetic of tile_fused_adamw. TT_ERR_ARG for a count out of range, a
+ * negative size or a null pointer of a non-empty tile. */
+#define TT_ADAMW_MAX_TILES 16
+int tile_fused_adamw_multi(void* stream, int count, float* const* p, const float* const* g,
+                           float* const* m, float* const* v, const int64_t* n, float lr, float beta1,
+                           float beta2, float eps, float weight_decay, const float* bias_corr);
 /* tile_adamw_advance -- device-side step counter: t = ++(*step) and
  * bias_corr = {1 - beta1^t, 1 - beta2^t} (step: device int32, bias_corr: device
  * float[2]). One tiny launch per optimiser step. */

@@ -341,6 +341,43 @@ def test_fused_adamw(n):
     assert_close_bound(host(P), rp, 1e-6 * np.abs(rp) + 1e-3 * 3e-4, "p")
 
 
+def test_fused_adamw_multi_equals_per_tile_launches():
+    """Several tiles in one launch (mixed sizes, a ragged one, an unaligned
+    one) give bitwise the per-tile results, which the test above pins to the
+    oracle; more tiles than the limit, or a negative size, are errors."""
+    sizes = [768, 3, 4096 + 2, 1 << 18, 1, 5000]
+    base = torch.from_numpy(synth.rand_normal((sum(sizes) + 64,), 73)).cuda()
+    grads = torch.from_numpy(synth.rand_normal((sum(sizes) + 64,), 74)).cuda()
+    step = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bc = empty((2,))
+    tt.tile_adamw_advance(None, step, bc, 0.9, 0.999)
+
+    def views(t, off=1):  # offset 1 float: the second tile set is not 16-byte aligned
+        out, o = [], off
+        for n in sizes:
+            out.append(t[o:o + n])
+            o += n
+        return out
+    results = []
+    for multi in (False, True):
+        P = [x.clone() for x in views(base)]
+        G = views(grads)
+        M = [torch.full_like(x, 0.01) for x in P]
+        V = [torch.full_like(x, 0.02) for x in P]
+        if multi:
+            tt.tile_fused_adamw_multi(None, P, G, M, V, 3e-4, 0.9, 0.999, 1e-8, 0.1, bc)
+        else:
+            for p_, g_, m_, v_ in zip(P, G, M, V):
+                tt.tile_fused_adamw(None, p_.numel(), p_, g_, m_, v_, 3e-4, 0.9, 0.999, 1e-8, 0.1, bc)
+        torch.cuda.synchronize()
+        results.append([host(x) for x in P + M + V])
+    for a, b in zip(*results):
+        assert np.array_equal(a, b)
+    with pytest.raises(tt.TTError):
+        tt.tile_fused_adamw_multi(None, [base] * 17, [grads] * 17, [base] * 17, [base] * 17, 3e-4, 0.9, 0.999, 1e-8,
+                                  0.1, bc)
+
+
 # ----------------------------------------------------- embedding / misc
 
 def test_embedding_fwd_bwd():

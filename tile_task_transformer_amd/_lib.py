@@ -91,6 +91,7 @@ SIGNATURES = {
     "tile_attention_fwd": (I, [P, I64, I64, I64, I64, I64, I64, I64, P, P, P, P, P, P, I, I, F]),
     "tile_attention_bwd": (I, [P, I, I64, I64, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P, I, I, F]),
     "tile_fused_adamw": (I, [P, I64, P, P, P, P, F, F, F, F, F, P]),
+    "tile_fused_adamw_multi": (I, [P, I, P, P, P, P, P, F, F, F, F, F, P]),
     "tile_adamw_advance": (I, [P, P, P, F, F]),
     "tile_embedding_fwd": (I, [P, I64, I64, P, I64, I64, I64, P, I64, P, I64, I64, I64, P, I64]),
     "tile_embedding_index": (I, [P, I64, P, P, P]),

@@ -107,6 +107,25 @@ __device__ __forceinline__ f32x4 load4(const float* __restrict__ p, int64_t ld, 
   return v;
 }
 
+// Thread -> (row, k) of a K-contiguous operand block [rows][BK]: float4
+// `idx` covers k = c..c+3 of row r. With BK = 32 eight consecutive threads
+// take one row (LDS row stride 36 floats: the 8 float4 of a store cycle hit
+// distinct banks). With BK = 16 the row stride is 20 floats, and two rows'
+// float4s would share banks within a cycle, so 16 consecutive threads take
+// 16 different rows at the same k: rows r and r' then differ by 5(r - r')
+// float4 units, distinct modulo 8 for 8 consecutive rows. Either way a wave
+// fetches the same bytes per load instruction.
+template <int BK>
+__device__ __forceinline__ void kc_index(int idx, int* r, int* c) {
+  if (BK == 16) {
+    *r = (idx >> 6) * 16 + (idx & 15);
+    *c = ((idx >> 4) & 3) * 4;
+  } else {
+    *r = idx / (BK / 4);
+    *c = (idx % (BK / 4)) * 4;
+  }
+}
+
 template <int BM, int BN, int BK, bool TA, bool TB, bool VA, bool VB, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   constexpr int WM = BM / 2, WN = BN / 2;      // wave sub-block
@@ -154,7 +173,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
     for (int i = 0; i < A_PT; ++i) {
       const int idx = tid + 256 * i;
       if (A_KC) {
-        const int r = idx / (BK / 4), c = (idx % (BK / 4)) * 4;
+        int r, c;
+        kc_index<BK>(idx, &r, &c);
         ra[i] = load4<VA>(g.A, g.lda, m0 + r, k0 + c, g.m, kend);
       } else {
         const int r = idx / (BM / 4), c = (idx % (BM / 4)) * 4;
@@ -165,7 +185,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
     for (int i = 0; i < B_PT; ++i) {
       const int idx = tid + 256 * i;
       if (B_KC) {
-        const int r = idx / (BK / 4), c = (idx % (BK / 4)) * 4;
+        int r, c;
+        kc_index<BK>(idx, &r, &c);
         rb[i] = load4<VB>(g.B, g.ldb, n0 + r, k0 + c, g.n, kend);
       } else {
         const int r = idx / (BN / 4), c = (idx % (BN / 4)) * 4;
@@ -179,15 +200,15 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < A_PT; ++i) {
       const int idx = tid + 256 * i;
-      const int r = A_KC ? idx / (BK / 4) : idx / (BM / 4);
-      const int c = A_KC ? (idx % (BK / 4)) * 4 : (idx % (BM / 4)) * 4;
+      int r = idx / (BM / 4), c = (idx % (BM / 4)) * 4;
+      if (A_KC) kc_index<BK>(idx, &r, &c);
       *reinterpret_cast<f32x4*>(As + r * A_LD + c) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < B_PT; ++i) {
       const int idx = tid + 256 * i;
-      const int r = B_KC ? idx / (BK / 4) : idx / (BN / 4);
-      const int c = B_KC ? (idx % (BK / 4)) * 4 : (idx % (BN / 4)) * 4;
+      int r = idx / (BN / 4), c = (idx % (BN / 4)) * 4;
+      if (B_KC) kc_index<BK>(idx, &r, &c);
       *reinterpret_cast<f32x4*>(Bs + r * B_LD + c) = rb[i];
     }
   };

@@ -801,16 +801,51 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
   // layer): the update overlaps the rest of the backward and finds p and g
   // still resident; the result is the same as updating at the end, since no
   // later task of the step reads these parameters
+  // Small tiles (LayerNorm gains, biases) would each be a launch of a few
+  // microseconds: tiles of the given parameters are packed into tasks of up
+  // to TT_ADAMW_MAX_TILES tiles and 4 Mi elements, one launch each.
   tt_tensor *stp = g->step, *bc = g->bc;
   const tt_adamw_hparams h = *hp;
-  auto adamw_of = [&](size_t i) -> int {
+  auto adamw_of = [&](std::initializer_list<size_t> params) -> int {
     if (!do_update) return TT_OK;
-    tt_tensor *p = g->P[i], *gr = g->G[i], *m = g->M[i], *v = g->Vv[i];
-    for (int64_t lt = 0; lt < p->ntiles; ++lt) {
-      const int64_t n = p->tile_elems(lt);
-      TRY(ctx->submit("adamw", {RW(p, lt), R(gr, lt), RW(m, lt), RW(v, lt), R(bc, 0)}, [=](hipStream_t s, void*) {
-        return tile_fused_adamw(s, n, F(p, lt), F(gr, lt), F(m, lt), F(v, lt), h.lr, h.beta1, h.beta2, h.eps,
-                                h.weight_decay, F(bc, 0));
+    struct Item {
+      size_t i;
+      int64_t lt, n;
+    };
+    std::vector<Item> items;
+    for (size_t i : params)
+      for (int64_t lt = 0; lt < g->P[i]->ntiles; ++lt) items.push_back({i, lt, g->P[i]->tile_elems(lt)});
+    size_t k = 0;
+    while (k < items.size()) {
+      std::vector<Item> grp;
+      int64_t elems = 0;
+      while (k < items.size() && (int)grp.size() < TT_ADAMW_MAX_TILES &&
+             (grp.empty() || elems + items[k].n <= (int64_t(4) << 20))) {
+        elems += items[k].n;
+        grp.push_back(items[k++]);
+      }
+      std::vector<Access> acc;
+      for (const Item& it : grp) {
+        acc.push_back(RW(g->P[it.i], it.lt));
+        acc.push_back(R(g->G[it.i], it.lt));
+        acc.push_back(RW(g->M[it.i], it.lt));
+        acc.push_back(RW(g->Vv[it.i], it.lt));
+      }
+      acc.push_back(R(bc, 0));
+      TRY(ctx->submit("adamw", acc, [=](hipStream_t s, void*) {
+        float *pp[TT_ADAMW_MAX_TILES], *mm[TT_ADAMW_MAX_TILES], *vv[TT_ADAMW_MAX_TILES];
+        const float* gg[TT_ADAMW_MAX_TILES];
+        int64_t nn[TT_ADAMW_MAX_TILES];
+        for (size_t j = 0; j < grp.size(); ++j) {
+          const Item& it = grp[j];
+          pp[j] = F(g->P[it.i], it.lt);
+          gg[j] = F(g->G[it.i], it.lt);
+          mm[j] = F(g->M[it.i], it.lt);
+          vv[j] = F(g->Vv[it.i], it.lt);
+          nn[j] = it.n;
+        }
+        return tile_fused_adamw_multi(s, (int)grp.size(), pp, gg, mm, vv, nn, h.lr, h.beta1, h.beta2, h.eps,
+                                      h.weight_decay, F(bc, 0));
       }));
     }
     return TT_OK;
@@ -865,8 +900,7 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
     for (int64_t si = 0; si < g->ns; ++si)
       TRY(ln_backward(g, g->dnf, g->h_last, lnfg, g->lnf, g->dh, 0, g->G[g->lnf_g()], g->G[g->lnf_g() + 1],
                       bi + g->nb * si, bi, si));
-  TRY(adamw_of(g->lnf_g()));
-  TRY(adamw_of(g->lnf_g() + 1));
+  TRY(adamw_of({(size_t)g->lnf_g(), (size_t)g->lnf_g() + 1}));
 
   // ---- blocks backward
   for (int l = c.n_layer - 1; l >= 0; --l) {
@@ -1023,7 +1057,11 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
                         bi, si));
       }
     (void)qkv;
-    for (int w = 0; w < 12; ++w) TRY(adamw_of(g->pidx(l, w)));
+    {
+      const size_t p0 = g->pidx(l, 0);
+      TRY(adamw_of({p0 + LN1G, p0 + LN1B, p0 + BQKV, p0 + BO, p0 + LN2G, p0 + LN2B, p0 + BFC, p0 + BP, p0 + WQKV,
+                    p0 + WO, p0 + WFC, p0 + WP}));
+    }
   }
 
   // ---- embedding backward: token rows into dwte (after its head part), positions into dwpe
@@ -1056,8 +1094,7 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
       }
 
   // ---- AdamW of the embeddings (their gradients are final now)
-  TRY(adamw_of(0));
-  TRY(adamw_of(1));
+  TRY(adamw_of({1, 0}));
   g->last_tasks = ctx->next_id - t0;
   return ctx->flush();
 }

@@ -9,8 +9,12 @@ using tt::f32x4;
 
 namespace {
 
+// Every operation rounds as written (no multiply-add contraction), so the
+// single-tile and multi-tile kernels give bitwise equal results whatever the
+// compiler's scheduling of the surrounding loop.
 __device__ __forceinline__ float adamw1(float& p, float g, float& m, float& v, float lr, float b1, float b2, float eps,
                                         float decay, float bc1, float bc2) {
+#pragma clang fp contract(off)
   p *= decay;
   m = b1 * m + (1.f - b1) * g;
   v = b2 * v + (1.f - b2) * g * g;
@@ -44,6 +48,57 @@ __global__ void adamw_scalar(int64_t n, float* __restrict__ p, const float* __re
   const float bc1 = bc[0], bc2 = bc[1];
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     adamw1(p[i], g[i], m[i], v[i], lr, b1, b2, eps, decay, bc1, bc2);
+}
+
+constexpr int kAdamwMaxTiles = TT_ADAMW_MAX_TILES;
+
+// Several tiles per launch (blockIdx.y = tile); each tile takes the float4
+// path when its four pointers are 16-byte aligned and its size is a
+// multiple of 4, else the scalar one. Same per-element arithmetic as above.
+struct AdamwSet {
+  float* p[kAdamwMaxTiles];
+  const float* g[kAdamwMaxTiles];
+  float* m[kAdamwMaxTiles];
+  float* v[kAdamwMaxTiles];
+  int64_t n[kAdamwMaxTiles];
+};
+
+__global__ __launch_bounds__(256) void adamw_multi(AdamwSet S, int count, float lr, float b1, float b2, float eps,
+                                                   float decay, const float* __restrict__ bc) {
+  const int t = blockIdx.y;
+  if (t >= count) return;
+  const float bc1 = bc[0], bc2 = bc[1];
+  const int64_t n = S.n[t];
+  float* __restrict__ p = S.p[t];
+  const float* __restrict__ g = S.g[t];
+  float* __restrict__ m = S.m[t];
+  float* __restrict__ v = S.v[t];
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const bool vec = (n & 3) == 0 && ((reinterpret_cast<uintptr_t>(p) | reinterpret_cast<uintptr_t>(g) |
+                                     reinterpret_cast<uintptr_t>(m) | reinterpret_cast<uintptr_t>(v)) & 15) == 0;
+  if (vec) {
+    f32x4* p4 = reinterpret_cast<f32x4*>(p);
+    const f32x4* g4 = reinterpret_cast<const f32x4*>(g);
+    f32x4* m4 = reinterpret_cast<f32x4*>(m);
+    f32x4* v4 = reinterpret_cast<f32x4*>(v);
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n / 4; i += stride) {
+      f32x4 pp = p4[i], gg = g4[i], mm = m4[i], vv = v4[i];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float a = pp[k], c = mm[k], e = vv[k];
+        adamw1(a, gg[k], c, e, lr, b1, b2, eps, decay, bc1, bc2);
+        pp[k] = a;
+        mm[k] = c;
+        vv[k] = e;
+      }
+      p4[i] = pp;
+      m4[i] = mm;
+      v4[i] = vv;
+    }
+  } else {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride)
+      adamw1(p[i], g[i], m[i], v[i], lr, b1, b2, eps, decay, bc1, bc2);
+  }
 }
 
 __global__ void adamw_advance_k(int32_t* step, float* bc, float b1, float b2) {
@@ -178,6 +233,32 @@ extern "C" int tile_fused_adamw(void* stream, int64_t n, float* p, const float* 
                        bias_corr);
   }
   return tt::launch_status("tile_fused_adamw");
+}
+
+extern "C" int tile_fused_adamw_multi(void* stream, int count, float* const* p, const float* const* g,
+                                      float* const* m, float* const* v, const int64_t* n, float lr, float beta1,
+                                      float beta2, float eps, float weight_decay, const float* bias_corr) {
+  using tt::fail;
+  if (count < 0 || count > kAdamwMaxTiles) return fail(TT_ERR_ARG, "tile_fused_adamw_multi: count out of range");
+  if (count == 0) return TT_OK;
+  if (!p || !g || !m || !v || !n || !bias_corr) return fail(TT_ERR_ARG, "tile_fused_adamw_multi: null pointer");
+  AdamwSet S{};
+  int64_t most = 0;
+  for (int i = 0; i < count; ++i) {
+    if (n[i] < 0) return fail(TT_ERR_ARG, "tile_fused_adamw_multi: negative size");
+    if (n[i] > 0 && (!p[i] || !g[i] || !m[i] || !v[i])) return fail(TT_ERR_ARG, "tile_fused_adamw_multi: null tile");
+    S.p[i] = p[i];
+    S.g[i] = g[i];
+    S.m[i] = m[i];
+    S.v[i] = v[i];
+    S.n[i] = n[i];
+    most = std::max(most, n[i]);
+  }
+  if (most == 0) return TT_OK;
+  const float decay = 1.f - lr * weight_decay;
+  hipLaunchKernelGGL(adamw_multi, dim3(grid_for((most + 3) / 4), count), dim3(256), 0, tt::as_stream(stream), S,
+                     count, lr, beta1, beta2, eps, decay, bias_corr);
+  return tt::launch_status("tile_fused_adamw_multi");
 }
 
 extern "C" int tile_adamw_advance(void* stream, int32_t* step, float* bias_corr, float beta1, float beta2) {
