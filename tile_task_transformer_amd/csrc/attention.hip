@@ -27,7 +27,10 @@
 // Splitting the rows halves the longest wave of a causal tile (the last
 // query block sees every key), which bounds the kernel's critical path.
 // The next stage's global loads are in flight (in registers) while the
-// current stage's MFMAs run. Per-element causal masking is applied only to
+// current stage's MFMAs run -- except in the dK/dV kernel, which keeps its
+// keys in LDS and issues the loads after the MFMAs: that frees the
+// registers for two workgroups per CU, whose waves cover each other's load
+// latency (measured: 497 -> 446 us per GPT2-small layer backward). Per-element causal masking is applied only to
 // sub-blocks that straddle the diagonal; sub-blocks wholly above it are
 // skipped per wave.
 #include "common.hpp"
@@ -438,7 +441,7 @@ __global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_bwd_dq(AttnGeom g, co
 
 // dK, dV: a group of 32 keys per wave pair; streams query blocks (Q, dO, lse, D).
 template <int HD>
-__global__ __launch_bounds__(kNT, 1) void attn_bwd_dkv(AttnGeom g, const float* __restrict__ Q,
+__global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_bwd_dkv(AttnGeom g, const float* __restrict__ Q,
                                                       const float* __restrict__ K, const float* __restrict__ V,
                                                       const float* __restrict__ dO, const float* __restrict__ lse,
                                                       const float* __restrict__ Dv, float* __restrict__ dK,
@@ -446,6 +449,7 @@ __global__ __launch_bounds__(kNT, 1) void attn_bwd_dkv(AttnGeom g, const float* 
   using C = Cfg<HD>;
   constexpr int LD = C::LD, NKB = C::NKB, NEB = C::NEB;
   __shared__ __attribute__((aligned(16))) float Qs[2 * kBS * LD];   // Q stage, then dO stage
+  __shared__ __attribute__((aligned(16))) float KVs[2 * kBS * LD];  // the workgroup's keys: K (pre-scaled), V
   __shared__ float Ls[kBS], Dd[kBS];
   float* Ds = Qs + kBS * LD;
 
@@ -459,18 +463,22 @@ __global__ __launch_bounds__(kNT, 1) void attn_bwd_dkv(AttnGeom g, const float* 
   const bool kvalid = key < g.k_len;
   const int64_t kpos = g.k_off + key;
 
-  f32x4 kf[NKB], vf[NKB];
+  // the workgroup's 64 keys stay in LDS (registers go to the accumulators);
+  // K is stored pre-scaled by scale * log2(e)
+  float* Kw = KVs;
+  float* Vw = KVs + kBS * LD;
   const float qs = g.scale * kLog2e;
+  {
+    Stager<HD, LD> sk, sv;
+    sk.load(K, b, h, kblk * kBQ, g.k_len, g.heads);
+    sv.load(V, b, h, kblk * kBQ, g.k_len, g.heads);
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
-    f32x4 v = {0.f, 0.f, 0.f, 0.f}, w = v;
-    if (kvalid) {
-      v = *reinterpret_cast<const f32x4*>(K + row_off(b, key, h, g.k_len, g.heads, HD) + 8 * kb + 4 * half);
-      w = *reinterpret_cast<const f32x4*>(V + row_off(b, key, h, g.k_len, g.heads, HD) + 8 * kb + 4 * half);
-    }
-    kf[kb] = v * qs;
-    vf[kb] = w;
+    for (int i = 0; i < Stager<HD, LD>::PT; ++i) sk.r[i] *= qs;
+    sk.store(Kw);
+    sv.store(Vw);
   }
+  const float* kown = Kw + (grp * 32 + l32) * LD + 4 * half;
+  const float* vown = Vw + (grp * 32 + l32) * LD + 4 * half;
   f32x16 dkv[2 * NEB];  // dK blocks, then dV blocks
 #pragma unroll
   for (int n = 0; n < 2 * NEB; ++n)
@@ -514,7 +522,6 @@ __global__ __launch_bounds__(kNT, 1) void attn_bwd_dkv(AttnGeom g, const float* 
   __syncthreads();
   for (int qb = qstart; qb < g.q_len; qb += kBS) {
     const bool more = qb + kBS < g.q_len;
-    if (more) load_rows(qb + kBS);
     const int qb0 = qb + part * 32;
     const float* qsb = Qs + part * 32 * LD;
     const float* dsb = Ds + part * 32 * LD;
@@ -531,10 +538,12 @@ __global__ __launch_bounds__(kNT, 1) void attn_bwd_dkv(AttnGeom g, const float* 
       for (int kb = 0; kb < NKB; ++kb) {
         const f32x4 qf = *reinterpret_cast<const f32x4*>(qsb + l32 * LD + 8 * kb + 4 * half);
         const f32x4 df = *reinterpret_cast<const f32x4*>(dsb + l32 * LD + 8 * kb + 4 * half);
+        const f32x4 kf = *reinterpret_cast<const f32x4*>(kown + 8 * kb);
+        const f32x4 vf = *reinterpret_cast<const f32x4*>(vown + 8 * kb);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          s = mfma(qf[i], kf[kb][i], s);     // S = Q K^T (log2 units); lane owns a key column
-          dp = mfma(df[i], vf[kb][i], dp);   // dP = dO V^T
+          s = mfma(qf[i], kf[i], s);     // S = Q K^T (log2 units); lane owns a key column
+          dp = mfma(df[i], vf[i], dp);   // dP = dO V^T
         }
       }
       const bool edge = qb0 + 31 >= g.q_len || g.q_off + qb0 < wave_kmax;
@@ -557,6 +566,10 @@ __global__ __launch_bounds__(kNT, 1) void attn_bwd_dkv(AttnGeom g, const float* 
         for (int r = 0; r < 16; ++r)
           dkv[eb] = mfma(qsb[kidx(r, half) * LD + eb * 32 + l32], s[r], dkv[eb]);  // dK^T += Q^T dS
     }
+    // the next stage's loads are issued after the MFMAs, so the staging
+    // registers are not live across them (two workgroups fit per CU; the
+    // other one's MFMAs cover this load's latency)
+    if (more) load_rows(qb + kBS);
     __syncthreads();
     if (more) store_rows();
     __syncthreads();
