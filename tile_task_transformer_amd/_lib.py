@@ -17,6 +17,15 @@ LIB_PATH = os.environ.get("TILETASK_LIB", os.path.join(_HERE, "libtiletask.so"))
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"libtiletask.so not found at {LIB_PATH}: build it with "
                       "`python tile_task_transformer_amd/build.py` (hipcc, gfx950)")
+# One HIP runtime per process. PyTorch-ROCm ships its own libamdhip64 and
+# asks for it as "libamdhip64.so"; this library asks for "libamdhip64.so.7".
+# Loaded after torch, ours resolves to torch's copy (same soname); loaded
+# first, torch would bring a second runtime, and whichever initialised
+# second would find no device. So torch, when present, is loaded first.
+try:
+    import torch  # noqa: F401
+except ImportError:
+    pass
 lib = C.CDLL(LIB_PATH)
 
 # ---- constants (mirror include/tiletask.h)

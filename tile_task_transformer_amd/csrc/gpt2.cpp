@@ -815,12 +815,17 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
     std::vector<Item> items;
     for (size_t i : params)
       for (int64_t lt = 0; lt < g->P[i]->ntiles; ++lt) items.push_back({i, lt, g->P[i]->tile_elems(lt)});
+    // with pinned-host homes a task's tiles must fit the device arena (p, g,
+    // m and v of every tile): a group then takes at most an eighth of it
+    int64_t max_elems = int64_t(4) << 20;
+    if (g->param_home == TT_HOME_PINNED_HOST && ctx->budget > 0)
+      max_elems = std::min<int64_t>(max_elems, (int64_t)(ctx->budget / (8 * 4 * sizeof(float))));
     size_t k = 0;
     while (k < items.size()) {
       std::vector<Item> grp;
       int64_t elems = 0;
       while (k < items.size() && (int)grp.size() < TT_ADAMW_MAX_TILES &&
-             (grp.empty() || elems + items[k].n <= (int64_t(4) << 20))) {
+             (grp.empty() || elems + items[k].n <= max_elems)) {
         elems += items[k].n;
         grp.push_back(items[k++]);
       }
