@@ -166,7 +166,7 @@ def tile_classes(w, reps=20, only=None):
 
     out = {}
     for label, f in GEMM_SHAPES.items():
-        if only and label != only:
+        if only and label != only:  # "attn": the attention classes only
             continue
         ta, tb, m, n, k, epi, beta = f(r, e, i, h, v)
         A = rnd(k, m) if ta else rnd(m, k)
@@ -180,7 +180,7 @@ def tile_classes(w, reps=20, only=None):
         tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
         out[label] = {"bound": "mfma", "shape": [m, n, k, ta, tb], "us": round(ms * 1e3, 1),
                       "achieved": round(tf, 2), "unit": "TFLOP/s", "frac": round(tf / MFMA_FP32_PEAK, 4)}
-    if only:
+    if only and only != "attn":
         return out
     # attention (per (batch tile, head tile) pair of the workload's seq tile)
     Q, K, V = rnd(t.batch, t.seq, t.head, hd), rnd(t.batch, t.seq, t.head, hd), rnd(t.batch, t.seq, t.head, hd)
@@ -197,6 +197,8 @@ def tile_classes(w, reps=20, only=None):
                                              None, dO, lse, Dv, dQ, dK, dV, 0, 0, sc))
     out["attn_bwd"] = {"bound": "mfma", "us": round(ms * 1e3, 1), "achieved": round(2.5 * fl / ms / 1e9, 2),
                        "unit": "TFLOP/s (model)", "frac": round(2.5 * fl / ms / 1e9 / MFMA_FP32_PEAK, 4)}
+    if only:
+        return out
 
     def hbm(label, nbytes, fn):
         ms = timed(fn)

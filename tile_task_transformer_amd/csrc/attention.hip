@@ -46,6 +46,13 @@ constexpr int kNT = 256;          // threads per workgroup (4 waves)
 constexpr int kBQ = 64;           // queries (dK/dV kernel: keys) owned per workgroup
 constexpr int kBS = 64;           // streamed rows per LDS stage (2 halves of 32)
 
+// 2^x with the hardware instruction: every argument here is <= 0 (scores
+// minus a running or final maximum), and a result below 2^-126 is
+// negligible next to the row sum (>= 1), so no denormal range handling.
+// Used in the forward (3% faster there); the backward kernels keep exp2f,
+// with which they measured 8% faster (instruction scheduling).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ f32x16 mfma(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
@@ -207,11 +214,11 @@ __global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_fwd(AttnGeom g, const
       for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, s[r]);
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
       const float mnew = fmaxf(m, mloc);
-      const float alpha = mnew == -INFINITY ? 1.f : exp2f(m - mnew);
+      const float alpha = mnew == -INFINITY ? 1.f : exp2_hw(m - mnew);
       float psum = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        s[r] = mnew == -INFINITY ? 0.f : exp2f(s[r] - mnew);
+        s[r] = mnew == -INFINITY ? 0.f : exp2_hw(s[r] - mnew);
         psum += s[r];
       }
       psum += __shfl_xor(psum, 32, 64);
@@ -250,7 +257,7 @@ __global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_fwd(AttnGeom g, const
     const float* p = xb + (grp * 64 + lane) * STR;
     const float m1 = p[0], l1 = p[1];
     const float mm = fmaxf(m, m1);
-    const float a0 = m == -INFINITY ? 0.f : exp2f(m - mm), a1 = m1 == -INFINITY ? 0.f : exp2f(m1 - mm);
+    const float a0 = m == -INFINITY ? 0.f : exp2_hw(m - mm), a1 = m1 == -INFINITY ? 0.f : exp2_hw(m1 - mm);
     l = l * a0 + l1 * a1;
     m = mm;
 #pragma unroll
