@@ -298,6 +298,13 @@ size_t tile_reduce_rows_workspace(int64_t rows, int64_t cols);
  * array tokens[b*(seq+1) + t] (int32), ids[b*seq + t] = tokens[b*(seq+1)+t]
  * and labels[b*seq + t] = tokens[b*(seq+1)+t+1] for b < batch, t < seq. */
 int tile_fill(void* stream, int64_t n, float* dst, float value);
+/* tile_fill_multi -- the same on `count` tiles (0 <= count <=
+ * TT_FILL_MAX_TILES) in one launch: dst[i][0..n[i]) = value. dst and n are
+ * HOST arrays (dst of DEVICE pointers), read before the call returns.
+ * TT_ERR_ARG for a count out of range, a negative size or a null pointer of
+ * a non-empty tile. */
+#define TT_FILL_MAX_TILES 16
+int tile_fill_multi(void* stream, int count, float* const* dst, const int64_t* n, float value);
 int tile_split_tokens(void* stream, int64_t batch, int64_t seq, const int32_t* tokens,
                       int32_t* ids, int32_t* labels);
 

@@ -378,6 +378,20 @@ def test_fused_adamw_multi_equals_per_tile_launches():
                                   0.1, bc)
 
 
+def test_fill_multi():
+    sizes = [1, 5, 768, 4097, 1 << 17]
+    buf = torch.full((sum(sizes) + 8,), 7.0, device="cuda")
+    tiles, o = [], 3
+    for n in sizes:
+        tiles.append(buf[o:o + n])
+        o += n
+    tt.tile_fill_multi(None, tiles, -2.5)
+    got = host(buf)
+    assert (got[:3] == 7.0).all() and (got[3:o] == -2.5).all() and (got[o:] == 7.0).all()
+    with pytest.raises(tt.TTError):
+        tt.tile_fill_multi(None, [buf] * 17, 0.0)
+
+
 # ----------------------------------------------------- embedding / misc
 
 def test_embedding_fwd_bwd():

@@ -108,6 +108,7 @@ SIGNATURES = {
     "tile_reduce_rows": (I, [P, I64, I64, P, I64, P, I, P]),
     "tile_reduce_rows_workspace": (SZ, [I64, I64]),
     "tile_fill": (I, [P, I64, P, F]),
+    "tile_fill_multi": (I, [P, I, P, P, F]),
     "tile_split_tokens": (I, [P, I64, I64, P, P, P]),
     "tt_ctx_create": (I, [I, I, I, SZ, PP]),
     "tt_ctx_destroy": (I, [P]),

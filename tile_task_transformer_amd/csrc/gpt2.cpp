@@ -130,10 +130,38 @@ int submit_gemm(tt_ctx* ctx, const char* label, const Gemm& q) {
   }, 2.0 * m * n * k);
 }
 
-int fill_task(tt_ctx* ctx, tt_tensor* t, int64_t lin, float v) {
-  const int64_t n = t->tile_elems(lin);
-  return ctx->submit("fill", {W(t, lin)}, [t, lin, n, v](hipStream_t s, void*) { return tile_fill(s, n, F(t, lin), v); });
+// tiles = value, TT_FILL_MAX_TILES tiles per task and launch (with
+// pinned-host homes a task's tiles take at most an eighth of the arena)
+int fill_tasks(tt_gpt2* g, const std::vector<TileRef>& tiles, float v) {
+  tt_ctx* ctx = g->ctx;
+  int64_t max_elems = int64_t(1) << 30;
+  if (g->param_home == TT_HOME_PINNED_HOST && ctx->budget > 0)
+    max_elems = (int64_t)(ctx->budget / (8 * sizeof(float)));
+  size_t k = 0;
+  while (k < tiles.size()) {
+    std::vector<TileRef> grp;
+    int64_t elems = 0;
+    while (k < tiles.size() && (int)grp.size() < TT_FILL_MAX_TILES &&
+           (grp.empty() || elems + tiles[k].t->tile_elems(tiles[k].lin) <= max_elems)) {
+      elems += tiles[k].t->tile_elems(tiles[k].lin);
+      grp.push_back(tiles[k++]);
+    }
+    std::vector<Access> acc;
+    for (const TileRef& r : grp) acc.push_back(W(r.t, r.lin));
+    int rc = ctx->submit("fill", acc, [grp, v](hipStream_t s, void*) {
+      float* dst[TT_FILL_MAX_TILES];
+      int64_t n[TT_FILL_MAX_TILES];
+      for (size_t j = 0; j < grp.size(); ++j) {
+        dst[j] = F(grp[j].t, grp[j].lin);
+        n[j] = grp[j].t->tile_elems(grp[j].lin);
+      }
+      return tile_fill_multi(s, (int)grp.size(), dst, n, v);
+    });
+    if (rc) return rc;
+  }
+  return TT_OK;
 }
+
 
 #define TRY(x)                 \
   do {                         \
@@ -892,14 +920,16 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
   // zero the LayerNorm and position gradients, which accumulate (over
   // token tiles, and over minibatches after the first)
   if (!later_mb) {
+    std::vector<TileRef> zero;
     for (int l = 0; l < c.n_layer; ++l)
       for (int w : {LN1G, LN1B, LN2G, LN2B})
-        for (int64_t e = 0; e < NE; ++e) TRY(fill_task(ctx, g->G[g->pidx(l, w)], e, 0.f));
+        for (int64_t e = 0; e < NE; ++e) zero.push_back({g->G[g->pidx(l, w)], e});
     for (int64_t e = 0; e < NE; ++e) {
-      TRY(fill_task(ctx, g->G[g->lnf_g()], e, 0.f));
-      TRY(fill_task(ctx, g->G[g->lnf_g() + 1], e, 0.f));
+      zero.push_back({g->G[g->lnf_g()], e});
+      zero.push_back({g->G[g->lnf_g() + 1], e});
     }
-    for (int64_t lt = 0; lt < g->G[1]->ntiles; ++lt) TRY(fill_task(ctx, g->G[1], lt, 0.f));
+    for (int64_t lt = 0; lt < g->G[1]->ntiles; ++lt) zero.push_back({g->G[1], lt});
+    TRY(fill_tasks(g, zero, 0.f));
   }
   for (int64_t bi = 0; bi < g->nb; ++bi)
     for (int64_t si = 0; si < g->ns; ++si)
@@ -1069,7 +1099,26 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
     }
   }
 
-  // ---- embedding backward: token rows into dwte (after its head part), positions into dwpe
+  // ---- embedding backward: token rows into dwte (after its head part), positions into dwpe.
+  // In HBM the dwte tiles of one embd column are one contiguous [V, et] slab
+  // (first grid axis fastest), so one launch per (embd tile, token tile)
+  // covers every vocab tile; staged pinned tiles are separate, one launch each.
+  if (gwte->home == TT_HOME_DEVICE) {
+    for (int64_t ek = 0; ek < NE; ++ek)
+      for (int64_t si = 0; si < g->ns; ++si)
+        for (int64_t bi = 0; bi < g->nb; ++bi) {
+          tt_tensor *dh = g->dh, *so = g->sorted, *pe = g->perm;
+          const int64_t ld = L(dh, {bi, si, ek}), li = L(so, {bi, si}), lw0 = L(gwte, {0, ek});
+          int64_t r, cols;
+          dh->mat(ld, &r, &cols);
+          std::vector<Access> acc = {R(dh, ld), R(so, li), R(pe, li)};
+          for (int64_t vj = 0; vj < NV; ++vj) acc.push_back(RW(gwte, L(gwte, {vj, ek})));
+          TRY(ctx->submit("emb_dw", acc, [=](hipStream_t s, void*) {
+            return tile_embedding_bwd(s, TT_EMB_TOKEN, rows, cols, I32(so, li), I32(pe, li), 0, V, sq, F(dh, ld), cols,
+                                      F(gwte, lw0), cols);
+          }));
+        }
+  } else
   for (int64_t vj = 0; vj < NV; ++vj)
     for (int64_t ek = 0; ek < NE; ++ek)
       for (int64_t si = 0; si < g->ns; ++si)

@@ -346,6 +346,40 @@ extern "C" int tile_fill(void* stream, int64_t n, float* dst, float value) {
   return tt::launch_status("tile_fill");
 }
 
+namespace {
+struct FillSet {
+  float* p[TT_FILL_MAX_TILES];
+  int64_t n[TT_FILL_MAX_TILES];
+};
+
+__global__ __launch_bounds__(256) void fill_multi(FillSet S, int count, float value) {
+  const int t = blockIdx.y;
+  if (t >= count) return;
+  float* __restrict__ p = S.p[t];
+  const int64_t n = S.n[t];
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = value;
+}
+}  // namespace
+
+extern "C" int tile_fill_multi(void* stream, int count, float* const* dst, const int64_t* n, float value) {
+  if (count < 0 || count > TT_FILL_MAX_TILES) return tt::fail(TT_ERR_ARG, "tile_fill_multi: count out of range");
+  if (count == 0) return TT_OK;
+  if (!dst || !n) return tt::fail(TT_ERR_ARG, "tile_fill_multi: null pointer");
+  FillSet S{};
+  int64_t most = 0;
+  for (int i = 0; i < count; ++i) {
+    if (n[i] < 0) return tt::fail(TT_ERR_ARG, "tile_fill_multi: negative size");
+    if (n[i] > 0 && !dst[i]) return tt::fail(TT_ERR_ARG, "tile_fill_multi: null tile");
+    S.p[i] = dst[i];
+    S.n[i] = n[i];
+    most = std::max(most, n[i]);
+  }
+  if (most == 0) return TT_OK;
+  hipLaunchKernelGGL(fill_multi, dim3(grid_for(most), count), dim3(256), 0, tt::as_stream(stream), S, count, value);
+  return tt::launch_status("tile_fill_multi");
+}
+
 extern "C" int tile_split_tokens(void* stream, int64_t batch, int64_t seq, const int32_t* tokens, int32_t* ids,
                                  int32_t* labels) {
   if (batch < 0 || seq < 0) return tt::fail(TT_ERR_ARG, "tile_split_tokens: negative size");

@@ -17,7 +17,7 @@ __all__ = [
     "tile_xentropy", "tile_attention_fwd", "tile_attention_bwd", "tile_fused_adamw", "tile_fused_adamw_multi",
     "tile_adamw_advance",
     "tile_embedding_fwd", "tile_embedding_index", "tile_embedding_bwd", "tile_reduce_rows",
-    "tile_reduce_rows_workspace", "tile_fill", "tile_split_tokens",
+    "tile_reduce_rows_workspace", "tile_fill", "tile_fill_multi", "tile_split_tokens",
     "TT_EPI_NONE", "TT_EPI_BIAS", "TT_EPI_RES", "TT_EPI_GELU", "TT_EPI_GELU_BWD", "TT_LN_PARTIAL",
     "TT_LN_MERGE", "TT_LN_APPLY", "TT_LN_FUSED", "TT_SM_STATS", "TT_SM_MERGE", "TT_SM_APPLY", "TT_XE_LOSS",
     "TT_XE_GRAD", "TT_ATT_PREP", "TT_ATT_GRAD", "TT_EMB_TOKEN", "TT_EMB_POS",
@@ -127,6 +127,15 @@ def tile_reduce_rows_workspace(rows, cols):
 
 def tile_fill(stream, n, dst, value):
     return check(lib.tile_fill(stream_handle(stream), n, ptr(dst), value))
+
+
+def tile_fill_multi(stream, dsts, value):
+    """Tiles given as a list of torch tensors (or (address, count) pairs)."""
+    import ctypes as C
+    k = len(dsts)
+    ptrs = (C.c_void_p * max(k, 1))(*[ptr(x[0] if isinstance(x, tuple) else x) for x in dsts])
+    ns = (C.c_int64 * max(k, 1))(*[int(x[1] if isinstance(x, tuple) else x.numel()) for x in dsts])
+    return check(lib.tile_fill_multi(stream_handle(stream), k, ptrs, ns, value))
 
 
 def tile_split_tokens(stream, batch, seq, tokens, ids, labels):

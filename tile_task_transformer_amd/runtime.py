@@ -20,6 +20,7 @@ class Context:
         h = C.c_void_p()
         check(lib.tt_ctx_create(device, n_streams, window, device_budget, C.byref(h)))
         self.h = h
+        self.n_streams = n_streams
         self.dryrun = device == L.TT_DEVICE_DRYRUN
         self._tensors: List["Tensor"] = []
 
@@ -198,10 +199,13 @@ class GPT2:
         the GPU (n_micro minibatches whose gradients accumulate); warm-up:
         start_lr at the first update, lr from update full_lr_iter on."""
         if hasattr(tokens_dev, "device") and getattr(tokens_dev.device, "type", "") == "cuda":
-            # the executor's streams do not order after torch's: the token
-            # buffer must be complete before the step's first task reads it
+            # the executor's streams do not order after torch's: they wait (on
+            # the device, the host does not block) for the work torch has
+            # queued so far, which includes whatever wrote the token buffer
             import torch
-            torch.cuda.current_stream(tokens_dev.device).synchronize()
+            cur = torch.cuda.current_stream(tokens_dev.device)
+            for i in range(self.ctx.n_streams):
+                torch.cuda.ExternalStream(self.ctx.stream(i), device=tokens_dev.device).wait_stream(cur)
         hp = L.tt_adamw_hparams(lr, beta1, beta2, eps, weight_decay, lr if start_lr is None else start_lr,
                                 full_lr_iter)
         check(lib.tt_gpt2_step_accum(self.h, L.ptr(tokens_dev), n_micro, C.byref(hp), int(update)))
