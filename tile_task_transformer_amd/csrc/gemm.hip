@@ -391,6 +391,29 @@ Plan plan_for(int64_t m, int64_t n, int64_t k, size_t ws_bytes) {
     }
     if (best_s > 1) return Plan{128, 128, 32, best_s, (int)best_chunk};
   }
+  // small tiles (the small-tile workload's weight gradients, e.g. 512 x 512
+  // x 1024): fewer 64x64 blocks than CUs and a K of at least 1024 tokens ->
+  // split over 64x64 blocks by the same balance rule
+  const int64_t b64 = blocks(64, 64);
+  if (k >= 1024 && b64 < kCUs && ws_bytes > 0) {
+    int best_s = 1;
+    int64_t best_chunk = k;
+    double best_bal = (double)b64 / (double)kCUs;
+    for (int s = 2; s <= 8; ++s) {
+      int64_t chunk = (k + s - 1) / s;
+      chunk = (chunk + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
+      const int64_t sa = (k + chunk - 1) / chunk;
+      if (chunk < 128 || (size_t)sa * m * n * sizeof(float) > ws_bytes) continue;
+      const int64_t nwg = b64 * sa;
+      const double bal = (double)nwg / (double)(((nwg + kCUs - 1) / kCUs) * kCUs);
+      if (bal > best_bal + 0.01) {
+        best_bal = bal;
+        best_s = (int)sa;
+        best_chunk = chunk;
+      }
+    }
+    if (best_s > 1) return Plan{64, 64, 32, best_s, (int)best_chunk};
+  }
   return Plan{64, 64, 32, 1, (int)k};
 }
 
