@@ -45,7 +45,8 @@ def test_gemm_parity(ta, tb, m, n, k):
 
 @pytest.mark.parametrize("ta,tb,m,n,k", [(1, 0, 768, 768, 4096), (1, 0, 700, 300, 5000), (0, 1, 1536, 768, 4096),
                                          (0, 0, 1000, 200, 2049), (1, 1, 3072, 768, 4096),
-                                         (1, 0, 512, 512, 1024), (0, 1, 1024, 512, 1024), (0, 0, 1000, 300, 1100)])
+                                         (1, 0, 512, 512, 1024), (0, 1, 1024, 512, 1024), (0, 0, 1000, 300, 1100),
+                                         (0, 1, 1024, 512, 512)])
 def test_gemm_split_k_workspace(ta, tb, m, n, k):
     """Tall-K shapes take the split-K path when given a workspace: same result
     within the fp32 bound, bitwise equal across runs, epilogue applied once."""

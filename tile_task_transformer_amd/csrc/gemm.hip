@@ -391,11 +391,11 @@ Plan plan_for(int64_t m, int64_t n, int64_t k, size_t ws_bytes) {
     }
     if (best_s > 1) return Plan{128, 128, 32, best_s, (int)best_chunk};
   }
-  // small tiles (the small-tile workload's weight gradients, e.g. 512 x 512
-  // x 1024): fewer 64x64 blocks than CUs and a K of at least 1024 tokens ->
-  // split over 64x64 blocks by the same balance rule
+  // small tiles (the small-tile workload's GEMMs, e.g. 512 x 512 x 1024 or
+  // 1024 x 512 x 512): fewer 64x64 blocks than CUs and a K of at least 512
+  // -> split over 64x64 blocks by the same balance rule
   const int64_t b64 = blocks(64, 64);
-  if (k >= 1024 && b64 < kCUs && ws_bytes > 0) {
+  if (k >= 512 && b64 < kCUs && ws_bytes > 0) {
     int best_s = 1;
     int64_t best_chunk = k;
     double best_bal = (double)b64 / (double)kCUs;
