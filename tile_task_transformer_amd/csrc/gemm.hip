@@ -8,9 +8,17 @@
 //     C; each wave owns a (BM/2) x (BN/2) sub-block made of 32x32 MFMA tiles
 //     whose fp32 accumulators stay in registers for the whole K loop;
 //   * K advances in steps of BK (16 or 32, per plan) through two LDS
-//     buffers: the next step's global loads are issued before the current
-//     step's MFMAs and written to the other buffer afterwards, so one
-//     barrier per step suffices;
+//     buffers and two register sets: the global loads of step t+2 are
+//     issued before step t's MFMAs, step t+1 (loaded a step earlier) is
+//     written to the other LDS buffer after them, and one barrier per step
+//     suffices; the global latency is covered by two steps of MFMAs;
+//   * inside a step the fragments of k group g+1 are requested from LDS
+//     before the MFMAs of group g (a scheduling barrier keeps the compiler
+//     from sinking them), so LDS latency is paid once per step, not once
+//     per group;
+//   * blocks whose every load is in range run a branch-free copy of the
+//     loop (uniform base pointer + per-thread offsets); edge blocks run the
+//     same loop with guarded, zero-filling loads;
 //   * each operand is staged in LDS in the orientation it has in HBM, so the
 //     global->LDS path is always 16-byte vector loads/stores:
 //       K-contiguous operands (A, or B^T)  -> LDS [rows][BK + 4]
@@ -167,51 +175,11 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   const int kbeg = split * g.kchunk;
   const int kend = min(g.k, kbeg + g.kchunk);
 
-  f32x4 ra[A_PT], rb[B_PT];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < A_PT; ++i) {
-      const int idx = tid + 256 * i;
-      if (A_KC) {
-        int r, c;
-        kc_index<BK>(idx, &r, &c);
-        ra[i] = load4<VA>(g.A, g.lda, m0 + r, k0 + c, g.m, kend);
-      } else {
-        const int r = idx / (BM / 4), c = (idx % (BM / 4)) * 4;
-        ra[i] = load4<VA>(g.A, g.lda, k0 + r, m0 + c, kend, g.m);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < B_PT; ++i) {
-      const int idx = tid + 256 * i;
-      if (B_KC) {
-        int r, c;
-        kc_index<BK>(idx, &r, &c);
-        rb[i] = load4<VB>(g.B, g.ldb, n0 + r, k0 + c, g.n, kend);
-      } else {
-        const int r = idx / (BN / 4), c = (idx % (BN / 4)) * 4;
-        rb[i] = load4<VB>(g.B, g.ldb, k0 + r, n0 + c, kend, g.n);
-      }
-    }
-  };
-  auto sstore = [&](int buf) {
-    float* As = lds + buf * (A_SZ + B_SZ);
-    float* Bs = As + A_SZ;
-#pragma unroll
-    for (int i = 0; i < A_PT; ++i) {
-      const int idx = tid + 256 * i;
-      int r = idx / (BM / 4), c = (idx % (BM / 4)) * 4;
-      if (A_KC) kc_index<BK>(idx, &r, &c);
-      *reinterpret_cast<f32x4*>(As + r * A_LD + c) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < B_PT; ++i) {
-      const int idx = tid + 256 * i;
-      int r = idx / (BN / 4), c = (idx % (BN / 4)) * 4;
-      if (B_KC) kc_index<BK>(idx, &r, &c);
-      *reinterpret_cast<f32x4*>(Bs + r * B_LD + c) = rb[i];
-    }
-  };
+  const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+  // Interior blocks (every load of every K step in range and 16-byte
+  // loadable) run a branch-free copy of the loop; edge blocks a guarded one.
+  const bool fast = VA && VB && m0 + BM <= g.m && n0 + BN <= g.n && (kend - kbeg) % BK == 0 &&
+                    (int64_t)BM * g.lda < INT32_MAX && (int64_t)BN * g.ldb < INT32_MAX;
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -221,21 +189,88 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
-  if (nk > 0) {
-    gload(kbeg);
-    sstore(0);
-  }
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kbeg + (kt + 1) * BK);
-    const float* As = lds + cur * (A_SZ + B_SZ);
-    const float* Bs = As + A_SZ;
+  auto run = [&](auto guard_tag) {
+    constexpr bool G = decltype(guard_tag)::value;
+    // Two register sets of staged operands: the global loads of step t+2
+    // are in flight while step t is multiplied and step t+1 is written to LDS.
+    f32x4 ra0[A_PT], rb0[B_PT], ra1[A_PT], rb1[B_PT];
+    // fast path: per-thread element offsets inside a K step (32-bit; the
+    // step's base pointer is uniform)
+    int oa[A_PT], ob[B_PT];
 #pragma unroll
-    for (int kb = 0; kb < BK / 8; ++kb) {
+    for (int i = 0; i < A_PT; ++i) {
+      const int idx = tid + 256 * i;
+      int r = idx / (BM / 4), c = (idx % (BM / 4)) * 4;
+      if (A_KC) kc_index<BK>(idx, &r, &c);
+      oa[i] = r * (int)g.lda + c;
+    }
+#pragma unroll
+    for (int i = 0; i < B_PT; ++i) {
+      const int idx = tid + 256 * i;
+      int r = idx / (BN / 4), c = (idx % (BN / 4)) * 4;
+      if (B_KC) kc_index<BK>(idx, &r, &c);
+      ob[i] = r * (int)g.ldb + c;
+    }
+    // K step `st` -> registers. st is clamped to the last step, so every
+    // call issues the same loads (the compiler's wait counts stay exact);
+    // the repeated loads of the last step are never stored.
+    auto gload = [&](int st, f32x4(&ra)[A_PT], f32x4(&rb)[B_PT]) {
+      const int k0 = kbeg + min(st, nk - 1) * BK;
+      if constexpr (!G) {
+        const float* pa = A_KC ? g.A + (int64_t)m0 * g.lda + k0 : g.A + (int64_t)k0 * g.lda + m0;
+        const float* pb = B_KC ? g.B + (int64_t)n0 * g.ldb + k0 : g.B + (int64_t)k0 * g.ldb + n0;
+#pragma unroll
+        for (int i = 0; i < A_PT; ++i) ra[i] = *reinterpret_cast<const f32x4*>(pa + oa[i]);
+#pragma unroll
+        for (int i = 0; i < B_PT; ++i) rb[i] = *reinterpret_cast<const f32x4*>(pb + ob[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < A_PT; ++i) {
+          const int idx = tid + 256 * i;
+          int r = idx / (BM / 4), c = (idx % (BM / 4)) * 4;
+          if (A_KC) {
+            kc_index<BK>(idx, &r, &c);
+            ra[i] = load4<VA>(g.A, g.lda, m0 + r, k0 + c, g.m, kend);
+          } else {
+            ra[i] = load4<VA>(g.A, g.lda, k0 + r, m0 + c, kend, g.m);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < B_PT; ++i) {
+          const int idx = tid + 256 * i;
+          int r = idx / (BN / 4), c = (idx % (BN / 4)) * 4;
+          if (B_KC) {
+            kc_index<BK>(idx, &r, &c);
+            rb[i] = load4<VB>(g.B, g.ldb, n0 + r, k0 + c, g.n, kend);
+          } else {
+            rb[i] = load4<VB>(g.B, g.ldb, k0 + r, n0 + c, kend, g.n);
+          }
+        }
+      }
+    };
+    auto sstore = [&](int buf, const f32x4(&ra)[A_PT], const f32x4(&rb)[B_PT]) {
+      float* As = lds + buf * (A_SZ + B_SZ);
+      float* Bs = As + A_SZ;
+#pragma unroll
+      for (int i = 0; i < A_PT; ++i) {
+        const int idx = tid + 256 * i;
+        int r = idx / (BM / 4), c = (idx % (BM / 4)) * 4;
+        if (A_KC) kc_index<BK>(idx, &r, &c);
+        *reinterpret_cast<f32x4*>(As + r * A_LD + c) = ra[i];
+      }
+#pragma unroll
+      for (int i = 0; i < B_PT; ++i) {
+        const int idx = tid + 256 * i;
+        int r = idx / (BN / 4), c = (idx % (BN / 4)) * 4;
+        if (B_KC) kc_index<BK>(idx, &r, &c);
+        *reinterpret_cast<f32x4*>(Bs + r * B_LD + c) = rb[i];
+      }
+    };
+    // fragments of k group kb (8 k values) of LDS buffer `buf`
+    auto frag = [&](int buf, int kb, f32x4(&fa)[FM], f32x4(&fb)[FN]) {
+      const float* As = lds + buf * (A_SZ + B_SZ);
+      const float* Bs = As + A_SZ;
       const int kk = kb * 8 + half * 4;
-      f32x4 fa[FM], fb[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int row = wm * WM + i * 32 + l32;
@@ -256,6 +291,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
           for (int s = 0; s < 4; ++s) fb[j][s] = Bs[(kk + s) * B_LD + col];
         }
       }
+    };
+    auto mfmas = [&](const f32x4(&fa)[FM], const f32x4(&fb)[FN]) {
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -263,10 +300,51 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
 #pragma unroll
           for (int j = 0; j < FN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][s], fb[j][s], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) sstore(cur ^ 1);
+    };
+    // One K step from LDS buffer `buf`, software-pipelined by k group: the
+    // fragments of group kb+1 are requested before the MFMAs of group kb
+    // are issued (the scheduling barrier keeps the compiler from sinking
+    // the reads next to their use, which would expose an LDS latency per
+    // group).
+    auto compute = [&](int buf) {
+      f32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+      frag(buf, 0, fa0, fb0);
+#pragma unroll
+      for (int kb = 0; kb < BK / 8; ++kb) {
+        if (kb + 1 < BK / 8) {
+          if (kb & 1) frag(buf, kb + 1, fa0, fb0);
+          else frag(buf, kb + 1, fa1, fb1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (kb & 1) mfmas(fa1, fb1);
+        else mfmas(fa0, fb0);
+      }
+    };
+
+    if (nk == 0) return;
+    gload(0, ra0, rb0);
+    gload(1, ra1, rb1);
+    sstore(0, ra0, rb0);
     __syncthreads();
-  }
+    // steps t (even) use LDS buffer 0 and register set 0, odd ones buffer 1
+    // and set 1; a set is reloaded (step t+2) as soon as step t is in LDS.
+    // The loop body has no early exit (an odd last step runs after it), so
+    // the accumulators keep one register assignment throughout.
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      gload(kt + 2, ra0, rb0);
+      compute(0);
+      sstore(1, ra1, rb1);
+      __syncthreads();
+      gload(kt + 3, ra1, rb1);
+      compute(1);
+      if (kt + 2 < nk) sstore(0, ra0, rb0);
+      __syncthreads();
+    }
+    if (kt < nk) compute(0);
+  };
+  if (fast) run(std::false_type{});
+  else run(std::true_type{});
 
   // ---- epilogue: accumulator register r of lane l holds
   //      row 8*(r/4) + 4*(l/32) + (r%4), column l%32 of its 32x32 tile
