@@ -203,10 +203,13 @@ __global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_fwd(AttnGeom g, const
         for (int i = 0; i < 4; ++i) s = mfma(kf[i], qf[kb][i], s);
       }
       if (kb0 + 31 >= g.k_len || g.k_off + kb0 + 31 > wave_qmin) {  // straddles the diagonal or the end
+        // key kl of this block is visible to the lane's query iff kl <= dlim
+        const int dlim = (int)max((int64_t)-1, min((int64_t)32, qpos - g.k_off - kb0));
+        const int klim = g.k_len - kb0;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kb0 + kidx(r, half);
-          if (key >= g.k_len || g.k_off + key > qpos) s[r] = -INFINITY;
+          const int kl = kidx(r, half);
+          s[r] = ((kl < klim) & (kl <= dlim)) ? s[r] : -INFINITY;
         }
       }
       float mloc = s[0];
@@ -410,11 +413,15 @@ __global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_bwd_dq(AttnGeom g, co
         }
       }
       const bool edge = kb0 + 31 >= g.k_len || g.k_off + kb0 + 31 > wave_qmin;
+      // key kl of this block is visible to the lane's query iff kl <= dlim
+      const int dlim = (int)max((int64_t)-1, min((int64_t)32, qpos - g.k_off - kb0));
+      const int klim = g.k_len - kb0;  // keys >= klim are past the tile
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = kb0 + kidx(r, half);
-        const bool ok = qvalid && (!edge || (key < g.k_len && g.k_off + key <= qpos));
-        const float p = ok ? exp2f(s[r] - lse2) : 0.f;
+        const int kl = kidx(r, half);
+        const bool ok = qvalid & (!edge | ((kl < klim) & (kl <= dlim)));
+        const float e = exp2f(s[r] - lse2);  // computed for every entry; masked ones select 0
+        const float p = ok ? e : 0.f;
         s[r] = p * (dp[r] - dq_d);           // dS^T
       }
 #pragma unroll
@@ -457,7 +464,8 @@ __global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_bwd_dkv(AttnGeom g, c
   constexpr int LD = C::LD, NKB = C::NKB, NEB = C::NEB;
   __shared__ __attribute__((aligned(16))) float Qs[2 * kBS * LD];   // Q stage, then dO stage
   __shared__ __attribute__((aligned(16))) float KVs[2 * kBS * LD];  // the workgroup's keys: K (pre-scaled), V
-  __shared__ float Ls[kBS], Dd[kBS];
+  __shared__ __attribute__((aligned(16))) float Ls[kBS];
+  __shared__ __attribute__((aligned(16))) float Dd[kBS];
   float* Ds = Qs + kBS * LD;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -554,11 +562,23 @@ __global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_bwd_dkv(AttnGeom g, c
         }
       }
       const bool edge = qb0 + 31 >= g.q_len || g.q_off + qb0 < wave_kmax;
+      // lse (log2 units) and D of the 16 query rows held by this lane's
+      // registers: rows 8*(r/4) + 4*half + r%4, i.e. four 16-byte reads each
+      f32x4 lv[4], dv[4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {         // P, in place of S
+      for (int g4 = 0; g4 < 4; ++g4) {
+        lv[g4] = *reinterpret_cast<const f32x4*>(lsb + 8 * g4 + 4 * half);
+        dv[g4] = *reinterpret_cast<const f32x4*>(ddb + 8 * g4 + 4 * half);
+      }
+      // query row ql of this block sees the lane's key iff ql >= dlim
+      const int dlim = (int)max((int64_t)-1, min((int64_t)32, kpos - g.q_off - qb0));
+      const int qlim = g.q_len - qb0;  // rows >= qlim are past the tile
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {         // P, in place of S (branch-free: masked entries select 0)
         const int ql = kidx(r, half);
-        const bool ok = kvalid && (!edge || (qb0 + ql < g.q_len && kpos <= g.q_off + qb0 + ql));
-        s[r] = ok ? exp2f(s[r] - lsb[ql]) : 0.f;
+        const bool ok = kvalid & (!edge | ((ql < qlim) & (ql >= dlim)));
+        const float p = exp2f(s[r] - lv[r >> 2][r & 3]);
+        s[r] = ok ? p : 0.f;
       }
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb)
@@ -566,7 +586,7 @@ __global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_bwd_dkv(AttnGeom g, c
         for (int r = 0; r < 16; ++r)
           dkv[NEB + eb] = mfma(dsb[kidx(r, half) * LD + eb * 32 + l32], s[r], dkv[NEB + eb]);  // dV^T += dO^T P
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] *= dp[r] - ddb[kidx(r, half)];  // dS, in place of P
+      for (int r = 0; r < 16; ++r) s[r] *= dp[r] - dv[r >> 2][r & 3];  // dS, in place of P
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll
