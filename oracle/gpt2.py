@@ -26,6 +26,10 @@ Regularization). Readings taken where the pages are silent:
   R8 AdamW: beta1 0.9, beta2 0.999, decoupled decay p *= (1 - lr*wd)
      applied before the moment step, bias correction on, eps outside the
      square root, one parameter group (decay on every parameter).
+  R9 SGD (the review's Adam/SGD update; the README's --optimizer flag
+     picks the optimizer): the plain step p - lr*g, no momentum and no
+     weight decay (the README ties weight decay to AdamW); the same lr
+     schedule.
 
 The arithmetic below is the plain definition of each layer; the only
 library primitive used is numpy's matmul (and exp/log/tanh/sqrt).
@@ -144,6 +148,11 @@ def adamw(p, g, m, v, t: int, lr: float, beta1: float, beta2: float, eps: float,
     return p - lr * mhat / (np.sqrt(vhat) + eps), m, v
 
 
+def sgd(p, g, lr: float):
+    """One plain stochastic-gradient step (R9)."""
+    return p - lr * g
+
+
 # ---------------------------------------------------------------------- model
 
 def _heads(x: np.ndarray, n_head: int) -> np.ndarray:
@@ -258,12 +267,16 @@ def lr_at(t: int, lr: float, start_lr: float, full_lr_iter: int) -> float:
 
 def step(params: Dict[str, np.ndarray], tokens: np.ndarray, n_layer: int, n_head: int,
          lr: float = 3e-4, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
-         wd: float = 0.1, t: int = 1, ln_eps: float = 1e-5, state=None):
-    """One training step: forward, loss, backward, AdamW on every parameter.
+         wd: float = 0.1, t: int = 1, ln_eps: float = 1e-5, state=None, optimizer: str = "adamw"):
+    """One training step: forward, loss, backward, then AdamW (or SGD, R9)
+    on every parameter.
 
     tokens: int [B, T+1] window; inputs are tokens[:, :-1], labels tokens[:, 1:].
-    state: optional dict name -> (m, v); zeros when absent (first step).
+    state: optional dict name -> (m, v); zeros when absent (first step); SGD
+    leaves it as given.
     Returns (loss, grads, new_params, new_state)."""
+    if optimizer not in ("adamw", "sgd"):
+        raise ValueError(f"unknown optimizer {optimizer!r}")
     tok = np.asarray(tokens, np.int64)
     x, y = tok[:, :-1], tok[:, 1:]
     loss, cache = forward(params, x, y, n_layer, n_head, ln_eps)
@@ -271,6 +284,11 @@ def step(params: Dict[str, np.ndarray], tokens: np.ndarray, n_layer: int, n_head
     new_p, new_s = {}, {}
     for name, p in params.items():
         p64 = np.asarray(p, np.float64)
+        if optimizer == "sgd":
+            new_p[name] = sgd(p64, grads[name], lr)
+            if state and name in state:
+                new_s[name] = state[name]
+            continue
         m, v = (state or {}).get(name, (np.zeros_like(p64), np.zeros_like(p64)))
         new_p[name], mm, vv = adamw(p64, grads[name], m, v, t, lr, beta1, beta2, eps, wd)
         new_s[name] = (mm, vv)

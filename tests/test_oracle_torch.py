@@ -73,6 +73,33 @@ def test_adamw_matches_torch_optim_three_steps():
         assert np.abs(p - pt.detach().numpy()).max() <= 1e-15
 
 
+def test_sgd_matches_torch_optim_three_steps():
+    rng = np.random.default_rng(2)
+    p0 = rng.standard_normal(64)
+    gs = [rng.standard_normal(64) * 10 ** rng.uniform(-5, 0) for _ in range(3)]
+    pt = torch.tensor(p0, requires_grad=True)
+    opt = torch.optim.SGD([pt], lr=3e-4, momentum=0.0, weight_decay=0.0, foreach=False)
+    p = p0.copy()
+    for g in gs:
+        pt.grad = torch.tensor(g)
+        opt.step()
+        p = og.sgd(p, g, 3e-4)
+        assert np.abs(p - pt.detach().numpy()).max() <= 1e-15
+
+
+def test_sgd_step_descends_the_loss():
+    # a small enough plain gradient step lowers the loss (first-order
+    # decrease lr*|g|^2 dominates the O(lr^2) term)
+    shape = synth.WORKLOADS["tiny"].shape
+    params = synth.init_params(shape, seed=0)
+    tokens = synth.token_stream(shape, seed=1)
+    loss0, grads, p1, _ = og.step(params, tokens, shape.n_layer, shape.n_head, lr=1e-2, optimizer="sgd")
+    loss1, _ = og.forward(p1, np.asarray(tokens)[:, :-1], np.asarray(tokens)[:, 1:], shape.n_layer, shape.n_head)
+    gnorm2 = sum(float(np.sum(g * g)) for g in grads.values())
+    assert loss1 < loss0
+    assert abs((loss0 - loss1) - 1e-2 * gnorm2) <= 0.05 * 1e-2 * gnorm2
+
+
 def _hf_model(shape, params):
     from transformers import GPT2Config, GPT2LMHeadModel
     cfg = GPT2Config(vocab_size=shape.vocab, n_positions=shape.seq, n_embd=shape.n_embd,
