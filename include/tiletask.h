@@ -247,6 +247,20 @@ int tile_fused_adamw(void* stream, int64_t n, float* p, const float* g, float* m
 int tile_fused_adamw_multi(void* stream, int count, float* const* p, const float* const* g,
                            float* const* m, float* const* v, const int64_t* n, float lr, float beta1,
                            float beta2, float eps, float weight_decay, const float* bias_corr);
+/* tile_sgd -- plain stochastic-gradient step on one tile (the pith.science
+ * review's "What carries the argument" lists Adam and SGD as the tile-wise
+ * updates; the README's --optimizer flag picks one): p[i] -= lr * g[i] for
+ * i < n. p and g are DEVICE arrays (16-byte aligned ones take the float4
+ * path). No momentum, no weight decay. TT_ERR_ARG for n < 0 or a null
+ * pointer with n > 0. */
+int tile_sgd(void* stream, int64_t n, float* p, const float* g, float lr);
+/* tile_sgd_multi -- the same step on `count` tiles (0 <= count <=
+ * TT_SGD_MAX_TILES) in one launch: tile i has n[i] elements at p[i], g[i]
+ * (HOST arrays of DEVICE pointers, read before the call returns); each
+ * element gets exactly tile_sgd's arithmetic. TT_ERR_ARG for a count out of
+ * range, a negative size or a null pointer of a non-empty tile. */
+#define TT_SGD_MAX_TILES 16
+int tile_sgd_multi(void* stream, int count, float* const* p, const float* const* g, const int64_t* n, float lr);
 /* tile_adamw_advance -- device-side step counter: t = ++(*step) and
  * bias_corr = {1 - beta1^t, 1 - beta2^t} (step: device int32, bias_corr: device
  * float[2]). One tiny launch per optimiser step. */
@@ -454,15 +468,20 @@ typedef struct {
 typedef struct {              /* README tile flags; vocab has no flag there */
     int batch, seq, embd, inner, head, vocab;
 } tt_gpt2_tiles;
-/* AdamW settings of the NNTile README's GPT example (fused AdamW, eps,
- * weight decay, lr) plus its warm-up flags: AdamW iteration 1 uses
- * start_lr, iteration full_lr_iter and later ones lr, linearly in between;
- * full_lr_iter <= 1 uses lr throughout. Iterations are counted per
- * tt_gpt2 from its creation. */
+/* Optimiser settings of the NNTile README's GPT example (fused AdamW, eps,
+ * weight decay, lr) plus its warm-up flags: update 1 uses start_lr, update
+ * full_lr_iter and later ones lr, linearly in between; full_lr_iter <= 1
+ * uses lr throughout. Updates are counted per tt_gpt2 from its creation.
+ * optimizer (the README's --optimizer flag): TT_OPT_ADAMW, or TT_OPT_SGD
+ * for the plain step p -= lr*g on every parameter (beta1, beta2, eps and
+ * weight_decay are then unused and the moments are left untouched). */
+#define TT_OPT_ADAMW 0
+#define TT_OPT_SGD 1
 typedef struct {
     float lr, beta1, beta2, eps, weight_decay;
     float start_lr;
     int full_lr_iter;
+    int optimizer;
 } tt_adamw_hparams;
 
 /* Allocates parameters, gradients, AdamW moments (zeroed) and activations

@@ -221,6 +221,30 @@ def test_gpt2_accumulating_step_dag_is_race_free(tmp_path):
         model.close()
 
 
+def test_gpt2_sgd_step_dag(tmp_path):
+    """The SGD update: race free, one sgd task per AdamW task of the AdamW
+    step, no moment or step-counter task; an unknown optimizer is refused."""
+    shape = synth.GPT2Shape(2, 100, 64, 4, 96, 32, 2)
+    tiles = synth.Tiles(1, 16, 32, 48, 2, 40)
+    counts = {}
+    for opt in ("adamw", "sgd"):
+        with Context(L.TT_DEVICE_DRYRUN, n_streams=4, window=100000) as ctx:
+            model = GPT2(ctx, shape, tiles)
+            model.step(None, optimizer=opt)
+            dag = ctx.dump_dag(str(tmp_path / f"dag_{opt}.jsonl"))
+            model.close()
+        _check_races(dag)
+        counts[opt] = {lab: sum(r["label"] == lab for r in dag) for lab in ("adamw", "adam_step", "sgd")}
+    assert counts["sgd"]["sgd"] == counts["adamw"]["adamw"] > 0
+    assert counts["sgd"]["adamw"] == counts["sgd"]["adam_step"] == 0
+    with Context(L.TT_DEVICE_DRYRUN, n_streams=2) as ctx:
+        model = GPT2(ctx, shape, tiles)
+        hp = L.tt_adamw_hparams(3e-4, 0.9, 0.999, 1e-8, 0.1, 3e-4, 1, 7)
+        import ctypes as C
+        assert L.lib.tt_gpt2_step_accum(model.h, None, 1, C.byref(hp), 1) == L.TT_ERR_ARG
+        model.close()
+
+
 def test_gpt2_rejects_bad_tiles():
     shape = synth.GPT2Shape(1, 100, 64, 4, 96, 32, 2)
     with Context(L.TT_DEVICE_DRYRUN) as ctx:

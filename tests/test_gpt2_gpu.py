@@ -194,3 +194,38 @@ def test_lr_warmup_schedule():
         assert np.abs(g - ref).max() <= 2 * sum(lrs) * (1 + 1e-3) + 1e-6 * np.abs(ref).max(), name
         if decided[name].any():
             assert normwise(g[decided[name]], ref[decided[name]]) <= 1e-3, name
+
+
+def test_sgd_steps_match_oracle():
+    """The README's --optimizer choice: plain SGD. The kernel applies exactly
+    p - lr*g to the GPU's own gradients, the moments stay untouched, and two
+    steps follow the oracle's chain (second loss within the loss bar, the
+    parameters within lr times the gradient bar)."""
+    shape = TINY.shape
+    params = synth.init_params(shape, seed=0)
+    tokens = synth.token_stream(shape, seed=1)
+    specs = synth.param_specs(shape)
+    lr = 0.1
+    with Context(0, n_streams=2) as ctx:
+        model = GPT2(ctx, shape, TINY.tiles)
+        model.set_params(params, specs)
+        tok = torch.from_numpy(tokens.astype(np.int32)).cuda()
+        model.step(tok, lr=lr, optimizer="sgd")
+        loss1, g1, p1 = model.loss(), model.get(specs, 1), model.get(specs, 0)
+        m, v = model.get(specs, 2), model.get(specs, 3)
+        model.step(tok, lr=lr, optimizer="sgd")
+        loss2 = model.loss()
+        model.close()
+    rl1, rg1, rp1, _ = og.step(params, tokens, shape.n_layer, shape.n_head, lr=lr, optimizer="sgd")
+    rl2, _, _, _ = og.step(rp1, tokens, shape.n_layer, shape.n_head, lr=lr, optimizer="sgd")
+    assert abs(loss1 - rl1) <= 1e-4 * abs(rl1)
+    assert abs(loss2 - rl2) <= 1e-4 * abs(rl2), (loss2, rl2)
+    assert loss2 < loss1
+    for name, p0 in params.items():
+        p0 = np.asarray(p0, np.float32).astype(np.float64)
+        got = p1[name].astype(np.float64)
+        own = og.sgd(p0, g1[name].astype(np.float64), lr)
+        assert np.abs(got - own).max() <= 2.0 ** -22 * (np.abs(p0).max() + lr * np.abs(g1[name]).max()), name
+        gmax = np.abs(rg1[name]).max()
+        assert np.abs(got - rp1[name]).max() <= lr * 1e-3 * gmax + 2.0 ** -22 * np.abs(p0).max() + 1e-30, name
+        assert not m[name].any() and not v[name].any(), name

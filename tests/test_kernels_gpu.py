@@ -394,6 +394,27 @@ def test_fill_multi():
         tt.tile_fill_multi(None, [buf] * 17, 0.0)
 
 
+def test_sgd_multi_and_single():
+    sizes = [1, 5, 768, 4097, 1 << 17]
+    lr = 0.05
+    ps = [synth.rand_normal((n,), 300 + i) for i, n in enumerate(sizes)]
+    gs = [synth.rand_normal((n,), 400 + i) for i, n in enumerate(sizes)]
+    P, Gr = [dev(x) for x in ps], [dev(x) for x in gs]
+    # an unaligned tile (offset by one float) takes the scalar path
+    pu = torch.from_numpy(np.concatenate([[0.0], ps[3]]).astype(np.float32)).cuda()[1:]
+    gu = torch.from_numpy(np.concatenate([[0.0], gs[3]]).astype(np.float32)).cuda()[1:]
+    tt.tile_sgd_multi(None, P + [pu], Gr + [gu], lr)
+    for x, g, got in zip(ps + [ps[3]], gs + [gs[3]], P + [pu]):
+        ref = og.sgd(x.astype(np.float32).astype(np.float64), g.astype(np.float32).astype(np.float64), lr)
+        bound = 2.0 ** -23 * (np.abs(x) + lr * np.abs(g)) * 2
+        assert (np.abs(host(got) - ref) <= bound + 1e-30).all()
+    one = dev(ps[2])
+    tt.tile_sgd(None, sizes[2], one, Gr[2], lr)
+    assert np.array_equal(host(one), host(P[2]))  # same arithmetic as the multi form
+    with pytest.raises(tt.TTError):
+        tt.tile_sgd_multi(None, [P[0]] * 17, [Gr[0]] * 17, lr)
+
+
 # ----------------------------------------------------- embedding / misc
 
 def test_embedding_fwd_bwd():

@@ -41,6 +41,8 @@ TT_F32, TT_I32 = 0, 1
 TT_HOME_DEVICE, TT_HOME_PINNED_HOST = 0, 1
 TT_DEVICE_DRYRUN = -1
 TT_R, TT_W, TT_RW = 1, 2, 3
+TT_OPT_ADAMW, TT_OPT_SGD = 0, 1
+TT_ADAMW_MAX_TILES = TT_SGD_MAX_TILES = TT_FILL_MAX_TILES = 16
 
 _ERRNAMES = {-1: "TT_ERR_ARG", -2: "TT_ERR_SHAPE", -3: "TT_ERR_OOM", -4: "TT_ERR_HIP", -5: "TT_ERR_STATE",
              -6: "TT_ERR_UNSUPPORTED"}
@@ -79,7 +81,8 @@ class tt_gpt2_tiles(C.Structure):
 
 class tt_adamw_hparams(C.Structure):
     _fields_ = [("lr", C.c_float), ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float),
-                ("weight_decay", C.c_float), ("start_lr", C.c_float), ("full_lr_iter", C.c_int)]
+                ("weight_decay", C.c_float), ("start_lr", C.c_float), ("full_lr_iter", C.c_int),
+                ("optimizer", C.c_int)]
 
 
 P, I, I64, F, SZ = C.c_void_p, C.c_int, C.c_int64, C.c_float, C.c_size_t
@@ -102,6 +105,8 @@ SIGNATURES = {
     "tile_fused_adamw": (I, [P, I64, P, P, P, P, F, F, F, F, F, P]),
     "tile_fused_adamw_multi": (I, [P, I, P, P, P, P, P, F, F, F, F, F, P]),
     "tile_adamw_advance": (I, [P, P, P, F, F]),
+    "tile_sgd": (I, [P, I64, P, P, F]),
+    "tile_sgd_multi": (I, [P, I, P, P, P, F]),
     "tile_embedding_fwd": (I, [P, I64, I64, P, I64, I64, I64, P, I64, P, I64, I64, I64, P, I64]),
     "tile_embedding_index": (I, [P, I64, P, P, P]),
     "tile_embedding_bwd": (I, [P, I, I64, I64, P, P, I64, I64, I64, P, I64, P, I64]),

@@ -530,6 +530,8 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
 
 // learning rate of AdamW iteration t (from 1): start_lr at 1, lr from
 // full_lr_iter on, linear in between (the README's warm-up flags)
+static_assert(TT_SGD_MAX_TILES >= TT_ADAMW_MAX_TILES, "SGD groups are formed with the AdamW group size");
+
 static float lr_at(int64_t t, const tt_adamw_hparams& h) {
   if (h.full_lr_iter <= 1 || t >= h.full_lr_iter) return h.lr;
   return h.start_lr + (h.lr - h.start_lr) * (float)(t - 1) / (float)(h.full_lr_iter - 1);
@@ -550,6 +552,8 @@ extern "C" int tt_gpt2_step_accum(tt_gpt2* g, const int32_t* tokens, int n_micro
   clear_error();
   if (!g || !hp) return fail(TT_ERR_ARG, "tt_gpt2_step: null argument");
   if (n_micro < 1) return fail(TT_ERR_ARG, "tt_gpt2_step_accum: n_micro must be >= 1");
+  if (hp->optimizer != TT_OPT_ADAMW && hp->optimizer != TT_OPT_SGD)
+    return fail(TT_ERR_ARG, "tt_gpt2_step: unknown optimizer");
   tt_ctx* ctx = g->ctx;
   if (!tokens && !ctx->dryrun) return fail(TT_ERR_ARG, "tt_gpt2_step: null tokens");
   tt_adamw_hparams h = *hp;
@@ -858,6 +862,24 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
         grp.push_back(items[k++]);
       }
       std::vector<Access> acc;
+      if (h.optimizer == TT_OPT_SGD) {  // p -= lr g: the moments are not touched
+        for (const Item& it : grp) {
+          acc.push_back(RW(g->P[it.i], it.lt));
+          acc.push_back(R(g->G[it.i], it.lt));
+        }
+        TRY(ctx->submit("sgd", acc, [=](hipStream_t s, void*) {
+          float* pp[TT_SGD_MAX_TILES];
+          const float* gg[TT_SGD_MAX_TILES];
+          int64_t nn[TT_SGD_MAX_TILES];
+          for (size_t j = 0; j < grp.size(); ++j) {
+            pp[j] = F(g->P[grp[j].i], grp[j].lt);
+            gg[j] = F(g->G[grp[j].i], grp[j].lt);
+            nn[j] = grp[j].n;
+          }
+          return tile_sgd_multi(s, (int)grp.size(), pp, gg, nn, h.lr);
+        }));
+        continue;
+      }
       for (const Item& it : grp) {
         acc.push_back(RW(g->P[it.i], it.lt));
         acc.push_back(R(g->G[it.i], it.lt));
@@ -883,7 +905,7 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
     }
     return TT_OK;
   };
-  if (do_update) {
+  if (do_update && h.optimizer == TT_OPT_ADAMW) {
     const float b1 = hp->beta1, b2 = hp->beta2;
     TRY(ctx->submit("adam_step", {RW(stp, 0), W(bc, 0)}, [=](hipStream_t s, void*) {
       return tile_adamw_advance(s, (int32_t*)stp->dev(0), F(bc, 0), b1, b2);

@@ -101,6 +101,31 @@ __global__ __launch_bounds__(256) void adamw_multi(AdamwSet S, int count, float 
   }
 }
 
+// plain SGD: p -= lr * g, several tiles per launch (blockIdx.y = tile)
+constexpr int kSgdMaxTiles = TT_SGD_MAX_TILES;
+struct SgdSet {
+  float* p[kSgdMaxTiles];
+  const float* g[kSgdMaxTiles];
+  int64_t n[kSgdMaxTiles];
+};
+
+__global__ __launch_bounds__(256) void sgd_multi(SgdSet S, int count, float lr) {
+  const int t = blockIdx.y;
+  if (t >= count) return;
+  const int64_t n = S.n[t];
+  float* __restrict__ p = S.p[t];
+  const float* __restrict__ g = S.g[t];
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const bool vec = (n & 3) == 0 && ((reinterpret_cast<uintptr_t>(p) | reinterpret_cast<uintptr_t>(g)) & 15) == 0;
+  if (vec) {
+    f32x4* p4 = reinterpret_cast<f32x4*>(p);
+    const f32x4* g4 = reinterpret_cast<const f32x4*>(g);
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n / 4; i += stride) p4[i] -= lr * g4[i];
+  } else {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) p[i] -= lr * g[i];
+  }
+}
+
 __global__ void adamw_advance_k(int32_t* step, float* bc, float b1, float b2) {
   const int t = ++step[0];
   // 1 - beta^t by repeated multiplication in double (t is small)
@@ -259,6 +284,34 @@ extern "C" int tile_fused_adamw_multi(void* stream, int count, float* const* p, 
   hipLaunchKernelGGL(adamw_multi, dim3(grid_for((most + 3) / 4), count), dim3(256), 0, tt::as_stream(stream), S,
                      count, lr, beta1, beta2, eps, decay, bias_corr);
   return tt::launch_status("tile_fused_adamw_multi");
+}
+
+extern "C" int tile_sgd_multi(void* stream, int count, float* const* p, const float* const* g, const int64_t* n,
+                              float lr) {
+  using tt::fail;
+  if (count < 0 || count > kSgdMaxTiles) return fail(TT_ERR_ARG, "tile_sgd_multi: count out of range");
+  if (count == 0) return TT_OK;
+  if (!p || !g || !n) return fail(TT_ERR_ARG, "tile_sgd_multi: null pointer");
+  SgdSet S{};
+  int64_t most = 0;
+  for (int i = 0; i < count; ++i) {
+    if (n[i] < 0) return fail(TT_ERR_ARG, "tile_sgd_multi: negative size");
+    if (n[i] > 0 && (!p[i] || !g[i])) return fail(TT_ERR_ARG, "tile_sgd_multi: null tile");
+    S.p[i] = p[i];
+    S.g[i] = g[i];
+    S.n[i] = n[i];
+    most = std::max(most, n[i]);
+  }
+  if (most == 0) return TT_OK;
+  hipLaunchKernelGGL(sgd_multi, dim3(grid_for((most + 3) / 4), count), dim3(256), 0, tt::as_stream(stream), S, count,
+                     lr);
+  return tt::launch_status("tile_sgd_multi");
+}
+
+extern "C" int tile_sgd(void* stream, int64_t n, float* p, const float* g, float lr) {
+  if (n < 0) return tt::fail(TT_ERR_ARG, "tile_sgd: negative size");
+  if (n > 0 && (!p || !g)) return tt::fail(TT_ERR_ARG, "tile_sgd: null pointer");
+  return tile_sgd_multi(stream, 1, &p, &g, &n, lr);
 }
 
 extern "C" int tile_adamw_advance(void* stream, int32_t* step, float* bias_corr, float beta1, float beta2) {

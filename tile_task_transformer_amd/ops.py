@@ -15,7 +15,7 @@ from ._lib import (TT_EPI_NONE, check, lib, ptr, stream_handle, TT_EPI_BIAS, TT_
 __all__ = [
     "tile_gemm", "tile_gemm_ws", "tile_gemm_workspace", "tile_layernorm_fwd", "tile_layernorm_bwd", "tile_layernorm_bwd_workspace", "tile_softmax",
     "tile_xentropy", "tile_attention_fwd", "tile_attention_bwd", "tile_fused_adamw", "tile_fused_adamw_multi",
-    "tile_adamw_advance",
+    "tile_adamw_advance", "tile_sgd", "tile_sgd_multi",
     "tile_embedding_fwd", "tile_embedding_index", "tile_embedding_bwd", "tile_reduce_rows",
     "tile_reduce_rows_workspace", "tile_fill", "tile_fill_multi", "tile_split_tokens",
     "TT_EPI_NONE", "TT_EPI_BIAS", "TT_EPI_RES", "TT_EPI_GELU", "TT_EPI_GELU_BWD", "TT_LN_PARTIAL",
@@ -96,6 +96,19 @@ def tile_fused_adamw_multi(stream, ps, gs, ms, vs, lr, beta1, beta2, eps, weight
     ns = (C.c_int64 * max(k, 1))(*[int(x.numel()) for x in ps])
     return check(lib.tile_fused_adamw_multi(stream_handle(stream), k, arr(ps), arr(gs), arr(ms), arr(vs), ns, lr,
                                             beta1, beta2, eps, weight_decay, ptr(bias_corr)))
+
+
+def tile_sgd(stream, n, p, g, lr):
+    return check(lib.tile_sgd(stream_handle(stream), n, ptr(p), ptr(g), lr))
+
+
+def tile_sgd_multi(stream, ps, gs, lr):
+    """Tiles given as lists of equal length (torch tensors or device addresses)."""
+    import ctypes as C
+    k = len(ps)
+    arr = lambda xs: (C.c_void_p * max(k, 1))(*[ptr(x) for x in xs])  # noqa: E731
+    ns = (C.c_int64 * max(k, 1))(*[int(x.numel()) for x in ps])
+    return check(lib.tile_sgd_multi(stream_handle(stream), k, arr(ps), arr(gs), ns, lr))
 
 
 def tile_adamw_advance(stream, step, bias_corr, beta1, beta2):

@@ -194,10 +194,12 @@ class GPT2:
         return {name: self._wrap(i, which, shp).copy_out() for i, (name, shp, _) in enumerate(specs)}
 
     def step(self, tokens_dev, lr=3e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1, update=True,
-             n_micro=1, start_lr=None, full_lr_iter=1):
+             n_micro=1, start_lr=None, full_lr_iter=1, optimizer="adamw"):
         """One optimiser step. tokens_dev: int32 [n_micro * batch, seq + 1] on
         the GPU (n_micro minibatches whose gradients accumulate); warm-up:
-        start_lr at the first update, lr from update full_lr_iter on."""
+        start_lr at the first update, lr from update full_lr_iter on;
+        optimizer "adamw" or "sgd" (plain p -= lr*g)."""
+        opt = {"adamw": L.TT_OPT_ADAMW, "sgd": L.TT_OPT_SGD}[optimizer]
         if hasattr(tokens_dev, "device") and getattr(tokens_dev.device, "type", "") == "cuda":
             # the executor's streams do not order after torch's: they wait (on
             # the device, the host does not block) for the work torch has
@@ -207,7 +209,7 @@ class GPT2:
             for i in range(self.ctx.n_streams):
                 torch.cuda.ExternalStream(self.ctx.stream(i), device=tokens_dev.device).wait_stream(cur)
         hp = L.tt_adamw_hparams(lr, beta1, beta2, eps, weight_decay, lr if start_lr is None else start_lr,
-                                full_lr_iter)
+                                full_lr_iter, opt)
         check(lib.tt_gpt2_step_accum(self.h, L.ptr(tokens_dev), n_micro, C.byref(hp), int(update)))
 
     def loss(self) -> float:
