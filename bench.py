@@ -11,6 +11,7 @@ Prints ONE JSON line:
                on one stream): its algorithmic flops per launch / its
                average launch duration, timed with HIP events on the
                executor stream that launches it, during the timed steps
+               (every 5th launch: an event pair costs ~4 us of queue time)
   classes      every task class's achieved throughput against its roofline
                (MFMA fp32 or HBM), from one extra step run on one stream
                with each task timed, so no kernel shares the GPU
@@ -37,6 +38,7 @@ import synth  # noqa: E402
 
 METRIC = "GPT2 train tokens/sec + TFLOP/s (% fp32 MFMA peak) per fwd+bwd+AdamW step, 1 GPU"
 MFMA_FP32_PEAK = 157.3  # TFLOP/s, MI355X dense fp32 matrix
+PROFILE_EVERY = 5       # timed-region sampling of the dominant class's launches
 HBM_PEAK = 8000.0       # GB/s
 
 
@@ -431,8 +433,11 @@ def main(argv=None):
     mfma_ms = {k: v["ms"] for k, v in classes.items() if v["bound"] == "mfma" and not k.startswith("attn")}
     dominant = max(mfma_ms, key=mfma_ms.get) if mfma_ms else "fc"
 
-    # timed region: K steps back to back, the dominant class bracketed by events
-    ctx.profile(dominant)
+    # timed region: K steps back to back, every PROFILE_EVERY-th task of the
+    # dominant class bracketed by events (an event pair costs ~4 us of queue
+    # time; 5 is prime to the 66 vocab tiles of GPT2-small, so the sample
+    # rotates through every tile, the ragged last one included)
+    ctx.profile(dominant, every=PROFILE_EVERY)
     ctx.reset_stats()
     torch.cuda.synchronize()
     ctx.wait()
@@ -451,7 +456,8 @@ def main(argv=None):
     tok_s = s.batch * s.seq / (elapsed / a.steps)
     tflops = model_flops(s) / (elapsed / a.steps) / 1e12
     launches = prof.get("count", 0)
-    per_launch = work[dominant][1] / (launches / a.steps) if launches else float("nan")
+    per_step = classes[dominant]["launches"] if dominant in classes else launches * PROFILE_EVERY / a.steps
+    per_launch = work[dominant][1] / per_step if launches else float("nan")
     avg_ms = prof["total_ms"] / launches if launches else float("nan")
     achieved = per_launch / (avg_ms * 1e-3) / 1e12
     out = {
@@ -470,7 +476,7 @@ def main(argv=None):
                      "peak": MFMA_FP32_PEAK, "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP32_PEAK, 4),
                      "traffic": traffic_bytes(a.workload, dominant), "flops_per_launch": per_launch,
                      "avg_launch_ms": round(avg_ms, 4),
-                     "launches": launches},
+                     "launches_timed": launches, "launches_per_step": per_step},
     }
     if a.pinned:
         out["residency"] = {k: st[k] / a.steps for k in ("h2d_bytes", "d2h_bytes", "evictions", "prefetches")}

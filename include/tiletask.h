@@ -445,6 +445,11 @@ typedef struct {
 } tt_profile_entry;
 int tt_ctx_profile(tt_ctx* ctx, const char* label_filter);
 int tt_profile_read(tt_ctx* ctx, tt_profile_entry* out, int max_entries, int* n_entries);
+/* Time only every `every`-th matching task (1 = all, the default): each
+ * event pair costs a few microseconds of queue time, so a timed region
+ * samples. Counting restarts at every tt_ctx_profile call. TT_ERR_ARG for
+ * every < 1. */
+int tt_ctx_profile_every(tt_ctx* ctx, int every);
 
 typedef struct {
     int64_t tasks;            /* tasks submitted since creation / reset     */

@@ -137,6 +137,7 @@ SIGNATURES = {
     "tt_get_stats": (I, [P, C.POINTER(tt_stats)]),
     "tt_ctx_profile": (I, [P, C.c_char_p]),
     "tt_profile_read": (I, [P, C.POINTER(tt_profile_entry), I, C.POINTER(I)]),
+    "tt_ctx_profile_every": (I, [P, I]),
     "tt_reset_stats": (I, [P]),
     "tt_gpt2_create": (I, [P, C.POINTER(tt_gpt2_config), C.POINTER(tt_gpt2_tiles), I, PP]),
     "tt_gpt2_destroy": (I, [P]),

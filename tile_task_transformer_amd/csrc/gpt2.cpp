@@ -636,6 +636,12 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
       }));
     }
 
+  // The inputs' tasks go to the GPU now, so it starts on this step while the
+  // host infers the dependencies of the rest (with a large window it would
+  // otherwise wait for the whole step's submission). Not with pinned homes:
+  // there the residency plan wants the whole step in one window.
+  if (g->param_home != TT_HOME_PINNED_HOST) TRY(ctx->flush());
+
   // ---- embedding forward
   tt_tensor* h0 = c.n_layer ? g->blk[0].h_in : g->h_last;
   for (int64_t bi = 0; bi < g->nb; ++bi)

@@ -293,12 +293,15 @@ int tt_ctx::flush() {
     li.seq = ++stream_seq[s];
     if (!dryrun && !latched) {
       int rc = make_resident(task, streams[s]);
-      const bool prof = prof_on && (prof_filter == "*" || prof_filter == task.label);
+      const bool prof = prof_on && (prof_filter == "*" || prof_filter == task.label) && prof_seen++ % prof_every == 0;
       if (prof && rc == TT_OK) {
         for (int k = 0; k < 2; ++k)
           if (prof_used + k >= (int)prof_events.size()) {
+            // timing events only order against this device's own work: no
+            // system-scope fence (with it every record drains the caches and
+            // stalls the queue a few microseconds)
             hipEvent_t e;
-            TT_HIP_TRY(hipEventCreate(&e));
+            TT_HIP_TRY(hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
             prof_events.push_back(e);
           }
         prof_pending.push_back({task.label, prof_used, prof_used + 1});
@@ -885,6 +888,13 @@ int tt_ctx_profile(tt_ctx* c, const char* label_filter) {
   if (int rc = c->flush()) return rc;
   c->prof_on = label_filter != nullptr;
   c->prof_filter = label_filter ? label_filter : "";
+  c->prof_seen = 0;
+  return TT_OK;
+}
+
+int tt_ctx_profile_every(tt_ctx* c, int every) {
+  if (!c || every < 1) return fail(TT_ERR_ARG, "tt_ctx_profile_every: bad argument");
+  c->prof_every = every;
   return TT_OK;
 }
 

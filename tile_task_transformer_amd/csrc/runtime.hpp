@@ -191,6 +191,8 @@ struct tt_ctx {
   // per-task GPU timing (tt_ctx_profile): event pairs around matching launches
   bool prof_on = false;
   std::string prof_filter;             // "*" = every task
+  int prof_every = 1;                  // time every n-th matching task
+  int64_t prof_seen = 0;               // matching tasks since tt_ctx_profile
   struct ProfRec {
     std::string label;
     int ev0, ev1;

@@ -94,8 +94,10 @@ class Context:
     def reset_stats(self):
         check(lib.tt_reset_stats(self.h))
 
-    def profile(self, label_filter):
-        """Time tasks with this label ("*" = all, None = off) with event pairs."""
+    def profile(self, label_filter, every: int = 1):
+        """Time tasks with this label ("*" = all, None = off) with event
+        pairs; every > 1 times only each every-th matching task."""
+        check(lib.tt_ctx_profile_every(self.h, every))
         check(lib.tt_ctx_profile(self.h, None if label_filter is None else label_filter.encode()))
 
     def profile_take(self) -> Dict[str, dict]:
