@@ -70,6 +70,45 @@ def test_gemm_split_k_workspace(ta, tb, m, n, k):
     assert torch.equal(outs[0], outs[1])
 
 
+@pytest.mark.parametrize("m,n,ks,beta", [
+    (4096, 768, [768] * 5 + [337], 0.0),          # the LM head's dnf: full vocab tiles + the ragged last one
+    (256, 192, [64, 96, 32, 0, 128], 0.5),        # a skipped empty pair, C kept with beta
+    (128, 128, [32] * 100, 1.0),                  # more pairs than one launch takes
+    (2048, 4096, [48, 64], 0.0),                  # the 128x128 plan (>= 512 blocks)
+    (100, 72, [40, 33], 0.25),                    # m, n off the block grid: every pair falls back
+])
+def test_gemm_ksum(m, n, ks, beta):
+    """C = alpha sum_t A_t B_t + beta C against the fp64 sum (fp32 bound over
+    the total K), bitwise equal across runs."""
+    seed = m + n + len(ks)
+    As = [synth.rand_normal((m, k), seed + 2 * i) for i, k in enumerate(ks)]
+    Bs = [synth.rand_normal((k, n), seed + 2 * i + 1) for i, k in enumerate(ks)]
+    c0 = synth.rand_normal((m, n), seed + 999)
+    dA, dB = [dev(a) for a in As], [dev(b) for b in Bs]
+    outs = []
+    for _ in range(2):
+        C = dev(c0)
+        tt.tile_gemm_ksum(None, m, n, ks, 0.75, dA, ks, dB, [n] * len(ks), beta, C, n)
+        outs.append(C)
+    ref = beta * c0.astype(np.float64)
+    bound = np.zeros((m, n))
+    for a, b in zip(As, Bs):
+        ref = ref + 0.75 * (a.astype(np.float64) @ b.astype(np.float64))
+        bound += 0.75 * (np.abs(a).astype(np.float64) @ np.abs(b).astype(np.float64))
+    bound *= (sum(ks) + len(ks) + 2) * EPS32
+    assert_close_bound(host(outs[0]), ref, bound + 4 * EPS32 * np.abs(ref) + 1e-30, f"ksum {m}x{n} {len(ks)} pairs")
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_gemm_ksum_empty_and_errors():
+    c0 = synth.rand_normal((64, 64), 5)
+    C = dev(c0)
+    tt.tile_gemm_ksum(None, 64, 64, [], 1.0, [], [], [], [], 0.5, C, 64)
+    assert np.array_equal(host(C), (0.5 * c0.astype(np.float32)).astype(np.float64))
+    with pytest.raises(tt.TTError):
+        tt.tile_gemm_ksum(None, 64, 64, [32], 1.0, [None], [32], [C], [64], 0.0, C, 64)
+
+
 @pytest.mark.parametrize("ld_pad", [0, 1, 4])
 def test_gemm_leading_dims_and_views(ld_pad):
     m, n, k = 96, 72, 40

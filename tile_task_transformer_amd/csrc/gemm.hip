@@ -532,6 +532,184 @@ int launch_t(GemmArgs g, bool va, bool vb, size_t ws_bytes, hipStream_t s) {
   return tt::launch_status("tile_gemm");
 }
 
+
+// ---- K-sum: C = alpha * sum_t A_t B_t + beta * C (both operands in HBM
+// orientation: A_t [m][k_t], B_t [k_t][n]) in one launch over a list of
+// tile pairs that share m, n and the leading dimensions, every k_t a
+// multiple of BK and every load 16-byte aligned and in range. The LM head's
+// input gradient is such a sum, one product per vocab tile; one launch
+// replaces a chain of accumulating GEMMs (each of which reads and writes C)
+// by one long K loop. Same main loop as gemm_kernel's fast path; the sum
+// runs over the pairs in list order.
+constexpr int kKsumMax = 96;  // pairs per launch (kernel arguments stay under 4 KB)
+struct KsumPair {
+  const float* A;
+  const float* B;
+  int64_t steps;  // k_t / BK
+};
+struct KsumArgs {
+  int m, n, nk;  // nk = total K steps over the pairs
+  float alpha, beta;
+  float* C;
+  int64_t lda, ldb, ldc;
+  KsumPair t[kKsumMax];
+};
+
+template <int BM, int BN, int BK>
+__global__ __launch_bounds__(256, 2) void gemm_ksum_kernel(KsumArgs P) {
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int FM = WM / 32, FN = WN / 32;
+  constexpr int A_LD = BK + 4, B_LD = BN + 8;  // A K-contiguous, B row-contiguous
+  constexpr int A_SZ = BM * A_LD, B_SZ = BK * B_LD;
+  constexpr int A_PT = BM * BK / 4 / 256, B_PT = BN * BK / 4 / 256;
+  static_assert(A_PT * 256 * 4 == BM * BK && B_PT * 256 * 4 == BN * BK, "tile must split evenly over 256 threads");
+  __shared__ __attribute__((aligned(16))) float lds[2 * (A_SZ + B_SZ)];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int half = lane >> 5, l32 = lane & 31;
+
+  // block -> C tile: XCD-contiguous, then grouped along M (as gemm_kernel)
+  const int grid_m = P.m / BM, grid_n = P.n / BN;
+  const int nb = grid_m * grid_n;
+  int b = blockIdx.x;
+  {
+    const int per = nb / 8, rem = nb % 8, x = b % 8;
+    b = x * per + min(x, rem) + b / 8;
+  }
+  constexpr int GROUP = 8;
+  const int in_group = GROUP * grid_n;
+  const int first_m = (b / in_group) * GROUP;
+  const int gsz = min(grid_m - first_m, GROUP);
+  const int tm = first_m + (b % in_group) % gsz;
+  const int tn = (b % in_group) / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nk = P.nk;
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  int oa[A_PT], ob[B_PT];
+#pragma unroll
+  for (int i = 0; i < A_PT; ++i) {
+    int r, c;
+    kc_index<BK>(tid + 256 * i, &r, &c);
+    oa[i] = r * (int)P.lda + c;
+  }
+#pragma unroll
+  for (int i = 0; i < B_PT; ++i) {
+    const int idx = tid + 256 * i;
+    ob[i] = (idx / (BN / 4)) * (int)P.ldb + (idx % (BN / 4)) * 4;
+  }
+  // step -> pair: the steps are requested in non-decreasing order, so a
+  // cursor walks the list (uniform, scalar)
+  int cur = 0;
+  int64_t before = 0;
+  f32x4 ra0[A_PT], rb0[B_PT], ra1[A_PT], rb1[B_PT];
+  auto gload = [&](int st, f32x4(&ra)[A_PT], f32x4(&rb)[B_PT]) {
+    st = min(st, nk - 1);
+    while (st >= before + P.t[cur].steps) before += P.t[cur++].steps;
+    const int k0 = (int)(st - before) * BK;
+    const float* pa = P.t[cur].A + (int64_t)m0 * P.lda + k0;
+    const float* pb = P.t[cur].B + (int64_t)k0 * P.ldb + n0;
+#pragma unroll
+    for (int i = 0; i < A_PT; ++i) ra[i] = *reinterpret_cast<const f32x4*>(pa + oa[i]);
+#pragma unroll
+    for (int i = 0; i < B_PT; ++i) rb[i] = *reinterpret_cast<const f32x4*>(pb + ob[i]);
+  };
+  auto sstore = [&](int buf, const f32x4(&ra)[A_PT], const f32x4(&rb)[B_PT]) {
+    float* As = lds + buf * (A_SZ + B_SZ);
+    float* Bs = As + A_SZ;
+#pragma unroll
+    for (int i = 0; i < A_PT; ++i) {
+      int r, c;
+      kc_index<BK>(tid + 256 * i, &r, &c);
+      *reinterpret_cast<f32x4*>(As + r * A_LD + c) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < B_PT; ++i) {
+      const int idx = tid + 256 * i;
+      *reinterpret_cast<f32x4*>(Bs + (idx / (BN / 4)) * B_LD + (idx % (BN / 4)) * 4) = rb[i];
+    }
+  };
+  auto frag = [&](int buf, int kb, f32x4(&fa)[FM], f32x4(&fb)[FN]) {
+    const float* As = lds + buf * (A_SZ + B_SZ);
+    const float* Bs = As + A_SZ;
+    const int kk = kb * 8 + half * 4;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[i] = *reinterpret_cast<const f32x4*>(As + (wm * WM + i * 32 + l32) * A_LD + kk);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = wn * WN + j * 32 + l32;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) fb[j][q] = Bs[(kk + q) * B_LD + col];
+    }
+  };
+  auto mfmas = [&](const f32x4(&fa)[FM], const f32x4(&fb)[FN]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][q], fb[j][q], acc[i][j], 0, 0, 0);
+  };
+  auto compute = [&](int buf) {
+    f32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+    frag(buf, 0, fa0, fb0);
+#pragma unroll
+    for (int kb = 0; kb < BK / 8; ++kb) {
+      if (kb + 1 < BK / 8) {
+        if (kb & 1) frag(buf, kb + 1, fa0, fb0);
+        else frag(buf, kb + 1, fa1, fb1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (kb & 1) mfmas(fa1, fb1);
+      else mfmas(fa0, fb0);
+    }
+  };
+
+  if (nk > 0) {
+    gload(0, ra0, rb0);
+    gload(1, ra1, rb1);
+    sstore(0, ra0, rb0);
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      gload(kt + 2, ra0, rb0);
+      compute(0);
+      sstore(1, ra1, rb1);
+      __syncthreads();
+      gload(kt + 3, ra1, rb1);
+      compute(1);
+      if (kt + 2 < nk) sstore(0, ra0, rb0);
+      __syncthreads();
+    }
+    if (kt < nk) compute(0);
+  }
+
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = n0 + wn * WN + j * 32 + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        float* c = P.C + (int64_t)row * P.ldc + col;
+        float v = P.alpha * acc[i][j][r];
+        if (P.beta != 0.f) v += P.beta * *c;
+        *c = v;
+      }
+    }
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 }  // namespace
@@ -580,4 +758,77 @@ extern "C" int tile_gemm(void* stream, int transA, int transB, int64_t m, int64_
                          int epilogue, const float* bias, const float* res, int64_t ldr, float* aux, int64_t ldaux) {
   return tile_gemm_ws(stream, transA, transB, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, epilogue, bias, res, ldr,
                       aux, ldaux, nullptr, 0);
+}
+
+extern "C" int tile_gemm_ksum(void* stream, int count, int64_t m, int64_t n, const int64_t* k, float alpha,
+                              const float* const* A, const int64_t* lda, const float* const* B, const int64_t* ldb,
+                              float beta, float* C, int64_t ldc) {
+  using tt::fail;
+  if (count < 0 || m < 0 || n < 0) return fail(TT_ERR_ARG, "tile_gemm_ksum: negative count or size");
+  if (m == 0 || n == 0) return TT_OK;
+  if (m > INT32_MAX || n > INT32_MAX) return fail(TT_ERR_ARG, "tile_gemm_ksum: size exceeds int32");
+  if (!C || ldc < n) return fail(TT_ERR_ARG, "tile_gemm_ksum: bad C");
+  if (count > 0 && (!k || !A || !lda || !B || !ldb)) return fail(TT_ERR_ARG, "tile_gemm_ksum: null array");
+  for (int t = 0; t < count; ++t) {
+    if (k[t] < 0 || k[t] > INT32_MAX) return fail(TT_ERR_ARG, "tile_gemm_ksum: bad k of pair %d", t);
+    if (k[t] > 0 && (!A[t] || !B[t] || lda[t] < k[t] || ldb[t] < n))
+      return fail(TT_ERR_ARG, "tile_gemm_ksum: bad operand of pair %d", t);
+  }
+  hipStream_t s = tt::as_stream(stream);
+  // the plan tile_gemm would pick for one pair (no split): 128x128x16 blocks
+  // when there are >= 512 of them, else 64x64x32
+  const bool big = (m / 128) * (n / 128) >= 512;
+  const int bm = big ? 128 : 64, bn = big ? 128 : 64, bk = big ? 16 : 32;
+  auto fits = [&](int t) {  // a pair the branch-free long-K launch can take
+    return k[t] % bk == 0 && m % bm == 0 && n % bn == 0 && aligned16(A[t]) && aligned16(B[t]) && lda[t] % 4 == 0 &&
+           ldb[t] % 4 == 0 && (int64_t)bm * lda[t] < INT32_MAX && (int64_t)bk * ldb[t] < INT32_MAX;
+  };
+  float b = beta;  // C's own weight: beta in the first contribution, 1 afterwards
+  bool wrote = false;
+  int t = 0;
+  while (t < count) {
+    if (k[t] == 0) {
+      ++t;
+      continue;
+    }
+    if (!fits(t)) {  // on its own, through the general kernel
+      if (int rc = tile_gemm(stream, 0, 0, m, n, k[t], alpha, A[t], lda[t], B[t], ldb[t], b, C, ldc, TT_EPI_NONE,
+                             nullptr, nullptr, 0, nullptr, 0))
+        return rc;
+      b = 1.f;
+      wrote = true;
+      ++t;
+      continue;
+    }
+    KsumArgs P{};
+    P.m = (int)m;
+    P.n = (int)n;
+    P.alpha = alpha;
+    P.beta = b;
+    P.C = C;
+    P.lda = lda[t];
+    P.ldb = ldb[t];
+    P.ldc = ldc;
+    int c = 0;
+    int64_t steps = 0;
+    while (t < count && c < kKsumMax && (k[t] == 0 || (fits(t) && lda[t] == P.lda && ldb[t] == P.ldb))) {
+      if (k[t] > 0) {
+        P.t[c++] = {A[t], B[t], k[t] / bk};
+        steps += k[t] / bk;
+      }
+      ++t;
+    }
+    if (steps > INT32_MAX) return fail(TT_ERR_ARG, "tile_gemm_ksum: K too long");
+    P.nk = (int)steps;
+    const dim3 grid((unsigned)((m / bm) * (n / bn)));
+    if (big) hipLaunchKernelGGL((gemm_ksum_kernel<128, 128, 16>), grid, dim3(256), 0, s, P);
+    else hipLaunchKernelGGL((gemm_ksum_kernel<64, 64, 32>), grid, dim3(256), 0, s, P);
+    if (int rc = tt::launch_status("tile_gemm_ksum")) return rc;
+    b = 1.f;
+    wrote = true;
+  }
+  if (!wrote)  // no product at all: C = beta * C
+    return tile_gemm(stream, 0, 0, m, n, 0, alpha, nullptr, 1, nullptr, n, beta, C, ldc, TT_EPI_NONE, nullptr, nullptr,
+                     0, nullptr, 0);
+  return TT_OK;
 }

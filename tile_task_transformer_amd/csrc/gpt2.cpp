@@ -934,17 +934,47 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
           q.beta = (ti > 0 || later_mb) ? 1.f : 0.f;
           TRY(submit_gemm(ctx, "head_dw", q));
         }
-      // dnf = sum over vocab tiles of dz wte
-      for (int64_t si = 0; si < g->ns; ++si)
-        for (int64_t bi = 0; bi < g->nb; ++bi) {
-          Gemm q;
-          q.A = {g->z, L(g->z, {bi, si, vj})};
-          q.B = {wte, L(wte, {vj, ek})};
-          q.C = {g->dnf, L(g->dnf, {bi, si, ek})};
-          q.beta = vj > 0 ? 1.f : 0.f;
-          TRY(submit_gemm(ctx, "head_dx", q));
-        }
     }
+  // dnf = sum over vocab tiles of dz wte: one task per (token tile, embd
+  // tile), one long-K product over every vocab tile (tile_gemm_ksum), instead
+  // of a chain of accumulating GEMMs that each read and write dnf
+  for (int64_t si = 0; si < g->ns; ++si)
+    for (int64_t bi = 0; bi < g->nb; ++bi)
+      for (int64_t ek = 0; ek < NE; ++ek) {
+        tt_tensor *z = g->z, *dnf = g->dnf;
+        const int64_t ld = L(dnf, {bi, si, ek});
+        std::vector<Access> acc;
+        for (int64_t vj = 0; vj < NV; ++vj) {
+          acc.push_back(R(z, L(z, {bi, si, vj})));
+          acc.push_back(R(wte, L(wte, {vj, ek})));
+        }
+        acc.push_back(W(dnf, ld));
+        int64_t dr, dc;
+        dnf->mat(ld, &dr, &dc);
+        double flops = 0;
+        for (int64_t vj = 0; vj < NV; ++vj) {
+          int64_t zr, zc;
+          z->mat(L(z, {bi, si, vj}), &zr, &zc);
+          flops += 2.0 * dr * dc * zc;
+        }
+        TRY(ctx->submit("head_dx", std::move(acc), [=](hipStream_t s, void*) {
+          std::vector<const float*> As(NV), Bs(NV);
+          std::vector<int64_t> ks(NV), ldas(NV), ldbs(NV);
+          for (int64_t vj = 0; vj < NV; ++vj) {
+            const int64_t lz = L(z, {bi, si, vj}), lw = L(wte, {vj, ek});
+            int64_t zr, zc, wr, wc;
+            z->mat(lz, &zr, &zc);
+            wte->mat(lw, &wr, &wc);
+            As[vj] = F(z, lz);
+            Bs[vj] = F(wte, lw);
+            ks[vj] = zc;
+            ldas[vj] = zc;
+            ldbs[vj] = wc;
+          }
+          return tile_gemm_ksum(s, (int)NV, dr, dc, ks.data(), 1.f, As.data(), ldas.data(), Bs.data(), ldbs.data(),
+                                0.f, F(dnf, ld), dc);
+        }, flops));
+      }
   // zero the LayerNorm and position gradients, which accumulate (over
   // token tiles, and over minibatches after the first)
   if (!later_mb) {

@@ -13,7 +13,7 @@ from ._lib import (TT_EPI_NONE, check, lib, ptr, stream_handle, TT_EPI_BIAS, TT_
                    TT_EMB_POS)
 
 __all__ = [
-    "tile_gemm", "tile_gemm_ws", "tile_gemm_workspace", "tile_layernorm_fwd", "tile_layernorm_bwd", "tile_layernorm_bwd_workspace", "tile_softmax",
+    "tile_gemm", "tile_gemm_ws", "tile_gemm_workspace", "tile_gemm_ksum", "tile_layernorm_fwd", "tile_layernorm_bwd", "tile_layernorm_bwd_workspace", "tile_softmax",
     "tile_xentropy", "tile_attention_fwd", "tile_attention_bwd", "tile_fused_adamw", "tile_fused_adamw_multi",
     "tile_adamw_advance", "tile_sgd", "tile_sgd_multi",
     "tile_embedding_fwd", "tile_embedding_index", "tile_embedding_bwd", "tile_reduce_rows",
@@ -39,6 +39,16 @@ def tile_gemm_ws(stream, transA, transB, m, n, k, alpha, A, lda, B, ldb, beta, C
 
 def tile_gemm_workspace(m, n, k):
     return lib.tile_gemm_workspace(m, n, k)
+
+
+def tile_gemm_ksum(stream, m, n, ks, alpha, As, ldas, Bs, ldbs, beta, C, ldc):
+    """C = alpha * sum_t A_t B_t + beta * C; pairs given as equal-length lists."""
+    import ctypes as C_
+    cnt = len(As)
+    i64 = lambda xs: (C_.c_int64 * max(cnt, 1))(*[int(x) for x in xs])  # noqa: E731
+    ptrs = lambda xs: (C_.c_void_p * max(cnt, 1))(*[ptr(x) for x in xs])  # noqa: E731
+    return check(lib.tile_gemm_ksum(stream_handle(stream), cnt, m, n, i64(ks), alpha, ptrs(As), i64(ldas), ptrs(Bs),
+                                    i64(ldbs), beta, ptr(C), ldc))
 
 
 def tile_layernorm_fwd(stream, phase, rows, cols, x, ldx, gamma, beta, parts, n_parts, part_stride, stats, y,
