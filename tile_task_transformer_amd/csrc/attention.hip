@@ -26,6 +26,12 @@
 // gradient partials by addition), so the result does not depend on timing.
 // Splitting the rows halves the longest wave of a causal tile (the last
 // query block sees every key), which bounds the kernel's critical path.
+// The grid is (b, h) pairs along x and blocks along y, so the hardware
+// dispatches the heaviest block of every (b, h) before any lighter one
+// (longest-first list scheduling over the whole launch), and, when the
+// pair count is a multiple of 8, every block of one (b, h) lands on the
+// same XCD (workgroups go to the XCDs round-robin), so its K and V stay in
+// that XCD's L2.
 // The next stage's global loads are in flight (in registers) while the
 // current stage's MFMAs run -- except in the dK/dV kernel, which keeps its
 // keys in LDS and issues the loads after the MFMAs: that frees the
@@ -134,8 +140,8 @@ __global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_fwd(AttnGeom g, const
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = wave & 1, part = wave >> 1;
   const int half = lane >> 5, l32 = lane & 31;
-  const int qblk = gridDim.x - 1 - blockIdx.x;  // heavy (late) query blocks first
-  const int bh = blockIdx.y, b = bh / g.heads, h = bh % g.heads;
+  const int qblk = gridDim.y - 1 - blockIdx.y;  // heavy (late) query blocks first, over all (b, h)
+  const int bh = blockIdx.x, b = bh / g.heads, h = bh % g.heads;
   const int q0 = qblk * kBQ + grp * 32;
   const int q = q0 + l32;
   const bool qvalid = q < g.q_len;
@@ -343,8 +349,8 @@ __global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_bwd_dq(AttnGeom g, co
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = wave & 1, part = wave >> 1;
   const int half = lane >> 5, l32 = lane & 31;
-  const int qblk = gridDim.x - 1 - blockIdx.x;
-  const int bh = blockIdx.y, b = bh / g.heads, h = bh % g.heads;
+  const int qblk = gridDim.y - 1 - blockIdx.y;
+  const int bh = blockIdx.x, b = bh / g.heads, h = bh % g.heads;
   const int q0 = qblk * kBQ + grp * 32;
   const int q = q0 + l32;
   const bool qvalid = q < g.q_len;
@@ -471,8 +477,8 @@ __global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_bwd_dkv(AttnGeom g, c
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = wave & 1, part = wave >> 1;
   const int half = lane >> 5, l32 = lane & 31;
-  const int kblk = blockIdx.x;   // early keys see the most queries: launched first
-  const int bh = blockIdx.y, b = bh / g.heads, h = bh % g.heads;
+  const int kblk = blockIdx.y;   // early keys see the most queries: launched first
+  const int bh = blockIdx.x, b = bh / g.heads, h = bh % g.heads;
   const int k0w = kblk * kBQ + grp * 32;
   const int key = k0w + l32;
   const bool kvalid = key < g.k_len;
@@ -631,7 +637,8 @@ int check_geom(const char* who, int64_t batch, int64_t heads, int64_t q_len, int
   if (batch < 0 || heads < 0 || q_len < 0 || k_len < 0) return tt::fail(TT_ERR_ARG, "%s: negative size", who);
   if (hd != 16 && hd != 32 && hd != 64 && hd != 128)
     return tt::fail(TT_ERR_UNSUPPORTED, "%s: head dim %lld not in {16, 32, 64, 128}", who, (long long)hd);
-  if (batch * heads > 65535 || q_len > INT32_MAX || k_len > INT32_MAX)
+  // grid: x = (batch, head) pairs, y = 64-row blocks of the query (key) axis
+  if (batch * heads > INT32_MAX || (q_len + kBQ - 1) / kBQ > 65535 || (k_len + kBQ - 1) / kBQ > 65535)
     return tt::fail(TT_ERR_SHAPE, "%s: grid too large", who);
   return TT_OK;
 }
@@ -648,7 +655,7 @@ extern "C" int tile_attention_fwd(void* stream, int64_t batch, int64_t heads, in
   if (!aligned16(Q) || !aligned16(O) || (k_len > 0 && (!aligned16(K) || !aligned16(V))))
     return tt::fail(TT_ERR_ARG, "tile_attention_fwd: tensors must be 16-byte aligned");
   AttnGeom g{(int)batch, (int)heads, (int)q_len, (int)k_len, q_off, k_off, scale};
-  dim3 grid((unsigned)((q_len + kBQ - 1) / kBQ), (unsigned)(batch * heads)), block(kNT);
+  dim3 grid((unsigned)(batch * heads), (unsigned)((q_len + kBQ - 1) / kBQ)), block(kNT);
   hipStream_t s = tt::as_stream(stream);
   switch (hd) {
     case 16: hipLaunchKernelGGL(attn_fwd<16>, grid, block, 0, s, g, Q, K, V, O, ml, lse, first, last); break;
@@ -683,8 +690,8 @@ extern "C" int tile_attention_bwd(void* stream, int phase, int64_t batch, int64_
                         (const void*)dK, (const void*)dV})
     if (!aligned16(p)) return tt::fail(TT_ERR_ARG, "tile_attention_bwd: 16-byte alignment required");
   AttnGeom g{(int)batch, (int)heads, (int)q_len, (int)k_len, q_off, k_off, scale};
-  dim3 gq((unsigned)((q_len + kBQ - 1) / kBQ), (unsigned)(batch * heads));
-  dim3 gk((unsigned)((k_len + kBQ - 1) / kBQ), (unsigned)(batch * heads));
+  dim3 gq((unsigned)(batch * heads), (unsigned)((q_len + kBQ - 1) / kBQ));
+  dim3 gk((unsigned)(batch * heads), (unsigned)((k_len + kBQ - 1) / kBQ));
   dim3 block(kNT);
 #define TT_ATT_BWD(HD)                                                                                   \
   hipLaunchKernelGGL(attn_bwd_dq<HD>, gq, block, 0, s, g, Q, K, V, dO, lse, Dvec, dQ, acc_dq);          \
