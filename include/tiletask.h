@@ -117,6 +117,24 @@ size_t tile_gemm_workspace(int64_t m, int64_t n, int64_t k);
 int tile_gemm_ksum(void* stream, int count, int64_t m, int64_t n, const int64_t* k, float alpha,
                    const float* const* A, const int64_t* lda, const float* const* B, const int64_t* ldb,
                    float beta, float* C, int64_t ldc);
+/* tile_gemm_batch -- independent products of one shape in one launch:
+ *   C_t = alpha * op(A_t) op(B_t) + beta * C_t,   t < count
+ * op() as in tile_gemm; every product shares transA, transB, m, n, k, lda,
+ * ldb and ldc. The tied LM head runs one such product per vocab tile
+ * (forward z_v = n wte_v^T and weight gradient dwte_v = dz_v^T n; tiled
+ * linear layer, pith.science review, "What carries the argument"); the
+ * batch fills the GPU where each product alone would not. A, B, C are HOST
+ * arrays of `count` DEVICE pointers (read before the call returns); C_t
+ * must not overlap C_u (u != t) or any A_u, B_u. Arbitrary (ragged) m, n,
+ * k; with leading dimensions that are multiples of 4 and 16-byte aligned
+ * operands the loads are 16-byte vectors. No epilogue, no split-K. When
+ * beta == 0, C_t is not read. Up to 96 products per launch (more make
+ * several launches). Deterministic. count = 0 (or m, n = 0) does nothing;
+ * TT_ERR_ARG for negative sizes, a null array or operand, or a leading
+ * dimension below its row length. */
+int tile_gemm_batch(void* stream, int count, int transA, int transB, int64_t m, int64_t n, int64_t k,
+                    float alpha, const float* const* A, int64_t lda, const float* const* B, int64_t ldb,
+                    float beta, float* const* C, int64_t ldc);
 
 /* tile_layernorm_fwd -- layer norm over the embedding axis, split into
  * feature tiles (layer list: pith.science review, "What carries the
@@ -202,6 +220,29 @@ int tile_softmax(void* stream, int phase, int64_t rows, int64_t cols,
 int tile_xentropy(void* stream, int phase, int64_t rows, int64_t v_len, int64_t v_off,
                   const int32_t* labels, float* logits, int64_t ldz, const float* lse,
                   const float* row_loss, float* loss, int accumulate, float inv_n);
+/* tile_xentropy_multi -- the cross-entropy sweeps over several vocab tiles
+ * of one token tile in one launch (the LM head's logits, one tile per vocab
+ * tile; NNTile README, "Minimal working GPT example": mean loss over the
+ * batch's tokens). Alone, each tile is a few microseconds of HBM traffic,
+ * too little to fill the GPU.
+ *   TT_XE_STATS parts[t*part_stride + r*3 + {0,1,2}] = (row max, sum of
+ *               exp(z - max), z[r][labels[r] - v_off[t]] when that column is
+ *               in tile t else 0): tile_softmax(TT_SM_STATS) of each tile,
+ *               ready for TT_SM_MERGE
+ *   TT_XE_GRAD  each tile replaced in place by (softmax - onehot(labels)) *
+ *               inv_n, given lse from TT_SM_MERGE: tile_xentropy(TT_XE_GRAD)
+ *               of each tile
+ * Tile t is rows x v_len[t] floats at logits[t] with leading dimension
+ * ldz[t] and vocab offset v_off[t]; v_len, v_off, logits, ldz are HOST
+ * arrays of `count` entries (device pointers in logits, read before the
+ * call returns). v_len[t] in [1, 2048], rows <= 65535, up to 64 tiles per
+ * launch (more make several launches). Same results as the per-tile calls.
+ * TT_ERR_ARG / TT_ERR_SHAPE for bad arguments. */
+#define TT_XE_STATS 2
+int tile_xentropy_multi(void* stream, int phase, int count, int64_t rows, const int64_t* v_len,
+                        const int64_t* v_off, const int32_t* labels, float* const* logits,
+                        const int64_t* ldz, float* parts, int64_t part_stride, const float* lse,
+                        float inv_n);
 
 /* tile_attention_fwd -- causal multi-head scaled dot-product attention for
  * one (query tile, key tile) pair (layer list: pith.science review; the

@@ -30,7 +30,7 @@ def _op(a, t):
 
 @pytest.mark.parametrize("ta,tb", [(0, 0), (0, 1), (1, 0), (1, 1)])
 @pytest.mark.parametrize("m,n,k", [(257, 130, 70), (128, 128, 16), (300, 513, 337), (1, 1, 1), (64, 200, 1),
-                                   (1100, 700, 256)])
+                                   (1100, 700, 256), (4000, 2304, 37)])
 def test_gemm_parity(ta, tb, m, n, k):
     seed = m * 7 + n * 3 + k + 10 * ta + 20 * tb
     a = synth.rand_normal((k, m) if ta else (m, k), seed)
@@ -107,6 +107,50 @@ def test_gemm_ksum_empty_and_errors():
     assert np.array_equal(host(C), (0.5 * c0.astype(np.float32)).astype(np.float64))
     with pytest.raises(tt.TTError):
         tt.tile_gemm_ksum(None, 64, 64, [32], 1.0, [None], [32], [C], [64], 0.0, C, 64)
+
+
+@pytest.mark.parametrize("ta,tb,m,n,k,count,beta,ld_pad", [
+    (1, 0, 768, 768, 256, 15, 1.0, 0),     # the head's dwte_v = dz_v^T nf shape, 128x128 blocks (>= 512 in all)
+    (0, 1, 512, 768, 768, 4, 0.0, 0),      # the head's z_v = nf wte_v^T shape, 64x64 blocks
+    (0, 0, 300, 130, 70, 3, 0.5, 0),       # ragged m, n, k: edge blocks
+    (1, 1, 200, 96, 40, 2, 0.25, 0),
+    (0, 1, 96, 72, 40, 3, 1.0, 1),         # leading dimensions not multiples of 4: scalar loads
+    (0, 0, 64, 64, 32, 100, 0.0, 0),       # more products than one launch takes
+    (1, 0, 128, 64, 0, 2, 0.5, 0),         # k = 0: C = beta C
+])
+def test_gemm_batch(ta, tb, m, n, k, count, beta, ld_pad):
+    """C_t = alpha op(A_t) op(B_t) + beta C_t for every product against the
+    fp64 products (fp32 bound), bitwise equal across runs."""
+    seed = m + 3 * n + 5 * k + count
+    As = [synth.rand_normal(((k, m + ld_pad) if ta else (m, k + ld_pad)), seed + 3 * i) for i in range(count)]
+    Bs = [synth.rand_normal(((n, k + ld_pad) if tb else (k, n + ld_pad)), seed + 3 * i + 1) for i in range(count)]
+    Cs0 = [synth.rand_normal((m, n), seed + 3 * i + 2) for i in range(count)]
+    dA, dB = [dev(a) for a in As], [dev(b) for b in Bs]
+    lda, ldb = As[0].shape[1], Bs[0].shape[1]
+    outs = []
+    for _ in range(2):
+        Cs = [dev(c) for c in Cs0]
+        tt.tile_gemm_batch(None, ta, tb, m, n, k, 0.75, dA, lda, dB, ldb, beta, Cs, n)
+        outs.append(Cs)
+    for t in range(count):
+        a = As[t][:, :m] if ta else As[t][:, :k]
+        b = Bs[t][:, :k] if tb else Bs[t][:, :n]
+        ref = 0.75 * (_op(a.astype(np.float64), ta) @ _op(b.astype(np.float64), tb)) + beta * Cs0[t]
+        bound = 0.75 * (np.abs(_op(a, ta)).astype(np.float64) @ np.abs(_op(b, tb)).astype(np.float64)) * (k + 2) * EPS32
+        assert_close_bound(host(outs[0][t]), ref, bound + 4 * EPS32 * np.abs(ref) + 1e-30,
+                           f"batch {ta}{tb} {m}x{n}x{k} product {t} of {count}")
+        assert torch.equal(outs[0][t], outs[1][t])
+
+
+def test_gemm_batch_empty_and_errors():
+    c0 = synth.rand_normal((64, 64), 6)
+    C = dev(c0)
+    tt.tile_gemm_batch(None, 0, 0, 64, 64, 32, 1.0, [], 32, [], 64, 0.5, [], 64)
+    assert np.array_equal(host(C), c0.astype(np.float32).astype(np.float64))
+    with pytest.raises(tt.TTError):
+        tt.tile_gemm_batch(None, 0, 0, 64, 64, 32, 1.0, [None], 32, [C], 64, 0.0, [C], 64)
+    with pytest.raises(tt.TTError):
+        tt.tile_gemm_batch(None, 0, 0, 64, 64, 32, 1.0, [C], 16, [C], 64, 0.0, [C], 64)
 
 
 @pytest.mark.parametrize("ld_pad", [0, 1, 4])
@@ -267,6 +311,53 @@ def test_cross_entropy_tiles(rows, cols, vt):
         tt.tile_xentropy(None, tt.TT_XE_GRAD, rows, c1 - c0, c0, Y, blk, c1 - c0, lse, None, None, 0, 1.0 / rows)
         dz[:, c0:c1] = blk
     assert_rel(host(dz), rdz, 1e-5, 1e-7 / rows, "dz")
+
+
+@pytest.mark.parametrize("rows,cols,vt", [(300, 5000, 768), (64, 256, 32), (33, 1873, 768), (20, 6600, 100)])
+def test_cross_entropy_multi_tile(rows, cols, vt):
+    """tile_xentropy_multi (all vocab tiles of a token tile per launch; more
+    than 64 tiles make two launches; a ragged 337-wide tile takes the scalar
+    path) equals the per-tile calls bitwise, and the loss, lse and dz the
+    fp64 oracle's."""
+    z = synth.rand_normal((rows, cols), 41, std=3.0)
+    y = np.random.default_rng(42).integers(0, cols, rows).astype(np.int32)
+    Y = dev(y)
+    tiles = otl.tiles(cols, vt)
+    blocks = [dev(z[:, c0:c1]) for c0, c1 in tiles]          # one allocation per tile, as in the step
+    lens, offs = [c1 - c0 for c0, c1 in tiles], [c0 for c0, _ in tiles]
+    parts = empty((len(tiles), rows, 3))
+    tt.tile_xentropy_multi(None, tt.TT_XE_STATS, rows, lens, offs, Y, blocks, lens, parts=parts, part_stride=rows * 3)
+    ref_parts = empty((len(tiles), rows, 3))
+    for i, (c0, c1) in enumerate(tiles):
+        tt.tile_softmax(None, tt.TT_SM_STATS, rows, c1 - c0, 0, c0, 1.0, 0, blocks[i], c1 - c0, Y, ref_parts[i], 0, 0,
+                        None, None, None, 0, 1.0)
+    assert torch.equal(parts, ref_parts)
+    lse, rl = empty((rows,)), empty((rows,))
+    tt.tile_softmax(None, tt.TT_SM_MERGE, rows, 0, 0, 0, 1.0, 0, None, 0, None, parts, len(tiles), rows * 3, lse, rl,
+                    None, 0, 1.0)
+    rloss, rdz, rlse = og.cross_entropy(z.astype(np.float64), y)
+    assert_rel(host(lse), rlse, 1e-6, 1e-6, "lse")
+    assert abs(host(rl).mean() - rloss) <= 1e-5 * abs(rloss)
+    singles = [b.clone() for b in blocks]
+    tt.tile_xentropy_multi(None, tt.TT_XE_GRAD, rows, lens, offs, Y, blocks, lens, lse=lse, inv_n=1.0 / rows)
+    for i, (c0, c1) in enumerate(tiles):
+        tt.tile_xentropy(None, tt.TT_XE_GRAD, rows, c1 - c0, c0, Y, singles[i], c1 - c0, lse, None, None, 0, 1.0 / rows)
+        assert torch.equal(blocks[i], singles[i])
+        assert_rel(host(blocks[i]), rdz[:, c0:c1], 1e-5, 1e-7 / rows, f"dz tile {i}")
+
+
+def test_cross_entropy_multi_errors():
+    z = dev(np.zeros((4, 8), np.float32))
+    y = dev(np.zeros(4, np.int32))
+    tt.tile_xentropy_multi(None, tt.TT_XE_STATS, 4, [], [], y, [], [], parts=z, part_stride=12)  # count 0: no-op
+    with pytest.raises(tt.TTError):
+        tt.tile_xentropy_multi(None, tt.TT_XE_STATS, 4, [8], [0], y, [z], [8], parts=None, part_stride=12)
+    with pytest.raises(tt.TTError):
+        tt.tile_xentropy_multi(None, tt.TT_XE_GRAD, 4, [8], [0], y, [z], [8], lse=None)
+    with pytest.raises(tt.TTError):
+        tt.tile_xentropy_multi(None, tt.TT_XE_GRAD, 4, [4096], [0], y, [z], [4096], lse=z)
+    with pytest.raises(tt.TTError):
+        tt.tile_xentropy_multi(None, 7, 4, [8], [0], y, [z], [8], lse=z)
 
 
 def test_softmax_causal_apply():

@@ -33,7 +33,7 @@ TT_OK, TT_ERR_ARG, TT_ERR_SHAPE, TT_ERR_OOM, TT_ERR_HIP, TT_ERR_STATE, TT_ERR_UN
 TT_EPI_NONE, TT_EPI_BIAS, TT_EPI_RES, TT_EPI_GELU, TT_EPI_GELU_BWD = 0, 1, 2, 4, 8
 TT_LN_PARTIAL, TT_LN_MERGE, TT_LN_APPLY, TT_LN_FUSED = 0, 1, 2, 3
 TT_SM_STATS, TT_SM_MERGE, TT_SM_APPLY = 0, 1, 2
-TT_XE_LOSS, TT_XE_GRAD = 0, 1
+TT_XE_LOSS, TT_XE_GRAD, TT_XE_STATS = 0, 1, 2
 TT_ATT_PREP, TT_ATT_GRAD = 0, 1
 TT_EMB_TOKEN, TT_EMB_POS = 0, 1
 TT_MAX_DIMS = 6
@@ -96,6 +96,8 @@ SIGNATURES = {
     "tile_gemm_ws": (I, [P, I, I, I64, I64, I64, F, P, I64, P, I64, F, P, I64, I, P, P, I64, P, I64, P, SZ]),
     "tile_gemm_workspace": (SZ, [I64, I64, I64]),
     "tile_gemm_ksum": (I, [P, I, I64, I64, P, F, P, P, P, P, F, P, I64]),
+    "tile_gemm_batch": (I, [P, I, I, I, I64, I64, I64, F, P, I64, P, I64, F, P, I64]),
+    "tile_xentropy_multi": (I, [P, I, I, I64, P, P, P, P, P, P, I64, P, F]),
     "tile_layernorm_fwd": (I, [P, I, I64, I64, P, I64, P, P, P, I64, I64, P, P, I64, F]),
     "tile_layernorm_bwd": (I, [P, I, I64, I64, I64, P, I64, P, I64, P, P, P, I64, I64, P, I64, I, P, P, P]),
     "tile_layernorm_bwd_workspace": (SZ, [I64, I64]),

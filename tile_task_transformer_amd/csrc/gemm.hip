@@ -37,7 +37,9 @@
 //     reducing a K range into its own slice of a workspace; a second kernel
 //     adds the slices in slice order and applies the epilogue (deterministic:
 //     no atomics). S is picked so the workgroup count sits just under a
-//     multiple of the CU count.
+//     multiple of the CU count;
+//   * block shape by C's shape: 128x128 (BK 16) for large C (the kernel
+//     keeps three workgroups per CU), 64x64 (BK 32) for small C.
 // Ragged M, N, K are handled by zero-filling out-of-range loads and
 // predicating stores; leading dimensions that are not multiples of 4 (or
 // unaligned pointers) select a scalar-load instantiation.
@@ -134,35 +136,45 @@ __device__ __forceinline__ void kc_index(int idx, int* r, int* c) {
   }
 }
 
+// LDS floats of one gemm_block configuration (two stages of A and B)
+template <int BM, int BN, int BK, bool TA, bool TB>
+struct GemmLds {
+  static constexpr int A_LD = !TA ? BK + 4 : BM + 8;
+  static constexpr int B_LD = TB ? BK + 4 : BN + 8;
+  static constexpr int A_SZ = !TA ? BM * A_LD : BK * A_LD;
+  static constexpr int B_SZ = TB ? BN * B_LD : BK * B_LD;
+  static constexpr int FLOATS = 2 * (A_SZ + B_SZ);
+};
+
+// Workgroups are dispatched round-robin over the 8 XCDs: linear index b ->
+// a block index such that consecutive blocks run on the same XCD (its L2
+// then serves their shared operand panels).
+__device__ __forceinline__ int xcd_contiguous(int b, int nb) {
+  const int per = nb / 8, rem = nb % 8, x = b % 8;
+  return x * per + min(x, rem) + b / 8;
+}
+
+// One BM x BN block of C (K range `split` of g.splits): block index b, after
+// the XCD remap, over the ntile * splits blocks of this product.
 template <int BM, int BN, int BK, bool TA, bool TB, bool VA, bool VB, bool SPLIT>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
+__device__ __forceinline__ void gemm_block(const GemmArgs& g, int b, float* lds) {
   constexpr int WM = BM / 2, WN = BN / 2;      // wave sub-block
   constexpr int FM = WM / 32, FN = WN / 32;    // 32x32 MFMA tiles per wave
   constexpr int A_KC = !TA, B_KC = TB;
-  constexpr int A_LD = A_KC ? BK + 4 : BM + 8;
-  constexpr int B_LD = B_KC ? BK + 4 : BN + 8;
-  constexpr int A_SZ = A_KC ? BM * A_LD : BK * A_LD;
-  constexpr int B_SZ = B_KC ? BN * B_LD : BK * B_LD;
+  using LL = GemmLds<BM, BN, BK, TA, TB>;
+  constexpr int A_LD = LL::A_LD, B_LD = LL::B_LD, A_SZ = LL::A_SZ, B_SZ = LL::B_SZ;
   constexpr int A_V4 = BM * BK / 4, B_V4 = BN * BK / 4;
   constexpr int A_PT = A_V4 / 256, B_PT = B_V4 / 256;
   static_assert(A_V4 % 256 == 0 && B_V4 % 256 == 0, "tile must split evenly over 256 threads");
-
-  __shared__ __attribute__((aligned(16))) float lds[2 * (A_SZ + B_SZ)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int half = lane >> 5, l32 = lane & 31;
 
-  // ---- block -> (C tile, K range): XCD-contiguous, then grouped along M
+  // ---- block -> (C tile, K range): grouped along M
   const int grid_m = (g.m + BM - 1) / BM, grid_n = (g.n + BN - 1) / BN;
   const int ntile = grid_m * grid_n;
-  const int nb = ntile * g.splits;
-  int b = blockIdx.x;
-  {
-    const int per = nb / 8, rem = nb % 8, x = b % 8;
-    b = x * per + min(x, rem) + b / 8;
-  }
   const int split = b / ntile;
   b -= split * ntile;
   constexpr int GROUP = 8;
@@ -364,6 +376,38 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
           epilogue_store(g, row, col, g.alpha * acc[i][j][r]);
       }
     }
+}
+
+template <int BM, int BN, int BK, bool TA, bool TB, bool VA, bool VB, bool SPLIT>
+__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) float lds[GemmLds<BM, BN, BK, TA, TB>::FLOATS];
+  const int nb = ((g.m + BM - 1) / BM) * ((g.n + BN - 1) / BN) * g.splits;
+  gemm_block<BM, BN, BK, TA, TB, VA, VB, SPLIT>(g, xcd_contiguous(blockIdx.x, nb), lds);
+}
+
+// ---- batch: C_t = alpha * op(A_t) op(B_t) + beta * C_t for a list of
+// products that share every size and leading dimension, one launch (the LM
+// head: one product per vocab tile). The blocks of all products form one
+// grid, remapped XCD-contiguously, so each XCD works through a contiguous
+// run of products and keeps their operand panels in its L2.
+constexpr int kBatchMax = 96;  // products per launch (kernel arguments stay under 4 KB)
+struct GemmBatch {
+  const float* A[kBatchMax];
+  const float* B[kBatchMax];
+  float* C[kBatchMax];
+};
+
+template <int BM, int BN, int BK, bool TA, bool TB, bool VA, bool VB>
+__global__ __launch_bounds__(256, 2) void gemm_batch_kernel(GemmArgs g, GemmBatch P) {
+  __shared__ __attribute__((aligned(16))) float lds[GemmLds<BM, BN, BK, TA, TB>::FLOATS];
+  const int ntile = ((g.m + BM - 1) / BM) * ((g.n + BN - 1) / BN);
+  const int b = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int t = b / ntile;
+  GemmArgs h = g;
+  h.A = P.A[t];
+  h.B = P.B[t];
+  h.C = P.C[t];
+  gemm_block<BM, BN, BK, TA, TB, VA, VB, false>(h, b - t * ntile, lds);
 }
 
 // Sum of the split-K slices in slice order, then the epilogue.
@@ -712,6 +756,20 @@ __global__ __launch_bounds__(256, 2) void gemm_ksum_kernel(KsumArgs P) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+template <int BM, int BN, int BK, bool TA, bool TB>
+void launch_batch_v(const GemmArgs& g, const GemmBatch& P, int count, bool vec, hipStream_t s) {
+  const int64_t ntile = ((g.m + BM - 1) / BM) * (int64_t)((g.n + BN - 1) / BN);
+  const dim3 grid((unsigned)(ntile * count)), block(256);
+  if (vec) hipLaunchKernelGGL((gemm_batch_kernel<BM, BN, BK, TA, TB, true, true>), grid, block, 0, s, g, P);
+  else hipLaunchKernelGGL((gemm_batch_kernel<BM, BN, BK, TA, TB, false, false>), grid, block, 0, s, g, P);
+}
+
+template <bool TA, bool TB>
+void launch_batch_t(const GemmArgs& g, const GemmBatch& P, int count, bool big, bool vec, hipStream_t s) {
+  if (big) launch_batch_v<128, 128, 16, TA, TB>(g, P, count, vec, s);
+  else launch_batch_v<64, 64, 32, TA, TB>(g, P, count, vec, s);
+}
+
 }  // namespace
 
 extern "C" size_t tile_gemm_workspace(int64_t m, int64_t n, int64_t k) {
@@ -830,5 +888,49 @@ extern "C" int tile_gemm_ksum(void* stream, int count, int64_t m, int64_t n, con
   if (!wrote)  // no product at all: C = beta * C
     return tile_gemm(stream, 0, 0, m, n, 0, alpha, nullptr, 1, nullptr, n, beta, C, ldc, TT_EPI_NONE, nullptr, nullptr,
                      0, nullptr, 0);
+  return TT_OK;
+}
+
+extern "C" int tile_gemm_batch(void* stream, int count, int transA, int transB, int64_t m, int64_t n, int64_t k,
+                               float alpha, const float* const* A, int64_t lda, const float* const* B, int64_t ldb,
+                               float beta, float* const* C, int64_t ldc) {
+  using tt::fail;
+  if (count < 0 || m < 0 || n < 0 || k < 0) return fail(TT_ERR_ARG, "tile_gemm_batch: negative count or size");
+  if (count == 0 || m == 0 || n == 0) return TT_OK;
+  if (m > INT32_MAX || n > INT32_MAX || k > INT32_MAX) return fail(TT_ERR_ARG, "tile_gemm_batch: size exceeds int32");
+  if (!A || !B || !C) return fail(TT_ERR_ARG, "tile_gemm_batch: null array");
+  if (ldc < n) return fail(TT_ERR_ARG, "tile_gemm_batch: ldc < n");
+  if (k > 0 && lda < (transA ? m : k)) return fail(TT_ERR_ARG, "tile_gemm_batch: lda too small");
+  if (k > 0 && ldb < (transB ? k : n)) return fail(TT_ERR_ARG, "tile_gemm_batch: ldb too small");
+  bool vec = k > 0 && lda % 4 == 0 && ldb % 4 == 0;
+  for (int t = 0; t < count; ++t) {
+    if (!C[t] || (k > 0 && (!A[t] || !B[t]))) return fail(TT_ERR_ARG, "tile_gemm_batch: null operand in product %d", t);
+    if (k > 0) vec = vec && aligned16(A[t]) && aligned16(B[t]);
+  }
+  hipStream_t s = tt::as_stream(stream);
+  // the plan tile_gemm would pick if the products were one C: 128x128x16
+  // blocks when there are >= 512 of them, else 64x64x32 (no split-K)
+  const int64_t b128 = ((m + 127) / 128) * ((n + 127) / 128);
+  const bool big = b128 * count >= 512;
+  const int64_t ntile = big ? b128 : ((m + 63) / 64) * ((n + 63) / 64);
+  // grid.x * 256 work-items must stay below 2^32
+  const int64_t per_launch = std::min<int64_t>(kBatchMax, (int64_t)(UINT32_MAX / 256) / ntile);
+  if (per_launch < 1) return fail(TT_ERR_SHAPE, "tile_gemm_batch: product too large for one launch");
+  GemmArgs g{(int)m, (int)n, (int)k, alpha, beta, nullptr, nullptr, nullptr, lda, ldb, ldc, TT_EPI_NONE, nullptr,
+             nullptr, 0, nullptr, 0, nullptr, 1, (int)k};
+  for (int t0 = 0; t0 < count; t0 += (int)per_launch) {
+    const int c = (int)std::min<int64_t>(per_launch, count - t0);
+    GemmBatch P{};
+    for (int u = 0; u < c; ++u) {
+      P.A[u] = A[t0 + u];
+      P.B[u] = B[t0 + u];
+      P.C[u] = C[t0 + u];
+    }
+    if (!transA && !transB) launch_batch_t<false, false>(g, P, c, big, vec, s);
+    else if (!transA && transB) launch_batch_t<false, true>(g, P, c, big, vec, s);
+    else if (transA && !transB) launch_batch_t<true, false>(g, P, c, big, vec, s);
+    else launch_batch_t<true, true>(g, P, c, big, vec, s);
+    if (int rc = tt::launch_status("tile_gemm_batch")) return rc;
+  }
   return TT_OK;
 }

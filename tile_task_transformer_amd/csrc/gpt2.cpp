@@ -130,6 +130,71 @@ int submit_gemm(tt_ctx* ctx, const char* label, const Gemm& q) {
   }, 2.0 * m * n * k);
 }
 
+// Independent products of one shape (the tied head's per-vocab-tile GEMMs)
+// as multi-tile tasks over tile_gemm_batch: consecutive products that share
+// transposes, scalars, sizes and leading dimensions form one task (up to
+// 96 products and 1 GiB of output tiles, so the grouping depends on the
+// tiling only); a product of another shape (the ragged last vocab tile)
+// is a task of its own. Each task reads its A and B tiles and writes (beta
+// == 0) or updates its C tiles.
+int submit_gemm_batch(tt_ctx* ctx, const char* label, const std::vector<Gemm>& qs) {
+  constexpr size_t kMaxProducts = 96;
+  constexpr int64_t kMaxBytes = int64_t(1) << 30;
+  struct Shape {
+    int64_t m, n, k, lda, ldb, ldc;
+  };
+  auto shape_of = [](const Gemm& q) {
+    int64_t ar, ac, br, bc, cr, cc;
+    q.A.t->mat(q.A.lin, &ar, &ac);
+    q.B.t->mat(q.B.lin, &br, &bc);
+    q.C.t->mat(q.C.lin, &cr, &cc);
+    return Shape{q.ta ? ac : ar, q.tb ? br : bc, q.ta ? ar : ac, ac, bc, cc};
+  };
+  size_t i = 0;
+  while (i < qs.size()) {
+    const Gemm& q0 = qs[i];
+    const Shape s0 = shape_of(q0);
+    const int64_t cbytes = s0.m * s0.n * (int64_t)sizeof(float);
+    size_t j = i + 1;
+    while (j < qs.size() && j - i < kMaxProducts && (int64_t)(j - i + 1) * cbytes <= kMaxBytes) {
+      const Gemm& q = qs[j];
+      const Shape sh = shape_of(q);
+      if (q.ta != q0.ta || q.tb != q0.tb || q.alpha != q0.alpha || q.beta != q0.beta || q.epi != TT_EPI_NONE ||
+          sh.m != s0.m || sh.n != s0.n || sh.k != s0.k || sh.lda != s0.lda || sh.ldb != s0.ldb || sh.ldc != s0.ldc)
+        break;
+      ++j;
+    }
+    if (j - i == 1 || q0.epi != TT_EPI_NONE) {
+      if (int rc = submit_gemm(ctx, label, q0)) return rc;
+      ++i;
+      continue;
+    }
+    std::vector<Gemm> grp(qs.begin() + i, qs.begin() + j);
+    std::vector<Access> acc;
+    for (const Gemm& q : grp) {
+      acc.push_back(R(q.A.t, q.A.lin));
+      acc.push_back(R(q.B.t, q.B.lin));
+      acc.push_back(q0.beta == 0.f ? W(q.C.t, q.C.lin) : RW(q.C.t, q.C.lin));
+    }
+    const double flops = 2.0 * s0.m * s0.n * s0.k * (double)grp.size();
+    int rc = ctx->submit(label, std::move(acc), [grp, s0](hipStream_t s, void*) {
+      const size_t c = grp.size();
+      std::vector<const float*> A(c), B(c);
+      std::vector<float*> C(c);
+      for (size_t u = 0; u < c; ++u) {
+        A[u] = F(grp[u].A.t, grp[u].A.lin);
+        B[u] = F(grp[u].B.t, grp[u].B.lin);
+        C[u] = F(grp[u].C.t, grp[u].C.lin);
+      }
+      return tile_gemm_batch(s, (int)c, grp[0].ta, grp[0].tb, s0.m, s0.n, s0.k, grp[0].alpha, A.data(), s0.lda,
+                             B.data(), s0.ldb, grp[0].beta, C.data(), s0.ldc);
+    }, flops);
+    if (rc) return rc;
+    i = j;
+  }
+  return TT_OK;
+}
+
 // tiles = value, TT_FILL_MAX_TILES tiles per task and launch (with
 // pinned-host homes a task's tiles take at most an eighth of the arena)
 int fill_tasks(tt_gpt2* g, const std::vector<TileRef>& tiles, float v) {
@@ -783,24 +848,47 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
     for (int64_t si = 0; si < g->ns; ++si) {
       const int64_t ti = bi + g->nb * si;
       TRY(ln_forward(g, g->h_last, lnfg, lnfb, g->lnf, g->nf, ti, bi, si));
-      for (int64_t vj = 0; vj < NV; ++vj) {
-        for (int64_t ek = 0; ek < NE; ++ek) {
+      // z_v = nf wte_v^T for every vocab tile v: per embd tile, one batch
+      // of equal-shape products (tile_gemm_batch), accumulating over embd tiles
+      for (int64_t ek = 0; ek < NE; ++ek) {
+        std::vector<Gemm> qs;
+        for (int64_t vj = 0; vj < NV; ++vj) {
           Gemm q;
           q.tb = 1;
           q.A = {g->nf, L(g->nf, {bi, si, ek})};
           q.B = {wte, L(wte, {vj, ek})};
           q.C = {g->z, L(g->z, {bi, si, vj})};
           q.beta = ek > 0 ? 1.f : 0.f;
-          TRY(submit_gemm(ctx, "head", q));
+          qs.push_back(q);
         }
+        TRY(submit_gemm_batch(ctx, "head", qs));
+      }
+      // per-vocab-tile (max, sum exp, target logit) partials: one task and
+      // launch over all vocab tiles of the token tile (tile_xentropy_multi)
+      {
         tt_tensor *z = g->z, *lab = g->labels, *parts = g->ce_parts;
-        const int64_t lz = L(z, {bi, si, vj}), ll = L(lab, {bi, si}), lp = L(parts, {vj, ti, 0});
-        int64_t r, cols;
-        z->mat(lz, &r, &cols);
-        const int64_t voff = vj * std::min<int64_t>(g->t.vocab, V);
-        TRY(ctx->submit("ce_stats", {R(z, lz), R(lab, ll), W(parts, lp)}, [=](hipStream_t s, void*) {
-          return tile_softmax(s, TT_SM_STATS, rows, cols, 0, voff, 1.f, 0, F(z, lz), cols, I32(lab, ll), F(parts, lp),
-                              0, 0, nullptr, nullptr, nullptr, 0, 1.f);
+        const int64_t ll = L(lab, {bi, si});
+        std::vector<Access> acc = {R(lab, ll)};
+        for (int64_t vj = 0; vj < NV; ++vj) {
+          acc.push_back(R(z, L(z, {bi, si, vj})));
+          acc.push_back(W(parts, L(parts, {vj, ti, 0})));
+        }
+        TRY(ctx->submit("ce_stats", std::move(acc), [=](hipStream_t s, void*) {
+          std::vector<float*> zs(NV);
+          std::vector<int64_t> lens(NV), offs(NV);
+          float* p0 = F(parts, L(parts, {0, ti, 0}));
+          for (int64_t vj = 0; vj < NV; ++vj) {
+            const int64_t lz = L(z, {bi, si, vj});
+            int64_t r, cols;
+            z->mat(lz, &r, &cols);
+            zs[vj] = F(z, lz);
+            lens[vj] = cols;
+            offs[vj] = vj * std::min<int64_t>(g->t.vocab, V);
+            if (F(parts, L(parts, {vj, ti, 0})) != p0 + vj * rows * 3)
+              return fail(TT_ERR_STATE, "ce_stats: partials of one token tile are not evenly spaced");
+          }
+          return tile_xentropy_multi(s, TT_XE_STATS, (int)NV, rows, lens.data(), offs.data(), I32(lab, ll),
+                                     zs.data(), lens.data(), p0, rows * 3, nullptr, 1.f);
         }));
       }
       {
@@ -820,15 +908,26 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
           return tile_xentropy(s, TT_XE_LOSS, rows, 0, 0, nullptr, nullptr, 0, nullptr, F(rl, ti), F(loss, 0),
                                accumulate, inv_n);
         }));
-        for (int64_t vj = 0; vj < NV; ++vj) {
+        // dz in place of the logits, all vocab tiles of the token tile in one
+        // task and launch
+        {
           tt_tensor *z = g->z, *lab = g->labels;
-          const int64_t lz = L(z, {bi, si, vj}), ll = L(lab, {bi, si});
-          int64_t r, cols;
-          z->mat(lz, &r, &cols);
-          const int64_t voff = vj * std::min<int64_t>(g->t.vocab, V);
-          TRY(ctx->submit("ce_grad", {RW(z, lz), R(lab, ll), R(lse, ti)}, [=](hipStream_t s, void*) {
-            return tile_xentropy(s, TT_XE_GRAD, rows, cols, voff, I32(lab, ll), F(z, lz), cols, F(lse, ti), nullptr,
-                                 nullptr, 0, inv_n);
+          const int64_t ll = L(lab, {bi, si});
+          std::vector<Access> acc = {R(lab, ll), R(lse, ti)};
+          for (int64_t vj = 0; vj < NV; ++vj) acc.push_back(RW(z, L(z, {bi, si, vj})));
+          TRY(ctx->submit("ce_grad", std::move(acc), [=](hipStream_t s, void*) {
+            std::vector<float*> zs(NV);
+            std::vector<int64_t> lens(NV), offs(NV);
+            for (int64_t vj = 0; vj < NV; ++vj) {
+              const int64_t lz = L(z, {bi, si, vj});
+              int64_t r, cols;
+              z->mat(lz, &r, &cols);
+              zs[vj] = F(z, lz);
+              lens[vj] = cols;
+              offs[vj] = vj * std::min<int64_t>(g->t.vocab, V);
+            }
+            return tile_xentropy_multi(s, TT_XE_GRAD, (int)NV, rows, lens.data(), offs.data(), I32(lab, ll),
+                                       zs.data(), lens.data(), nullptr, 0, F(lse, ti), inv_n);
           }));
         }
       }
@@ -919,22 +1018,25 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
   }
 
   // ---- backward: head (dz is in place of the logits)
+  // dwte (head part) = sum over token tiles of dz^T nf: per (embd tile,
+  // token tile), one batch of equal-shape products over the vocab tiles
   tt_tensor* gwte = g->G[0];
-  for (int64_t vj = 0; vj < NV; ++vj)
-    for (int64_t ek = 0; ek < NE; ++ek) {
-      // dwte (head part) = sum over token tiles of dz^T nf
-      for (int64_t si = 0; si < g->ns; ++si)
-        for (int64_t bi = 0; bi < g->nb; ++bi) {
-          const int64_t ti = bi + g->nb * si;
+  for (int64_t ek = 0; ek < NE; ++ek)
+    for (int64_t si = 0; si < g->ns; ++si)
+      for (int64_t bi = 0; bi < g->nb; ++bi) {
+        const int64_t ti = bi + g->nb * si;
+        std::vector<Gemm> qs;
+        for (int64_t vj = 0; vj < NV; ++vj) {
           Gemm q;
           q.ta = 1;
           q.A = {g->z, L(g->z, {bi, si, vj})};
           q.B = {g->nf, L(g->nf, {bi, si, ek})};
           q.C = {gwte, L(gwte, {vj, ek})};
           q.beta = (ti > 0 || later_mb) ? 1.f : 0.f;
-          TRY(submit_gemm(ctx, "head_dw", q));
+          qs.push_back(q);
         }
-    }
+        TRY(submit_gemm_batch(ctx, "head_dw", qs));
+      }
   // dnf = sum over vocab tiles of dz wte: one task per (token tile, embd
   // tile), one long-K product over every vocab tile (tile_gemm_ksum), instead
   // of a chain of accumulating GEMMs that each read and write dnf

@@ -14,13 +14,12 @@ namespace {
 
 constexpr int kWaves = 4;
 
+// (max, sum exp(x - max), picked target) of one row of one tile, by one wave
 template <int NV, bool VEC>
-__global__ __launch_bounds__(256) void sm_stats(int rows, int cols, int64_t row_off, int64_t col_off, float scale,
-                                                int causal, const float* __restrict__ X, int64_t ldx,
-                                                const int32_t* __restrict__ labels, float* __restrict__ parts) {
+__device__ __forceinline__ void stats_row(int row, int cols, int64_t row_off, int64_t col_off, float scale,
+                                          int causal, const float* __restrict__ X, int64_t ldx,
+                                          const int32_t* __restrict__ labels, float* __restrict__ parts) {
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
-  if (row >= rows) return;
   // valid columns of this row: c < lim
   int lim = cols;
   if (causal) {
@@ -60,6 +59,33 @@ __global__ __launch_bounds__(256) void sm_stats(int rows, int cols, int64_t row_
   }
 }
 
+template <int NV, bool VEC>
+__global__ __launch_bounds__(256) void sm_stats(int rows, int cols, int64_t row_off, int64_t col_off, float scale,
+                                                int causal, const float* __restrict__ X, int64_t ldx,
+                                                const int32_t* __restrict__ labels, float* __restrict__ parts) {
+  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  stats_row<NV, VEC>(row, cols, row_off, col_off, scale, causal, X, ldx, labels, parts);
+}
+
+// several vocab tiles of one token tile per launch (blockIdx.y = tile)
+constexpr int kXeMax = 64;
+struct XeTiles {
+  float* z[kXeMax];
+  int64_t ld[kXeMax];
+  int64_t off[kXeMax];
+  int cols[kXeMax];
+};
+
+template <int NV, bool VEC>
+__global__ __launch_bounds__(256) void xe_stats_multi(int rows, XeTiles P, const int32_t* __restrict__ labels,
+                                                      float* __restrict__ parts, int64_t part_stride) {
+  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int t = blockIdx.y;
+  stats_row<NV, VEC>(row, P.cols[t], 0, P.off[t], 1.f, 0, P.z[t], P.ld[t], labels, parts + t * part_stride);
+}
+
 __global__ void sm_merge(int rows, int n_parts, const float* __restrict__ parts, int64_t stride,
                          float* __restrict__ lse, float* __restrict__ row_loss) {
   const int row = blockIdx.x * blockDim.x + threadIdx.x;
@@ -78,13 +104,11 @@ __global__ void sm_merge(int rows, int n_parts, const float* __restrict__ parts,
   if (row_loss) row_loss[row] = l - picked;
 }
 
+// 4 columns c..c+3 of one row: (exp(x * scale - lse) - onehot) * grad_scale
 template <bool VEC>
-__global__ void sm_apply(int rows, int cols, int64_t row_off, int64_t col_off, float scale, int causal,
-                         const float* X, int64_t ldx, const int32_t* __restrict__ labels,
-                         const float* __restrict__ lse, float* Y, int64_t ldy, float grad_scale) {
-  const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
-  const int row = blockIdx.y;
-  if (c >= cols) return;
+__device__ __forceinline__ void apply4(int row, int c, int cols, int64_t row_off, int64_t col_off, float scale,
+                                       int causal, const float* X, int64_t ldx, const int32_t* __restrict__ labels,
+                                       const float* __restrict__ lse, float* Y, int64_t ldy, float grad_scale) {
   const float l = lse[row];
   const int64_t lab = labels ? labels[row] - col_off : -1;
   const int64_t lim = causal ? row_off + row - col_off + 1 : (int64_t)cols;
@@ -97,6 +121,26 @@ __global__ void sm_apply(int rows, int cols, int64_t row_off, int64_t col_off, f
     y[i] = p * grad_scale;
   }
   tt::st4<VEC>(Y, ldy, row, c, cols, y);
+}
+
+template <bool VEC>
+__global__ void sm_apply(int rows, int cols, int64_t row_off, int64_t col_off, float scale, int causal,
+                         const float* X, int64_t ldx, const int32_t* __restrict__ labels,
+                         const float* __restrict__ lse, float* Y, int64_t ldy, float grad_scale) {
+  const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  const int row = blockIdx.y;
+  if (c >= cols) return;
+  apply4<VEC>(row, c, cols, row_off, col_off, scale, causal, X, ldx, labels, lse, Y, ldy, grad_scale);
+}
+
+template <bool VEC>
+__global__ void xe_grad_multi(XeTiles P, const int32_t* __restrict__ labels, const float* __restrict__ lse,
+                              float inv_n) {
+  const int t = blockIdx.z;
+  const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  const int row = blockIdx.y;
+  if (c >= P.cols[t]) return;
+  apply4<VEC>(row, c, P.cols[t], 0, P.off[t], 1.f, 0, P.z[t], P.ld[t], labels, lse, P.z[t], P.ld[t], inv_n);
 }
 
 __global__ __launch_bounds__(256) void xe_loss(int rows, const float* __restrict__ row_loss, float* loss,
@@ -142,6 +186,14 @@ int launch_apply(int rows, int cols, int64_t row_off, int64_t col_off, float sca
 
 constexpr int kMaxCols = 2048;
 constexpr int64_t kMaxRows = 65535;
+
+template <int NV>
+void launch_stats_multi(bool vec, int rows, int count, const XeTiles& P, const int32_t* labels, float* parts,
+                        int64_t part_stride, hipStream_t s) {
+  dim3 grid((unsigned)((rows + kWaves - 1) / kWaves), (unsigned)count), block(256);
+  if (vec) hipLaunchKernelGGL((xe_stats_multi<NV, true>), grid, block, 0, s, rows, P, labels, parts, part_stride);
+  else hipLaunchKernelGGL((xe_stats_multi<NV, false>), grid, block, 0, s, rows, P, labels, parts, part_stride);
+}
 
 }  // namespace
 
@@ -203,4 +255,58 @@ extern "C" int tile_xentropy(void* stream, int phase, int64_t rows, int64_t v_le
     return launch_apply((int)rows, (int)v_len, 0, v_off, 1.f, 0, logits, ldz, labels, lse, logits, ldz, inv_n, s);
   }
   return fail(TT_ERR_ARG, "tile_xentropy: bad phase %d", phase);
+}
+
+extern "C" int tile_xentropy_multi(void* stream, int phase, int count, int64_t rows, const int64_t* v_len,
+                                   const int64_t* v_off, const int32_t* labels, float* const* logits,
+                                   const int64_t* ldz, float* parts, int64_t part_stride, const float* lse,
+                                   float inv_n) {
+  using tt::fail;
+  hipStream_t s = tt::as_stream(stream);
+  if (count < 0 || rows < 0) return fail(TT_ERR_ARG, "tile_xentropy_multi: negative count or size");
+  if (count == 0 || rows == 0) return TT_OK;
+  if (phase != TT_XE_STATS && phase != TT_XE_GRAD) return fail(TT_ERR_ARG, "tile_xentropy_multi: bad phase %d", phase);
+  if (rows > kMaxRows) return fail(TT_ERR_SHAPE, "tile_xentropy_multi: rows > %lld", (long long)kMaxRows);
+  if (!v_len || !v_off || !logits || !ldz || !labels) return fail(TT_ERR_ARG, "tile_xentropy_multi: null array");
+  if (phase == TT_XE_STATS && (!parts || part_stride < rows * 3))
+    return fail(TT_ERR_ARG, "tile_xentropy_multi(STATS): bad parts");
+  if (phase == TT_XE_GRAD && !lse) return fail(TT_ERR_ARG, "tile_xentropy_multi(GRAD): null lse");
+  for (int t = 0; t < count; ++t) {
+    if (v_len[t] < 1 || v_len[t] > kMaxCols)
+      return fail(TT_ERR_SHAPE, "tile_xentropy_multi: v_len of tile %d not in [1, %d]", t, kMaxCols);
+    if (!logits[t] || ldz[t] < v_len[t]) return fail(TT_ERR_ARG, "tile_xentropy_multi: bad tile %d", t);
+  }
+  for (int t0 = 0; t0 < count; t0 += kXeMax) {
+    const int c = std::min(kXeMax, count - t0);
+    XeTiles P{};
+    bool vec = true;
+    int maxc = 1;
+    for (int u = 0; u < c; ++u) {
+      P.z[u] = logits[t0 + u];
+      P.ld[u] = ldz[t0 + u];
+      P.off[u] = v_off[t0 + u];
+      P.cols[u] = (int)v_len[t0 + u];
+      vec = vec && ldz[t0 + u] % 4 == 0 && tt::aligned16(logits[t0 + u]);
+      maxc = std::max(maxc, P.cols[u]);
+    }
+    if (phase == TT_XE_STATS) {
+      float* pp = parts + t0 * part_stride;
+      const int r = (int)rows;
+      switch ((maxc + 255) / 256) {
+        case 1: launch_stats_multi<1>(vec, r, c, P, labels, pp, part_stride, s); break;
+        case 2: launch_stats_multi<2>(vec, r, c, P, labels, pp, part_stride, s); break;
+        case 3: launch_stats_multi<3>(vec, r, c, P, labels, pp, part_stride, s); break;
+        case 4: launch_stats_multi<4>(vec, r, c, P, labels, pp, part_stride, s); break;
+        case 5: case 6: launch_stats_multi<6>(vec, r, c, P, labels, pp, part_stride, s); break;
+        default: launch_stats_multi<8>(vec, r, c, P, labels, pp, part_stride, s); break;
+      }
+      if (int rc = tt::launch_status("tile_xentropy_multi(STATS)")) return rc;
+    } else {
+      dim3 grid((unsigned)((maxc / 4 + 1 + 255) / 256), (unsigned)rows, (unsigned)c), block(256);
+      if (vec) hipLaunchKernelGGL(xe_grad_multi<true>, grid, block, 0, s, P, labels, lse, inv_n);
+      else hipLaunchKernelGGL(xe_grad_multi<false>, grid, block, 0, s, P, labels, lse, inv_n);
+      if (int rc = tt::launch_status("tile_xentropy_multi(GRAD)")) return rc;
+    }
+  }
+  return TT_OK;
 }

@@ -9,18 +9,20 @@ from __future__ import annotations
 
 from ._lib import (TT_EPI_NONE, check, lib, ptr, stream_handle, TT_EPI_BIAS, TT_EPI_RES, TT_EPI_GELU,  # noqa: F401
                    TT_EPI_GELU_BWD, TT_LN_PARTIAL, TT_LN_MERGE, TT_LN_APPLY, TT_LN_FUSED, TT_SM_STATS,
-                   TT_SM_MERGE, TT_SM_APPLY, TT_XE_LOSS, TT_XE_GRAD, TT_ATT_PREP, TT_ATT_GRAD, TT_EMB_TOKEN,
-                   TT_EMB_POS)
+                   TT_SM_MERGE, TT_SM_APPLY, TT_XE_LOSS, TT_XE_GRAD, TT_XE_STATS, TT_ATT_PREP, TT_ATT_GRAD,
+                   TT_EMB_TOKEN, TT_EMB_POS)
 
 __all__ = [
-    "tile_gemm", "tile_gemm_ws", "tile_gemm_workspace", "tile_gemm_ksum", "tile_layernorm_fwd", "tile_layernorm_bwd", "tile_layernorm_bwd_workspace", "tile_softmax",
-    "tile_xentropy", "tile_attention_fwd", "tile_attention_bwd", "tile_fused_adamw", "tile_fused_adamw_multi",
+    "tile_gemm", "tile_gemm_ws", "tile_gemm_workspace", "tile_gemm_ksum", "tile_gemm_batch", "tile_layernorm_fwd",
+    "tile_layernorm_bwd", "tile_layernorm_bwd_workspace", "tile_softmax",
+    "tile_xentropy", "tile_xentropy_multi", "tile_attention_fwd", "tile_attention_bwd", "tile_fused_adamw",
+    "tile_fused_adamw_multi",
     "tile_adamw_advance", "tile_sgd", "tile_sgd_multi",
     "tile_embedding_fwd", "tile_embedding_index", "tile_embedding_bwd", "tile_reduce_rows",
     "tile_reduce_rows_workspace", "tile_fill", "tile_fill_multi", "tile_split_tokens",
     "TT_EPI_NONE", "TT_EPI_BIAS", "TT_EPI_RES", "TT_EPI_GELU", "TT_EPI_GELU_BWD", "TT_LN_PARTIAL",
     "TT_LN_MERGE", "TT_LN_APPLY", "TT_LN_FUSED", "TT_SM_STATS", "TT_SM_MERGE", "TT_SM_APPLY", "TT_XE_LOSS",
-    "TT_XE_GRAD", "TT_ATT_PREP", "TT_ATT_GRAD", "TT_EMB_TOKEN", "TT_EMB_POS",
+    "TT_XE_GRAD", "TT_XE_STATS", "TT_ATT_PREP", "TT_ATT_GRAD", "TT_EMB_TOKEN", "TT_EMB_POS",
 ]
 
 
@@ -51,6 +53,15 @@ def tile_gemm_ksum(stream, m, n, ks, alpha, As, ldas, Bs, ldbs, beta, C, ldc):
                                     i64(ldbs), beta, ptr(C), ldc))
 
 
+def tile_gemm_batch(stream, transA, transB, m, n, k, alpha, As, lda, Bs, ldb, beta, Cs, ldc):
+    """C_t = alpha op(A_t) op(B_t) + beta C_t for equal-length lists of tensors of one shape."""
+    import ctypes as C_
+    cnt = len(Cs)
+    ptrs = lambda xs: (C_.c_void_p * max(cnt, 1))(*[ptr(x) for x in xs])  # noqa: E731
+    return check(lib.tile_gemm_batch(stream_handle(stream), cnt, transA, transB, m, n, k, alpha, ptrs(As), lda,
+                                     ptrs(Bs), ldb, beta, ptrs(Cs), ldc))
+
+
 def tile_layernorm_fwd(stream, phase, rows, cols, x, ldx, gamma, beta, parts, n_parts, part_stride, stats, y,
                        ldy, eps):
     return check(lib.tile_layernorm_fwd(stream_handle(stream), phase, rows, cols, ptr(x), ldx, ptr(gamma),
@@ -78,6 +89,17 @@ def tile_softmax(stream, phase, rows, cols, row_offset, col_offset, scale, causa
 def tile_xentropy(stream, phase, rows, v_len, v_off, labels, logits, ldz, lse, row_loss, loss, accumulate, inv_n):
     return check(lib.tile_xentropy(stream_handle(stream), phase, rows, v_len, v_off, ptr(labels), ptr(logits), ldz,
                                    ptr(lse), ptr(row_loss), ptr(loss), accumulate, inv_n))
+
+
+def tile_xentropy_multi(stream, phase, rows, v_lens, v_offs, labels, logits, ldzs, parts=None, part_stride=0,
+                        lse=None, inv_n=1.0):
+    """STATS or GRAD of several vocab tiles (equal-length lists) in one launch."""
+    import ctypes as C_
+    cnt = len(logits)
+    i64 = lambda xs: (C_.c_int64 * max(cnt, 1))(*[int(x) for x in xs])  # noqa: E731
+    ptrs = (C_.c_void_p * max(cnt, 1))(*[ptr(x) for x in logits])
+    return check(lib.tile_xentropy_multi(stream_handle(stream), phase, cnt, rows, i64(v_lens), i64(v_offs),
+                                         ptr(labels), ptrs, i64(ldzs), ptr(parts), part_stride, ptr(lse), inv_n))
 
 
 def tile_attention_fwd(stream, batch, heads, q_len, k_len, hd, q_off, k_off, Q, K, V, O, ml, lse, first, last,
