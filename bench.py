@@ -437,7 +437,9 @@ def main(argv=None):
     # dominant class bracketed by events (an event pair costs ~4 us of queue
     # time; 5 is prime to the 66 vocab tiles of GPT2-small, so the sample
     # rotates through every tile, the ragged last one included)
-    ctx.profile(dominant, every=PROFILE_EVERY)
+    # (a class with fewer launches per step than that is timed at every launch)
+    every = PROFILE_EVERY if classes.get(dominant, {}).get("launches", PROFILE_EVERY) >= PROFILE_EVERY else 1
+    ctx.profile(dominant, every=every)
     ctx.reset_stats()
     torch.cuda.synchronize()
     ctx.wait()
@@ -456,7 +458,7 @@ def main(argv=None):
     tok_s = s.batch * s.seq / (elapsed / a.steps)
     tflops = model_flops(s) / (elapsed / a.steps) / 1e12
     launches = prof.get("count", 0)
-    per_step = classes[dominant]["launches"] if dominant in classes else launches * PROFILE_EVERY / a.steps
+    per_step = classes[dominant]["launches"] if dominant in classes else launches * every / a.steps
     per_launch = work[dominant][1] / per_step if launches else float("nan")
     avg_ms = prof["total_ms"] / launches if launches else float("nan")
     achieved = per_launch / (avg_ms * 1e-3) / 1e12

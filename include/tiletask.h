@@ -117,24 +117,29 @@ size_t tile_gemm_workspace(int64_t m, int64_t n, int64_t k);
 int tile_gemm_ksum(void* stream, int count, int64_t m, int64_t n, const int64_t* k, float alpha,
                    const float* const* A, const int64_t* lda, const float* const* B, const int64_t* ldb,
                    float beta, float* C, int64_t ldc);
-/* tile_gemm_batch -- independent products of one shape in one launch:
+/* tile_gemm_batch -- independent products in one launch:
  *   C_t = alpha * op(A_t) op(B_t) + beta * C_t,   t < count
- * op() as in tile_gemm; every product shares transA, transB, m, n, k, lda,
- * ldb and ldc. The tied LM head runs one such product per vocab tile
- * (forward z_v = n wte_v^T and weight gradient dwte_v = dz_v^T n; tiled
- * linear layer, pith.science review, "What carries the argument"); the
- * batch fills the GPU where each product alone would not. A, B, C are HOST
- * arrays of `count` DEVICE pointers (read before the call returns); C_t
- * must not overlap C_u (u != t) or any A_u, B_u. Arbitrary (ragged) m, n,
- * k; with leading dimensions that are multiples of 4 and 16-byte aligned
- * operands the loads are 16-byte vectors. No epilogue, no split-K. When
- * beta == 0, C_t is not read. Up to 96 products per launch (more make
- * several launches). Deterministic. count = 0 (or m, n = 0) does nothing;
- * TT_ERR_ARG for negative sizes, a null array or operand, or a leading
- * dimension below its row length. */
-int tile_gemm_batch(void* stream, int count, int transA, int transB, int64_t m, int64_t n, int64_t k,
-                    float alpha, const float* const* A, int64_t lda, const float* const* B, int64_t ldb,
-                    float beta, float* const* C, int64_t ldc);
+ * op() as in tile_gemm; the products share transA, transB, k, alpha and
+ * beta; each has its own m[t], n[t] and leading dimensions lda[t], ldb[t],
+ * ldc[t]. The tied LM head runs one such product per vocab tile (forward
+ * z_v = n wte_v^T and weight gradient dwte_v = dz_v^T n, the last vocab tile
+ * ragged; tiled linear layer, pith.science review, "What carries the
+ * argument"); the batch fills the GPU where each product alone would not.
+ * m, n, A, lda, B, ldb, C, ldc are HOST arrays of `count` entries (device
+ * pointers in A, B, C; read before the call returns). C_t must not overlap
+ * C_u (u != t) or any A_u, B_u. Arbitrary (ragged) sizes; an operand whose
+ * leading dimension is a multiple of 4 and whose base is 16-byte aligned is
+ * loaded 16 bytes at a time, any other 4 (per product and operand);
+ * products with a 4-byte operand are scheduled first. No epilogue, no
+ * split-K. When beta == 0, C_t is not read. Up to 72 products
+ * per launch (more make several launches). Deterministic. Products with
+ * m[t] or n[t] = 0 are skipped; count = 0 does nothing. TT_ERR_ARG for a
+ * negative size, a null array or operand, or a leading dimension below its
+ * row length (or above 2^31 - 1). */
+int tile_gemm_batch(void* stream, int count, int transA, int transB, const int64_t* m, const int64_t* n,
+                    int64_t k, float alpha, const float* const* A, const int64_t* lda,
+                    const float* const* B, const int64_t* ldb, float beta, float* const* C,
+                    const int64_t* ldc);
 
 /* tile_layernorm_fwd -- layer norm over the embedding axis, split into
  * feature tiles (layer list: pith.science review, "What carries the

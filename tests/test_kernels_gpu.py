@@ -142,6 +142,30 @@ def test_gemm_batch(ta, tb, m, n, k, count, beta, ld_pad):
         assert torch.equal(outs[0][t], outs[1][t])
 
 
+@pytest.mark.parametrize("ta,tb,ms,ns,k", [
+    (1, 0, [768] * 6 + [337], [768] * 7, 256),    # dwte_v = dz_v^T nf: ragged last vocab tile (lda 337: scalar loads)
+    (0, 1, [512] * 4, [768] * 3 + [337], 768),    # z_v = nf wte_v^T: ragged last tile (ldc 337)
+    (0, 0, [100, 0, 64, 300], [72, 50, 0, 130], 70),  # empty products are skipped
+    (1, 1, [64] * 80, [32] * 80, 48),             # more products than one launch takes
+])
+def test_gemm_batch_ragged_products(ta, tb, ms, ns, k):
+    """Products of different sizes and leading dimensions in one call against
+    the fp64 products; a vector-load product and a scalar one side by side."""
+    cnt = len(ms)
+    seed = 7 * cnt + k
+    As = [synth.rand_normal(((k, m) if ta else (m, k)), seed + 3 * i) for i, m in enumerate(ms)]
+    Bs = [synth.rand_normal(((n, k) if tb else (k, n)), seed + 3 * i + 1) for i, n in enumerate(ns)]
+    Cs0 = [synth.rand_normal((m, n), seed + 3 * i + 2) for i, (m, n) in enumerate(zip(ms, ns))]
+    Cs = [dev(c) for c in Cs0]
+    tt.tile_gemm_batch(None, ta, tb, ms, ns, k, 1.25, [dev(a) for a in As], [a.shape[1] for a in As],
+                       [dev(b) for b in Bs], [b.shape[1] for b in Bs], 0.5, Cs, list(ns))
+    for t in range(cnt):
+        a, b = As[t], Bs[t]
+        ref = 1.25 * (_op(a.astype(np.float64), ta) @ _op(b.astype(np.float64), tb)) + 0.5 * Cs0[t]
+        bound = 1.25 * (np.abs(_op(a, ta)).astype(np.float64) @ np.abs(_op(b, tb)).astype(np.float64)) * (k + 2) * EPS32
+        assert_close_bound(host(Cs[t]), ref, bound + 4 * EPS32 * np.abs(ref) + 1e-30, f"batch product {t}")
+
+
 def test_gemm_batch_empty_and_errors():
     c0 = synth.rand_normal((64, 64), 6)
     C = dev(c0)

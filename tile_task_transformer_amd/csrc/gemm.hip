@@ -45,6 +45,7 @@
 // unaligned pointers) select a scalar-load instantiation.
 #include <cstdlib>
 #include <type_traits>
+#include <vector>
 
 #include "common.hpp"
 
@@ -386,28 +387,48 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
 }
 
 // ---- batch: C_t = alpha * op(A_t) op(B_t) + beta * C_t for a list of
-// products that share every size and leading dimension, one launch (the LM
-// head: one product per vocab tile). The blocks of all products form one
-// grid, remapped XCD-contiguously, so each XCD works through a contiguous
-// run of products and keeps their operand panels in its L2.
-constexpr int kBatchMax = 96;  // products per launch (kernel arguments stay under 4 KB)
+// independent products that share transposes, K and the scalars, each with
+// its own m, n and leading dimensions (the LM head: one product per vocab
+// tile, the last one ragged), in one launch. The blocks of all products
+// form one grid, remapped XCD-contiguously, so each XCD works through a
+// contiguous run of products and keeps their operand panels in its L2;
+// each operand of each product loads 16 bytes at a time where its leading
+// dimension and alignment allow, else 4 (chosen per product and operand).
+constexpr int kBatchMax = 72;  // products per launch (kernel arguments stay under 4 KB)
 struct GemmBatch {
   const float* A[kBatchMax];
   const float* B[kBatchMax];
   float* C[kBatchMax];
+  int m[kBatchMax], n[kBatchMax];
+  int lda[kBatchMax], ldb[kBatchMax], ldc[kBatchMax];
+  int first[kBatchMax];                       // first block of each product
+  unsigned va[(kBatchMax + 31) / 32];         // bit t: product t loads A 16 bytes at a time
+  unsigned vb[(kBatchMax + 31) / 32];         // bit t: product t loads B 16 bytes at a time
+  int count;
 };
+static_assert(sizeof(GemmArgs) + sizeof(GemmBatch) <= 4096, "kernel arguments over 4 KB");
 
-template <int BM, int BN, int BK, bool TA, bool TB, bool VA, bool VB>
+template <int BM, int BN, int BK, bool TA, bool TB>
 __global__ __launch_bounds__(256, 2) void gemm_batch_kernel(GemmArgs g, GemmBatch P) {
   __shared__ __attribute__((aligned(16))) float lds[GemmLds<BM, BN, BK, TA, TB>::FLOATS];
-  const int ntile = ((g.m + BM - 1) / BM) * ((g.n + BN - 1) / BN);
   const int b = xcd_contiguous(blockIdx.x, gridDim.x);
-  const int t = b / ntile;
+  int t = 0;  // the product owning block b (uniform)
+  while (t + 1 < P.count && P.first[t + 1] <= b) ++t;
   GemmArgs h = g;
+  h.m = P.m[t];
+  h.n = P.n[t];
   h.A = P.A[t];
   h.B = P.B[t];
   h.C = P.C[t];
-  gemm_block<BM, BN, BK, TA, TB, VA, VB, false>(h, b - t * ntile, lds);
+  h.lda = P.lda[t];
+  h.ldb = P.ldb[t];
+  h.ldc = P.ldc[t];
+  const bool va = (P.va[t >> 5] >> (t & 31)) & 1u, vb = (P.vb[t >> 5] >> (t & 31)) & 1u;
+  const int lb = b - P.first[t];
+  if (va && vb) gemm_block<BM, BN, BK, TA, TB, true, true, false>(h, lb, lds);
+  else if (vb) gemm_block<BM, BN, BK, TA, TB, false, true, false>(h, lb, lds);
+  else if (va) gemm_block<BM, BN, BK, TA, TB, true, false, false>(h, lb, lds);
+  else gemm_block<BM, BN, BK, TA, TB, false, false, false>(h, lb, lds);
 }
 
 // Sum of the split-K slices in slice order, then the epilogue.
@@ -756,18 +777,11 @@ __global__ __launch_bounds__(256, 2) void gemm_ksum_kernel(KsumArgs P) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-template <int BM, int BN, int BK, bool TA, bool TB>
-void launch_batch_v(const GemmArgs& g, const GemmBatch& P, int count, bool vec, hipStream_t s) {
-  const int64_t ntile = ((g.m + BM - 1) / BM) * (int64_t)((g.n + BN - 1) / BN);
-  const dim3 grid((unsigned)(ntile * count)), block(256);
-  if (vec) hipLaunchKernelGGL((gemm_batch_kernel<BM, BN, BK, TA, TB, true, true>), grid, block, 0, s, g, P);
-  else hipLaunchKernelGGL((gemm_batch_kernel<BM, BN, BK, TA, TB, false, false>), grid, block, 0, s, g, P);
-}
-
 template <bool TA, bool TB>
-void launch_batch_t(const GemmArgs& g, const GemmBatch& P, int count, bool big, bool vec, hipStream_t s) {
-  if (big) launch_batch_v<128, 128, 16, TA, TB>(g, P, count, vec, s);
-  else launch_batch_v<64, 64, 32, TA, TB>(g, P, count, vec, s);
+void launch_batch(const GemmArgs& g, const GemmBatch& P, int blocks, bool big, hipStream_t s) {
+  const dim3 grid((unsigned)blocks), block(256);
+  if (big) hipLaunchKernelGGL((gemm_batch_kernel<128, 128, 16, TA, TB>), grid, block, 0, s, g, P);
+  else hipLaunchKernelGGL((gemm_batch_kernel<64, 64, 32, TA, TB>), grid, block, 0, s, g, P);
 }
 
 }  // namespace
@@ -891,45 +905,77 @@ extern "C" int tile_gemm_ksum(void* stream, int count, int64_t m, int64_t n, con
   return TT_OK;
 }
 
-extern "C" int tile_gemm_batch(void* stream, int count, int transA, int transB, int64_t m, int64_t n, int64_t k,
-                               float alpha, const float* const* A, int64_t lda, const float* const* B, int64_t ldb,
-                               float beta, float* const* C, int64_t ldc) {
+extern "C" int tile_gemm_batch(void* stream, int count, int transA, int transB, const int64_t* m, const int64_t* n,
+                               int64_t k, float alpha, const float* const* A, const int64_t* lda,
+                               const float* const* B, const int64_t* ldb, float beta, float* const* C,
+                               const int64_t* ldc) {
   using tt::fail;
-  if (count < 0 || m < 0 || n < 0 || k < 0) return fail(TT_ERR_ARG, "tile_gemm_batch: negative count or size");
-  if (count == 0 || m == 0 || n == 0) return TT_OK;
-  if (m > INT32_MAX || n > INT32_MAX || k > INT32_MAX) return fail(TT_ERR_ARG, "tile_gemm_batch: size exceeds int32");
-  if (!A || !B || !C) return fail(TT_ERR_ARG, "tile_gemm_batch: null array");
-  if (ldc < n) return fail(TT_ERR_ARG, "tile_gemm_batch: ldc < n");
-  if (k > 0 && lda < (transA ? m : k)) return fail(TT_ERR_ARG, "tile_gemm_batch: lda too small");
-  if (k > 0 && ldb < (transB ? k : n)) return fail(TT_ERR_ARG, "tile_gemm_batch: ldb too small");
-  bool vec = k > 0 && lda % 4 == 0 && ldb % 4 == 0;
+  if (count < 0 || k < 0) return fail(TT_ERR_ARG, "tile_gemm_batch: negative count or k");
+  if (count == 0) return TT_OK;
+  if (k > INT32_MAX) return fail(TT_ERR_ARG, "tile_gemm_batch: k exceeds int32");
+  if (!m || !n || !A || !lda || !B || !ldb || !C || !ldc) return fail(TT_ERR_ARG, "tile_gemm_batch: null array");
   for (int t = 0; t < count; ++t) {
-    if (!C[t] || (k > 0 && (!A[t] || !B[t]))) return fail(TT_ERR_ARG, "tile_gemm_batch: null operand in product %d", t);
-    if (k > 0) vec = vec && aligned16(A[t]) && aligned16(B[t]);
+    if (m[t] < 0 || n[t] < 0 || m[t] > INT32_MAX || n[t] > INT32_MAX)
+      return fail(TT_ERR_ARG, "tile_gemm_batch: bad size of product %d", t);
+    if (m[t] == 0 || n[t] == 0) continue;
+    if (!C[t] || ldc[t] < n[t] || ldc[t] > INT32_MAX) return fail(TT_ERR_ARG, "tile_gemm_batch: bad C of product %d", t);
+    if (k > 0 && (!A[t] || !B[t] || lda[t] < (transA ? m[t] : k) || ldb[t] < (transB ? k : n[t]) ||
+                  lda[t] > INT32_MAX || ldb[t] > INT32_MAX))
+      return fail(TT_ERR_ARG, "tile_gemm_batch: bad operand of product %d", t);
   }
   hipStream_t s = tt::as_stream(stream);
   // the plan tile_gemm would pick if the products were one C: 128x128x16
   // blocks when there are >= 512 of them, else 64x64x32 (no split-K)
-  const int64_t b128 = ((m + 127) / 128) * ((n + 127) / 128);
-  const bool big = b128 * count >= 512;
-  const int64_t ntile = big ? b128 : ((m + 63) / 64) * ((n + 63) / 64);
-  // grid.x * 256 work-items must stay below 2^32
-  const int64_t per_launch = std::min<int64_t>(kBatchMax, (int64_t)(UINT32_MAX / 256) / ntile);
-  if (per_launch < 1) return fail(TT_ERR_SHAPE, "tile_gemm_batch: product too large for one launch");
-  GemmArgs g{(int)m, (int)n, (int)k, alpha, beta, nullptr, nullptr, nullptr, lda, ldb, ldc, TT_EPI_NONE, nullptr,
+  int64_t b128 = 0;
+  for (int t = 0; t < count; ++t) b128 += ((m[t] + 127) / 128) * ((n[t] + 127) / 128);
+  const bool big = b128 >= 512;
+  const int bm = big ? 128 : 64, bn = bm;
+  GemmArgs g{0, 0, (int)k, alpha, beta, nullptr, nullptr, nullptr, 0, 0, 0, TT_EPI_NONE, nullptr,
              nullptr, 0, nullptr, 0, nullptr, 1, (int)k};
-  for (int t0 = 0; t0 < count; t0 += (int)per_launch) {
-    const int c = (int)std::min<int64_t>(per_launch, count - t0);
+  // products whose loads are scalar (a ragged tile's odd leading dimension)
+  // run slower blocks: they go first in the grid, so the hardware starts
+  // them first and the rest fill in around them (longest first)
+  auto vec_a = [&](int t) { return k > 0 && lda[t] % 4 == 0 && aligned16(A[t]); };
+  auto vec_b = [&](int t) { return k > 0 && ldb[t] % 4 == 0 && aligned16(B[t]); };
+  auto vec_ok = [&](int t) { return vec_a(t) && vec_b(t); };
+  std::vector<int> order;
+  for (int t = 0; t < count; ++t)
+    if (!vec_ok(t)) order.push_back(t);
+  for (int t = 0; t < count; ++t)
+    if (vec_ok(t)) order.push_back(t);
+  // grid.x * 256 work-items must stay below 2^32
+  const int64_t max_blocks = (int64_t)(UINT32_MAX / 256);
+  int o = 0;
+  while (o < count) {
     GemmBatch P{};
-    for (int u = 0; u < c; ++u) {
-      P.A[u] = A[t0 + u];
-      P.B[u] = B[t0 + u];
-      P.C[u] = C[t0 + u];
+    int64_t blocks = 0;
+    while (o < count && P.count < kBatchMax) {
+      const int t = order[o];
+      const int64_t nb = m[t] == 0 || n[t] == 0 ? 0 : ((m[t] + bm - 1) / bm) * ((n[t] + bn - 1) / bn);
+      if (nb > max_blocks) return fail(TT_ERR_SHAPE, "tile_gemm_batch: product %d too large for one launch", t);
+      if (blocks + nb > max_blocks) break;
+      if (nb > 0) {
+        const int c = P.count++;
+        P.A[c] = A[t];
+        P.B[c] = B[t];
+        P.C[c] = C[t];
+        P.m[c] = (int)m[t];
+        P.n[c] = (int)n[t];
+        P.lda[c] = (int)lda[t];
+        P.ldb[c] = (int)ldb[t];
+        P.ldc[c] = (int)ldc[t];
+        P.first[c] = (int)blocks;
+        if (vec_a(t)) P.va[c >> 5] |= 1u << (c & 31);
+        if (vec_b(t)) P.vb[c >> 5] |= 1u << (c & 31);
+        blocks += nb;
+      }
+      ++o;
     }
-    if (!transA && !transB) launch_batch_t<false, false>(g, P, c, big, vec, s);
-    else if (!transA && transB) launch_batch_t<false, true>(g, P, c, big, vec, s);
-    else if (transA && !transB) launch_batch_t<true, false>(g, P, c, big, vec, s);
-    else launch_batch_t<true, true>(g, P, c, big, vec, s);
+    if (P.count == 0) continue;
+    if (!transA && !transB) launch_batch<false, false>(g, P, (int)blocks, big, s);
+    else if (!transA && transB) launch_batch<false, true>(g, P, (int)blocks, big, s);
+    else if (transA && !transB) launch_batch<true, false>(g, P, (int)blocks, big, s);
+    else launch_batch<true, true>(g, P, (int)blocks, big, s);
     if (int rc = tt::launch_status("tile_gemm_batch")) return rc;
   }
   return TT_OK;

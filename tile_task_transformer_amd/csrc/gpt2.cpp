@@ -130,13 +130,13 @@ int submit_gemm(tt_ctx* ctx, const char* label, const Gemm& q) {
   }, 2.0 * m * n * k);
 }
 
-// Independent products of one shape (the tied head's per-vocab-tile GEMMs)
-// as multi-tile tasks over tile_gemm_batch: consecutive products that share
-// transposes, scalars, sizes and leading dimensions form one task (up to
-// 96 products and 1 GiB of output tiles, so the grouping depends on the
-// tiling only); a product of another shape (the ragged last vocab tile)
-// is a task of its own. Each task reads its A and B tiles and writes (beta
-// == 0) or updates its C tiles.
+// Independent products (the tied head's per-vocab-tile GEMMs) as
+// multi-tile tasks over tile_gemm_batch: consecutive products that share
+// transposes, scalars and K form one task (up to 96 products and 1 GiB of
+// output tiles, so the grouping depends on the tiling only; sizes and
+// leading dimensions may differ, e.g. the ragged last vocab tile). Each
+// task reads its A and B tiles and writes (beta == 0) or updates its C
+// tiles.
 int submit_gemm_batch(tt_ctx* ctx, const char* label, const std::vector<Gemm>& qs) {
   constexpr size_t kMaxProducts = 96;
   constexpr int64_t kMaxBytes = int64_t(1) << 30;
@@ -153,41 +153,57 @@ int submit_gemm_batch(tt_ctx* ctx, const char* label, const std::vector<Gemm>& q
   size_t i = 0;
   while (i < qs.size()) {
     const Gemm& q0 = qs[i];
-    const Shape s0 = shape_of(q0);
-    const int64_t cbytes = s0.m * s0.n * (int64_t)sizeof(float);
-    size_t j = i + 1;
-    while (j < qs.size() && j - i < kMaxProducts && (int64_t)(j - i + 1) * cbytes <= kMaxBytes) {
-      const Gemm& q = qs[j];
-      const Shape sh = shape_of(q);
-      if (q.ta != q0.ta || q.tb != q0.tb || q.alpha != q0.alpha || q.beta != q0.beta || q.epi != TT_EPI_NONE ||
-          sh.m != s0.m || sh.n != s0.n || sh.k != s0.k || sh.lda != s0.lda || sh.ldb != s0.ldb || sh.ldc != s0.ldc)
-        break;
-      ++j;
-    }
-    if (j - i == 1 || q0.epi != TT_EPI_NONE) {
+    std::vector<Shape> sh = {shape_of(q0)};
+    if (q0.epi != TT_EPI_NONE) {
       if (int rc = submit_gemm(ctx, label, q0)) return rc;
       ++i;
       continue;
     }
+    int64_t bytes = sh[0].m * sh[0].n * (int64_t)sizeof(float);
+    size_t j = i + 1;
+    while (j < qs.size() && j - i < kMaxProducts) {
+      const Gemm& q = qs[j];
+      const Shape s1 = shape_of(q);
+      const int64_t b1 = s1.m * s1.n * (int64_t)sizeof(float);
+      if (q.ta != q0.ta || q.tb != q0.tb || q.alpha != q0.alpha || q.beta != q0.beta || q.epi != TT_EPI_NONE ||
+          s1.k != sh[0].k || bytes + b1 > kMaxBytes)
+        break;
+      sh.push_back(s1);
+      bytes += b1;
+      ++j;
+    }
     std::vector<Gemm> grp(qs.begin() + i, qs.begin() + j);
     std::vector<Access> acc;
-    for (const Gemm& q : grp) {
+    double flops = 0.0;
+    for (size_t u = 0; u < grp.size(); ++u) {
+      const Gemm& q = grp[u];
+      int64_t cr, cc;
+      q.C.t->mat(q.C.lin, &cr, &cc);
+      if (sh[u].m != cr || sh[u].n != cc)
+        return fail(TT_ERR_SHAPE, "%s: op(A) %lldx%lld does not match C %lldx%lld", label, (long long)sh[u].m,
+                    (long long)sh[u].k, (long long)cr, (long long)cc);
       acc.push_back(R(q.A.t, q.A.lin));
       acc.push_back(R(q.B.t, q.B.lin));
       acc.push_back(q0.beta == 0.f ? W(q.C.t, q.C.lin) : RW(q.C.t, q.C.lin));
+      flops += 2.0 * sh[u].m * sh[u].n * sh[u].k;
     }
-    const double flops = 2.0 * s0.m * s0.n * s0.k * (double)grp.size();
-    int rc = ctx->submit(label, std::move(acc), [grp, s0](hipStream_t s, void*) {
+    int rc = ctx->submit(label, std::move(acc), [grp, sh](hipStream_t s, void*) {
       const size_t c = grp.size();
       std::vector<const float*> A(c), B(c);
       std::vector<float*> C(c);
+      std::vector<int64_t> m(c), n(c), lda(c), ldb(c), ldc(c);
       for (size_t u = 0; u < c; ++u) {
         A[u] = F(grp[u].A.t, grp[u].A.lin);
         B[u] = F(grp[u].B.t, grp[u].B.lin);
         C[u] = F(grp[u].C.t, grp[u].C.lin);
+        m[u] = sh[u].m;
+        n[u] = sh[u].n;
+        lda[u] = sh[u].lda;
+        ldb[u] = sh[u].ldb;
+        ldc[u] = sh[u].ldc;
       }
-      return tile_gemm_batch(s, (int)c, grp[0].ta, grp[0].tb, s0.m, s0.n, s0.k, grp[0].alpha, A.data(), s0.lda,
-                             B.data(), s0.ldb, grp[0].beta, C.data(), s0.ldc);
+      return tile_gemm_batch(s, (int)c, grp[0].ta, grp[0].tb, m.data(), n.data(), sh[0].k, grp[0].alpha, A.data(),
+                             lda.data(), B.data(), ldb.data(), grp[0].beta, C.data(), ldc.data());
     }, flops);
     if (rc) return rc;
     i = j;

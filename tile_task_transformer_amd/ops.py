@@ -53,13 +53,16 @@ def tile_gemm_ksum(stream, m, n, ks, alpha, As, ldas, Bs, ldbs, beta, C, ldc):
                                     i64(ldbs), beta, ptr(C), ldc))
 
 
-def tile_gemm_batch(stream, transA, transB, m, n, k, alpha, As, lda, Bs, ldb, beta, Cs, ldc):
-    """C_t = alpha op(A_t) op(B_t) + beta C_t for equal-length lists of tensors of one shape."""
+def tile_gemm_batch(stream, transA, transB, ms, ns, k, alpha, As, ldas, Bs, ldbs, beta, Cs, ldcs):
+    """C_t = alpha op(A_t) op(B_t) + beta C_t; per-product sizes and leading
+    dimensions as equal-length lists (an int is used for every product)."""
     import ctypes as C_
     cnt = len(Cs)
+    per = lambda x: list(x) if isinstance(x, (list, tuple)) else [x] * cnt  # noqa: E731
+    i64 = lambda xs: (C_.c_int64 * max(cnt, 1))(*[int(x) for x in per(xs)])  # noqa: E731
     ptrs = lambda xs: (C_.c_void_p * max(cnt, 1))(*[ptr(x) for x in xs])  # noqa: E731
-    return check(lib.tile_gemm_batch(stream_handle(stream), cnt, transA, transB, m, n, k, alpha, ptrs(As), lda,
-                                     ptrs(Bs), ldb, beta, ptrs(Cs), ldc))
+    return check(lib.tile_gemm_batch(stream_handle(stream), cnt, transA, transB, i64(ms), i64(ns), k, alpha, ptrs(As),
+                                     i64(ldas), ptrs(Bs), i64(ldbs), beta, ptrs(Cs), i64(ldcs)))
 
 
 def tile_layernorm_fwd(stream, phase, rows, cols, x, ldx, gamma, beta, parts, n_parts, part_stride, stats, y,
