@@ -123,6 +123,9 @@ def class_rooflines(breakdown: dict, s) -> dict:
     return res
 
 
+# entry point of each task class's launches (the rest are tile_gemm)
+KERNEL_OF = {"head": "tile_gemm_batch", "head_dw": "tile_gemm_batch", "head_dx": "tile_gemm_ksum"}
+
 GEMM_SHAPES = {  # label -> (transA, transB, m, n, k, epilogue, beta) in tile terms
     "qkv": lambda r, e, i, h, v: (0, 0, r, h, e, 1, 0.0), "attn_proj": lambda r, e, i, h, v: (0, 0, r, e, h, 3, 0.0),
     "fc": lambda r, e, i, h, v: (0, 0, r, i, e, 5, 0.0), "mlp_proj": lambda r, e, i, h, v: (0, 0, r, e, i, 3, 0.0),
@@ -167,8 +170,32 @@ def tile_classes(w, reps=20, only=None):
         return a.elapsed_time(b) / reps
 
     out = {}
+    # the tied head runs over every vocab tile in one task: z_v = nf wte_v^T
+    # and dwte_v = dz_v^T nf as one tile_gemm_batch launch, dnf = sum_v dz_v
+    # wte_v as one tile_gemm_ksum launch (the last vocab tile ragged)
+    lens = [min(v, s.vocab - v0) for v0 in range(0, s.vocab, v)]
+    head_flops = 2.0 * r * e * s.vocab
+    for label in ("head", "head_dw", "head_dx"):
+        if only and label != only:
+            continue
+        X = rnd(r, e)
+        Z = [rnd(r, n) for n in lens]
+        W = [rnd(n, e) for n in lens]
+        if label == "head":
+            fn = lambda: tt.tile_gemm_batch(st, 0, 1, r, lens, e, 1.0, [X] * len(lens), e, W, e, 0.0, Z, lens)  # noqa
+        elif label == "head_dw":
+            fn = lambda: tt.tile_gemm_batch(st, 1, 0, lens, e, r, 1.0, Z, lens, [X] * len(lens), e, 1.0, W, e)  # noqa
+        else:
+            fn = lambda: tt.tile_gemm_ksum(st, r, e, lens, 1.0, Z, lens, W, [e] * len(lens), 0.0, X, e)  # noqa
+        ms = timed(fn)
+        tf = head_flops / (ms * 1e-3) / 1e12
+        out[label] = {"bound": "mfma", "shape": [r, e, s.vocab, len(lens)], "us": round(ms * 1e3, 1),
+                      "achieved": round(tf, 2), "unit": "TFLOP/s", "frac": round(tf / MFMA_FP32_PEAK, 4)}
+        del X, Z, W
     for label, f in GEMM_SHAPES.items():
         if only and label != only:  # "attn": the attention classes only
+            continue
+        if label in ("head", "head_dw", "head_dx"):
             continue
         ta, tb, m, n, k, epi, beta = f(r, e, i, h, v)
         A = rnd(k, m) if ta else rnd(m, k)
@@ -474,7 +501,8 @@ def main(argv=None):
         "tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_FP32_PEAK, 4),
         "tasks_per_step": model.task_count(), "loss": round(loss, 5),
         "host_submit_ms_per_step": round(1e3 * st["submit_seconds"] / a.steps, 3),
-        "roofline": {"bound": "mfma", "kernel": f"tile_gemm[{dominant}]", "achieved": round(achieved, 2),
+        "roofline": {"bound": "mfma", "kernel": f"{KERNEL_OF.get(dominant, 'tile_gemm')}[{dominant}]",
+                     "achieved": round(achieved, 2),
                      "peak": MFMA_FP32_PEAK, "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP32_PEAK, 4),
                      "traffic": traffic_bytes(a.workload, dominant), "flops_per_launch": per_launch,
                      "avg_launch_ms": round(avg_ms, 4),

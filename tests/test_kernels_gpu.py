@@ -604,6 +604,19 @@ def test_embedding_fwd_bwd():
     assert_rel(host(dp), dh.astype(np.float64).reshape(bt, st, d).sum(0), 1e-6, 1e-6, "dwpe")
 
 
+@pytest.mark.parametrize("rows,vocab", [(1, 5), (17, 3), (4096, 50257), (5000, 40), (65536, 50257)])
+def test_embedding_index_is_a_stable_sort(rows, vocab):
+    """The per-token-tile index (sorted ids, permutation) equals numpy's
+    stable argsort: one row, ragged workgroups, many duplicates, several LDS
+    chunks, the largest tile allowed."""
+    ids = np.random.default_rng(rows).integers(0, vocab, rows).astype(np.int32)
+    srt = torch.empty(rows, dtype=torch.int32, device="cuda")
+    perm = torch.empty(rows, dtype=torch.int32, device="cuda")
+    tt.tile_embedding_index(None, rows, dev(ids), srt, perm)
+    order = np.argsort(ids, kind="stable")
+    assert np.array_equal(perm.cpu().numpy(), order) and np.array_equal(srt.cpu().numpy(), ids[order])
+
+
 def test_embedding_out_of_range_id_gives_nan_row():
     ids = np.array([0, 5, 99, -1], np.int32)
     wte = synth.rand_normal((5, 8), 1)

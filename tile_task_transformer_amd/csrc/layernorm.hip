@@ -226,14 +226,19 @@ __global__ __launch_bounds__(64 * bwd_waves(NV)) void ln_bwd_rows(
 
 }  // namespace
 
-// Column sums of nblk partial rows -> out[c] (+)= sum_b ws[b*ws_ld + c], in a
-// fixed order. One workgroup: 64 columns x 16 row groups; group g sums rows
-// g, g+16, ... (loads issued 4 at a time), then the 16 group sums are added
-// in group order.
+// Column sums of nblk partial rows -> out[c] (+)= sum_b ws[b*ws_ld + ws_off + c],
+// in a fixed order. One workgroup: 64 columns x 16 row groups; group g sums
+// rows g, g+16, ... (loads issued 4 at a time), then the 16 group sums are
+// added in group order. blockIdx.y = 1 does the same for (ws_off2, out2):
+// LayerNorm's dgamma and dbeta in one launch.
 __global__ __launch_bounds__(1024) void colsum_finish(int nblk, int cols, const float* __restrict__ ws,
                                                       int64_t ws_ld, int64_t ws_off, float* __restrict__ out,
-                                                      int accumulate) {
+                                                      int accumulate, int64_t ws_off2, float* __restrict__ out2) {
   __shared__ float red[16][64];
+  if (blockIdx.y == 1) {
+    ws_off = ws_off2;
+    out = out2;
+  }
   const int cl = threadIdx.x & 63, grp = threadIdx.x >> 6;
   const int c = blockIdx.x * 64 + cl;
   float s = 0.f;
@@ -396,9 +401,9 @@ extern "C" int tile_layernorm_bwd(void* stream, int phase, int64_t rows, int64_t
 #undef TT_LNB
   if (rc || phase == TT_LN_PARTIAL) return rc;
   const int nblk = (int)((r + bwd_rows_per_block(c) - 1) / bwd_rows_per_block(c));
-  dim3 grid((c + 63) / 64), block(1024);
-  hipLaunchKernelGGL(colsum_finish, grid, block, 0, s, nblk, c, ws, (int64_t)2 * c, (int64_t)0, dgamma, 1);
-  hipLaunchKernelGGL(colsum_finish, grid, block, 0, s, nblk, c, ws, (int64_t)2 * c, (int64_t)c, dbeta, 1);
+  dim3 grid((c + 63) / 64, 2), block(1024);
+  hipLaunchKernelGGL(colsum_finish, grid, block, 0, s, nblk, c, ws, (int64_t)2 * c, (int64_t)0, dgamma, 1, (int64_t)c,
+                     dbeta);
   return tt::launch_status("tile_layernorm_bwd(colsum)");
 }
 
@@ -462,6 +467,6 @@ extern "C" int tile_reduce_rows(void* stream, int64_t rows, int64_t cols, const 
     if (int rc = tt::launch_status("tile_reduce_rows")) return rc;
   }
   hipLaunchKernelGGL(colsum_finish, dim3((c + 63) / 64), dim3(1024), 0, s, nblk, c, ws, (int64_t)c, (int64_t)0, out,
-                     beta);
+                     beta, (int64_t)0, out);
   return tt::launch_status("tile_reduce_rows(finish)");
 }

@@ -167,11 +167,18 @@ __global__ void emb_fwd(int rows, int cols, const int32_t* __restrict__ ids, int
   tt::st4<VEC>(out, ldo, r, c, cols, o);
 }
 
-// stable rank of each id: number of ids that are smaller, or equal and earlier
+// stable rank of each id: number of ids that are smaller, or equal and earlier.
+// A workgroup ranks kIdxTok ids; each id's comparisons are split over
+// kIdxPart consecutive lanes (every kIdxPart-th id of the tile), whose
+// integer counts are summed with shuffles, so the launch has rows / 16
+// workgroups instead of rows / 256 and the result does not depend on the
+// split (integer sums).
+constexpr int kIdxTok = 16, kIdxPart = 16;
 __global__ __launch_bounds__(256) void emb_index(int rows, const int32_t* __restrict__ ids, int32_t* __restrict__ sorted,
                                                  int32_t* __restrict__ perm) {
   __shared__ int32_t chunk[2048];
-  const int r = blockIdx.x * 256 + threadIdx.x;
+  const int part = threadIdx.x % kIdxPart;
+  const int r = blockIdx.x * kIdxTok + threadIdx.x / kIdxPart;
   const int32_t me = r < rows ? ids[r] : 0;
   int rank = 0;
   for (int base = 0; base < rows; base += 2048) {
@@ -180,12 +187,14 @@ __global__ __launch_bounds__(256) void emb_index(int rows, const int32_t* __rest
     for (int i = threadIdx.x; i < n; i += 256) chunk[i] = ids[base + i];
     __syncthreads();
     if (r < rows)
-      for (int i = 0; i < n; ++i) {
+      for (int i = part; i < n; i += kIdxPart) {
         const int32_t o = chunk[i];
         rank += (o < me) || (o == me && base + i < r);
       }
   }
-  if (r < rows) {
+#pragma unroll
+  for (int o = kIdxPart / 2; o > 0; o >>= 1) rank += __shfl_xor(rank, o, kIdxPart);
+  if (r < rows && part == 0) {
     sorted[rank] = me;
     perm[rank] = r;
   }
@@ -350,8 +359,8 @@ extern "C" int tile_embedding_index(void* stream, int64_t rows, const int32_t* i
   if (rows < 0 || rows > 65536) return fail(TT_ERR_ARG, "tile_embedding_index: rows must be in [0, 65536]");
   if (rows == 0) return TT_OK;
   if (!ids || !sorted_ids || !perm) return fail(TT_ERR_ARG, "tile_embedding_index: null pointer");
-  hipLaunchKernelGGL(emb_index, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, tt::as_stream(stream), (int)rows,
-                     ids, sorted_ids, perm);
+  hipLaunchKernelGGL(emb_index, dim3((unsigned)((rows + kIdxTok - 1) / kIdxTok)), dim3(256), 0, tt::as_stream(stream),
+                     (int)rows, ids, sorted_ids, perm);
   return tt::launch_status("tile_embedding_index");
 }
 
