@@ -177,6 +177,26 @@ def test_gemm_batch_empty_and_errors():
         tt.tile_gemm_batch(None, 0, 0, 64, 64, 32, 1.0, [C], 16, [C], 64, 0.0, [C], 64)
 
 
+def test_gemm_gelu_epilogue_over_the_whole_range():
+    """GELU and GELU' epilogues on pre-activations from -20 to 20 (tanh
+    saturated at both ends), around 0 and at tiny values, against the fp64
+    oracle: the products are exact (k = 1, B = 1), so only the epilogue's
+    arithmetic is measured."""
+    u = np.concatenate([np.linspace(-20, 20, 4001), np.linspace(-1e-3, 1e-3, 201), [0.0, 1e-30, -1e-30, 3e-8]])
+    u = u.astype(np.float32)
+    m = u.size
+    A, B = dev(u.reshape(m, 1)), dev(np.ones((1, 1), np.float32))
+    C, aux = empty((m, 1)), empty((m, 1))
+    tt.tile_gemm(None, 0, 0, m, 1, 1, 1.0, A, 1, B, 1, 0.0, C, 1, tt.TT_EPI_GELU, None, None, 0, aux, 1)
+    u64 = u.astype(np.float64)
+    assert np.array_equal(host(aux)[:, 0], u64)
+    assert_rel(host(C)[:, 0], og.gelu(u64), 2e-6, 2e-6, "gelu over the range")
+    G = dev(u.reshape(m, 1))
+    tt.tile_gemm(None, 0, 0, m, 1, 1, 1.0, dev(np.ones((m, 1), np.float32)), 1, B, 1, 0.0, C, 1, tt.TT_EPI_GELU_BWD,
+                 None, None, 0, G, 1)
+    assert_rel(host(C)[:, 0], og.gelu_grad(u64), 2e-6, 2e-6, "gelu' over the range")
+
+
 @pytest.mark.parametrize("ld_pad", [0, 1, 4])
 def test_gemm_leading_dims_and_views(ld_pad):
     m, n, k = 96, 72, 40
