@@ -140,6 +140,19 @@ int tile_gemm_batch(void* stream, int count, int transA, int transB, const int64
                     int64_t k, float alpha, const float* const* A, const int64_t* lda,
                     const float* const* B, const int64_t* ldb, float beta, float* const* C,
                     const int64_t* ldc);
+/* tile_gemm_batch with a device workspace (caller-owned, not used
+ * concurrently by another launch): when the products together have few
+ * 128x128 blocks (at most 144) and K is long (>= 2048) -- the attention
+ * block's q, k and v weight gradients, K = tokens -- K is split over
+ * workgroups that write partial sums to the workspace, and one more kernel
+ * adds them in slice order for every product (same result on every run).
+ * tile_gemm_batch_workspace(count, m, n, k) is the size that enables the
+ * split (0 = never splits); a smaller workspace disables it. */
+int tile_gemm_batch_ws(void* stream, int count, int transA, int transB, const int64_t* m, const int64_t* n,
+                       int64_t k, float alpha, const float* const* A, const int64_t* lda,
+                       const float* const* B, const int64_t* ldb, float beta, float* const* C,
+                       const int64_t* ldc, void* workspace, size_t workspace_bytes);
+size_t tile_gemm_batch_workspace(int count, const int64_t* m, const int64_t* n, int64_t k);
 
 /* tile_layernorm_fwd -- layer norm over the embedding axis, split into
  * feature tiles (layer list: pith.science review, "What carries the

@@ -166,6 +166,40 @@ def test_gemm_batch_ragged_products(ta, tb, ms, ns, k):
         assert_close_bound(host(Cs[t]), ref, bound + 4 * EPS32 * np.abs(ref) + 1e-30, f"batch product {t}")
 
 
+@pytest.mark.parametrize("ta,tb,ms,ns,k,beta", [
+    (1, 0, [768] * 3, [768] * 3, 4096, 1.0),        # the q, k, v weight gradients of one layer
+    (1, 0, [700, 100], [300, 72], 5000, 0.0),       # ragged products, K not a multiple of the slice
+    (0, 1, [256, 128, 384], [128, 256, 96], 2304, 0.5),
+])
+def test_gemm_batch_split_k(ta, tb, ms, ns, k, beta):
+    """Batched split-K (few blocks, long K, with a workspace) against the
+    fp64 products; bitwise equal across runs; a workspace too small to split
+    gives a result within the same bound."""
+    cnt = len(ms)
+    need = tt.tile_gemm_batch_workspace(ms, ns, k)
+    assert need > 0
+    seed = 11 * cnt + k
+    As = [synth.rand_normal(((k, m) if ta else (m, k)), seed + 3 * i) for i, m in enumerate(ms)]
+    Bs = [synth.rand_normal(((n, k) if tb else (k, n)), seed + 3 * i + 1) for i, n in enumerate(ns)]
+    Cs0 = [synth.rand_normal((m, n), seed + 3 * i + 2) for i, (m, n) in enumerate(zip(ms, ns))]
+    dA, dB = [dev(a) for a in As], [dev(b) for b in Bs]
+    outs = []
+    for wsb in (need, need, 1024):
+        ws = torch.empty(max(wsb // 4, 1), device="cuda")
+        Cs = [dev(c) for c in Cs0]
+        tt.tile_gemm_batch_ws(None, ta, tb, ms, ns, k, 0.75, dA, [a.shape[1] for a in As], dB, [b.shape[1] for b in Bs],
+                              beta, Cs, list(ns), ws, wsb)
+        outs.append(Cs)
+    for t in range(cnt):
+        a, b = As[t], Bs[t]
+        ref = 0.75 * (_op(a.astype(np.float64), ta) @ _op(b.astype(np.float64), tb)) + beta * Cs0[t]
+        bound = 0.75 * (np.abs(_op(a, ta)).astype(np.float64) @ np.abs(_op(b, tb)).astype(np.float64)) * (k + 2) * EPS32
+        for run in (0, 2):
+            assert_close_bound(host(outs[run][t]), ref, bound + 4 * EPS32 * np.abs(ref) + 1e-30,
+                               f"split batch product {t} run {run}")
+        assert torch.equal(outs[0][t], outs[1][t])
+
+
 def test_gemm_batch_empty_and_errors():
     c0 = synth.rand_normal((64, 64), 6)
     C = dev(c0)

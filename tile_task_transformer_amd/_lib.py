@@ -97,6 +97,8 @@ SIGNATURES = {
     "tile_gemm_workspace": (SZ, [I64, I64, I64]),
     "tile_gemm_ksum": (I, [P, I, I64, I64, P, F, P, P, P, P, F, P, I64]),
     "tile_gemm_batch": (I, [P, I, I, I, P, P, I64, F, P, P, P, P, F, P, P]),
+    "tile_gemm_batch_ws": (I, [P, I, I, I, P, P, I64, F, P, P, P, P, F, P, P, P, SZ]),
+    "tile_gemm_batch_workspace": (SZ, [I, P, P, I64]),
     "tile_xentropy_multi": (I, [P, I, I, I64, P, P, P, P, P, P, I64, P, F]),
     "tile_layernorm_fwd": (I, [P, I, I64, I64, P, I64, P, P, P, I64, I64, P, P, I64, F]),
     "tile_layernorm_bwd": (I, [P, I, I64, I64, I64, P, I64, P, I64, P, P, P, I64, I64, P, I64, I, P, P, P]),

@@ -419,7 +419,12 @@ struct GemmBatch {
 };
 static_assert(sizeof(GemmArgs) + sizeof(GemmBatch) <= 4096, "kernel arguments over 4 KB");
 
-template <int BM, int BN, int BK, bool TA, bool TB>
+// With split-K (g.splits > 1) every product's blocks come in g.splits K
+// ranges; the partial sums of product t go to the workspace region that
+// starts at its first block times BM * BN floats (a region of (blocks of t)
+// x BM x BN floats holds its splits x m x n partials), and
+// gemm_batch_finish adds them in slice order.
+template <int BM, int BN, int BK, bool TA, bool TB, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void gemm_batch_kernel(GemmArgs g, GemmBatch P) {
   __shared__ __attribute__((aligned(16))) float lds[GemmLds<BM, BN, BK, TA, TB>::FLOATS];
   const int b = xcd_contiguous(blockIdx.x, gridDim.x);
@@ -434,19 +439,33 @@ __global__ __launch_bounds__(256, 2) void gemm_batch_kernel(GemmArgs g, GemmBatc
   h.lda = P.lda[t];
   h.ldb = P.ldb[t];
   h.ldc = P.ldc[t];
+  if (SPLIT) h.ws = g.ws + (int64_t)P.first[t] * (BM * BN);
   const bool va = (P.va[t >> 5] >> (t & 31)) & 1u, vb = (P.vb[t >> 5] >> (t & 31)) & 1u;
   const int lb = b - P.first[t];
-  if (va && vb) gemm_block<BM, BN, BK, TA, TB, true, true, false>(h, lb, lds);
-  else if (vb) gemm_block<BM, BN, BK, TA, TB, false, true, false>(h, lb, lds);
-  else if (va) gemm_block<BM, BN, BK, TA, TB, true, false, false>(h, lb, lds);
-  else gemm_block<BM, BN, BK, TA, TB, false, false, false>(h, lb, lds);
+  if (va && vb) gemm_block<BM, BN, BK, TA, TB, true, true, SPLIT>(h, lb, lds);
+  else if (vb) gemm_block<BM, BN, BK, TA, TB, false, true, SPLIT>(h, lb, lds);
+  else if (va) gemm_block<BM, BN, BK, TA, TB, true, false, SPLIT>(h, lb, lds);
+  else gemm_block<BM, BN, BK, TA, TB, false, false, SPLIT>(h, lb, lds);
+}
+
+// split-K finish of every product of a batch launch (blockIdx.y = product)
+template <int BM, int BN, int VEC>
+__global__ __launch_bounds__(256) void gemm_batch_finish(GemmArgs g, GemmBatch P) {
+  const int t = blockIdx.y;
+  GemmArgs h = g;
+  h.m = P.m[t];
+  h.n = P.n[t];
+  h.C = P.C[t];
+  h.ldc = P.ldc[t];
+  h.ws = g.ws + (int64_t)P.first[t] * (BM * BN);
+  split_finish<VEC>(h);
 }
 
 // Sum of the split-K slices in slice order, then the epilogue.
 // Each thread sums VEC consecutive elements; the loads of up to 8 slices are
 // issued together, the additions stay in slice order.
 template <int VEC>
-__global__ __launch_bounds__(256) void gemm_split_finish(GemmArgs g) {
+__device__ __forceinline__ void split_finish(const GemmArgs& g) {
   using V = typename std::conditional<VEC == 4, f32x4, float>::type;
   const int64_t i = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) * VEC;
   const int64_t mn = (int64_t)g.m * g.n;
@@ -469,6 +488,11 @@ __global__ __launch_bounds__(256) void gemm_split_finish(GemmArgs g) {
   } else {
     epilogue_store(g, (int)(i / g.n), (int)(i % g.n), g.alpha * s);
   }
+}
+
+template <int VEC>
+__global__ __launch_bounds__(256) void gemm_split_finish(GemmArgs g) {
+  split_finish<VEC>(g);
 }
 
 template <int BM, int BN, int BK, bool TA, bool TB, bool SPLIT>
@@ -788,11 +812,50 @@ __global__ __launch_bounds__(256, 2) void gemm_ksum_kernel(KsumArgs P) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// plans of a batch launch: 128x128x16 / 64x64x32 blocks, or 128x128x32 with split-K
+enum BatchPlan { kBatchBig, kBatchSmall, kBatchSplit };
+
 template <bool TA, bool TB>
-void launch_batch(const GemmArgs& g, const GemmBatch& P, int blocks, bool big, hipStream_t s) {
+int launch_batch(const GemmArgs& g, const GemmBatch& P, int blocks, BatchPlan plan, int64_t max_mn, bool vec_mn,
+                 hipStream_t s) {
   const dim3 grid((unsigned)blocks), block(256);
-  if (big) hipLaunchKernelGGL((gemm_batch_kernel<128, 128, 16, TA, TB>), grid, block, 0, s, g, P);
-  else hipLaunchKernelGGL((gemm_batch_kernel<64, 64, 32, TA, TB>), grid, block, 0, s, g, P);
+  if (plan == kBatchBig) hipLaunchKernelGGL((gemm_batch_kernel<128, 128, 16, TA, TB, false>), grid, block, 0, s, g, P);
+  else if (plan == kBatchSmall) hipLaunchKernelGGL((gemm_batch_kernel<64, 64, 32, TA, TB, false>), grid, block, 0, s, g, P);
+  else hipLaunchKernelGGL((gemm_batch_kernel<128, 128, 32, TA, TB, true>), grid, block, 0, s, g, P);
+  if (int rc = tt::launch_status("tile_gemm_batch")) return rc;
+  if (plan != kBatchSplit) return TT_OK;
+  // the workspace is 256-byte aligned and every product's region starts at
+  // a multiple of 128 x 128 floats
+  if (vec_mn)
+    hipLaunchKernelGGL((gemm_batch_finish<128, 128, 4>), dim3((unsigned)((max_mn / 4 + 255) / 256), (unsigned)P.count),
+                       block, 0, s, g, P);
+  else
+    hipLaunchKernelGGL((gemm_batch_finish<128, 128, 1>), dim3((unsigned)((max_mn + 255) / 256), (unsigned)P.count),
+                       block, 0, s, g, P);
+  return tt::launch_status("tile_gemm_batch(split finish)");
+}
+
+// split count for a batch whose products have b128 128x128 blocks in all
+// and share k: as plan_for (long K, few blocks; workgroup count just under
+// a multiple of the CU count); 1 = no split
+int batch_splits(int64_t b128, int64_t k, size_t ws_bytes, int64_t* chunk_out) {
+  if (k < 2048 || b128 > 144 || ws_bytes == 0) return 1;
+  int best_s = 1;
+  double best_bal = 0.0;
+  for (int s = 2; s <= 8; ++s) {
+    int64_t chunk = (k + s - 1) / s;
+    chunk = (chunk + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
+    const int64_t sa = (k + chunk - 1) / chunk;
+    if (chunk < 256 || (size_t)(b128 * sa) * 128 * 128 * sizeof(float) > ws_bytes) continue;
+    const int64_t nwg = b128 * sa;
+    const double bal = (double)nwg / (double)(((nwg + kCUs - 1) / kCUs) * kCUs);
+    if (bal > best_bal + 0.01) {
+      best_bal = bal;
+      best_s = (int)sa;
+      *chunk_out = chunk;
+    }
+  }
+  return best_s;
 }
 
 }  // namespace
@@ -916,15 +979,26 @@ extern "C" int tile_gemm_ksum(void* stream, int count, int64_t m, int64_t n, con
   return TT_OK;
 }
 
-extern "C" int tile_gemm_batch(void* stream, int count, int transA, int transB, const int64_t* m, const int64_t* n,
-                               int64_t k, float alpha, const float* const* A, const int64_t* lda,
-                               const float* const* B, const int64_t* ldb, float beta, float* const* C,
-                               const int64_t* ldc) {
+extern "C" size_t tile_gemm_batch_workspace(int count, const int64_t* m, const int64_t* n, int64_t k) {
+  if (count <= 0 || !m || !n || k <= 0) return 0;
+  int64_t b128 = 0;
+  for (int t = 0; t < count; ++t)
+    if (m[t] > 0 && n[t] > 0) b128 += ((m[t] + 127) / 128) * ((n[t] + 127) / 128);
+  int64_t chunk = k;
+  const int sp = batch_splits(b128, k, (size_t)-1, &chunk);
+  return sp > 1 ? (size_t)(b128 * sp) * 128 * 128 * sizeof(float) : 0;
+}
+
+extern "C" int tile_gemm_batch_ws(void* stream, int count, int transA, int transB, const int64_t* m,
+                                  const int64_t* n, int64_t k, float alpha, const float* const* A, const int64_t* lda,
+                                  const float* const* B, const int64_t* ldb, float beta, float* const* C,
+                                  const int64_t* ldc, void* workspace, size_t workspace_bytes) {
   using tt::fail;
   if (count < 0 || k < 0) return fail(TT_ERR_ARG, "tile_gemm_batch: negative count or k");
   if (count == 0) return TT_OK;
   if (k > INT32_MAX) return fail(TT_ERR_ARG, "tile_gemm_batch: k exceeds int32");
   if (!m || !n || !A || !lda || !B || !ldb || !C || !ldc) return fail(TT_ERR_ARG, "tile_gemm_batch: null array");
+  if (workspace_bytes > 0 && !workspace) return fail(TT_ERR_ARG, "tile_gemm_batch: null workspace");
   for (int t = 0; t < count; ++t) {
     if (m[t] < 0 || n[t] < 0 || m[t] > INT32_MAX || n[t] > INT32_MAX)
       return fail(TT_ERR_ARG, "tile_gemm_batch: bad size of product %d", t);
@@ -935,14 +1009,18 @@ extern "C" int tile_gemm_batch(void* stream, int count, int transA, int transB, 
       return fail(TT_ERR_ARG, "tile_gemm_batch: bad operand of product %d", t);
   }
   hipStream_t s = tt::as_stream(stream);
-  // the plan tile_gemm would pick if the products were one C: 128x128x16
-  // blocks when there are >= 512 of them, else 64x64x32 (no split-K)
+  // the plan tile_gemm would pick if the products were one C: split-K over
+  // 128x128x32 blocks for few blocks and a long K (with a workspace),
+  // 128x128x16 blocks when there are >= 512 of them, else 64x64x32
   int64_t b128 = 0;
-  for (int t = 0; t < count; ++t) b128 += ((m[t] + 127) / 128) * ((n[t] + 127) / 128);
-  const bool big = b128 >= 512;
-  const int bm = big ? 128 : 64, bn = bm;
+  for (int t = 0; t < count; ++t)
+    if (m[t] > 0 && n[t] > 0) b128 += ((m[t] + 127) / 128) * ((n[t] + 127) / 128);
+  int64_t chunk = k;
+  const int splits = batch_splits(b128, k, workspace ? workspace_bytes : 0, &chunk);
+  const BatchPlan plan = splits > 1 ? kBatchSplit : b128 >= 512 ? kBatchBig : kBatchSmall;
+  const int bm = plan == kBatchSmall ? 64 : 128, bn = bm;
   GemmArgs g{0, 0, (int)k, alpha, beta, nullptr, nullptr, nullptr, 0, 0, 0, TT_EPI_NONE, nullptr,
-             nullptr, 0, nullptr, 0, nullptr, 1, (int)k};
+             nullptr, 0, nullptr, 0, (float*)workspace, splits, (int)chunk};
   // products whose loads are scalar (a ragged tile's odd leading dimension)
   // run slower blocks: they go first in the grid, so the hardware starts
   // them first and the rest fill in around them (longest first)
@@ -959,10 +1037,12 @@ extern "C" int tile_gemm_batch(void* stream, int count, int transA, int transB, 
   int o = 0;
   while (o < count) {
     GemmBatch P{};
-    int64_t blocks = 0;
+    int64_t blocks = 0, max_mn = 0;
+    bool vec_mn = true;
     while (o < count && P.count < kBatchMax) {
       const int t = order[o];
-      const int64_t nb = m[t] == 0 || n[t] == 0 ? 0 : ((m[t] + bm - 1) / bm) * ((n[t] + bn - 1) / bn);
+      const int64_t nb =
+          m[t] == 0 || n[t] == 0 ? 0 : ((m[t] + bm - 1) / bm) * ((n[t] + bn - 1) / bn) * (int64_t)splits;
       if (nb > max_blocks) return fail(TT_ERR_SHAPE, "tile_gemm_batch: product %d too large for one launch", t);
       if (blocks + nb > max_blocks) break;
       if (nb > 0) {
@@ -979,15 +1059,25 @@ extern "C" int tile_gemm_batch(void* stream, int count, int transA, int transB, 
         if (vec_a(t)) P.va[c >> 5] |= 1u << (c & 31);
         if (vec_b(t)) P.vb[c >> 5] |= 1u << (c & 31);
         blocks += nb;
+        max_mn = std::max<int64_t>(max_mn, m[t] * n[t]);
+        vec_mn = vec_mn && (m[t] * n[t]) % 4 == 0;
       }
       ++o;
     }
     if (P.count == 0) continue;
-    if (!transA && !transB) launch_batch<false, false>(g, P, (int)blocks, big, s);
-    else if (!transA && transB) launch_batch<false, true>(g, P, (int)blocks, big, s);
-    else if (transA && !transB) launch_batch<true, false>(g, P, (int)blocks, big, s);
-    else launch_batch<true, true>(g, P, (int)blocks, big, s);
-    if (int rc = tt::launch_status("tile_gemm_batch")) return rc;
+    int rc;
+    if (!transA && !transB) rc = launch_batch<false, false>(g, P, (int)blocks, plan, max_mn, vec_mn, s);
+    else if (!transA && transB) rc = launch_batch<false, true>(g, P, (int)blocks, plan, max_mn, vec_mn, s);
+    else if (transA && !transB) rc = launch_batch<true, false>(g, P, (int)blocks, plan, max_mn, vec_mn, s);
+    else rc = launch_batch<true, true>(g, P, (int)blocks, plan, max_mn, vec_mn, s);
+    if (rc) return rc;
   }
   return TT_OK;
+}
+
+extern "C" int tile_gemm_batch(void* stream, int count, int transA, int transB, const int64_t* m, const int64_t* n,
+                               int64_t k, float alpha, const float* const* A, const int64_t* lda,
+                               const float* const* B, const int64_t* ldb, float beta, float* const* C,
+                               const int64_t* ldc) {
+  return tile_gemm_batch_ws(stream, count, transA, transB, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, nullptr, 0);
 }

@@ -136,8 +136,9 @@ int submit_gemm(tt_ctx* ctx, const char* label, const Gemm& q) {
 // output tiles, so the grouping depends on the tiling only; sizes and
 // leading dimensions may differ, e.g. the ragged last vocab tile). Each
 // task reads its A and B tiles and writes (beta == 0) or updates its C
-// tiles.
-int submit_gemm_batch(tt_ctx* ctx, const char* label, const std::vector<Gemm>& qs) {
+// tiles. With `split`, the task may split K over its stream's workspace
+// (few, tall products: the attention weight gradients).
+int submit_gemm_batch(tt_ctx* ctx, const char* label, const std::vector<Gemm>& qs, bool split = false) {
   constexpr size_t kMaxProducts = 96;
   constexpr int64_t kMaxBytes = int64_t(1) << 30;
   struct Shape {
@@ -187,7 +188,7 @@ int submit_gemm_batch(tt_ctx* ctx, const char* label, const std::vector<Gemm>& q
       acc.push_back(q0.beta == 0.f ? W(q.C.t, q.C.lin) : RW(q.C.t, q.C.lin));
       flops += 2.0 * sh[u].m * sh[u].n * sh[u].k;
     }
-    int rc = ctx->submit(label, std::move(acc), [grp, sh](hipStream_t s, void*) {
+    int rc = ctx->submit(label, std::move(acc), [grp, sh, split, ctx](hipStream_t s, void* ws) {
       const size_t c = grp.size();
       std::vector<const float*> A(c), B(c);
       std::vector<float*> C(c);
@@ -202,8 +203,10 @@ int submit_gemm_batch(tt_ctx* ctx, const char* label, const std::vector<Gemm>& q
         ldb[u] = sh[u].ldb;
         ldc[u] = sh[u].ldc;
       }
-      return tile_gemm_batch(s, (int)c, grp[0].ta, grp[0].tb, m.data(), n.data(), sh[0].k, grp[0].alpha, A.data(),
-                             lda.data(), B.data(), ldb.data(), grp[0].beta, C.data(), ldc.data());
+      const bool w = split && ws;
+      return tile_gemm_batch_ws(s, (int)c, grp[0].ta, grp[0].tb, m.data(), n.data(), sh[0].k, grp[0].alpha, A.data(),
+                                lda.data(), B.data(), ldb.data(), grp[0].beta, C.data(), ldc.data(),
+                                w ? ws : nullptr, w ? ctx->workspace_bytes : 0);
     }, flops);
     if (rc) return rc;
     i = j;
@@ -536,6 +539,11 @@ extern "C" int tt_gpt2_create(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_g
                                  {in, e, r}, {e, in, r}, {hw, e, r}, {e, hw, r}};
     size_t g = 0;
     for (auto& s : shapes) g = std::max(g, tile_gemm_workspace(s[0], s[1], s[2]));
+    {  // the batched q/k/v weight gradients of one token tile
+      const int64_t nq = 3 * G->NH * G->NE;
+      std::vector<int64_t> bm(nq, e), bn(nq, hw);
+      g = std::max(g, tile_gemm_batch_workspace((int)nq, bm.data(), bn.data(), r));
+    }
     ws = std::max(ws, std::min<size_t>(g, (size_t)256 << 20));
   }
   if (int rc = ctx->ensure_workspace(ws)) return fail_clean(rc);
@@ -1239,8 +1247,12 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
     for (int64_t si = 0; si < g->ns; ++si)
       for (int64_t bi = 0; bi < g->nb; ++bi) {
         const int64_t ti = bi + g->nb * si;
+        // the q, k and v weight gradients of every (head, embd) tile pair:
+        // independent products of one K (the token tile), one batched task
+        // (split-K over the stream's workspace when they are few)
+        std::vector<Gemm> qs;
         for (int cq = 0; cq < 3; ++cq)
-          for (int64_t hj = 0; hj < NH; ++hj) {
+          for (int64_t hj = 0; hj < NH; ++hj)
             for (int64_t ek = 0; ek < NE; ++ek) {
               Gemm q;
               q.ta = 1;
@@ -1248,8 +1260,11 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
               q.B = {dqkv[cq], L(dqkv[cq], {bi, si, hj, 0})};
               q.C = {gwqkv, L(gwqkv, {ek, cq, hj, 0})};
               q.beta = (ti > 0 || later_mb) ? 1.f : 0.f;
-              TRY(submit_gemm(ctx, "qkv_dw", q));
+              qs.push_back(q);
             }
+        TRY(submit_gemm_batch(ctx, "qkv_dw", qs, true));
+        for (int cq = 0; cq < 3; ++cq)
+          for (int64_t hj = 0; hj < NH; ++hj) {
             TRY(colsum_task(ctx, dqkv[cq], L(dqkv[cq], {bi, si, hj, 0}), gbqkv, L(gbqkv, {cq, hj, 0}), ti > 0 || later_mb));
           }
         for (int64_t ek = 0; ek < NE; ++ek) {

@@ -13,7 +13,8 @@ from ._lib import (TT_EPI_NONE, check, lib, ptr, stream_handle, TT_EPI_BIAS, TT_
                    TT_EMB_TOKEN, TT_EMB_POS)
 
 __all__ = [
-    "tile_gemm", "tile_gemm_ws", "tile_gemm_workspace", "tile_gemm_ksum", "tile_gemm_batch", "tile_layernorm_fwd",
+    "tile_gemm", "tile_gemm_ws", "tile_gemm_workspace", "tile_gemm_ksum", "tile_gemm_batch", "tile_gemm_batch_ws",
+    "tile_gemm_batch_workspace", "tile_layernorm_fwd",
     "tile_layernorm_bwd", "tile_layernorm_bwd_workspace", "tile_softmax",
     "tile_xentropy", "tile_xentropy_multi", "tile_attention_fwd", "tile_attention_bwd", "tile_fused_adamw",
     "tile_fused_adamw_multi",
@@ -53,16 +54,35 @@ def tile_gemm_ksum(stream, m, n, ks, alpha, As, ldas, Bs, ldbs, beta, C, ldc):
                                     i64(ldbs), beta, ptr(C), ldc))
 
 
-def tile_gemm_batch(stream, transA, transB, ms, ns, k, alpha, As, ldas, Bs, ldbs, beta, Cs, ldcs):
-    """C_t = alpha op(A_t) op(B_t) + beta C_t; per-product sizes and leading
-    dimensions as equal-length lists (an int is used for every product)."""
+def _batch_args(ms, ns, As, ldas, Bs, ldbs, Cs, ldcs):
     import ctypes as C_
     cnt = len(Cs)
     per = lambda x: list(x) if isinstance(x, (list, tuple)) else [x] * cnt  # noqa: E731
     i64 = lambda xs: (C_.c_int64 * max(cnt, 1))(*[int(x) for x in per(xs)])  # noqa: E731
     ptrs = lambda xs: (C_.c_void_p * max(cnt, 1))(*[ptr(x) for x in xs])  # noqa: E731
-    return check(lib.tile_gemm_batch(stream_handle(stream), cnt, transA, transB, i64(ms), i64(ns), k, alpha, ptrs(As),
-                                     i64(ldas), ptrs(Bs), i64(ldbs), beta, ptrs(Cs), i64(ldcs)))
+    return cnt, i64(ms), i64(ns), ptrs(As), i64(ldas), ptrs(Bs), i64(ldbs), ptrs(Cs), i64(ldcs)
+
+
+def tile_gemm_batch(stream, transA, transB, ms, ns, k, alpha, As, ldas, Bs, ldbs, beta, Cs, ldcs):
+    """C_t = alpha op(A_t) op(B_t) + beta C_t; per-product sizes and leading
+    dimensions as equal-length lists (an int is used for every product)."""
+    cnt, m, n, a, la, b, lb, c, lc = _batch_args(ms, ns, As, ldas, Bs, ldbs, Cs, ldcs)
+    return check(lib.tile_gemm_batch(stream_handle(stream), cnt, transA, transB, m, n, k, alpha, a, la, b, lb, beta,
+                                     c, lc))
+
+
+def tile_gemm_batch_ws(stream, transA, transB, ms, ns, k, alpha, As, ldas, Bs, ldbs, beta, Cs, ldcs, workspace,
+                       workspace_bytes):
+    cnt, m, n, a, la, b, lb, c, lc = _batch_args(ms, ns, As, ldas, Bs, ldbs, Cs, ldcs)
+    return check(lib.tile_gemm_batch_ws(stream_handle(stream), cnt, transA, transB, m, n, k, alpha, a, la, b, lb,
+                                        beta, c, lc, ptr(workspace), workspace_bytes))
+
+
+def tile_gemm_batch_workspace(ms, ns, k):
+    import ctypes as C_
+    cnt = len(ms)
+    i64 = lambda xs: (C_.c_int64 * max(cnt, 1))(*[int(x) for x in xs])  # noqa: E731
+    return lib.tile_gemm_batch_workspace(cnt, i64(ms), i64(ns), k)
 
 
 def tile_layernorm_fwd(stream, phase, rows, cols, x, ldx, gamma, beta, parts, n_parts, part_stride, stats, y,
