@@ -539,10 +539,16 @@ extern "C" int tt_gpt2_create(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_g
                                  {in, e, r}, {e, in, r}, {hw, e, r}, {e, hw, r}};
     size_t g = 0;
     for (auto& s : shapes) g = std::max(g, tile_gemm_workspace(s[0], s[1], s[2]));
-    {  // the batched q/k/v weight gradients of one token tile
-      const int64_t nq = 3 * G->NH * G->NE;
-      std::vector<int64_t> bm(nq, e), bn(nq, hw);
-      g = std::max(g, tile_gemm_batch_workspace((int)nq, bm.data(), bn.data(), r));
+    {  // the batched weight gradients of one token tile (q/k/v, attention
+       // projection, fc, MLP projection), split-K when the products are few
+      auto batch = [&](int64_t cnt, int64_t m, int64_t n) {
+        std::vector<int64_t> bm(cnt, m), bn(cnt, n);
+        g = std::max(g, tile_gemm_batch_workspace((int)cnt, bm.data(), bn.data(), r));
+      };
+      batch(3 * G->NH * G->NE, e, hw);
+      batch(G->NE * G->NH, hw, e);
+      batch(G->NI * G->NE, e, in);
+      batch(G->NE * G->NI, in, e);
     }
     ws = std::max(ws, std::min<size_t>(g, (size_t)256 << 20));
   }
@@ -1138,18 +1144,24 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
     for (int64_t si = 0; si < g->ns; ++si)
       for (int64_t bi = 0; bi < g->nb; ++bi) {
         const int64_t ti = bi + g->nb * si;
-        for (int64_t ej = 0; ej < NE; ++ej) {
-          for (int64_t ik = 0; ik < NI; ++ik) {
-            Gemm q;
-            q.ta = 1;
-            q.A = {b.g, L(b.g, {bi, si, ik})};
-            q.B = {g->dh, L(g->dh, {bi, si, ej})};
-            q.C = {gwp, L(gwp, {ik, ej})};
-            q.beta = (ti > 0 || later_mb) ? 1.f : 0.f;
-            TRY(submit_gemm(ctx, "mlp_proj_dw", q));
-          }
-          TRY(colsum_task(ctx, g->dh, L(g->dh, {bi, si, ej}), gbp, ej, ti > 0 || later_mb));
+        // weight gradients of every (inner, embd) tile pair: one batched task
+        // (split-K over the stream's workspace when the products are few)
+        {
+          std::vector<Gemm> qs;
+          for (int64_t ej = 0; ej < NE; ++ej)
+            for (int64_t ik = 0; ik < NI; ++ik) {
+              Gemm q;
+              q.ta = 1;
+              q.A = {b.g, L(b.g, {bi, si, ik})};
+              q.B = {g->dh, L(g->dh, {bi, si, ej})};
+              q.C = {gwp, L(gwp, {ik, ej})};
+              q.beta = (ti > 0 || later_mb) ? 1.f : 0.f;
+              qs.push_back(q);
+            }
+          TRY(submit_gemm_batch(ctx, "mlp_proj_dw", qs, true));
         }
+        for (int64_t ej = 0; ej < NE; ++ej)
+          TRY(colsum_task(ctx, g->dh, L(g->dh, {bi, si, ej}), gbp, ej, ti > 0 || later_mb));
         for (int64_t ik = 0; ik < NI; ++ik)
           for (int64_t ej = 0; ej < NE; ++ej) {
             Gemm q;
@@ -1164,18 +1176,22 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
             }
             TRY(submit_gemm(ctx, "mlp_proj_dx", q));
           }
-        for (int64_t ik = 0; ik < NI; ++ik) {
-          for (int64_t ek = 0; ek < NE; ++ek) {
-            Gemm q;
-            q.ta = 1;
-            q.A = {b.n2, L(b.n2, {bi, si, ek})};
-            q.B = {g->dgu, L(g->dgu, {bi, si, ik})};
-            q.C = {gwfc, L(gwfc, {ek, ik})};
-            q.beta = (ti > 0 || later_mb) ? 1.f : 0.f;
-            TRY(submit_gemm(ctx, "fc_dw", q));
-          }
-          TRY(colsum_task(ctx, g->dgu, L(g->dgu, {bi, si, ik}), gbfc, ik, ti > 0 || later_mb));
+        {
+          std::vector<Gemm> qs;
+          for (int64_t ik = 0; ik < NI; ++ik)
+            for (int64_t ek = 0; ek < NE; ++ek) {
+              Gemm q;
+              q.ta = 1;
+              q.A = {b.n2, L(b.n2, {bi, si, ek})};
+              q.B = {g->dgu, L(g->dgu, {bi, si, ik})};
+              q.C = {gwfc, L(gwfc, {ek, ik})};
+              q.beta = (ti > 0 || later_mb) ? 1.f : 0.f;
+              qs.push_back(q);
+            }
+          TRY(submit_gemm_batch(ctx, "fc_dw", qs, true));
         }
+        for (int64_t ik = 0; ik < NI; ++ik)
+          TRY(colsum_task(ctx, g->dgu, L(g->dgu, {bi, si, ik}), gbfc, ik, ti > 0 || later_mb));
         for (int64_t ek = 0; ek < NE; ++ek)
           for (int64_t ik = 0; ik < NI; ++ik) {
             Gemm q;
@@ -1189,18 +1205,22 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
         TRY(ln_backward(g, g->dn, b.h_mid, ln2g, b.ln2, g->dh, 1, g->G[g->pidx(l, LN2G)], g->G[g->pidx(l, LN2B)], ti,
                         bi, si));
         // attention projection: h_mid = h_in + O W_o + b_o
-        for (int64_t ej = 0; ej < NE; ++ej) {
-          for (int64_t hk = 0; hk < NH; ++hk) {
-            Gemm q;
-            q.ta = 1;
-            q.A = {b.o, L(b.o, {bi, si, hk, 0})};
-            q.B = {g->dh, L(g->dh, {bi, si, ej})};
-            q.C = {gwo, L(gwo, {hk, 0, ej})};
-            q.beta = (ti > 0 || later_mb) ? 1.f : 0.f;
-            TRY(submit_gemm(ctx, "attn_proj_dw", q));
-          }
-          TRY(colsum_task(ctx, g->dh, L(g->dh, {bi, si, ej}), gbo, ej, ti > 0 || later_mb));
+        {
+          std::vector<Gemm> qs;
+          for (int64_t ej = 0; ej < NE; ++ej)
+            for (int64_t hk = 0; hk < NH; ++hk) {
+              Gemm q;
+              q.ta = 1;
+              q.A = {b.o, L(b.o, {bi, si, hk, 0})};
+              q.B = {g->dh, L(g->dh, {bi, si, ej})};
+              q.C = {gwo, L(gwo, {hk, 0, ej})};
+              q.beta = (ti > 0 || later_mb) ? 1.f : 0.f;
+              qs.push_back(q);
+            }
+          TRY(submit_gemm_batch(ctx, "attn_proj_dw", qs, true));
         }
+        for (int64_t ej = 0; ej < NE; ++ej)
+          TRY(colsum_task(ctx, g->dh, L(g->dh, {bi, si, ej}), gbo, ej, ti > 0 || later_mb));
         for (int64_t hk = 0; hk < NH; ++hk)
           for (int64_t ej = 0; ej < NE; ++ej) {
             Gemm q;
