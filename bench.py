@@ -18,7 +18,7 @@ Prints ONE JSON line:
   cpu_baseline the fp64 oracle step timed on this host's cores on a bounded
                sample (one of the batch's sequences), scaled to tokens/s
 Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload NAME]
-       [--streams S (default: 1; wide4 2; small tiles 4)] [--pinned --budget-gb G]
+       [--streams S (default: 1; small tiles 4)] [--pinned --budget-gb G]
 """
 from __future__ import annotations
 
@@ -366,7 +366,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gpt2_small", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--streams", type=int, default=0,
-                    help="executor streams (0 = measured best per workload: 1; wide4 2; small tiles 4; pinned 1)")
+                    help="executor streams (0 = measured best per workload: 1; small tiles 4; pinned 1)")
     ap.add_argument("--heavy-gflops", type=float, default=0.0,
                     help="tasks of at least this many GFLOP run in order on stream 0 (0 = off)")
     ap.add_argument("--pinned", action="store_true",
@@ -398,11 +398,12 @@ def main(argv=None):
 
     w = synth.WORKLOADS[a.workload]
     if a.streams <= 0:
-        # measured on MI355X: many small tasks need concurrency; GPT2-small's
-        # tasks fill the GPU alone and run faster one at a time (no cache
-        # interference); the wide model gains a little from two; staged
-        # tiles want one (fewer tiles needed at once)
-        a.streams = {"wide4_small_tiles": 4, "wide4": 2}.get(a.workload, 1) if not a.pinned else 1
+        # measured on MI355X: many small tasks need concurrency (small tiles:
+        # 911 ms on 4 streams, 1018 on 2); GPT2-small's and the wide model's
+        # tasks fill the GPU alone and run faster one at a time (35.0 vs
+        # 35.8 ms; 741.5 vs 753.8 ms); staged tiles want one (fewer tiles
+        # needed at once)
+        a.streams = {"wide4_small_tiles": 4}.get(a.workload, 1) if not a.pinned else 1
     if a.tile_classes:
         res = tile_classes(w, only=a.only)
         if a.copy_probe_mib:
