@@ -124,7 +124,8 @@ def class_rooflines(breakdown: dict, s) -> dict:
 
 
 # entry point of each task class's launches (the rest are tile_gemm)
-KERNEL_OF = {"head": "tile_gemm_batch", "head_dw": "tile_gemm_batch", "head_dx": "tile_gemm_ksum"}
+KERNEL_OF = {"head": "tile_gemm_batch", "head_dw": "tile_gemm_batch", "head_dx": "tile_gemm_ksum",
+             "qkv_dx": "tile_gemm_ksum"}
 
 GEMM_SHAPES = {  # label -> (transA, transB, m, n, k, epilogue, beta) in tile terms
     "qkv": lambda r, e, i, h, v: (0, 0, r, h, e, 1, 0.0), "attn_proj": lambda r, e, i, h, v: (0, 0, r, e, h, 3, 0.0),

@@ -101,20 +101,22 @@ int tile_gemm_ws(void* stream, int transA, int transB, int64_t m, int64_t n, int
                  void* workspace, size_t workspace_bytes);
 size_t tile_gemm_workspace(int64_t m, int64_t n, int64_t k);
 /* tile_gemm_ksum -- a sum of products into one tile:
- *   C = alpha * sum_{t < count} A_t B_t + beta * C
- * with A_t [m x k[t]] (A_t[i*lda[t] + p]) and B_t [k[t] x n] (B_t[p*ldb[t] + j])
- * -- the LM head's input gradient dnf = sum over vocab tiles of dz_v wte_v
- * (tiled linear layer backward; pith.science review, "What carries the
- * argument"). A, B, k, lda, ldb are HOST arrays of `count` entries (A[t],
- * B[t] DEVICE pointers; read before the call returns). Runs of pairs that
- * share lda and ldb, with k[t] a multiple of the K step, 16-byte aligned
- * operands and m, n multiples of the block size go through one long-K
- * launch each (up to 96 pairs); any other pair runs on its own through
- * tile_gemm, accumulating. The pairs are summed in list order: same result
- * on every run. k[t] = 0 contributes nothing; count = 0 gives C = beta*C.
- * TT_ERR_ARG for negative sizes, a null array, or a pair with a null
- * operand or a leading dimension below its row length. */
-int tile_gemm_ksum(void* stream, int count, int64_t m, int64_t n, const int64_t* k, float alpha,
+ *   C = alpha * sum_{t < count} A_t op(B_t) + beta * C
+ * with A_t [m x k[t]] (A_t[i*lda[t] + p]) and op(B_t) [k[t] x n]: B_t[p*ldb[t] + j]
+ * (transB = 0) or B_t[j*ldb[t] + p] (transB = 1) -- a linear layer's input
+ * gradient summed over tiles of its output axis: the LM head's dnf = sum over
+ * vocab tiles of dz_v wte_v, and dX = sum_t dY_t W_t^T of the attention block's
+ * q, k, v projections (tiled linear layer backward; pith.science review,
+ * "What carries the argument"). A, B, k, lda, ldb are HOST arrays of `count`
+ * entries (A[t], B[t] DEVICE pointers; read before the call returns). Runs of
+ * pairs that share lda and ldb, with k[t] a multiple of the K step, 16-byte
+ * aligned operands and m, n multiples of the block size go through one
+ * long-K launch each (up to 96 pairs); any other pair runs on its own
+ * through tile_gemm, accumulating. The pairs are summed in list order: same
+ * result on every run. k[t] = 0 contributes nothing; count = 0 gives
+ * C = beta*C. TT_ERR_ARG for negative sizes, a null array, or a pair with a
+ * null operand or a leading dimension below its row length. */
+int tile_gemm_ksum(void* stream, int count, int transB, int64_t m, int64_t n, const int64_t* k, float alpha,
                    const float* const* A, const int64_t* lda, const float* const* B, const int64_t* ldb,
                    float beta, float* C, int64_t ldc);
 /* tile_gemm_batch -- independent products in one launch:

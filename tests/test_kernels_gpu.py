@@ -70,29 +70,32 @@ def test_gemm_split_k_workspace(ta, tb, m, n, k):
     assert torch.equal(outs[0], outs[1])
 
 
+@pytest.mark.parametrize("tb", [0, 1])
 @pytest.mark.parametrize("m,n,ks,beta", [
     (4096, 768, [768] * 5 + [337], 0.0),          # the LM head's dnf: full vocab tiles + the ragged last one
     (256, 192, [64, 96, 32, 0, 128], 0.5),        # a skipped empty pair, C kept with beta
     (128, 128, [32] * 100, 1.0),                  # more pairs than one launch takes
     (2048, 4096, [48, 64], 0.0),                  # the 128x128 plan (>= 512 blocks)
     (100, 72, [40, 33], 0.25),                    # m, n off the block grid: every pair falls back
+    (4096, 768, [768] * 3, 0.0),                  # the q/k/v input gradient (B transposed)
 ])
-def test_gemm_ksum(m, n, ks, beta):
-    """C = alpha sum_t A_t B_t + beta C against the fp64 sum (fp32 bound over
-    the total K), bitwise equal across runs."""
-    seed = m + n + len(ks)
+def test_gemm_ksum(m, n, ks, beta, tb):
+    """C = alpha sum_t A_t op(B_t) + beta C against the fp64 sum (fp32 bound
+    over the total K), bitwise equal across runs; B as [k][n] or [n][k]."""
+    seed = m + n + len(ks) + 5 * tb
     As = [synth.rand_normal((m, k), seed + 2 * i) for i, k in enumerate(ks)]
-    Bs = [synth.rand_normal((k, n), seed + 2 * i + 1) for i, k in enumerate(ks)]
+    Bs = [synth.rand_normal((n, k) if tb else (k, n), seed + 2 * i + 1) for i, k in enumerate(ks)]
     c0 = synth.rand_normal((m, n), seed + 999)
     dA, dB = [dev(a) for a in As], [dev(b) for b in Bs]
     outs = []
     for _ in range(2):
         C = dev(c0)
-        tt.tile_gemm_ksum(None, m, n, ks, 0.75, dA, ks, dB, [n] * len(ks), beta, C, n)
+        tt.tile_gemm_ksum(None, m, n, ks, 0.75, dA, ks, dB, [b.shape[1] for b in Bs], beta, C, n, transB=tb)
         outs.append(C)
     ref = beta * c0.astype(np.float64)
     bound = np.zeros((m, n))
     for a, b in zip(As, Bs):
+        b = b.T if tb else b
         ref = ref + 0.75 * (a.astype(np.float64) @ b.astype(np.float64))
         bound += 0.75 * (np.abs(a).astype(np.float64) @ np.abs(b).astype(np.float64))
     bound *= (sum(ks) + len(ks) + 2) * EPS32

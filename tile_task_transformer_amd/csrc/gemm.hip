@@ -655,12 +655,14 @@ struct KsumArgs {
   KsumPair t[kKsumMax];
 };
 
-template <int BM, int BN, int BK>
+// TB: B_t is stored [n][k_t] (B_t^T in HBM, K-contiguous, the linear
+// layers' input gradients dX = sum_t dY_t W_t^T) instead of [k_t][n].
+template <int BM, int BN, int BK, bool TB>
 __global__ __launch_bounds__(256, 2) void gemm_ksum_kernel(KsumArgs P) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int FM = WM / 32, FN = WN / 32;
-  constexpr int A_LD = BK + 4, B_LD = BN + 8;  // A K-contiguous, B row-contiguous
-  constexpr int A_SZ = BM * A_LD, B_SZ = BK * B_LD;
+  constexpr int A_LD = BK + 4, B_LD = TB ? BK + 4 : BN + 8;  // A K-contiguous; B either way
+  constexpr int A_SZ = BM * A_LD, B_SZ = TB ? BN * B_LD : BK * B_LD;
   constexpr int A_PT = BM * BK / 4 / 256, B_PT = BN * BK / 4 / 256;
   static_assert(A_PT * 256 * 4 == BM * BK && B_PT * 256 * 4 == BN * BK, "tile must split evenly over 256 threads");
   __shared__ __attribute__((aligned(16))) float lds[2 * (A_SZ + B_SZ)];
@@ -705,7 +707,13 @@ __global__ __launch_bounds__(256, 2) void gemm_ksum_kernel(KsumArgs P) {
 #pragma unroll
   for (int i = 0; i < B_PT; ++i) {
     const int idx = tid + 256 * i;
-    ob[i] = (idx / (BN / 4)) * (int)P.ldb + (idx % (BN / 4)) * 4;
+    if (TB) {
+      int r, c;
+      kc_index<BK>(idx, &r, &c);
+      ob[i] = r * (int)P.ldb + c;
+    } else {
+      ob[i] = (idx / (BN / 4)) * (int)P.ldb + (idx % (BN / 4)) * 4;
+    }
   }
   // step -> pair: the steps are requested in non-decreasing order, so a
   // cursor walks the list (uniform, scalar)
@@ -717,7 +725,7 @@ __global__ __launch_bounds__(256, 2) void gemm_ksum_kernel(KsumArgs P) {
     while (st >= before + P.t[cur].steps) before += P.t[cur++].steps;
     const int k0 = (int)(st - before) * BK;
     const float* pa = P.t[cur].A + (int64_t)m0 * P.lda + k0;
-    const float* pb = P.t[cur].B + (int64_t)k0 * P.ldb + n0;
+    const float* pb = TB ? P.t[cur].B + (int64_t)n0 * P.ldb + k0 : P.t[cur].B + (int64_t)k0 * P.ldb + n0;
 #pragma unroll
     for (int i = 0; i < A_PT; ++i) ra[i] = *reinterpret_cast<const f32x4*>(pa + oa[i]);
 #pragma unroll
@@ -735,7 +743,13 @@ __global__ __launch_bounds__(256, 2) void gemm_ksum_kernel(KsumArgs P) {
 #pragma unroll
     for (int i = 0; i < B_PT; ++i) {
       const int idx = tid + 256 * i;
-      *reinterpret_cast<f32x4*>(Bs + (idx / (BN / 4)) * B_LD + (idx % (BN / 4)) * 4) = rb[i];
+      if (TB) {
+        int r, c;
+        kc_index<BK>(idx, &r, &c);
+        *reinterpret_cast<f32x4*>(Bs + r * B_LD + c) = rb[i];
+      } else {
+        *reinterpret_cast<f32x4*>(Bs + (idx / (BN / 4)) * B_LD + (idx % (BN / 4)) * 4) = rb[i];
+      }
     }
   };
   auto frag = [&](int buf, int kb, f32x4(&fa)[FM], f32x4(&fb)[FN]) {
@@ -747,8 +761,12 @@ __global__ __launch_bounds__(256, 2) void gemm_ksum_kernel(KsumArgs P) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int col = wn * WN + j * 32 + l32;
+      if (TB) {
+        fb[j] = *reinterpret_cast<const f32x4*>(Bs + col * B_LD + kk);
+      } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) fb[j][q] = Bs[(kk + q) * B_LD + col];
+        for (int q = 0; q < 4; ++q) fb[j][q] = Bs[(kk + q) * B_LD + col];
+      }
     }
   };
   auto mfmas = [&](const f32x4(&fa)[FM], const f32x4(&fb)[FN]) {
@@ -906,9 +924,9 @@ extern "C" int tile_gemm(void* stream, int transA, int transB, int64_t m, int64_
                       aux, ldaux, nullptr, 0);
 }
 
-extern "C" int tile_gemm_ksum(void* stream, int count, int64_t m, int64_t n, const int64_t* k, float alpha,
-                              const float* const* A, const int64_t* lda, const float* const* B, const int64_t* ldb,
-                              float beta, float* C, int64_t ldc) {
+extern "C" int tile_gemm_ksum(void* stream, int count, int transB, int64_t m, int64_t n, const int64_t* k,
+                              float alpha, const float* const* A, const int64_t* lda, const float* const* B,
+                              const int64_t* ldb, float beta, float* C, int64_t ldc) {
   using tt::fail;
   if (count < 0 || m < 0 || n < 0) return fail(TT_ERR_ARG, "tile_gemm_ksum: negative count or size");
   if (m == 0 || n == 0) return TT_OK;
@@ -917,7 +935,7 @@ extern "C" int tile_gemm_ksum(void* stream, int count, int64_t m, int64_t n, con
   if (count > 0 && (!k || !A || !lda || !B || !ldb)) return fail(TT_ERR_ARG, "tile_gemm_ksum: null array");
   for (int t = 0; t < count; ++t) {
     if (k[t] < 0 || k[t] > INT32_MAX) return fail(TT_ERR_ARG, "tile_gemm_ksum: bad k of pair %d", t);
-    if (k[t] > 0 && (!A[t] || !B[t] || lda[t] < k[t] || ldb[t] < n))
+    if (k[t] > 0 && (!A[t] || !B[t] || lda[t] < k[t] || ldb[t] < (transB ? k[t] : n)))
       return fail(TT_ERR_ARG, "tile_gemm_ksum: bad operand of pair %d", t);
   }
   hipStream_t s = tt::as_stream(stream);
@@ -927,7 +945,7 @@ extern "C" int tile_gemm_ksum(void* stream, int count, int64_t m, int64_t n, con
   const int bm = big ? 128 : 64, bn = big ? 128 : 64, bk = big ? 16 : 32;
   auto fits = [&](int t) {  // a pair the branch-free long-K launch can take
     return k[t] % bk == 0 && m % bm == 0 && n % bn == 0 && aligned16(A[t]) && aligned16(B[t]) && lda[t] % 4 == 0 &&
-           ldb[t] % 4 == 0 && (int64_t)bm * lda[t] < INT32_MAX && (int64_t)bk * ldb[t] < INT32_MAX;
+           ldb[t] % 4 == 0 && (int64_t)bm * lda[t] < INT32_MAX && (int64_t)(transB ? bn : bk) * ldb[t] < INT32_MAX;
   };
   float b = beta;  // C's own weight: beta in the first contribution, 1 afterwards
   bool wrote = false;
@@ -938,8 +956,8 @@ extern "C" int tile_gemm_ksum(void* stream, int count, int64_t m, int64_t n, con
       continue;
     }
     if (!fits(t)) {  // on its own, through the general kernel
-      if (int rc = tile_gemm(stream, 0, 0, m, n, k[t], alpha, A[t], lda[t], B[t], ldb[t], b, C, ldc, TT_EPI_NONE,
-                             nullptr, nullptr, 0, nullptr, 0))
+      if (int rc = tile_gemm(stream, 0, transB ? 1 : 0, m, n, k[t], alpha, A[t], lda[t], B[t], ldb[t], b, C, ldc,
+                             TT_EPI_NONE, nullptr, nullptr, 0, nullptr, 0))
         return rc;
       b = 1.f;
       wrote = true;
@@ -967,8 +985,13 @@ extern "C" int tile_gemm_ksum(void* stream, int count, int64_t m, int64_t n, con
     if (steps > INT32_MAX) return fail(TT_ERR_ARG, "tile_gemm_ksum: K too long");
     P.nk = (int)steps;
     const dim3 grid((unsigned)((m / bm) * (n / bn)));
-    if (big) hipLaunchKernelGGL((gemm_ksum_kernel<128, 128, 16>), grid, dim3(256), 0, s, P);
-    else hipLaunchKernelGGL((gemm_ksum_kernel<64, 64, 32>), grid, dim3(256), 0, s, P);
+    if (transB) {
+      if (big) hipLaunchKernelGGL((gemm_ksum_kernel<128, 128, 16, true>), grid, dim3(256), 0, s, P);
+      else hipLaunchKernelGGL((gemm_ksum_kernel<64, 64, 32, true>), grid, dim3(256), 0, s, P);
+    } else {
+      if (big) hipLaunchKernelGGL((gemm_ksum_kernel<128, 128, 16, false>), grid, dim3(256), 0, s, P);
+      else hipLaunchKernelGGL((gemm_ksum_kernel<64, 64, 32, false>), grid, dim3(256), 0, s, P);
+    }
     if (int rc = tt::launch_status("tile_gemm_ksum")) return rc;
     b = 1.f;
     wrote = true;

@@ -1105,7 +1105,7 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
             ldas[vj] = zc;
             ldbs[vj] = wc;
           }
-          return tile_gemm_ksum(s, (int)NV, dr, dc, ks.data(), 1.f, As.data(), ldas.data(), Bs.data(), ldbs.data(),
+          return tile_gemm_ksum(s, (int)NV, 0, dr, dc, ks.data(), 1.f, As.data(), ldas.data(), Bs.data(), ldbs.data(),
                                 0.f, F(dnf, ld), dc);
         }, flops));
       }
@@ -1287,19 +1287,45 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
           for (int64_t hj = 0; hj < NH; ++hj) {
             TRY(colsum_task(ctx, dqkv[cq], L(dqkv[cq], {bi, si, hj, 0}), gbqkv, L(gbqkv, {cq, hj, 0}), ti > 0 || later_mb));
           }
+        // dn = sum over (q|k|v, head tile) of dqkv W_qkv^T: one task per embd
+        // tile, one long-K product over the 3 * NH pairs (tile_gemm_ksum)
         for (int64_t ek = 0; ek < NE; ++ek) {
-          bool firstk = true;
+          tt_tensor* dn = g->dn;
+          const int64_t ld = L(dn, {bi, si, ek});
+          std::vector<Access> acc;
+          std::vector<TileRef> As, Bs;
+          double flops = 0;
+          int64_t dr, dc;
+          dn->mat(ld, &dr, &dc);
           for (int cq = 0; cq < 3; ++cq)
             for (int64_t hj = 0; hj < NH; ++hj) {
-              Gemm q;
-              q.tb = 1;
-              q.A = {dqkv[cq], L(dqkv[cq], {bi, si, hj, 0})};
-              q.B = {wqkv, L(wqkv, {ek, cq, hj, 0})};
-              q.C = {g->dn, L(g->dn, {bi, si, ek})};
-              q.beta = firstk ? 0.f : 1.f;
-              firstk = false;
-              TRY(submit_gemm(ctx, "qkv_dx", q));
+              As.push_back({dqkv[cq], L(dqkv[cq], {bi, si, hj, 0})});
+              Bs.push_back({wqkv, L(wqkv, {ek, cq, hj, 0})});
+              acc.push_back(R(As.back().t, As.back().lin));
+              acc.push_back(R(Bs.back().t, Bs.back().lin));
+              int64_t ar, ac;
+              As.back().t->mat(As.back().lin, &ar, &ac);
+              flops += 2.0 * dr * dc * ac;
             }
+          acc.push_back(W(dn, ld));
+          TRY(ctx->submit("qkv_dx", std::move(acc), [=](hipStream_t s, void*) {
+            const size_t np = As.size();
+            std::vector<const float*> a(np), bb(np);
+            std::vector<int64_t> ks(np), lda(np), ldb(np);
+            for (size_t u = 0; u < np; ++u) {
+              int64_t ar, ac, br, bc;
+              As[u].t->mat(As[u].lin, &ar, &ac);
+              Bs[u].t->mat(Bs[u].lin, &br, &bc);
+              if (ar != dr || br != dc || bc != ac) return fail(TT_ERR_SHAPE, "qkv_dx: pair %zu does not match", u);
+              a[u] = F(As[u].t, As[u].lin);
+              bb[u] = F(Bs[u].t, Bs[u].lin);
+              ks[u] = ac;
+              lda[u] = ac;
+              ldb[u] = bc;
+            }
+            return tile_gemm_ksum(s, (int)np, 1, dr, dc, ks.data(), 1.f, a.data(), lda.data(), bb.data(), ldb.data(),
+                                  0.f, F(dn, ld), dc);
+          }, flops));
         }
         TRY(ln_backward(g, g->dn, b.h_in, ln1g, b.ln1, g->dh, 1, g->G[g->pidx(l, LN1G)], g->G[g->pidx(l, LN1B)], ti,
                         bi, si));

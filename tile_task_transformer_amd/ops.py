@@ -44,14 +44,14 @@ def tile_gemm_workspace(m, n, k):
     return lib.tile_gemm_workspace(m, n, k)
 
 
-def tile_gemm_ksum(stream, m, n, ks, alpha, As, ldas, Bs, ldbs, beta, C, ldc):
-    """C = alpha * sum_t A_t B_t + beta * C; pairs given as equal-length lists."""
+def tile_gemm_ksum(stream, m, n, ks, alpha, As, ldas, Bs, ldbs, beta, C, ldc, transB=0):
+    """C = alpha * sum_t A_t op(B_t) + beta * C; pairs given as equal-length lists."""
     import ctypes as C_
     cnt = len(As)
     i64 = lambda xs: (C_.c_int64 * max(cnt, 1))(*[int(x) for x in xs])  # noqa: E731
     ptrs = lambda xs: (C_.c_void_p * max(cnt, 1))(*[ptr(x) for x in xs])  # noqa: E731
-    return check(lib.tile_gemm_ksum(stream_handle(stream), cnt, m, n, i64(ks), alpha, ptrs(As), i64(ldas), ptrs(Bs),
-                                    i64(ldbs), beta, ptr(C), ldc))
+    return check(lib.tile_gemm_ksum(stream_handle(stream), cnt, transB, m, n, i64(ks), alpha, ptrs(As), i64(ldas),
+                                    ptrs(Bs), i64(ldbs), beta, ptr(C), ldc))
 
 
 def _batch_args(ms, ns, As, ldas, Bs, ldbs, Cs, ldcs):
