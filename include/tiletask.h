@@ -385,6 +385,17 @@ int tile_embedding_bwd(void* stream, int phase, int64_t rows, int64_t cols,
 int tile_reduce_rows(void* stream, int64_t rows, int64_t cols, const float* X, int64_t ldx,
                      float* out, int beta, void* workspace);
 size_t tile_reduce_rows_workspace(int64_t rows, int64_t cols);
+/* tile_reduce_rows_multi -- tile_reduce_rows of up to 16 tiles that share
+ * the row count, in one pair of launches (the attention block's q, k and v
+ * bias gradients: one column sum per tile, each alone a few microseconds):
+ * out_t[c] = (beta ? out_t[c] : 0) + sum_r X_t[r*ldx[t] + c], c < cols[t].
+ * cols, X, ldx, out are HOST arrays of `count` entries (device pointers in X
+ * and out). The workspace holds every tile's partial rows: at least
+ * sum_t tile_reduce_rows_workspace(rows, cols[t]) bytes (TT_ERR_ARG when
+ * smaller). Same result as the per-tile calls (fixed order, deterministic). */
+int tile_reduce_rows_multi(void* stream, int count, int64_t rows, const int64_t* cols, const float* const* X,
+                           const int64_t* ldx, float* const* out, int beta, void* workspace,
+                           size_t workspace_bytes);
 
 /* tile_fill -- dst[i] = value for i < n. tile_split_tokens -- from a window
  * array tokens[b*(seq+1) + t] (int32), ids[b*seq + t] = tokens[b*(seq+1)+t]

@@ -699,6 +699,31 @@ def test_reduce_rows(rows, cols):
     assert torch.equal(out, out2)
 
 
+@pytest.mark.parametrize("rows,cols,beta", [(4096, [768, 768, 768], 1), (1000, [100, 3, 768, 257], 0),
+                                             (65, [64] * 16, 1)])
+def test_reduce_rows_multi(rows, cols, beta):
+    """Column sums of several tiles in one pair of launches: bitwise equal to
+    the per-tile calls and within the fp32 bound of the fp64 sums; ragged rows
+    and columns, 16 tiles; a too-small workspace is an error."""
+    xs = [synth.rand_normal((rows, c), 93 + i) for i, c in enumerate(cols)]
+    need = sum(tt.tile_reduce_rows_workspace(rows, c) for c in cols)
+    ws = torch.empty(need // 4 + 1, device="cuda")
+    dx = [dev(x) for x in xs]
+    outs = [dev(np.full(c, 2.0, np.float32)) for c in cols]
+    tt.tile_reduce_rows_multi(None, rows, cols, dx, cols, outs, beta, ws, need)
+    for x, c, o in zip(dx, cols, outs):
+        single = dev(np.full(c, 2.0, np.float32))
+        w1 = torch.empty(tt.tile_reduce_rows_workspace(rows, c) // 4 + 1, device="cuda")
+        tt.tile_reduce_rows(None, rows, c, x, c, single, beta, w1)
+        assert torch.equal(o, single)
+    for x, o in zip(xs, outs):
+        ref = 2.0 * beta + x.astype(np.float64).sum(0)
+        bound = (np.abs(x).astype(np.float64).sum(0) + 2) * rows * EPS32
+        assert_close_bound(host(o), ref, bound, "reduce_rows_multi")
+    with pytest.raises(tt.TTError):
+        tt.tile_reduce_rows_multi(None, rows, cols, dx, cols, outs, beta, ws, need - 4)
+
+
 def test_fill_and_split_tokens():
     f = empty((1000,))
     tt.tile_fill(None, 1000, f, 3.5)

@@ -117,6 +117,7 @@ SIGNATURES = {
     "tile_embedding_bwd": (I, [P, I, I64, I64, P, P, I64, I64, I64, P, I64, P, I64]),
     "tile_reduce_rows": (I, [P, I64, I64, P, I64, P, I, P]),
     "tile_reduce_rows_workspace": (SZ, [I64, I64]),
+    "tile_reduce_rows_multi": (I, [P, I, I64, P, P, P, P, I, P, SZ]),
     "tile_fill": (I, [P, I64, P, F]),
     "tile_fill_multi": (I, [P, I, P, P, F]),
     "tile_split_tokens": (I, [P, I64, I64, P, P, P]),

@@ -298,21 +298,30 @@ __global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_fwd(AttnGeom g, const
 
 // --------------------------------------------------------------- backward
 
-__global__ void attn_prep(int batch, int heads, int q_len, int hd, const float* __restrict__ O,
-                          const float* __restrict__ dO, float* __restrict__ Dv) {
-  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;  // (b, t, h) row
-  if (i >= (int64_t)batch * q_len * heads) return;
-  const int h = (int)(i % heads);
-  const int64_t bt = i / heads;
-  const int t = (int)(bt % q_len), b = (int)(bt / q_len);
-  const f32x4* o = reinterpret_cast<const f32x4*>(O + i * hd);
-  const f32x4* d = reinterpret_cast<const f32x4*>(dO + i * hd);
+// D[b, h, t] = sum_e dO[b, t, h, e] * O[b, t, h, e]: hd / 4 consecutive lanes
+// per (b, t, h) row, one float4 each (a wave reads whole rows, coalesced),
+// summed by a fixed butterfly of shuffles
+template <int LPR>
+__global__ __launch_bounds__(256) void attn_prep(int batch, int heads, int q_len, const float* __restrict__ O,
+                                                 const float* __restrict__ dO, float* __restrict__ Dv) {
+  const int64_t gid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const int64_t i = gid / LPR;  // (b, t, h) row
+  const int part = (int)(gid % LPR);
+  const bool live = i < (int64_t)batch * q_len * heads;
   float s = 0.f;
-  for (int e = 0; e < hd / 4; ++e) {
-    const f32x4 a = o[e], c = d[e];
-    s += a[0] * c[0] + a[1] * c[1] + a[2] * c[2] + a[3] * c[3];
+  if (live) {
+    const f32x4 a = reinterpret_cast<const f32x4*>(O)[i * LPR + part];
+    const f32x4 c = reinterpret_cast<const f32x4*>(dO)[i * LPR + part];
+    s = a[0] * c[0] + a[1] * c[1] + a[2] * c[2] + a[3] * c[3];
   }
-  Dv[((int64_t)b * heads + h) * q_len + t] = s;
+#pragma unroll
+  for (int o = LPR / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, LPR);
+  if (live && part == 0) {
+    const int h = (int)(i % heads);
+    const int64_t bt = i / heads;
+    const int t = (int)(bt % q_len), b = (int)(bt / q_len);
+    Dv[((int64_t)b * heads + h) * q_len + t] = s;
+  }
 }
 
 // sum of the two parts' register blocks, part 0 + part 1, through LDS
@@ -678,8 +687,13 @@ extern "C" int tile_attention_bwd(void* stream, int phase, int64_t batch, int64_
     if (!O || !dO || !Dvec) return tt::fail(TT_ERR_ARG, "tile_attention_bwd(PREP): null tensor");
     if (!aligned16(O) || !aligned16(dO)) return tt::fail(TT_ERR_ARG, "tile_attention_bwd: 16-byte alignment required");
     const int64_t rows = batch * q_len * heads;
-    hipLaunchKernelGGL(attn_prep, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, (int)batch, (int)heads,
-                       (int)q_len, (int)hd, O, dO, Dvec);
+    const dim3 grid((unsigned)((rows * (hd / 4) + 255) / 256)), block(256);
+    switch (hd) {
+      case 16: hipLaunchKernelGGL(attn_prep<4>, grid, block, 0, s, (int)batch, (int)heads, (int)q_len, O, dO, Dvec); break;
+      case 32: hipLaunchKernelGGL(attn_prep<8>, grid, block, 0, s, (int)batch, (int)heads, (int)q_len, O, dO, Dvec); break;
+      case 64: hipLaunchKernelGGL(attn_prep<16>, grid, block, 0, s, (int)batch, (int)heads, (int)q_len, O, dO, Dvec); break;
+      default: hipLaunchKernelGGL(attn_prep<32>, grid, block, 0, s, (int)batch, (int)heads, (int)q_len, O, dO, Dvec); break;
+    }
     return tt::launch_status("tile_attention_bwd(PREP)");
   }
   if (phase != TT_ATT_GRAD) return tt::fail(TT_ERR_ARG, "tile_attention_bwd: bad phase %d", phase);

@@ -532,6 +532,8 @@ extern "C" int tt_gpt2_create(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_g
   // per-stream workspace for the deterministic column sums
   const int64_t widest = std::max<int64_t>({et, std::min<int64_t>(it, I), ht * hd});
   size_t ws = std::max(tile_layernorm_bwd_workspace(G->rows, et), tile_reduce_rows_workspace(G->rows, widest));
+  // the q/k/v bias gradients: up to 15 head tiles per multi-tile column sum
+  ws = std::max(ws, tile_reduce_rows_workspace(G->rows, std::min<int64_t>(15, 3 * G->NH) * ht * hd));
   {
     // split-K slices of the step's GEMM shapes (m, n, k), capped at 256 MiB per stream
     const int64_t r = G->rows, e = et, in = std::min<int64_t>(it, I), hw = ht * hd, vv = vt;
@@ -1283,10 +1285,44 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
               qs.push_back(q);
             }
         TRY(submit_gemm_batch(ctx, "qkv_dw", qs, true));
-        for (int cq = 0; cq < 3; ++cq)
-          for (int64_t hj = 0; hj < NH; ++hj) {
-            TRY(colsum_task(ctx, dqkv[cq], L(dqkv[cq], {bi, si, hj, 0}), gbqkv, L(gbqkv, {cq, hj, 0}), ti > 0 || later_mb));
+        // the q, k and v bias gradients of every head tile: one task, one
+        // pair of launches (tile_reduce_rows_multi), up to 15 tiles each
+        {
+          std::vector<TileRef> xs, os;
+          for (int cq = 0; cq < 3; ++cq)
+            for (int64_t hj = 0; hj < NH; ++hj) {
+              xs.push_back({dqkv[cq], L(dqkv[cq], {bi, si, hj, 0})});
+              os.push_back({gbqkv, L(gbqkv, {cq, hj, 0})});
+            }
+          const int beta = ti > 0 || later_mb;
+          for (size_t u0 = 0; u0 < xs.size(); u0 += 15) {
+            const size_t u1 = std::min(xs.size(), u0 + 15);
+            std::vector<TileRef> xg(xs.begin() + u0, xs.begin() + u1), og(os.begin() + u0, os.begin() + u1);
+            std::vector<Access> acc;
+            for (size_t u = 0; u < xg.size(); ++u) {
+              acc.push_back(R(xg[u].t, xg[u].lin));
+              acc.push_back(beta ? RW(og[u].t, og[u].lin) : W(og[u].t, og[u].lin));
+            }
+            TRY(ctx->submit("colsum", std::move(acc), [xg, og, beta, ctx](hipStream_t s, void* ws) {
+              const size_t c = xg.size();
+              std::vector<const float*> X(c);
+              std::vector<float*> O(c);
+              std::vector<int64_t> cols(c), ldx(c);
+              int64_t rows = 0;
+              for (size_t u = 0; u < c; ++u) {
+                int64_t r, cc;
+                xg[u].t->mat(xg[u].lin, &r, &cc);
+                rows = r;
+                X[u] = F(xg[u].t, xg[u].lin);
+                O[u] = F(og[u].t, og[u].lin);
+                cols[u] = cc;
+                ldx[u] = cc;
+              }
+              return tile_reduce_rows_multi(s, (int)c, rows, cols.data(), X.data(), ldx.data(), O.data(), beta, ws,
+                                            ctx->workspace_bytes);
+            }));
           }
+        }
         // dn = sum over (q|k|v, head tile) of dqkv W_qkv^T: one task per embd
         // tile, one long-K product over the 3 * NH pairs (tile_gemm_ksum)
         for (int64_t ek = 0; ek < NE; ++ek) {

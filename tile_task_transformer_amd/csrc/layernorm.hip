@@ -231,14 +231,9 @@ __global__ __launch_bounds__(64 * bwd_waves(NV)) void ln_bwd_rows(
 // rows g, g+16, ... (loads issued 4 at a time), then the 16 group sums are
 // added in group order. blockIdx.y = 1 does the same for (ws_off2, out2):
 // LayerNorm's dgamma and dbeta in one launch.
-__global__ __launch_bounds__(1024) void colsum_finish(int nblk, int cols, const float* __restrict__ ws,
-                                                      int64_t ws_ld, int64_t ws_off, float* __restrict__ out,
-                                                      int accumulate, int64_t ws_off2, float* __restrict__ out2) {
+__device__ __forceinline__ void colsum_finish_block(int nblk, int cols, const float* __restrict__ ws, int64_t ws_ld,
+                                                    int64_t ws_off, float* __restrict__ out, int accumulate) {
   __shared__ float red[16][64];
-  if (blockIdx.y == 1) {
-    ws_off = ws_off2;
-    out = out2;
-  }
   const int cl = threadIdx.x & 63, grp = threadIdx.x >> 6;
   const int c = blockIdx.x * 64 + cl;
   float s = 0.f;
@@ -263,6 +258,13 @@ __global__ __launch_bounds__(1024) void colsum_finish(int nblk, int cols, const 
     for (int i = 0; i < 16; ++i) t += red[i][cl];
     out[c] = accumulate ? out[c] + t : t;
   }
+}
+
+__global__ __launch_bounds__(1024) void colsum_finish(int nblk, int cols, const float* __restrict__ ws,
+                                                      int64_t ws_ld, int64_t ws_off, float* __restrict__ out,
+                                                      int accumulate, int64_t ws_off2, float* __restrict__ out2) {
+  if (blockIdx.y == 1) colsum_finish_block(nblk, cols, ws, ws_ld, ws_off2, out2, accumulate);
+  else colsum_finish_block(nblk, cols, ws, ws_ld, ws_off, out, accumulate);
 }
 
 namespace {
@@ -413,8 +415,8 @@ namespace {
 constexpr int kReduceRows = 64;  // rows per stage-1 block
 
 template <bool VEC>
-__global__ __launch_bounds__(256) void reduce_rows_stage1(int rows, int cols, const float* __restrict__ X,
-                                                          int64_t ldx, float* __restrict__ ws) {
+__device__ __forceinline__ void reduce_rows_block(int rows, int cols, const float* __restrict__ X, int64_t ldx,
+                                                  float* __restrict__ ws) {
   __shared__ f32x4 red[4][64];
   const int cl = threadIdx.x & 63, grp = threadIdx.x >> 6;
   const int c = (blockIdx.y * 64 + cl) * 4;
@@ -441,6 +443,38 @@ __global__ __launch_bounds__(256) void reduce_rows_stage1(int rows, int cols, co
     for (int i = 0; i < 4; ++i)
       if (c + i < cols) out[c + i] = t[i];
   }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void reduce_rows_stage1(int rows, int cols, const float* __restrict__ X,
+                                                          int64_t ldx, float* __restrict__ ws) {
+  reduce_rows_block<VEC>(rows, cols, X, ldx, ws);
+}
+
+// several tiles of one row count per launch (the attention block's q, k
+// and v bias gradients): tile t in blockIdx.z (stage 1) / blockIdx.y
+// (finish), its partial rows in its own workspace region
+constexpr int kRowsMax = 16;
+struct RowsTiles {
+  const float* X[kRowsMax];
+  float* out[kRowsMax];
+  int64_t ldx[kRowsMax];
+  int64_t ws_off[kRowsMax];
+  int cols[kRowsMax];
+};
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void reduce_rows_stage1_multi(int rows, RowsTiles P, float* __restrict__ ws) {
+  const int t = blockIdx.z;
+  if ((int)blockIdx.y * 256 >= P.cols[t]) return;  // whole workgroup past this tile's columns
+  reduce_rows_block<VEC>(rows, P.cols[t], P.X[t], P.ldx[t], ws + P.ws_off[t]);
+}
+
+__global__ __launch_bounds__(1024) void colsum_finish_multi(int nblk, RowsTiles P, const float* __restrict__ ws,
+                                                            int accumulate) {
+  const int t = blockIdx.y;
+  if ((int)blockIdx.x * 64 >= P.cols[t]) return;
+  colsum_finish_block(nblk, P.cols[t], ws, P.cols[t], P.ws_off[t], P.out[t], accumulate);
 }
 }  // namespace
 
@@ -469,4 +503,45 @@ extern "C" int tile_reduce_rows(void* stream, int64_t rows, int64_t cols, const 
   hipLaunchKernelGGL(colsum_finish, dim3((c + 63) / 64), dim3(1024), 0, s, nblk, c, ws, (int64_t)c, (int64_t)0, out,
                      beta, (int64_t)0, out);
   return tt::launch_status("tile_reduce_rows(finish)");
+}
+
+extern "C" int tile_reduce_rows_multi(void* stream, int count, int64_t rows, const int64_t* cols, const float* const* X,
+                                      const int64_t* ldx, float* const* out, int beta, void* workspace,
+                                      size_t workspace_bytes) {
+  using tt::fail;
+  hipStream_t s = tt::as_stream(stream);
+  if (count < 0 || rows < 0) return fail(TT_ERR_ARG, "tile_reduce_rows_multi: negative count or size");
+  if (count == 0) return TT_OK;
+  if (count > kRowsMax) return fail(TT_ERR_ARG, "tile_reduce_rows_multi: more than %d tiles", kRowsMax);
+  if (!cols || !out || (rows > 0 && (!X || !ldx)) || !workspace)
+    return fail(TT_ERR_ARG, "tile_reduce_rows_multi: null array or workspace");
+  if (rows > INT32_MAX) return fail(TT_ERR_ARG, "tile_reduce_rows_multi: size exceeds int32");
+  const int r = (int)rows;
+  const int nblk = (r + kReduceRows - 1) / kReduceRows;
+  RowsTiles P{};
+  int64_t off = 0, maxc = 0;
+  bool vec = true;
+  for (int t = 0; t < count; ++t) {
+    if (cols[t] < 1 || cols[t] > INT32_MAX || !out[t]) return fail(TT_ERR_ARG, "tile_reduce_rows_multi: bad tile %d", t);
+    if (rows > 0 && (!X[t] || ldx[t] < cols[t])) return fail(TT_ERR_ARG, "tile_reduce_rows_multi: bad X of tile %d", t);
+    P.X[t] = rows > 0 ? X[t] : nullptr;
+    P.ldx[t] = rows > 0 ? ldx[t] : 0;
+    P.out[t] = out[t];
+    P.cols[t] = (int)cols[t];
+    P.ws_off[t] = off;
+    off += (int64_t)std::max(nblk, 1) * cols[t];
+    maxc = std::max(maxc, cols[t]);
+    if (rows > 0) vec = vec && ldx[t] % 4 == 0 && tt::aligned16(X[t]);
+  }
+  if ((size_t)off * sizeof(float) > workspace_bytes) return fail(TT_ERR_ARG, "tile_reduce_rows_multi: workspace too small");
+  float* ws = (float*)workspace;
+  if (rows > 0) {
+    dim3 grid(nblk, (unsigned)((maxc + 255) / 256), count), block(256);
+    if (vec) hipLaunchKernelGGL(reduce_rows_stage1_multi<true>, grid, block, 0, s, r, P, ws);
+    else hipLaunchKernelGGL(reduce_rows_stage1_multi<false>, grid, block, 0, s, r, P, ws);
+    if (int rc = tt::launch_status("tile_reduce_rows_multi")) return rc;
+  }
+  hipLaunchKernelGGL(colsum_finish_multi, dim3((unsigned)((maxc + 63) / 64), count), dim3(1024), 0, s, nblk, P, ws,
+                     beta);
+  return tt::launch_status("tile_reduce_rows_multi(finish)");
 }

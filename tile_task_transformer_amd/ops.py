@@ -20,7 +20,7 @@ __all__ = [
     "tile_fused_adamw_multi",
     "tile_adamw_advance", "tile_sgd", "tile_sgd_multi",
     "tile_embedding_fwd", "tile_embedding_index", "tile_embedding_bwd", "tile_reduce_rows",
-    "tile_reduce_rows_workspace", "tile_fill", "tile_fill_multi", "tile_split_tokens",
+    "tile_reduce_rows_workspace", "tile_reduce_rows_multi", "tile_fill", "tile_fill_multi", "tile_split_tokens",
     "TT_EPI_NONE", "TT_EPI_BIAS", "TT_EPI_RES", "TT_EPI_GELU", "TT_EPI_GELU_BWD", "TT_LN_PARTIAL",
     "TT_LN_MERGE", "TT_LN_APPLY", "TT_LN_FUSED", "TT_SM_STATS", "TT_SM_MERGE", "TT_SM_APPLY", "TT_XE_LOSS",
     "TT_XE_GRAD", "TT_XE_STATS", "TT_ATT_PREP", "TT_ATT_GRAD", "TT_EMB_TOKEN", "TT_EMB_POS",
@@ -191,6 +191,16 @@ def tile_reduce_rows(stream, rows, cols, X, ldx, out, beta, workspace):
 
 def tile_reduce_rows_workspace(rows, cols):
     return lib.tile_reduce_rows_workspace(rows, cols)
+
+
+def tile_reduce_rows_multi(stream, rows, cols, Xs, ldxs, outs, beta, workspace, workspace_bytes):
+    """Column sums of several tiles (equal-length lists) in one pair of launches."""
+    import ctypes as C_
+    cnt = len(outs)
+    i64 = lambda xs: (C_.c_int64 * max(cnt, 1))(*[int(x) for x in xs])  # noqa: E731
+    ptrs = lambda xs: (C_.c_void_p * max(cnt, 1))(*[ptr(x) for x in xs])  # noqa: E731
+    return check(lib.tile_reduce_rows_multi(stream_handle(stream), cnt, rows, i64(cols), ptrs(Xs), i64(ldxs),
+                                            ptrs(outs), beta, ptr(workspace), workspace_bytes))
 
 
 def tile_fill(stream, n, dst, value):
