@@ -125,7 +125,8 @@ def class_rooflines(breakdown: dict, s) -> dict:
 
 # entry point of each task class's launches (the rest are tile_gemm)
 KERNEL_OF = {"head": "tile_gemm_batch", "head_dw": "tile_gemm_batch", "head_dx": "tile_gemm_ksum",
-             "qkv_dx": "tile_gemm_ksum"}
+             "qkv_dw": "tile_gemm_batch", "qkv_dx": "tile_gemm_ksum", "attn_proj_dw": "tile_gemm_batch",
+             "fc_dw": "tile_gemm_batch", "mlp_proj_dw": "tile_gemm_batch"}
 
 GEMM_SHAPES = {  # label -> (transA, transB, m, n, k, epilogue, beta) in tile terms
     "qkv": lambda r, e, i, h, v: (0, 0, r, h, e, 1, 0.0), "attn_proj": lambda r, e, i, h, v: (0, 0, r, e, h, 3, 0.0),
@@ -193,10 +194,32 @@ def tile_classes(w, reps=20, only=None):
         out[label] = {"bound": "mfma", "shape": [r, e, s.vocab, len(lens)], "us": round(ms * 1e3, 1),
                       "achieved": round(tf, 2), "unit": "TFLOP/s", "frac": round(tf / MFMA_FP32_PEAK, 4)}
         del X, Z, W
+    # the attention block's q, k and v weight gradients as one batched
+    # (split-K) launch, its input gradient as one long-K launch over the
+    # 3 x head-tile pairs (as the step runs them)
+    nq = 3 * (s.n_head // t.head)
+    for label in ("qkv_dw", "qkv_dx"):
+        if only and label != only:
+            continue
+        X = rnd(r, e)
+        D = [rnd(r, h) for _ in range(nq)]
+        W = [rnd(e, h) for _ in range(nq)]
+        if label == "qkv_dw":
+            nws = tt.tile_gemm_batch_workspace([e] * nq, [h] * nq, r)
+            ws = torch.empty(max(nws // 4, 1), device="cuda")
+            fn = lambda: tt.tile_gemm_batch_ws(st, 1, 0, e, h, r, 1.0, [X] * nq, e, D, h, 0.0, W, h, ws, nws)  # noqa
+        else:
+            fn = lambda: tt.tile_gemm_ksum(st, r, e, [h] * nq, 1.0, D, [h] * nq, W, [h] * nq, 0.0, X, e,  # noqa
+                                           transB=1)
+        ms = timed(fn)
+        tf = 2.0 * r * e * h * nq / (ms * 1e-3) / 1e12
+        out[label] = {"bound": "mfma", "shape": [r, e, h, nq], "us": round(ms * 1e3, 1),
+                      "achieved": round(tf, 2), "unit": "TFLOP/s", "frac": round(tf / MFMA_FP32_PEAK, 4)}
+        del X, D, W
     for label, f in GEMM_SHAPES.items():
         if only and label != only:  # "attn": the attention classes only
             continue
-        if label in ("head", "head_dw", "head_dx"):
+        if label in ("head", "head_dw", "head_dx", "qkv_dw", "qkv_dx"):
             continue
         ta, tb, m, n, k, epi, beta = f(r, e, i, h, v)
         A = rnd(k, m) if ta else rnd(m, k)
