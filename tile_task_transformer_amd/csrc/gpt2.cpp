@@ -214,6 +214,56 @@ int submit_gemm_batch(tt_ctx* ctx, const char* label, const std::vector<Gemm>& q
   return TT_OK;
 }
 
+// C = sum_t A_t B_t^T over the (A, B) tile pairs as one task and one long-K
+// launch (tile_gemm_ksum with B transposed): a linear layer's input
+// gradient summed over the tiles of its output axis, instead of a chain of
+// accumulating GEMMs that each read and write C. A single pair is an
+// ordinary tile_gemm task.
+int submit_ksum_tb(tt_ctx* ctx, const char* label, TileRef C, const std::vector<TileRef>& As,
+                   const std::vector<TileRef>& Bs) {
+  if (As.size() == 1) {
+    Gemm q;
+    q.tb = 1;
+    q.A = As[0];
+    q.B = Bs[0];
+    q.C = C;
+    return submit_gemm(ctx, label, q);
+  }
+  int64_t dr, dc;
+  C.t->mat(C.lin, &dr, &dc);
+  std::vector<Access> acc;
+  double flops = 0;
+  for (size_t u = 0; u < As.size(); ++u) {
+    int64_t ar, ac, br, bc;
+    As[u].t->mat(As[u].lin, &ar, &ac);
+    Bs[u].t->mat(Bs[u].lin, &br, &bc);
+    if (ar != dr || br != dc || bc != ac)
+      return fail(TT_ERR_SHAPE, "%s: pair %zu (%lldx%lld, %lldx%lld) does not match C %lldx%lld", label, u,
+                  (long long)ar, (long long)ac, (long long)br, (long long)bc, (long long)dr, (long long)dc);
+    acc.push_back(R(As[u].t, As[u].lin));
+    acc.push_back(R(Bs[u].t, Bs[u].lin));
+    flops += 2.0 * dr * dc * ac;
+  }
+  acc.push_back(W(C.t, C.lin));
+  return ctx->submit(label, std::move(acc), [=](hipStream_t s, void*) {
+    const size_t np = As.size();
+    std::vector<const float*> a(np), bb(np);
+    std::vector<int64_t> ks(np), lda(np), ldb(np);
+    for (size_t u = 0; u < np; ++u) {
+      int64_t ar, ac, br, bc;
+      As[u].t->mat(As[u].lin, &ar, &ac);
+      Bs[u].t->mat(Bs[u].lin, &br, &bc);
+      a[u] = F(As[u].t, As[u].lin);
+      bb[u] = F(Bs[u].t, Bs[u].lin);
+      ks[u] = ac;
+      lda[u] = ac;
+      ldb[u] = bc;
+    }
+    return tile_gemm_ksum(s, (int)np, 1, dr, dc, ks.data(), 1.f, a.data(), lda.data(), bb.data(), ldb.data(), 0.f,
+                          F(C.t, C.lin), dc);
+  }, flops);
+}
+
 // tiles = value, TT_FILL_MAX_TILES tiles per task and launch (with
 // pinned-host homes a task's tiles take at most an eighth of the arena)
 int fill_tasks(tt_gpt2* g, const std::vector<TileRef>& tiles, float v) {
@@ -1194,6 +1244,8 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
         }
         for (int64_t ik = 0; ik < NI; ++ik)
           TRY(colsum_task(ctx, g->dgu, L(g->dgu, {bi, si, ik}), gbfc, ik, ti > 0 || later_mb));
+        // (a chain of accumulating GEMMs: as one long-K task per embd tile it
+        // measured slower on the wide model, 65 -> 71 ms per step)
         for (int64_t ek = 0; ek < NE; ++ek)
           for (int64_t ik = 0; ik < NI; ++ik) {
             Gemm q;
@@ -1326,42 +1378,13 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
         // dn = sum over (q|k|v, head tile) of dqkv W_qkv^T: one task per embd
         // tile, one long-K product over the 3 * NH pairs (tile_gemm_ksum)
         for (int64_t ek = 0; ek < NE; ++ek) {
-          tt_tensor* dn = g->dn;
-          const int64_t ld = L(dn, {bi, si, ek});
-          std::vector<Access> acc;
           std::vector<TileRef> As, Bs;
-          double flops = 0;
-          int64_t dr, dc;
-          dn->mat(ld, &dr, &dc);
           for (int cq = 0; cq < 3; ++cq)
             for (int64_t hj = 0; hj < NH; ++hj) {
               As.push_back({dqkv[cq], L(dqkv[cq], {bi, si, hj, 0})});
               Bs.push_back({wqkv, L(wqkv, {ek, cq, hj, 0})});
-              acc.push_back(R(As.back().t, As.back().lin));
-              acc.push_back(R(Bs.back().t, Bs.back().lin));
-              int64_t ar, ac;
-              As.back().t->mat(As.back().lin, &ar, &ac);
-              flops += 2.0 * dr * dc * ac;
             }
-          acc.push_back(W(dn, ld));
-          TRY(ctx->submit("qkv_dx", std::move(acc), [=](hipStream_t s, void*) {
-            const size_t np = As.size();
-            std::vector<const float*> a(np), bb(np);
-            std::vector<int64_t> ks(np), lda(np), ldb(np);
-            for (size_t u = 0; u < np; ++u) {
-              int64_t ar, ac, br, bc;
-              As[u].t->mat(As[u].lin, &ar, &ac);
-              Bs[u].t->mat(Bs[u].lin, &br, &bc);
-              if (ar != dr || br != dc || bc != ac) return fail(TT_ERR_SHAPE, "qkv_dx: pair %zu does not match", u);
-              a[u] = F(As[u].t, As[u].lin);
-              bb[u] = F(Bs[u].t, Bs[u].lin);
-              ks[u] = ac;
-              lda[u] = ac;
-              ldb[u] = bc;
-            }
-            return tile_gemm_ksum(s, (int)np, 1, dr, dc, ks.data(), 1.f, a.data(), lda.data(), bb.data(), ldb.data(),
-                                  0.f, F(dn, ld), dc);
-          }, flops));
+          TRY(submit_ksum_tb(ctx, "qkv_dx", {g->dn, L(g->dn, {bi, si, ek})}, As, Bs));
         }
         TRY(ln_backward(g, g->dn, b.h_in, ln1g, b.ln1, g->dh, 1, g->G[g->pidx(l, LN1G)], g->G[g->pidx(l, LN1B)], ti,
                         bi, si));
