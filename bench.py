@@ -1,22 +1,30 @@
 """Benchmark: one GPT2 training step (forward + backward + AdamW) as tile
-tasks on one MI355X, GPT2-small shape (12 blocks, d 768, 12 heads, inner
-3072, vocab 50257, seq 1024, batch 4) with the NNTile README's example tiles
-(seq 1024, embd 768, inner 3072, head 12, batch 4; vocab tile 768).
+tasks on one MI355X. Default workload: the wide 4-block model (d 8192, 64
+heads, inner 32768, vocab 50257, seq 1024, batch 4; 3.64 B parameters, all
+state in HBM) with large tiles (batch 4, seq 1024, embd 2048, inner 8192,
+head 16, vocab 2048) -- the largest configuration that fits one GPU. The
+GPT2-small step (12 blocks, d 768, the NNTile README's example tiles) is
+timed after it and reported under "gpt2_small".
 
 Prints ONE JSON line:
   value        tokens/s of the whole step (inputs resident in HBM)
   tflops       model TFLOP/s = 3 x forward matmul flops (causal attention
                counted over T(T+1)/2 pairs) / step time; mfma_frac = / 157.3
-  roofline     the dominant GEMM task class (largest share of a step run
-               on one stream): its algorithmic flops per launch / its
-               average launch duration, timed with HIP events on the
-               executor stream that launches it, during the timed steps
-               (every 5th launch: an event pair costs ~4 us of queue time)
+  roofline     the dominant task class (largest share of a step run on one
+               stream, attention included): its algorithmic flops per
+               launch / its average launch duration, timed with HIP events
+               on the executor stream that launches it, during the timed
+               steps (every 5th launch when a step has 5 or more: an event
+               pair costs ~4 us of queue time)
   classes      every task class's achieved throughput against its roofline
                (MFMA fp32 or HBM), from one extra step run on one stream
                with each task timed, so no kernel shares the GPU
-  cpu_baseline the fp64 oracle step timed on this host's cores on a bounded
-               sample (one of the batch's sequences), scaled to tokens/s
+  probes       on-device ceilings measured in the same run: the fp32
+               matrix-core peak (tt_probe_mfma_f32) and a 2 GiB HBM copy
+  cpu_baseline the fp64 oracle timed on this host's cores (BLAS threads =
+               the CPUs this process may run on) on a bounded sample of the
+               workload, scaled to tokens/s of the whole step (see
+               cpu_baseline())
 Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload NAME]
        [--streams S (default: 1; small tiles 4)] [--pinned --budget-gb G]
 """
@@ -365,22 +373,110 @@ def pmc_summary(paths, copy_mib: int) -> dict:
     return out
 
 
-def cpu_baseline(w, params, tokens):
-    """The fp64 oracle on the host, one sequence of the batch (bounded sample)."""
+def blas_setup():
+    """BLAS threads = the CPUs this process may run on; returns (cores,
+    vendor string) for the report."""
+    cores = len(os.sched_getaffinity(0))
+    vendor = "unknown"
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threadpool_limits(limits=cores, user_api="blas")
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            vendor = f"{info[0].get('internal_api')} {info[0].get('version')} ({info[0].get('num_threads')} threads)"
+    except Exception:  # noqa: BLE001
+        pass
+    return cores, vendor
+
+
+def cpu_baseline(w, params, tokens, sample_tokens: int = 0):
+    """The fp64 oracle on the host's cores, on a bounded sample of the step.
+
+    Small models (<= 200 M parameters): the oracle's whole step on one
+    sequence of the batch, once after a warm-up, scaled to the batch by
+    token count. Larger models: block 0 of the model plus the tied head on
+    the first `sample_tokens` tokens of sequence 0 (oracle forward and
+    backward), and the oracle's AdamW on that block's attention-projection weight; the
+    full step's time is extrapolated by model flops (forward + backward)
+    and by parameter count (AdamW), and labelled so."""
     import numpy as np
     from oracle import gpt2 as og
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # noqa: BLE001
-        cores = 1
-    sample = np.asarray(tokens[:1], np.int64)
+    cores, vendor = blas_setup()
+    s = w.shape
+    n_params = sum(int(np.prod(shp)) for _, shp, _ in synth.param_specs(s))
+    if n_params <= 200_000_000:
+        sample = np.asarray(tokens[:1], np.int64)
+        og.step(params, sample[:, :65], s.n_layer, s.n_head, lr=w.lr, wd=w.weight_decay)  # warm-up
+        t0 = time.perf_counter()
+        og.step(params, sample, s.n_layer, s.n_head, lr=w.lr, wd=w.weight_decay)
+        dt = time.perf_counter() - t0
+        return {"value": round(s.seq / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle", "blas": vendor,
+                "extrapolated": False, "seconds": round(dt, 2),
+                "sample": f"one {s.seq}-token sequence of the batch (1 of {s.batch}): the oracle's whole step "
+                          f"(fwd+bwd+AdamW, fp64 numpy) after a warm-up; tokens/s = {s.seq} / time"}
+    T = sample_tokens or min(s.seq, 256)
+    sub = {k: np.asarray(v, np.float64) for k, v in params.items()
+           if not k.startswith("h") or k.startswith("h0.")}
+    tok = np.asarray(tokens[:1, :T + 1], np.int64)
+    x, y = tok[:, :-1], tok[:, 1:]
+    og.forward(sub, x[:, :16], y[:, :16], 1, s.n_head)  # warm-up (BLAS threads, page-in)
     t0 = time.perf_counter()
-    og.step(params, sample, w.shape.n_layer, w.shape.n_head, lr=w.lr, wd=w.weight_decay)
-    dt = time.perf_counter() - t0
-    return {"value": round(w.shape.seq / dt, 2), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"one {w.shape.seq}-token sequence of the batch (1 of {w.shape.batch}), full model fwd+bwd+AdamW "
-                      f"in fp64 numpy, {dt:.1f} s"}
+    _, cache = og.forward(sub, x, y, 1, s.n_head)
+    og.backward(cache, 1, s.n_head)
+    t_fb = time.perf_counter() - t0
+    del cache
+    wfc = sub["h0.w_o"]
+    g = np.full_like(wfc, 1e-3)
+    t0 = time.perf_counter()
+    og.adamw(wfc, g, np.zeros_like(wfc), np.zeros_like(wfc), 1, w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)
+    t_opt = time.perf_counter() - t0
+    samp = synth.GPT2Shape(1, s.vocab, s.n_embd, s.n_head, s.n_inner, T, 1)
+    f_ratio = model_flops(s) / model_flops(samp)
+    p_ratio = n_params / wfc.size
+    step_s = t_fb * f_ratio + t_opt * p_ratio
+    return {"value": round(s.batch * s.seq / step_s, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "blas": vendor, "extrapolated": True, "seconds_per_step": round(step_s, 1),
+            "sample_seconds": {"fwd_bwd": round(t_fb, 2), "adamw": round(t_opt, 2)},
+            "sample": f"extrapolated: the oracle's forward+backward (fp64 numpy) of block 0 plus embedding, final "
+                      f"LayerNorm and tied head on the first {T} tokens of sequence 0 ({t_fb:.1f} s), scaled by "
+                      f"model flops x{f_ratio:.1f} to {s.n_layer} blocks x {s.batch}x{s.seq} tokens; the oracle's "
+                      f"AdamW on block 0's attention-projection weight ({wfc.size / 1e6:.0f} M parameters, {t_opt:.1f} s), scaled by "
+                      f"parameter count x{p_ratio:.1f}"}
+
+
+def probes() -> dict:
+    """On-device ceilings, in the benchmark's own process: the fp32 matrix
+    peak (a launch of the library's MFMA probe, best of 3) and the rate of a
+    2 GiB device-to-device copy (torch's copy kernel, best of 3)."""
+    import torch
+
+    import tile_task_transformer_amd as tt
+    st = torch.cuda.current_stream()
+    blocks, iters = 2048, 8192
+    out = torch.empty(blocks * 256, device="cuda")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = float("inf")
+    flops = 0.0
+    for _ in range(4):
+        a.record(st)
+        flops = tt.tt_probe_mfma_f32(st, blocks, iters, out)
+        b.record(st)
+        b.synchronize()
+        best = min(best, a.elapsed_time(b))
+    mfma = flops / (best * 1e-3) / 1e12
+    n = 2 ** 29  # 2 GiB of fp32
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty(n, device="cuda")
+    cbest = float("inf")
+    for _ in range(4):
+        a.record(st)
+        dst.copy_(src)
+        b.record(st)
+        b.synchronize()
+        cbest = min(cbest, a.elapsed_time(b))
+    del src, dst, out
+    return {"mfma_f32_tflops": round(mfma, 2), "mfma_f32_frac_of_spec": round(mfma / MFMA_FP32_PEAK, 4),
+            "hbm_copy_GBps": round(2 * 4 * n / (cbest * 1e-3) / 1e9, 1)}
 
 
 def main(argv=None):
@@ -388,7 +484,9 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="gpt2_small", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--workload", default="wide4", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--also", default="gpt2_small",
+                    help="a second workload timed after the first and reported under its name ('' = none)")
     ap.add_argument("--streams", type=int, default=0,
                     help="executor streams (0 = measured best per workload: 1; small tiles 4; pinned 1)")
     ap.add_argument("--heavy-gflops", type=float, default=0.0,
@@ -415,11 +513,6 @@ def main(argv=None):
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
         return 2
 
-    import torch
-
-    from tile_task_transformer_amd import _lib as L
-    from tile_task_transformer_amd.runtime import Context, GPT2
-
     w = synth.WORKLOADS[a.workload]
     if a.streams <= 0:
         # measured on MI355X: many small tasks need concurrency (small tiles:
@@ -439,64 +532,95 @@ def main(argv=None):
             print(f"{k:14s} {v['us']:9.1f} us  {v['achieved']:8.1f} {v['unit']:16s} {100 * v['frac']:5.1f}%",
                   file=sys.stderr)
         return 0
+    probe = probes()
+    print(f"[bench] probes: {probe}", file=sys.stderr, flush=True)
+    out, keep = run(w, a, a.streams, a.breakdown, probe)
+    out["probes"] = probe
+    if a.also and a.also != a.workload:
+        w2 = synth.WORKLOADS[a.also]
+        o2, _ = run(w2, a, {"wide4_small_tiles": 4}.get(a.also, 1), "", probe, steps=max(a.steps, 10),
+                    warmup=max(a.warmup, 3), want_params=False)
+        out[a.also] = {k: o2[k] for k in ("value", "unit", "ms_per_step", "tflops", "mfma_frac", "tasks_per_step",
+                                          "loss", "roofline")}
+        out[a.also]["config"] = o2["config"]
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, keep["params"], keep["tokens"])
+        cb = out["cpu_baseline"]
+        cb["gpu_speedup"] = round(out["value"] / cb["value"], 1)
+        print(f"[bench] cpu baseline {cb['value']} tokens/s on {cb['cores']} cores", file=sys.stderr, flush=True)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def run(w, a, streams, breakdown_path, probe, steps=None, warmup=None, want_params=True):
+    """Time `steps` steps of workload w after `warmup` ones; returns the JSON
+    fields and (if want_params) the host parameters and tokens the CPU
+    baseline samples."""
+    import torch
+
+    from tile_task_transformer_amd import _lib as L
+    from tile_task_transformer_amd.runtime import Context, GPT2
+    steps = steps or a.steps
+    warmup = a.warmup if warmup is None else warmup
     s, t = w.shape, w.tiles
     specs = synth.param_specs(s)
     t0 = time.perf_counter()
-    params = synth.init_params(s, seed=0, threads=min(16, os.cpu_count() or 1))
+    params = synth.init_params(s, seed=0, threads=min(16, len(os.sched_getaffinity(0))))
     tokens = synth.token_stream(s, seed=1)
     home = L.TT_HOME_PINNED_HOST if a.pinned else L.TT_HOME_DEVICE
-    ctx = Context(0, n_streams=a.streams, window=4096, device_budget=int(a.budget_gb * 2 ** 30))
+    ctx = Context(0, n_streams=streams, window=4096, device_budget=int(a.budget_gb * 2 ** 30))
     if a.heavy_gflops > 0:
         ctx.heavy_lane(a.heavy_gflops * 1e9)
     model = GPT2(ctx, s, t, param_home=home)
     model.set_params(params, specs)
-    if a.no_cpu_baseline:
+    if not want_params or a.no_cpu_baseline:
         params = None  # the oracle sample is not needed: free the host copy
     tok = torch.from_numpy(tokens.astype(np.int32)).cuda()
     hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
-    print(f"[bench] {a.workload}: parameters ready in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    print(f"[bench] {w.name}: parameters ready in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
 
-    for k in range(a.warmup):
+    for k in range(warmup):
         model.step(tok, **hp)
-        print(f"[bench] warmup step {k + 1}/{a.warmup} loss {model.loss():.4f}", file=sys.stderr, flush=True)
+        print(f"[bench] warmup step {k + 1}/{warmup} loss {model.loss():.4f}", file=sys.stderr, flush=True)
     print(f"[bench] {model.task_count()} tasks/step", file=sys.stderr, flush=True)
 
     # one step on a single stream with every task timed: each kernel has the
     # GPU to itself, which gives the per-class rooflines
-    breakdown, classes = {}, {}
-    if a.breakdown:
-        ctx.streams_active(1)
-        ctx.profile("*")
-        model.step(tok, **hp)
-        breakdown = ctx.profile_take()
-        ctx.profile(None)
-        ctx.streams_active(a.streams)
-        classes = class_rooflines(breakdown, s)
-        os.makedirs(os.path.dirname(a.breakdown) or ".", exist_ok=True)
-        with open(a.breakdown, "w") as f:
-            json.dump({"workload": a.workload, "tasks": breakdown, "classes": classes}, f, indent=1, sort_keys=True)
-        print("[bench] serialized step by class (ms, achieved, % of roofline):", file=sys.stderr)
-        for k, v in sorted(classes.items(), key=lambda kv: -kv[1]["ms"]):
-            print(f"  {k:14s} {v['ms']:9.2f} ms  {v['achieved']:9.1f} {v['unit']:8s} {100 * v['frac']:5.1f}%",
-                  file=sys.stderr)
-        print(f"  serialized total {sum(b['total_ms'] for b in breakdown.values()):.2f} ms", file=sys.stderr,
-              flush=True)
+    ctx.streams_active(1)
+    ctx.profile("*")
+    model.step(tok, **hp)
+    breakdown = ctx.profile_take()
+    ctx.profile(None)
+    ctx.streams_active(streams)
+    classes = class_rooflines(breakdown, s)
+    if breakdown_path:
+        os.makedirs(os.path.dirname(breakdown_path) or ".", exist_ok=True)
+        with open(breakdown_path, "w") as f:
+            json.dump({"workload": w.name, "tasks": breakdown, "classes": classes}, f, indent=1, sort_keys=True)
+    print(f"[bench] {w.name}: serialized step by class (ms, achieved, % of roofline):", file=sys.stderr)
+    for k, v in sorted(classes.items(), key=lambda kv: -kv[1]["ms"]):
+        print(f"  {k:14s} {v['ms']:9.2f} ms  {v['achieved']:9.1f} {v['unit']:8s} {100 * v['frac']:5.1f}%",
+              file=sys.stderr)
+    print(f"  serialized total {sum(b['total_ms'] for b in breakdown.values()):.2f} ms", file=sys.stderr,
+          flush=True)
     work = class_work(s)
-    mfma_ms = {k: v["ms"] for k, v in classes.items() if v["bound"] == "mfma" and not k.startswith("attn")}
+    # the dominant class: the largest share of the serialized step among the
+    # matrix-core classes (GEMM and attention alike)
+    mfma_ms = {k: v["ms"] for k, v in classes.items() if v["bound"] == "mfma"}
     dominant = max(mfma_ms, key=mfma_ms.get) if mfma_ms else "fc"
 
     # timed region: K steps back to back, every PROFILE_EVERY-th task of the
     # dominant class bracketed by events (an event pair costs ~4 us of queue
     # time; 5 is prime to the 66 vocab tiles of GPT2-small, so the sample
-    # rotates through every tile, the ragged last one included)
-    # (a class with fewer launches per step than that is timed at every launch)
+    # rotates through every tile, the ragged last one included); a class
+    # with fewer launches per step than that is timed at every launch
     every = PROFILE_EVERY if classes.get(dominant, {}).get("launches", PROFILE_EVERY) >= PROFILE_EVERY else 1
     ctx.profile(dominant, every=every)
     ctx.reset_stats()
     torch.cuda.synchronize()
     ctx.wait()
     t0 = time.perf_counter()
-    for _ in range(a.steps):
+    for _ in range(steps):
         model.step(tok, **hp)
     ctx.wait()
     torch.cuda.synchronize()
@@ -506,49 +630,52 @@ def main(argv=None):
     prof = ctx.profile_take().get(dominant, {})
     ctx.profile(None)
 
-    ms = 1e3 * elapsed / a.steps
-    tok_s = s.batch * s.seq / (elapsed / a.steps)
-    tflops = model_flops(s) / (elapsed / a.steps) / 1e12
+    ms = 1e3 * elapsed / steps
+    tok_s = s.batch * s.seq / (elapsed / steps)
+    tflops = model_flops(s) / (elapsed / steps) / 1e12
     launches = prof.get("count", 0)
-    per_step = classes[dominant]["launches"] if dominant in classes else launches * every / a.steps
+    per_step = classes[dominant]["launches"] if dominant in classes else launches * every / steps
     per_launch = work[dominant][1] / per_step if launches else float("nan")
     avg_ms = prof["total_ms"] / launches if launches else float("nan")
     achieved = per_launch / (avg_ms * 1e-3) / 1e12
+    largest = max(classes, key=lambda k: classes[k]["ms"]) if classes else None
     out = {
-        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
-        "warmup": a.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": a.workload, "global_batch": s.batch, "seq_len": s.seq, "n_layer": s.n_layer,
+        "config": {"workload": w.name, "global_batch": s.batch, "seq_len": s.seq, "n_layer": s.n_layer,
                    "n_embd": s.n_embd, "n_inner": s.n_inner, "n_head": s.n_head, "vocab": s.vocab,
                    "tiles": {"batch": t.batch, "seq": t.seq, "embd": t.embd, "inner": t.inner, "head": t.head,
-                             "vocab": t.vocab}, "streams": a.streams, "heavy_gflops": a.heavy_gflops,
+                             "vocab": t.vocab}, "streams": streams, "heavy_gflops": a.heavy_gflops,
                    "param_home": "pinned_host" if a.pinned else "device"},
         "tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_FP32_PEAK, 4),
+        "mfma_frac_of_probe": round(tflops / probe["mfma_f32_tflops"], 4) if probe else None,
         "tasks_per_step": model.task_count(), "loss": round(loss, 5),
-        "host_submit_ms_per_step": round(1e3 * st["submit_seconds"] / a.steps, 3),
+        "host_submit_ms_per_step": round(1e3 * st["submit_seconds"] / steps, 3),
         "roofline": {"bound": "mfma", "kernel": f"{KERNEL_OF.get(dominant, 'tile_gemm')}[{dominant}]",
                      "achieved": round(achieved, 2),
                      "peak": MFMA_FP32_PEAK, "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP32_PEAK, 4),
-                     "traffic": traffic_bytes(a.workload, dominant), "flops_per_launch": per_launch,
+                     "frac_of_probe": round(achieved / probe["mfma_f32_tflops"], 4) if probe else None,
+                     "traffic": traffic_bytes(w.name, dominant), "flops_per_launch": per_launch,
                      "avg_launch_ms": round(avg_ms, 4),
                      "launches_timed": launches, "launches_per_step": per_step},
+        "largest_class": ({"class": largest, "frac": classes[largest]["frac"], "ms": classes[largest]["ms"]}
+                          if largest else None),
     }
     if a.pinned:
-        out["residency"] = {k: st[k] / a.steps for k in ("h2d_bytes", "d2h_bytes", "evictions", "prefetches")}
+        out["residency"] = {k: st[k] / steps for k in ("h2d_bytes", "d2h_bytes", "evictions", "prefetches")}
         out["residency"]["link_GBps"] = round((st["h2d_bytes"] + st["d2h_bytes"]) / elapsed / 1e9, 2)
         out["residency"]["budget_gb"] = a.budget_gb
         out["residency"]["probe"] = link_probe()
-    if classes:
-        out["classes"] = {k: {"frac": v["frac"], "achieved": v["achieved"], "unit": v["unit"], "ms": v["ms"]}
-                          for k, v in classes.items()}
-    print(f"[bench] timed {a.steps} steps: {ms:.2f} ms/step, {tok_s:.0f} tokens/s, {tflops:.1f} TFLOP/s",
+    out["classes"] = {k: {"frac": v["frac"], "achieved": v["achieved"], "unit": v["unit"], "ms": v["ms"]}
+                      for k, v in classes.items()}
+    print(f"[bench] {w.name}: timed {steps} steps: {ms:.2f} ms/step, {tok_s:.0f} tokens/s, {tflops:.1f} TFLOP/s",
           file=sys.stderr, flush=True)
     model.close()
     ctx.close()
-    if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, params, tokens)
-    print(json.dumps(out), flush=True)
-    return 0
+    del tok
+    torch.cuda.empty_cache()
+    return out, {"params": params, "tokens": tokens}
 
 
 if __name__ == "__main__":

@@ -59,6 +59,17 @@ const char* tt_last_error(void);
 /* Library version string, e.g. "tiletask 0.1 gfx950". */
 const char* tt_version(void);
 
+/* tt_probe_mfma_f32 -- device peak probe, not part of the step: `blocks`
+ * workgroups of 4 waves each issue `iters` x 4 independent fp32 matrix-core
+ * products (32x32x2, 4096 flops each) with no memory traffic, so the launch
+ * time gives the fp32 matrix throughput the GEMM and attention tiles are
+ * measured against (published MI355X figure: 157.3 TFLOP/s). *flops (host,
+ * may be NULL) receives blocks * 4 * iters * 4 * 4096. out: DEVICE float
+ * [blocks * 256] (one sum per lane, so the work is not optimised away).
+ * TT_ERR_ARG for blocks outside 1..65535, iters outside 1..2^24 or a null
+ * out. Asynchronous on `stream`. */
+int tt_probe_mfma_f32(void* stream, int64_t blocks, int64_t iters, float* out, double* flops);
+
 /* ============================================================ 1. tile ops */
 
 /* tile_gemm -- the linear layer's tile task (forward Y = X W + b and its
@@ -513,6 +524,208 @@ int tt_submit_gemm(tt_ctx* ctx, int transA, int transB, float alpha,
                    float beta, tt_tensor* C, const int64_t* ic);
 /* Every element of tile idx = value (access W). */
 int tt_submit_fill(tt_ctx* ctx, tt_tensor* t, const int64_t* idx, float value);
+/* ---- generic task submission: every tile op as a task over tiled tensors
+ *
+ * The pith.science review of NNTile ("What carries the argument") describes
+ * the programming model: every layer of the network is expressed as tasks
+ * that read and write a few tiles, submitted in program order; the runtime
+ * derives the ordering from those reads and writes. tt_submit is that
+ * interface for every tile op of this library: `op` names the operation,
+ * `tiles` lists the tiles it touches in the order given below, `scalars`
+ * points at the op's scalar struct (scalars_size = its sizeof; NULL and 0
+ * for ops without one). The access mode of each tile (read, write, update)
+ * is implied by the op and its scalars, as listed; the executor turns them
+ * into read-after-write, write-after-read and write-after-write edges.
+ *
+ * Tiles are addressed by tensor and tile index. A 2-D "matrix view" of a
+ * tile is rows x cols where rows is the product of the tile's extents over
+ * all axes but the last and cols the last extent (for a tensor created with
+ * tt_tensor_create). Shapes are checked at submit time (TT_ERR_SHAPE), the
+ * argument list and dtypes too (TT_ERR_ARG); errors of the launch itself
+ * latch in the context and are reported by the next submit or tt_wait.
+ * Ops that need scratch memory use the context's per-stream workspace,
+ * enlarged at submit time when needed (this drains the context first, so
+ * the first submit of a larger op may block).
+ */
+typedef struct {
+    tt_tensor* tensor;
+    int64_t tile[TT_MAX_DIMS];
+} tt_tile;
+
+/* TT_OP_FILL: tiles d_0..d_{n-1} (1 <= n <= TT_FILL_MAX_TILES, f32), each
+ * written (W) with `value`. Scalars tt_op_fill. */
+#define TT_OP_FILL 1
+typedef struct { float value; } tt_op_fill;
+
+/* TT_OP_GEMM -- one tile of a linear layer (tile_gemm; layer list: review,
+ * "What carries the argument"): C = alpha op(A) op(B) + beta C, then the
+ * epilogue. tiles: A, B, C, then bias (if epilogue & TT_EPI_BIAS; n
+ * elements), res (if & TT_EPI_RES; m x n), aux (if & (TT_EPI_GELU |
+ * TT_EPI_GELU_BWD); m x n), in that order. Accesses: A, B, bias, res read;
+ * C written (beta == 0 or GELU) else updated; aux updated by GELU when
+ * beta != 0, written when beta == 0, read by GELU_BWD. split_k != 0 lets a
+ * launch with few output blocks and a long K split K over the workspace
+ * (deterministic). Scalars tt_op_gemm.
+ * TT_OP_GEMM_BATCH -- independent products sharing K and the scalars
+ * (tile_gemm_batch; the tied head's per-vocab-tile products): tiles A_0,
+ * B_0, C_0, A_1, B_1, C_1, ... (1..96 products); epilogue must be 0. C_t
+ * written (beta == 0) or updated.
+ * TT_OP_GEMM_KSUM -- a sum of products into one tile (tile_gemm_ksum: a
+ * linear layer's input gradient summed over the tiles of its output axis):
+ * tiles C, A_0, B_0, A_1, B_1, ... (1..96 pairs); C = alpha sum_t A_t op(B_t)
+ * + beta C with transA = 0. */
+#define TT_OP_GEMM       2
+#define TT_OP_GEMM_BATCH 3
+#define TT_OP_GEMM_KSUM  4
+typedef struct {
+    int transA, transB, epilogue;
+    float alpha, beta;
+    int split_k;
+} tt_op_gemm;
+
+/* TT_OP_LAYERNORM_FWD -- layer norm of one block of rows whose features are
+ * split over n tiles (review, "What carries the argument"; definition after
+ * the "Layer Normalization" paper on the arXiv index page): tiles x_0..x_{n-1}
+ * (rows x c_i), gamma_0..gamma_{n-1} (c_i), beta_0..beta_{n-1} (c_i), stats
+ * (>= 2*rows floats: mean, rstd per row), y_0..y_{n-1} (rows x c_i) -- 4n+1
+ * tiles. Reads x, gamma, beta; writes stats and y. Statistics over all
+ * sum(c_i) features, biased variance, eps inside the square root.
+ * Scalars tt_op_layernorm (eps).
+ * TT_OP_LAYERNORM_BWD -- its gradient: tiles dy_0.., x_0.., gamma_0..,
+ * stats, dx_0.., dgamma_0.., dbeta_0.. -- 6n+1 tiles. Reads dy, x, gamma,
+ * stats; writes dx (updates it, adding, when dx_acc != 0); updates
+ * dgamma += sum_rows dy*xhat and dbeta += sum_rows dy (fixed order). */
+#define TT_OP_LAYERNORM_FWD 5
+#define TT_OP_LAYERNORM_BWD 6
+typedef struct {
+    float eps;
+    int dx_acc;
+} tt_op_layernorm;
+
+/* TT_OP_ATTENTION_FWD -- causal attention of one (query tile, key tile)
+ * pair (tile_attention_fwd; "Attention Is All You Need", arXiv index page
+ * "Builds on"): tiles Q, K, V, O, ml, lse. Q and O are 4-D tiles [batch,
+ * q_len, heads, hd], K and V [batch, k_len, heads, hd] (same batch, heads,
+ * hd); ml holds >= 2*batch*heads*q_len floats, lse >= batch*heads*q_len.
+ * Reads Q, K, V; O written when first, else updated; ml written (first) or
+ * updated, not touched when first && last; lse written when last, else not
+ * touched. Scalars tt_op_attention (q_off, k_off: global positions of the
+ * tiles' first query and key; scale usually 1/sqrt(hd)).
+ * TT_OP_ATTENTION_PREP -- tiles O, dO, Dvec: Dvec = rowsum(dO * O) per
+ * (b, h, query) (reads O, dO; writes Dvec).
+ * TT_OP_ATTENTION_BWD -- tiles Q, K, V, dO, lse, Dvec, dQ, dK, dV:
+ * dQ += , dK += , dV += the pair's gradient (tile_attention_bwd
+ * TT_ATT_GRAD); reads the first six; dQ written unless acc_dq (then
+ * updated), dK and dV written unless acc_dkv. */
+#define TT_OP_ATTENTION_FWD  7
+#define TT_OP_ATTENTION_PREP 8
+#define TT_OP_ATTENTION_BWD  9
+typedef struct {
+    int64_t q_off, k_off;
+    int first, last;
+    int acc_dq, acc_dkv;
+    float scale;
+} tt_op_attention;
+
+/* Cross-entropy over vocab tiles (NNTile README, "Minimal working GPT
+ * example": the loss is the mean over the batch's tokens), rows = tokens of
+ * one token tile. The vocab offset of a logits tile is its tile index along
+ * the tensor's last axis times that axis's tile size.
+ * TT_OP_XENTROPY_STATS -- tiles labels (i32, rows), z_0..z_{n-1} (rows x
+ * v_j, v_j <= 2048), parts_0..parts_{n-1} (>= 3*rows floats each, equally
+ * spaced in memory, e.g. consecutive tiles of one tensor): per tile the
+ * (row max, sum exp, picked target logit). Reads labels, z; writes parts.
+ * TT_OP_XENTROPY_MERGE -- tiles lse (rows), row_loss (rows),
+ * parts_0..parts_{n-1}: lse = merged logsumexp, row_loss = lse - target
+ * logit. Reads parts; writes lse and row_loss.
+ * TT_OP_XENTROPY_LOSS -- tiles row_loss, loss (1 float): loss =
+ * (accumulate ? loss : 0) + inv_n * sum row_loss. Reads row_loss; loss
+ * written, or updated when accumulate.
+ * TT_OP_XENTROPY_GRAD -- tiles labels, lse, z_0..z_{n-1}: every z_j replaced
+ * in place by (softmax - onehot(label)) * inv_n. Reads labels, lse; updates
+ * z. Scalars tt_op_xentropy. */
+#define TT_OP_XENTROPY_STATS 10
+#define TT_OP_XENTROPY_MERGE 11
+#define TT_OP_XENTROPY_LOSS  12
+#define TT_OP_XENTROPY_GRAD  13
+typedef struct {
+    int accumulate;
+    float inv_n;
+} tt_op_xentropy;
+
+/* Optimiser steps (NNTile README, "Minimal working GPT example": fused
+ * AdamW; the review's "What carries the argument" lists the Adam/SGD
+ * update as tile tasks). Scalars tt_op_optim.
+ * TT_OP_ADAMW -- tiles bias_corr (2 floats, from TT_OP_ADAMW_ADVANCE), then
+ * p_i, g_i, m_i, v_i for i < n (1 <= n <= TT_ADAMW_MAX_TILES): the update of
+ * tile_fused_adamw on each. Reads bias_corr and g; updates p, m, v.
+ * TT_OP_ADAMW_ADVANCE -- tiles step (i32, 1 element), bias_corr (2 floats):
+ * t = ++step, bias_corr = {1 - beta1^t, 1 - beta2^t}. Updates step, writes
+ * bias_corr.
+ * TT_OP_SGD -- tiles p_i, g_i (1 <= n <= TT_SGD_MAX_TILES pairs): p -= lr g.
+ * Reads g; updates p. */
+#define TT_OP_ADAMW         14
+#define TT_OP_ADAMW_ADVANCE 15
+#define TT_OP_SGD           16
+typedef struct {
+    float lr, beta1, beta2, eps, weight_decay;
+} tt_op_optim;
+
+/* Embedding layer (review, "What carries the argument"). Scalars
+ * tt_op_embedding: seq_len = rows per sequence in the token tile (row r has
+ * position r % seq_len within the wpe tile).
+ * TT_OP_EMBEDDING_FWD -- tiles ids (i32, rows), wpe (positions x cols), out
+ * (rows x cols), wte_0..wte_{n-1}: all vocab tiles of one embd tile column of
+ * the token table, in vocab order. out = wte[id] + wpe[pos]; an id outside
+ * [0, vocab) gives a NaN row. Reads ids, wpe, wte; writes out.
+ * TT_OP_EMBEDDING_INDEX -- tiles ids, sorted, perm (i32, rows <= 65536):
+ * stable sort of the ids. Reads ids; writes sorted, perm.
+ * TT_OP_EMBEDDING_BWD -- tiles dh (rows x cols), sorted, perm,
+ * dwte_0..dwte_{n-1} (as in FWD): dwte[id] += sum of the dh rows with that
+ * id, in row order. Reads dh, sorted, perm; updates dwte.
+ * TT_OP_EMBEDDING_POS_BWD -- tiles dh, dwpe: dwpe[pos] += sum over the
+ * tile's sequences of dh. Reads dh; updates dwpe. */
+#define TT_OP_EMBEDDING_FWD     17
+#define TT_OP_EMBEDDING_INDEX   18
+#define TT_OP_EMBEDDING_BWD     19
+#define TT_OP_EMBEDDING_POS_BWD 20
+typedef struct { int64_t seq_len; } tt_op_embedding;
+
+/* TT_OP_REDUCE_ROWS -- bias gradients of a linear layer (column sums):
+ * tiles X_0, out_0, X_1, out_1, ... (1..16 pairs, equal row counts):
+ * out_t = (beta ? out_t : 0) + sum_rows X_t in a fixed order. Reads X;
+ * out written, or updated when beta. Scalars tt_op_reduce. */
+#define TT_OP_REDUCE_ROWS 21
+typedef struct { int beta; } tt_op_reduce;
+
+/* TT_OP_SPLIT_TOKENS -- the token batch (NNTile README, "Minimal working
+ * GPT example": windows of a token stream): tiles tokens (i32 [B, T+1] in a
+ * single tile), ids, labels (tile (bi, si) of i32 [B, T] tensors tiled [bt,
+ * st]): ids = windows bi*bt.. at positions si*st.., labels the same shifted
+ * by one. Reads tokens; writes ids and labels. No scalars.
+ * TT_OP_COPY_IN -- tiles dst: dst = tile_bytes(dst) bytes copied from the
+ * DEVICE address src (device to device). The source is read when the task
+ * runs, which can be after tt_submit returns: it must stay allocated and
+ * unchanged until then (tt_wait, or work ordered after the context with
+ * tt_ctx_join_stream). Writes dst. Scalars tt_op_copy. */
+#define TT_OP_SPLIT_TOKENS 22
+#define TT_OP_COPY_IN      23
+typedef struct { const void* src; } tt_op_copy;
+
+int tt_submit(tt_ctx* ctx, int op, const tt_tile* tiles, int ntiles, const void* scalars, size_t scalars_size);
+
+/* Ordering against streams the context does not own (e.g. a framework's
+ * current stream), on the device, without blocking the host:
+ * tt_ctx_wait_stream -- tasks launched from now on run after the work
+ *   queued on `stream` so far (an event recorded there, waited on by every
+ *   executor stream);
+ * tt_ctx_join_stream -- work queued on `stream` from now on runs after
+ *   every task the context has launched so far (each executor stream's
+ *   tail, waited on by `stream`). Tasks still held in the submit window are
+ *   launched first. */
+int tt_ctx_wait_stream(tt_ctx* ctx, void* stream);
+int tt_ctx_join_stream(tt_ctx* ctx, void* stream);
+
 /* Launch everything queued and wait for the GPU; returns the first latched
  * error, if any. */
 int tt_wait(tt_ctx* ctx);

@@ -92,6 +92,7 @@ PP = C.POINTER(C.c_void_p)
 SIGNATURES = {
     "tt_last_error": (C.c_char_p, []),
     "tt_version": (C.c_char_p, []),
+    "tt_probe_mfma_f32": (I, [P, I64, I64, P, C.POINTER(C.c_double)]),
     "tile_gemm": (I, [P, I, I, I64, I64, I64, F, P, I64, P, I64, F, P, I64, I, P, P, I64, P, I64]),
     "tile_gemm_ws": (I, [P, I, I, I64, I64, I64, F, P, I64, P, I64, F, P, I64, I, P, P, I64, P, I64, P, SZ]),
     "tile_gemm_workspace": (SZ, [I64, I64, I64]),

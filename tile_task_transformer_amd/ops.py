@@ -21,6 +21,7 @@ __all__ = [
     "tile_adamw_advance", "tile_sgd", "tile_sgd_multi",
     "tile_embedding_fwd", "tile_embedding_index", "tile_embedding_bwd", "tile_reduce_rows",
     "tile_reduce_rows_workspace", "tile_reduce_rows_multi", "tile_fill", "tile_fill_multi", "tile_split_tokens",
+    "tt_probe_mfma_f32",
     "TT_EPI_NONE", "TT_EPI_BIAS", "TT_EPI_RES", "TT_EPI_GELU", "TT_EPI_GELU_BWD", "TT_LN_PARTIAL",
     "TT_LN_MERGE", "TT_LN_APPLY", "TT_LN_FUSED", "TT_SM_STATS", "TT_SM_MERGE", "TT_SM_APPLY", "TT_XE_LOSS",
     "TT_XE_GRAD", "TT_XE_STATS", "TT_ATT_PREP", "TT_ATT_GRAD", "TT_EMB_TOKEN", "TT_EMB_POS",
@@ -218,3 +219,11 @@ def tile_fill_multi(stream, dsts, value):
 
 def tile_split_tokens(stream, batch, seq, tokens, ids, labels):
     return check(lib.tile_split_tokens(stream_handle(stream), batch, seq, ptr(tokens), ptr(ids), ptr(labels)))
+
+
+def tt_probe_mfma_f32(stream, blocks, iters, out):
+    """Launch the fp32 matrix-core peak probe; returns its flop count."""
+    import ctypes as C
+    f = C.c_double()
+    check(lib.tt_probe_mfma_f32(stream_handle(stream), blocks, iters, ptr(out), C.byref(f)))
+    return f.value
