@@ -213,6 +213,36 @@ int tile_layernorm_bwd(void* stream, int phase, int64_t rows, int64_t cols, int6
                        void* workspace);
 size_t tile_layernorm_bwd_workspace(int64_t rows, int64_t cols);
 
+/* tile_layernorm_fwd_multi / tile_layernorm_bwd_multi -- the layer norm of
+ * one block of rows whose features are split over `count` tiles (2..16),
+ * in one pass over the tiles instead of the partial / merge / apply phases
+ * (layer list: pith.science review, "What carries the argument";
+ * definition after the "Layer Normalization" paper on the arXiv index
+ * page). Tile t is rows x cols[t] floats, row-major with leading dimension
+ * cols[t], at x[t] (dy[t], y[t], dx[t]); gamma[t], beta[t], dgamma[t],
+ * dbeta[t] hold cols[t] floats. x, gamma, beta, dy, y, dx and the workspace
+ * are DEVICE memory aligned to 16 bytes; the pointer arrays and cols are
+ * HOST arrays read before the call returns. Every tile is as wide as the
+ * first except the last, which may be narrower; widths are multiples of 4
+ * and sum to at most 16384 (TT_ERR_SHAPE otherwise).
+ *   forward:  stats[r*2 + {0,1}] = (mean, rstd) of row r over all the tiles'
+ *             features; y = (x - mean) * rstd * gamma + beta.
+ *   backward: dx = rstd*(dxhat - mean(dxhat) - xhat*mean(dxhat*xhat)) with
+ *             dxhat = dy*gamma, added to dx's contents when dx_acc != 0;
+ *             dgamma += sum_rows dy*xhat, dbeta += sum_rows dy, in a fixed
+ *             order through `workspace` (at least
+ *             tile_layernorm_bwd_multi_workspace(rows, sum of cols) bytes,
+ *             not used concurrently by another launch).
+ * Same arithmetic as the single-tile FUSED phase up to summation order. */
+int tile_layernorm_fwd_multi(void* stream, int count, int64_t rows, const int64_t* cols, const float* const* x,
+                             const float* const* gamma, const float* const* beta, float* stats, float* const* y,
+                             float eps);
+int tile_layernorm_bwd_multi(void* stream, int count, int64_t rows, const int64_t* cols, const float* const* dy,
+                             const float* const* x, const float* const* gamma, const float* stats, float* const* dx,
+                             int dx_acc, float* const* dgamma, float* const* dbeta, void* workspace,
+                             size_t workspace_bytes);
+size_t tile_layernorm_bwd_multi_workspace(int64_t rows, int64_t total_cols);
+
 /* tile_softmax -- row softmax of a tile whose columns are one tile of a
  * longer row (layer list: pith.science review, "What carries the argument").
  * Element (r, c) of the tile is logit x = scale * X[r*ldx + c] at global
@@ -485,6 +515,13 @@ int tt_tensor_create(tt_ctx* ctx, int ndim, const int64_t* shape, const int64_t*
 int tt_tensor_wrap(tt_ctx* ctx, int ndim, const int64_t* shape, const int64_t* tile_shape,
                    int dtype, void* device_base, tt_tensor** out);
 int tt_tensor_destroy(tt_tensor* t);
+/* Matrix view of every tile: rows = product of the tile's extents over the
+ * first k axes, cols = product over the rest (0 <= k <= ndim; default
+ * ndim - 1). Token-major activations with a head axis, [B, T, H, hd] tiled
+ * [bt, st, ht, hd], take k = 2 so that a tile is the [bt*st, ht*hd] matrix a
+ * linear layer writes. Set it before the tensor's first task. TT_ERR_ARG for
+ * k out of range. */
+int tt_tensor_set_matrix_split(tt_tensor* t, int k);
 int64_t tt_tensor_bytes(const tt_tensor* t);
 /* Number of tiles along axis d, and the total. */
 int tt_tensor_grid(const tt_tensor* t, int64_t* grid_out /* ndim */, int64_t* ntiles);
@@ -568,12 +605,13 @@ typedef struct { float value; } tt_op_fill;
  * (deterministic). Scalars tt_op_gemm.
  * TT_OP_GEMM_BATCH -- independent products sharing K and the scalars
  * (tile_gemm_batch; the tied head's per-vocab-tile products): tiles A_0,
- * B_0, C_0, A_1, B_1, C_1, ... (1..96 products); epilogue must be 0. C_t
- * written (beta == 0) or updated.
+ * B_0, C_0, A_1, B_1, C_1, ... (one or more products; more than 72 make
+ * several launches); epilogue must be 0. C_t written (beta == 0) or
+ * updated.
  * TT_OP_GEMM_KSUM -- a sum of products into one tile (tile_gemm_ksum: a
  * linear layer's input gradient summed over the tiles of its output axis):
- * tiles C, A_0, B_0, A_1, B_1, ... (1..96 pairs); C = alpha sum_t A_t op(B_t)
- * + beta C with transA = 0. */
+ * tiles C, A_0, B_0, A_1, B_1, ... (one or more pairs; more than 96 make
+ * several launches); C = alpha sum_t A_t op(B_t) + beta C with transA = 0. */
 #define TT_OP_GEMM       2
 #define TT_OP_GEMM_BATCH 3
 #define TT_OP_GEMM_KSUM  4
@@ -681,8 +719,10 @@ typedef struct {
  * TT_OP_EMBEDDING_INDEX -- tiles ids, sorted, perm (i32, rows <= 65536):
  * stable sort of the ids. Reads ids; writes sorted, perm.
  * TT_OP_EMBEDDING_BWD -- tiles dh (rows x cols), sorted, perm,
- * dwte_0..dwte_{n-1} (as in FWD): dwte[id] += sum of the dh rows with that
- * id, in row order. Reads dh, sorted, perm; updates dwte.
+ * dwte_0..dwte_{n-1}: consecutive vocab tiles of one embd tile column of the
+ * table's gradient, in vocab order (all of them, or a run: ids outside the
+ * run are skipped): dwte[id] += sum of the dh rows with that id, in row
+ * order. Reads dh, sorted, perm; updates dwte.
  * TT_OP_EMBEDDING_POS_BWD -- tiles dh, dwpe: dwpe[pos] += sum over the
  * tile's sequences of dh. Reads dh; updates dwpe. */
 #define TT_OP_EMBEDDING_FWD     17

@@ -254,3 +254,27 @@ def test_gpt2_rejects_bad_tiles():
             with pytest.raises(L.TTError) as e:
                 GPT2(ctx, shape, bad)
             assert e.value.code == L.TT_ERR_SHAPE
+
+
+def test_out_of_core_wide_model_step_dag(tmp_path):
+    """The 26.6 B-parameter out-of-core model (8 blocks, d 16384, inner
+    65536, vocab 50257, batch 2) with parameters, gradients and moments in
+    pinned host RAM, built as a dry run: the whole step's task graph is
+    race free, with the task count the tiling implies."""
+    w = synth.WORKLOADS["wide8_ooc"]
+    with Context(L.TT_DEVICE_DRYRUN, n_streams=1, window=1 << 20) as ctx:
+        model = GPT2(ctx, w.shape, w.tiles, param_home=L.TT_HOME_PINNED_HOST)
+        model.step(None)
+        n = model.task_count()
+        dag = ctx.dump_dag(str(tmp_path / "ooc.jsonl"))
+        model.close()
+    assert n == len(dag)
+    _check_races(dag)
+    by = {}
+    for r in dag:
+        by[r["label"]] = by.get(r["label"], 0) + 1
+    # 8 embd tiles, 8 inner tiles, 8 head tiles, 25 vocab tiles, one token tile
+    assert by["attn_fwd"] == by["attn_bwd"] == 8 * 8
+    assert by["ln_fwd"] == 2 * 8 + 1 and by["ln_bwd"] == 2 * 8 + 1
+    assert by["head_dx"] == 8 and by["emb_dw"] == 8 * 25  # pinned table: one task per vocab tile
+

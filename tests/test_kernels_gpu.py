@@ -364,6 +364,67 @@ def test_layernorm_bwd_fused(rows, cols):
     assert_rel(host(dbet), rdb, 1e-4, 1e-4, "dbeta")
 
 
+@pytest.mark.parametrize("rows,cols", [
+    (96, [64, 64, 32]),            # 160 features: 256-thread rows, narrower last tile, ragged row blocks
+    (33, [512, 512, 512, 512]),    # 2048 features: 512-thread rows
+    (64, [2048, 2048, 2048, 1024]),  # 7168: 1024 threads, 2 float4 each
+    (20, [4096, 4096, 4096, 4096]),  # 16384: 4 float4 each (the widest model's row)
+])
+@pytest.mark.parametrize("dx_acc", [0, 1])
+def test_layernorm_multi_tile_one_pass(rows, cols, dx_acc):
+    """LayerNorm over several feature tiles in one pass (forward and
+    backward) against the oracle on the whole row; bitwise reproducible."""
+    total = sum(cols)
+    x = synth.rand_normal((rows, total), 41, std=2.0) + 0.3
+    g = synth.rand_normal((total,), 42) + 1
+    b = synth.rand_normal((total,), 43)
+    dy = synth.rand_normal((rows, total), 44)
+    edges = np.cumsum([0] + cols)
+    sl = [slice(edges[i], edges[i + 1]) for i in range(len(cols))]
+    xs = [dev(x[:, q]) for q in sl]
+    gs, bs = [dev(g[q]) for q in sl], [dev(b[q]) for q in sl]
+    ys = [empty((rows, c)) for c in cols]
+    stats = empty((rows, 2))
+    tt.tile_layernorm_fwd_multi(None, rows, cols, xs, gs, bs, stats, ys, 1e-5)
+    x64, g64 = x.astype(np.float64), g.astype(np.float64)
+    ry, (mu, rs) = og.layernorm_fwd(x64, g64, b.astype(np.float64))
+    got = np.concatenate([host(y) for y in ys], 1)
+    assert_rel(got, ry, 2e-5, 2e-5, "ln multi y")
+    assert_rel(host(stats)[:, 0], mu, 1e-5, 1e-6, "ln multi mean")
+    assert_rel(host(stats)[:, 1], rs, 1e-5, 0, "ln multi rstd")
+    # backward, twice (bitwise equal), dx accumulating onto an existing gradient when dx_acc
+    rdx, rdg, rdb = og.layernorm_bwd(dy.astype(np.float64), x64, g64, mu, rs)
+    dx0 = synth.rand_normal((rows, total), 45)
+    nws = tt.tile_layernorm_bwd_multi_workspace(rows, total)
+    outs = []
+    for _ in range(2):
+        dxs = [dev(dx0[:, q]) if dx_acc else empty((rows, c)) for q, c in zip(sl, cols)]
+        dgs = [dev(np.full(c, 0.25, np.float32)) for c in cols]
+        dbs = [dev(np.zeros(c, np.float32)) for c in cols]
+        ws = torch.empty(nws // 4 + 1, device="cuda")
+        tt.tile_layernorm_bwd_multi(None, rows, cols, [dev(dy[:, q]) for q in sl], xs, gs, stats, dxs, dx_acc, dgs,
+                                    dbs, ws, nws)
+        outs.append([np.concatenate([host(a) for a in lst], -1) for lst in (dxs, dgs, dbs)])
+    (dxg, dgg, dbg), again = outs
+    for a, b_ in zip(outs[0], again):
+        assert np.array_equal(a, b_)
+    assert_rel(dxg, rdx + (dx0 if dx_acc else 0), 1e-4, 1e-5, "ln multi dx")
+    assert_rel(dgg, rdg + 0.25, 1e-4, 1e-4, "ln multi dgamma")
+    assert_rel(dbg, rdb, 1e-4, 1e-4, "ln multi dbeta")
+
+
+def test_layernorm_multi_tile_rejects_bad_shapes():
+    a = empty((8, 64))
+    with pytest.raises(tt.TTError) as e:
+        tt.tile_layernorm_fwd_multi(None, 8, [64], [a], [a], [a], a, [a])       # one tile: the fused phase's job
+    assert e.value.code == tt._lib.TT_ERR_ARG
+    for cols in ([64, 66], [32, 64], [8192, 8192, 4]):                          # width, order, total
+        with pytest.raises(tt.TTError) as e:
+            tt.tile_layernorm_fwd_multi(None, 8, cols, [a] * len(cols), [a] * len(cols), [a] * len(cols), a,
+                                        [a] * len(cols))
+        assert e.value.code == tt._lib.TT_ERR_SHAPE, cols
+
+
 # ------------------------------------------------------- softmax / CE
 
 @pytest.mark.parametrize("rows,cols,vt", [(64, 256, 32), (300, 5000, 768), (7, 2049, 2048), (33, 100, 100)])

@@ -26,7 +26,7 @@ import pytest
 torch = pytest.importorskip("torch")
 
 import synth  # noqa: E402
-from gpu_util import normwise  # noqa: E402
+from tests.gpu_util import normwise  # noqa: E402
 from oracle import gpt2 as og  # noqa: E402
 from tile_task_transformer_amd import _lib as L  # noqa: E402
 from tile_task_transformer_amd.runtime import Context, GPT2  # noqa: E402

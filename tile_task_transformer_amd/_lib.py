@@ -43,6 +43,11 @@ TT_DEVICE_DRYRUN = -1
 TT_R, TT_W, TT_RW = 1, 2, 3
 TT_OPT_ADAMW, TT_OPT_SGD = 0, 1
 TT_ADAMW_MAX_TILES = TT_SGD_MAX_TILES = TT_FILL_MAX_TILES = 16
+(TT_OP_FILL, TT_OP_GEMM, TT_OP_GEMM_BATCH, TT_OP_GEMM_KSUM, TT_OP_LAYERNORM_FWD, TT_OP_LAYERNORM_BWD,
+ TT_OP_ATTENTION_FWD, TT_OP_ATTENTION_PREP, TT_OP_ATTENTION_BWD, TT_OP_XENTROPY_STATS, TT_OP_XENTROPY_MERGE,
+ TT_OP_XENTROPY_LOSS, TT_OP_XENTROPY_GRAD, TT_OP_ADAMW, TT_OP_ADAMW_ADVANCE, TT_OP_SGD, TT_OP_EMBEDDING_FWD,
+ TT_OP_EMBEDDING_INDEX, TT_OP_EMBEDDING_BWD, TT_OP_EMBEDDING_POS_BWD, TT_OP_REDUCE_ROWS, TT_OP_SPLIT_TOKENS,
+ TT_OP_COPY_IN) = range(1, 24)
 
 _ERRNAMES = {-1: "TT_ERR_ARG", -2: "TT_ERR_SHAPE", -3: "TT_ERR_OOM", -4: "TT_ERR_HIP", -5: "TT_ERR_STATE",
              -6: "TT_ERR_UNSUPPORTED"}
@@ -56,6 +61,49 @@ class TTError(RuntimeError):
 
 class tt_access(C.Structure):
     _fields_ = [("tensor", C.c_void_p), ("tile", C.c_int64 * TT_MAX_DIMS), ("mode", C.c_int)]
+
+
+class tt_tile(C.Structure):
+    _fields_ = [("tensor", C.c_void_p), ("tile", C.c_int64 * TT_MAX_DIMS)]
+
+
+class tt_op_fill(C.Structure):
+    _fields_ = [("value", C.c_float)]
+
+
+class tt_op_gemm(C.Structure):
+    _fields_ = [("transA", C.c_int), ("transB", C.c_int), ("epilogue", C.c_int), ("alpha", C.c_float),
+                ("beta", C.c_float), ("split_k", C.c_int)]
+
+
+class tt_op_layernorm(C.Structure):
+    _fields_ = [("eps", C.c_float), ("dx_acc", C.c_int)]
+
+
+class tt_op_attention(C.Structure):
+    _fields_ = [("q_off", C.c_int64), ("k_off", C.c_int64), ("first", C.c_int), ("last", C.c_int),
+                ("acc_dq", C.c_int), ("acc_dkv", C.c_int), ("scale", C.c_float)]
+
+
+class tt_op_xentropy(C.Structure):
+    _fields_ = [("accumulate", C.c_int), ("inv_n", C.c_float)]
+
+
+class tt_op_optim(C.Structure):
+    _fields_ = [("lr", C.c_float), ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float),
+                ("weight_decay", C.c_float)]
+
+
+class tt_op_embedding(C.Structure):
+    _fields_ = [("seq_len", C.c_int64)]
+
+
+class tt_op_reduce(C.Structure):
+    _fields_ = [("beta", C.c_int)]
+
+
+class tt_op_copy(C.Structure):
+    _fields_ = [("src", C.c_void_p)]
 
 
 class tt_stats(C.Structure):
@@ -104,6 +152,9 @@ SIGNATURES = {
     "tile_layernorm_fwd": (I, [P, I, I64, I64, P, I64, P, P, P, I64, I64, P, P, I64, F]),
     "tile_layernorm_bwd": (I, [P, I, I64, I64, I64, P, I64, P, I64, P, P, P, I64, I64, P, I64, I, P, P, P]),
     "tile_layernorm_bwd_workspace": (SZ, [I64, I64]),
+    "tile_layernorm_fwd_multi": (I, [P, I, I64, P, P, P, P, P, P, F]),
+    "tile_layernorm_bwd_multi": (I, [P, I, I64, P, P, P, P, P, P, I, P, P, P, SZ]),
+    "tile_layernorm_bwd_multi_workspace": (SZ, [I64, I64]),
     "tile_softmax": (I, [P, I, I64, I64, I64, I64, F, I, P, I64, P, P, I64, I64, P, P, P, I64, F]),
     "tile_xentropy": (I, [P, I, I64, I64, I64, P, P, I64, P, P, P, I, F]),
     "tile_attention_fwd": (I, [P, I64, I64, I64, I64, I64, I64, I64, P, P, P, P, P, P, I, I, F]),
@@ -132,6 +183,7 @@ SIGNATURES = {
     "tt_tensor_wrap": (I, [P, I, C.POINTER(I64), C.POINTER(I64), I, P, PP]),
     "tt_tensor_destroy": (I, [P]),
     "tt_tensor_bytes": (I64, [P]),
+    "tt_tensor_set_matrix_split": (I, [P, I]),
     "tt_tensor_grid": (I, [P, C.POINTER(I64), C.POINTER(I64)]),
     "tt_tensor_tile": (I, [P, C.POINTER(I64), PP, C.POINTER(I64)]),
     "tt_tensor_copy_in": (I, [P, P]),
@@ -139,6 +191,9 @@ SIGNATURES = {
     "tt_submit_nop": (I, [P, C.c_char_p, C.POINTER(tt_access), I]),
     "tt_submit_gemm": (I, [P, I, I, F, P, C.POINTER(I64), P, C.POINTER(I64), F, P, C.POINTER(I64)]),
     "tt_submit_fill": (I, [P, P, C.POINTER(I64), F]),
+    "tt_submit": (I, [P, I, C.POINTER(tt_tile), I, P, SZ]),
+    "tt_ctx_wait_stream": (I, [P, P]),
+    "tt_ctx_join_stream": (I, [P, P]),
     "tt_wait": (I, [P]),
     "tt_dump_dag": (I, [P, C.c_char_p]),
     "tt_get_stats": (I, [P, C.POINTER(tt_stats)]),

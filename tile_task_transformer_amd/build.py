@@ -23,7 +23,7 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtiletask.so")
 ARCH = os.environ.get("TT_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["runtime.cpp", "gpt2.cpp", "gemm.hip", "layernorm.hip", "softmax.hip", "attention.hip", "misc.hip",
+SOURCES = ["runtime.cpp", "tasks.cpp", "gpt2.cpp", "gemm.hip", "layernorm.hip", "softmax.hip", "attention.hip", "misc.hip",
            "probe.hip"]
 
 

@@ -24,7 +24,7 @@
 #include <cstring>
 #include <memory>
 
-#include "runtime.hpp"
+#include "tasks.hpp"
 
 using namespace tt;
 
@@ -49,7 +49,7 @@ struct tt_gpt2 {
   tt_tensor *tokens = nullptr, *ids = nullptr, *labels = nullptr, *sorted = nullptr, *perm = nullptr;
   std::vector<BlockT> blk;
   tt_tensor *h_last = nullptr, *lnf = nullptr, *nf = nullptr, *z = nullptr;
-  tt_tensor *ml = nullptr, *ln_parts = nullptr, *lnb_parts = nullptr, *ce_parts = nullptr;
+  tt_tensor *ml = nullptr, *ce_parts = nullptr;
   tt_tensor *ce_lse = nullptr, *row_loss = nullptr, *loss = nullptr;
   tt_tensor *dnf = nullptr, *dh = nullptr, *dgu = nullptr, *dn = nullptr, *dO = nullptr, *dq = nullptr,
             *dk = nullptr, *dv = nullptr, *Dv = nullptr;
@@ -101,33 +101,16 @@ struct Gemm {
   TileRef bias, res, aux;
 };
 
+TileArg ta(const TileRef& r) { return TileArg{r.t, r.lin}; }
+
 int submit_gemm(tt_ctx* ctx, const char* label, const Gemm& q) {
-  int64_t ar, ac, br, bc, cr, cc;
-  q.A.t->mat(q.A.lin, &ar, &ac);
-  q.B.t->mat(q.B.lin, &br, &bc);
-  q.C.t->mat(q.C.lin, &cr, &cc);
-  const int64_t m = q.ta ? ac : ar, k = q.ta ? ar : ac;
-  const int64_t kb = q.tb ? bc : br, n = q.tb ? br : bc;
-  if (k != kb || m != cr || n != cc)
-    return fail(TT_ERR_SHAPE, "%s: op(A) %lldx%lld op(B) %lldx%lld C %lldx%lld", label, (long long)m, (long long)k,
-                (long long)kb, (long long)n, (long long)cr, (long long)cc);
-  std::vector<Access> acc = {R(q.A.t, q.A.lin), R(q.B.t, q.B.lin)};
-  const bool gelu = q.epi & TT_EPI_GELU;
-  // C is only written when beta == 0 or when the GELU epilogue accumulates in aux
-  acc.push_back((q.beta == 0.f || gelu) ? W(q.C.t, q.C.lin) : RW(q.C.t, q.C.lin));
-  if (q.bias.valid()) acc.push_back(R(q.bias.t, q.bias.lin));
-  if (q.res.valid()) acc.push_back(R(q.res.t, q.res.lin));
-  if (q.aux.valid()) acc.push_back(gelu ? RW(q.aux.t, q.aux.lin) : R(q.aux.t, q.aux.lin));
-  Gemm p = q;
-  return ctx->submit(label, std::move(acc), [p, m, n, k, ac, bc, cc, ctx](hipStream_t s, void* ws) {
-    int64_t ldr = 0, ldaux = 0, rr;
-    if (p.res.valid()) p.res.t->mat(p.res.lin, &rr, &ldr);
-    if (p.aux.valid()) p.aux.t->mat(p.aux.lin, &rr, &ldaux);
-    return tile_gemm_ws(s, p.ta, p.tb, m, n, k, p.alpha, F(p.A.t, p.A.lin), ac, F(p.B.t, p.B.lin), bc, p.beta,
-                        F(p.C.t, p.C.lin), cc, p.epi, p.bias.valid() ? F(p.bias.t, p.bias.lin) : nullptr,
-                        p.res.valid() ? F(p.res.t, p.res.lin) : nullptr, ldr,
-                        p.aux.valid() ? F(p.aux.t, p.aux.lin) : nullptr, ldaux, ws, ws ? ctx->workspace_bytes : 0);
-  }, 2.0 * m * n * k);
+  TileArg T[6] = {ta(q.A), ta(q.B), ta(q.C)};
+  int n = 3;
+  if (q.epi & TT_EPI_BIAS) T[n++] = ta(q.bias);
+  if (q.epi & TT_EPI_RES) T[n++] = ta(q.res);
+  if (q.epi & (TT_EPI_GELU | TT_EPI_GELU_BWD)) T[n++] = ta(q.aux);
+  const tt_op_gemm sc{q.ta, q.tb, q.epi, q.alpha, q.beta, 1};
+  return submit_op(ctx, TT_OP_GEMM, T, n, &sc, sizeof(sc), label, false);
 }
 
 // Independent products (the tied head's per-vocab-tile GEMMs) as
@@ -173,41 +156,14 @@ int submit_gemm_batch(tt_ctx* ctx, const char* label, const std::vector<Gemm>& q
       bytes += b1;
       ++j;
     }
-    std::vector<Gemm> grp(qs.begin() + i, qs.begin() + j);
-    std::vector<Access> acc;
-    double flops = 0.0;
-    for (size_t u = 0; u < grp.size(); ++u) {
-      const Gemm& q = grp[u];
-      int64_t cr, cc;
-      q.C.t->mat(q.C.lin, &cr, &cc);
-      if (sh[u].m != cr || sh[u].n != cc)
-        return fail(TT_ERR_SHAPE, "%s: op(A) %lldx%lld does not match C %lldx%lld", label, (long long)sh[u].m,
-                    (long long)sh[u].k, (long long)cr, (long long)cc);
-      acc.push_back(R(q.A.t, q.A.lin));
-      acc.push_back(R(q.B.t, q.B.lin));
-      acc.push_back(q0.beta == 0.f ? W(q.C.t, q.C.lin) : RW(q.C.t, q.C.lin));
-      flops += 2.0 * sh[u].m * sh[u].n * sh[u].k;
+    std::vector<TileArg> T;
+    for (size_t u = i; u < j; ++u) {
+      T.push_back(ta(qs[u].A));
+      T.push_back(ta(qs[u].B));
+      T.push_back(ta(qs[u].C));
     }
-    int rc = ctx->submit(label, std::move(acc), [grp, sh, split, ctx](hipStream_t s, void* ws) {
-      const size_t c = grp.size();
-      std::vector<const float*> A(c), B(c);
-      std::vector<float*> C(c);
-      std::vector<int64_t> m(c), n(c), lda(c), ldb(c), ldc(c);
-      for (size_t u = 0; u < c; ++u) {
-        A[u] = F(grp[u].A.t, grp[u].A.lin);
-        B[u] = F(grp[u].B.t, grp[u].B.lin);
-        C[u] = F(grp[u].C.t, grp[u].C.lin);
-        m[u] = sh[u].m;
-        n[u] = sh[u].n;
-        lda[u] = sh[u].lda;
-        ldb[u] = sh[u].ldb;
-        ldc[u] = sh[u].ldc;
-      }
-      const bool w = split && ws;
-      return tile_gemm_batch_ws(s, (int)c, grp[0].ta, grp[0].tb, m.data(), n.data(), sh[0].k, grp[0].alpha, A.data(),
-                                lda.data(), B.data(), ldb.data(), grp[0].beta, C.data(), ldc.data(),
-                                w ? ws : nullptr, w ? ctx->workspace_bytes : 0);
-    }, flops);
+    const tt_op_gemm sc{q0.ta, q0.tb, TT_EPI_NONE, q0.alpha, q0.beta, split ? 1 : 0};
+    int rc = submit_op(ctx, TT_OP_GEMM_BATCH, T.data(), (int)T.size(), &sc, sizeof(sc), label, false);
     if (rc) return rc;
     i = j;
   }
@@ -229,39 +185,13 @@ int submit_ksum_tb(tt_ctx* ctx, const char* label, TileRef C, const std::vector<
     q.C = C;
     return submit_gemm(ctx, label, q);
   }
-  int64_t dr, dc;
-  C.t->mat(C.lin, &dr, &dc);
-  std::vector<Access> acc;
-  double flops = 0;
+  std::vector<TileArg> T = {ta(C)};
   for (size_t u = 0; u < As.size(); ++u) {
-    int64_t ar, ac, br, bc;
-    As[u].t->mat(As[u].lin, &ar, &ac);
-    Bs[u].t->mat(Bs[u].lin, &br, &bc);
-    if (ar != dr || br != dc || bc != ac)
-      return fail(TT_ERR_SHAPE, "%s: pair %zu (%lldx%lld, %lldx%lld) does not match C %lldx%lld", label, u,
-                  (long long)ar, (long long)ac, (long long)br, (long long)bc, (long long)dr, (long long)dc);
-    acc.push_back(R(As[u].t, As[u].lin));
-    acc.push_back(R(Bs[u].t, Bs[u].lin));
-    flops += 2.0 * dr * dc * ac;
+    T.push_back(ta(As[u]));
+    T.push_back(ta(Bs[u]));
   }
-  acc.push_back(W(C.t, C.lin));
-  return ctx->submit(label, std::move(acc), [=](hipStream_t s, void*) {
-    const size_t np = As.size();
-    std::vector<const float*> a(np), bb(np);
-    std::vector<int64_t> ks(np), lda(np), ldb(np);
-    for (size_t u = 0; u < np; ++u) {
-      int64_t ar, ac, br, bc;
-      As[u].t->mat(As[u].lin, &ar, &ac);
-      Bs[u].t->mat(Bs[u].lin, &br, &bc);
-      a[u] = F(As[u].t, As[u].lin);
-      bb[u] = F(Bs[u].t, Bs[u].lin);
-      ks[u] = ac;
-      lda[u] = ac;
-      ldb[u] = bc;
-    }
-    return tile_gemm_ksum(s, (int)np, 1, dr, dc, ks.data(), 1.f, a.data(), lda.data(), bb.data(), ldb.data(), 0.f,
-                          F(C.t, C.lin), dc);
-  }, flops);
+  const tt_op_gemm sc{0, 1, TT_EPI_NONE, 1.f, 0.f, 0};
+  return submit_op(ctx, TT_OP_GEMM_KSUM, T.data(), (int)T.size(), &sc, sizeof(sc), label, false);
 }
 
 // tiles = value, TT_FILL_MAX_TILES tiles per task and launch (with
@@ -280,17 +210,10 @@ int fill_tasks(tt_gpt2* g, const std::vector<TileRef>& tiles, float v) {
       elems += tiles[k].t->tile_elems(tiles[k].lin);
       grp.push_back(tiles[k++]);
     }
-    std::vector<Access> acc;
-    for (const TileRef& r : grp) acc.push_back(W(r.t, r.lin));
-    int rc = ctx->submit("fill", acc, [grp, v](hipStream_t s, void*) {
-      float* dst[TT_FILL_MAX_TILES];
-      int64_t n[TT_FILL_MAX_TILES];
-      for (size_t j = 0; j < grp.size(); ++j) {
-        dst[j] = F(grp[j].t, grp[j].lin);
-        n[j] = grp[j].t->tile_elems(grp[j].lin);
-      }
-      return tile_fill_multi(s, (int)grp.size(), dst, n, v);
-    });
+    std::vector<TileArg> T;
+    for (const TileRef& r : grp) T.push_back(ta(r));
+    const tt_op_fill sc{v};
+    int rc = submit_op(ctx, TT_OP_FILL, T.data(), (int)T.size(), &sc, sizeof(sc), "fill", false);
     if (rc) return rc;
   }
   return TT_OK;
@@ -305,108 +228,44 @@ int fill_tasks(tt_gpt2* g, const std::vector<TileRef>& tiles, float v) {
 
 // ------------------------------------------------------------ LayerNorm
 
-// y = LN(x) over the embd tiles of token tile ti
-int ln_forward(tt_gpt2* g, tt_tensor* x, tt_tensor* gam, tt_tensor* bet, tt_tensor* stats, tt_tensor* y, int64_t ti,
-               int64_t bi, int64_t si) {
-  tt_ctx* ctx = g->ctx;
-  const float eps = g->c.ln_eps;
-  const int64_t rows = g->rows;
-  const int64_t st = L(stats, {bi, si, 0});
-  if (g->NE == 1) {
-    const int64_t lx = L(x, {bi, si, 0}), ly = L(y, {bi, si, 0});
-    const int64_t cols = g->c.n_embd;
-    return ctx->submit("ln_fwd", {R(x, lx), R(gam, 0), R(bet, 0), W(stats, st), W(y, ly)},
-                       [=](hipStream_t s, void*) {
-                         return tile_layernorm_fwd(s, TT_LN_FUSED, rows, cols, F(x, lx), cols, F(gam, 0), F(bet, 0),
-                                                   nullptr, 0, 0, F(stats, st), F(y, ly), cols, eps);
-                       });
-  }
-  tt_tensor* parts = g->ln_parts;
-  std::vector<Access> merge_acc;
-  for (int64_t e = 0; e < g->NE; ++e) {
-    const int64_t lx = L(x, {bi, si, e}), lp = L(parts, {e, ti, 0});
-    int64_t r, cols;
-    x->mat(lx, &r, &cols);
-    TRY(ctx->submit("ln_part", {R(x, lx), W(parts, lp)}, [=](hipStream_t s, void*) {
-      return tile_layernorm_fwd(s, TT_LN_PARTIAL, rows, cols, F(x, lx), cols, nullptr, nullptr, F(parts, lp), 0, 0,
-                                nullptr, nullptr, 0, eps);
-    }));
-    merge_acc.push_back(R(parts, lp));
-  }
-  merge_acc.push_back(W(stats, st));
-  const int64_t lp0 = L(parts, {0, ti, 0});
-  const int64_t stride = rows * 3, ne = g->NE;
-  TRY(ctx->submit("ln_merge", merge_acc, [=](hipStream_t s, void*) {
-    return tile_layernorm_fwd(s, TT_LN_MERGE, rows, 0, nullptr, 0, nullptr, nullptr, F(parts, lp0), ne, stride,
-                              F(stats, st), nullptr, 0, eps);
-  }));
-  for (int64_t e = 0; e < g->NE; ++e) {
-    const int64_t lx = L(x, {bi, si, e}), ly = L(y, {bi, si, e});
-    int64_t r, cols;
-    x->mat(lx, &r, &cols);
-    TRY(ctx->submit("ln_apply", {R(x, lx), R(gam, e), R(bet, e), R(stats, st), W(y, ly)}, [=](hipStream_t s, void*) {
-      return tile_layernorm_fwd(s, TT_LN_APPLY, rows, cols, F(x, lx), cols, F(gam, e), F(bet, e), nullptr, 0, 0,
-                                F(stats, st), F(y, ly), cols, eps);
-    }));
-  }
-  return TT_OK;
+// y = LN(x) over the embd tiles of token tile (bi, si): one task over the
+// row block's feature tiles
+int ln_forward(tt_gpt2* g, tt_tensor* x, tt_tensor* gam, tt_tensor* bet, tt_tensor* stats, tt_tensor* y, int64_t bi,
+               int64_t si) {
+  std::vector<TileArg> T;
+  for (int64_t e = 0; e < g->NE; ++e) T.push_back({x, L(x, {bi, si, e})});
+  for (int64_t e = 0; e < g->NE; ++e) T.push_back({gam, e});
+  for (int64_t e = 0; e < g->NE; ++e) T.push_back({bet, e});
+  T.push_back({stats, L(stats, {bi, si, 0})});
+  for (int64_t e = 0; e < g->NE; ++e) T.push_back({y, L(y, {bi, si, e})});
+  const tt_op_layernorm sc{g->c.ln_eps, 0};
+  return submit_op(g->ctx, TT_OP_LAYERNORM_FWD, T.data(), (int)T.size(), &sc, sizeof(sc), "ln_fwd", false);
 }
 
-// dx (+)= LN_bwd(dy) for token tile ti; dgamma/dbeta accumulate
+// dx (+)= LN_bwd(dy) for token tile (bi, si); dgamma/dbeta accumulate
 int ln_backward(tt_gpt2* g, tt_tensor* dy, tt_tensor* x, tt_tensor* gam, tt_tensor* stats, tt_tensor* dx,
-                int dx_acc, tt_tensor* dgam, tt_tensor* dbet, int64_t ti, int64_t bi, int64_t si) {
-  tt_ctx* ctx = g->ctx;
-  const int64_t rows = g->rows, n_total = g->c.n_embd;
-  const int64_t st = L(stats, {bi, si, 0});
-  if (g->NE == 1) {
-    const int64_t ly = L(dy, {bi, si, 0}), lx = L(x, {bi, si, 0}), ld = L(dx, {bi, si, 0});
-    const int64_t cols = n_total;
-    return ctx->submit("ln_bwd",
-                       {R(dy, ly), R(x, lx), R(gam, 0), R(stats, st), dx_acc ? RW(dx, ld) : W(dx, ld), RW(dgam, 0),
-                        RW(dbet, 0)},
-                       [=](hipStream_t s, void* ws) {
-                         return tile_layernorm_bwd(s, TT_LN_FUSED, rows, cols, n_total, F(dy, ly), cols, F(x, lx),
-                                                   cols, F(gam, 0), F(stats, st), nullptr, 0, 0, F(dx, ld), cols,
-                                                   dx_acc, F(dgam, 0), F(dbet, 0), ws);
-                       });
-  }
-  tt_tensor* parts = g->lnb_parts;
-  std::vector<Access> part_reads;
-  for (int64_t e = 0; e < g->NE; ++e) {
-    const int64_t ly = L(dy, {bi, si, e}), lx = L(x, {bi, si, e}), lp = L(parts, {e, ti, 0});
-    int64_t r, cols;
-    x->mat(lx, &r, &cols);
-    TRY(ctx->submit("lnb_part", {R(dy, ly), R(x, lx), R(gam, e), R(stats, st), W(parts, lp)},
-                    [=](hipStream_t s, void*) {
-                      return tile_layernorm_bwd(s, TT_LN_PARTIAL, rows, cols, n_total, F(dy, ly), cols, F(x, lx),
-                                                cols, F(gam, e), F(stats, st), F(parts, lp), 0, 0, nullptr, 0, 0,
-                                                nullptr, nullptr, nullptr);
-                    }));
-    part_reads.push_back(R(parts, lp));
-  }
-  const int64_t lp0 = L(parts, {0, ti, 0}), stride = rows * 2, ne = g->NE;
-  for (int64_t e = 0; e < g->NE; ++e) {
-    const int64_t ly = L(dy, {bi, si, e}), lx = L(x, {bi, si, e}), ld = L(dx, {bi, si, e});
-    int64_t r, cols;
-    x->mat(lx, &r, &cols);
-    std::vector<Access> acc = part_reads;
-    acc.insert(acc.end(), {R(dy, ly), R(x, lx), R(gam, e), R(stats, st), dx_acc ? RW(dx, ld) : W(dx, ld),
-                           RW(dgam, e), RW(dbet, e)});
-    TRY(ctx->submit("lnb_apply", acc, [=](hipStream_t s, void* ws) {
-      return tile_layernorm_bwd(s, TT_LN_APPLY, rows, cols, n_total, F(dy, ly), cols, F(x, lx), cols, F(gam, e),
-                                F(stats, st), F(parts, lp0), ne, stride, F(dx, ld), cols, dx_acc, F(dgam, e),
-                                F(dbet, e), ws);
-    }));
-  }
-  return TT_OK;
+                int dx_acc, tt_tensor* dgam, tt_tensor* dbet, int64_t bi, int64_t si) {
+  std::vector<TileArg> T;
+  for (int64_t e = 0; e < g->NE; ++e) T.push_back({dy, L(dy, {bi, si, e})});
+  for (int64_t e = 0; e < g->NE; ++e) T.push_back({x, L(x, {bi, si, e})});
+  for (int64_t e = 0; e < g->NE; ++e) T.push_back({gam, e});
+  T.push_back({stats, L(stats, {bi, si, 0})});
+  for (int64_t e = 0; e < g->NE; ++e) T.push_back({dx, L(dx, {bi, si, e})});
+  for (int64_t e = 0; e < g->NE; ++e) T.push_back({dgam, e});
+  for (int64_t e = 0; e < g->NE; ++e) T.push_back({dbet, e});
+  const tt_op_layernorm sc{g->c.ln_eps, dx_acc};
+  return submit_op(g->ctx, TT_OP_LAYERNORM_BWD, T.data(), (int)T.size(), &sc, sizeof(sc), "ln_bwd", false);
 }
 
-int colsum_task(tt_ctx* ctx, tt_tensor* x, int64_t lx, tt_tensor* out, int64_t lo, int beta) {
-  int64_t r, c;
-  x->mat(lx, &r, &c);
-  return ctx->submit("colsum", {R(x, lx), beta ? RW(out, lo) : W(out, lo)}, [=](hipStream_t s, void* ws) {
-    return tile_reduce_rows(s, r, c, F(x, lx), c, F(out, lo), beta, ws);
-  });
+// column sums (bias gradients) of the (X, out) tile pairs: one task
+int colsum_task(tt_ctx* ctx, const std::vector<TileRef>& xs, const std::vector<TileRef>& outs, int beta) {
+  std::vector<TileArg> T;
+  for (size_t u = 0; u < xs.size(); ++u) {
+    T.push_back(ta(xs[u]));
+    T.push_back(ta(outs[u]));
+  }
+  const tt_op_reduce sc{beta};
+  return submit_op(ctx, TT_OP_REDUCE_ROWS, T.data(), (int)T.size(), &sc, sizeof(sc), "colsum", false);
 }
 
 }  // namespace
@@ -561,8 +420,6 @@ extern "C" int tt_gpt2_create(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_g
   MK(&G->nf, "nf", {B, T, d}, {bt, sq, et}, 2);
   MK(&G->z, "logits", {B, T, V}, {bt, sq, vt}, 2);
   MK(&G->ml, "attn_ml", {B / bt, T / sq, H / ht, bt * sq * ht * 2}, {1, 1, 1, bt * sq * ht * 2}, 3);
-  MK(&G->ln_parts, "ln_parts", {G->NE, G->ntok, G->rows * 3}, {1, 1, G->rows * 3}, 2);
-  MK(&G->lnb_parts, "lnb_parts", {G->NE, G->ntok, G->rows * 2}, {1, 1, G->rows * 2}, 2);
   MK(&G->ce_parts, "ce_parts", {G->NV, G->ntok, G->rows * 3}, {1, 1, G->rows * 3}, 2);
   MK(&G->ce_lse, "ce_lse", {G->ntok, G->rows}, {1, G->rows}, 1);
   MK(&G->row_loss, "row_loss", {G->ntok, G->rows}, {1, G->rows}, 1);
@@ -579,9 +436,12 @@ extern "C" int tt_gpt2_create(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_g
   MK(&G->step, "adam_step", {1}, {1}, 0, TT_I32);
   MK(&G->bc, "adam_bias_corr", {2}, {2}, 0);
 #undef MK
-  // per-stream workspace for the deterministic column sums
+  // per-stream workspace: LayerNorm partial statistics and column sums, the
+  // deterministic column sums of the bias gradients (up to 16 tiles per
+  // task), split-K partial sums
   const int64_t widest = std::max<int64_t>({et, std::min<int64_t>(it, I), ht * hd});
-  size_t ws = std::max(tile_layernorm_bwd_workspace(G->rows, et), tile_reduce_rows_workspace(G->rows, widest));
+  size_t ws = std::max(layernorm_fwd_workspace(G->NE, G->rows), layernorm_bwd_workspace(G->NE, G->rows, et));
+  ws = std::max(ws, std::min<int64_t>(16, std::max(G->NE, G->NI)) * tile_reduce_rows_workspace(G->rows, widest));
   // the q/k/v bias gradients: up to 15 head tiles per multi-tile column sum
   ws = std::max(ws, tile_reduce_rows_workspace(G->rows, std::min<int64_t>(15, 3 * G->NH) * ht * hd));
   {
@@ -758,61 +618,37 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
 
   // ---- inputs: copy the token windows, split into ids/labels, index for the embedding backward
   {
-    tt_tensor* tok = g->tokens;
-    const size_t bytes = (size_t)B * (T + 1) * 4;
-    TRY(ctx->submit("tokens", {W(tok, 0)}, [tok, tokens, bytes](hipStream_t s, void*) {
-      TT_HIP_TRY(hipMemcpyAsync(tok->dev(0), tokens, bytes, hipMemcpyDeviceToDevice, s));
-      return TT_OK;
-    }));
+    const TileArg T[1] = {{g->tokens, 0}};
+    const tt_op_copy sc{tokens};
+    TRY(submit_op(ctx, TT_OP_COPY_IN, T, 1, &sc, sizeof(sc), "tokens", false));
   }
   for (int64_t bi = 0; bi < g->nb; ++bi)
     for (int64_t si = 0; si < g->ns; ++si) {
-      tt_tensor *tok = g->tokens, *ids = g->ids, *lab = g->labels, *so = g->sorted, *pe = g->perm;
-      const int64_t li = L(ids, {bi, si});
-      // split: rows of this tile start at window bi*bt, position si*sq; one launch per batch row
-      TRY(ctx->submit("split", {R(tok, 0), W(ids, li), W(lab, li)}, [=](hipStream_t s, void*) {
-        for (int64_t b = 0; b < bt; ++b) {
-          const int32_t* src = (const int32_t*)tok->dev(0) + (bi * bt + b) * (T + 1) + si * sq;
-          int rc = tile_split_tokens(s, 1, sq, src, (int32_t*)ids->dev(li) + b * sq, (int32_t*)lab->dev(li) + b * sq);
-          if (rc) return rc;
-        }
-        return TT_OK;
-      }));
-      TRY(ctx->submit("emb_index", {R(ids, li), W(so, li), W(pe, li)}, [=](hipStream_t s, void*) {
-        return tile_embedding_index(s, rows, I32(ids, li), (int32_t*)so->dev(li), (int32_t*)pe->dev(li));
-      }));
+      const int64_t li = L(g->ids, {bi, si});
+      const TileArg sp[3] = {{g->tokens, 0}, {g->ids, li}, {g->labels, li}};
+      TRY(submit_op(ctx, TT_OP_SPLIT_TOKENS, sp, 3, nullptr, 0, "split", false));
+      const TileArg ix[3] = {{g->ids, li}, {g->sorted, li}, {g->perm, li}};
+      TRY(submit_op(ctx, TT_OP_EMBEDDING_INDEX, ix, 3, nullptr, 0, "emb_index", false));
     }
 
   // The inputs' tasks go to the GPU now, so it starts on this step while the
   // host infers the dependencies of the rest (with a large window it would
-  // otherwise wait for the whole step's submission). Not with pinned homes:
-  // there the residency plan wants the whole step in one window.
-  if (g->param_home != TT_HOME_PINNED_HOST) TRY(ctx->flush());
+  // otherwise wait for the whole step's submission), and the copy of the
+  // caller's token buffer is queued before this call returns. The inputs
+  // touch no pinned-host tile, so the residency plan of the rest still
+  // covers the whole step.
+  TRY(ctx->flush());
 
   // ---- embedding forward
   tt_tensor* h0 = c.n_layer ? g->blk[0].h_in : g->h_last;
   for (int64_t bi = 0; bi < g->nb; ++bi)
     for (int64_t si = 0; si < g->ns; ++si)
       for (int64_t e = 0; e < NE; ++e) {
-        tt_tensor *wte = g->P[0], *wpe = g->P[1], *ids = g->ids;
-        const int64_t li = L(ids, {bi, si}), lo = L(h0, {bi, si, e}), lp = L(wpe, {si, e});
-        int64_t r, cols;
-        h0->mat(lo, &r, &cols);
-        std::vector<Access> acc = {R(ids, li), R(wpe, lp), W(h0, lo)};
-        for (int64_t v = 0; v < NV; ++v) acc.push_back(R(wte, L(wte, {v, e})));
-        const int64_t lw = L(wte, {0, e}), vt = std::min<int64_t>(g->t.vocab, V), nv = NV;
-        TRY(ctx->submit("emb_fwd", acc, [=](hipStream_t s, void*) {
-          if (wte->home == TT_HOME_DEVICE)  // the vocab tiles of one embd column form one contiguous slab
-            return tile_embedding_fwd(s, rows, cols, I32(ids, li), V, 0, V, F(wte, lw), cols, F(wpe, lp), cols, sq, 0,
-                                      F(h0, lo), cols);
-          for (int64_t v = 0; v < nv; ++v) {  // staged tiles are separate: one gather per vocab tile
-            const int64_t lv = L(wte, {v, e}), v_off = v * vt;
-            int rc = tile_embedding_fwd(s, rows, cols, I32(ids, li), V, v_off, std::min(vt, V - v_off), F(wte, lv),
-                                        cols, F(wpe, lp), cols, sq, 0, F(h0, lo), cols);
-            if (rc) return rc;
-          }
-          return TT_OK;
-        }));
+        tt_tensor *wte = g->P[0], *wpe = g->P[1];
+        std::vector<TileArg> T = {{g->ids, L(g->ids, {bi, si})}, {wpe, L(wpe, {si, e})}, {h0, L(h0, {bi, si, e})}};
+        for (int64_t v = 0; v < NV; ++v) T.push_back({wte, L(wte, {v, e})});
+        const tt_op_embedding sc{sq};
+        TRY(submit_op(ctx, TT_OP_EMBEDDING_FWD, T.data(), (int)T.size(), &sc, sizeof(sc), "emb_fwd", false));
       }
 
   // ---- blocks forward
@@ -829,7 +665,7 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
     for (int64_t bi = 0; bi < g->nb; ++bi)
       for (int64_t si = 0; si < g->ns; ++si) {
         const int64_t ti = bi + g->nb * si;
-        TRY(ln_forward(g, b.h_in, ln1g, ln1b, b.ln1, b.n1, ti, bi, si));
+        TRY(ln_forward(g, b.h_in, ln1g, ln1b, b.ln1, b.n1, bi, si));
         for (int cq = 0; cq < 3; ++cq)
           for (int64_t hj = 0; hj < NH; ++hj)
             for (int64_t ek = 0; ek < NE; ++ek) {
@@ -850,19 +686,11 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
       for (int64_t hj = 0; hj < NH; ++hj)
         for (int64_t qi = 0; qi < g->ns; ++qi)
           for (int64_t ki = 0; ki <= qi; ++ki) {
-            tt_tensor *Q = b.q, *K = b.k, *Vt = b.v, *O = b.o, *ml = g->ml, *lse = b.lse;
-            const int64_t lq = L(Q, {bi, qi, hj, 0}), lk = L(K, {bi, ki, hj, 0});
-            const int64_t ls = L(lse, {bi, qi, hj, 0}), lm = L(ml, {bi, qi, hj, 0});
-            const int first = ki == 0, last = ki == qi;
-            std::vector<Access> acc = {R(Q, lq), R(K, lk), R(Vt, lk), first ? W(O, lq) : RW(O, lq)};
-            if (!(first && last)) acc.push_back(first ? W(ml, lm) : RW(ml, lm));
-            if (last) acc.push_back(W(lse, ls));
-            // QK^T and PV over the visible (query, key) pairs of the tile pair
-            const double pairs = last ? sq * (sq + 1) / 2.0 : (double)sq * sq;
-            TRY(ctx->submit("attn_fwd", acc, [=](hipStream_t s, void*) {
-              return tile_attention_fwd(s, bt, ht, sq, sq, hd, qi * sq, ki * sq, F(Q, lq), F(K, lk), F(Vt, lk),
-                                        F(O, lq), F(ml, lm), F(lse, ls), first, last, scale);
-            }, 4.0 * bt * ht * hd * pairs));
+            const int64_t lq = L(b.q, {bi, qi, hj, 0}), lk = L(b.k, {bi, ki, hj, 0});
+            const TileArg T[6] = {{b.q, lq}, {b.k, lk}, {b.v, lk}, {b.o, lq}, {g->ml, L(g->ml, {bi, qi, hj, 0})},
+                                  {b.lse, L(b.lse, {bi, qi, hj, 0})}};
+            const tt_op_attention sc{qi * sq, ki * sq, ki == 0, ki == qi, 0, 0, scale};
+            TRY(submit_op(ctx, TT_OP_ATTENTION_FWD, T, 6, &sc, sizeof(sc), "attn_fwd", false));
           }
     for (int64_t bi = 0; bi < g->nb; ++bi)
       for (int64_t si = 0; si < g->ns; ++si) {
@@ -885,7 +713,7 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
             }
             TRY(submit_gemm(ctx, "attn_proj", q));
           }
-        TRY(ln_forward(g, b.h_mid, ln2g, ln2b, b.ln2, b.n2, ti, bi, si));
+        TRY(ln_forward(g, b.h_mid, ln2g, ln2b, b.ln2, b.n2, bi, si));
         // g = gelu(n2 W_fc + b_fc), pre-activation kept in u
         for (int64_t ij = 0; ij < NI; ++ij)
           for (int64_t ek = 0; ek < NE; ++ek) {
@@ -929,7 +757,7 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
   for (int64_t bi = 0; bi < g->nb; ++bi)
     for (int64_t si = 0; si < g->ns; ++si) {
       const int64_t ti = bi + g->nb * si;
-      TRY(ln_forward(g, g->h_last, lnfg, lnfb, g->lnf, g->nf, ti, bi, si));
+      TRY(ln_forward(g, g->h_last, lnfg, lnfb, g->lnf, g->nf, bi, si));
       // z_v = nf wte_v^T for every vocab tile v: per embd tile, one batch
       // of equal-shape products (tile_gemm_batch), accumulating over embd tiles
       for (int64_t ek = 0; ek < NE; ++ek) {
@@ -947,71 +775,31 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
       }
       // per-vocab-tile (max, sum exp, target logit) partials: one task and
       // launch over all vocab tiles of the token tile (tile_xentropy_multi)
+      tt_tensor *z = g->z, *parts = g->ce_parts;
+      const int64_t ll = L(g->labels, {bi, si});
       {
-        tt_tensor *z = g->z, *lab = g->labels, *parts = g->ce_parts;
-        const int64_t ll = L(lab, {bi, si});
-        std::vector<Access> acc = {R(lab, ll)};
-        for (int64_t vj = 0; vj < NV; ++vj) {
-          acc.push_back(R(z, L(z, {bi, si, vj})));
-          acc.push_back(W(parts, L(parts, {vj, ti, 0})));
-        }
-        TRY(ctx->submit("ce_stats", std::move(acc), [=](hipStream_t s, void*) {
-          std::vector<float*> zs(NV);
-          std::vector<int64_t> lens(NV), offs(NV);
-          float* p0 = F(parts, L(parts, {0, ti, 0}));
-          for (int64_t vj = 0; vj < NV; ++vj) {
-            const int64_t lz = L(z, {bi, si, vj});
-            int64_t r, cols;
-            z->mat(lz, &r, &cols);
-            zs[vj] = F(z, lz);
-            lens[vj] = cols;
-            offs[vj] = vj * std::min<int64_t>(g->t.vocab, V);
-            if (F(parts, L(parts, {vj, ti, 0})) != p0 + vj * rows * 3)
-              return fail(TT_ERR_STATE, "ce_stats: partials of one token tile are not evenly spaced");
-          }
-          return tile_xentropy_multi(s, TT_XE_STATS, (int)NV, rows, lens.data(), offs.data(), I32(lab, ll),
-                                     zs.data(), lens.data(), p0, rows * 3, nullptr, 1.f);
-        }));
+        std::vector<TileArg> T = {{g->labels, ll}};
+        for (int64_t vj = 0; vj < NV; ++vj) T.push_back({z, L(z, {bi, si, vj})});
+        for (int64_t vj = 0; vj < NV; ++vj) T.push_back({parts, L(parts, {vj, ti, 0})});
+        TRY(submit_op(ctx, TT_OP_XENTROPY_STATS, T.data(), (int)T.size(), nullptr, 0, "ce_stats", false));
       }
       {
-        tt_tensor *parts = g->ce_parts, *lse = g->ce_lse, *rl = g->row_loss;
-        std::vector<Access> acc;
-        for (int64_t vj = 0; vj < NV; ++vj) acc.push_back(R(parts, L(parts, {vj, ti, 0})));
-        acc.push_back(W(lse, ti));
-        acc.push_back(W(rl, ti));
-        const int64_t lp0 = L(parts, {0, ti, 0});
-        TRY(ctx->submit("ce_merge", acc, [=](hipStream_t s, void*) {
-          return tile_softmax(s, TT_SM_MERGE, rows, 0, 0, 0, 1.f, 0, nullptr, 0, nullptr, F(parts, lp0), NV, rows * 3,
-                              F(lse, ti), F(rl, ti), nullptr, 0, 1.f);
-        }));
-        tt_tensor* loss = g->loss;
-        const int accumulate = ti > 0 || later_mb;
-        TRY(ctx->submit("ce_loss", {R(rl, ti), accumulate ? RW(loss, 0) : W(loss, 0)}, [=](hipStream_t s, void*) {
-          return tile_xentropy(s, TT_XE_LOSS, rows, 0, 0, nullptr, nullptr, 0, nullptr, F(rl, ti), F(loss, 0),
-                               accumulate, inv_n);
-        }));
+        std::vector<TileArg> T = {{g->ce_lse, ti}, {g->row_loss, ti}};
+        for (int64_t vj = 0; vj < NV; ++vj) T.push_back({parts, L(parts, {vj, ti, 0})});
+        TRY(submit_op(ctx, TT_OP_XENTROPY_MERGE, T.data(), (int)T.size(), nullptr, 0, "ce_merge", false));
+      }
+      {
+        const TileArg T[2] = {{g->row_loss, ti}, {g->loss, 0}};
+        const tt_op_xentropy sc{ti > 0 || later_mb, inv_n};
+        TRY(submit_op(ctx, TT_OP_XENTROPY_LOSS, T, 2, &sc, sizeof(sc), "ce_loss", false));
+      }
+      {
         // dz in place of the logits, all vocab tiles of the token tile in one
         // task and launch
-        {
-          tt_tensor *z = g->z, *lab = g->labels;
-          const int64_t ll = L(lab, {bi, si});
-          std::vector<Access> acc = {R(lab, ll), R(lse, ti)};
-          for (int64_t vj = 0; vj < NV; ++vj) acc.push_back(RW(z, L(z, {bi, si, vj})));
-          TRY(ctx->submit("ce_grad", std::move(acc), [=](hipStream_t s, void*) {
-            std::vector<float*> zs(NV);
-            std::vector<int64_t> lens(NV), offs(NV);
-            for (int64_t vj = 0; vj < NV; ++vj) {
-              const int64_t lz = L(z, {bi, si, vj});
-              int64_t r, cols;
-              z->mat(lz, &r, &cols);
-              zs[vj] = F(z, lz);
-              lens[vj] = cols;
-              offs[vj] = vj * std::min<int64_t>(g->t.vocab, V);
-            }
-            return tile_xentropy_multi(s, TT_XE_GRAD, (int)NV, rows, lens.data(), offs.data(), I32(lab, ll),
-                                       zs.data(), lens.data(), nullptr, 0, F(lse, ti), inv_n);
-          }));
-        }
+        std::vector<TileArg> T = {{g->labels, ll}, {g->ce_lse, ti}};
+        for (int64_t vj = 0; vj < NV; ++vj) T.push_back({z, L(z, {bi, si, vj})});
+        const tt_op_xentropy sc{0, inv_n};
+        TRY(submit_op(ctx, TT_OP_XENTROPY_GRAD, T.data(), (int)T.size(), &sc, sizeof(sc), "ce_grad", false));
       }
     }
 
@@ -1050,55 +838,31 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
         elems += items[k].n;
         grp.push_back(items[k++]);
       }
-      std::vector<Access> acc;
+      std::vector<TileArg> T;
+      const tt_op_optim sc{h.lr, h.beta1, h.beta2, h.eps, h.weight_decay};
       if (h.optimizer == TT_OPT_SGD) {  // p -= lr g: the moments are not touched
         for (const Item& it : grp) {
-          acc.push_back(RW(g->P[it.i], it.lt));
-          acc.push_back(R(g->G[it.i], it.lt));
+          T.push_back({g->P[it.i], it.lt});
+          T.push_back({g->G[it.i], it.lt});
         }
-        TRY(ctx->submit("sgd", acc, [=](hipStream_t s, void*) {
-          float* pp[TT_SGD_MAX_TILES];
-          const float* gg[TT_SGD_MAX_TILES];
-          int64_t nn[TT_SGD_MAX_TILES];
-          for (size_t j = 0; j < grp.size(); ++j) {
-            pp[j] = F(g->P[grp[j].i], grp[j].lt);
-            gg[j] = F(g->G[grp[j].i], grp[j].lt);
-            nn[j] = grp[j].n;
-          }
-          return tile_sgd_multi(s, (int)grp.size(), pp, gg, nn, h.lr);
-        }));
+        TRY(submit_op(ctx, TT_OP_SGD, T.data(), (int)T.size(), &sc, sizeof(sc), "sgd", false));
         continue;
       }
+      T.push_back({bc, 0});
       for (const Item& it : grp) {
-        acc.push_back(RW(g->P[it.i], it.lt));
-        acc.push_back(R(g->G[it.i], it.lt));
-        acc.push_back(RW(g->M[it.i], it.lt));
-        acc.push_back(RW(g->Vv[it.i], it.lt));
+        T.push_back({g->P[it.i], it.lt});
+        T.push_back({g->G[it.i], it.lt});
+        T.push_back({g->M[it.i], it.lt});
+        T.push_back({g->Vv[it.i], it.lt});
       }
-      acc.push_back(R(bc, 0));
-      TRY(ctx->submit("adamw", acc, [=](hipStream_t s, void*) {
-        float *pp[TT_ADAMW_MAX_TILES], *mm[TT_ADAMW_MAX_TILES], *vv[TT_ADAMW_MAX_TILES];
-        const float* gg[TT_ADAMW_MAX_TILES];
-        int64_t nn[TT_ADAMW_MAX_TILES];
-        for (size_t j = 0; j < grp.size(); ++j) {
-          const Item& it = grp[j];
-          pp[j] = F(g->P[it.i], it.lt);
-          gg[j] = F(g->G[it.i], it.lt);
-          mm[j] = F(g->M[it.i], it.lt);
-          vv[j] = F(g->Vv[it.i], it.lt);
-          nn[j] = it.n;
-        }
-        return tile_fused_adamw_multi(s, (int)grp.size(), pp, gg, mm, vv, nn, h.lr, h.beta1, h.beta2, h.eps,
-                                      h.weight_decay, F(bc, 0));
-      }));
+      TRY(submit_op(ctx, TT_OP_ADAMW, T.data(), (int)T.size(), &sc, sizeof(sc), "adamw", false));
     }
     return TT_OK;
   };
   if (do_update && h.optimizer == TT_OPT_ADAMW) {
-    const float b1 = hp->beta1, b2 = hp->beta2;
-    TRY(ctx->submit("adam_step", {RW(stp, 0), W(bc, 0)}, [=](hipStream_t s, void*) {
-      return tile_adamw_advance(s, (int32_t*)stp->dev(0), F(bc, 0), b1, b2);
-    }));
+    const TileArg T[2] = {{stp, 0}, {bc, 0}};
+    const tt_op_optim sc{h.lr, hp->beta1, hp->beta2, h.eps, h.weight_decay};
+    TRY(submit_op(ctx, TT_OP_ADAMW_ADVANCE, T, 2, &sc, sizeof(sc), "adam_step", false));
   }
 
   // ---- backward: head (dz is in place of the logits)
@@ -1127,39 +891,13 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
   for (int64_t si = 0; si < g->ns; ++si)
     for (int64_t bi = 0; bi < g->nb; ++bi)
       for (int64_t ek = 0; ek < NE; ++ek) {
-        tt_tensor *z = g->z, *dnf = g->dnf;
-        const int64_t ld = L(dnf, {bi, si, ek});
-        std::vector<Access> acc;
+        std::vector<TileArg> T = {{g->dnf, L(g->dnf, {bi, si, ek})}};
         for (int64_t vj = 0; vj < NV; ++vj) {
-          acc.push_back(R(z, L(z, {bi, si, vj})));
-          acc.push_back(R(wte, L(wte, {vj, ek})));
+          T.push_back({g->z, L(g->z, {bi, si, vj})});
+          T.push_back({wte, L(wte, {vj, ek})});
         }
-        acc.push_back(W(dnf, ld));
-        int64_t dr, dc;
-        dnf->mat(ld, &dr, &dc);
-        double flops = 0;
-        for (int64_t vj = 0; vj < NV; ++vj) {
-          int64_t zr, zc;
-          z->mat(L(z, {bi, si, vj}), &zr, &zc);
-          flops += 2.0 * dr * dc * zc;
-        }
-        TRY(ctx->submit("head_dx", std::move(acc), [=](hipStream_t s, void*) {
-          std::vector<const float*> As(NV), Bs(NV);
-          std::vector<int64_t> ks(NV), ldas(NV), ldbs(NV);
-          for (int64_t vj = 0; vj < NV; ++vj) {
-            const int64_t lz = L(z, {bi, si, vj}), lw = L(wte, {vj, ek});
-            int64_t zr, zc, wr, wc;
-            z->mat(lz, &zr, &zc);
-            wte->mat(lw, &wr, &wc);
-            As[vj] = F(z, lz);
-            Bs[vj] = F(wte, lw);
-            ks[vj] = zc;
-            ldas[vj] = zc;
-            ldbs[vj] = wc;
-          }
-          return tile_gemm_ksum(s, (int)NV, 0, dr, dc, ks.data(), 1.f, As.data(), ldas.data(), Bs.data(), ldbs.data(),
-                                0.f, F(dnf, ld), dc);
-        }, flops));
+        const tt_op_gemm sc{0, 0, TT_EPI_NONE, 1.f, 0.f, 0};
+        TRY(submit_op(ctx, TT_OP_GEMM_KSUM, T.data(), (int)T.size(), &sc, sizeof(sc), "head_dx", false));
       }
   // zero the LayerNorm and position gradients, which accumulate (over
   // token tiles, and over minibatches after the first)
@@ -1177,9 +915,23 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
   }
   for (int64_t bi = 0; bi < g->nb; ++bi)
     for (int64_t si = 0; si < g->ns; ++si)
-      TRY(ln_backward(g, g->dnf, g->h_last, lnfg, g->lnf, g->dh, 0, g->G[g->lnf_g()], g->G[g->lnf_g() + 1],
-                      bi + g->nb * si, bi, si));
+      TRY(ln_backward(g, g->dnf, g->h_last, lnfg, g->lnf, g->dh, 0, g->G[g->lnf_g()], g->G[g->lnf_g() + 1], bi,
+                      si));
   TRY(adamw_of({(size_t)g->lnf_g(), (size_t)g->lnf_g() + 1}));
+
+  // bias gradients of a row of tiles (token tile (bi, si), n feature
+  // tiles): up to 16 tiles per task, one pair of launches each
+  auto colsum_row = [&](tt_tensor* x, tt_tensor* out, int64_t n, int64_t bi, int64_t si, int beta) -> int {
+    for (int64_t f0 = 0; f0 < n; f0 += 16) {
+      std::vector<TileRef> xs, os;
+      for (int64_t f = f0; f < std::min(n, f0 + 16); ++f) {
+        xs.push_back({x, L(x, {bi, si, f})});
+        os.push_back({out, f});
+      }
+      TRY(colsum_task(ctx, xs, os, beta));
+    }
+    return TT_OK;
+  };
 
   // ---- blocks backward
   for (int l = c.n_layer - 1; l >= 0; --l) {
@@ -1212,8 +964,7 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
             }
           TRY(submit_gemm_batch(ctx, "mlp_proj_dw", qs, true));
         }
-        for (int64_t ej = 0; ej < NE; ++ej)
-          TRY(colsum_task(ctx, g->dh, L(g->dh, {bi, si, ej}), gbp, ej, ti > 0 || later_mb));
+        TRY(colsum_row(g->dh, gbp, NE, bi, si, ti > 0 || later_mb));
         for (int64_t ik = 0; ik < NI; ++ik)
           for (int64_t ej = 0; ej < NE; ++ej) {
             Gemm q;
@@ -1242,8 +993,7 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
             }
           TRY(submit_gemm_batch(ctx, "fc_dw", qs, true));
         }
-        for (int64_t ik = 0; ik < NI; ++ik)
-          TRY(colsum_task(ctx, g->dgu, L(g->dgu, {bi, si, ik}), gbfc, ik, ti > 0 || later_mb));
+        TRY(colsum_row(g->dgu, gbfc, NI, bi, si, ti > 0 || later_mb));
         // (a chain of accumulating GEMMs: as one long-K task per embd tile it
         // measured slower on the wide model, 65 -> 71 ms per step)
         for (int64_t ek = 0; ek < NE; ++ek)
@@ -1256,8 +1006,8 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
             q.beta = ik > 0 ? 1.f : 0.f;
             TRY(submit_gemm(ctx, "fc_dx", q));
           }
-        TRY(ln_backward(g, g->dn, b.h_mid, ln2g, b.ln2, g->dh, 1, g->G[g->pidx(l, LN2G)], g->G[g->pidx(l, LN2B)], ti,
-                        bi, si));
+        TRY(ln_backward(g, g->dn, b.h_mid, ln2g, b.ln2, g->dh, 1, g->G[g->pidx(l, LN2G)], g->G[g->pidx(l, LN2B)], bi,
+                        si));
         // attention projection: h_mid = h_in + O W_o + b_o
         {
           std::vector<Gemm> qs;
@@ -1273,8 +1023,7 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
             }
           TRY(submit_gemm_batch(ctx, "attn_proj_dw", qs, true));
         }
-        for (int64_t ej = 0; ej < NE; ++ej)
-          TRY(colsum_task(ctx, g->dh, L(g->dh, {bi, si, ej}), gbo, ej, ti > 0 || later_mb));
+        TRY(colsum_row(g->dh, gbo, NE, bi, si, ti > 0 || later_mb));
         for (int64_t hk = 0; hk < NH; ++hk)
           for (int64_t ej = 0; ej < NE; ++ej) {
             Gemm q;
@@ -1290,31 +1039,19 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
     for (int64_t bi = 0; bi < g->nb; ++bi)
       for (int64_t hj = 0; hj < NH; ++hj) {
         for (int64_t qi = 0; qi < g->ns; ++qi) {
-          tt_tensor *O = b.o, *dO = g->dO, *Dv = g->Dv;
-          const int64_t lq = L(O, {bi, qi, hj, 0}), ld = L(Dv, {bi, qi, hj, 0});
-          TRY(ctx->submit("attn_prep", {R(O, lq), R(dO, lq), W(Dv, ld)}, [=](hipStream_t s, void*) {
-            return tile_attention_bwd(s, TT_ATT_PREP, bt, ht, sq, sq, hd, 0, 0, nullptr, nullptr, nullptr, F(O, lq),
-                                      F(dO, lq), nullptr, F(Dv, ld), nullptr, nullptr, nullptr, 0, 0, scale);
-          }));
+          const int64_t lq = L(b.o, {bi, qi, hj, 0});
+          const TileArg T[3] = {{b.o, lq}, {g->dO, lq}, {g->Dv, L(g->Dv, {bi, qi, hj, 0})}};
+          const tt_op_attention sc{0, 0, 0, 0, 0, 0, scale};
+          TRY(submit_op(ctx, TT_OP_ATTENTION_PREP, T, 3, &sc, sizeof(sc), "attn_prep", false));
         }
         for (int64_t qi = 0; qi < g->ns; ++qi)
           for (int64_t ki = 0; ki <= qi; ++ki) {
-            tt_tensor *Q = b.q, *K = b.k, *Vt = b.v, *dO = g->dO, *lse = b.lse, *Dv = g->Dv;
-            tt_tensor *dq = g->dq, *dk = g->dk, *dv = g->dv;
-            const int64_t lq = L(Q, {bi, qi, hj, 0}), lk = L(K, {bi, ki, hj, 0});
-            const int64_t ls = L(lse, {bi, qi, hj, 0});
-            const int acc_q = ki > 0, acc_kv = qi > ki;
-            TRY(ctx->submit("attn_bwd",
-                            {R(Q, lq), R(K, lk), R(Vt, lk), R(dO, lq), R(lse, ls), R(Dv, ls),
-                             acc_q ? RW(dq, lq) : W(dq, lq), acc_kv ? RW(dk, lk) : W(dk, lk),
-                             acc_kv ? RW(dv, lk) : W(dv, lk)},
-                            [=](hipStream_t s, void*) {
-                              return tile_attention_bwd(s, TT_ATT_GRAD, bt, ht, sq, sq, hd, qi * sq, ki * sq, F(Q, lq),
-                                                        F(K, lk), F(Vt, lk), nullptr, F(dO, lq), F(lse, ls),
-                                                        F(Dv, ls), F(dq, lq), F(dk, lk), F(dv, lk), acc_q, acc_kv,
-                                                        scale);
-                            },
-                            10.0 * bt * ht * hd * (qi == ki ? sq * (sq + 1) / 2.0 : (double)sq * sq)));
+            const int64_t lq = L(b.q, {bi, qi, hj, 0}), lk = L(b.k, {bi, ki, hj, 0});
+            const int64_t ls = L(b.lse, {bi, qi, hj, 0});
+            const TileArg T[9] = {{b.q, lq},   {b.k, lk},   {b.v, lk},   {g->dO, lq}, {b.lse, ls},
+                                  {g->Dv, ls}, {g->dq, lq}, {g->dk, lk}, {g->dv, lk}};
+            const tt_op_attention sc{qi * sq, ki * sq, 0, 0, ki > 0, qi > ki, scale};
+            TRY(submit_op(ctx, TT_OP_ATTENTION_BWD, T, 9, &sc, sizeof(sc), "attn_bwd", false));
           }
       }
     // QKV projection backward
@@ -1346,33 +1083,10 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
               xs.push_back({dqkv[cq], L(dqkv[cq], {bi, si, hj, 0})});
               os.push_back({gbqkv, L(gbqkv, {cq, hj, 0})});
             }
-          const int beta = ti > 0 || later_mb;
           for (size_t u0 = 0; u0 < xs.size(); u0 += 15) {
             const size_t u1 = std::min(xs.size(), u0 + 15);
-            std::vector<TileRef> xg(xs.begin() + u0, xs.begin() + u1), og(os.begin() + u0, os.begin() + u1);
-            std::vector<Access> acc;
-            for (size_t u = 0; u < xg.size(); ++u) {
-              acc.push_back(R(xg[u].t, xg[u].lin));
-              acc.push_back(beta ? RW(og[u].t, og[u].lin) : W(og[u].t, og[u].lin));
-            }
-            TRY(ctx->submit("colsum", std::move(acc), [xg, og, beta, ctx](hipStream_t s, void* ws) {
-              const size_t c = xg.size();
-              std::vector<const float*> X(c);
-              std::vector<float*> O(c);
-              std::vector<int64_t> cols(c), ldx(c);
-              int64_t rows = 0;
-              for (size_t u = 0; u < c; ++u) {
-                int64_t r, cc;
-                xg[u].t->mat(xg[u].lin, &r, &cc);
-                rows = r;
-                X[u] = F(xg[u].t, xg[u].lin);
-                O[u] = F(og[u].t, og[u].lin);
-                cols[u] = cc;
-                ldx[u] = cc;
-              }
-              return tile_reduce_rows_multi(s, (int)c, rows, cols.data(), X.data(), ldx.data(), O.data(), beta, ws,
-                                            ctx->workspace_bytes);
-            }));
+            TRY(colsum_task(ctx, {xs.begin() + u0, xs.begin() + u1}, {os.begin() + u0, os.begin() + u1},
+                            ti > 0 || later_mb));
           }
         }
         // dn = sum over (q|k|v, head tile) of dqkv W_qkv^T: one task per embd
@@ -1386,8 +1100,8 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
             }
           TRY(submit_ksum_tb(ctx, "qkv_dx", {g->dn, L(g->dn, {bi, si, ek})}, As, Bs));
         }
-        TRY(ln_backward(g, g->dn, b.h_in, ln1g, b.ln1, g->dh, 1, g->G[g->pidx(l, LN1G)], g->G[g->pidx(l, LN1B)], ti,
-                        bi, si));
+        TRY(ln_backward(g, g->dn, b.h_in, ln1g, b.ln1, g->dh, 1, g->G[g->pidx(l, LN1G)], g->G[g->pidx(l, LN1B)], bi,
+                        si));
       }
     (void)qkv;
     {
@@ -1401,48 +1115,28 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
   // In HBM the dwte tiles of one embd column are one contiguous [V, et] slab
   // (first grid axis fastest), so one launch per (embd tile, token tile)
   // covers every vocab tile; staged pinned tiles are separate, one launch each.
-  if (gwte->home == TT_HOME_DEVICE) {
-    for (int64_t ek = 0; ek < NE; ++ek)
-      for (int64_t si = 0; si < g->ns; ++si)
-        for (int64_t bi = 0; bi < g->nb; ++bi) {
-          tt_tensor *dh = g->dh, *so = g->sorted, *pe = g->perm;
-          const int64_t ld = L(dh, {bi, si, ek}), li = L(so, {bi, si}), lw0 = L(gwte, {0, ek});
-          int64_t r, cols;
-          dh->mat(ld, &r, &cols);
-          std::vector<Access> acc = {R(dh, ld), R(so, li), R(pe, li)};
-          for (int64_t vj = 0; vj < NV; ++vj) acc.push_back(RW(gwte, L(gwte, {vj, ek})));
-          TRY(ctx->submit("emb_dw", acc, [=](hipStream_t s, void*) {
-            return tile_embedding_bwd(s, TT_EMB_TOKEN, rows, cols, I32(so, li), I32(pe, li), 0, V, sq, F(dh, ld), cols,
-                                      F(gwte, lw0), cols);
-          }));
+  for (int64_t ek = 0; ek < NE; ++ek)
+    for (int64_t si = 0; si < g->ns; ++si)
+      for (int64_t bi = 0; bi < g->nb; ++bi) {
+        const int64_t li = L(g->sorted, {bi, si});
+        const TileArg head[3] = {{g->dh, L(g->dh, {bi, si, ek})}, {g->sorted, li}, {g->perm, li}};
+        const tt_op_embedding sc{sq};
+        // in HBM the dwte tiles of one embd column are one contiguous slab:
+        // one task and launch over every vocab tile; staged pinned tiles are
+        // separate, one task per vocab tile
+        const int64_t per = gwte->home == TT_HOME_DEVICE ? NV : 1;
+        for (int64_t v0 = 0; v0 < NV; v0 += per) {
+          std::vector<TileArg> T(head, head + 3);
+          for (int64_t vj = v0; vj < v0 + per; ++vj) T.push_back({gwte, L(gwte, {vj, ek})});
+          TRY(submit_op(ctx, TT_OP_EMBEDDING_BWD, T.data(), (int)T.size(), &sc, sizeof(sc), "emb_dw", false));
         }
-  } else
-  for (int64_t vj = 0; vj < NV; ++vj)
-    for (int64_t ek = 0; ek < NE; ++ek)
-      for (int64_t si = 0; si < g->ns; ++si)
-        for (int64_t bi = 0; bi < g->nb; ++bi) {
-          tt_tensor *dh = g->dh, *so = g->sorted, *pe = g->perm;
-          const int64_t ld = L(dh, {bi, si, ek}), li = L(so, {bi, si}), lw = L(gwte, {vj, ek});
-          int64_t r, cols, vr, vc;
-          dh->mat(ld, &r, &cols);
-          gwte->mat(lw, &vr, &vc);
-          const int64_t voff = vj * std::min<int64_t>(g->t.vocab, V);
-          TRY(ctx->submit("emb_dw", {R(dh, ld), R(so, li), R(pe, li), RW(gwte, lw)}, [=](hipStream_t s, void*) {
-            return tile_embedding_bwd(s, TT_EMB_TOKEN, rows, cols, I32(so, li), I32(pe, li), voff, vr, sq, F(dh, ld),
-                                      cols, F(gwte, lw), cols);
-          }));
-        }
+      }
   for (int64_t si = 0; si < g->ns; ++si)
     for (int64_t ek = 0; ek < NE; ++ek)
       for (int64_t bi = 0; bi < g->nb; ++bi) {
-        tt_tensor *dh = g->dh, *gwpe = g->G[1];
-        const int64_t ld = L(dh, {bi, si, ek}), lw = L(gwpe, {si, ek});
-        int64_t r, cols;
-        dh->mat(ld, &r, &cols);
-        TRY(ctx->submit("emb_dpos", {R(dh, ld), RW(gwpe, lw)}, [=](hipStream_t s, void*) {
-          return tile_embedding_bwd(s, TT_EMB_POS, rows, cols, nullptr, nullptr, 0, 0, sq, F(dh, ld), cols,
-                                    F(gwpe, lw), cols);
-        }));
+        const TileArg T[2] = {{g->dh, L(g->dh, {bi, si, ek})}, {g->G[1], L(g->G[1], {si, ek})}};
+        const tt_op_embedding sc{sq};
+        TRY(submit_op(ctx, TT_OP_EMBEDDING_POS_BWD, T, 2, &sc, sizeof(sc), "emb_dpos", false));
       }
 
   // ---- AdamW of the embeddings (their gradients are final now)

@@ -409,6 +409,317 @@ extern "C" int tile_layernorm_bwd(void* stream, int phase, int64_t rows, int64_t
   return tt::launch_status("tile_layernorm_bwd(colsum)");
 }
 
+// ------------------------------------------- LayerNorm over several tiles
+//
+// A row block whose features are split over n tiles (n >= 2, all tiles as
+// wide as the first but the last, widths multiples of 4) in one pass: every
+// row is read once and written once, so the forward moves 8 bytes per
+// element and the backward 12 (16 when dx accumulates) -- against 12 and
+// 20 for the per-tile partial / merge / apply phases, which read every tile
+// twice. A workgroup of BT threads holds a whole row in registers (VPT
+// float4 per thread) and takes several consecutive rows, keeping gamma and
+// beta in registers across them. Sums over a row combine the lanes of each
+// wave by a fixed butterfly and the waves in wave order (deterministic).
+
+namespace {
+
+constexpr int kLnTilesMax = 16;
+struct LnRowTiles {
+  const float* x[kLnTilesMax];
+  const float* dy[kLnTilesMax];
+  const float* g[kLnTilesMax];
+  const float* b[kLnTilesMax];
+  float* y[kLnTilesMax];   // forward: y; backward: dx
+  float* dg[kLnTilesMax];
+  float* db[kLnTilesMax];
+  int n, c0, total;
+};
+
+// tile of row element `col` (a multiple of 4), its column in that tile and the tile's width
+__device__ __forceinline__ int ln_tile(const LnRowTiles& P, int col, int* within, int* width) {
+  int t = col / P.c0;
+  if (t > P.n - 1) t = P.n - 1;
+  *within = col - t * P.c0;
+  *width = t < P.n - 1 ? P.c0 : P.total - (P.n - 1) * P.c0;
+  return t;
+}
+
+// sum over the workgroup: waves by butterfly, then the wave sums in wave
+// order by every thread (the same order everywhere)
+template <int BT>
+__device__ __forceinline__ void block_sum2(float& a, float& b, float (*red)[BT / 64]) {
+  a = tt::wave_sum(a);
+  b = tt::wave_sum(b);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red[0][w] = a;
+    red[1][w] = b;
+  }
+  __syncthreads();
+  a = 0.f;
+  b = 0.f;
+#pragma unroll
+  for (int i = 0; i < BT / 64; ++i) {
+    a += red[0][i];
+    b += red[1][i];
+  }
+  __syncthreads();
+}
+
+template <int BT, int VPT>
+__global__ __launch_bounds__(BT) void ln_fwd_multi(int rows, int rows_per_block, LnRowTiles P,
+                                                   float* __restrict__ stats, float eps) {
+  __shared__ float red[2][BT / 64];
+  const float* xp[VPT];
+  float* yp[VPT];
+  int ld[VPT];
+  bool ok[VPT];
+  f32x4 g[VPT], b[VPT];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int col = 4 * ((int)threadIdx.x + k * BT);
+    ok[k] = col < P.total;
+    int w = 0, width = 4, t = 0;
+    if (ok[k]) t = ln_tile(P, col, &w, &width);
+    xp[k] = P.x[t] + w;
+    yp[k] = P.y[t] + w;
+    ld[k] = width;
+    g[k] = ok[k] ? *reinterpret_cast<const f32x4*>(P.g[t] + w) : f32x4{0.f, 0.f, 0.f, 0.f};
+    b[k] = ok[k] ? *reinterpret_cast<const f32x4*>(P.b[t] + w) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float inv_n = 1.f / (float)P.total;
+  const int r0 = blockIdx.x * rows_per_block, r1 = min(rows, r0 + rows_per_block);
+  for (int r = r0; r < r1; ++r) {
+    f32x4 v[VPT];
+    float s = 0.f, unused = 0.f;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      v[k] = ok[k] ? *reinterpret_cast<const f32x4*>(xp[k] + (int64_t)r * ld[k]) : f32x4{0.f, 0.f, 0.f, 0.f};
+      s += (v[k][0] + v[k][1]) + (v[k][2] + v[k][3]);
+    }
+    block_sum2<BT>(s, unused, red);
+    const float mean = s * inv_n;
+    float m2 = 0.f;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k)
+      if (ok[k]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float d = v[k][i] - mean;
+          m2 += d * d;
+        }
+      }
+    unused = 0.f;
+    block_sum2<BT>(m2, unused, red);
+    const float rstd = 1.f / sqrtf(m2 * inv_n + eps);
+    if (threadIdx.x == 0) {
+      stats[(int64_t)r * 2] = mean;
+      stats[(int64_t)r * 2 + 1] = rstd;
+    }
+#pragma unroll
+    for (int k = 0; k < VPT; ++k)
+      if (ok[k]) {
+        f32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = (v[k][i] - mean) * rstd * g[k][i] + b[k][i];
+        *reinterpret_cast<f32x4*>(yp[k] + (int64_t)r * ld[k]) = o;
+      }
+  }
+}
+
+// dx (+)= rstd * (dxhat - mean(dxhat) - xhat * mean(dxhat * xhat)) for the
+// block's rows; the block's column partials of dy*xhat and dy go to
+// ws[block][2][total]
+template <int BT, int VPT>
+__global__ __launch_bounds__(BT) void ln_bwd_multi(int rows, int rows_per_block, LnRowTiles P,
+                                                   const float* __restrict__ stats, int dx_acc, float* __restrict__ ws) {
+  __shared__ float red[2][BT / 64];
+  const float *xp[VPT], *dyp[VPT];
+  float* dxp[VPT];
+  int ld[VPT];
+  bool ok[VPT];
+  f32x4 g[VPT], dg[VPT], db[VPT];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int col = 4 * ((int)threadIdx.x + k * BT);
+    ok[k] = col < P.total;
+    int w = 0, width = 4, t = 0;
+    if (ok[k]) t = ln_tile(P, col, &w, &width);
+    xp[k] = P.x[t] + w;
+    dyp[k] = P.dy[t] + w;
+    dxp[k] = P.y[t] + w;
+    ld[k] = width;
+    g[k] = ok[k] ? *reinterpret_cast<const f32x4*>(P.g[t] + w) : f32x4{0.f, 0.f, 0.f, 0.f};
+    dg[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    db[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float inv_n = 1.f / (float)P.total;
+  const int r0 = blockIdx.x * rows_per_block, r1 = min(rows, r0 + rows_per_block);
+  for (int r = r0; r < r1; ++r) {
+    const float mean = stats[(int64_t)r * 2], rstd = stats[(int64_t)r * 2 + 1];
+    f32x4 xh[VPT], dxh[VPT];
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      f32x4 xv = f32x4{0.f, 0.f, 0.f, 0.f}, dv = xv;
+      if (ok[k]) {
+        xv = *reinterpret_cast<const f32x4*>(xp[k] + (int64_t)r * ld[k]);
+        dv = *reinterpret_cast<const f32x4*>(dyp[k] + (int64_t)r * ld[k]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xh[k][i] = ok[k] ? (xv[i] - mean) * rstd : 0.f;
+        dxh[k][i] = dv[i] * g[k][i];
+        s1 += dxh[k][i];
+        s2 += dxh[k][i] * xh[k][i];
+        dg[k][i] += dv[i] * xh[k][i];
+        db[k][i] += dv[i];
+      }
+    }
+    block_sum2<BT>(s1, s2, red);
+    const float a1 = s1 * inv_n, a2 = s2 * inv_n;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k)
+      if (ok[k]) {
+        float* q = dxp[k] + (int64_t)r * ld[k];
+        f32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = rstd * (dxh[k][i] - a1 - xh[k][i] * a2);
+        if (dx_acc) o += *reinterpret_cast<const f32x4*>(q);
+        *reinterpret_cast<f32x4*>(q) = o;
+      }
+  }
+  float* out = ws + (int64_t)blockIdx.x * 2 * P.total;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k)
+    if (ok[k]) {
+      const int col = 4 * ((int)threadIdx.x + k * BT);
+      *reinterpret_cast<f32x4*>(out + col) = dg[k];
+      *reinterpret_cast<f32x4*>(out + P.total + col) = db[k];
+    }
+}
+
+// dgamma / dbeta of every tile += the column sums of the block partials,
+// blockIdx.y = 2 * tile + (0: dgamma, 1: dbeta)
+__global__ __launch_bounds__(1024) void ln_colsum_finish_multi(int nblk, LnRowTiles P, const float* __restrict__ ws) {
+  const int t = blockIdx.y >> 1, which = blockIdx.y & 1;
+  const int width = t < P.n - 1 ? P.c0 : P.total - (P.n - 1) * P.c0;
+  if ((int)blockIdx.x * 64 >= width) return;
+  colsum_finish_block(nblk, width, ws, (int64_t)2 * P.total, (int64_t)which * P.total + (int64_t)t * P.c0,
+                      which ? P.db[t] : P.dg[t], 1);
+}
+
+constexpr int kLnFwdRowsPerBlock = 4;
+constexpr int kLnBwdRowsPerBlock = 16;
+
+// workgroup size and float4 per thread for a row of `total` features
+void ln_multi_geometry(int64_t total, int* bt, int* vpt) {
+  const int64_t f4 = total / 4;
+  *bt = f4 <= 256 ? 256 : (f4 <= 512 ? 512 : 1024);
+  const int v = (int)((f4 + *bt - 1) / *bt);
+  *vpt = v <= 1 ? 1 : (v <= 2 ? 2 : 4);
+}
+
+// checks shared by both directions; fills the tile table's geometry
+int ln_multi_check(const char* nm, int count, int64_t rows, const int64_t* cols, LnRowTiles* P) {
+  using tt::fail;
+  if (count < 2 || count > kLnTilesMax) return fail(TT_ERR_ARG, "%s: count must be 2..%d", nm, kLnTilesMax);
+  if (rows < 0 || rows > INT32_MAX) return fail(TT_ERR_ARG, "%s: bad row count", nm);
+  if (!cols) return fail(TT_ERR_ARG, "%s: null cols", nm);
+  int64_t total = 0;
+  for (int t = 0; t < count; ++t) {
+    if (cols[t] < 4 || cols[t] % 4 || (t < count - 1 && cols[t] != cols[0]) || cols[t] > cols[0])
+      return fail(TT_ERR_SHAPE, "%s: tile widths must be multiples of 4, equal but for a narrower last tile", nm);
+    total += cols[t];
+  }
+  if (total > 16384) return fail(TT_ERR_SHAPE, "%s: %lld features exceed 16384", nm, (long long)total);
+  P->n = count;
+  P->c0 = (int)cols[0];
+  P->total = (int)total;
+  return TT_OK;
+}
+
+}  // namespace
+
+extern "C" int tile_layernorm_fwd_multi(void* stream, int count, int64_t rows, const int64_t* cols,
+                                        const float* const* x, const float* const* gamma, const float* const* beta,
+                                        float* stats, float* const* y, float eps) {
+  using tt::fail;
+  LnRowTiles P{};
+  if (int rc = ln_multi_check("tile_layernorm_fwd_multi", count, rows, cols, &P)) return rc;
+  if (rows == 0) return TT_OK;
+  if (!x || !gamma || !beta || !y || !stats) return fail(TT_ERR_ARG, "tile_layernorm_fwd_multi: null array");
+  for (int t = 0; t < count; ++t) {
+    if (!tt::aligned16(x[t]) || !tt::aligned16(y[t]) || !tt::aligned16(gamma[t]) || !tt::aligned16(beta[t]))
+      return fail(TT_ERR_ARG, "tile_layernorm_fwd_multi: tile %d is null or not 16-byte aligned", t);
+    P.x[t] = x[t];
+    P.y[t] = y[t];
+    P.g[t] = gamma[t];
+    P.b[t] = beta[t];
+  }
+  int bt, vpt;
+  ln_multi_geometry(P.total, &bt, &vpt);
+  const int r = (int)rows;
+  dim3 grid((unsigned)((r + kLnFwdRowsPerBlock - 1) / kLnFwdRowsPerBlock));
+  hipStream_t s = tt::as_stream(stream);
+#define TT_LNF(BT, VPT) hipLaunchKernelGGL((ln_fwd_multi<BT, VPT>), grid, dim3(BT), 0, s, r, kLnFwdRowsPerBlock, P, stats, eps)
+  if (bt == 256) TT_LNF(256, 1);
+  else if (bt == 512) TT_LNF(512, 1);
+  else if (vpt == 1) TT_LNF(1024, 1);
+  else if (vpt == 2) TT_LNF(1024, 2);
+  else TT_LNF(1024, 4);
+#undef TT_LNF
+  return tt::launch_status("tile_layernorm_fwd_multi");
+}
+
+extern "C" size_t tile_layernorm_bwd_multi_workspace(int64_t rows, int64_t total) {
+  const int64_t nblk = (rows + kLnBwdRowsPerBlock - 1) / kLnBwdRowsPerBlock;
+  return (size_t)(nblk * 2 * total * sizeof(float));
+}
+
+extern "C" int tile_layernorm_bwd_multi(void* stream, int count, int64_t rows, const int64_t* cols,
+                                        const float* const* dy, const float* const* x, const float* const* gamma,
+                                        const float* stats, float* const* dx, int dx_acc, float* const* dgamma,
+                                        float* const* dbeta, void* workspace, size_t workspace_bytes) {
+  using tt::fail;
+  LnRowTiles P{};
+  if (int rc = ln_multi_check("tile_layernorm_bwd_multi", count, rows, cols, &P)) return rc;
+  if (rows == 0) return TT_OK;
+  if (!dy || !x || !gamma || !dx || !dgamma || !dbeta || !stats || !workspace)
+    return fail(TT_ERR_ARG, "tile_layernorm_bwd_multi: null array or workspace");
+  if (workspace_bytes < tile_layernorm_bwd_multi_workspace(rows, P.total) || !tt::aligned16(workspace))
+    return fail(TT_ERR_ARG, "tile_layernorm_bwd_multi: workspace too small or misaligned");
+  for (int t = 0; t < count; ++t) {
+    if (!tt::aligned16(x[t]) || !tt::aligned16(dy[t]) || !tt::aligned16(dx[t]) || !tt::aligned16(gamma[t]) ||
+        !dgamma[t] || !dbeta[t])
+      return fail(TT_ERR_ARG, "tile_layernorm_bwd_multi: tile %d is null or not 16-byte aligned", t);
+    P.x[t] = x[t];
+    P.dy[t] = dy[t];
+    P.y[t] = dx[t];
+    P.g[t] = gamma[t];
+    P.dg[t] = dgamma[t];
+    P.db[t] = dbeta[t];
+  }
+  int bt, vpt;
+  ln_multi_geometry(P.total, &bt, &vpt);
+  const int r = (int)rows;
+  const int nblk = (r + kLnBwdRowsPerBlock - 1) / kLnBwdRowsPerBlock;
+  float* ws = (float*)workspace;
+  hipStream_t s = tt::as_stream(stream);
+#define TT_LNB(BT, VPT) \
+  hipLaunchKernelGGL((ln_bwd_multi<BT, VPT>), dim3(nblk), dim3(BT), 0, s, r, kLnBwdRowsPerBlock, P, stats, dx_acc, ws)
+  if (bt == 256) TT_LNB(256, 1);
+  else if (bt == 512) TT_LNB(512, 1);
+  else if (vpt == 1) TT_LNB(1024, 1);
+  else if (vpt == 2) TT_LNB(1024, 2);
+  else TT_LNB(1024, 4);
+#undef TT_LNB
+  if (int rc = tt::launch_status("tile_layernorm_bwd_multi")) return rc;
+  hipLaunchKernelGGL(ln_colsum_finish_multi, dim3((unsigned)((P.c0 + 63) / 64), (unsigned)(2 * count)), dim3(1024), 0,
+                     s, nblk, P, ws);
+  return tt::launch_status("tile_layernorm_bwd_multi(colsum)");
+}
+
 // ------------------------------------------------------------ reduce_rows
 
 namespace {

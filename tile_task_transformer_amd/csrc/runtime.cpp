@@ -144,6 +144,19 @@ int tt_ctx::acquire_event(int* idx) {
   return TT_OK;
 }
 
+// events that order the executor against streams it does not own: each
+// hipStreamWaitEvent takes the event's state at the time of the call, so a
+// small fixed set is reused
+int tt_ctx::ext_events_init() {
+  const size_t want = streams.size() + 3;
+  while (ext_events.size() < want) {
+    hipEvent_t e;
+    TT_HIP_TRY(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    ext_events.push_back(e);
+  }
+  return TT_OK;
+}
+
 int tt_ctx::ensure_workspace(size_t bytes) {
   if (bytes <= workspace_bytes || dryrun) {
     workspace_bytes = std::max(workspace_bytes, bytes);
@@ -700,9 +713,14 @@ int tt_ctx::wait_all() {
 }
 
 void tt_ctx::forget_launched() {
-  // write-back events are recycled with the others
-  for (auto& t : tensors)
+  // write-back events are recycled with the others; every reader recorded
+  // so far has completed, so no later task needs an edge to it (tiles that
+  // are only read, such as parameters in steps without an update, would
+  // otherwise collect reader ids without bound)
+  for (auto& t : tensors) {
     for (auto& r : t->res) r.wb_event = -1;
+    for (auto& st : t->state) st.readers.clear();
+  }
   dirty_free.clear();
   done_below = next_id;
   launched.clear();
@@ -847,6 +865,7 @@ int tt_ctx_destroy(tt_ctx* c) {
       if (p) (void)hipFree(p);
     for (auto e : c->events) (void)hipEventDestroy(e);
     for (auto e : c->prof_events) (void)hipEventDestroy(e);
+    for (auto e : c->ext_events) (void)hipEventDestroy(e);
     for (auto s : c->streams) (void)hipStreamDestroy(s);
     if (c->copy_stream) (void)hipStreamDestroy(c->copy_stream);
     if (c->d2h_stream) (void)hipStreamDestroy(c->d2h_stream);
@@ -958,6 +977,13 @@ int tt_tensor_destroy(tt_tensor* t) {
   auto it = std::find(c->tensors.begin(), c->tensors.end(), t);
   if (it != c->tensors.end()) c->tensors.erase(it);
   delete t;
+  return TT_OK;
+}
+
+int tt_tensor_set_matrix_split(tt_tensor* t, int k) {
+  clear_error();
+  if (!t || k < 0 || k > t->ndim) return fail(TT_ERR_ARG, "tt_tensor_set_matrix_split: bad argument");
+  t->mat_split = k;
   return TT_OK;
 }
 
@@ -1117,6 +1143,35 @@ int tt_submit_fill(tt_ctx* c, tt_tensor* t, const int64_t* idx, float value) {
   return c->submit("fill", {tt::W(t, l)}, [=](hipStream_t s, void*) {
     return tile_fill(s, n, (float*)t->dev(l), value);
   });
+}
+
+int tt_ctx_wait_stream(tt_ctx* c, void* stream) {
+  clear_error();
+  if (!c) return fail(TT_ERR_ARG, "tt_ctx_wait_stream: null");
+  if (c->capturing) return fail(TT_ERR_STATE, "tt_ctx_wait_stream: a graph is being captured");
+  if (c->dryrun) return TT_OK;
+  // tasks still held in the window launch later, so they wait too
+  if (int rc = c->ext_events_init()) return rc;
+  TT_HIP_TRY(hipEventRecord(c->ext_events[0], as_stream(stream)));
+  for (auto s : c->streams) TT_HIP_TRY(hipStreamWaitEvent(s, c->ext_events[0], 0));
+  return TT_OK;
+}
+
+int tt_ctx_join_stream(tt_ctx* c, void* stream) {
+  clear_error();
+  if (!c) return fail(TT_ERR_ARG, "tt_ctx_join_stream: null");
+  if (c->capturing) return fail(TT_ERR_STATE, "tt_ctx_join_stream: a graph is being captured");
+  if (c->dryrun) return c->flush();
+  if (int rc = c->flush()) return rc;
+  if (int rc = c->ext_events_init()) return rc;
+  std::vector<hipStream_t> all(c->streams);
+  all.push_back(c->copy_stream);
+  all.push_back(c->d2h_stream);
+  for (size_t i = 0; i < all.size(); ++i) {
+    TT_HIP_TRY(hipEventRecord(c->ext_events[1 + i], all[i]));
+    TT_HIP_TRY(hipStreamWaitEvent(as_stream(stream), c->ext_events[1 + i], 0));
+  }
+  return TT_OK;
 }
 
 int tt_wait(tt_ctx* c) {

@@ -156,6 +156,8 @@ struct tt_ctx {
   // events
   std::vector<hipEvent_t> events;
   int events_used = 0;
+  std::vector<hipEvent_t> ext_events;  // tt_ctx_wait_stream / tt_ctx_join_stream
+  int ext_events_init();
 
   // residency of pinned-host tiles: device copies live in one arena of
   // `budget` bytes (first-fit with coalescing); LRU eviction writes dirty

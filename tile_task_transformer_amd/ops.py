@@ -21,7 +21,8 @@ __all__ = [
     "tile_adamw_advance", "tile_sgd", "tile_sgd_multi",
     "tile_embedding_fwd", "tile_embedding_index", "tile_embedding_bwd", "tile_reduce_rows",
     "tile_reduce_rows_workspace", "tile_reduce_rows_multi", "tile_fill", "tile_fill_multi", "tile_split_tokens",
-    "tt_probe_mfma_f32",
+    "tt_probe_mfma_f32", "tile_layernorm_fwd_multi", "tile_layernorm_bwd_multi",
+    "tile_layernorm_bwd_multi_workspace",
     "TT_EPI_NONE", "TT_EPI_BIAS", "TT_EPI_RES", "TT_EPI_GELU", "TT_EPI_GELU_BWD", "TT_LN_PARTIAL",
     "TT_LN_MERGE", "TT_LN_APPLY", "TT_LN_FUSED", "TT_SM_STATS", "TT_SM_MERGE", "TT_SM_APPLY", "TT_XE_LOSS",
     "TT_XE_GRAD", "TT_XE_STATS", "TT_ATT_PREP", "TT_ATT_GRAD", "TT_EMB_TOKEN", "TT_EMB_POS",
@@ -227,3 +228,31 @@ def tt_probe_mfma_f32(stream, blocks, iters, out):
     f = C.c_double()
     check(lib.tt_probe_mfma_f32(stream_handle(stream), blocks, iters, ptr(out), C.byref(f)))
     return f.value
+
+
+def _arrs(n, *lists):
+    import ctypes as C
+    return [(C.c_void_p * max(n, 1))(*[ptr(x) for x in lst]) for lst in lists]
+
+
+def tile_layernorm_fwd_multi(stream, rows, cols, xs, gammas, betas, stats, ys, eps=1e-5):
+    """LayerNorm of a row block over several feature tiles in one pass."""
+    import ctypes as C
+    n = len(xs)
+    c = (C.c_int64 * n)(*[int(v) for v in cols])
+    x, g, b, y = _arrs(n, xs, gammas, betas, ys)
+    return check(lib.tile_layernorm_fwd_multi(stream_handle(stream), n, rows, c, x, g, b, ptr(stats), y, eps))
+
+
+def tile_layernorm_bwd_multi(stream, rows, cols, dys, xs, gammas, stats, dxs, dx_acc, dgammas, dbetas, workspace,
+                             workspace_bytes):
+    import ctypes as C
+    n = len(xs)
+    c = (C.c_int64 * n)(*[int(v) for v in cols])
+    dy, x, g, dx, dg, db = _arrs(n, dys, xs, gammas, dxs, dgammas, dbetas)
+    return check(lib.tile_layernorm_bwd_multi(stream_handle(stream), n, rows, c, dy, x, g, ptr(stats), dx, dx_acc,
+                                              dg, db, ptr(workspace), workspace_bytes))
+
+
+def tile_layernorm_bwd_multi_workspace(rows, total_cols):
+    return lib.tile_layernorm_bwd_multi_workspace(rows, total_cols)

@@ -78,6 +78,29 @@ class Context:
     def submit_fill(self, t, idx, value: float):
         check(lib.tt_submit_fill(self.h, t.h, L.i64_array(idx), value))
 
+    def submit(self, op: int, tiles, scalars=None):
+        """Generic task submission (tt_submit): `tiles` is a sequence of
+        (Tensor, tile index tuple) in the op's order, `scalars` the op's
+        ctypes scalar struct (L.tt_op_*) or None."""
+        tl = list(tiles)
+        arr = (L.tt_tile * max(1, len(tl)))()
+        for i, (t, idx) in enumerate(tl):
+            arr[i].tensor = t.h
+            for j, v in enumerate(idx):
+                arr[i].tile[j] = int(v)
+        sp = C.cast(C.byref(scalars), C.c_void_p) if scalars is not None else None
+        check(lib.tt_submit(self.h, op, arr, len(tl), sp, C.sizeof(scalars) if scalars is not None else 0))
+
+    def wait_stream(self, stream):
+        """Tasks launched from now on run after the work queued on `stream`
+        (a torch stream or a raw hipStream_t) so far (device-side)."""
+        check(lib.tt_ctx_wait_stream(self.h, L.stream_handle(stream)))
+
+    def join_stream(self, stream):
+        """Work queued on `stream` from now on runs after every task the
+        context has launched (device-side)."""
+        check(lib.tt_ctx_join_stream(self.h, L.stream_handle(stream)))
+
     def wait(self):
         check(lib.tt_wait(self.h))
 
@@ -132,6 +155,11 @@ class Tensor:
         n = C.c_int64()
         check(lib.tt_tensor_grid(self.h, g, C.byref(n)))
         return tuple(g[i] for i in range(len(self.shape))), n.value
+
+    def set_matrix_split(self, k: int):
+        """Rows of a tile's matrix view = product of the first k extents."""
+        check(lib.tt_tensor_set_matrix_split(self.h, k))
+        return self
 
     def nbytes(self) -> int:
         return lib.tt_tensor_bytes(self.h)
@@ -202,17 +230,22 @@ class GPT2:
         start_lr at the first update, lr from update full_lr_iter on;
         optimizer "adamw" or "sgd" (plain p -= lr*g)."""
         opt = {"adamw": L.TT_OPT_ADAMW, "sgd": L.TT_OPT_SGD}[optimizer]
+        cur = None
         if hasattr(tokens_dev, "device") and getattr(tokens_dev.device, "type", "") == "cuda":
             # the executor's streams do not order after torch's: they wait (on
             # the device, the host does not block) for the work torch has
             # queued so far, which includes whatever wrote the token buffer
             import torch
             cur = torch.cuda.current_stream(tokens_dev.device)
-            for i in range(self.ctx.n_streams):
-                torch.cuda.ExternalStream(self.ctx.stream(i), device=tokens_dev.device).wait_stream(cur)
+            self.ctx.wait_stream(cur)
         hp = L.tt_adamw_hparams(lr, beta1, beta2, eps, weight_decay, lr if start_lr is None else start_lr,
                                 full_lr_iter, opt)
         check(lib.tt_gpt2_step_accum(self.h, L.ptr(tokens_dev), n_micro, C.byref(hp), int(update)))
+        if cur is not None:
+            # the step's copy of the token buffer is queued on an executor
+            # stream when the call returns; torch's later work (which may
+            # reuse the buffer's memory once the caller drops it) runs after it
+            self.ctx.join_stream(cur)
 
     def loss(self) -> float:
         f = C.c_float()
