@@ -243,6 +243,24 @@ int tile_layernorm_bwd_multi(void* stream, int count, int64_t rows, const int64_
                              size_t workspace_bytes);
 size_t tile_layernorm_bwd_multi_workspace(int64_t rows, int64_t total_cols);
 
+/* tile_layernorm_bwd_noalloc -- for callers that cannot allocate (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): tile_layernorm_bwd with the same arguments and results except
+ * the workspace, whose column partials live in a device array of the
+ * library instead (16 MiB per device, held until the process ends;
+ * tile_layernorm_bwd_noalloc_max_bytes() returns the size). The array's
+ * device address is looked up on the first call on each device, so make
+ * that call outside a graph capture. Calls no allocating routine. Every
+ * call on one device uses the same array: calls that overlap on a device
+ * (on two streams at once) race, calls in stream order do not. TT_ERR_ARG
+ * when tile_layernorm_bwd_workspace(rows, cols) exceeds the array, before
+ * anything is launched; otherwise as tile_layernorm_bwd. */
+int tile_layernorm_bwd_noalloc(void* stream, int phase, int64_t rows, int64_t cols, int64_t n_total,
+                               const float* dy, int64_t lddy, const float* x, int64_t ldx, const float* gamma,
+                               const float* stats, float* parts, int64_t n_parts, int64_t part_stride, float* dx,
+                               int64_t lddx, int dx_acc, float* dgamma, float* dbeta);
+size_t tile_layernorm_bwd_noalloc_max_bytes(void);
+
 /* tile_softmax -- row softmax of a tile whose columns are one tile of a
  * longer row (layer list: pith.science review, "What carries the argument").
  * Element (r, c) of the tile is logit x = scale * X[r*ldx + c] at global

@@ -152,6 +152,8 @@ SIGNATURES = {
     "tile_layernorm_fwd": (I, [P, I, I64, I64, P, I64, P, P, P, I64, I64, P, P, I64, F]),
     "tile_layernorm_bwd": (I, [P, I, I64, I64, I64, P, I64, P, I64, P, P, P, I64, I64, P, I64, I, P, P, P]),
     "tile_layernorm_bwd_workspace": (SZ, [I64, I64]),
+    "tile_layernorm_bwd_noalloc": (I, [P, I, I64, I64, I64, P, I64, P, I64, P, P, P, I64, I64, P, I64, I, P, P]),
+    "tile_layernorm_bwd_noalloc_max_bytes": (SZ, []),
     "tile_layernorm_fwd_multi": (I, [P, I, I64, P, P, P, P, P, P, F]),
     "tile_layernorm_bwd_multi": (I, [P, I, I64, P, P, P, P, P, P, I, P, P, P, SZ]),
     "tile_layernorm_bwd_multi_workspace": (SZ, [I64, I64]),

@@ -10,6 +10,8 @@
 // with the parallel-variance update of Chan, Golub and LeVeque.
 #include "rowops.hpp"
 
+#include <mutex>
+
 using tt::f32x4;
 
 namespace {
@@ -718,6 +720,65 @@ extern "C" int tile_layernorm_bwd_multi(void* stream, int count, int64_t rows, c
   hipLaunchKernelGGL(ln_colsum_finish_multi, dim3((unsigned)((P.c0 + 63) / 64), (unsigned)(2 * count)), dim3(1024), 0,
                      s, nblk, P, ws);
   return tt::launch_status("tile_layernorm_bwd_multi(colsum)");
+}
+
+// ------------------------------------ LayerNorm backward without allocation
+//
+// tile_layernorm_bwd_noalloc: tile_layernorm_bwd with its column-sum
+// partials in a file-scope device array instead of a caller workspace, for
+// callers that may not allocate (graph capture, serving loops). Each device
+// holds its own copy of the array; its address is looked up once per
+// device with hipGetSymbolAddress and kept -- the array's name in host code
+// is not a device address. Every call on one device shares the array, so
+// calls that overlap on a device (two streams at once) race; the partials
+// are written in full by each call before they are read, so nothing needs
+// clearing between calls.
+
+namespace {
+
+constexpr size_t kLnScratchBytes = size_t(16) << 20;  // 16 MiB per device
+__device__ __align__(256) unsigned char scratch[kLnScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_for_current_device(void** out) {
+  int dev = 0;
+  TT_HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return tt::fail(TT_ERR_ARG, "layernorm scratch: device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return tt::fail(TT_ERR_HIP, "layernorm scratch: hipGetSymbolAddress failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return TT_OK;
+}
+
+}  // namespace
+
+extern "C" size_t tile_layernorm_bwd_noalloc_max_bytes(void) { return kLnScratchBytes; }
+
+extern "C" int tile_layernorm_bwd_noalloc(void* stream, int phase, int64_t rows, int64_t cols, int64_t n_total,
+                                          const float* dy, int64_t lddy, const float* x, int64_t ldx,
+                                          const float* gamma, const float* stats, float* parts, int64_t n_parts,
+                                          int64_t part_stride, float* dx, int64_t lddx, int dx_acc, float* dgamma,
+                                          float* dbeta) {
+  if (rows < 0 || cols < 0) return tt::fail(TT_ERR_ARG, "tile_layernorm_bwd_noalloc: negative size");
+  if (phase != TT_LN_PARTIAL && rows > 0 && cols > 0 &&
+      tile_layernorm_bwd_workspace(rows, cols) > kLnScratchBytes)
+    return tt::fail(TT_ERR_ARG,
+                    "tile_layernorm_bwd_noalloc: %lld rows x %lld columns need %zu bytes of column partials, above "
+                    "the %zu-byte scratch array",
+                    (long long)rows, (long long)cols, tile_layernorm_bwd_workspace(rows, cols), kLnScratchBytes);
+  void* ws = nullptr;
+  if (int rc = scratch_for_current_device(&ws)) return rc;
+  return tile_layernorm_bwd(stream, phase, rows, cols, n_total, dy, lddy, x, ldx, gamma, stats, parts, n_parts,
+                            part_stride, dx, lddx, dx_acc, dgamma, dbeta, ws);
 }
 
 // ------------------------------------------------------------ reduce_rows
