@@ -491,14 +491,23 @@ __global__ __launch_bounds__(BT) void ln_fwd_multi(int rows, int rows_per_block,
   }
   const float inv_n = 1.f / (float)P.total;
   const int r0 = blockIdx.x * rows_per_block, r1 = min(rows, r0 + rows_per_block);
+  // the next row's loads are issued before this row's reductions (the
+  // barriers wait for LDS only), so they overlap the compute and stores
+  f32x4 v[VPT];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k)
+    v[k] = ok[k] && r0 < r1 ? *reinterpret_cast<const f32x4*>(xp[k] + (int64_t)r0 * ld[k])
+                            : f32x4{0.f, 0.f, 0.f, 0.f};
   for (int r = r0; r < r1; ++r) {
-    f32x4 v[VPT];
+    f32x4 nx[VPT];
+    const bool more = r + 1 < r1;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k)
+      nx[k] = ok[k] && more ? *reinterpret_cast<const f32x4*>(xp[k] + (int64_t)(r + 1) * ld[k])
+                            : f32x4{0.f, 0.f, 0.f, 0.f};
     float s = 0.f, unused = 0.f;
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      v[k] = ok[k] ? *reinterpret_cast<const f32x4*>(xp[k] + (int64_t)r * ld[k]) : f32x4{0.f, 0.f, 0.f, 0.f};
-      s += (v[k][0] + v[k][1]) + (v[k][2] + v[k][3]);
-    }
+    for (int k = 0; k < VPT; ++k) s += (v[k][0] + v[k][1]) + (v[k][2] + v[k][3]);
     block_sum2<BT>(s, unused, red);
     const float mean = s * inv_n;
     float m2 = 0.f;
@@ -526,6 +535,8 @@ __global__ __launch_bounds__(BT) void ln_fwd_multi(int rows, int rows_per_block,
         for (int i = 0; i < 4; ++i) o[i] = (v[k][i] - mean) * rstd * g[k][i] + b[k][i];
         *reinterpret_cast<f32x4*>(yp[k] + (int64_t)r * ld[k]) = o;
       }
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) v[k] = nx[k];
   }
 }
 
