@@ -130,6 +130,20 @@ size_t tile_gemm_workspace(int64_t m, int64_t n, int64_t k);
 int tile_gemm_ksum(void* stream, int count, int transB, int64_t m, int64_t n, const int64_t* k, float alpha,
                    const float* const* A, const int64_t* lda, const float* const* B, const int64_t* ldb,
                    float beta, float* C, int64_t ldc);
+/* tile_gemm_ksum_ex -- the same sum followed by tile_gemm's epilogue on the
+ * whole of it (TT_EPI_BIAS, TT_EPI_RES, TT_EPI_GELU with its pre-activation
+ * in aux, TT_EPI_GELU_BWD; the arguments as in tile_gemm): a linear layer
+ * whose input features are split over several tiles, e.g. the MLP's first
+ * layer g = gelu(sum over embd tiles of n2_e W_e + b) as one long-K launch
+ * instead of a chain of accumulating GEMMs (layer list: pith.science
+ * review, "What carries the argument"). With an epilogue every pair must go
+ * through the one long-K launch (as described above, at most 96 pairs with
+ * equal leading dimensions): TT_ERR_UNSUPPORTED otherwise, before anything
+ * is launched. epilogue = 0 is tile_gemm_ksum. */
+int tile_gemm_ksum_ex(void* stream, int count, int transB, int64_t m, int64_t n, const int64_t* k, float alpha,
+                      const float* const* A, const int64_t* lda, const float* const* B, const int64_t* ldb,
+                      float beta, float* C, int64_t ldc, int epilogue, const float* bias, const float* res,
+                      int64_t ldr, float* aux, int64_t ldaux);
 /* tile_gemm_batch -- independent products in one launch:
  *   C_t = alpha * op(A_t) op(B_t) + beta * C_t,   t < count
  * op() as in tile_gemm; the products share transA, transB, k, alpha and
@@ -626,10 +640,15 @@ typedef struct { float value; } tt_op_fill;
  * B_0, C_0, A_1, B_1, C_1, ... (one or more products; more than 72 make
  * several launches); epilogue must be 0. C_t written (beta == 0) or
  * updated.
- * TT_OP_GEMM_KSUM -- a sum of products into one tile (tile_gemm_ksum: a
- * linear layer's input gradient summed over the tiles of its output axis):
- * tiles C, A_0, B_0, A_1, B_1, ... (one or more pairs; more than 96 make
- * several launches); C = alpha sum_t A_t op(B_t) + beta C with transA = 0. */
+ * TT_OP_GEMM_KSUM -- a sum of products into one tile (tile_gemm_ksum_ex: a
+ * linear layer whose contraction axis is split over several tiles, forward
+ * or backward): tiles C, then bias / res / aux as the epilogue requires (as
+ * for TT_OP_GEMM), then A_0, B_0, A_1, B_1, ... (one or more pairs; more
+ * than 96 make several launches); C = epilogue(alpha sum_t A_t op(B_t) +
+ * beta C) with transA = 0. Accesses as TT_OP_GEMM. Where one long-K launch
+ * cannot take every pair (shapes not multiples of its blocks, misaligned
+ * tiles, more than 96 pairs), the task runs a chain of products instead:
+ * the same result up to the order of the additions. */
 #define TT_OP_GEMM       2
 #define TT_OP_GEMM_BATCH 3
 #define TT_OP_GEMM_KSUM  4

@@ -103,6 +103,52 @@ def test_gemm_ksum(m, n, ks, beta, tb):
     assert torch.equal(outs[0], outs[1])
 
 
+@pytest.mark.parametrize("m,n,k,count,tb,epi", [
+    (4096, 2048, 512, 4, 0, "bias_res"),      # 512 blocks of 128x128 (BK 16): the attention projection's shape
+    (1024, 1024, 256, 3, 0, "gelu"),          # 64 blocks of 64x64: the MLP input layer with its activation
+    (4096, 4096, 256, 2, 1, "gelu_bwd"),      # 1024 blocks (BK 32), B stored [n][k]: the MLP output's input gradient
+])
+def test_gemm_ksum_epilogues(m, n, k, count, tb, epi):
+    """K-sum with tile_gemm's epilogues on the whole sum: bias + residual,
+    GELU (pre-activation kept in aux) and GELU' against the fp64 sum."""
+    seed = m + n + count
+    As = [synth.rand_normal((m, k), seed + i, std=0.2) for i in range(count)]
+    Bs = [synth.rand_normal((n, k) if tb else (k, n), seed + 50 + i, std=0.2) for i in range(count)]
+    bias, res = synth.rand_normal((n,), seed + 100), synth.rand_normal((m, n), seed + 101)
+    aux0 = synth.rand_normal((m, n), seed + 102)
+    ref = np.zeros((m, n))
+    bound = np.zeros((m, n))
+    for a, b in zip(As, Bs):
+        b = (b.T if tb else b).astype(np.float64)
+        ref += a.astype(np.float64) @ b
+        bound += np.abs(a).astype(np.float64) @ np.abs(b)
+    bound *= (count * k + count + 4) * EPS32
+    C, aux = empty((m, n)), dev(aux0)
+    flag = {"bias_res": tt.TT_EPI_BIAS | tt.TT_EPI_RES, "gelu": tt.TT_EPI_GELU | tt.TT_EPI_BIAS,
+            "gelu_bwd": tt.TT_EPI_GELU_BWD}[epi]
+    tt.tile_gemm_ksum_ex(None, m, n, [k] * count, 1.0, [dev(a) for a in As], [k] * count, [dev(b) for b in Bs],
+                         [b.shape[1] for b in Bs], 0.0, C, n, transB=tb, epilogue=flag, bias=dev(bias), res=dev(res),
+                         ldr=n, aux=aux, ldaux=n)
+    if epi == "bias_res":
+        want = ref + bias + res
+        assert_close_bound(host(C), want, bound + 4 * EPS32 * np.abs(want) + 1e-6, "ksum bias+res")
+    elif epi == "gelu":
+        pre = ref + bias
+        assert_close_bound(host(aux), pre, bound + 4 * EPS32 * np.abs(pre) + 1e-6, "ksum gelu pre-activation")
+        assert_close_bound(host(C), og.gelu(pre), 1.2 * bound + 4e-6, "ksum gelu")
+    else:
+        want = ref * og.gelu_grad(aux0.astype(np.float64))
+        assert_close_bound(host(C), want, 1.2 * bound + 4e-6 * np.abs(ref) + 1e-6, "ksum gelu'")
+
+
+def test_gemm_ksum_epilogue_needs_one_launch():
+    a = empty((96, 64))
+    with pytest.raises(tt.TTError) as e:   # 96 rows: edge blocks, the long-K launch cannot take the pair
+        tt.tile_gemm_ksum_ex(None, 96, 64, [64, 64], 1.0, [a, a], [64, 64], [a, a], [64, 64], 0.0, a, 64,
+                             epilogue=tt.TT_EPI_BIAS, bias=a)
+    assert e.value.code == tt._lib.TT_ERR_UNSUPPORTED
+
+
 def test_gemm_ksum_empty_and_errors():
     c0 = synth.rand_normal((64, 64), 5)
     C = dev(c0)

@@ -145,6 +145,7 @@ SIGNATURES = {
     "tile_gemm_ws": (I, [P, I, I, I64, I64, I64, F, P, I64, P, I64, F, P, I64, I, P, P, I64, P, I64, P, SZ]),
     "tile_gemm_workspace": (SZ, [I64, I64, I64]),
     "tile_gemm_ksum": (I, [P, I, I, I64, I64, P, F, P, P, P, P, F, P, I64]),
+    "tile_gemm_ksum_ex": (I, [P, I, I, I64, I64, P, F, P, P, P, P, F, P, I64, I, P, P, I64, P, I64]),
     "tile_gemm_batch": (I, [P, I, I, I, P, P, I64, F, P, P, P, P, F, P, P]),
     "tile_gemm_batch_ws": (I, [P, I, I, I, P, P, I64, F, P, P, P, P, F, P, P, P, SZ]),
     "tile_gemm_batch_workspace": (SZ, [I, P, P, I64]),

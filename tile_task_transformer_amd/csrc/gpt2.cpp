@@ -194,6 +194,69 @@ int submit_ksum_tb(tt_ctx* ctx, const char* label, TileRef C, const std::vector<
   return submit_op(ctx, TT_OP_GEMM_KSUM, T.data(), (int)T.size(), &sc, sizeof(sc), label, false);
 }
 
+// C = epilogue(sum_t A_t op(B_t)) over the tiles of a linear layer's
+// contraction axis as one task: one long-K launch (tile_gemm_ksum_ex) reads
+// and writes C once and runs one prologue and epilogue per output block,
+// against one per contraction tile for a chain of accumulating GEMMs
+// (wide model, MLP input layer 4096 x 8192 x 4 x 2048: 75.5 -> 82.0 % of the
+// fp32 peak, measured). A single pair is an ordinary GEMM task.
+int submit_ksum(tt_ctx* ctx, const char* label, int tb, TileRef C, const std::vector<TileRef>& As,
+                const std::vector<TileRef>& Bs, int epi = TT_EPI_NONE, TileRef bias = {}, TileRef res = {},
+                TileRef aux = {}) {
+  if (As.size() == 1) {
+    Gemm q;
+    q.tb = tb;
+    q.A = As[0];
+    q.B = Bs[0];
+    q.C = C;
+    q.epi = epi;
+    q.bias = bias;
+    q.res = res;
+    q.aux = aux;
+    return submit_gemm(ctx, label, q);
+  }
+  std::vector<TileArg> T = {ta(C)};
+  if (epi & TT_EPI_BIAS) T.push_back(ta(bias));
+  if (epi & TT_EPI_RES) T.push_back(ta(res));
+  if (epi & (TT_EPI_GELU | TT_EPI_GELU_BWD)) T.push_back(ta(aux));
+  for (size_t u = 0; u < As.size(); ++u) {
+    T.push_back(ta(As[u]));
+    T.push_back(ta(Bs[u]));
+  }
+  const tt_op_gemm sc{0, tb, epi, 1.f, 0.f, 1};
+  return submit_op(ctx, TT_OP_GEMM_KSUM, T.data(), (int)T.size(), &sc, sizeof(sc), label, false);
+}
+
+// whether a linear layer's contraction over several tiles runs as one K-sum
+// task (else a chain of accumulating GEMM tasks), by the output tile's
+// block counts (measured per task class, one stream, each task alone):
+//  * >= 1024 blocks of 128x128: the long-K launch wins (wide model, MLP input
+//    layer 4096 x 8192: 74.1 -> 67.6 ms per step; its input gradient 72.7 ->
+//    70.8 ms);
+//  * 512..1023: it loses (MLP output layer 65.5 -> 70.5 ms, fc input gradient
+//    65.1 -> 73.9, attention projection 18.3 -> 18.5): every link of the
+//    chain already runs a long K loop;
+//  * fewer: the long-K launch takes it when its 64x64 blocks fill the CUs
+//    (the small-tile model's MLP input layer, 1024 x 2048: 66 % of the
+//    fp32 peak); narrower outputs (1024 x 512: 128 blocks, 31 % as one long-K
+//    launch) stay chains, whose links split K over the CUs.
+// TT_KSUM_CLASSES="qkv,fc,..." forces the given task classes to K-sum tasks
+// and every other class to chains (tuning).
+bool use_ksum(const char* label, const TileRef& C) {
+  static std::string set;
+  static int mode = -1;
+  if (mode < 0) {
+    const char* e = getenv("TT_KSUM_CLASSES");
+    mode = e ? 1 : 0;
+    if (e) set = std::string(",") + e + ",";
+  }
+  if (mode == 1) return set.find(std::string(",") + label + ",") != std::string::npos;
+  int64_t r, c;
+  C.t->mat(C.lin, &r, &c);
+  const int64_t nb = (r / 128) * (c / 128), nb64 = (r / 64) * (c / 64);
+  return nb >= 1024 || (nb < 512 && nb64 >= 256);
+}
+
 // tiles = value, TT_FILL_MAX_TILES tiles per task and launch (with
 // pinned-host homes a task's tiles take at most an eighth of the arena)
 int fill_tasks(tt_gpt2* g, const std::vector<TileRef>& tiles, float v) {
@@ -667,19 +730,30 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
         const int64_t ti = bi + g->nb * si;
         TRY(ln_forward(g, b.h_in, ln1g, ln1b, b.ln1, b.n1, bi, si));
         for (int cq = 0; cq < 3; ++cq)
-          for (int64_t hj = 0; hj < NH; ++hj)
+          for (int64_t hj = 0; hj < NH; ++hj) {
+            const TileRef C = {qkv[cq], L(qkv[cq], {bi, si, hj, 0})}, bias = {bqkv, L(bqkv, {cq, hj, 0})};
+            if (use_ksum("qkv", C)) {
+              std::vector<TileRef> As, Bs;
+              for (int64_t ek = 0; ek < NE; ++ek) {
+                As.push_back({b.n1, L(b.n1, {bi, si, ek})});
+                Bs.push_back({wqkv, L(wqkv, {ek, cq, hj, 0})});
+              }
+              TRY(submit_ksum(ctx, "qkv", 0, C, As, Bs, TT_EPI_BIAS, bias));
+              continue;
+            }
             for (int64_t ek = 0; ek < NE; ++ek) {
               Gemm q;
               q.A = {b.n1, L(b.n1, {bi, si, ek})};
               q.B = {wqkv, L(wqkv, {ek, cq, hj, 0})};
-              q.C = {qkv[cq], L(qkv[cq], {bi, si, hj, 0})};
+              q.C = C;
               q.beta = ek > 0 ? 1.f : 0.f;
               if (ek == NE - 1) {
                 q.epi = TT_EPI_BIAS;
-                q.bias = {bqkv, L(bqkv, {cq, hj, 0})};
+                q.bias = bias;
               }
               TRY(submit_gemm(ctx, "qkv", q));
             }
+          }
       }
     // attention: (query tile, key tile) pairs, key tiles in order
     for (int64_t bi = 0; bi < g->nb; ++bi)
@@ -696,7 +770,17 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
       for (int64_t si = 0; si < g->ns; ++si) {
         const int64_t ti = bi + g->nb * si;
         // h_mid = h_in + O W_o + b_o
-        for (int64_t ej = 0; ej < NE; ++ej)
+        for (int64_t ej = 0; ej < NE; ++ej) {
+          if (use_ksum("attn_proj", {b.h_mid, L(b.h_mid, {bi, si, ej})})) {
+            std::vector<TileRef> As, Bs;
+            for (int64_t hk = 0; hk < NH; ++hk) {
+              As.push_back({b.o, L(b.o, {bi, si, hk, 0})});
+              Bs.push_back({wo, L(wo, {hk, 0, ej})});
+            }
+            TRY(submit_ksum(ctx, "attn_proj", 0, {b.h_mid, L(b.h_mid, {bi, si, ej})}, As, Bs,
+                            TT_EPI_RES | TT_EPI_BIAS, {bo, ej}, {b.h_in, L(b.h_in, {bi, si, ej})}));
+            continue;
+          }
           for (int64_t hk = 0; hk < NH; ++hk) {
             Gemm q;
             q.A = {b.o, L(b.o, {bi, si, hk, 0})};
@@ -713,9 +797,20 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
             }
             TRY(submit_gemm(ctx, "attn_proj", q));
           }
+        }
         TRY(ln_forward(g, b.h_mid, ln2g, ln2b, b.ln2, b.n2, bi, si));
         // g = gelu(n2 W_fc + b_fc), pre-activation kept in u
-        for (int64_t ij = 0; ij < NI; ++ij)
+        for (int64_t ij = 0; ij < NI; ++ij) {
+          if (use_ksum("fc", {b.g, L(b.g, {bi, si, ij})})) {
+            std::vector<TileRef> As, Bs;
+            for (int64_t ek = 0; ek < NE; ++ek) {
+              As.push_back({b.n2, L(b.n2, {bi, si, ek})});
+              Bs.push_back({wfc, L(wfc, {ek, ij})});
+            }
+            TRY(submit_ksum(ctx, "fc", 0, {b.g, L(b.g, {bi, si, ij})}, As, Bs, TT_EPI_GELU | TT_EPI_BIAS, {bfc, ij},
+                            {}, {b.u, L(b.u, {bi, si, ij})}));
+            continue;
+          }
           for (int64_t ek = 0; ek < NE; ++ek) {
             Gemm q;
             q.A = {b.n2, L(b.n2, {bi, si, ek})};
@@ -731,8 +826,19 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
             }
             TRY(submit_gemm(ctx, "fc", q));
           }
+        }
         // h_out = h_mid + g W_p + b_p
-        for (int64_t ej = 0; ej < NE; ++ej)
+        for (int64_t ej = 0; ej < NE; ++ej) {
+          if (use_ksum("mlp_proj", {hout, L(hout, {bi, si, ej})})) {
+            std::vector<TileRef> As, Bs;
+            for (int64_t ik = 0; ik < NI; ++ik) {
+              As.push_back({b.g, L(b.g, {bi, si, ik})});
+              Bs.push_back({wp, L(wp, {ik, ej})});
+            }
+            TRY(submit_ksum(ctx, "mlp_proj", 0, {hout, L(hout, {bi, si, ej})}, As, Bs, TT_EPI_RES | TT_EPI_BIAS,
+                            {bp, ej}, {b.h_mid, L(b.h_mid, {bi, si, ej})}));
+            continue;
+          }
           for (int64_t ik = 0; ik < NI; ++ik) {
             Gemm q;
             q.A = {b.g, L(b.g, {bi, si, ik})};
@@ -749,6 +855,7 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
             }
             TRY(submit_gemm(ctx, "mlp_proj", q));
           }
+        }
       }
   }
 
@@ -965,7 +1072,17 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
           TRY(submit_gemm_batch(ctx, "mlp_proj_dw", qs, true));
         }
         TRY(colsum_row(g->dh, gbp, NE, bi, si, ti > 0 || later_mb));
-        for (int64_t ik = 0; ik < NI; ++ik)
+        for (int64_t ik = 0; ik < NI; ++ik) {
+          if (use_ksum("mlp_proj_dx", {g->dgu, L(g->dgu, {bi, si, ik})})) {
+            std::vector<TileRef> As, Bs;
+            for (int64_t ej = 0; ej < NE; ++ej) {
+              As.push_back({g->dh, L(g->dh, {bi, si, ej})});
+              Bs.push_back({wp, L(wp, {ik, ej})});
+            }
+            TRY(submit_ksum(ctx, "mlp_proj_dx", 1, {g->dgu, L(g->dgu, {bi, si, ik})}, As, Bs, TT_EPI_GELU_BWD, {}, {},
+                            {b.u, L(b.u, {bi, si, ik})}));
+            continue;
+          }
           for (int64_t ej = 0; ej < NE; ++ej) {
             Gemm q;
             q.tb = 1;
@@ -979,6 +1096,7 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
             }
             TRY(submit_gemm(ctx, "mlp_proj_dx", q));
           }
+        }
         {
           std::vector<Gemm> qs;
           for (int64_t ik = 0; ik < NI; ++ik)
@@ -996,7 +1114,16 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
         TRY(colsum_row(g->dgu, gbfc, NI, bi, si, ti > 0 || later_mb));
         // (a chain of accumulating GEMMs: as one long-K task per embd tile it
         // measured slower on the wide model, 65 -> 71 ms per step)
-        for (int64_t ek = 0; ek < NE; ++ek)
+        for (int64_t ek = 0; ek < NE; ++ek) {
+          if (use_ksum("fc_dx", {g->dn, L(g->dn, {bi, si, ek})})) {
+            std::vector<TileRef> As, Bs;
+            for (int64_t ik = 0; ik < NI; ++ik) {
+              As.push_back({g->dgu, L(g->dgu, {bi, si, ik})});
+              Bs.push_back({wfc, L(wfc, {ek, ik})});
+            }
+            TRY(submit_ksum(ctx, "fc_dx", 1, {g->dn, L(g->dn, {bi, si, ek})}, As, Bs));
+            continue;
+          }
           for (int64_t ik = 0; ik < NI; ++ik) {
             Gemm q;
             q.tb = 1;
@@ -1006,6 +1133,7 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
             q.beta = ik > 0 ? 1.f : 0.f;
             TRY(submit_gemm(ctx, "fc_dx", q));
           }
+        }
         TRY(ln_backward(g, g->dn, b.h_mid, ln2g, b.ln2, g->dh, 1, g->G[g->pidx(l, LN2G)], g->G[g->pidx(l, LN2B)], bi,
                         si));
         // attention projection: h_mid = h_in + O W_o + b_o
@@ -1024,7 +1152,16 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
           TRY(submit_gemm_batch(ctx, "attn_proj_dw", qs, true));
         }
         TRY(colsum_row(g->dh, gbo, NE, bi, si, ti > 0 || later_mb));
-        for (int64_t hk = 0; hk < NH; ++hk)
+        for (int64_t hk = 0; hk < NH; ++hk) {
+          if (use_ksum("attn_proj_dx", {g->dO, L(g->dO, {bi, si, hk, 0})})) {
+            std::vector<TileRef> As, Bs;
+            for (int64_t ej = 0; ej < NE; ++ej) {
+              As.push_back({g->dh, L(g->dh, {bi, si, ej})});
+              Bs.push_back({wo, L(wo, {hk, 0, ej})});
+            }
+            TRY(submit_ksum(ctx, "attn_proj_dx", 1, {g->dO, L(g->dO, {bi, si, hk, 0})}, As, Bs));
+            continue;
+          }
           for (int64_t ej = 0; ej < NE; ++ej) {
             Gemm q;
             q.tb = 1;
@@ -1034,6 +1171,7 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
             q.beta = ej > 0 ? 1.f : 0.f;
             TRY(submit_gemm(ctx, "attn_proj_dx", q));
           }
+        }
       }
     // attention backward
     for (int64_t bi = 0; bi < g->nb; ++bi)

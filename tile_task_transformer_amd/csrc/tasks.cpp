@@ -168,19 +168,50 @@ int op_gemm_batch(tt_ctx* ctx, const TileArg* T, int n, const tt_op_gemm& q, con
 
 int op_gemm_ksum(tt_ctx* ctx, const TileArg* T, int n, const tt_op_gemm& q, const char* label) {
   const char* nm = "TT_OP_GEMM_KSUM";
-  if (n < 3 || (n - 1) % 2) return fail(TT_ERR_ARG, "%s: needs C and (A, B) pairs", nm);
-  if (q.transA || q.epilogue != TT_EPI_NONE) return fail(TT_ERR_ARG, "%s: transA and the epilogue must be 0", nm);
+  const int epi = q.epilogue;
+  if (q.transA) return fail(TT_ERR_ARG, "%s: transA must be 0", nm);
+  if (epi & ~(TT_EPI_BIAS | TT_EPI_RES | TT_EPI_GELU | TT_EPI_GELU_BWD))
+    return fail(TT_ERR_ARG, "%s: unknown epilogue bits", nm);
+  if ((epi & TT_EPI_GELU) && (epi & TT_EPI_GELU_BWD)) return fail(TT_ERR_ARG, "%s: GELU and GELU_BWD", nm);
+  const bool has_bias = epi & TT_EPI_BIAS, has_res = epi & TT_EPI_RES;
+  const bool has_aux = epi & (TT_EPI_GELU | TT_EPI_GELU_BWD), gelu = epi & TT_EPI_GELU;
+  const int ne = 1 + has_bias + has_res + has_aux;
+  if (n < ne + 2 || (n - ne) % 2) return fail(TT_ERR_ARG, "%s: needs C, the epilogue's tiles and (A, B) pairs", nm);
   if (int rc = need_f32(T, n, nm)) return rc;
-  const int cnt = (n - 1) / 2;
+  const int cnt = (n - ne) / 2;
   int64_t dr, dc;
   matv(T[0], &dr, &dc);
+  int at = 1;
+  TileArg bias, res, aux;
+  int64_t ldr = 0, ldaux = 0;
+  if (has_bias) {
+    bias = T[at++];
+    if (elems(bias) != dc) return fail(TT_ERR_SHAPE, "%s: bias has %lld elements, C has %lld columns", nm,
+                                       (long long)elems(bias), (long long)dc);
+  }
+  if (has_res) {
+    res = T[at++];
+    int64_t r, c;
+    matv(res, &r, &c);
+    if (r != dr || c != dc) return fail(TT_ERR_SHAPE, "%s: residual tile is not %lldx%lld", nm, (long long)dr,
+                                        (long long)dc);
+    ldr = c;
+  }
+  if (has_aux) {
+    aux = T[at++];
+    int64_t r, c;
+    matv(aux, &r, &c);
+    if (r != dr || c != dc) return fail(TT_ERR_SHAPE, "%s: aux tile is not %lldx%lld", nm, (long long)dr,
+                                        (long long)dc);
+    ldaux = c;
+  }
   std::vector<int64_t> ks(cnt), lda(cnt), ldb(cnt);
   std::vector<Access> acc;
   double flops = 0;
   for (int u = 0; u < cnt; ++u) {
     int64_t ar, ac, br, bc;
-    matv(T[1 + 2 * u], &ar, &ac);
-    matv(T[2 + 2 * u], &br, &bc);
+    matv(T[ne + 2 * u], &ar, &ac);
+    matv(T[ne + 1 + 2 * u], &br, &bc);
     const int64_t kb = q.transB ? bc : br, nb = q.transB ? br : bc;
     if (ar != dr || kb != ac || nb != dc)
       return fail(TT_ERR_SHAPE, "%s: pair %d (%lldx%lld, %lldx%lld) does not match C %lldx%lld", nm, u, (long long)ar,
@@ -188,21 +219,46 @@ int op_gemm_ksum(tt_ctx* ctx, const TileArg* T, int n, const tt_op_gemm& q, cons
     ks[u] = ac;
     lda[u] = ac;
     ldb[u] = bc;
-    acc.push_back(acc_of(T[1 + 2 * u], TT_R));
-    acc.push_back(acc_of(T[2 + 2 * u], TT_R));
+    acc.push_back(acc_of(T[ne + 2 * u], TT_R));
+    acc.push_back(acc_of(T[ne + 1 + 2 * u], TT_R));
     flops += 2.0 * dr * dc * ac;
   }
-  acc.push_back(acc_of(T[0], q.beta == 0.f ? TT_W : TT_RW));
+  acc.push_back(acc_of(T[0], (q.beta == 0.f || gelu) ? TT_W : TT_RW));
+  if (has_bias) acc.push_back(acc_of(bias, TT_R));
+  if (has_res) acc.push_back(acc_of(res, TT_R));
+  if (has_aux) acc.push_back(acc_of(aux, gelu ? (q.beta == 0.f ? TT_W : TT_RW) : TT_R));
   std::vector<TileArg> tl(T, T + n);
   const tt_op_gemm p = q;
-  return ctx->submit(label ? label : "gemm_ksum", std::move(acc), [=](hipStream_t s, void*) {
+  return ctx->submit(label ? label : "gemm_ksum", std::move(acc), [=](hipStream_t s, void* ws) {
     std::vector<const float*> A(cnt), B(cnt);
     for (int u = 0; u < cnt; ++u) {
-      A[u] = Fp(tl[1 + 2 * u]);
-      B[u] = Fp(tl[2 + 2 * u]);
+      A[u] = Fp(tl[ne + 2 * u]);
+      B[u] = Fp(tl[ne + 1 + 2 * u]);
     }
-    return tile_gemm_ksum(s, cnt, p.transB, dr, dc, ks.data(), p.alpha, A.data(), lda.data(), B.data(), ldb.data(),
-                          p.beta, Fp(tl[0]), dc);
+    float* bp = has_bias ? Fp(bias) : nullptr;
+    float* rp = has_res ? Fp(res) : nullptr;
+    float* xp = has_aux ? Fp(aux) : nullptr;
+    const int rc = tile_gemm_ksum_ex(s, cnt, p.transB, dr, dc, ks.data(), p.alpha, A.data(), lda.data(), B.data(),
+                                     ldb.data(), p.beta, Fp(tl[0]), dc, p.epilogue, bp, rp, ldr, xp, ldaux);
+    if (rc != TT_ERR_UNSUPPORTED) return rc;
+    // the epilogue could not be fused into one long-K launch: a chain of
+    // accumulating products inside this task, the residual with the first,
+    // bias and activation with the last (the GELU chain accumulates the
+    // pre-activation in aux)
+    clear_error();
+    const size_t wsb = p.split_k && ws ? ctx->workspace_bytes : 0;
+    for (int u = 0; u < cnt; ++u) {
+      const bool first = u == 0, last = u == cnt - 1;
+      const int ep = (first ? (p.epilogue & TT_EPI_RES) : 0) |
+                     (last ? (p.epilogue & (TT_EPI_BIAS | TT_EPI_GELU | TT_EPI_GELU_BWD)) : 0);
+      const bool to_aux = gelu && !last;
+      float* tgt = to_aux ? xp : Fp(tl[0]);
+      const int64_t ldt = to_aux ? ldaux : dc;
+      if (int rc2 = tile_gemm_ws(s, 0, p.transB, dr, dc, ks[u], p.alpha, A[u], lda[u], B[u], ldb[u],
+                                 first ? p.beta : 1.f, tgt, ldt, ep, bp, rp, ldr, xp, ldaux, wsb ? ws : nullptr, wsb))
+        return rc2;
+    }
+    return TT_OK;
   }, flops);
 }
 

@@ -14,7 +14,7 @@ from ._lib import (TT_EPI_NONE, check, lib, ptr, stream_handle, TT_EPI_BIAS, TT_
 
 __all__ = [
     "tile_gemm", "tile_gemm_ws", "tile_gemm_workspace", "tile_gemm_ksum", "tile_gemm_batch", "tile_gemm_batch_ws",
-    "tile_gemm_batch_workspace", "tile_layernorm_fwd",
+    "tile_gemm_batch_workspace", "tile_gemm_ksum_ex", "tile_layernorm_fwd",
     "tile_layernorm_bwd", "tile_layernorm_bwd_workspace", "tile_softmax",
     "tile_xentropy", "tile_xentropy_multi", "tile_attention_fwd", "tile_attention_bwd", "tile_fused_adamw",
     "tile_fused_adamw_multi",
@@ -54,6 +54,18 @@ def tile_gemm_ksum(stream, m, n, ks, alpha, As, ldas, Bs, ldbs, beta, C, ldc, tr
     ptrs = lambda xs: (C_.c_void_p * max(cnt, 1))(*[ptr(x) for x in xs])  # noqa: E731
     return check(lib.tile_gemm_ksum(stream_handle(stream), cnt, transB, m, n, i64(ks), alpha, ptrs(As), i64(ldas),
                                     ptrs(Bs), i64(ldbs), beta, ptr(C), ldc))
+
+
+def tile_gemm_ksum_ex(stream, m, n, ks, alpha, As, ldas, Bs, ldbs, beta, C, ldc, transB=0, epilogue=TT_EPI_NONE,
+                      bias=None, res=None, ldr=0, aux=None, ldaux=0):
+    """tile_gemm_ksum followed by tile_gemm's epilogue on the whole sum."""
+    import ctypes as C_
+    cnt = len(As)
+    i64 = lambda xs: (C_.c_int64 * max(cnt, 1))(*[int(x) for x in xs])  # noqa: E731
+    ptrs = lambda xs: (C_.c_void_p * max(cnt, 1))(*[ptr(x) for x in xs])  # noqa: E731
+    return check(lib.tile_gemm_ksum_ex(stream_handle(stream), cnt, transB, m, n, i64(ks), alpha, ptrs(As), i64(ldas),
+                                       ptrs(Bs), i64(ldbs), beta, ptr(C), ldc, epilogue, ptr(bias), ptr(res), ldr,
+                                       ptr(aux), ldaux))
 
 
 def _batch_args(ms, ns, As, ldas, Bs, ldbs, Cs, ldcs):
