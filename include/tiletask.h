@@ -376,6 +376,24 @@ int tile_attention_bwd(void* stream, int phase, int64_t batch, int64_t heads, in
                        const float* dO, const float* lse, float* Dvec,
                        float* dQ, float* dK, float* dV, int acc_dq, int acc_dkv, float scale);
 
+/* tile_attention_bwd_ws -- tile_attention_bwd with a caller-owned device
+ * workspace of at least tile_attention_bwd_workspace(batch, heads, q_len,
+ * k_len) bytes, 16-byte aligned. TT_ATT_GRAD then computes S, dP and dS once
+ * per 32 x 32 block of the pair (dK/dV kernel), stores dS there and forms
+ * dQ += scale * dS K from it (dQ kernel): five matrix products per block
+ * instead of the seven of the recomputing form. Same results up to rounding
+ * order; deterministic. A null, misaligned or short workspace selects the
+ * recomputing form. The workspace holds no state between calls; calls that
+ * share one must be ordered (same stream).
+ */
+size_t tile_attention_bwd_workspace(int64_t batch, int64_t heads, int64_t q_len, int64_t k_len);
+int tile_attention_bwd_ws(void* stream, int phase, int64_t batch, int64_t heads, int64_t q_len,
+                          int64_t k_len, int64_t hd, int64_t q_off, int64_t k_off,
+                          const float* Q, const float* K, const float* V, const float* O,
+                          const float* dO, const float* lse, float* Dvec,
+                          float* dQ, float* dK, float* dV, int acc_dq, int acc_dkv, float scale,
+                          void* workspace, size_t workspace_bytes);
+
 /* tile_fused_adamw -- one decoupled-weight-decay Adam step over one
  * parameter tile, one pass over p, g, m, v (NNTile README, "Minimal working
  * GPT example": fused AdamW; the "Decoupled Weight Decay Regularization"
@@ -691,7 +709,9 @@ typedef struct {
  * TT_OP_ATTENTION_BWD -- tiles Q, K, V, dO, lse, Dvec, dQ, dK, dV:
  * dQ += , dK += , dV += the pair's gradient (tile_attention_bwd
  * TT_ATT_GRAD); reads the first six; dQ written unless acc_dq (then
- * updated), dK and dV written unless acc_dkv. */
+ * updated), dK and dV written unless acc_dkv. dS passes through the
+ * stream's workspace (tile_attention_bwd_ws), which the op enlarges to
+ * tile_attention_bwd_workspace of the pair when needed. */
 #define TT_OP_ATTENTION_FWD  7
 #define TT_OP_ATTENTION_PREP 8
 #define TT_OP_ATTENTION_BWD  9

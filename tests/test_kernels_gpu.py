@@ -594,8 +594,13 @@ def test_attention_fwd_single_tile(b, t, h, hd):
     assert_rel(host(lse), rlse, 1e-5, 1e-5, "attn lse")
 
 
-@pytest.mark.parametrize("hd,st", [(64, 64), (128, 96), (16, 8)])
-def test_attention_fwd_bwd_tile_pairs(hd, st):
+@pytest.mark.parametrize("stored_ds", [False, True])
+@pytest.mark.parametrize("hd,st", [(64, 64), (128, 96), (16, 8), (32, 40)])
+def test_attention_fwd_bwd_tile_pairs(hd, st, stored_ds):
+    """Both backward forms: recomputing dS in the dQ kernel, and dS handed
+    from the dK/dV kernel through a workspace (the workspace is filled with
+    NaN first: a block the dQ kernel reads but the other kernel did not
+    write would show)."""
     b, h, t = 2, 2, 3 * st
     q, k, v = _attn_inputs(b, t, h, hd, 61)
     do = synth.rand_normal((b, t, h, hd), 64)
@@ -625,10 +630,17 @@ def test_attention_fwd_bwd_tile_pairs(hd, st):
     for qi in range(n):
         tt.tile_attention_bwd(None, tt.TT_ATT_PREP, b, h, st, st, hd, 0, 0, None, None, None, O[qi], dO[qi], None,
                               Dv[qi], None, None, None, 0, 0, scale)
+    wsb = tt.tile_attention_bwd_workspace(b, h, st, st)
+    assert wsb == b * h * (-(-st // 32)) ** 2 * 1024 * 4
+    ws = torch.full((wsb // 4,), float("nan"), device="cuda")
     for qi in range(n):
         for ki in range(qi + 1):
-            tt.tile_attention_bwd(None, tt.TT_ATT_GRAD, b, h, st, st, hd, qi * st, ki * st, Q[qi], K[ki], V[ki], None,
-                                  dO[qi], lse[qi], Dv[qi], dQ[qi], dK[ki], dV[ki], int(ki > 0), int(qi > ki), scale)
+            args = (None, tt.TT_ATT_GRAD, b, h, st, st, hd, qi * st, ki * st, Q[qi], K[ki], V[ki], None,
+                    dO[qi], lse[qi], Dv[qi], dQ[qi], dK[ki], dV[ki], int(ki > 0), int(qi > ki), scale)
+            if stored_ds:
+                tt.tile_attention_bwd_ws(*args, ws, wsb)
+            else:
+                tt.tile_attention_bwd(*args)
     f = lambda a: a.astype(np.float64).transpose(0, 2, 1, 3)  # noqa: E731
     rdq, rdk, rdv = og.causal_attention_bwd(f(do), f(q), f(k), f(v), rp)
     cat = lambda xs: np.concatenate([host(x) for x in xs], axis=1).transpose(0, 2, 1, 3)  # noqa: E731

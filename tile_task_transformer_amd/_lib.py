@@ -162,6 +162,9 @@ SIGNATURES = {
     "tile_xentropy": (I, [P, I, I64, I64, I64, P, P, I64, P, P, P, I, F]),
     "tile_attention_fwd": (I, [P, I64, I64, I64, I64, I64, I64, I64, P, P, P, P, P, P, I, I, F]),
     "tile_attention_bwd": (I, [P, I, I64, I64, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P, I, I, F]),
+    "tile_attention_bwd_workspace": (SZ, [I64, I64, I64, I64]),
+    "tile_attention_bwd_ws": (I, [P, I, I64, I64, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P, I, I, F, P,
+                                  SZ]),
     "tile_fused_adamw": (I, [P, I64, P, P, P, P, F, F, F, F, F, P]),
     "tile_fused_adamw_multi": (I, [P, I, P, P, P, P, P, F, F, F, F, F, P]),
     "tile_adamw_advance": (I, [P, P, P, F, F]),

@@ -468,13 +468,130 @@ __global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_bwd_dq(AttnGeom g, co
     }
 }
 
+// dQ = scale * dS K from the dS blocks the dK/dV kernel stored (5 products
+// per tile pair instead of 7: S and dP are not recomputed). Same work split
+// as attn_bwd_dq: 32 queries per wave pair, each wave half of every 64-key
+// stage. A stage's four 32 x 32 blocks (2 query groups x 2 key halves) are
+// loaded with 16-byte accesses and transposed into LDS (row stride 33: the
+// wave's reads of one key row by its 32 query lanes hit 32 banks), then fed
+// to the MFMAs in the register layout of the recomputing kernel.
+template <int HD>
+__global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_bwd_dq_ds(AttnGeom g, const float* __restrict__ K,
+                                                                    const float* __restrict__ dsw,
+                                                                    float* __restrict__ dQ, int acc) {
+  using C = Cfg<HD>;
+  constexpr int LD = C::LD, NEB = C::NEB;
+  constexpr int TLD = 33;
+  __shared__ __attribute__((aligned(16))) float Ks[kBS * LD];
+  __shared__ float Ts[4 * 32 * TLD];  // the stage's dS blocks, [block][key][query]
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = wave & 1, part = wave >> 1;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int qblk = gridDim.y - 1 - blockIdx.y;
+  const int bh = blockIdx.x, b = bh / g.heads, h = bh % g.heads;
+  const int q0 = qblk * kBQ + grp * 32;
+  const int q = q0 + l32;
+  const bool qvalid = q < g.q_len;
+  const int nq32 = (g.q_len + 31) / 32, nk32 = (g.k_len + 31) / 32;
+  const float* dsb = dsw + (int64_t)bh * nq32 * nk32 * 1024;
+
+  f32x16 dacc[NEB];
+#pragma unroll
+  for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dacc[eb][r] = 0.f;
+
+  const int64_t qmax = g.q_off + min(g.q_len, qblk * kBQ + kBQ) - 1;
+  const int kend = (int)max((int64_t)0, min((int64_t)g.k_len, qmax - g.k_off + 1));
+  const int64_t wave_qmax = g.q_off + min(g.q_len - 1, q0 + 31);
+  const bool wave_live = q0 < g.q_len;
+
+  // float4 i of the thread: block idx >> 8 of the stage (query group
+  // blk >> 1, key half blk & 1), elements 4 * (idx & 255) .. + 3 in register
+  // order: element p holds query kidx(p >> 6, (p >> 5) & 1), key p & 31
+  f32x4 dr[4];
+  auto ds_load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = (int)threadIdx.x + kNT * i, blk = idx >> 8;
+      const int q32 = qblk * 2 + (blk >> 1), k32 = k0 / 32 + (blk & 1);
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (q32 < nq32 && k32 < nk32)
+        v = *reinterpret_cast<const f32x4*>(dsb + ((int64_t)q32 * nk32 + k32) * 1024 + (idx & 255) * 4);
+      dr[i] = v;
+    }
+  };
+  auto ds_store = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = (int)threadIdx.x + kNT * i, blk = idx >> 8;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int p = (idx & 255) * 4 + e;
+        Ts[blk * 32 * TLD + (p & 31) * TLD + kidx(p >> 6, (p >> 5) & 1)] = dr[i][e];
+      }
+    }
+  };
+
+  zero_pad<HD, LD>(Ks);
+  Stager<HD, LD> sk;
+  if (kend > 0) {
+    sk.load(K, b, h, 0, g.k_len, g.heads);
+    ds_load(0);
+    sk.store(Ks);
+    ds_store();
+  }
+  __syncthreads();
+  for (int k0 = 0; k0 < kend; k0 += kBS) {
+    const bool more = k0 + kBS < kend;
+    if (more) {
+      sk.load(K, b, h, k0 + kBS, g.k_len, g.heads);
+      ds_load(k0 + kBS);
+    }
+    const int kb0 = k0 + part * 32;
+    const float* ks = Ks + part * 32 * LD;
+    const float* ts = Ts + (grp * 2 + part) * 32 * TLD;
+    if (wave_live && kb0 < g.k_len && g.k_off + kb0 <= wave_qmax) {
+      f32x16 dst;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dst[r] = ts[kidx(r, half) * TLD + l32];  // dS^T: lane owns a query column
+#pragma unroll
+      for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dacc[eb] = mfma(ks[kidx(r, half) * LD + eb * 32 + l32], dst[r], dacc[eb]);
+    }
+    __syncthreads();
+    if (more) {
+      sk.store(Ks);
+      ds_store();
+    }
+    __syncthreads();
+  }
+  merge_add<NEB>(Ks, grp, part, lane, dacc);
+  if (part == 1 || !qvalid) return;
+  float* drow = dQ + row_off(b, q, h, g.q_len, g.heads, HD);
+#pragma unroll
+  for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int e = eb * 32 + 8 * gq + 4 * half;
+      if (e < HD) {
+        f32x4 v = {dacc[eb][4 * gq], dacc[eb][4 * gq + 1], dacc[eb][4 * gq + 2], dacc[eb][4 * gq + 3]};
+        v *= g.scale;
+        if (acc) v += *reinterpret_cast<const f32x4*>(drow + e);
+        *reinterpret_cast<f32x4*>(drow + e) = v;
+      }
+    }
+}
+
 // dK, dV: a group of 32 keys per wave pair; streams query blocks (Q, dO, lse, D).
 template <int HD>
 __global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_bwd_dkv(AttnGeom g, const float* __restrict__ Q,
                                                       const float* __restrict__ K, const float* __restrict__ V,
                                                       const float* __restrict__ dO, const float* __restrict__ lse,
                                                       const float* __restrict__ Dv, float* __restrict__ dK,
-                                                      float* __restrict__ dV, int acc) {
+                                                      float* __restrict__ dV, int acc, float* __restrict__ dsw) {
   using C = Cfg<HD>;
   constexpr int LD = C::LD, NKB = C::NKB, NEB = C::NEB;
   __shared__ __attribute__((aligned(16))) float Qs[2 * kBS * LD];   // Q stage, then dO stage
@@ -602,6 +719,12 @@ __global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_bwd_dkv(AttnGeom g, c
           dkv[NEB + eb] = mfma(dsb[kidx(r, half) * LD + eb * 32 + l32], s[r], dkv[NEB + eb]);  // dV^T += dO^T P
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] *= dp[r] - dv[r >> 2][r & 3];  // dS, in place of P
+      if (dsw) {  // the 32 x 32 block of dS for the dQ kernel, in register order (coalesced per register)
+        const int nq32 = (g.q_len + 31) / 32, nk32 = (g.k_len + 31) / 32;
+        float* blk = dsw + (((int64_t)bh * nq32 + qb0 / 32) * nk32 + k0w / 32) * 1024 + lane;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) blk[r * 64] = s[r];
+      }
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll
@@ -675,10 +798,16 @@ extern "C" int tile_attention_fwd(void* stream, int64_t batch, int64_t heads, in
   return tt::launch_status("tile_attention_fwd");
 }
 
-extern "C" int tile_attention_bwd(void* stream, int phase, int64_t batch, int64_t heads, int64_t q_len, int64_t k_len,
-                                  int64_t hd, int64_t q_off, int64_t k_off, const float* Q, const float* K,
-                                  const float* V, const float* O, const float* dO, const float* lse, float* Dvec,
-                                  float* dQ, float* dK, float* dV, int acc_dq, int acc_dkv, float scale) {
+extern "C" size_t tile_attention_bwd_workspace(int64_t batch, int64_t heads, int64_t q_len, int64_t k_len) {
+  if (batch <= 0 || heads <= 0 || q_len <= 0 || k_len <= 0) return 0;
+  return (size_t)(batch * heads) * (size_t)((q_len + 31) / 32) * (size_t)((k_len + 31) / 32) * 1024 * sizeof(float);
+}
+
+extern "C" int tile_attention_bwd_ws(void* stream, int phase, int64_t batch, int64_t heads, int64_t q_len,
+                                     int64_t k_len, int64_t hd, int64_t q_off, int64_t k_off, const float* Q,
+                                     const float* K, const float* V, const float* O, const float* dO, const float* lse,
+                                     float* Dvec, float* dQ, float* dK, float* dV, int acc_dq, int acc_dkv,
+                                     float scale, void* workspace, size_t workspace_bytes) {
   if (int rc = check_geom("tile_attention_bwd", batch, heads, q_len, k_len, hd)) return rc;
   if (batch == 0 || heads == 0) return TT_OK;
   hipStream_t s = tt::as_stream(stream);
@@ -707,9 +836,19 @@ extern "C" int tile_attention_bwd(void* stream, int phase, int64_t batch, int64_
   dim3 gq((unsigned)(batch * heads), (unsigned)((q_len + kBQ - 1) / kBQ));
   dim3 gk((unsigned)(batch * heads), (unsigned)((k_len + kBQ - 1) / kBQ));
   dim3 block(kNT);
-#define TT_ATT_BWD(HD)                                                                                   \
-  hipLaunchKernelGGL(attn_bwd_dq<HD>, gq, block, 0, s, g, Q, K, V, dO, lse, Dvec, dQ, acc_dq);          \
-  hipLaunchKernelGGL(attn_bwd_dkv<HD>, gk, block, 0, s, g, Q, K, V, dO, lse, Dvec, dK, dV, acc_dkv)
+  const bool stored = workspace && aligned16(workspace) &&
+                      workspace_bytes >= tile_attention_bwd_workspace(batch, heads, q_len, k_len);
+  float* dsw = stored ? (float*)workspace : nullptr;
+  // with a workspace the dK/dV kernel stores dS and the dQ kernel reads it;
+  // without, the dQ kernel recomputes S and dP
+#define TT_ATT_BWD(HD)                                                                                          \
+  if (stored) {                                                                                                 \
+    hipLaunchKernelGGL(attn_bwd_dkv<HD>, gk, block, 0, s, g, Q, K, V, dO, lse, Dvec, dK, dV, acc_dkv, dsw);    \
+    hipLaunchKernelGGL(attn_bwd_dq_ds<HD>, gq, block, 0, s, g, K, (const float*)dsw, dQ, acc_dq);               \
+  } else {                                                                                                      \
+    hipLaunchKernelGGL(attn_bwd_dq<HD>, gq, block, 0, s, g, Q, K, V, dO, lse, Dvec, dQ, acc_dq);               \
+    hipLaunchKernelGGL(attn_bwd_dkv<HD>, gk, block, 0, s, g, Q, K, V, dO, lse, Dvec, dK, dV, acc_dkv, nullptr); \
+  }
   switch (hd) {
     case 16: TT_ATT_BWD(16); break;
     case 32: TT_ATT_BWD(32); break;
@@ -718,4 +857,12 @@ extern "C" int tile_attention_bwd(void* stream, int phase, int64_t batch, int64_
   }
 #undef TT_ATT_BWD
   return tt::launch_status("tile_attention_bwd(GRAD)");
+}
+
+extern "C" int tile_attention_bwd(void* stream, int phase, int64_t batch, int64_t heads, int64_t q_len, int64_t k_len,
+                                  int64_t hd, int64_t q_off, int64_t k_off, const float* Q, const float* K,
+                                  const float* V, const float* O, const float* dO, const float* lse, float* Dvec,
+                                  float* dQ, float* dK, float* dV, int acc_dq, int acc_dkv, float scale) {
+  return tile_attention_bwd_ws(stream, phase, batch, heads, q_len, k_len, hd, q_off, k_off, Q, K, V, O, dO, lse, Dvec,
+                               dQ, dK, dV, acc_dq, acc_dkv, scale, nullptr, 0);
 }

@@ -507,6 +507,8 @@ extern "C" int tt_gpt2_create(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_g
   ws = std::max(ws, std::min<int64_t>(16, std::max(G->NE, G->NI)) * tile_reduce_rows_workspace(G->rows, widest));
   // the q/k/v bias gradients: up to 15 head tiles per multi-tile column sum
   ws = std::max(ws, tile_reduce_rows_workspace(G->rows, std::min<int64_t>(15, 3 * G->NH) * ht * hd));
+  // dS of one attention tile pair (the backward's dK/dV kernel hands it to the dQ kernel)
+  ws = std::max(ws, tile_attention_bwd_workspace(bt, ht, sq, sq));
   {
     // split-K slices of the step's GEMM shapes (m, n, k), capped at 256 MiB per stream
     const int64_t r = G->rows, e = et, in = std::min<int64_t>(it, I), hw = ht * hd, vv = vt;

@@ -527,7 +527,7 @@ int op_att_prep(tt_ctx* ctx, const TileArg* T, int n, const tt_op_attention& q, 
                      });
 }
 
-int op_att_bwd(tt_ctx* ctx, const TileArg* T, int n, const tt_op_attention& q, const char* label) {
+int op_att_bwd(tt_ctx* ctx, const TileArg* T, int n, const tt_op_attention& q, const char* label, bool grow) {
   const char* nm = "TT_OP_ATTENTION_BWD";
   if (n != 9) return fail(TT_ERR_ARG, "%s: tiles Q, K, V, dO, lse, Dvec, dQ, dK, dV", nm);
   if (int rc = need_f32(T, n, nm)) return rc;
@@ -546,10 +546,15 @@ int op_att_bwd(tt_ctx* ctx, const TileArg* T, int n, const tt_op_attention& q, c
   std::vector<TileArg> tl(T, T + n);
   const tt_op_attention p = q;
   const double flops = 10.0 * g.batch * g.heads * g.hd * visible_pairs(g.q_len, g.k_len, q.q_off, q.k_off);
-  return ctx->submit(label ? label : "attn_bwd", std::move(acc), [=](hipStream_t s, void*) {
-    return tile_attention_bwd(s, TT_ATT_GRAD, g.batch, g.heads, g.q_len, g.k_len, g.hd, p.q_off, p.k_off, Fp(tl[0]),
-                              Fp(tl[1]), Fp(tl[2]), nullptr, Fp(tl[3]), Fp(tl[4]), Fp(tl[5]), Fp(tl[6]), Fp(tl[7]),
-                              Fp(tl[8]), p.acc_dq, p.acc_dkv, p.scale);
+  // dS goes through the stream workspace (5 products per tile pair instead of 7)
+  const size_t need = tile_attention_bwd_workspace(g.batch, g.heads, g.q_len, g.k_len);
+  if (grow)
+    if (int rc = ctx->ensure_workspace(need)) return rc;
+  return ctx->submit(label ? label : "attn_bwd", std::move(acc), [=](hipStream_t s, void* ws) {
+    return tile_attention_bwd_ws(s, TT_ATT_GRAD, g.batch, g.heads, g.q_len, g.k_len, g.hd, p.q_off, p.k_off,
+                                 Fp(tl[0]), Fp(tl[1]), Fp(tl[2]), nullptr, Fp(tl[3]), Fp(tl[4]), Fp(tl[5]), Fp(tl[6]),
+                                 Fp(tl[7]), Fp(tl[8]), p.acc_dq, p.acc_dkv, p.scale, ws,
+                                 ws ? ctx->workspace_bytes : 0);
   }, flops);
 }
 
@@ -1022,7 +1027,7 @@ int submit_op(tt_ctx* ctx, int op, const TileArg* T, int n, const void* sc, size
       if (int rc = scal(sc, size, "TT_OP_ATTENTION*", &q)) return rc;
       if (op == TT_OP_ATTENTION_FWD) return op_att_fwd(ctx, T, n, q, label);
       if (op == TT_OP_ATTENTION_PREP) return op_att_prep(ctx, T, n, q, label);
-      return op_att_bwd(ctx, T, n, q, label);
+      return op_att_bwd(ctx, T, n, q, label, grow);
     }
     case TT_OP_XENTROPY_STATS:
       return op_xe_stats(ctx, T, n, label);

@@ -16,7 +16,8 @@ __all__ = [
     "tile_gemm", "tile_gemm_ws", "tile_gemm_workspace", "tile_gemm_ksum", "tile_gemm_batch", "tile_gemm_batch_ws",
     "tile_gemm_batch_workspace", "tile_gemm_ksum_ex", "tile_layernorm_fwd",
     "tile_layernorm_bwd", "tile_layernorm_bwd_workspace", "tile_softmax",
-    "tile_xentropy", "tile_xentropy_multi", "tile_attention_fwd", "tile_attention_bwd", "tile_fused_adamw",
+    "tile_xentropy", "tile_xentropy_multi", "tile_attention_fwd", "tile_attention_bwd",
+    "tile_attention_bwd_workspace", "tile_attention_bwd_ws", "tile_fused_adamw",
     "tile_fused_adamw_multi",
     "tile_adamw_advance", "tile_sgd", "tile_sgd_multi",
     "tile_embedding_fwd", "tile_embedding_index", "tile_embedding_bwd", "tile_reduce_rows",
@@ -150,6 +151,18 @@ def tile_attention_bwd(stream, phase, batch, heads, q_len, k_len, hd, q_off, k_o
     return check(lib.tile_attention_bwd(stream_handle(stream), phase, batch, heads, q_len, k_len, hd, q_off, k_off,
                                         ptr(Q), ptr(K), ptr(V), ptr(O), ptr(dO), ptr(lse), ptr(Dvec), ptr(dQ),
                                         ptr(dK), ptr(dV), acc_dq, acc_dkv, scale))
+
+
+def tile_attention_bwd_workspace(batch, heads, q_len, k_len):
+    return lib.tile_attention_bwd_workspace(batch, heads, q_len, k_len)
+
+
+def tile_attention_bwd_ws(stream, phase, batch, heads, q_len, k_len, hd, q_off, k_off, Q, K, V, O, dO, lse, Dvec, dQ,
+                          dK, dV, acc_dq, acc_dkv, scale, workspace, workspace_bytes):
+    return check(lib.tile_attention_bwd_ws(stream_handle(stream), phase, batch, heads, q_len, k_len, hd, q_off, k_off,
+                                           ptr(Q), ptr(K), ptr(V), ptr(O), ptr(dO), ptr(lse), ptr(Dvec), ptr(dQ),
+                                           ptr(dK), ptr(dV), acc_dq, acc_dkv, scale, ptr(workspace),
+                                           workspace_bytes))
 
 
 def tile_fused_adamw(stream, n, p, g, m, v, lr, beta1, beta2, eps, weight_decay, bias_corr):
