@@ -671,11 +671,51 @@ def run(w, a, streams, breakdown_path, probe, steps=None, warmup=None, want_para
                       for k, v in classes.items()}
     print(f"[bench] {w.name}: timed {steps} steps: {ms:.2f} ms/step, {tok_s:.0f} tokens/s, {tflops:.1f} TFLOP/s",
           file=sys.stderr, flush=True)
+    out["executor"] = executor_figures(w, model, ctx, tok, hp, streams, ms, st, steps)
+    print(f"[bench] {w.name}: executor {out['executor']}", file=sys.stderr, flush=True)
     model.close()
     ctx.close()
     del tok
     torch.cuda.empty_cache()
     return out, {"params": params, "tokens": tokens}
+
+
+def executor_figures(w, model, ctx, tok, hp, streams, ms, st, steps, busy_steps=2):
+    """Executor overhead beside the timed step: tasks per step and GPU time
+    per task; the host's own cost of building a step's task graph (the same
+    step submitted to a dry-run context: dependency inference, stream
+    assignment and bookkeeping without launches, so the GPU cannot hold it
+    back); host time inside submit calls in the timed region (launches
+    included, which block once the GPU queues are full); and the GPU's idle
+    fraction: every task of busy_steps extra steps bracketed by timing
+    events, 1 - (union of their GPU intervals) / (first start to last end)."""
+    from tile_task_transformer_amd import _lib as L
+    from tile_task_transformer_amd.runtime import Context, GPT2
+    ntask = model.task_count()
+    with Context(L.TT_DEVICE_DRYRUN, n_streams=streams, window=4096) as dctx:
+        dm = GPT2(dctx, w.shape, w.tiles)
+        dm.step(None, **hp)
+        t0 = time.perf_counter()
+        for _ in range(2):
+            dm.step(None, **hp)
+        dry = (time.perf_counter() - t0) / 2
+        dm.close()
+    ctx.profile("*", every=1)
+    for _ in range(busy_steps):
+        model.step(tok, **hp)
+    busy = ctx.profile_busy()
+    ctx.profile_take()
+    ctx.profile(None)
+    span = busy["span_ms"]
+    return {
+        "tasks_per_step": ntask,
+        "gpu_us_per_task": round(1e3 * ms / ntask, 2),
+        "host_graph_ms_per_step": round(1e3 * dry, 3),
+        "host_graph_us_per_task": round(1e6 * dry / ntask, 2),
+        "host_submit_ms_per_step": round(1e3 * st["submit_seconds"] / steps, 3),
+        "gpu_idle_frac": round(1.0 - busy["busy_ms"] / span, 4) if span > 0 else None,
+        "timed_tasks": busy["tasks"], "timed_span_ms_per_step": round(span / busy_steps, 3),
+    }
 
 
 if __name__ == "__main__":

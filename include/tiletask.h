@@ -144,6 +144,21 @@ int tile_gemm_ksum_ex(void* stream, int count, int transB, int64_t m, int64_t n,
                       const float* const* A, const int64_t* lda, const float* const* B, const int64_t* ldb,
                       float beta, float* C, int64_t ldc, int epilogue, const float* bias, const float* res,
                       int64_t ldr, float* aux, int64_t ldaux);
+/* tile_gemm_ksum_ws -- tile_gemm_ksum_ex with a DEVICE workspace (16-byte
+ * aligned; null with 0 bytes = none). An output of fewer than 256 blocks
+ * of 128 x 128 (m and n multiples of 128) then splits the concatenated K
+ * steps of each long-K launch into up to 16 slices that run side by side
+ * (about 512 workgroups), each summing its slice into its own m x n region
+ * of the workspace; a second kernel adds the slices in slice order and
+ * applies alpha, beta and the epilogue. Deterministic: same result on every
+ * run. tile_gemm_ksum_workspace(m, n) is the size that allows the widest
+ * split (0 where none applies); a smaller workspace splits less. TT_ERR_ARG
+ * also for a null or misaligned workspace with nonzero bytes. */
+size_t tile_gemm_ksum_workspace(int64_t m, int64_t n);
+int tile_gemm_ksum_ws(void* stream, int count, int transB, int64_t m, int64_t n, const int64_t* k, float alpha,
+                      const float* const* A, const int64_t* lda, const float* const* B, const int64_t* ldb,
+                      float beta, float* C, int64_t ldc, int epilogue, const float* bias, const float* res,
+                      int64_t ldr, float* aux, int64_t ldaux, void* workspace, size_t workspace_bytes);
 /* tile_gemm_batch -- independent products in one launch:
  *   C_t = alpha * op(A_t) op(B_t) + beta * C_t,   t < count
  * op() as in tile_gemm; the products share transA, transB, k, alpha and
@@ -663,7 +678,9 @@ typedef struct { float value; } tt_op_fill;
  * or backward): tiles C, then bias / res / aux as the epilogue requires (as
  * for TT_OP_GEMM), then A_0, B_0, A_1, B_1, ... (one or more pairs; more
  * than 96 make several launches); C = epilogue(alpha sum_t A_t op(B_t) +
- * beta C) with transA = 0. Accesses as TT_OP_GEMM. Where one long-K launch
+ * beta C) with transA = 0. Accesses as TT_OP_GEMM. split_k != 0 lets an
+ * output of few blocks split K over the stream's workspace
+ * (tile_gemm_ksum_ws; the op enlarges it as needed). Where one long-K launch
  * cannot take every pair (shapes not multiples of its blocks, misaligned
  * tiles, more than 96 pairs), the task runs a chain of products instead:
  * the same result up to the order of the additions. */
@@ -833,6 +850,7 @@ int tt_dump_dag(tt_ctx* ctx, const char* path);
 /* Per-task GPU timing. Tasks whose label equals label_filter ("*" = every
  * task, NULL = off) are bracketed by a pair of timing events on their
  * stream; the durations are aggregated per label when the context drains.
+ * tt_ctx_profile first waits for the work already queued.
  * tt_profile_read waits, fills up to max_entries entries (one per label,
  * *n_entries = number of labels seen) and clears the aggregate. Timing
  * events add a little GPU time per bracketed task, so narrow filters are
@@ -849,6 +867,17 @@ int tt_profile_read(tt_ctx* ctx, tt_profile_entry* out, int max_entries, int* n_
  * samples. Counting restarts at every tt_ctx_profile call. TT_ERR_ARG for
  * every < 1. */
 int tt_ctx_profile_every(tt_ctx* ctx, int every);
+/* GPU occupancy of the timed tasks: tt_ctx_profile drains the context and
+ * records a reference event; every task timed since has a [start, end]
+ * interval against it. tt_profile_busy waits and returns the length of the
+ * union of those intervals (*busy_ms: time at least one timed task was on
+ * the GPU), the time from the first start to the last end (*span_ms) and
+ * the number of intervals, then clears them. With the filter "*" and every
+ * = 1, 1 - busy/span is the fraction of the span the GPU had no task of the
+ * context running (the gaps between dependent tasks and launch latency not
+ * hidden by other streams); the timing events add a few microseconds per
+ * task to that span. */
+int tt_profile_busy(tt_ctx* ctx, double* busy_ms, double* span_ms, int64_t* n_tasks);
 
 typedef struct {
     int64_t tasks;            /* tasks submitted since creation / reset     */

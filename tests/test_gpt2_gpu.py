@@ -229,3 +229,29 @@ def test_sgd_steps_match_oracle():
         gmax = np.abs(rg1[name]).max()
         assert np.abs(got - rp1[name]).max() <= lr * 1e-3 * gmax + 2.0 ** -22 * np.abs(p0).max() + 1e-30, name
         assert not m[name].any() and not v[name].any(), name
+
+
+def test_task_timing_and_busy_union():
+    """Per-task timing over a whole step: every task of the step is timed
+    once, the union of their GPU intervals is positive and no longer than
+    the span from the first start to the last end, and the per-label totals
+    are at least the union (overlapping tasks on several streams count once
+    in the union, once each in the totals)."""
+    shape, tiles = TINY.shape, TINY.tiles
+    params = synth.init_params(shape, seed=0)
+    tokens = synth.token_stream(shape, seed=1)
+    with Context(0, n_streams=4) as ctx:
+        model = GPT2(ctx, shape, tiles)
+        model.set_params(params, synth.param_specs(shape))
+        tok = torch.from_numpy(tokens.astype(np.int32)).cuda()
+        model.step(tok)
+        ctx.profile("*")
+        model.step(tok)
+        busy = ctx.profile_busy()
+        per_label = ctx.profile_take()
+        ctx.profile(None)
+        n = model.task_count()
+        model.close()
+    assert busy["tasks"] == n == sum(v["count"] for v in per_label.values())
+    assert 0 < busy["busy_ms"] <= busy["span_ms"] * (1 + 1e-6)
+    assert sum(v["total_ms"] for v in per_label.values()) >= busy["busy_ms"] * (1 - 1e-6)

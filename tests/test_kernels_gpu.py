@@ -70,6 +70,16 @@ def test_gemm_split_k_workspace(ta, tb, m, n, k):
     assert torch.equal(outs[0], outs[1])
 
 
+def _ksum_ws(m, n, use):
+    """a NaN-filled workspace of the size that allows the widest K split (a
+    slice the kernels failed to write would show), or none"""
+    if not use:
+        return None, 0
+    wsb = tt.tile_gemm_ksum_workspace(m, n)
+    return torch.full((max(wsb, 4) // 4,), float("nan"), device="cuda"), wsb
+
+
+@pytest.mark.parametrize("ws", [False, True])
 @pytest.mark.parametrize("tb", [0, 1])
 @pytest.mark.parametrize("m,n,ks,beta", [
     (4096, 768, [768] * 5 + [337], 0.0),          # the LM head's dnf: full vocab tiles + the ragged last one
@@ -78,19 +88,24 @@ def test_gemm_split_k_workspace(ta, tb, m, n, k):
     (2048, 4096, [48, 64], 0.0),                  # the 128x128 plan (>= 512 blocks)
     (100, 72, [40, 33], 0.25),                    # m, n off the block grid: every pair falls back
     (4096, 768, [768] * 3, 0.0),                  # the q/k/v input gradient (B transposed)
+    (1024, 512, [1024] * 6, 0.5),                 # a narrow output: 32 blocks, K split into 12 slices
+    (512, 384, [512, 160, 512, 96], 1.0),         # slices that start and end inside pairs of unequal K
 ])
-def test_gemm_ksum(m, n, ks, beta, tb):
+def test_gemm_ksum(m, n, ks, beta, tb, ws):
     """C = alpha sum_t A_t op(B_t) + beta C against the fp64 sum (fp32 bound
-    over the total K), bitwise equal across runs; B as [k][n] or [n][k]."""
+    over the total K), bitwise equal across runs; B as [k][n] or [n][k];
+    without and with a workspace (split K for outputs of few blocks)."""
     seed = m + n + len(ks) + 5 * tb
     As = [synth.rand_normal((m, k), seed + 2 * i) for i, k in enumerate(ks)]
     Bs = [synth.rand_normal((n, k) if tb else (k, n), seed + 2 * i + 1) for i, k in enumerate(ks)]
     c0 = synth.rand_normal((m, n), seed + 999)
     dA, dB = [dev(a) for a in As], [dev(b) for b in Bs]
+    W, wsb = _ksum_ws(m, n, ws)
     outs = []
     for _ in range(2):
         C = dev(c0)
-        tt.tile_gemm_ksum(None, m, n, ks, 0.75, dA, ks, dB, [b.shape[1] for b in Bs], beta, C, n, transB=tb)
+        tt.tile_gemm_ksum_ex(None, m, n, ks, 0.75, dA, ks, dB, [b.shape[1] for b in Bs], beta, C, n, transB=tb,
+                             workspace=W, workspace_bytes=wsb)
         outs.append(C)
     ref = beta * c0.astype(np.float64)
     bound = np.zeros((m, n))
@@ -103,14 +118,18 @@ def test_gemm_ksum(m, n, ks, beta, tb):
     assert torch.equal(outs[0], outs[1])
 
 
-@pytest.mark.parametrize("m,n,k,count,tb,epi", [
-    (4096, 2048, 512, 4, 0, "bias_res"),      # 512 blocks of 128x128 (BK 16): the attention projection's shape
-    (1024, 1024, 256, 3, 0, "gelu"),          # 64 blocks of 64x64: the MLP input layer with its activation
-    (4096, 4096, 256, 2, 1, "gelu_bwd"),      # 1024 blocks (BK 32), B stored [n][k]: the MLP output's input gradient
+@pytest.mark.parametrize("m,n,k,count,tb,epi,ws", [
+    (4096, 2048, 512, 4, 0, "bias_res", False),   # 512 blocks of 128x128 (BK 16): the attention projection's shape
+    (1024, 1024, 256, 3, 0, "gelu", False),       # 64 blocks of 64x64: the MLP input layer with its activation
+    (4096, 4096, 256, 2, 1, "gelu_bwd", False),   # 1024 blocks (BK 32), B stored [n][k]: the MLP output's dX
+    (1024, 512, 1024, 3, 0, "bias_res", True),    # split K (6 slices), then bias + residual on the slice sum
+    (1024, 1024, 512, 4, 0, "gelu", True),        # split K (4 slices), GELU on the slice sum
+    (1024, 512, 512, 4, 1, "gelu_bwd", True),     # split K (4 slices), B stored [n][k], GELU'
 ])
-def test_gemm_ksum_epilogues(m, n, k, count, tb, epi):
+def test_gemm_ksum_epilogues(m, n, k, count, tb, epi, ws):
     """K-sum with tile_gemm's epilogues on the whole sum: bias + residual,
-    GELU (pre-activation kept in aux) and GELU' against the fp64 sum."""
+    GELU (pre-activation kept in aux) and GELU' against the fp64 sum, also
+    with K split into slices over a workspace."""
     seed = m + n + count
     As = [synth.rand_normal((m, k), seed + i, std=0.2) for i in range(count)]
     Bs = [synth.rand_normal((n, k) if tb else (k, n), seed + 50 + i, std=0.2) for i in range(count)]
@@ -126,9 +145,10 @@ def test_gemm_ksum_epilogues(m, n, k, count, tb, epi):
     C, aux = empty((m, n)), dev(aux0)
     flag = {"bias_res": tt.TT_EPI_BIAS | tt.TT_EPI_RES, "gelu": tt.TT_EPI_GELU | tt.TT_EPI_BIAS,
             "gelu_bwd": tt.TT_EPI_GELU_BWD}[epi]
+    W, wsb = _ksum_ws(m, n, ws)
     tt.tile_gemm_ksum_ex(None, m, n, [k] * count, 1.0, [dev(a) for a in As], [k] * count, [dev(b) for b in Bs],
                          [b.shape[1] for b in Bs], 0.0, C, n, transB=tb, epilogue=flag, bias=dev(bias), res=dev(res),
-                         ldr=n, aux=aux, ldaux=n)
+                         ldr=n, aux=aux, ldaux=n, workspace=W, workspace_bytes=wsb)
     if epi == "bias_res":
         want = ref + bias + res
         assert_close_bound(host(C), want, bound + 4 * EPS32 * np.abs(want) + 1e-6, "ksum bias+res")

@@ -146,6 +146,8 @@ SIGNATURES = {
     "tile_gemm_workspace": (SZ, [I64, I64, I64]),
     "tile_gemm_ksum": (I, [P, I, I, I64, I64, P, F, P, P, P, P, F, P, I64]),
     "tile_gemm_ksum_ex": (I, [P, I, I, I64, I64, P, F, P, P, P, P, F, P, I64, I, P, P, I64, P, I64]),
+    "tile_gemm_ksum_ws": (I, [P, I, I, I64, I64, P, F, P, P, P, P, F, P, I64, I, P, P, I64, P, I64, P, SZ]),
+    "tile_gemm_ksum_workspace": (SZ, [I64, I64]),
     "tile_gemm_batch": (I, [P, I, I, I, P, P, I64, F, P, P, P, P, F, P, P]),
     "tile_gemm_batch_ws": (I, [P, I, I, I, P, P, I64, F, P, P, P, P, F, P, P, P, SZ]),
     "tile_gemm_batch_workspace": (SZ, [I, P, P, I64]),
@@ -205,6 +207,7 @@ SIGNATURES = {
     "tt_get_stats": (I, [P, C.POINTER(tt_stats)]),
     "tt_ctx_profile": (I, [P, C.c_char_p]),
     "tt_profile_read": (I, [P, C.POINTER(tt_profile_entry), I, C.POINTER(I)]),
+    "tt_profile_busy": (I, [P, C.POINTER(C.c_double), C.POINTER(C.c_double), C.POINTER(I64)]),
     "tt_ctx_profile_every": (I, [P, I]),
     "tt_reset_stats": (I, [P]),
     "tt_gpt2_create": (I, [P, C.POINTER(tt_gpt2_config), C.POINTER(tt_gpt2_tiles), I, PP]),

@@ -658,13 +658,19 @@ struct KsumArgs {
   int64_t ldr;
   float* aux;
   int64_t ldaux;
+  float* ws;   // split-K partial sums (SPLIT): splits x m x n, slice-major
+  int chunk;   // K steps per slice (SPLIT)
   KsumPair t[kKsumMax];
 };
 static_assert(sizeof(KsumArgs) <= 4096, "kernel arguments over 4 KB");
 
 // TB: B_t is stored [n][k_t] (B_t^T in HBM, K-contiguous, the linear
 // layers' input gradients dX = sum_t dY_t W_t^T) instead of [k_t][n].
-template <int BM, int BN, int BK, bool TB>
+// SPLIT: the grid holds nb x splits blocks; slice z sums the K steps
+// [z * chunk, (z + 1) * chunk) of the concatenated pair list into its own
+// m x n region of P.ws (no epilogue); gemm_split_finish adds the slices in
+// slice order and applies alpha, beta and the epilogue.
+template <int BM, int BN, int BK, bool TB, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void gemm_ksum_kernel(KsumArgs P) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int FM = WM / 32, FN = WN / 32;
@@ -684,8 +690,14 @@ __global__ __launch_bounds__(256, 2) void gemm_ksum_kernel(KsumArgs P) {
   const int nb = grid_m * grid_n;
   int b = blockIdx.x;
   {
-    const int per = nb / 8, rem = nb % 8, x = b % 8;
+    const int tot = (int)gridDim.x;  // nb, or nb x splits
+    const int per = tot / 8, rem = tot % 8, x = b % 8;
     b = x * per + min(x, rem) + b / 8;
+  }
+  int split = 0;
+  if (SPLIT) {  // consecutive blocks on an XCD: one slice, neighbouring C tiles
+    split = b / nb;
+    b -= split * nb;
   }
   constexpr int GROUP = 8;
   const int in_group = GROUP * grid_n;
@@ -694,7 +706,8 @@ __global__ __launch_bounds__(256, 2) void gemm_ksum_kernel(KsumArgs P) {
   const int tm = first_m + (b % in_group) % gsz;
   const int tn = (b % in_group) / gsz;
   const int m0 = tm * BM, n0 = tn * BN;
-  const int nk = P.nk;
+  const int kbeg = SPLIT ? split * P.chunk : 0;
+  const int nk = SPLIT ? min(P.nk - kbeg, P.chunk) : P.nk;  // steps of this block
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -728,7 +741,7 @@ __global__ __launch_bounds__(256, 2) void gemm_ksum_kernel(KsumArgs P) {
   int64_t before = 0;
   f32x4 ra0[A_PT], rb0[B_PT], ra1[A_PT], rb1[B_PT];
   auto gload = [&](int st, f32x4(&ra)[A_PT], f32x4(&rb)[B_PT]) {
-    st = min(st, nk - 1);
+    st = kbeg + min(st, nk - 1);
     while (st >= before + P.t[cur].steps) before += P.t[cur++].steps;
     const int k0 = (int)(st - before) * BK;
     const float* pa = P.t[cur].A + (int64_t)m0 * P.lda + k0;
@@ -819,6 +832,21 @@ __global__ __launch_bounds__(256, 2) void gemm_ksum_kernel(KsumArgs P) {
     if (kt < nk) compute(0);
   }
 
+  if (SPLIT) {
+    float* w = P.ws + (int64_t)split * P.m * P.n;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = n0 + wn * WN + j * 32 + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          w[(int64_t)row * P.n + col] = acc[i][j][r];
+        }
+      }
+    return;
+  }
   GemmArgs g{};
   g.beta = P.beta;
   g.C = P.C;
@@ -956,10 +984,45 @@ int ksum_big_bk(int64_t blocks128) {
 
 }  // namespace
 
+namespace {
+
+// Split-K K-sums: outputs of fewer than 256 blocks of 128 x 128 (m and n
+// multiples of 128) with a workspace split the concatenated K steps (BK 32)
+// into slices so that blocks x slices comes to about 512 (two workgroups per
+// CU), at most 16 slices of at least 16 steps each.
+constexpr int kKsumSplitMax = 16, kKsumSplitMinSteps = 16;
+bool ksum_split_shape(int64_t m, int64_t n) {
+  return m % 128 == 0 && n % 128 == 0 && (m / 128) * (n / 128) < 256;
+}
+int ksum_splits(int64_t m, int64_t n, int64_t steps, size_t ws_bytes) {
+  const int64_t b128 = (m / 128) * (n / 128);
+  int64_t sp = std::min<int64_t>(kKsumSplitMax, std::max<int64_t>(1, 512 / b128));
+  sp = std::min<int64_t>(sp, steps / kKsumSplitMinSteps);
+  sp = std::min<int64_t>(sp, (int64_t)(ws_bytes / ((size_t)m * n * sizeof(float))));
+  return (int)std::max<int64_t>(1, sp);
+}
+
+}  // namespace
+
+extern "C" size_t tile_gemm_ksum_workspace(int64_t m, int64_t n) {
+  if (m <= 0 || n <= 0 || !ksum_split_shape(m, n)) return 0;
+  const int64_t b128 = (m / 128) * (n / 128);
+  return (size_t)std::min<int64_t>(kKsumSplitMax, std::max<int64_t>(1, 512 / b128)) * m * n * sizeof(float);
+}
+
 extern "C" int tile_gemm_ksum_ex(void* stream, int count, int transB, int64_t m, int64_t n, const int64_t* k,
                                  float alpha, const float* const* A, const int64_t* lda, const float* const* B,
                                  const int64_t* ldb, float beta, float* C, int64_t ldc, int epilogue,
                                  const float* bias, const float* res, int64_t ldr, float* aux, int64_t ldaux) {
+  return tile_gemm_ksum_ws(stream, count, transB, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, epilogue, bias, res,
+                           ldr, aux, ldaux, nullptr, 0);
+}
+
+extern "C" int tile_gemm_ksum_ws(void* stream, int count, int transB, int64_t m, int64_t n, const int64_t* k,
+                                 float alpha, const float* const* A, const int64_t* lda, const float* const* B,
+                                 const int64_t* ldb, float beta, float* C, int64_t ldc, int epilogue,
+                                 const float* bias, const float* res, int64_t ldr, float* aux, int64_t ldaux,
+                                 void* workspace, size_t workspace_bytes) {
   using tt::fail;
   if (count < 0 || m < 0 || n < 0) return fail(TT_ERR_ARG, "tile_gemm_ksum: negative count or size");
   if (m == 0 || n == 0) return TT_OK;
@@ -979,12 +1042,18 @@ extern "C" int tile_gemm_ksum_ex(void* stream, int count, int transB, int64_t m,
     if (k[t] > 0 && (!A[t] || !B[t] || lda[t] < k[t] || ldb[t] < (transB ? k[t] : n)))
       return fail(TT_ERR_ARG, "tile_gemm_ksum: bad operand of pair %d", t);
   }
+  if (workspace_bytes > 0 && (!workspace || !aligned16(workspace)))
+    return fail(TT_ERR_ARG, "tile_gemm_ksum: null or misaligned workspace");
   hipStream_t s = tt::as_stream(stream);
-  // the plan tile_gemm would pick for one pair (no split): 128x128 blocks
-  // when there are >= 512 of them, else 64x64x32
+  // block plan: 128x128 blocks when there are >= 512 of them; split-K over
+  // 128x128x32 blocks for fewer than 256 with a workspace; else 64x64x32
   const int64_t b128 = (m / 128) * (n / 128);
   const bool big = b128 >= 512;
-  const int bm = big ? 128 : 64, bn = big ? 128 : 64, bk = big ? ksum_big_bk(b128) : 32;
+  int64_t total_steps = 0;
+  for (int t = 0; t < count; ++t) total_steps += k[t] / 32;
+  const bool try_split = !big && workspace && ksum_split_shape(m, n) &&
+                         ksum_splits(m, n, total_steps, workspace_bytes) > 1;
+  const int bm = big || try_split ? 128 : 64, bn = bm, bk = big ? ksum_big_bk(b128) : 32;
   auto fits = [&](int t) {  // a pair the branch-free long-K launch can take
     return k[t] % bk == 0 && m % bm == 0 && n % bn == 0 && aligned16(A[t]) && aligned16(B[t]) && lda[t] % 4 == 0 &&
            ldb[t] % 4 == 0 && (int64_t)bm * lda[t] < INT32_MAX && (int64_t)(transB ? bn : bk) * ldb[t] < INT32_MAX;
@@ -1043,17 +1112,35 @@ extern "C" int tile_gemm_ksum_ex(void* stream, int count, int transB, int64_t m,
     }
     if (steps > INT32_MAX) return fail(TT_ERR_ARG, "tile_gemm_ksum: K too long");
     P.nk = (int)steps;
-    const dim3 grid((unsigned)((m / bm) * (n / bn)));
-    if (transB) {
-      if (big && bk == 32) hipLaunchKernelGGL((gemm_ksum_kernel<128, 128, 32, true>), grid, dim3(256), 0, s, P);
-      else if (big) hipLaunchKernelGGL((gemm_ksum_kernel<128, 128, 16, true>), grid, dim3(256), 0, s, P);
-      else hipLaunchKernelGGL((gemm_ksum_kernel<64, 64, 32, true>), grid, dim3(256), 0, s, P);
+    const int splits = try_split ? ksum_splits(m, n, steps, workspace_bytes) : 1;
+    if (splits > 1) {
+      P.ws = (float*)workspace;
+      P.chunk = (int)((steps + splits - 1) / splits);
+      const int used = (int)((steps + P.chunk - 1) / P.chunk);  // every slice non-empty
+      const dim3 grid((unsigned)(b128 * used));
+      if (transB) hipLaunchKernelGGL((gemm_ksum_kernel<128, 128, 32, true, true>), grid, dim3(256), 0, s, P);
+      else hipLaunchKernelGGL((gemm_ksum_kernel<128, 128, 32, false, true>), grid, dim3(256), 0, s, P);
+      if (int rc = tt::launch_status("tile_gemm_ksum(split)")) return rc;
+      GemmArgs g{(int)m, (int)n, 0, alpha, b, nullptr, nullptr, C, 0, 0, ldc, epilogue, bias, res, ldr, aux, ldaux,
+                 (float*)workspace, used, 0};
+      const int64_t mn = m * n;  // a multiple of 128 x 128
+      hipLaunchKernelGGL(gemm_split_finish<4>, dim3((unsigned)((mn / 4 + 255) / 256)), dim3(256), 0, s, g);
+      if (int rc = tt::launch_status("tile_gemm_ksum(split finish)")) return rc;
     } else {
-      if (big && bk == 32) hipLaunchKernelGGL((gemm_ksum_kernel<128, 128, 32, false>), grid, dim3(256), 0, s, P);
-      else if (big) hipLaunchKernelGGL((gemm_ksum_kernel<128, 128, 16, false>), grid, dim3(256), 0, s, P);
-      else hipLaunchKernelGGL((gemm_ksum_kernel<64, 64, 32, false>), grid, dim3(256), 0, s, P);
+      const dim3 grid((unsigned)((m / bm) * (n / bn)));
+      if (transB) {
+        if (big && bk == 32) hipLaunchKernelGGL((gemm_ksum_kernel<128, 128, 32, true, false>), grid, dim3(256), 0, s, P);
+        else if (big) hipLaunchKernelGGL((gemm_ksum_kernel<128, 128, 16, true, false>), grid, dim3(256), 0, s, P);
+        else if (bm == 128) hipLaunchKernelGGL((gemm_ksum_kernel<128, 128, 32, true, false>), grid, dim3(256), 0, s, P);
+        else hipLaunchKernelGGL((gemm_ksum_kernel<64, 64, 32, true, false>), grid, dim3(256), 0, s, P);
+      } else {
+        if (big && bk == 32) hipLaunchKernelGGL((gemm_ksum_kernel<128, 128, 32, false, false>), grid, dim3(256), 0, s, P);
+        else if (big) hipLaunchKernelGGL((gemm_ksum_kernel<128, 128, 16, false, false>), grid, dim3(256), 0, s, P);
+        else if (bm == 128) hipLaunchKernelGGL((gemm_ksum_kernel<128, 128, 32, false, false>), grid, dim3(256), 0, s, P);
+        else hipLaunchKernelGGL((gemm_ksum_kernel<64, 64, 32, false, false>), grid, dim3(256), 0, s, P);
+      }
+      if (int rc = tt::launch_status("tile_gemm_ksum")) return rc;
     }
-    if (int rc = tt::launch_status("tile_gemm_ksum")) return rc;
     b = 1.f;
     wrote = true;
   }

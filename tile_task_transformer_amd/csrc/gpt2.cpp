@@ -190,7 +190,7 @@ int submit_ksum_tb(tt_ctx* ctx, const char* label, TileRef C, const std::vector<
     T.push_back(ta(As[u]));
     T.push_back(ta(Bs[u]));
   }
-  const tt_op_gemm sc{0, 1, TT_EPI_NONE, 1.f, 0.f, 0};
+  const tt_op_gemm sc{0, 1, TT_EPI_NONE, 1.f, 0.f, 1};
   return submit_op(ctx, TT_OP_GEMM_KSUM, T.data(), (int)T.size(), &sc, sizeof(sc), label, false);
 }
 
@@ -236,10 +236,11 @@ int submit_ksum(tt_ctx* ctx, const char* label, int tb, TileRef C, const std::ve
 //  * 512..1023: it loses (MLP output layer 65.5 -> 70.5 ms, fc input gradient
 //    65.1 -> 73.9, attention projection 18.3 -> 18.5): every link of the
 //    chain already runs a long K loop;
-//  * fewer: the long-K launch takes it when its 64x64 blocks fill the CUs
-//    (the small-tile model's MLP input layer, 1024 x 2048: 66 % of the
-//    fp32 peak); narrower outputs (1024 x 512: 128 blocks, 31 % as one long-K
-//    launch) stay chains, whose links split K over the CUs.
+//  * fewer: the long-K launch takes it, split over K into slices through
+//    the stream workspace when there are fewer than 256 blocks of 128 x 128
+//    (the small-tile model's 1024 x 512 outputs: 32 blocks x 16 slices),
+//    else with 64x64 blocks; one launch and a slice sum per task against
+//    one launch per contraction tile.
 // TT_KSUM_CLASSES="qkv,fc,..." forces the given task classes to K-sum tasks
 // and every other class to chains (tuning).
 bool use_ksum(const char* label, const TileRef& C) {
@@ -253,8 +254,8 @@ bool use_ksum(const char* label, const TileRef& C) {
   if (mode == 1) return set.find(std::string(",") + label + ",") != std::string::npos;
   int64_t r, c;
   C.t->mat(C.lin, &r, &c);
-  const int64_t nb = (r / 128) * (c / 128), nb64 = (r / 64) * (c / 64);
-  return nb >= 1024 || (nb < 512 && nb64 >= 256);
+  const int64_t nb = (r / 128) * (c / 128);
+  return nb >= 1024 || nb < 512;
 }
 
 // tiles = value, TT_FILL_MAX_TILES tiles per task and launch (with
@@ -509,6 +510,9 @@ extern "C" int tt_gpt2_create(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_g
   ws = std::max(ws, tile_reduce_rows_workspace(G->rows, std::min<int64_t>(15, 3 * G->NH) * ht * hd));
   // dS of one attention tile pair (the backward's dK/dV kernel hands it to the dQ kernel)
   ws = std::max(ws, tile_attention_bwd_workspace(bt, ht, sq, sq));
+  // K slices of the linear layers' long-K sums over token-tile outputs
+  for (int64_t cols : {et, std::min<int64_t>(it, I), ht * hd, vt})
+    ws = std::max(ws, tile_gemm_ksum_workspace(G->rows, cols));
   {
     // split-K slices of the step's GEMM shapes (m, n, k), capped at 256 MiB per stream
     const int64_t r = G->rows, e = et, in = std::min<int64_t>(it, I), hw = ht * hd, vv = vt;
@@ -1005,7 +1009,7 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
           T.push_back({g->z, L(g->z, {bi, si, vj})});
           T.push_back({wte, L(wte, {vj, ek})});
         }
-        const tt_op_gemm sc{0, 0, TT_EPI_NONE, 1.f, 0.f, 0};
+        const tt_op_gemm sc{0, 0, TT_EPI_NONE, 1.f, 0.f, 1};
         TRY(submit_op(ctx, TT_OP_GEMM_KSUM, T.data(), (int)T.size(), &sc, sizeof(sc), "head_dx", false));
       }
   // zero the LayerNorm and position gradients, which accumulate (over

@@ -803,6 +803,11 @@ int tt_ctx::prof_collect() {
   for (auto& r : prof_pending) {
     float ms = 0.f;
     TT_HIP_TRY(hipEventElapsedTime(&ms, prof_events[r.ev0], prof_events[r.ev1]));
+    if (prof_base_set) {
+      float t0 = 0.f;
+      TT_HIP_TRY(hipEventElapsedTime(&t0, prof_base, prof_events[r.ev0]));
+      prof_iv.push_back({t0, t0 + ms});
+    }
     ProfAgg* a = nullptr;
     for (auto& p : prof_agg)
       if (p.first == r.label) a = &p.second;
@@ -865,6 +870,7 @@ int tt_ctx_destroy(tt_ctx* c) {
       if (p) (void)hipFree(p);
     for (auto e : c->events) (void)hipEventDestroy(e);
     for (auto e : c->prof_events) (void)hipEventDestroy(e);
+    if (c->prof_base) (void)hipEventDestroy(c->prof_base);
     for (auto e : c->ext_events) (void)hipEventDestroy(e);
     for (auto s : c->streams) (void)hipStreamDestroy(s);
     if (c->copy_stream) (void)hipStreamDestroy(c->copy_stream);
@@ -904,10 +910,50 @@ int tt_ctx_record(tt_ctx* c, int on) {
 int tt_ctx_profile(tt_ctx* c, const char* label_filter) {
   if (!c) return fail(TT_ERR_ARG, "tt_ctx_profile: null");
   if (c->capturing) return fail(TT_ERR_STATE, "tt_ctx_profile: a graph is being captured");
-  if (int rc = c->flush()) return rc;
+  // drain first: the reference event below then precedes every timed task
+  // on every stream
+  if (int rc = c->wait_all()) return rc;
   c->prof_on = label_filter != nullptr;
   c->prof_filter = label_filter ? label_filter : "";
   c->prof_seen = 0;
+  c->prof_iv.clear();
+  c->prof_base_set = false;
+  if (c->prof_on && !c->dryrun) {
+    if (!c->prof_base) TT_HIP_TRY(hipEventCreateWithFlags(&c->prof_base, hipEventDisableSystemFence));
+    TT_HIP_TRY(hipEventRecord(c->prof_base, c->streams[0]));
+    c->prof_base_set = true;
+  }
+  return TT_OK;
+}
+
+int tt_profile_busy(tt_ctx* c, double* busy_ms, double* span_ms, int64_t* n_tasks) {
+  clear_error();
+  if (!c || !busy_ms || !span_ms || !n_tasks) return fail(TT_ERR_ARG, "tt_profile_busy: bad argument");
+  if (int rc = c->wait_all()) return rc;
+  auto& iv = c->prof_iv;
+  std::sort(iv.begin(), iv.end());
+  double busy = 0, lo = 0, hi = 0, first = 0, last = 0;
+  for (size_t i = 0; i < iv.size(); ++i) {
+    const double a = iv[i].first, b = std::max(iv[i].first, iv[i].second);
+    if (i == 0) {
+      lo = first = a;
+      hi = last = b;
+      continue;
+    }
+    last = std::max(last, b);
+    if (a > hi) {
+      busy += hi - lo;
+      lo = a;
+      hi = b;
+    } else {
+      hi = std::max(hi, b);
+    }
+  }
+  if (!iv.empty()) busy += hi - lo;
+  *busy_ms = busy;
+  *span_ms = iv.empty() ? 0.0 : last - first;
+  *n_tasks = (int64_t)iv.size();
+  iv.clear();
   return TT_OK;
 }
 

@@ -202,6 +202,9 @@ struct tt_ctx {
   std::vector<ProfRec> prof_pending;
   std::vector<hipEvent_t> prof_events;
   int prof_used = 0;
+  hipEvent_t prof_base = nullptr;      // recorded by tt_ctx_profile on an idle device
+  bool prof_base_set = false;
+  std::vector<std::pair<float, float>> prof_iv;  // [start, end] of each timed task, ms after prof_base
   struct ProfAgg {
     int64_t count = 0;
     double total = 0, mn = 1e30, mx = 0;

@@ -166,7 +166,7 @@ int op_gemm_batch(tt_ctx* ctx, const TileArg* T, int n, const tt_op_gemm& q, con
   }, flops);
 }
 
-int op_gemm_ksum(tt_ctx* ctx, const TileArg* T, int n, const tt_op_gemm& q, const char* label) {
+int op_gemm_ksum(tt_ctx* ctx, const TileArg* T, int n, const tt_op_gemm& q, const char* label, bool grow) {
   const char* nm = "TT_OP_GEMM_KSUM";
   const int epi = q.epilogue;
   if (q.transA) return fail(TT_ERR_ARG, "%s: transA must be 0", nm);
@@ -227,6 +227,8 @@ int op_gemm_ksum(tt_ctx* ctx, const TileArg* T, int n, const tt_op_gemm& q, cons
   if (has_bias) acc.push_back(acc_of(bias, TT_R));
   if (has_res) acc.push_back(acc_of(res, TT_R));
   if (has_aux) acc.push_back(acc_of(aux, gelu ? (q.beta == 0.f ? TT_W : TT_RW) : TT_R));
+  if (q.split_k && grow)
+    if (int rc = ctx->ensure_workspace(std::min(kSplitCap, tile_gemm_ksum_workspace(dr, dc)))) return rc;
   std::vector<TileArg> tl(T, T + n);
   const tt_op_gemm p = q;
   return ctx->submit(label ? label : "gemm_ksum", std::move(acc), [=](hipStream_t s, void* ws) {
@@ -238,8 +240,10 @@ int op_gemm_ksum(tt_ctx* ctx, const TileArg* T, int n, const tt_op_gemm& q, cons
     float* bp = has_bias ? Fp(bias) : nullptr;
     float* rp = has_res ? Fp(res) : nullptr;
     float* xp = has_aux ? Fp(aux) : nullptr;
-    const int rc = tile_gemm_ksum_ex(s, cnt, p.transB, dr, dc, ks.data(), p.alpha, A.data(), lda.data(), B.data(),
-                                     ldb.data(), p.beta, Fp(tl[0]), dc, p.epilogue, bp, rp, ldr, xp, ldaux);
+    const bool split = p.split_k && ws;
+    const int rc = tile_gemm_ksum_ws(s, cnt, p.transB, dr, dc, ks.data(), p.alpha, A.data(), lda.data(), B.data(),
+                                     ldb.data(), p.beta, Fp(tl[0]), dc, p.epilogue, bp, rp, ldr, xp, ldaux,
+                                     split ? ws : nullptr, split ? ctx->workspace_bytes : 0);
     if (rc != TT_ERR_UNSUPPORTED) return rc;
     // the epilogue could not be fused into one long-K launch: a chain of
     // accumulating products inside this task, the residual with the first,
@@ -1012,7 +1016,7 @@ int submit_op(tt_ctx* ctx, int op, const TileArg* T, int n, const void* sc, size
       if (int rc = scal(sc, size, "TT_OP_GEMM*", &q)) return rc;
       if (op == TT_OP_GEMM) return op_gemm(ctx, T, n, q, label, grow);
       if (op == TT_OP_GEMM_BATCH) return op_gemm_batch(ctx, T, n, q, label, grow);
-      return op_gemm_ksum(ctx, T, n, q, label);
+      return op_gemm_ksum(ctx, T, n, q, label, grow);
     }
     case TT_OP_LAYERNORM_FWD:
     case TT_OP_LAYERNORM_BWD: {

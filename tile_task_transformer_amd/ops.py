@@ -17,7 +17,7 @@ __all__ = [
     "tile_gemm_batch_workspace", "tile_gemm_ksum_ex", "tile_layernorm_fwd",
     "tile_layernorm_bwd", "tile_layernorm_bwd_workspace", "tile_softmax",
     "tile_xentropy", "tile_xentropy_multi", "tile_attention_fwd", "tile_attention_bwd",
-    "tile_attention_bwd_workspace", "tile_attention_bwd_ws", "tile_fused_adamw",
+    "tile_attention_bwd_workspace", "tile_attention_bwd_ws", "tile_gemm_ksum_workspace", "tile_fused_adamw",
     "tile_fused_adamw_multi",
     "tile_adamw_advance", "tile_sgd", "tile_sgd_multi",
     "tile_embedding_fwd", "tile_embedding_index", "tile_embedding_bwd", "tile_reduce_rows",
@@ -58,15 +58,22 @@ def tile_gemm_ksum(stream, m, n, ks, alpha, As, ldas, Bs, ldbs, beta, C, ldc, tr
 
 
 def tile_gemm_ksum_ex(stream, m, n, ks, alpha, As, ldas, Bs, ldbs, beta, C, ldc, transB=0, epilogue=TT_EPI_NONE,
-                      bias=None, res=None, ldr=0, aux=None, ldaux=0):
-    """tile_gemm_ksum followed by tile_gemm's epilogue on the whole sum."""
+                      bias=None, res=None, ldr=0, aux=None, ldaux=0, workspace=None, workspace_bytes=0):
+    """tile_gemm_ksum followed by tile_gemm's epilogue on the whole sum;
+    with a workspace, tile_gemm_ksum_ws (split K for outputs of few blocks)."""
     import ctypes as C_
     cnt = len(As)
     i64 = lambda xs: (C_.c_int64 * max(cnt, 1))(*[int(x) for x in xs])  # noqa: E731
     ptrs = lambda xs: (C_.c_void_p * max(cnt, 1))(*[ptr(x) for x in xs])  # noqa: E731
-    return check(lib.tile_gemm_ksum_ex(stream_handle(stream), cnt, transB, m, n, i64(ks), alpha, ptrs(As), i64(ldas),
-                                       ptrs(Bs), i64(ldbs), beta, ptr(C), ldc, epilogue, ptr(bias), ptr(res), ldr,
-                                       ptr(aux), ldaux))
+    args = (stream_handle(stream), cnt, transB, m, n, i64(ks), alpha, ptrs(As), i64(ldas), ptrs(Bs), i64(ldbs), beta,
+            ptr(C), ldc, epilogue, ptr(bias), ptr(res), ldr, ptr(aux), ldaux)
+    if workspace is None:
+        return check(lib.tile_gemm_ksum_ex(*args))
+    return check(lib.tile_gemm_ksum_ws(*args, ptr(workspace), workspace_bytes))
+
+
+def tile_gemm_ksum_workspace(m, n):
+    return lib.tile_gemm_ksum_workspace(m, n)
 
 
 def _batch_args(ms, ns, As, ldas, Bs, ldbs, Cs, ldcs):

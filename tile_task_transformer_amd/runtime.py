@@ -132,6 +132,14 @@ class Context:
                                             max_ms=buf[i].max_ms) for i in range(min(n.value, 256))}
 
 
+    def profile_busy(self) -> dict:
+        """Wait; {busy_ms, span_ms, tasks} of the tasks timed since profile()
+        (busy = union of their GPU intervals), and clear them."""
+        busy, span, n = C.c_double(), C.c_double(), C.c_int64()
+        check(lib.tt_profile_busy(self.h, C.byref(busy), C.byref(span), C.byref(n)))
+        return dict(busy_ms=busy.value, span_ms=span.value, tasks=n.value)
+
+
 class Tensor:
     def __init__(self, ctx: Context, shape, tile, dtype=L.TT_F32, home=L.TT_HOME_DEVICE, handle=None):
         self.ctx = ctx
