@@ -109,6 +109,21 @@ def class_work(s) -> dict:
     return out
 
 
+# share of each memory class's algorithmic bytes that are writes: LayerNorm
+# forward reads x and writes y; its backward reads dy, x and the dx it adds
+# to and writes dx; the statistics and column sums only read; the gradient
+# of the logits reads z and writes dz; AdamW reads p, g, m, v and writes p,
+# m, v
+WRITE_SHARE = {"ln_fwd": 0.5, "ln_bwd": 0.25, "ce_stats": 0.0, "ce_grad": 0.5, "colsum": 0.0, "adamw": 3 / 7}
+
+
+def hbm_ceiling(probe: dict, write_share: float) -> float:
+    """Stream-probe rate for a traffic mix (GB/s): the read probe for pure
+    reads, the 1:1 copy probe at half writes, linear in between."""
+    r, c = probe["hbm_read_GBps"], probe["hbm_copy_GBps_lib"]
+    return r + (c - r) * min(write_share, 0.5) / 0.5
+
+
 # task labels whose kernels together do one class's work (LayerNorm over
 # several embd tiles runs as partial statistics, merge and apply tasks)
 CLASS_LABELS = {"ln_fwd": ("ln_fwd", "ln_part", "ln_merge", "ln_apply"), "ln_bwd": ("ln_bwd", "lnb_part", "lnb_apply")}
@@ -446,8 +461,9 @@ def cpu_baseline(w, params, tokens, sample_tokens: int = 0):
 
 def probes() -> dict:
     """On-device ceilings, in the benchmark's own process: the fp32 matrix
-    peak (a launch of the library's MFMA probe, best of 3) and the rate of a
-    2 GiB device-to-device copy (torch's copy kernel, best of 3)."""
+    peak (a launch of the library's MFMA probe, best of 4), the rate of a
+    2 GiB device-to-device copy (torch's copy kernel, best of 4) and the
+    library's HBM stream probes over the same 2 GiB (read, write, copy)."""
     import torch
 
     import tile_task_transformer_amd as tt
@@ -474,9 +490,23 @@ def probes() -> dict:
         b.record(st)
         b.synchronize()
         cbest = min(cbest, a.elapsed_time(b))
+    # the library's stream probes: read, write and 1:1 copy, each the best
+    # over grid sizes and store kinds
+    hbm = {}
+    for name, kind in (("read", tt.TT_PROBE_READ), ("write", tt.TT_PROBE_WRITE), ("copy", tt.TT_PROBE_COPY)):
+        rate = 0.0
+        for nt in (0, tt.TT_PROBE_NONTEMPORAL):
+            for blocks in (1024, 2048, 4096, 8192):
+                for _ in range(3):
+                    a.record(st)
+                    moved = tt.tt_probe_hbm(st, kind | nt, src, dst, n, blocks)
+                    b.record(st)
+                    b.synchronize()
+                    rate = max(rate, moved / (a.elapsed_time(b) * 1e-3) / 1e9)
+        hbm[f"hbm_{name}_GBps" + ("_lib" if name == "copy" else "")] = round(rate, 1)
     del src, dst, out
     return {"mfma_f32_tflops": round(mfma, 2), "mfma_f32_frac_of_spec": round(mfma / MFMA_FP32_PEAK, 4),
-            "hbm_copy_GBps": round(2 * 4 * n / (cbest * 1e-3) / 1e9, 1)}
+            "hbm_copy_GBps": round(2 * 4 * n / (cbest * 1e-3) / 1e9, 1), **hbm}
 
 
 def main(argv=None):
@@ -593,13 +623,22 @@ def run(w, a, streams, breakdown_path, probe, steps=None, warmup=None, want_para
     ctx.profile(None)
     ctx.streams_active(streams)
     classes = class_rooflines(breakdown, s)
+    if probe:
+        # matrix classes against the measured matrix peak; memory classes
+        # against the stream probe of their traffic mix
+        for k, v in classes.items():
+            if v["bound"] == "mfma":
+                v["frac_of_probe"] = round(v["achieved"] / probe["mfma_f32_tflops"], 4)
+            elif k in WRITE_SHARE:
+                v["frac_of_probe"] = round(v["achieved"] / hbm_ceiling(probe, WRITE_SHARE[k]), 4)
     if breakdown_path:
         os.makedirs(os.path.dirname(breakdown_path) or ".", exist_ok=True)
         with open(breakdown_path, "w") as f:
             json.dump({"workload": w.name, "tasks": breakdown, "classes": classes}, f, indent=1, sort_keys=True)
-    print(f"[bench] {w.name}: serialized step by class (ms, achieved, % of roofline):", file=sys.stderr)
+    print(f"[bench] {w.name}: serialized step by class (ms, achieved, % of roofline, % of probe):", file=sys.stderr)
     for k, v in sorted(classes.items(), key=lambda kv: -kv[1]["ms"]):
-        print(f"  {k:14s} {v['ms']:9.2f} ms  {v['achieved']:9.1f} {v['unit']:8s} {100 * v['frac']:5.1f}%",
+        fp = f"{100 * v['frac_of_probe']:5.1f}%" if "frac_of_probe" in v else ""
+        print(f"  {k:14s} {v['ms']:9.2f} ms  {v['achieved']:9.1f} {v['unit']:8s} {100 * v['frac']:5.1f}%  {fp}",
               file=sys.stderr)
     print(f"  serialized total {sum(b['total_ms'] for b in breakdown.values()):.2f} ms", file=sys.stderr,
           flush=True)
@@ -667,7 +706,7 @@ def run(w, a, streams, breakdown_path, probe, steps=None, warmup=None, want_para
         out["residency"]["link_GBps"] = round((st["h2d_bytes"] + st["d2h_bytes"]) / elapsed / 1e9, 2)
         out["residency"]["budget_gb"] = a.budget_gb
         out["residency"]["probe"] = link_probe()
-    out["classes"] = {k: {"frac": v["frac"], "achieved": v["achieved"], "unit": v["unit"], "ms": v["ms"]}
+    out["classes"] = {k: {x: v[x] for x in ("frac", "frac_of_probe", "achieved", "unit", "ms") if x in v}
                       for k, v in classes.items()}
     print(f"[bench] {w.name}: timed {steps} steps: {ms:.2f} ms/step, {tok_s:.0f} tokens/s, {tflops:.1f} TFLOP/s",
           file=sys.stderr, flush=True)

@@ -69,6 +69,23 @@ const char* tt_version(void);
  * TT_ERR_ARG for blocks outside 1..65535, iters outside 1..2^24 or a null
  * out. Asynchronous on `stream`. */
 int tt_probe_mfma_f32(void* stream, int64_t blocks, int64_t iters, float* out, double* flops);
+/* tt_probe_hbm -- device bandwidth probe, not part of the step: one
+ * grid-stride pass of `blocks` workgroups (256 threads, 16-byte accesses)
+ * over n floats. mode TT_PROBE_READ sums src (n floats) and writes one sum
+ * per thread to dst (blocks * 256 floats); TT_PROBE_WRITE fills dst (n
+ * floats) with a constant; TT_PROBE_COPY copies src to dst (n floats each).
+ * | TT_PROBE_NONTEMPORAL makes the loads and stores non-temporal. *bytes (host, may be
+ * NULL) receives the bytes moved: 4n, or 8n for a copy. The launch time
+ * gives the practical HBM rate of each traffic mix (published MI355X
+ * figure: 8 TB/s). TT_ERR_ARG for an unknown mode, n not a multiple of 4,
+ * blocks outside 1..65535, a null or misaligned buffer. Asynchronous on
+ * `stream`. */
+#define TT_PROBE_READ  0
+#define TT_PROBE_WRITE 1
+#define TT_PROBE_COPY  2
+#define TT_PROBE_NONTEMPORAL 4
+int tt_probe_hbm(void* stream, int mode, const float* src, float* dst, int64_t n, int64_t blocks,
+                 double* bytes);
 
 /* ============================================================ 1. tile ops */
 

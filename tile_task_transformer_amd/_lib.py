@@ -36,6 +36,7 @@ TT_SM_STATS, TT_SM_MERGE, TT_SM_APPLY = 0, 1, 2
 TT_XE_LOSS, TT_XE_GRAD, TT_XE_STATS = 0, 1, 2
 TT_ATT_PREP, TT_ATT_GRAD = 0, 1
 TT_EMB_TOKEN, TT_EMB_POS = 0, 1
+TT_PROBE_READ, TT_PROBE_WRITE, TT_PROBE_COPY, TT_PROBE_NONTEMPORAL = 0, 1, 2, 4
 TT_MAX_DIMS = 6
 TT_F32, TT_I32 = 0, 1
 TT_HOME_DEVICE, TT_HOME_PINNED_HOST = 0, 1
@@ -141,6 +142,7 @@ SIGNATURES = {
     "tt_last_error": (C.c_char_p, []),
     "tt_version": (C.c_char_p, []),
     "tt_probe_mfma_f32": (I, [P, I64, I64, P, C.POINTER(C.c_double)]),
+    "tt_probe_hbm": (I, [P, I, P, P, I64, I64, C.POINTER(C.c_double)]),
     "tile_gemm": (I, [P, I, I, I64, I64, I64, F, P, I64, P, I64, F, P, I64, I, P, P, I64, P, I64]),
     "tile_gemm_ws": (I, [P, I, I, I64, I64, I64, F, P, I64, P, I64, F, P, I64, I, P, P, I64, P, I64, P, SZ]),
     "tile_gemm_workspace": (SZ, [I64, I64, I64]),

@@ -493,18 +493,21 @@ __global__ __launch_bounds__(BT) void ln_fwd_multi(int rows, int rows_per_block,
   const int r0 = blockIdx.x * rows_per_block, r1 = min(rows, r0 + rows_per_block);
   // the next row's loads are issued before this row's reductions (the
   // barriers wait for LDS only), so they overlap the compute and stores
+  // x is read once: non-temporal loads (y stays a plain store: the next
+  // GEMM reads it)
   f32x4 v[VPT];
 #pragma unroll
   for (int k = 0; k < VPT; ++k)
-    v[k] = ok[k] && r0 < r1 ? *reinterpret_cast<const f32x4*>(xp[k] + (int64_t)r0 * ld[k])
+    v[k] = ok[k] && r0 < r1 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(xp[k] + (int64_t)r0 * ld[k]))
                             : f32x4{0.f, 0.f, 0.f, 0.f};
   for (int r = r0; r < r1; ++r) {
     f32x4 nx[VPT];
     const bool more = r + 1 < r1;
 #pragma unroll
     for (int k = 0; k < VPT; ++k)
-      nx[k] = ok[k] && more ? *reinterpret_cast<const f32x4*>(xp[k] + (int64_t)(r + 1) * ld[k])
-                            : f32x4{0.f, 0.f, 0.f, 0.f};
+      nx[k] = ok[k] && more
+                  ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(xp[k] + (int64_t)(r + 1) * ld[k]))
+                  : f32x4{0.f, 0.f, 0.f, 0.f};
     float s = 0.f, unused = 0.f;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) s += (v[k][0] + v[k][1]) + (v[k][2] + v[k][3]);
@@ -575,9 +578,9 @@ __global__ __launch_bounds__(BT) void ln_bwd_multi(int rows, int rows_per_block,
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       f32x4 xv = f32x4{0.f, 0.f, 0.f, 0.f}, dv = xv;
-      if (ok[k]) {
-        xv = *reinterpret_cast<const f32x4*>(xp[k] + (int64_t)r * ld[k]);
-        dv = *reinterpret_cast<const f32x4*>(dyp[k] + (int64_t)r * ld[k]);
+      if (ok[k]) {  // x, dy and dx are each read or written once: non-temporal accesses
+        xv = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(xp[k] + (int64_t)r * ld[k]));
+        dv = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(dyp[k] + (int64_t)r * ld[k]));
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -598,8 +601,8 @@ __global__ __launch_bounds__(BT) void ln_bwd_multi(int rows, int rows_per_block,
         f32x4 o;
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = rstd * (dxh[k][i] - a1 - xh[k][i] * a2);
-        if (dx_acc) o += *reinterpret_cast<const f32x4*>(q);
-        *reinterpret_cast<f32x4*>(q) = o;
+        if (dx_acc) o += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(q));
+        __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(q));
       }
   }
   float* out = ws + (int64_t)blockIdx.x * 2 * P.total;
@@ -811,7 +814,7 @@ __device__ __forceinline__ void reduce_rows_block(int rows, int cols, const floa
     f32x4 v[R];
 #pragma unroll
     for (int q = 0; q < R; ++q)
-      v[q] = r0 + q < rows ? tt::ld4<VEC>(X, ldx, r0 + q, c, cols) : f32x4{0.f, 0.f, 0.f, 0.f};
+      v[q] = r0 + q < rows ? tt::ld4_nt<VEC>(X, ldx, r0 + q, c, cols) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int q = 0; q < R; ++q) acc += v[q];
   }

@@ -35,3 +35,77 @@ extern "C" int tt_probe_mfma_f32(void* stream, int64_t blocks, int64_t iters, fl
   hipLaunchKernelGGL(mfma_probe, dim3((unsigned)blocks), dim3(256), 0, tt::as_stream(stream), (int)iters, out);
   return tt::launch_status("tt_probe_mfma_f32");
 }
+
+// ---- HBM probes: the practical bandwidth of plain streams on the running
+// device, the ceiling the memory-bound kernels are measured against beside
+// the published 8 TB/s. Grid-stride over 16-byte elements with four loads
+// in flight per thread; read (every element summed, one sum per thread
+// written), write (a constant stored) and copy (1:1 read and write), the
+// loads and stores optionally non-temporal.
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int MODE, bool NT>
+__global__ __launch_bounds__(256) void hbm_probe(const f32x4* __restrict__ src, f32x4* __restrict__ dst, int64_t n4,
+                                                 float* __restrict__ red) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  auto put = [&](int64_t k, f32x4 v) {
+    if (NT) __builtin_nontemporal_store(v, dst + k);
+    else dst[k] = v;
+  };
+  auto get = [&](int64_t k) -> f32x4 {
+    if (NT) return __builtin_nontemporal_load(src + k);
+    return src[k];
+  };
+  if (MODE == TT_PROBE_READ) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (; i + 3 * stride < n4; i += 4 * stride) {
+      const f32x4 v0 = get(i), v1 = get(i + stride), v2 = get(i + 2 * stride), v3 = get(i + 3 * stride);
+      acc += (v0 + v1) + (v2 + v3);
+    }
+    for (; i < n4; i += stride) acc += get(i);
+    red[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc[0] + acc[1] + acc[2] + acc[3];
+  } else if (MODE == TT_PROBE_WRITE) {
+    const f32x4 v = {1.f, 2.f, 3.f, (float)blockIdx.x};
+    for (; i < n4; i += stride) put(i, v);
+  } else {
+    for (; i + 3 * stride < n4; i += 4 * stride) {
+      const f32x4 v0 = get(i), v1 = get(i + stride), v2 = get(i + 2 * stride), v3 = get(i + 3 * stride);
+      put(i, v0);
+      put(i + stride, v1);
+      put(i + 2 * stride, v2);
+      put(i + 3 * stride, v3);
+    }
+    for (; i < n4; i += stride) put(i, get(i));
+  }
+}
+
+}  // namespace
+
+extern "C" int tt_probe_hbm(void* stream, int mode, const float* src, float* dst, int64_t n, int64_t blocks,
+                            double* bytes) {
+  const int kind = mode & 3;
+  const bool nt = (mode & TT_PROBE_NONTEMPORAL) != 0;
+  if ((mode & ~(3 | TT_PROBE_NONTEMPORAL)) || kind > TT_PROBE_COPY)
+    return tt::fail(TT_ERR_ARG, "tt_probe_hbm: unknown mode %d", mode);
+  if (n < 0 || n % 4 || blocks < 1 || blocks > 65535)
+    return tt::fail(TT_ERR_ARG, "tt_probe_hbm: n must be a multiple of 4 and blocks 1..65535");
+  if ((kind != TT_PROBE_WRITE && !src) || !dst) return tt::fail(TT_ERR_ARG, "tt_probe_hbm: null buffer");
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15)
+    return tt::fail(TT_ERR_ARG, "tt_probe_hbm: buffers must be 16-byte aligned");
+  if (bytes) *bytes = (double)n * 4.0 * (kind == TT_PROBE_COPY ? 2.0 : 1.0);
+  hipStream_t s = tt::as_stream(stream);
+  const dim3 grid((unsigned)blocks), block(256);
+  const f32x4* a = reinterpret_cast<const f32x4*>(src);
+  f32x4* b = reinterpret_cast<f32x4*>(dst);
+  if (kind == TT_PROBE_READ && nt) hipLaunchKernelGGL((hbm_probe<TT_PROBE_READ, true>), grid, block, 0, s, a, b, n / 4, dst);
+  else if (kind == TT_PROBE_READ) hipLaunchKernelGGL((hbm_probe<TT_PROBE_READ, false>), grid, block, 0, s, a, b, n / 4, dst);
+  else if (kind == TT_PROBE_WRITE && nt) hipLaunchKernelGGL((hbm_probe<TT_PROBE_WRITE, true>), grid, block, 0, s, a, b, n / 4, dst);
+  else if (kind == TT_PROBE_WRITE) hipLaunchKernelGGL((hbm_probe<TT_PROBE_WRITE, false>), grid, block, 0, s, a, b, n / 4, dst);
+  else if (nt) hipLaunchKernelGGL((hbm_probe<TT_PROBE_COPY, true>), grid, block, 0, s, a, b, n / 4, dst);
+  else hipLaunchKernelGGL((hbm_probe<TT_PROBE_COPY, false>), grid, block, 0, s, a, b, n / 4, dst);
+  return tt::launch_status("tt_probe_hbm");
+}

@@ -35,6 +35,19 @@ __device__ __forceinline__ f32x4 ld4(const float* __restrict__ p, int64_t ld, in
   return v;
 }
 
+// ld4 for data read once (a streaming sweep): the 16-byte load is
+// non-temporal
+template <bool VEC>
+__device__ __forceinline__ f32x4 ld4_nt(const float* __restrict__ p, int64_t ld, int64_t r, int c, int cols) {
+  const float* q = p + r * ld + c;
+  if (VEC && c + 3 < cols) return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(q));
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (c + i < cols) v[i] = q[i];
+  return v;
+}
+
 template <bool VEC>
 __device__ __forceinline__ void st4(float* __restrict__ p, int64_t ld, int64_t r, int c, int cols, f32x4 v) {
   float* q = p + r * ld + c;

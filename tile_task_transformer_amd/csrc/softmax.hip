@@ -82,6 +82,7 @@ struct XeTiles {
   int64_t ld[kXeMax];
   int64_t off[kXeMax];
   int cols[kXeMax];
+  int part[kXeMax];  // index of the tile's partials (position in the caller's list)
 };
 
 template <int NV, bool VEC>
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(256) void xe_stats_multi(int rows, XeTiles P, const
   const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (row >= rows) return;
   const int t = blockIdx.y;
-  stats_row<NV, VEC>(row, P.cols[t], 0, P.off[t], 1.f, 0, P.z[t], P.ld[t], labels, parts + t * part_stride);
+  stats_row<NV, VEC>(row, P.cols[t], 0, P.off[t], 1.f, 0, P.z[t], P.ld[t], labels, parts + P.part[t] * part_stride);
 }
 
 __global__ void sm_merge(int rows, int n_parts, const float* __restrict__ parts, int64_t stride,
@@ -299,48 +300,56 @@ extern "C" int tile_xentropy_multi(void* stream, int phase, int count, int64_t r
       return fail(TT_ERR_SHAPE, "tile_xentropy_multi: v_len of tile %d not in [1, %d]", t, kMaxCols);
     if (!logits[t] || ldz[t] < v_len[t]) return fail(TT_ERR_ARG, "tile_xentropy_multi: bad tile %d", t);
   }
-  for (int t0 = 0; t0 < count; t0 += kXeMax) {
-    const int c = std::min(kXeMax, count - t0);
-    XeTiles P{};
-    bool vec = true;
-    int maxc = 1;
-    for (int u = 0; u < c; ++u) {
-      P.z[u] = logits[t0 + u];
-      P.ld[u] = ldz[t0 + u];
-      P.off[u] = v_off[t0 + u];
-      P.cols[u] = (int)v_len[t0 + u];
-      vec = vec && ldz[t0 + u] % 4 == 0 && tt::aligned16(logits[t0 + u]);
-      maxc = std::max(maxc, P.cols[u]);
-    }
-    if (phase == TT_XE_STATS) {
-      float* pp = parts + t0 * part_stride;
-      const int r = (int)rows;
-      switch ((maxc + 255) / 256) {
-        case 1: launch_stats_multi<1>(vec, r, c, P, labels, pp, part_stride, s); break;
-        case 2: launch_stats_multi<2>(vec, r, c, P, labels, pp, part_stride, s); break;
-        case 3: launch_stats_multi<3>(vec, r, c, P, labels, pp, part_stride, s); break;
-        case 4: launch_stats_multi<4>(vec, r, c, P, labels, pp, part_stride, s); break;
-        case 5: case 6: launch_stats_multi<6>(vec, r, c, P, labels, pp, part_stride, s); break;
-        default: launch_stats_multi<8>(vec, r, c, P, labels, pp, part_stride, s); break;
+  // tiles in two groups, each launched as one multi-tile kernel per up to
+  // kXeMax tiles: those the 16-byte paths take (statistics: ld a multiple
+  // of 4 and aligned; gradient: contiguous, ld == cols a multiple of 4, as
+  // one flat stream) and the rest (a ragged last vocab tile), so that one
+  // odd tile does not send every tile down the scalar path
+  const bool grad = phase != TT_XE_STATS;
+  auto fast = [&](int t) {
+    return grad ? (ldz[t] == v_len[t] && v_len[t] % 4 == 0 && tt::aligned16(logits[t]))
+                : (ldz[t] % 4 == 0 && tt::aligned16(logits[t]));
+  };
+  for (int group = 0; group < 2; ++group) {
+    std::vector<int> ids;
+    for (int t = 0; t < count; ++t)
+      if (fast(t) == (group == 0)) ids.push_back(t);
+    for (size_t t0 = 0; t0 < ids.size(); t0 += kXeMax) {
+      const int c = (int)std::min<size_t>(kXeMax, ids.size() - t0);
+      XeTiles P{};
+      int maxc = 1;
+      for (int u = 0; u < c; ++u) {
+        const int t = ids[t0 + u];
+        P.z[u] = logits[t];
+        P.ld[u] = ldz[t];
+        P.off[u] = v_off[t];
+        P.cols[u] = (int)v_len[t];
+        P.part[u] = t;
+        maxc = std::max(maxc, P.cols[u]);
       }
-      if (int rc = tt::launch_status("tile_xentropy_multi(STATS)")) return rc;
-    } else {
-      // the flat stream needs every tile contiguous (ld == cols) with cols a
-      // multiple of 4 and 16-byte aligned; otherwise one row per workgroup
-      bool flat = true;
-      for (int u = 0; u < c; ++u)
-        flat = flat && P.ld[u] == P.cols[u] && P.cols[u] % 4 == 0 && tt::aligned16(P.z[u]);
-      if (flat) {
+      const bool vec = group == 0;
+      if (!grad) {
+        const int r = (int)rows;
+        switch ((maxc + 255) / 256) {
+          case 1: launch_stats_multi<1>(vec, r, c, P, labels, parts, part_stride, s); break;
+          case 2: launch_stats_multi<2>(vec, r, c, P, labels, parts, part_stride, s); break;
+          case 3: launch_stats_multi<3>(vec, r, c, P, labels, parts, part_stride, s); break;
+          case 4: launch_stats_multi<4>(vec, r, c, P, labels, parts, part_stride, s); break;
+          case 5: case 6: launch_stats_multi<6>(vec, r, c, P, labels, parts, part_stride, s); break;
+          default: launch_stats_multi<8>(vec, r, c, P, labels, parts, part_stride, s); break;
+        }
+        if (int rc = tt::launch_status("tile_xentropy_multi(STATS)")) return rc;
+      } else if (vec) {
         const int64_t most = rows * (int64_t)maxc / 4;
         const unsigned gx = (unsigned)std::min<int64_t>((most + 255) / 256, std::max<int64_t>(1, 2048 / c));
         hipLaunchKernelGGL(xe_grad_multi, dim3(gx, (unsigned)c), dim3(256), 0, s, (int)rows, P, labels, lse, inv_n);
+        if (int rc = tt::launch_status("tile_xentropy_multi(GRAD)")) return rc;
       } else {
         for (int u = 0; u < c; ++u)
           if (int rc = launch_apply((int)rows, P.cols[u], 0, P.off[u], 1.f, 0, P.z[u], P.ld[u], labels, lse, P.z[u],
                                     P.ld[u], inv_n, s))
             return rc;
       }
-      if (int rc = tt::launch_status("tile_xentropy_multi(GRAD)")) return rc;
     }
   }
   return TT_OK;

@@ -10,14 +10,15 @@ from __future__ import annotations
 from ._lib import (TT_EPI_NONE, check, lib, ptr, stream_handle, TT_EPI_BIAS, TT_EPI_RES, TT_EPI_GELU,  # noqa: F401
                    TT_EPI_GELU_BWD, TT_LN_PARTIAL, TT_LN_MERGE, TT_LN_APPLY, TT_LN_FUSED, TT_SM_STATS,
                    TT_SM_MERGE, TT_SM_APPLY, TT_XE_LOSS, TT_XE_GRAD, TT_XE_STATS, TT_ATT_PREP, TT_ATT_GRAD,
-                   TT_EMB_TOKEN, TT_EMB_POS)
+                   TT_EMB_TOKEN, TT_EMB_POS, TT_PROBE_READ, TT_PROBE_WRITE, TT_PROBE_COPY, TT_PROBE_NONTEMPORAL)
 
 __all__ = [
     "tile_gemm", "tile_gemm_ws", "tile_gemm_workspace", "tile_gemm_ksum", "tile_gemm_batch", "tile_gemm_batch_ws",
     "tile_gemm_batch_workspace", "tile_gemm_ksum_ex", "tile_layernorm_fwd",
     "tile_layernorm_bwd", "tile_layernorm_bwd_workspace", "tile_softmax",
     "tile_xentropy", "tile_xentropy_multi", "tile_attention_fwd", "tile_attention_bwd",
-    "tile_attention_bwd_workspace", "tile_attention_bwd_ws", "tile_gemm_ksum_workspace", "tile_fused_adamw",
+    "tile_attention_bwd_workspace", "tile_attention_bwd_ws", "tile_gemm_ksum_workspace", "tt_probe_hbm",
+    "TT_PROBE_READ", "TT_PROBE_WRITE", "TT_PROBE_COPY", "TT_PROBE_NONTEMPORAL", "tile_fused_adamw",
     "tile_fused_adamw_multi",
     "tile_adamw_advance", "tile_sgd", "tile_sgd_multi",
     "tile_embedding_fwd", "tile_embedding_index", "tile_embedding_bwd", "tile_reduce_rows",
@@ -259,6 +260,14 @@ def tt_probe_mfma_f32(stream, blocks, iters, out):
     import ctypes as C
     f = C.c_double()
     check(lib.tt_probe_mfma_f32(stream_handle(stream), blocks, iters, ptr(out), C.byref(f)))
+    return f.value
+
+
+def tt_probe_hbm(stream, mode, src, dst, n, blocks):
+    """Launch the HBM bandwidth probe; returns the bytes it moves."""
+    import ctypes as C
+    f = C.c_double()
+    check(lib.tt_probe_hbm(stream_handle(stream), mode, ptr(src), ptr(dst), n, blocks, C.byref(f)))
     return f.value
 
 
