@@ -162,7 +162,7 @@ int tile_gemm_ksum_ex(void* stream, int count, int transB, int64_t m, int64_t n,
                       float beta, float* C, int64_t ldc, int epilogue, const float* bias, const float* res,
                       int64_t ldr, float* aux, int64_t ldaux);
 /* tile_gemm_ksum_ws -- tile_gemm_ksum_ex with a DEVICE workspace (16-byte
- * aligned; null with 0 bytes = none). An output of fewer than 256 blocks
+ * aligned; null with 0 bytes = none). An output of at most 128 blocks
  * of 128 x 128 (m and n multiples of 128) then splits the concatenated K
  * steps of each long-K launch into up to 16 slices that run side by side
  * (about 512 workgroups), each summing its slice into its own m x n region

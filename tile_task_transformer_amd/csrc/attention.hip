@@ -471,19 +471,17 @@ __global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_bwd_dq(AttnGeom g, co
 // dQ = scale * dS K from the dS blocks the dK/dV kernel stored (5 products
 // per tile pair instead of 7: S and dP are not recomputed). Same work split
 // as attn_bwd_dq: 32 queries per wave pair, each wave half of every 64-key
-// stage. A stage's four 32 x 32 blocks (2 query groups x 2 key halves) are
-// loaded with 16-byte accesses and transposed into LDS (row stride 33: the
-// wave's reads of one key row by its 32 query lanes hit 32 banks), then fed
-// to the MFMAs in the register layout of the recomputing kernel.
+// stage. A wave reads its 32 x 32 block of dS straight into registers: lane
+// (query l32, half h) takes keys 16h .. 16h + 15 of its query's row (four
+// 16-byte loads, issued a stage ahead), and MFMA step j pairs key 16h + j
+// of that row with row 16h + j of K in LDS.
 template <int HD>
 __global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_bwd_dq_ds(AttnGeom g, const float* __restrict__ K,
                                                                     const float* __restrict__ dsw,
                                                                     float* __restrict__ dQ, int acc) {
   using C = Cfg<HD>;
   constexpr int LD = C::LD, NEB = C::NEB;
-  constexpr int TLD = 33;
   __shared__ __attribute__((aligned(16))) float Ks[kBS * LD];
-  __shared__ float Ts[4 * 32 * TLD];  // the stage's dS blocks, [block][key][query]
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = wave & 1, part = wave >> 1;
@@ -494,7 +492,6 @@ __global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_bwd_dq_ds(AttnGeom g,
   const int q = q0 + l32;
   const bool qvalid = q < g.q_len;
   const int nq32 = (g.q_len + 31) / 32, nk32 = (g.k_len + 31) / 32;
-  const float* dsb = dsw + (int64_t)bh * nq32 * nk32 * 1024;
 
   f32x16 dacc[NEB];
 #pragma unroll
@@ -506,65 +503,52 @@ __global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_bwd_dq_ds(AttnGeom g,
   const int kend = (int)max((int64_t)0, min((int64_t)g.k_len, qmax - g.k_off + 1));
   const int64_t wave_qmax = g.q_off + min(g.q_len - 1, q0 + 31);
   const bool wave_live = q0 < g.q_len;
-
-  // float4 i of the thread: block idx >> 8 of the stage (query group
-  // blk >> 1, key half blk & 1), elements 4 * (idx & 255) .. + 3 in register
-  // order: element p holds query kidx(p >> 6, (p >> 5) & 1), key p & 31
-  f32x4 dr[4];
-  auto ds_load = [&](int k0) {
+  // the blocks of this wave's 32 queries (query group q0 / 32 < nq32 when live)
+  const float* dsrow = dsw + ((int64_t)bh * nq32 + q0 / 32) * nk32 * 1024 + l32 * 32 + 16 * half;
+  // a stage's block is live (stored by the dK/dV kernel, which computes every
+  // block with a visible pair) when some key of the wave's half sees some query
+  auto live = [&](int kb) { return wave_live && kb < g.k_len && g.k_off + kb <= wave_qmax; };
+  auto ds_load = [&](int k0, f32x4(&d)[4]) {
+    const int kb = k0 + part * 32;
+    if (live(kb)) {
+      const float* p = dsrow + (int64_t)(kb / 32) * 1024;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = (int)threadIdx.x + kNT * i, blk = idx >> 8;
-      const int q32 = qblk * 2 + (blk >> 1), k32 = k0 / 32 + (blk & 1);
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (q32 < nq32 && k32 < nk32)
-        v = *reinterpret_cast<const f32x4*>(dsb + ((int64_t)q32 * nk32 + k32) * 1024 + (idx & 255) * 4);
-      dr[i] = v;
-    }
-  };
-  auto ds_store = [&]() {
+      for (int i = 0; i < 4; ++i) d[i] = *reinterpret_cast<const f32x4*>(p + 4 * i);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = (int)threadIdx.x + kNT * i, blk = idx >> 8;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int p = (idx & 255) * 4 + e;
-        Ts[blk * 32 * TLD + (p & 31) * TLD + kidx(p >> 6, (p >> 5) & 1)] = dr[i][e];
-      }
+      for (int i = 0; i < 4; ++i) d[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   };
 
   zero_pad<HD, LD>(Ks);
   Stager<HD, LD> sk;
+  f32x4 dc[4], dn[4];
   if (kend > 0) {
     sk.load(K, b, h, 0, g.k_len, g.heads);
-    ds_load(0);
+    ds_load(0, dc);
     sk.store(Ks);
-    ds_store();
   }
   __syncthreads();
   for (int k0 = 0; k0 < kend; k0 += kBS) {
     const bool more = k0 + kBS < kend;
     if (more) {
       sk.load(K, b, h, k0 + kBS, g.k_len, g.heads);
-      ds_load(k0 + kBS);
+      ds_load(k0 + kBS, dn);
     }
-    const int kb0 = k0 + part * 32;
-    const float* ks = Ks + part * 32 * LD;
-    const float* ts = Ts + (grp * 2 + part) * 32 * TLD;
-    if (wave_live && kb0 < g.k_len && g.k_off + kb0 <= wave_qmax) {
-      f32x16 dst;
+    const float* ks = Ks + (part * 32 + 16 * half) * LD;
+    if (live(k0 + part * 32)) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dst[r] = ts[kidx(r, half) * TLD + l32];  // dS^T: lane owns a query column
+      for (int j = 0; j < 16; ++j) {
+        const float dsv = dc[j >> 2][j & 3];
 #pragma unroll
-      for (int eb = 0; eb < NEB; ++eb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dacc[eb] = mfma(ks[kidx(r, half) * LD + eb * 32 + l32], dst[r], dacc[eb]);
+        for (int eb = 0; eb < NEB; ++eb) dacc[eb] = mfma(ks[j * LD + eb * 32 + l32], dsv, dacc[eb]);
+      }
     }
     __syncthreads();
     if (more) {
       sk.store(Ks);
-      ds_store();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dc[i] = dn[i];
     }
     __syncthreads();
   }
@@ -719,11 +703,11 @@ __global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_bwd_dkv(AttnGeom g, c
           dkv[NEB + eb] = mfma(dsb[kidx(r, half) * LD + eb * 32 + l32], s[r], dkv[NEB + eb]);  // dV^T += dO^T P
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] *= dp[r] - dv[r >> 2][r & 3];  // dS, in place of P
-      if (dsw) {  // the 32 x 32 block of dS for the dQ kernel, in register order (coalesced per register)
+      if (dsw) {  // the 32 x 32 block of dS for the dQ kernel, row-major by query (two 128-byte rows per store)
         const int nq32 = (g.q_len + 31) / 32, nk32 = (g.k_len + 31) / 32;
-        float* blk = dsw + (((int64_t)bh * nq32 + qb0 / 32) * nk32 + k0w / 32) * 1024 + lane;
+        float* blk = dsw + (((int64_t)bh * nq32 + qb0 / 32) * nk32 + k0w / 32) * 1024 + l32;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) blk[r * 64] = s[r];
+        for (int r = 0; r < 16; ++r) blk[kidx(r, half) * 32] = s[r];
       }
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb)

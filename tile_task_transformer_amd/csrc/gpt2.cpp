@@ -237,7 +237,7 @@ int submit_ksum(tt_ctx* ctx, const char* label, int tb, TileRef C, const std::ve
 //    65.1 -> 73.9, attention projection 18.3 -> 18.5): every link of the
 //    chain already runs a long K loop;
 //  * fewer: the long-K launch takes it, split over K into slices through
-//    the stream workspace when there are fewer than 256 blocks of 128 x 128
+//    the stream workspace when there are at most 128 blocks of 128 x 128
 //    (the small-tile model's 1024 x 512 outputs: 32 blocks x 16 slices),
 //    else with 64x64 blocks; one launch and a slice sum per task against
 //    one launch per contraction tile.
