@@ -229,21 +229,24 @@ int submit_ksum(tt_ctx* ctx, const char* label, int tb, TileRef C, const std::ve
 
 // whether a linear layer's contraction over several tiles runs as one K-sum
 // task (else a chain of accumulating GEMM tasks), by the output tile's
-// block counts (measured per task class, one stream, each task alone):
-//  * >= 1024 blocks of 128x128: the long-K launch wins (wide model, MLP input
-//    layer 4096 x 8192: 74.1 -> 67.6 ms per step; its input gradient 72.7 ->
-//    70.8 ms);
-//  * 512..1023: it loses (MLP output layer 65.5 -> 70.5 ms, fc input gradient
-//    65.1 -> 73.9, attention projection 18.3 -> 18.5): every link of the
-//    chain already runs a long K loop;
-//  * fewer: the long-K launch takes it, split over K into slices through
-//    the stream workspace when there are at most 128 blocks of 128 x 128
-//    (the small-tile model's 1024 x 512 outputs: 32 blocks x 16 slices),
-//    else with 64x64 blocks; one launch and a slice sum per task against
-//    one launch per contraction tile.
+// block count, the orientation of B and the contraction tile's width A0
+// (measured per shape, each task alone, on the wide model's tiles):
+//  * the long-K launch wins almost everywhere: 4096 x 8192 outputs (2048
+//    blocks of 128x128, K 4 x 2048) 74.1 -> 67.6 ms per step for the MLP
+//    input layer; 4096 x 2048 outputs (512 blocks) with 2048-wide
+//    contraction tiles 1133 -> 1047 us per task (q, k, v), and with 8192-wide
+//    ones and B stored [n][k] 4019 -> 3996 us (fc input gradient);
+//  * except 512..1023 blocks with B stored [k][n] and contraction tiles of
+//    >= 8192, where every link of the chain already runs a long K loop
+//    (MLP output layer: 4062 us as a chain, 4153 us as one sum);
+//  * below 512 blocks the long-K launch is split over K into slices through
+//    the stream workspace (at most 128 blocks of 128 x 128: the small-tile
+//    model's 1024 x 512 outputs, 32 blocks x 16 slices) or runs 64x64
+//    blocks; one launch and a slice sum per task against one launch per
+//    contraction tile.
 // TT_KSUM_CLASSES="qkv,fc,..." forces the given task classes to K-sum tasks
 // and every other class to chains (tuning).
-bool use_ksum(const char* label, const TileRef& C) {
+bool use_ksum(const char* label, const TileRef& C, int tb, const TileRef& A0) {
   static std::string set;
   static int mode = -1;
   if (mode < 0) {
@@ -252,10 +255,11 @@ bool use_ksum(const char* label, const TileRef& C) {
     if (e) set = std::string(",") + e + ",";
   }
   if (mode == 1) return set.find(std::string(",") + label + ",") != std::string::npos;
-  int64_t r, c;
+  int64_t r, c, ar, ak;
   C.t->mat(C.lin, &r, &c);
+  A0.t->mat(A0.lin, &ar, &ak);
   const int64_t nb = (r / 128) * (c / 128);
-  return nb >= 1024 || nb < 512;
+  return !(nb >= 512 && nb < 1024 && !tb && ak >= 8192);
 }
 
 // tiles = value, TT_FILL_MAX_TILES tiles per task and launch (with
@@ -738,7 +742,7 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
         for (int cq = 0; cq < 3; ++cq)
           for (int64_t hj = 0; hj < NH; ++hj) {
             const TileRef C = {qkv[cq], L(qkv[cq], {bi, si, hj, 0})}, bias = {bqkv, L(bqkv, {cq, hj, 0})};
-            if (use_ksum("qkv", C)) {
+            if (use_ksum("qkv", C, 0, {b.n1, L(b.n1, {bi, si, 0})})) {
               std::vector<TileRef> As, Bs;
               for (int64_t ek = 0; ek < NE; ++ek) {
                 As.push_back({b.n1, L(b.n1, {bi, si, ek})});
@@ -777,7 +781,7 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
         const int64_t ti = bi + g->nb * si;
         // h_mid = h_in + O W_o + b_o
         for (int64_t ej = 0; ej < NE; ++ej) {
-          if (use_ksum("attn_proj", {b.h_mid, L(b.h_mid, {bi, si, ej})})) {
+          if (use_ksum("attn_proj", {b.h_mid, L(b.h_mid, {bi, si, ej})}, 0, {b.o, L(b.o, {bi, si, 0, 0})})) {
             std::vector<TileRef> As, Bs;
             for (int64_t hk = 0; hk < NH; ++hk) {
               As.push_back({b.o, L(b.o, {bi, si, hk, 0})});
@@ -807,7 +811,7 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
         TRY(ln_forward(g, b.h_mid, ln2g, ln2b, b.ln2, b.n2, bi, si));
         // g = gelu(n2 W_fc + b_fc), pre-activation kept in u
         for (int64_t ij = 0; ij < NI; ++ij) {
-          if (use_ksum("fc", {b.g, L(b.g, {bi, si, ij})})) {
+          if (use_ksum("fc", {b.g, L(b.g, {bi, si, ij})}, 0, {b.n2, L(b.n2, {bi, si, 0})})) {
             std::vector<TileRef> As, Bs;
             for (int64_t ek = 0; ek < NE; ++ek) {
               As.push_back({b.n2, L(b.n2, {bi, si, ek})});
@@ -835,7 +839,7 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
         }
         // h_out = h_mid + g W_p + b_p
         for (int64_t ej = 0; ej < NE; ++ej) {
-          if (use_ksum("mlp_proj", {hout, L(hout, {bi, si, ej})})) {
+          if (use_ksum("mlp_proj", {hout, L(hout, {bi, si, ej})}, 0, {b.g, L(b.g, {bi, si, 0})})) {
             std::vector<TileRef> As, Bs;
             for (int64_t ik = 0; ik < NI; ++ik) {
               As.push_back({b.g, L(b.g, {bi, si, ik})});
@@ -1079,7 +1083,7 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
         }
         TRY(colsum_row(g->dh, gbp, NE, bi, si, ti > 0 || later_mb));
         for (int64_t ik = 0; ik < NI; ++ik) {
-          if (use_ksum("mlp_proj_dx", {g->dgu, L(g->dgu, {bi, si, ik})})) {
+          if (use_ksum("mlp_proj_dx", {g->dgu, L(g->dgu, {bi, si, ik})}, 1, {g->dh, L(g->dh, {bi, si, 0})})) {
             std::vector<TileRef> As, Bs;
             for (int64_t ej = 0; ej < NE; ++ej) {
               As.push_back({g->dh, L(g->dh, {bi, si, ej})});
@@ -1121,7 +1125,7 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
         // (a chain of accumulating GEMMs: as one long-K task per embd tile it
         // measured slower on the wide model, 65 -> 71 ms per step)
         for (int64_t ek = 0; ek < NE; ++ek) {
-          if (use_ksum("fc_dx", {g->dn, L(g->dn, {bi, si, ek})})) {
+          if (use_ksum("fc_dx", {g->dn, L(g->dn, {bi, si, ek})}, 1, {g->dgu, L(g->dgu, {bi, si, 0})})) {
             std::vector<TileRef> As, Bs;
             for (int64_t ik = 0; ik < NI; ++ik) {
               As.push_back({g->dgu, L(g->dgu, {bi, si, ik})});
@@ -1159,7 +1163,7 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
         }
         TRY(colsum_row(g->dh, gbo, NE, bi, si, ti > 0 || later_mb));
         for (int64_t hk = 0; hk < NH; ++hk) {
-          if (use_ksum("attn_proj_dx", {g->dO, L(g->dO, {bi, si, hk, 0})})) {
+          if (use_ksum("attn_proj_dx", {g->dO, L(g->dO, {bi, si, hk, 0})}, 1, {g->dh, L(g->dh, {bi, si, 0})})) {
             std::vector<TileRef> As, Bs;
             for (int64_t ej = 0; ej < NE; ++ej) {
               As.push_back({g->dh, L(g->dh, {bi, si, ej})});
