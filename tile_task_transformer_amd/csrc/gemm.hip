@@ -879,14 +879,18 @@ __global__ __launch_bounds__(256, 2) void gemm_ksum_kernel(KsumArgs P) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-// plans of a batch launch: 128x128x16 / 64x64x32 blocks, or 128x128x32 with split-K
+// plans of a batch launch: 128x128x32 / 64x64x32 blocks, or 128x128x32 with
+// split-K. The big plan's BK 32 (two workgroups per CU) against BK 16
+// (three): 85.3 against 82.6 % of the fp32 peak for 16 products 8192 x 2048
+// x 4096 with A stored [k][m], 85.1 against 81.2 % for 25 products 4096 x
+// 2048 x 2048 with B stored [n][k]
 enum BatchPlan { kBatchBig, kBatchSmall, kBatchSplit };
 
 template <bool TA, bool TB>
 int launch_batch(const GemmArgs& g, const GemmBatch& P, int blocks, BatchPlan plan, int64_t max_mn, bool vec_mn,
                  hipStream_t s) {
   const dim3 grid((unsigned)blocks), block(256);
-  if (plan == kBatchBig) hipLaunchKernelGGL((gemm_batch_kernel<128, 128, 16, TA, TB, false>), grid, block, 0, s, g, P);
+  if (plan == kBatchBig) hipLaunchKernelGGL((gemm_batch_kernel<128, 128, 32, TA, TB, false>), grid, block, 0, s, g, P);
   else if (plan == kBatchSmall) hipLaunchKernelGGL((gemm_batch_kernel<64, 64, 32, TA, TB, false>), grid, block, 0, s, g, P);
   else hipLaunchKernelGGL((gemm_batch_kernel<128, 128, 32, TA, TB, true>), grid, block, 0, s, g, P);
   if (int rc = tt::launch_status("tile_gemm_batch")) return rc;
@@ -1199,7 +1203,7 @@ extern "C" int tile_gemm_batch_ws(void* stream, int count, int transA, int trans
   hipStream_t s = tt::as_stream(stream);
   // the plan tile_gemm would pick if the products were one C: split-K over
   // 128x128x32 blocks for few blocks and a long K (with a workspace),
-  // 128x128x16 blocks when there are >= 512 of them, else 64x64x32
+  // 128x128x32 blocks when there are >= 512 of them, else 64x64x32
   int64_t b128 = 0;
   for (int t = 0; t < count; ++t)
     if (m[t] > 0 && n[t] > 0) b128 += ((m[t] + 127) / 128) * ((n[t] + 127) / 128);
