@@ -60,6 +60,9 @@ TRAFFIC = {
     ("gpt2_small", "head_dw"): {"source": "tile_task_transformer_amd/csrc/gemm.hip", "sha256": "fa7bf9abd8f9b062",
                                 "fetch_kib": 1689378.8, "fetch_factor": 2.0,
                                 "write_kib": 150771.0, "write_factor": 1.0},
+    # profiles/gemm_ksum_fc_wide4_traffic.md
+    ("wide4", "fc"): {"source": "tile_task_transformer_amd/csrc/gemm.hip", "sha256": "43ecee1903aacb99",
+                      "fetch_kib": 1050161.9, "fetch_factor": 2.0, "write_kib": 262144.0, "write_factor": 1.0},
 }
 
 
@@ -149,7 +152,30 @@ def class_rooflines(breakdown: dict, s) -> dict:
 # entry point of each task class's launches (the rest are tile_gemm)
 KERNEL_OF = {"head": "tile_gemm_batch", "head_dw": "tile_gemm_batch", "head_dx": "tile_gemm_ksum",
              "qkv_dw": "tile_gemm_batch", "qkv_dx": "tile_gemm_ksum", "attn_proj_dw": "tile_gemm_batch",
-             "fc_dw": "tile_gemm_batch", "mlp_proj_dw": "tile_gemm_batch"}
+             "fc_dw": "tile_gemm_batch", "mlp_proj_dw": "tile_gemm_batch", "attn_fwd": "tile_attention_fwd",
+             "attn_bwd": "tile_attention_bwd_ws"}
+# linear layers whose contraction the step sums as one long-K task when it
+# spans several tiles (the MLP output layer stays a chain of tile_gemm at
+# 512-1023 output blocks with 8192-wide contraction tiles)
+KSUM_WHEN_SPLIT = {"qkv": "embd", "attn_proj": "head", "fc": "embd", "mlp_proj": "inner", "mlp_proj_dx": "embd",
+                   "fc_dx": "inner", "attn_proj_dx": "embd"}
+
+
+def kernel_of(label: str, s, t) -> str:
+    """The entry point a class's launches go through at this tiling."""
+    axis = KSUM_WHEN_SPLIT.get(label)
+    if axis:
+        full = {"embd": s.n_embd, "inner": s.n_inner, "head": s.n_head}[axis]
+        tile = getattr(t, axis)
+        if tile < full:
+            rows = (t.batch * t.seq) // 128
+            cols = {"qkv": t.head * (s.n_embd // s.n_head), "attn_proj": t.embd, "fc": t.inner, "mlp_proj": t.embd,
+                    "mlp_proj_dx": t.inner, "fc_dx": t.embd, "attn_proj_dx": t.head * (s.n_embd // s.n_head)}[label]
+            k_tile = {"embd": t.embd, "inner": t.inner, "head": t.head * (s.n_embd // s.n_head)}[axis]
+            nb = rows * (cols // 128)
+            chain = 512 <= nb < 1024 and label in ("qkv", "attn_proj", "fc", "mlp_proj") and k_tile >= 8192
+            return "tile_gemm" if chain else "tile_gemm_ksum"
+    return KERNEL_OF.get(label, "tile_gemm")
 
 GEMM_SHAPES = {  # label -> (transA, transB, m, n, k, epilogue, beta) in tile terms
     "qkv": lambda r, e, i, h, v: (0, 0, r, h, e, 1, 0.0), "attn_proj": lambda r, e, i, h, v: (0, 0, r, e, h, 3, 0.0),
@@ -643,10 +669,12 @@ def run(w, a, streams, breakdown_path, probe, steps=None, warmup=None, want_para
     print(f"  serialized total {sum(b['total_ms'] for b in breakdown.values()):.2f} ms", file=sys.stderr,
           flush=True)
     work = class_work(s)
-    # the dominant class: the largest share of the serialized step among the
-    # matrix-core classes (GEMM and attention alike)
-    mfma_ms = {k: v["ms"] for k, v in classes.items() if v["bound"] == "mfma"}
-    dominant = max(mfma_ms, key=mfma_ms.get) if mfma_ms else "fc"
+    # the dominant class: the largest share of the step's model flops among
+    # the matrix-core classes (GEMM and attention alike), ties (the MLP's
+    # six products of equal size) broken by name, so that the choice does
+    # not flip between runs whose times differ by noise
+    mfma = [k for k, v in classes.items() if v["bound"] == "mfma"]
+    dominant = min(mfma, key=lambda k: (-work[k][1], k)) if mfma else "fc"
 
     # timed region: K steps back to back, every PROFILE_EVERY-th task of the
     # dominant class bracketed by events (an event pair costs ~4 us of queue
@@ -691,7 +719,7 @@ def run(w, a, streams, breakdown_path, probe, steps=None, warmup=None, want_para
         "mfma_frac_of_probe": round(tflops / probe["mfma_f32_tflops"], 4) if probe else None,
         "tasks_per_step": model.task_count(), "loss": round(loss, 5),
         "host_submit_ms_per_step": round(1e3 * st["submit_seconds"] / steps, 3),
-        "roofline": {"bound": "mfma", "kernel": f"{KERNEL_OF.get(dominant, 'tile_gemm')}[{dominant}]",
+        "roofline": {"bound": "mfma", "kernel": f"{kernel_of(dominant, s, t)}[{dominant}]",
                      "achieved": round(achieved, 2),
                      "peak": MFMA_FP32_PEAK, "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP32_PEAK, 4),
                      "frac_of_probe": round(achieved / probe["mfma_f32_tflops"], 4) if probe else None,
