@@ -112,6 +112,7 @@ int tt_probe_hbm(void* stream, int mode, const float* src, float* dst, int64_t n
 #define TT_EPI_RES       2
 #define TT_EPI_GELU      4
 #define TT_EPI_GELU_BWD  8
+#define TT_EPI_XSTATS   16  /* cross-entropy statistics: tile_gemm_batch_xstats and its task op only */
 int tile_gemm(void* stream, int transA, int transB, int64_t m, int64_t n, int64_t k,
               float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
               float beta, float* C, int64_t ldc, int epilogue, const float* bias,
@@ -212,6 +213,26 @@ int tile_gemm_batch_ws(void* stream, int count, int transA, int transB, const in
                        const float* const* B, const int64_t* ldb, float beta, float* const* C,
                        const int64_t* ldc, void* workspace, size_t workspace_bytes);
 size_t tile_gemm_batch_workspace(int count, const int64_t* m, const int64_t* n, int64_t k);
+/* tile_gemm_batch_xstats -- the tied LM head's logits with the statistics of
+ * the cross-entropy in the epilogue (pith.science review, "What carries the
+ * argument": the head and the loss are tile tasks; the softmax statistics
+ * are taken from the logits while they are in registers instead of a second
+ * pass over them). Product t: C_t = alpha A_t op(B_t) + beta C_t (A_t m x k,
+ * transA = 0, op() as in tile_gemm), C_t holding vocab columns
+ * v_off0 + t*v_tile .. + n[t] - 1 (n[t] <= v_tile) of m rows. Then, for every
+ * row i and 64-column group q of C_t, with x the stored values of the
+ * group's columns inside C_t:
+ *   parts + t*part_stride + (q*m + i)*3 = { max x, sum exp(x - max x),
+ *     x[labels[i] - v_off0 - t*v_tile - 64q] if that column is in the group, else 0 }
+ * labels: DEVICE int32 [m]; parts: DEVICE, part_stride >= ceil(max n / 64)*m*3
+ * floats. Always 128x128 blocks, no split; deterministic. The groups merge
+ * with tile_xentropy_merge_groups. TT_ERR_ARG for null arrays, n[t] outside
+ * 1..v_tile, a short part_stride, or more than 32767 products. */
+int tile_gemm_batch_xstats(void* stream, int count, int transB, int64_t m, const int64_t* n, int64_t k,
+                           float alpha, const float* const* A, const int64_t* lda, const float* const* B,
+                           const int64_t* ldb, float beta, float* const* C, const int64_t* ldc,
+                           const int32_t* labels, int64_t v_off0, int64_t v_tile, float* parts,
+                           int64_t part_stride);
 
 /* tile_layernorm_fwd -- layer norm over the embedding axis, split into
  * feature tiles (layer list: pith.science review, "What carries the
@@ -368,6 +389,16 @@ int tile_xentropy_multi(void* stream, int phase, int count, int64_t rows, const 
                         const int64_t* v_off, const int32_t* labels, float* const* logits,
                         const int64_t* ldz, float* parts, int64_t part_stride, const float* lse,
                         float inv_n);
+/* tile_xentropy_merge_groups -- lse and per-row loss from group partials
+ * (tile_gemm_batch_xstats): tile t holds ceil(v_len[t] / group) partials
+ * of rows x 3 floats at parts + t*part_stride (group-major), each (max, sum
+ * exp(x - max), picked target logit). lse[r] = logsumexp over all of them,
+ * row_loss[r] (may be NULL) = lse[r] - sum of the picked logits. One wave
+ * per row, each lane merging every 64th partial in order, then a fixed xor
+ * tree: deterministic. v_len: HOST array of `count` entries. TT_ERR_ARG for
+ * null pointers, rows > 65535, group < 1 or v_len[t] < 1. */
+int tile_xentropy_merge_groups(void* stream, int64_t rows, int count, const int64_t* v_len, int group,
+                               const float* parts, int64_t part_stride, float* lse, float* row_loss);
 
 /* tile_attention_fwd -- causal multi-head scaled dot-product attention for
  * one (query tile, key tile) pair (layer list: pith.science review; the
@@ -688,8 +719,13 @@ typedef struct { float value; } tt_op_fill;
  * TT_OP_GEMM_BATCH -- independent products sharing K and the scalars
  * (tile_gemm_batch; the tied head's per-vocab-tile products): tiles A_0,
  * B_0, C_0, A_1, B_1, C_1, ... (one or more products; more than 72 make
- * several launches); epilogue must be 0. C_t written (beta == 0) or
- * updated.
+ * several launches); epilogue 0. C_t written (beta == 0) or updated.
+ * With epilogue TT_EPI_XSTATS (tile_gemm_batch_xstats; transA = 0): the
+ * triples, then labels (i32, >= m elements), then one partials tile per
+ * product (>= ceil(v_tile / 64) * m * 3 floats, equally spaced in memory);
+ * the C tiles are consecutive tiles along the last axis of one tensor (the
+ * logits), whose tile index times tile size gives each product's vocab
+ * offset; labels read, partials written.
  * TT_OP_GEMM_KSUM -- a sum of products into one tile (tile_gemm_ksum_ex: a
  * linear layer whose contraction axis is split over several tiles, forward
  * or backward): tiles C, then bias / res / aux as the epilogue requires (as
@@ -766,7 +802,11 @@ typedef struct {
  * (row max, sum exp, picked target logit). Reads labels, z; writes parts.
  * TT_OP_XENTROPY_MERGE -- tiles lse (rows), row_loss (rows),
  * parts_0..parts_{n-1}: lse = merged logsumexp, row_loss = lse - target
- * logit. Reads parts; writes lse and row_loss.
+ * logit. Reads parts; writes lse and row_loss. No scalars: one partial per
+ * tile (from TT_OP_XENTROPY_STATS). Scalars tt_op_xe_groups: tile j holds
+ * the column-group partials of vocab tile j (of vocab / v_tile tiles,
+ * rounded up; from the head's TT_EPI_XSTATS epilogue), merged by
+ * tile_xentropy_merge_groups.
  * TT_OP_XENTROPY_LOSS -- tiles row_loss, loss (1 float): loss =
  * (accumulate ? loss : 0) + inv_n * sum row_loss. Reads row_loss; loss
  * written, or updated when accumulate.
@@ -781,6 +821,10 @@ typedef struct {
     int accumulate;
     float inv_n;
 } tt_op_xentropy;
+typedef struct {
+    int64_t vocab, v_tile;
+    int group;            /* 64 for the TT_EPI_XSTATS partials */
+} tt_op_xe_groups;
 
 /* Optimiser steps (NNTile README, "Minimal working GPT example": fused
  * AdamW; the review's "What carries the argument" lists the Adam/SGD

@@ -19,8 +19,12 @@ from tile_task_transformer_amd import _lib as L
 
 
 class SubmitGPT2:
-    def __init__(self, ctx, s: synth.GPT2Shape, t: synth.Tiles):
-        self.ctx, self.s, self.t = ctx, s, t
+    def __init__(self, ctx, s: synth.GPT2Shape, t: synth.Tiles, fused_head: bool = False):
+        """fused_head: the head's last embd tile as one batched task over all
+        vocab tiles with the cross-entropy statistics in its epilogue
+        (TT_EPI_XSTATS), merged by 64-column groups; else every product its
+        own task and a separate statistics pass."""
+        self.ctx, self.s, self.t, self.fused_head = ctx, s, t, fused_head
         d, I, H, V, T, B = s.n_embd, s.n_inner, s.n_head, s.vocab, s.seq, s.batch
         hd = d // H
         et, it, ht, vt, st, bt = min(t.embd, d), min(t.inner, I), t.head, min(t.vocab, V), t.seq, t.batch
@@ -68,7 +72,8 @@ class SubmitGPT2:
         self.lnf, self.nf = act((B, T, 2), (bt, st, 2)), act((B, T, d), (bt, st, et))
         self.z = act((B, T, V), (bt, st, vt))
         self.ml = act((B // bt, T // st, H // ht, 2 * nq), (1, 1, 1, 2 * nq), 3)
-        self.ce_parts = act((self.NV, ntok, self.rows * 3), (1, 1, self.rows * 3))
+        groups = -(-vt // 64) if fused_head else 1
+        self.ce_parts = act((self.NV, ntok, groups * self.rows * 3), (1, 1, groups * self.rows * 3))
         self.ce_lse, self.row_loss = act((ntok, self.rows), (1, self.rows), 1), act((ntok, self.rows), (1, self.rows), 1)
         self.loss = act((1,), (1,), 0)
         self.dnf, self.dh, self.dn = (act((B, T, d), (bt, st, et)) for _ in range(3))
@@ -168,13 +173,27 @@ class SubmitGPT2:
             for si in range(ns):
                 ti = bi + nb * si
                 ln_fwd(s.h_last, P["lnf_g"], P["lnf_b"], s.lnf, s.nf, bi, si)
-                for vj in range(NV):
-                    for ek in range(NE):
-                        s.gemm(s.nf, (bi, si, ek), P["wte"], (vj, ek), s.z, (bi, si, vj), tb=1, beta=float(ek > 0))
-                s.sub(L.TT_OP_XENTROPY_STATS, [(s.labels, (bi, si))] + [(s.z, (bi, si, v)) for v in range(NV)] +
-                      [(s.ce_parts, (v, ti, 0)) for v in range(NV)])
-                s.sub(L.TT_OP_XENTROPY_MERGE, [(s.ce_lse, (ti, 0)), (s.row_loss, (ti, 0))] +
-                      [(s.ce_parts, (v, ti, 0)) for v in range(NV)])
+                if s.fused_head:
+                    for vj in range(NV):
+                        for ek in range(NE - 1):
+                            s.gemm(s.nf, (bi, si, ek), P["wte"], (vj, ek), s.z, (bi, si, vj), tb=1,
+                                   beta=float(ek > 0))
+                    last = NE - 1
+                    tl = [x for vj in range(NV) for x in ((s.nf, (bi, si, last)), (P["wte"], (vj, last)),
+                                                          (s.z, (bi, si, vj)))]
+                    tl += [(s.labels, (bi, si))] + [(s.ce_parts, (v, ti, 0)) for v in range(NV)]
+                    s.sub(L.TT_OP_GEMM_BATCH, tl, L.tt_op_gemm(0, 1, L.TT_EPI_XSTATS, 1.0, float(last > 0), 0))
+                    s.sub(L.TT_OP_XENTROPY_MERGE, [(s.ce_lse, (ti, 0)), (s.row_loss, (ti, 0))] +
+                          [(s.ce_parts, (v, ti, 0)) for v in range(NV)], L.tt_op_xe_groups(sh.vocab, s.vt, 64))
+                else:
+                    for vj in range(NV):
+                        for ek in range(NE):
+                            s.gemm(s.nf, (bi, si, ek), P["wte"], (vj, ek), s.z, (bi, si, vj), tb=1,
+                                   beta=float(ek > 0))
+                    s.sub(L.TT_OP_XENTROPY_STATS, [(s.labels, (bi, si))] + [(s.z, (bi, si, v)) for v in range(NV)] +
+                          [(s.ce_parts, (v, ti, 0)) for v in range(NV)])
+                    s.sub(L.TT_OP_XENTROPY_MERGE, [(s.ce_lse, (ti, 0)), (s.row_loss, (ti, 0))] +
+                          [(s.ce_parts, (v, ti, 0)) for v in range(NV)])
                 s.sub(L.TT_OP_XENTROPY_LOSS, [(s.row_loss, (ti, 0)), (s.loss, (0,))],
                       L.tt_op_xentropy(int(ti > 0), inv_n))
                 s.sub(L.TT_OP_XENTROPY_GRAD, [(s.labels, (bi, si)), (s.ce_lse, (ti, 0))] +

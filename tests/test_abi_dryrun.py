@@ -189,9 +189,16 @@ def test_gpt2_step_dag_is_race_free(tiles, tmp_path):
     assert n == len(dag) > 0
     _check_races(dag)
     labels = {r["label"] for r in dag}
-    for need in ("emb_fwd", "qkv", "attn_fwd", "attn_proj", "fc", "mlp_proj", "head", "ce_stats", "ce_merge",
+    for need in ("emb_fwd", "qkv", "attn_fwd", "attn_proj", "fc", "mlp_proj", "head", "ce_merge",
                  "ce_loss", "ce_grad", "head_dw", "head_dx", "attn_bwd", "adamw", "emb_dw", "emb_dpos"):
         assert need in labels, need
+    # the cross-entropy statistics come from the head's last batch (its
+    # epilogue), not from a separate pass over the logits: every merge reads
+    # partials that a head task wrote
+    assert "ce_stats" not in labels
+    label_of = {r["id"]: r["label"] for r in dag}
+    merges = [r for r in dag if r["label"] == "ce_merge"]
+    assert merges and all(any(label_of[d] == "head" for d in r["deps"]) for r in merges)
 
 
 def test_gpt2_accumulating_step_dag_is_race_free(tmp_path):

@@ -554,6 +554,75 @@ def test_cross_entropy_multi_tile(rows, cols, vt):
         assert_rel(host(blocks[i]), rdz[:, c0:c1], 1e-5, 1e-7 / rows, f"dz tile {i}")
 
 
+@pytest.mark.parametrize("rows,vocab,vt,k,beta", [
+    (300, 1000, 256, 96, 0.0),     # ragged rows, 4 vocab tiles (the last 232 wide)
+    (130, 2500, 1105, 64, 1.0),    # the wide model's ragged vocab tile width, C accumulated (beta 1)
+    (64, 5000, 768, 128, 0.0),     # 7 tiles, the last 392 wide
+    (96, 200, 64, 32, 0.5),        # one 64-column group per tile, rows below one block
+])
+def test_head_xstats_epilogue_and_group_merge(rows, vocab, vt, k, beta):
+    """The head's batched products with the cross-entropy statistics in the
+    epilogue, merged by 64-column groups: the logits against the fp64
+    products, lse and the per-row loss against the oracle's cross-entropy of
+    the fp64 logits and against the separate statistics pass over the GPU's
+    own logits; the partials start as NaN, so a group the epilogue failed to
+    write would show; bitwise equal across runs."""
+    x = synth.rand_normal((rows, k), 81 + k, std=0.5)
+    w = synth.rand_normal((vocab, k), 82 + k, std=0.5)
+    c0 = synth.rand_normal((rows, vocab), 83, std=2.0)
+    y = np.random.default_rng(84).integers(0, vocab, rows).astype(np.int32)
+    tiles = otl.tiles(vocab, vt)
+    lens = [c1 - c0_ for c0_, c1 in tiles]
+    X, Y = dev(x), dev(y)
+    Ws = [dev(w[a:b]) for a, b in tiles]
+    groups = -(-vt // 64)
+    stride = groups * rows * 3
+    outs = []
+    for _ in range(2):
+        Zs = [dev(c0[:, a:b]) for a, b in tiles]
+        parts = torch.full((len(tiles), stride), float("nan"), device="cuda")
+        tt.tile_gemm_batch_xstats(None, 1, rows, lens, k, 1.0, [X] * len(tiles), [k] * len(tiles), Ws,
+                                  [k] * len(tiles), beta, Zs, lens, Y, 0, vt, parts, stride)
+        lse, rl = empty((rows,)), empty((rows,))
+        tt.tile_xentropy_merge_groups(None, rows, lens, 64, parts, stride, lse, rl)
+        outs.append((torch.cat(Zs, dim=1), lse, rl))
+    assert all(torch.equal(a, b) for a, b in zip(outs[0], outs[1]))
+    z_gpu, lse, rl = outs[0]
+    ref = beta * c0.astype(np.float64) + x.astype(np.float64) @ w.astype(np.float64).T
+    bound = (np.abs(x).astype(np.float64) @ np.abs(w).astype(np.float64).T) * (k + 2) * EPS32
+    assert_close_bound(host(z_gpu), ref, bound + 4 * EPS32 * np.abs(ref) + 1e-30, "head logits")
+    rloss, _, rlse = og.cross_entropy(ref, y)
+    assert_rel(host(lse), rlse, 1e-5, 1e-5, "lse (fused statistics)")
+    assert abs(host(rl).mean() - rloss) <= 1e-5 * abs(rloss)
+    # against the separate statistics pass over the same fp32 logits
+    blocks = [z_gpu[:, a:b].contiguous() for a, b in tiles]
+    p1 = empty((len(tiles), rows, 3))
+    tt.tile_xentropy_multi(None, tt.TT_XE_STATS, rows, lens, [a for a, _ in tiles], Y, blocks, lens, parts=p1,
+                           part_stride=rows * 3)
+    lse1, rl1 = empty((rows,)), empty((rows,))
+    tt.tile_softmax(None, tt.TT_SM_MERGE, rows, 0, 0, 0, 1.0, 0, None, 0, None, p1, len(tiles), rows * 3, lse1, rl1,
+                    None, 0, 1.0)
+    assert_rel(host(lse), host(lse1), 2e-6, 2e-6, "lse fused vs separate pass")
+    # the picked target logit is the GPU's own logit (a sum of one value and zeros)
+    picked = host(lse) - host(rl)
+    zl = host(z_gpu)[np.arange(rows), y]
+    assert np.abs(picked - zl).max() <= 4 * EPS32 * (np.abs(host(lse)).max() + np.abs(zl).max())
+
+
+def test_head_xstats_errors():
+    a = empty((64, 64))
+    lab = torch.zeros(64, dtype=torch.int32, device="cuda")
+    p = empty((64 * 3,))
+    with pytest.raises(tt.TTError):   # n above the vocab tile
+        tt.tile_gemm_batch_xstats(None, 1, 64, [64], 64, 1.0, [a], [64], [a], [64], 0.0, [a], [64], lab, 0, 32, p,
+                                  64 * 3)
+    with pytest.raises(tt.TTError):   # partials too small for the groups
+        tt.tile_gemm_batch_xstats(None, 1, 64, [64], 64, 1.0, [a], [64], [a], [64], 0.0, [a], [64], lab, 0, 128, p,
+                                  64 * 2)
+    with pytest.raises(tt.TTError):
+        tt.tile_xentropy_merge_groups(None, 64, [64], 0, p, 64 * 3, p)
+
+
 def test_cross_entropy_multi_errors():
     z = dev(np.zeros((4, 8), np.float32))
     y = dev(np.zeros(4, np.int32))

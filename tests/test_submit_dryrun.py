@@ -60,6 +60,68 @@ def test_step_edges_follow_the_stf_rule_and_are_race_free(step_dag):
     _check_races(dag)
 
 
+def test_fused_head_step_edges_and_access_modes(tmp_path):
+    """The same step with the head's last embd tile as one batched task
+    carrying the cross-entropy statistics (TT_EPI_XSTATS): STF edges,
+    race-free, and the task's access modes (logits written or updated,
+    labels read, one partials tile per vocab tile written); the merge reads
+    exactly those partials."""
+    path = str(tmp_path / "fused.jsonl")
+    with Context(L.TT_DEVICE_DRYRUN, n_streams=4, window=100000) as ctx:
+        m = SubmitGPT2(ctx, SHAPE, TILES, fused_head=True)
+        m.submit_step(None)
+        dag = ctx.dump_dag(path)
+        ids = {id(t): i for i, t in enumerate(ctx._tensors)}
+    assert {r["id"]: sorted(r["deps"]) for r in dag} == stf_edges(dag)
+    _check_races(dag)
+    assert not [r for r in dag if r["label"] == "ce_stats"]
+    heads = [r for r in dag if r["label"] == "gemm_batch_xstats"]
+    assert len(heads) == m.nb * m.ns
+    pid, zid, lid = ids[id(m.ce_parts)], ids[id(m.z)], ids[id(m.labels)]
+    for r in heads:
+        modes = {}
+        for t, lin, md in r["acc"]:
+            modes.setdefault(t, set()).add(md)
+        assert modes[pid] == {W} and modes[lid] == {R} and modes[zid] == {RW}  # two embd tiles: beta = 1
+        assert sum(t == pid for t, _, _ in r["acc"]) == m.NV
+    merges = [r for r in dag if r["label"] == "ce_merge"]
+    for r in merges:
+        assert {(t, lin) for t, lin, md in r["acc"] if t == pid} <= {(t, lin) for h in heads for t, lin, _ in h["acc"]
+                                                                      if t == pid}
+
+
+def test_fused_head_argument_errors():
+    with Context(L.TT_DEVICE_DRYRUN, n_streams=1) as ctx:
+        A = ctx.tensor((64, 32), (64, 32))
+        Bt = ctx.tensor((96, 32), (48, 32))
+        Z = ctx.tensor((64, 96), (64, 48))
+        lab = ctx.tensor((64,), (64,), L.TT_I32)
+        parts = ctx.tensor((2, 64 * 3), (1, 64 * 3))
+        sc = L.tt_op_gemm(0, 1, L.TT_EPI_XSTATS, 1.0, 0.0, 0)
+        tl = [(A, (0, 0)), (Bt, (0, 0)), (Z, (0, 0)), (A, (0, 0)), (Bt, (1, 0)), (Z, (0, 1)), (lab, (0,)),
+              (parts, (0, 0)), (parts, (1, 0))]
+        ctx.submit(L.TT_OP_GEMM_BATCH, tl, sc)                                    # fine
+        bad = [
+            (tl[:3] + tl[6:8], L.tt_op_gemm(1, 1, L.TT_EPI_XSTATS, 1.0, 0.0, 0), L.TT_ERR_ARG),   # transA
+            (tl[:3] + tl[6:8] + [tl[8]], sc, L.TT_ERR_ARG),                                        # tile count
+            (tl[3:6] + tl[:3] + tl[6:], sc, L.TT_ERR_ARG),                                         # vocab order
+            (tl[:3] + [(A, (0, 0)), (Bt, (1, 0)), (Z, (0, 1))] + [(A, (0, 0))] + tl[7:], sc, L.TT_ERR_ARG),  # labels f32
+        ]
+        for tiles, s, code in bad:
+            with pytest.raises(L.TTError) as e:
+                ctx.submit(L.TT_OP_GEMM_BATCH, tiles, s)
+            assert e.value.code == code, e.value
+        small = ctx.tensor((2, 3), (1, 3))
+        with pytest.raises(L.TTError) as e:
+            ctx.submit(L.TT_OP_GEMM_BATCH, tl[:7] + [(small, (0, 0)), (small, (1, 0))], sc)
+        assert e.value.code == L.TT_ERR_SHAPE
+        lse = ctx.tensor((64,), (64,))
+        with pytest.raises(L.TTError) as e:   # 3 vocab tiles of 48 for vocab 96 would be 2
+            ctx.submit(L.TT_OP_XENTROPY_MERGE, [(lse, (0,)), (lse, (0,)), (parts, (0, 0))],
+                       L.tt_op_xe_groups(96, 48, 64))
+        assert e.value.code == L.TT_ERR_ARG
+
+
 def _modes(task, ids, tensors_and_tiles):
     """mode of each given (tensor, tile lin) in a task's dumped accesses."""
     acc = {(t, l): md for t, l, md in task["acc"]}

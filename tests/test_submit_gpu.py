@@ -15,16 +15,17 @@ from tests.test_gpt2_gpu import check_against_oracle  # noqa: E402
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("shape,tiles", [
-    (synth.GPT2Shape(2, 100, 64, 4, 96, 32, 2), synth.Tiles(1, 16, 32, 48, 2, 40)),   # every axis split, ragged
-    (synth.WORKLOADS["tiny"].shape, synth.WORKLOADS["tiny"].tiles),
+@pytest.mark.parametrize("shape,tiles,fused", [
+    (synth.GPT2Shape(2, 100, 64, 4, 96, 32, 2), synth.Tiles(1, 16, 32, 48, 2, 40), False),   # every axis split, ragged
+    (synth.GPT2Shape(2, 100, 64, 4, 96, 32, 2), synth.Tiles(1, 16, 32, 48, 2, 40), True),    # head statistics fused
+    (synth.WORKLOADS["tiny"].shape, synth.WORKLOADS["tiny"].tiles, False),
 ])
-def test_user_built_step_matches_oracle(shape, tiles):
+def test_user_built_step_matches_oracle(shape, tiles, fused):
     w = synth.WORKLOADS["tiny"]
     params = synth.init_params(shape, seed=0)
     tokens = synth.token_stream(shape, seed=1)
     with Context(0, n_streams=4, window=4096) as ctx:
-        m = SubmitGPT2(ctx, shape, tiles)
+        m = SubmitGPT2(ctx, shape, tiles, fused_head=fused)
         m.set_params(params)
         tok = torch.from_numpy(tokens.astype(np.int32)).cuda()
         ctx.wait_stream(torch.cuda.current_stream())

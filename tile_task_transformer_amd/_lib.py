@@ -30,7 +30,7 @@ lib = C.CDLL(LIB_PATH)
 
 # ---- constants (mirror include/tiletask.h)
 TT_OK, TT_ERR_ARG, TT_ERR_SHAPE, TT_ERR_OOM, TT_ERR_HIP, TT_ERR_STATE, TT_ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
-TT_EPI_NONE, TT_EPI_BIAS, TT_EPI_RES, TT_EPI_GELU, TT_EPI_GELU_BWD = 0, 1, 2, 4, 8
+TT_EPI_NONE, TT_EPI_BIAS, TT_EPI_RES, TT_EPI_GELU, TT_EPI_GELU_BWD, TT_EPI_XSTATS = 0, 1, 2, 4, 8, 16
 TT_LN_PARTIAL, TT_LN_MERGE, TT_LN_APPLY, TT_LN_FUSED = 0, 1, 2, 3
 TT_SM_STATS, TT_SM_MERGE, TT_SM_APPLY = 0, 1, 2
 TT_XE_LOSS, TT_XE_GRAD, TT_XE_STATS = 0, 1, 2
@@ -88,6 +88,10 @@ class tt_op_attention(C.Structure):
 
 class tt_op_xentropy(C.Structure):
     _fields_ = [("accumulate", C.c_int), ("inv_n", C.c_float)]
+
+
+class tt_op_xe_groups(C.Structure):
+    _fields_ = [("vocab", C.c_int64), ("v_tile", C.c_int64), ("group", C.c_int)]
 
 
 class tt_op_optim(C.Structure):
@@ -154,6 +158,8 @@ SIGNATURES = {
     "tile_gemm_batch_ws": (I, [P, I, I, I, P, P, I64, F, P, P, P, P, F, P, P, P, SZ]),
     "tile_gemm_batch_workspace": (SZ, [I, P, P, I64]),
     "tile_xentropy_multi": (I, [P, I, I, I64, P, P, P, P, P, P, I64, P, F]),
+    "tile_xentropy_merge_groups": (I, [P, I64, I, P, I, P, I64, P, P]),
+    "tile_gemm_batch_xstats": (I, [P, I, I, I64, P, I64, F, P, P, P, P, F, P, P, P, I64, I64, P, I64]),
     "tile_layernorm_fwd": (I, [P, I, I64, I64, P, I64, P, P, P, I64, I64, P, P, I64, F]),
     "tile_layernorm_bwd": (I, [P, I, I64, I64, I64, P, I64, P, I64, P, P, P, I64, I64, P, I64, I, P, P, P]),
     "tile_layernorm_bwd_workspace": (SZ, [I64, I64]),

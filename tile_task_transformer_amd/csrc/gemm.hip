@@ -73,6 +73,14 @@ struct GemmArgs {
   float* ws;       // split-K partials [splits][m][n], or null
   int splits;      // K ranges (1 = no split)
   int kchunk;      // K per split (multiple of kSplitAlign)
+  // TT_EPI_XSTATS (128x128 blocks, no split): per row and 64-column group of
+  // C, (max, sum exp(x - max), x at the row's label) -> xparts[(group * m +
+  // row) * 3 ..]; the label's column is xlab[row] - xvoff
+  const int32_t* xlab;
+  float* xparts;
+  int64_t xvoff;
+  int64_t xstride;  // batched: floats between the partials of consecutive products
+  int64_t xvtile;   // batched: vocab offset step between consecutive products
 };
 
 // tanh(a) = 1 - 2 / (exp(2a) + 1), on the hardware exp2 and reciprocal
@@ -99,8 +107,9 @@ __device__ __forceinline__ float gelu_tanh_grad(float u) {
   return 0.5f * (1.f + t) + 0.5f * u * (1.f - t * t) * c * (1.f + 3.f * 0.044715f * u * u);
 }
 
-// acc (already alpha-scaled) -> C, with beta source, bias, residual, GELU
-__device__ __forceinline__ void epilogue_store(const GemmArgs& g, int row, int col, float v) {
+// acc (already alpha-scaled) -> C, with beta source, bias, residual, GELU;
+// returns the value stored
+__device__ __forceinline__ float epilogue_store(const GemmArgs& g, int row, int col, float v) {
   const bool gelu = g.epi & TT_EPI_GELU;
   if (g.beta != 0.f)
     v += g.beta * (gelu ? g.aux[(int64_t)row * g.ldaux + col] : g.C[(int64_t)row * g.ldc + col]);
@@ -113,6 +122,7 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& g, int row, int c
     v *= gelu_tanh_grad(g.aux[(int64_t)row * g.ldaux + col]);
   }
   g.C[(int64_t)row * g.ldc + col] = v;
+  return v;
 }
 
 // float4 of an operand at (r, c) of a `rows` x `cols` row-major matrix with
@@ -385,9 +395,44 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, int b, float* lds)
         if (SPLIT)
           g.ws[((int64_t)split * g.m + row) * g.n + col] = acc[i][j][r];
         else
-          epilogue_store(g, row, col, g.alpha * acc[i][j][r]);
+          acc[i][j][r] = epilogue_store(g, row, col, g.alpha * acc[i][j][r]);
       }
     }
+  // ---- cross-entropy statistics of the stored values: each wave's 64
+  // columns are one group. The wave's 64 x 64 values go through LDS (the
+  // staging buffers, free once every wave is past its last K step) so that
+  // lane l owns row l of the tile: it takes (max, sum exp(x - max), x at the
+  // row's label) over the group's columns inside C in column order and
+  // writes them, 64 lanes to 64 consecutive rows
+  // (128x128x32 blocks: the plan tile_gemm_batch_xstats always launches)
+  constexpr int XLD = 65;  // row stride: lane l reads row l, consecutive lanes hit consecutive banks
+  if constexpr (!SPLIT && WN == 64 && LL::FLOATS >= 4 * 64 * XLD) {
+    if (g.epi & TT_EPI_XSTATS) {
+      __syncthreads();
+      float* xs = lds + wave * 64 * XLD;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) xs[(i * 32 + 8 * (r >> 2) + 4 * half + (r & 3)) * XLD + j * 32 + l32] = acc[i][j][r];
+      __syncthreads();
+      const int c0 = n0 + wn * WN, row = m0 + wm * WM + lane;
+      if (c0 < g.n && row < g.m) {
+        const float* rp = xs + lane * XLD;
+        const int ncol = min(64, g.n - c0);
+        const int64_t lab = (int64_t)g.xlab[row] - g.xvoff - c0;
+        float mx = -INFINITY;
+        for (int c = 0; c < ncol; ++c) mx = fmaxf(mx, rp[c]);
+        float se = 0.f;
+        for (int c = 0; c < ncol; ++c) se += __builtin_amdgcn_exp2f((rp[c] - mx) * 1.4426950408889634f);
+        float* q = g.xparts + ((int64_t)(c0 / 64) * g.m + row) * 3;
+        q[0] = mx;
+        q[1] = se;
+        q[2] = (lab >= 0 && lab < ncol) ? rp[lab] : 0.f;
+      }
+    }
+  }
 }
 
 template <int BM, int BN, int BK, bool TA, bool TB, bool VA, bool VB, bool SPLIT>
@@ -415,6 +460,7 @@ struct GemmBatch {
   int first[kBatchMax];                       // first block of each product
   unsigned va[(kBatchMax + 31) / 32];         // bit t: product t loads A 16 bytes at a time
   unsigned vb[(kBatchMax + 31) / 32];         // bit t: product t loads B 16 bytes at a time
+  short orig[kBatchMax];                      // position of product t in the caller's list
   int count;
 };
 static_assert(sizeof(GemmArgs) + sizeof(GemmBatch) <= 4096, "kernel arguments over 4 KB");
@@ -440,6 +486,11 @@ __global__ __launch_bounds__(256, 2) void gemm_batch_kernel(GemmArgs g, GemmBatc
   h.ldb = P.ldb[t];
   h.ldc = P.ldc[t];
   if (SPLIT) h.ws = g.ws + (int64_t)P.first[t] * (BM * BN);
+  if (g.epi & TT_EPI_XSTATS) {  // product o of the call: its partials region and vocab offset
+    const int o = P.orig[t];
+    h.xparts = g.xparts + (int64_t)o * g.xstride;
+    h.xvoff = g.xvoff + (int64_t)o * g.xvtile;
+  }
   const bool va = (P.va[t >> 5] >> (t & 31)) & 1u, vb = (P.vb[t >> 5] >> (t & 31)) & 1u;
   const int lb = b - P.first[t];
   if (va && vb) gemm_block<BM, BN, BK, TA, TB, true, true, SPLIT>(h, lb, lds);
@@ -1181,10 +1232,19 @@ extern "C" size_t tile_gemm_batch_workspace(int count, const int64_t* m, const i
   return sp > 1 ? (size_t)(b128 * sp) * 128 * 128 * sizeof(float) : 0;
 }
 
-extern "C" int tile_gemm_batch_ws(void* stream, int count, int transA, int transB, const int64_t* m,
-                                  const int64_t* n, int64_t k, float alpha, const float* const* A, const int64_t* lda,
-                                  const float* const* B, const int64_t* ldb, float beta, float* const* C,
-                                  const int64_t* ldc, void* workspace, size_t workspace_bytes) {
+namespace {
+
+// cross-entropy statistics epilogue of a batched launch (tile_gemm_batch_xstats)
+struct XStats {
+  const int32_t* labels;
+  float* parts;
+  int64_t part_stride, v_off0, v_tile;
+};
+
+int batch_run(void* stream, int count, int transA, int transB, const int64_t* m, const int64_t* n, int64_t k,
+              float alpha, const float* const* A, const int64_t* lda, const float* const* B, const int64_t* ldb,
+              float beta, float* const* C, const int64_t* ldc, void* workspace, size_t workspace_bytes,
+              const XStats* xs) {
   using tt::fail;
   if (count < 0 || k < 0) return fail(TT_ERR_ARG, "tile_gemm_batch: negative count or k");
   if (count == 0) return TT_OK;
@@ -1208,11 +1268,20 @@ extern "C" int tile_gemm_batch_ws(void* stream, int count, int transA, int trans
   for (int t = 0; t < count; ++t)
     if (m[t] > 0 && n[t] > 0) b128 += ((m[t] + 127) / 128) * ((n[t] + 127) / 128);
   int64_t chunk = k;
-  const int splits = batch_splits(b128, k, workspace ? workspace_bytes : 0, &chunk);
-  const BatchPlan plan = splits > 1 ? kBatchSplit : b128 >= 512 ? kBatchBig : kBatchSmall;
+  // the statistics epilogue needs whole 128x128 blocks in one pass
+  const int splits = xs ? 1 : batch_splits(b128, k, workspace ? workspace_bytes : 0, &chunk);
+  const BatchPlan plan = splits > 1 ? kBatchSplit : (b128 >= 512 || xs) ? kBatchBig : kBatchSmall;
   const int bm = plan == kBatchSmall ? 64 : 128, bn = bm;
   GemmArgs g{0, 0, (int)k, alpha, beta, nullptr, nullptr, nullptr, 0, 0, 0, TT_EPI_NONE, nullptr,
              nullptr, 0, nullptr, 0, (float*)workspace, splits, (int)chunk};
+  if (xs) {
+    g.epi = TT_EPI_XSTATS;
+    g.xlab = xs->labels;
+    g.xparts = xs->parts;
+    g.xvoff = xs->v_off0;
+    g.xstride = xs->part_stride;
+    g.xvtile = xs->v_tile;
+  }
   // products whose loads are scalar (a ragged tile's odd leading dimension)
   // run slower blocks: they go first in the grid, so the hardware starts
   // them first and the rest fill in around them (longest first)
@@ -1248,6 +1317,7 @@ extern "C" int tile_gemm_batch_ws(void* stream, int count, int transA, int trans
         P.ldb[c] = (int)ldb[t];
         P.ldc[c] = (int)ldc[t];
         P.first[c] = (int)blocks;
+        P.orig[c] = (short)t;
         if (vec_a(t)) P.va[c >> 5] |= 1u << (c & 31);
         if (vec_b(t)) P.vb[c >> 5] |= 1u << (c & 31);
         blocks += nb;
@@ -1265,6 +1335,39 @@ extern "C" int tile_gemm_batch_ws(void* stream, int count, int transA, int trans
     if (rc) return rc;
   }
   return TT_OK;
+}
+
+}  // namespace
+
+extern "C" int tile_gemm_batch_ws(void* stream, int count, int transA, int transB, const int64_t* m,
+                                  const int64_t* n, int64_t k, float alpha, const float* const* A, const int64_t* lda,
+                                  const float* const* B, const int64_t* ldb, float beta, float* const* C,
+                                  const int64_t* ldc, void* workspace, size_t workspace_bytes) {
+  return batch_run(stream, count, transA, transB, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
+                   workspace_bytes, nullptr);
+}
+
+extern "C" int tile_gemm_batch_xstats(void* stream, int count, int transB, int64_t m, const int64_t* n, int64_t k,
+                                      float alpha, const float* const* A, const int64_t* lda, const float* const* B,
+                                      const int64_t* ldb, float beta, float* const* C, const int64_t* ldc,
+                                      const int32_t* labels, int64_t v_off0, int64_t v_tile, float* parts,
+                                      int64_t part_stride) {
+  using tt::fail;
+  if (count < 0 || m < 0 || k < 0) return fail(TT_ERR_ARG, "tile_gemm_batch_xstats: negative count or size");
+  if (count == 0 || m == 0) return TT_OK;
+  if (count > INT16_MAX) return fail(TT_ERR_ARG, "tile_gemm_batch_xstats: more than %d products", INT16_MAX);
+  if (!n || !labels || !parts || v_tile < 1 || v_off0 < 0)
+    return fail(TT_ERR_ARG, "tile_gemm_batch_xstats: null array, labels or partials, or bad vocab offsets");
+  int64_t groups = 0;
+  for (int t = 0; t < count; ++t) {
+    if (n[t] < 1 || n[t] > v_tile) return fail(TT_ERR_ARG, "tile_gemm_batch_xstats: n of product %d not in 1..v_tile", t);
+    groups = std::max<int64_t>(groups, (n[t] + 63) / 64);
+  }
+  if (part_stride < groups * m * 3)
+    return fail(TT_ERR_ARG, "tile_gemm_batch_xstats: part_stride below %lld floats", (long long)(groups * m * 3));
+  std::vector<int64_t> ms(count, m);
+  const XStats xs{labels, parts, part_stride, v_off0, v_tile};
+  return batch_run(stream, count, 0, transB, ms.data(), n, k, alpha, A, lda, B, ldb, beta, C, ldc, nullptr, 0, &xs);
 }
 
 extern "C" int tile_gemm_batch(void* stream, int count, int transA, int transB, const int64_t* m, const int64_t* n,

@@ -262,6 +262,18 @@ bool use_ksum(const char* label, const TileRef& C, int tb, const TileRef& A0) {
   return !(nb >= 512 && nb < 1024 && !tb && ak >= 8192);
 }
 
+// whether the head's last batch takes the cross-entropy statistics in its
+// epilogue (else a separate pass over the logits); TT_HEAD_XSTATS=0 selects
+// the separate pass (comparison)
+bool head_xstats() {
+  static int on = -1;
+  if (on < 0) {
+    const char* e = getenv("TT_HEAD_XSTATS");
+    on = (e && atoi(e) == 0) ? 0 : 1;
+  }
+  return on == 1;
+}
+
 // tiles = value, TT_FILL_MAX_TILES tiles per task and launch (with
 // pinned-host homes a task's tiles take at most an eighth of the arena)
 int fill_tasks(tt_gpt2* g, const std::vector<TileRef>& tiles, float v) {
@@ -488,7 +500,11 @@ extern "C" int tt_gpt2_create(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_g
   MK(&G->nf, "nf", {B, T, d}, {bt, sq, et}, 2);
   MK(&G->z, "logits", {B, T, V}, {bt, sq, vt}, 2);
   MK(&G->ml, "attn_ml", {B / bt, T / sq, H / ht, bt * sq * ht * 2}, {1, 1, 1, bt * sq * ht * 2}, 3);
-  MK(&G->ce_parts, "ce_parts", {G->NV, G->ntok, G->rows * 3}, {1, 1, G->rows * 3}, 2);
+  // cross-entropy partials per (vocab tile, token tile): one (max, sum exp,
+  // picked) triple per row for each 64-column group of the vocab tile (the
+  // head's statistics epilogue), or one per tile (the separate statistics pass)
+  const int64_t xgroups = (vt + 63) / 64;
+  MK(&G->ce_parts, "ce_parts", {G->NV, G->ntok, xgroups * G->rows * 3}, {1, 1, xgroups * G->rows * 3}, 2);
   MK(&G->ce_lse, "ce_lse", {G->ntok, G->rows}, {1, G->rows}, 1);
   MK(&G->row_loss, "row_loss", {G->ntok, G->rows}, {1, G->rows}, 1);
   MK(&G->loss, "loss", {1}, {1}, 0);
@@ -876,7 +892,14 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
       const int64_t ti = bi + g->nb * si;
       TRY(ln_forward(g, g->h_last, lnfg, lnfb, g->lnf, g->nf, bi, si));
       // z_v = nf wte_v^T for every vocab tile v: per embd tile, one batch
-      // of equal-shape products (tile_gemm_batch), accumulating over embd tiles
+      // of equal-shape products (tile_gemm_batch), accumulating over embd
+      // tiles; the last embd tile's batch also takes the cross-entropy
+      // statistics of the finished logits in its epilogue (per row and
+      // 64-column group: max, sum exp, target logit), so the logits are not
+      // read again for them
+      tt_tensor *z = g->z, *parts = g->ce_parts;
+      const int64_t ll = L(g->labels, {bi, si});
+      const bool fused = head_xstats();
       for (int64_t ek = 0; ek < NE; ++ek) {
         std::vector<Gemm> qs;
         for (int64_t vj = 0; vj < NV; ++vj) {
@@ -888,13 +911,30 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
           q.beta = ek > 0 ? 1.f : 0.f;
           qs.push_back(q);
         }
-        TRY(submit_gemm_batch(ctx, "head", qs));
+        if (fused && ek == NE - 1) {
+          // tasks of up to 96 consecutive vocab tiles and 1 GiB of logits
+          const int64_t tile_bytes = g->rows * std::min<int64_t>(g->t.vocab, c.vocab) * (int64_t)sizeof(float);
+          const int64_t per = std::max<int64_t>(1, std::min<int64_t>(96, (int64_t(1) << 30) / tile_bytes));
+          for (int64_t v0 = 0; v0 < NV; v0 += per) {
+            const int64_t v1 = std::min(NV, v0 + per);
+            std::vector<TileArg> T;
+            for (int64_t vj = v0; vj < v1; ++vj) {
+              T.push_back(ta(qs[vj].A));
+              T.push_back(ta(qs[vj].B));
+              T.push_back(ta(qs[vj].C));
+            }
+            T.push_back({g->labels, ll});
+            for (int64_t vj = v0; vj < v1; ++vj) T.push_back({parts, L(parts, {vj, ti, 0})});
+            const tt_op_gemm sc{0, 1, TT_EPI_XSTATS, 1.f, qs[0].beta, 0};
+            TRY(submit_op(ctx, TT_OP_GEMM_BATCH, T.data(), (int)T.size(), &sc, sizeof(sc), "head", false));
+          }
+        } else {
+          TRY(submit_gemm_batch(ctx, "head", qs));
+        }
       }
-      // per-vocab-tile (max, sum exp, target logit) partials: one task and
-      // launch over all vocab tiles of the token tile (tile_xentropy_multi)
-      tt_tensor *z = g->z, *parts = g->ce_parts;
-      const int64_t ll = L(g->labels, {bi, si});
-      {
+      if (!fused) {
+        // per-vocab-tile (max, sum exp, target logit) partials: one task and
+        // launch over all vocab tiles of the token tile (tile_xentropy_multi)
         std::vector<TileArg> T = {{g->labels, ll}};
         for (int64_t vj = 0; vj < NV; ++vj) T.push_back({z, L(z, {bi, si, vj})});
         for (int64_t vj = 0; vj < NV; ++vj) T.push_back({parts, L(parts, {vj, ti, 0})});
@@ -903,7 +943,9 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
       {
         std::vector<TileArg> T = {{g->ce_lse, ti}, {g->row_loss, ti}};
         for (int64_t vj = 0; vj < NV; ++vj) T.push_back({parts, L(parts, {vj, ti, 0})});
-        TRY(submit_op(ctx, TT_OP_XENTROPY_MERGE, T.data(), (int)T.size(), nullptr, 0, "ce_merge", false));
+        const tt_op_xe_groups gs{c.vocab, std::min<int64_t>(g->t.vocab, c.vocab), 64};
+        TRY(submit_op(ctx, TT_OP_XENTROPY_MERGE, T.data(), (int)T.size(), fused ? &gs : nullptr,
+                      fused ? sizeof(gs) : 0, "ce_merge", false));
       }
       {
         const TileArg T[2] = {{g->row_loss, ti}, {g->loss, 0}};

@@ -94,6 +94,48 @@ __global__ __launch_bounds__(256) void xe_stats_multi(int rows, XeTiles P, const
   stats_row<NV, VEC>(row, P.cols[t], 0, P.off[t], 1.f, 0, P.z[t], P.ld[t], labels, parts + P.part[t] * part_stride);
 }
 
+// lse from many (max, sum exp, picked) partials: the 64-column groups of
+// the LM head's statistics epilogue. One wave per row; lane l merges the
+// partials l, l + 64, ... of the (tile, group) list in order, then the lanes
+// combine along a fixed xor tree (each step is commutative, so every lane
+// holds the same result and the order is the same on every run).
+constexpr int kMergeMaxTiles = 256;
+struct GroupList {
+  int first[kMergeMaxTiles + 1];  // first[t] = partials before tile t
+};
+
+__device__ __forceinline__ void merge3(float& m, float& s, float& p, float mb, float sb, float pb) {
+  const float mn = fmaxf(m, mb);
+  if (mn > -INFINITY) s = (m > -INFINITY ? s * expf(m - mn) : 0.f) + (mb > -INFINITY ? sb * expf(mb - mn) : 0.f);
+  m = mn;
+  p += pb;
+}
+
+__global__ __launch_bounds__(256) void xe_merge_groups(int rows, int count, GroupList G,
+                                                       const float* __restrict__ parts, int64_t stride,
+                                                       float* __restrict__ lse, float* __restrict__ row_loss) {
+  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int total = G.first[count];
+  float m = -INFINITY, sm = 0.f, pk = 0.f;
+  int t = 0;
+  for (int p = lane; p < total; p += 64) {
+    while (G.first[t + 1] <= p) ++t;
+    const float* q = parts + t * stride + ((int64_t)(p - G.first[t]) * rows + row) * 3;
+    merge3(m, sm, pk, q[0], q[1], q[2]);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float mb = __shfl_xor(m, o, 64), sb = __shfl_xor(sm, o, 64), pb = __shfl_xor(pk, o, 64);
+    merge3(m, sm, pk, mb, sb, pb);
+  }
+  if (lane == 0) {
+    const float l = m + logf(sm);
+    lse[row] = l;
+    if (row_loss) row_loss[row] = l - pk;
+  }
+}
+
 __global__ void sm_merge(int rows, int n_parts, const float* __restrict__ parts, int64_t stride,
                          float* __restrict__ lse, float* __restrict__ row_loss) {
   const int row = blockIdx.x * blockDim.x + threadIdx.x;
@@ -353,4 +395,27 @@ extern "C" int tile_xentropy_multi(void* stream, int phase, int count, int64_t r
     }
   }
   return TT_OK;
+}
+
+extern "C" int tile_xentropy_merge_groups(void* stream, int64_t rows, int count, const int64_t* v_len, int group,
+                                          const float* parts, int64_t part_stride, float* lse, float* row_loss) {
+  using tt::fail;
+  if (rows < 0 || count < 0) return fail(TT_ERR_ARG, "tile_xentropy_merge_groups: negative size");
+  if (rows == 0) return TT_OK;
+  if (rows > kMaxRows) return fail(TT_ERR_ARG, "tile_xentropy_merge_groups: rows > %lld", (long long)kMaxRows);
+  if (count < 1 || count > kMergeMaxTiles || group < 1 || !v_len || !parts || !lse)
+    return fail(TT_ERR_ARG, "tile_xentropy_merge_groups: need 1..%d tiles, group >= 1, parts and lse",
+                kMergeMaxTiles);
+  GroupList G{};
+  int64_t most = 0;
+  for (int t = 0; t < count; ++t) {
+    if (v_len[t] < 1) return fail(TT_ERR_ARG, "tile_xentropy_merge_groups: v_len of tile %d < 1", t);
+    const int64_t gt = (v_len[t] + group - 1) / group;
+    most = std::max(most, gt);
+    G.first[t + 1] = G.first[t] + (int)gt;
+  }
+  if (part_stride < most * rows * 3) return fail(TT_ERR_ARG, "tile_xentropy_merge_groups: part_stride too small");
+  hipLaunchKernelGGL(xe_merge_groups, dim3((unsigned)((rows + kWaves - 1) / kWaves)), dim3(256), 0,
+                     tt::as_stream(stream), (int)rows, count, G, parts, part_stride, lse, row_loss);
+  return tt::launch_status("tile_xentropy_merge_groups");
 }

@@ -111,8 +111,11 @@ int op_gemm(tt_ctx* ctx, const TileArg* T, int n, const tt_op_gemm& q, const cha
   }, 2.0 * m * nn * k);
 }
 
+int op_gemm_batch_xstats(tt_ctx* ctx, const TileArg* T, int n, const tt_op_gemm& q, const char* label);
+
 int op_gemm_batch(tt_ctx* ctx, const TileArg* T, int n, const tt_op_gemm& q, const char* label, bool grow) {
   const char* nm = "TT_OP_GEMM_BATCH";
+  if (q.epilogue == TT_EPI_XSTATS) return op_gemm_batch_xstats(ctx, T, n, q, label);
   if (n < 3 || n % 3) return fail(TT_ERR_ARG, "%s: needs (A, B, C) triples", nm);
   if (q.epilogue != TT_EPI_NONE) return fail(TT_ERR_ARG, "%s: no epilogue", nm);
   if (int rc = need_f32(T, n, nm)) return rc;
@@ -163,6 +166,73 @@ int op_gemm_batch(tt_ctx* ctx, const TileArg* T, int n, const tt_op_gemm& q, con
     return tile_gemm_batch_ws(s, cnt, p.transA, p.transB, m.data(), nn.data(), k, p.alpha, A.data(), lda.data(),
                               B.data(), ldb.data(), p.beta, C.data(), ldc.data(), split ? ws : nullptr,
                               split ? ctx->workspace_bytes : 0);
+  }, flops);
+}
+
+// the tied head's vocab-tile products with the cross-entropy statistics in
+// the epilogue: tiles (A, B, C) per product, labels, then one partials tile
+// per product (tile_gemm_batch_xstats)
+int op_gemm_batch_xstats(tt_ctx* ctx, const TileArg* T, int n, const tt_op_gemm& q, const char* label) {
+  const char* nm = "TT_OP_GEMM_BATCH (TT_EPI_XSTATS)";
+  if (n < 5 || n % 4 != 1) return fail(TT_ERR_ARG, "%s: needs (A, B, C) triples, labels, one partials tile each", nm);
+  const int cnt = (n - 1) / 4;
+  if (q.transA) return fail(TT_ERR_ARG, "%s: transA must be 0", nm);
+  if (int rc = need_f32(T, 3 * cnt, nm)) return rc;
+  if (int rc = need_i32(T[3 * cnt], nm, "labels")) return rc;
+  if (int rc = need_f32(T + 3 * cnt + 1, cnt, nm)) return rc;
+  const tt_tensor* zt = T[2].t;
+  const int64_t v_tile = zt->tshape[zt->ndim - 1], v_off0 = last_axis_offset(T[2]);
+  std::vector<int64_t> nn(cnt), lda(cnt), ldb(cnt), ldc(cnt);
+  int64_t m = -1, k = -1;
+  std::vector<Access> acc;
+  double flops = 0;
+  const int64_t groups = (v_tile + 63) / 64;
+  for (int u = 0; u < cnt; ++u) {
+    const TileArg &A = T[3 * u], &B = T[3 * u + 1], &C = T[3 * u + 2], &P = T[3 * cnt + 1 + u];
+    int64_t ar, ac, br, bc, cr, cc;
+    matv(A, &ar, &ac);
+    matv(B, &br, &bc);
+    matv(C, &cr, &cc);
+    const int64_t kb = q.transB ? bc : br, nu = q.transB ? br : bc;
+    if (ac != kb || nu != cc || ar != cr || (m >= 0 && (ar != m || ac != k)))
+      return fail(TT_ERR_SHAPE, "%s: product %d does not match (shared m and K)", nm, u);
+    if (C.t != zt || last_axis_offset(C) != v_off0 + u * v_tile)
+      return fail(TT_ERR_ARG, "%s: C tiles must be consecutive vocab tiles of one tensor", nm);
+    if (elems(P) < groups * ar * 3)
+      return fail(TT_ERR_SHAPE, "%s: partials tile %d holds %lld floats, %lld needed", nm, u, (long long)elems(P),
+                  (long long)(groups * ar * 3));
+    m = ar;
+    k = ac;
+    nn[u] = nu;
+    lda[u] = ac;
+    ldb[u] = bc;
+    ldc[u] = cc;
+    acc.push_back(acc_of(A, TT_R));
+    acc.push_back(acc_of(B, TT_R));
+    acc.push_back(acc_of(C, q.beta == 0.f ? TT_W : TT_RW));
+    acc.push_back(acc_of(P, TT_W));
+    flops += 2.0 * ar * nu * ac;
+  }
+  if (elems(T[3 * cnt]) < m) return fail(TT_ERR_SHAPE, "%s: labels tile smaller than the rows", nm);
+  acc.push_back(acc_of(T[3 * cnt], TT_R));
+  std::vector<TileArg> tl(T, T + n);
+  const tt_op_gemm p = q;
+  return ctx->submit(label ? label : "gemm_batch_xstats", std::move(acc), [=](hipStream_t s, void*) {
+    std::vector<const float*> A(cnt), B(cnt);
+    std::vector<float*> C(cnt);
+    for (int u = 0; u < cnt; ++u) {
+      A[u] = Fp(tl[3 * u]);
+      B[u] = Fp(tl[3 * u + 1]);
+      C[u] = Fp(tl[3 * u + 2]);
+    }
+    float* p0 = Fp(tl[3 * cnt + 1]);
+    const int64_t stride = cnt > 1 ? Fp(tl[3 * cnt + 2]) - p0 : groups * m * 3;
+    for (int u = 0; u < cnt; ++u)
+      if (Fp(tl[3 * cnt + 1 + u]) != p0 + u * stride)
+        return fail(TT_ERR_SHAPE, "%s: the partials tiles are not equally spaced", "TT_OP_GEMM_BATCH (TT_EPI_XSTATS)");
+    return tile_gemm_batch_xstats(s, cnt, p.transB, m, nn.data(), k, p.alpha, A.data(), lda.data(), B.data(),
+                                  ldb.data(), p.beta, C.data(), ldc.data(),
+                                  (const int32_t*)tl[3 * cnt].t->dev(tl[3 * cnt].lin), v_off0, v_tile, p0, stride);
   }, flops);
 }
 
@@ -600,27 +670,39 @@ int op_xe_stats(tt_ctx* ctx, const TileArg* T, int n, const char* label) {
   });
 }
 
-int op_xe_merge(tt_ctx* ctx, const TileArg* T, int n, const char* label) {
+int op_xe_merge(tt_ctx* ctx, const TileArg* T, int n, const tt_op_xe_groups* grp, const char* label) {
   const char* nm = "TT_OP_XENTROPY_MERGE";
   if (n < 3) return fail(TT_ERR_ARG, "%s: tiles lse, row_loss, parts_0..parts_{n-1}", nm);
   if (int rc = need_f32(T, n, nm)) return rc;
   const int np = n - 2;
   const int64_t rows = elems(T[0]);
   if (elems(T[1]) < rows) return fail(TT_ERR_SHAPE, "%s: row_loss smaller than lse", nm);
+  // group mode: partials tile j holds the 64-column groups of vocab tile j
+  std::vector<int64_t> vlen;
+  if (grp) {
+    if (grp->group < 1 || grp->v_tile < 1 || grp->vocab < 1 || (grp->vocab + grp->v_tile - 1) / grp->v_tile != np)
+      return fail(TT_ERR_ARG, "%s: groups need group >= 1 and one partials tile per vocab tile", nm);
+    for (int j = 0; j < np; ++j) vlen.push_back(std::min(grp->v_tile, grp->vocab - j * grp->v_tile));
+  }
   std::vector<Access> acc;
   for (int j = 0; j < np; ++j) {
-    if (elems(T[2 + j]) < 3 * rows) return fail(TT_ERR_SHAPE, "%s: partials tile %d too small", nm, j);
+    const int64_t need = 3 * rows * (grp ? (vlen[j] + grp->group - 1) / grp->group : 1);
+    if (elems(T[2 + j]) < need) return fail(TT_ERR_SHAPE, "%s: partials tile %d too small", nm, j);
     acc.push_back(acc_of(T[2 + j], TT_R));
   }
   acc.push_back(acc_of(T[0], TT_W));
   acc.push_back(acc_of(T[1], TT_W));
   std::vector<TileArg> tl(T, T + n);
+  const int group = grp ? grp->group : 0;
   return ctx->submit(label ? label : "ce_merge", std::move(acc), [=](hipStream_t s, void*) {
     float* p0 = Fp(tl[2]);
-    const int64_t stride = np > 1 ? Fp(tl[3]) - p0 : rows * 3;
+    const int64_t least = group ? 3 * rows * ((vlen[0] + group - 1) / group) : rows * 3;
+    const int64_t stride = np > 1 ? Fp(tl[3]) - p0 : least;
     for (int j = 0; j < np; ++j)
-      if (Fp(tl[2 + j]) != p0 + j * stride || stride < rows * 3)
+      if (Fp(tl[2 + j]) != p0 + j * stride || stride < least)
         return fail(TT_ERR_SHAPE, "cross-entropy merge: the partials tiles are not equally spaced");
+    if (group)
+      return tile_xentropy_merge_groups(s, rows, np, vlen.data(), group, p0, stride, Fp(tl[0]), Fp(tl[1]));
     return tile_softmax(s, TT_SM_MERGE, rows, 0, 0, 0, 1.f, 0, nullptr, 0, nullptr, p0, np, stride, Fp(tl[0]),
                         Fp(tl[1]), nullptr, 0, 1.f);
   });
@@ -1036,7 +1118,12 @@ int submit_op(tt_ctx* ctx, int op, const TileArg* T, int n, const void* sc, size
     case TT_OP_XENTROPY_STATS:
       return op_xe_stats(ctx, T, n, label);
     case TT_OP_XENTROPY_MERGE:
-      return op_xe_merge(ctx, T, n, label);
+      if (sc || size) {
+        tt_op_xe_groups q;
+        if (int rc = scal(sc, size, "TT_OP_XENTROPY_MERGE", &q)) return rc;
+        return op_xe_merge(ctx, T, n, &q, label);
+      }
+      return op_xe_merge(ctx, T, n, nullptr, label);
     case TT_OP_XENTROPY_LOSS:
     case TT_OP_XENTROPY_GRAD: {
       tt_op_xentropy q;

@@ -10,14 +10,15 @@ from __future__ import annotations
 from ._lib import (TT_EPI_NONE, check, lib, ptr, stream_handle, TT_EPI_BIAS, TT_EPI_RES, TT_EPI_GELU,  # noqa: F401
                    TT_EPI_GELU_BWD, TT_LN_PARTIAL, TT_LN_MERGE, TT_LN_APPLY, TT_LN_FUSED, TT_SM_STATS,
                    TT_SM_MERGE, TT_SM_APPLY, TT_XE_LOSS, TT_XE_GRAD, TT_XE_STATS, TT_ATT_PREP, TT_ATT_GRAD,
-                   TT_EMB_TOKEN, TT_EMB_POS, TT_PROBE_READ, TT_PROBE_WRITE, TT_PROBE_COPY, TT_PROBE_NONTEMPORAL)
+                   TT_EMB_TOKEN, TT_EMB_POS, TT_EPI_XSTATS, TT_PROBE_READ, TT_PROBE_WRITE, TT_PROBE_COPY, TT_PROBE_NONTEMPORAL)
 
 __all__ = [
     "tile_gemm", "tile_gemm_ws", "tile_gemm_workspace", "tile_gemm_ksum", "tile_gemm_batch", "tile_gemm_batch_ws",
     "tile_gemm_batch_workspace", "tile_gemm_ksum_ex", "tile_layernorm_fwd",
     "tile_layernorm_bwd", "tile_layernorm_bwd_workspace", "tile_softmax",
     "tile_xentropy", "tile_xentropy_multi", "tile_attention_fwd", "tile_attention_bwd",
-    "tile_attention_bwd_workspace", "tile_attention_bwd_ws", "tile_gemm_ksum_workspace", "tt_probe_hbm",
+    "tile_attention_bwd_workspace", "tile_attention_bwd_ws", "tile_gemm_ksum_workspace", "tt_probe_hbm", "tile_gemm_batch_xstats",
+    "tile_xentropy_merge_groups", "TT_EPI_XSTATS",
     "TT_PROBE_READ", "TT_PROBE_WRITE", "TT_PROBE_COPY", "TT_PROBE_NONTEMPORAL", "tile_fused_adamw",
     "tile_fused_adamw_multi",
     "tile_adamw_advance", "tile_sgd", "tile_sgd_multi",
@@ -99,6 +100,23 @@ def tile_gemm_batch_ws(stream, transA, transB, ms, ns, k, alpha, As, ldas, Bs, l
     cnt, m, n, a, la, b, lb, c, lc = _batch_args(ms, ns, As, ldas, Bs, ldbs, Cs, ldcs)
     return check(lib.tile_gemm_batch_ws(stream_handle(stream), cnt, transA, transB, m, n, k, alpha, a, la, b, lb,
                                         beta, c, lc, ptr(workspace), workspace_bytes))
+
+
+def tile_gemm_batch_xstats(stream, transB, m, ns, k, alpha, As, ldas, Bs, ldbs, beta, Cs, ldcs, labels, v_off0,
+                           v_tile, parts, part_stride):
+    """Batched head products with the cross-entropy statistics of each
+    64-column group of every C in the epilogue."""
+    cnt, _, n, a, la, b, lb, c, lc = _batch_args([m] * len(Cs), ns, As, ldas, Bs, ldbs, Cs, ldcs)
+    return check(lib.tile_gemm_batch_xstats(stream_handle(stream), cnt, transB, m, n, k, alpha, a, la, b, lb, beta, c,
+                                            lc, ptr(labels), v_off0, v_tile, ptr(parts), part_stride))
+
+
+def tile_xentropy_merge_groups(stream, rows, v_lens, group, parts, part_stride, lse, row_loss=None):
+    import ctypes as C_
+    cnt = len(v_lens)
+    arr = (C_.c_int64 * max(cnt, 1))(*[int(x) for x in v_lens])
+    return check(lib.tile_xentropy_merge_groups(stream_handle(stream), rows, cnt, arr, group, ptr(parts), part_stride,
+                                                ptr(lse), ptr(row_loss)))
 
 
 def tile_gemm_batch_workspace(ms, ns, k):
