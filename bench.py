@@ -758,6 +758,7 @@ def executor_figures(w, model, ctx, tok, hp, streams, ms, st, steps, busy_steps=
     events, 1 - (union of their GPU intervals) / (first start to last end)."""
     from tile_task_transformer_amd import _lib as L
     from tile_task_transformer_amd.runtime import Context, GPT2
+    import tempfile
     ntask = model.task_count()
     with Context(L.TT_DEVICE_DRYRUN, n_streams=streams, window=4096) as dctx:
         dm = GPT2(dctx, w.shape, w.tiles)
@@ -766,6 +767,12 @@ def executor_figures(w, model, ctx, tok, hp, streams, ms, st, steps, busy_steps=
         for _ in range(2):
             dm.step(None, **hp)
         dry = (time.perf_counter() - t0) / 2
+        dm.close()
+    with tempfile.TemporaryDirectory() as tmp, Context(L.TT_DEVICE_DRYRUN, n_streams=streams, window=4096) as dctx:
+        dctx.record(True)
+        dm = GPT2(dctx, w.shape, w.tiles)
+        dm.step(None, **hp)
+        depth = dag_depth(dctx.dump_dag(os.path.join(tmp, "step.jsonl")))
         dm.close()
     ctx.profile("*", every=1)
     for _ in range(busy_steps):
@@ -782,7 +789,26 @@ def executor_figures(w, model, ctx, tok, hp, streams, ms, st, steps, busy_steps=
         "host_submit_ms_per_step": round(1e3 * st["submit_seconds"] / steps, 3),
         "gpu_idle_frac": round(1.0 - busy["busy_ms"] / span, 4) if span > 0 else None,
         "timed_tasks": busy["tasks"], "timed_span_ms_per_step": round(span / busy_steps, 3),
+        **depth,
     }
+
+
+def dag_depth(dag) -> dict:
+    """Depth of one step's task graph (a dry-run dump): the longest chain of
+    dependent tasks, and the flops on the costliest chain over all flops (1 /
+    that bounds the speedup any launch order or stream count could get from
+    running independent tasks side by side, at equal throughput per flop)."""
+    cp, dp = {}, {}
+    for r in dag:  # ids ascend in submission order, a topological order
+        ds = [d for d in r["deps"] if d in cp]
+        cp[r["id"]] = r.get("cost", 0.0) + max((cp[d] for d in ds), default=0.0)
+        dp[r["id"]] = 1 + max((dp[d] for d in ds), default=0)
+    total = sum(r.get("cost", 0.0) for r in dag)
+    levels = {}
+    for v in dp.values():
+        levels[v] = levels.get(v, 0) + 1
+    return {"dag_depth_tasks": max(dp.values(), default=0), "dag_max_width": max(levels.values(), default=0),
+            "critical_path_flop_frac": round(max(cp.values(), default=0.0) / total, 4) if total else None}
 
 
 if __name__ == "__main__":

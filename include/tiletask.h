@@ -905,7 +905,8 @@ int tt_ctx_join_stream(tt_ctx* ctx, void* stream);
  * error, if any. */
 int tt_wait(tt_ctx* ctx);
 /* Write the recorded task graph as JSON lines: one object per task with
- * id, label, stream, deps and accesses (dry-run and real contexts). */
+ * id, label, stream, cost (the task's flop estimate, 0 for memory-bound
+ * tasks), deps and accesses (dry-run and real contexts). */
 int tt_dump_dag(tt_ctx* ctx, const char* path);
 
 /* Per-task GPU timing. Tasks whose label equals label_filter ("*" = every

@@ -298,6 +298,7 @@ int tt_ctx::flush() {
       r.label = task.label;
       r.stream = s;
       r.deps = task.deps;
+      r.cost = task.cost;
       for (auto& a : task.acc) r.acc.push_back({a.ref.t->id, {a.ref.lin, a.mode}});
       records.push_back(std::move(r));
     }
@@ -1233,7 +1234,8 @@ int tt_dump_dag(tt_ctx* c, const char* path) {
   std::ofstream f(path);
   if (!f) return fail(TT_ERR_ARG, "tt_dump_dag: cannot open %s", path);
   for (auto& r : c->records) {
-    f << "{\"id\":" << r.id << ",\"label\":\"" << r.label << "\",\"stream\":" << r.stream << ",\"deps\":[";
+    f << "{\"id\":" << r.id << ",\"label\":\"" << r.label << "\",\"stream\":" << r.stream
+      << ",\"cost\":" << r.cost << ",\"deps\":[";
     for (size_t i = 0; i < r.deps.size(); ++i) f << (i ? "," : "") << r.deps[i];
     f << "],\"acc\":[";
     for (size_t i = 0; i < r.acc.size(); ++i)

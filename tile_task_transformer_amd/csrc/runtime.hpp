@@ -117,6 +117,7 @@ struct TaskRecord {        // kept for tt_dump_dag
   int stream;
   std::vector<int64_t> deps;
   std::vector<std::pair<int64_t, std::pair<int64_t, int>>> acc;  // tensor id, tile lin, mode
+  double cost = 0.0;       // flop estimate (0 for memory-bound tasks)
 };
 
 }  // namespace tt
