@@ -570,7 +570,7 @@ __global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_bwd_dq_ds(AttnGeom g,
 }
 
 // dK, dV: a group of 32 keys per wave pair; streams query blocks (Q, dO, lse, D).
-template <int HD>
+template <int HD, bool STORE_DS>
 __global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_bwd_dkv(AttnGeom g, const float* __restrict__ Q,
                                                       const float* __restrict__ K, const float* __restrict__ V,
                                                       const float* __restrict__ dO, const float* __restrict__ lse,
@@ -623,6 +623,12 @@ __global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_bwd_dkv(AttnGeom g, c
   const bool wave_live = k0w < g.k_len;
   const int64_t wave_kmin = g.k_off + k0w;
   const int64_t wave_kmax = g.k_off + min(g.k_len - 1, k0w + 31);
+  // dS blocks of this wave's 32 keys: block (query group qg) at dsk + qg *
+  // ds_qstride; the lane's column l32 and its half's rows 4h .. folded in
+  const int nk32 = (g.k_len + 31) / 32;
+  const int64_t ds_qstride = (int64_t)nk32 * 1024;
+  float* const dsk = STORE_DS ? dsw + ((int64_t)bh * ((g.q_len + 31) / 32) * nk32 + k0w / 32) * 1024 + 4 * half * 32 + l32
+                              : nullptr;
 
   zero_pad<HD, LD>(Qs);
   zero_pad<HD, LD>(Ds);
@@ -680,12 +686,10 @@ __global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_bwd_dkv(AttnGeom g, c
       const bool edge = qb0 + 31 >= g.q_len || g.q_off + qb0 < wave_kmax;
       // lse (log2 units) and D of the 16 query rows held by this lane's
       // registers: rows 8*(r/4) + 4*half + r%4, i.e. four 16-byte reads each
+      // (D read only after the dV products, so the two are not live together)
       f32x4 lv[4], dv[4];
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        lv[g4] = *reinterpret_cast<const f32x4*>(lsb + 8 * g4 + 4 * half);
-        dv[g4] = *reinterpret_cast<const f32x4*>(ddb + 8 * g4 + 4 * half);
-      }
+      for (int g4 = 0; g4 < 4; ++g4) lv[g4] = *reinterpret_cast<const f32x4*>(lsb + 8 * g4 + 4 * half);
       // query row ql of this block sees the lane's key iff ql >= dlim
       const int dlim = (int)max((int64_t)-1, min((int64_t)32, kpos - g.q_off - qb0));
       const int qlim = g.q_len - qb0;  // rows >= qlim are past the tile
@@ -702,12 +706,13 @@ __global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_bwd_dkv(AttnGeom g, c
         for (int r = 0; r < 16; ++r)
           dkv[NEB + eb] = mfma(dsb[kidx(r, half) * LD + eb * 32 + l32], s[r], dkv[NEB + eb]);  // dV^T += dO^T P
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] *= dp[r] - dv[r >> 2][r & 3];  // dS, in place of P
-      if (dsw) {  // the 32 x 32 block of dS for the dQ kernel, row-major by query (two 128-byte rows per store)
-        const int nq32 = (g.q_len + 31) / 32, nk32 = (g.k_len + 31) / 32;
-        float* blk = dsw + (((int64_t)bh * nq32 + qb0 / 32) * nk32 + k0w / 32) * 1024 + l32;
+      for (int g4 = 0; g4 < 4; ++g4) dv[g4] = *reinterpret_cast<const f32x4*>(ddb + 8 * g4 + 4 * half);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) blk[kidx(r, half) * 32] = s[r];
+      for (int r = 0; r < 16; ++r) s[r] *= dp[r] - dv[r >> 2][r & 3];  // dS, in place of P
+      if constexpr (STORE_DS) {  // the 32 x 32 block of dS for the dQ kernel, row-major by query (two 128-byte rows per store)
+        float* blk = dsk + (int64_t)(qb0 / 32) * ds_qstride;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) blk[(8 * (r >> 2) + (r & 3)) * 32] = s[r];
       }
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb)
@@ -827,11 +832,12 @@ extern "C" int tile_attention_bwd_ws(void* stream, int phase, int64_t batch, int
   // without, the dQ kernel recomputes S and dP
 #define TT_ATT_BWD(HD)                                                                                          \
   if (stored) {                                                                                                 \
-    hipLaunchKernelGGL(attn_bwd_dkv<HD>, gk, block, 0, s, g, Q, K, V, dO, lse, Dvec, dK, dV, acc_dkv, dsw);    \
+    hipLaunchKernelGGL((attn_bwd_dkv<HD, true>), gk, block, 0, s, g, Q, K, V, dO, lse, Dvec, dK, dV, acc_dkv, dsw); \
     hipLaunchKernelGGL(attn_bwd_dq_ds<HD>, gq, block, 0, s, g, K, (const float*)dsw, dQ, acc_dq);               \
   } else {                                                                                                      \
     hipLaunchKernelGGL(attn_bwd_dq<HD>, gq, block, 0, s, g, Q, K, V, dO, lse, Dvec, dQ, acc_dq);               \
-    hipLaunchKernelGGL(attn_bwd_dkv<HD>, gk, block, 0, s, g, Q, K, V, dO, lse, Dvec, dK, dV, acc_dkv, nullptr); \
+    hipLaunchKernelGGL((attn_bwd_dkv<HD, false>), gk, block, 0, s, g, Q, K, V, dO, lse, Dvec, dK, dV, acc_dkv,    \
+                       nullptr);                                                                                \
   }
   switch (hd) {
     case 16: TT_ATT_BWD(16); break;
