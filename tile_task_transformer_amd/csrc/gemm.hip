@@ -200,11 +200,25 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, int b, float* lds)
   const int split = b / ntile;
   b -= split * ntile;
   constexpr int GROUP = 8;
-  const int in_group = GROUP * grid_n;
-  const int first_m = (b / in_group) * GROUP;
-  const int gsz = min(grid_m - first_m, GROUP);
-  const int tm = first_m + (b % in_group) % gsz;
-  const int tn = (b % in_group) / gsz;
+  int tm, tn;
+  if (TA) {
+    // A stored [k][m] (the weight gradients: A = an activation or logits
+    // tile read down its columns): grouped along N, so the blocks that share
+    // an A panel run side by side and find it in L2 (25 products 2048 x
+    // 2048 x 4096: 80.9 -> 81.8 % of the fp32 peak; 16 products 8192 x 2048
+    // x 4096: 84.5 -> 85.2 %)
+    const int in_group = GROUP * grid_m;
+    const int first_n = (b / in_group) * GROUP;
+    const int gsz = min(grid_n - first_n, GROUP);
+    tn = first_n + (b % in_group) % gsz;
+    tm = (b % in_group) / gsz;
+  } else {
+    const int in_group = GROUP * grid_n;
+    const int first_m = (b / in_group) * GROUP;
+    const int gsz = min(grid_m - first_m, GROUP);
+    tm = first_m + (b % in_group) % gsz;
+    tn = (b % in_group) / gsz;
+  }
   const int m0 = tm * BM, n0 = tn * BN;
   const int kbeg = split * g.kchunk;
   const int kend = min(g.k, kbeg + g.kchunk);
