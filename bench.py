@@ -57,12 +57,12 @@ HBM_PEAK = 8000.0       # GB/s
 # on gfx950: factor 2.0; WRITE_SIZE: 1.0). Valid only for the kernel source
 # the counters were taken on (sha256 prefix of the file); else null.
 TRAFFIC = {
-    ("gpt2_small", "head_dw"): {"source": "tile_task_transformer_amd/csrc/gemm.hip", "sha256": "fa7bf9abd8f9b062",
-                                "fetch_kib": 1689378.8, "fetch_factor": 2.0,
-                                "write_kib": 150771.0, "write_factor": 1.0},
     # profiles/gemm_ksum_fc_wide4_traffic.md
-    ("wide4", "fc"): {"source": "tile_task_transformer_amd/csrc/gemm.hip", "sha256": "43ecee1903aacb99",
-                      "fetch_kib": 1050161.9, "fetch_factor": 2.0, "write_kib": 262144.0, "write_factor": 1.0},
+    ("wide4", "fc"): {"source": "tile_task_transformer_amd/csrc/gemm.hip", "sha256": "e13227a89603814d",
+                      "fetch_kib": 1050257.7, "fetch_factor": 2.0, "write_kib": 262144.0, "write_factor": 1.0},
+    # profiles/gemm_batch_head_gpt2_small_traffic.md
+    ("gpt2_small", "head"): {"source": "tile_task_transformer_amd/csrc/gemm.hip", "sha256": "e13227a89603814d",
+                             "fetch_kib": 974927.4, "fetch_factor": 2.0, "write_kib": 842536.2, "write_factor": 1.0},
 }
 
 
