@@ -15,9 +15,9 @@ from tile_task_transformer_amd.runtime import Context, GPT2  # noqa: E402
 pytestmark = pytest.mark.gpu
 
 
-def _run(shape, tiles, params, tokens, home, budget, steps=2, window=0):
+def _run(shape, tiles, params, tokens, home, budget, steps=2, window=0, streams=4):
     specs = synth.param_specs(shape)
-    with Context(0, n_streams=4, window=window, device_budget=budget) as ctx:
+    with Context(0, n_streams=streams, window=window, device_budget=budget) as ctx:
         model = GPT2(ctx, shape, tiles, param_home=home)
         model.set_params(params, specs)
         tok = torch.from_numpy(tokens.astype(np.int32)).cuda()
@@ -62,6 +62,27 @@ def test_pinned_step_over_many_small_windows_is_bitwise_equal_to_hbm():
         for name in ref[key]:
             assert np.array_equal(got[key][name], ref[key][name]), (key, name)
     assert got["stats"]["evictions"] > 0
+
+
+@pytest.mark.parametrize("streams", [1, 4])
+def test_pinned_mid_size_step_with_prefetch_is_bitwise_equal_to_hbm(streams):
+    """Kernels long enough for copies and compute to overlap (d 512, inner
+    2048, vocab 8000, 2 x 512 tokens, tiles of 128 x 256): each task waits
+    only for the copy-stream point at which its own tiles became ready, so a
+    missing order between a prefetch, an eviction and the tasks around it
+    would show here as a difference from the all-in-HBM step."""
+    shape = synth.GPT2Shape(2, 8000, 512, 8, 2048, 512, 2)
+    tiles = synth.Tiles(1, 128, 256, 512, 4, 1024)
+    params = synth.init_params(shape, seed=3)
+    tokens = synth.token_stream(shape, seed=4)
+    ref = _run(shape, tiles, params, tokens, L.TT_HOME_DEVICE, 0, steps=2, streams=streams)
+    got = _run(shape, tiles, params, tokens, L.TT_HOME_PINNED_HOST, 24 << 20, steps=2, streams=streams)
+    assert got["loss"] == ref["loss"]
+    for key in ("params", "grads", "m", "v"):
+        for name in ref[key]:
+            assert np.array_equal(got[key][name], ref[key][name]), (key, name)
+    st = got["stats"]
+    assert st["evictions"] > 0 and st["prefetches"] > 0, st
 
 
 def test_fresh_token_buffer_every_step():

@@ -511,11 +511,11 @@ int tt_ctx::evict_one(bool spare_prefetched, int64_t later_than) {
   arena_release(r.off, r.bytes);
   r.dev = nullptr;
   r.dev_valid = false;
+  r.ready_event = -1;
   r.users.clear();
   resident[best] = resident.back();
   resident.pop_back();
   stats.evictions++;
-  copy_pending = true;
   return TT_OK;
 }
 
@@ -523,6 +523,12 @@ int tt_ctx::evict_one(bool spare_prefetched, int64_t later_than) {
 // `soft`/`use` as for arena_alloc (returns 1 when a prefetch finds no room)
 static int stage_tile(tt_ctx* c, tt_tensor* t, int64_t lin, bool load, bool soft, int64_t use) {
   tt::Residency& r = t->res[lin];
+  auto mark = [&]() {  // copy-stream work for this tile: it gets the next ready event
+    if (!r.staged) {
+      r.staged = true;
+      c->staged.push_back(&r);
+    }
+  };
   if (!r.dev) {
     size_t off;
     const size_t bytes = (size_t)t->tile_elems(lin) * 4;
@@ -533,9 +539,11 @@ static int stage_tile(tt_ctx* c, tt_tensor* t, int64_t lin, bool load, bool soft
     r.dev_valid = false;
     c->resident.push_back(tt::TileRef{t, lin});
     // whoever writes the range next (this copy, or the task through the
-    // copy stream's event) comes after write-backs that freed it
+    // tile's ready event on the copy stream) comes after the write-backs
+    // that freed it, and after the users of evicted occupants (the copy
+    // stream waited for them when they were evicted)
     if (int rc = c->wait_dirty_free(r.off, r.bytes, c->copy_stream)) return rc;
-    c->copy_pending = true;
+    mark();
   }
   if (load && !r.dev_valid) {
     if (!r.host_valid) return fail(TT_ERR_STATE, "tile has neither a valid host nor device copy");
@@ -544,8 +552,24 @@ static int stage_tile(tt_ctx* c, tt_tensor* t, int64_t lin, bool load, bool soft
                               c->copy_stream));
     c->stats.h2d_bytes += t->tile_elems(lin) * 4;
     r.dev_valid = true;
-    c->copy_pending = true;
+    mark();
   }
+  return TT_OK;
+}
+
+// one event on the copy stream after everything staged since the last one
+int tt_ctx::mark_ready() {
+  if (staged.empty()) return TT_OK;
+  int ev;
+  if (int rc = acquire_event(&ev)) return rc;
+  TT_HIP_TRY(hipEventRecord(events[ev], copy_stream));
+  if ((int)ready_seq.size() <= ev) ready_seq.resize(ev + 1, 0);
+  ready_seq[ev] = ++ready_count;
+  for (tt::Residency* r : staged) {
+    r->ready_event = ev;
+    r->staged = false;
+  }
+  staged.clear();
   return TT_OK;
 }
 
@@ -564,19 +588,20 @@ int tt_ctx::make_resident(tt::Task& task, hipStream_t s) {
     if (t->home != TT_HOME_PINNED_HOST) continue;
     if (int rc = stage_tile(this, t, a.ref.lin, (a.mode & TT_R) != 0, false, task.id)) return rc;
   }
-  // the task's stream runs after every copy (and eviction) queued so far
-  if (copy_pending) {
-    int ev;
-    if (int rc = acquire_event(&ev)) return rc;
-    TT_HIP_TRY(hipEventRecord(events[ev], copy_stream));
-    copy_event = ev;
-    copy_pending = false;
-  }
-  if (copy_event >= 0) {
+  // the task's stream runs after the copy-stream point at which the last of
+  // its tiles became ready (copy-stream events complete in order)
+  if (int rc = mark_ready()) return rc;
+  int need = -1;
+  for (auto& a : task.acc)
+    if (a.ref.t->home == TT_HOME_PINNED_HOST) {
+      const int ev = a.ref.t->res[a.ref.lin].ready_event;
+      if (ev >= 0 && (need < 0 || ready_seq[ev] > ready_seq[need])) need = ev;
+    }
+  if (need >= 0) {
     const int si = (int)(std::find(streams.begin(), streams.end(), s) - streams.begin());
-    if (si < n_streams && waited_copy[si] != copy_event) {
-      TT_HIP_TRY(hipStreamWaitEvent(s, events[copy_event], 0));
-      waited_copy[si] = copy_event;
+    if (si < n_streams && waited_copy[si] < ready_seq[need]) {
+      TT_HIP_TRY(hipStreamWaitEvent(s, events[need], 0));
+      waited_copy[si] = ready_seq[need];
     }
   }
   for (auto& a : task.acc) {
@@ -671,10 +696,13 @@ int tt_ctx::prefetch(size_t i) {
       planned_bytes += (size_t)t->tile_elems(a.ref.lin) * 4;
       if (planned_bytes > arena_bytes / 4) return TT_OK;
       const int rc = stage_tile(this, t, a.ref.lin, true, true, pending[j].id);
-      if (rc == 1) return TT_OK;  // no room without evicting what is needed sooner: stop here
+      if (rc == 1) return mark_ready();  // no room without evicting what is needed sooner: stop here
       if (rc) return rc;
       stats.prefetches++;
     }
+    // task j's tiles get their own ready event: task j + 1 does not wait for
+    // the copies of the tasks after it
+    if (int rc = mark_ready()) return rc;
   }
   return TT_OK;
 }
@@ -719,7 +747,10 @@ void tt_ctx::forget_launched() {
   // are only read, such as parameters in steps without an update, would
   // otherwise collect reader ids without bound)
   for (auto& t : tensors) {
-    for (auto& r : t->res) r.wb_event = -1;
+    for (auto& r : t->res) {
+      r.wb_event = -1;
+      r.ready_event = -1;  // every copy has completed; the event is recycled
+    }
     for (auto& st : t->state) st.readers.clear();
   }
   dirty_free.clear();
@@ -727,9 +758,10 @@ void tt_ctx::forget_launched() {
   launched.clear();
   launched_base = next_id;
   events_used = 0;
-  copy_event = -1;
-  copy_pending = false;
-  std::fill(waited_copy.begin(), waited_copy.end(), -1);
+  ready_count = 0;
+  for (tt::Residency* r : staged) r->staged = false;  // (only after a failed staging)
+  staged.clear();
+  std::fill(waited_copy.begin(), waited_copy.end(), 0);
   for (auto& w : waited) std::fill(w.begin(), w.end(), 0);
   for (int s = 0; s < n_streams; ++s) {
     stream_seq[s] = 0;
@@ -847,7 +879,7 @@ int tt_ctx_create(int device, int n_streams, int window, size_t device_budget_by
   c->stream_seq.assign(n_streams, 0);
   c->last_assigned.assign(n_streams, -1);
   c->waited.assign(n_streams, std::vector<int64_t>(n_streams, 0));
-  c->waited_copy.assign(n_streams, -1);
+  c->waited_copy.assign(n_streams, 0);
   if (!c->dryrun) {
     if (device < 0) return fail(TT_ERR_ARG, "tt_ctx_create: bad device %d", device);
     TT_HIP_TRY(hipSetDevice(device));

@@ -43,6 +43,8 @@ struct Residency {
   std::vector<int64_t> future;     // ids of the tasks in the launching window that access it (ascending)
   size_t fpos = 0;                 // first entry of `future` not yet passed
   int wb_event = -1;               // event after its last write-back (host copy in flight until then)
+  int ready_event = -1;            // copy-stream event after which the device copy is usable (-1: already)
+  bool staged = false;             // in tt_ctx::staged (awaiting its ready event)
 };
 
 }  // namespace tt
@@ -168,9 +170,15 @@ struct tt_ctx {
   std::map<size_t, size_t> arena_free;  // offset -> size
   std::vector<tt::TileRef> resident;    // tiles with a device copy
   int64_t cur_task = -1;                // id of the task being launched
-  bool copy_pending = false;            // copy-stream work not yet covered by copy_event
-  int copy_event = -1;                  // event after the latest copy-stream work
-  std::vector<int> waited_copy;         // per stream: copy_event it already waited on
+  // copy-stream ordering of staged tiles: each tile gets the event recorded
+  // right after its own staging (its range freed of earlier occupants, its
+  // data copied in), so a task waits for its own tiles and not for the
+  // prefetches of later tasks queued behind them
+  std::vector<tt::Residency*> staged;   // staged since the last ready event
+  std::vector<int> ready_seq;           // per event index: its position among ready events (ascending)
+  int ready_count = 0;                  // ready events recorded since the last drain
+  std::vector<int> waited_copy;         // per stream: highest ready position it waited on
+  int mark_ready();
   int arena_init();
   int arena_alloc(size_t bytes, size_t* off, bool soft, int64_t use);
   void arena_release(size_t off, size_t bytes);
