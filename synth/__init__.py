@@ -27,7 +27,7 @@ from typing import Dict, List, Tuple
 import numpy as np
 
 __all__ = [
-    "GPT2Shape", "Tiles", "Workload", "WORKLOADS", "param_specs",
+    "GPT2Shape", "Tiles", "Workload", "WORKLOADS", "LLAMA_WORKLOADS", "param_specs", "llama_param_specs",
     "init_params", "init_param", "token_stream", "split_tokens",
     "rand_normal", "rand_uniform",
 ]
@@ -97,6 +97,20 @@ WORKLOADS: Dict[str, Workload] = {
 }
 
 
+# LLaMA-style models (RMSNorm, rotary embedding, SwiGLU MLP, untied head):
+# n_inner is the SwiGLU hidden width (about 8/3 d, a multiple of 256)
+LLAMA_WORKLOADS: Dict[str, Workload] = {
+    "llama_tiny": Workload("llama_tiny", GPT2Shape(1, 256, 64, 4, 176, 32, 2),
+                           Tiles(2, 32, 32, 32, 4, 32)),
+    # GPT2-small's width and depth with a LLaMA block and a 32000-token vocabulary
+    "llama_small": Workload("llama_small", GPT2Shape(12, 32000, 768, 12, 2048, 1024, 4),
+                            Tiles(4, 1024, 768, 2048, 12, 768)),
+    # the wide model's width with a LLaMA block (inner 22016, as LLaMA's d 8192 models)
+    "llama_wide4": Workload("llama_wide4", GPT2Shape(4, 32000, 8192, 64, 22016, 1024, 4),
+                            Tiles(4, 1024, 2048, 8192, 16, 2048)),
+}
+
+
 def param_specs(s: GPT2Shape) -> List[Tuple[str, Tuple[int, ...], str]]:
     """Ordered GPT2 parameter list: (name, shape, init kind).
 
@@ -123,6 +137,29 @@ def param_specs(s: GPT2Shape) -> List[Tuple[str, Tuple[int, ...], str]]:
     return specs
 
 
+def llama_param_specs(s: GPT2Shape) -> List[Tuple[str, Tuple[int, ...], str]]:
+    """Ordered LLaMA-style parameter list: (name, shape, init kind).
+
+    wte, then per block the attention RMSNorm gain, the [d, 3d] QKV weight
+    (column blocks q | k | v as for GPT2), w_o, the MLP RMSNorm gain, the
+    SwiGLU gate and up weights [d, I] and the down weight [I, d], then the
+    final RMSNorm gain and the untied head [V, d]. No biases, no position
+    table. `n_inner` is the SwiGLU hidden width.
+    """
+    d, i_, v = s.n_embd, s.n_inner, s.vocab
+    specs: List[Tuple[str, Tuple[int, ...], str]] = [("wte", (v, d), "normal")]
+    for l in range(s.n_layer):
+        p = f"h{l}."
+        specs += [
+            (p + "attn_norm_g", (d,), "ones"), (p + "w_qkv", (d, 3 * d), "normal"),
+            (p + "w_o", (d, d), "normal"), (p + "mlp_norm_g", (d,), "ones"),
+            (p + "w_gate", (d, i_), "normal"), (p + "w_up", (d, i_), "normal"),
+            (p + "w_down", (i_, d), "normal"),
+        ]
+    specs += [("norm_f_g", (d,), "ones"), ("w_head", (v, d), "normal")]
+    return specs
+
+
 def init_param(spec: Tuple[str, Tuple[int, ...], str], index: int, seed: int = 0,
                std: float = 0.02) -> np.ndarray:
     """One parameter tensor as float32 (normal draws are made in float64)."""
@@ -135,11 +172,12 @@ def init_param(spec: Tuple[str, Tuple[int, ...], str], index: int, seed: int = 0
     return (rng.standard_normal(shape) * std).astype(np.float32)
 
 
-def init_params(s: GPT2Shape, seed: int = 0, std: float = 0.02, threads: int = 1) -> Dict[str, np.ndarray]:
-    """Every parameter, in param_specs order. Each tensor has its own seeded
-    stream, so `threads` (drawing several tensors at once) changes nothing
-    but the wall time."""
-    specs = param_specs(s)
+def init_params(s: GPT2Shape, seed: int = 0, std: float = 0.02, threads: int = 1,
+                specs=None) -> Dict[str, np.ndarray]:
+    """Every parameter, in param_specs order (or the order of `specs`, e.g.
+    llama_param_specs). Each tensor has its own seeded stream, so `threads`
+    (drawing several tensors at once) changes nothing but the wall time."""
+    specs = param_specs(s) if specs is None else specs
     if threads <= 1:
         return {spec[0]: init_param(spec, i, seed, std) for i, spec in enumerate(specs)}
     from concurrent.futures import ThreadPoolExecutor
