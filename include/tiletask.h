@@ -310,6 +310,50 @@ int tile_layernorm_bwd_multi(void* stream, int count, int64_t rows, const int64_
                              size_t workspace_bytes);
 size_t tile_layernorm_bwd_multi_workspace(int64_t rows, int64_t total_cols);
 
+/* tile_rmsnorm_fwd / tile_rmsnorm_bwd -- the LLaMA block's normalisation
+ * (RMSNorm: the published LLaMA architecture; the NNTile README's notebook
+ * list names LLaMa as its second model) over one block of rows whose
+ * features are split over `count` tiles (1..16), with the tile layout and
+ * pointer conventions of tile_layernorm_fwd_multi above (widths multiples
+ * of 4, equal but for a narrower last tile, at most 16384 in all; DEVICE
+ * data aligned to 16 bytes; HOST pointer arrays and cols).
+ *   forward:  rstd[r] = 1 / sqrt(mean over the row's features of x^2 + eps);
+ *             y = x * rstd * gamma (no mean, no shift).
+ *   backward: with n = x * rstd and dn = dy * gamma,
+ *             dx = rstd * (dn - n * mean(dn * n)), added to dx's contents
+ *             when dx_acc != 0; dgamma += sum_rows dy * n in a fixed order
+ *             through `workspace` (at least tile_rmsnorm_bwd_workspace(rows,
+ *             sum of cols) bytes, not used concurrently by another launch).
+ * TT_ERR_ARG / TT_ERR_SHAPE for bad arguments, before anything runs. */
+int tile_rmsnorm_fwd(void* stream, int count, int64_t rows, const int64_t* cols, const float* const* x,
+                     const float* const* gamma, float* rstd, float* const* y, float eps);
+int tile_rmsnorm_bwd(void* stream, int count, int64_t rows, const int64_t* cols, const float* const* dy,
+                     const float* const* x, const float* const* gamma, const float* rstd, float* const* dx,
+                     int dx_acc, float* const* dgamma, void* workspace, size_t workspace_bytes);
+size_t tile_rmsnorm_bwd_workspace(int64_t rows, int64_t total_cols);
+
+/* tile_rope_table / tile_rope -- rotary position embedding of q and k (the
+ * published LLaMA architecture; the README's notebook list names LLaMa).
+ * tile_rope_table fills table[t*hd + i] = cos(t * base^(-2i/hd)) and
+ * table[t*hd + hd/2 + i] = sin(same) for t < seq, i < hd/2 (DEVICE float
+ * [seq, hd], angles and functions in double precision, rounded once).
+ * tile_rope rotates, in place, the pair (x_i, x_{i+hd/2}) of every head of
+ * every row of a q or k tile: x is DEVICE [rows, heads, hd] (rows = batch
+ * x length of the tile, row-major, 16-byte aligned); row r has position
+ * pos_off + r % seq_len, which must lie below table_rows. inverse != 0
+ * applies the transposed rotation (the backward). hd in {16, 32, 64, 128}.
+ * TT_ERR_ARG / TT_ERR_SHAPE for bad arguments. */
+int tile_rope_table(void* stream, int64_t seq, int64_t hd, double base, float* table);
+int tile_rope(void* stream, float* x, int64_t rows, int64_t heads, int64_t hd, int64_t seq_len,
+              int64_t pos_off, const float* table, int64_t table_rows, int inverse);
+/* tile_swiglu_fwd / tile_swiglu_bwd -- the LLaMA MLP's gate over n
+ * contiguous DEVICE floats: h = silu(a) * b, silu(a) = a / (1 + exp(-a));
+ * backward da = dh * b * silu'(a), db = dh * silu(a). da and db may be a
+ * and b themselves (in place). TT_ERR_ARG for n < 0 or null pointers. */
+int tile_swiglu_fwd(void* stream, int64_t n, const float* a, const float* b, float* h);
+int tile_swiglu_bwd(void* stream, int64_t n, const float* dh, const float* a, const float* b, float* da,
+                    float* db);
+
 /* tile_layernorm_bwd_noalloc -- for callers that cannot allocate (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): tile_layernorm_bwd with the same arguments and results except
@@ -508,7 +552,8 @@ int tile_adamw_advance(void* stream, int32_t* step, float* bias_corr, float beta
  * column of the tiled table, which is contiguous) and wpe at a
  * [positions x cols] slab. Other rows are left untouched, except that rows
  * whose id is outside [0, vocab) get NaN when v_off == 0 -- ids are checked
- * on the device and never read out of bounds. */
+ * on the device and never read out of bounds. wpe may be NULL: no position
+ * term (a model without a position table; ld_wpe is then ignored). */
 int tile_embedding_fwd(void* stream, int64_t rows, int64_t cols, const int32_t* ids, int64_t vocab,
                        int64_t v_off, int64_t v_len, const float* wte, int64_t ld_wte, const float* wpe,
                        int64_t ld_wpe, int64_t seq_len, int64_t pos_offset, float* out, int64_t ldo);
@@ -887,6 +932,42 @@ typedef struct { int beta; } tt_op_reduce;
 #define TT_OP_COPY_IN      23
 typedef struct { const void* src; } tt_op_copy;
 
+/* Ops of the LLaMA block (the README's notebook list names LLaMa as its
+ * second model; definitions after the published LLaMA architecture).
+ * TT_OP_RMSNORM_FWD -- tiles x_0..x_{n-1} (rows x c_i), gamma_0..gamma_{n-1},
+ * rstd (>= rows floats), y_0..y_{n-1}: tile_rmsnorm_fwd over the row block
+ * (3n+1 tiles, n <= 16). Reads x, gamma; writes rstd and y. Scalars
+ * tt_op_layernorm (eps).
+ * TT_OP_RMSNORM_BWD -- tiles dy_0.., x_0.., gamma_0.., rstd, dx_0..,
+ * dgamma_0.. (5n+1 tiles): tile_rmsnorm_bwd. Reads dy, x, gamma, rstd;
+ * writes dx (updates it when dx_acc); updates dgamma. Scalars
+ * tt_op_layernorm (dx_acc).
+ * TT_OP_ROPE -- tiles x_0..x_{n-1} (1..4 tiles [batch, len, heads, hd] of
+ * equal shape, e.g. a q and a k tile), then table ([>= positions, hd],
+ * from TT_OP_ROPE_TABLE): tile_rope in place on each x (updated; table
+ * read). Row r of a tile has position pos_off + r % len. Scalars tt_op_rope.
+ * TT_OP_ROPE_TABLE -- tiles table [seq, hd]: tile_rope_table (written).
+ * Scalars tt_op_rope (base; pos_off and inverse unused).
+ * TT_OP_SWIGLU_FWD -- tiles a_0, b_0, h_0, a_1, b_1, h_1, ... (equal element
+ * counts per triple, 1..16 triples): h = silu(a) * b. Reads a, b; writes h.
+ * TT_OP_SWIGLU_BWD -- tiles dh_0, a_0, b_0, ...: a_t <- dh * b * silu'(a),
+ * b_t <- dh * silu(a), in place (a and b updated, dh read).
+ * TT_OP_EMBEDDING_TOKEN_FWD -- tiles ids, out, wte_0..wte_{n-1}: as
+ * TT_OP_EMBEDDING_FWD without the position term (out = wte[id]). Scalars
+ * tt_op_embedding (seq_len = rows, or any divisor of them). */
+#define TT_OP_RMSNORM_FWD         24
+#define TT_OP_RMSNORM_BWD         25
+#define TT_OP_ROPE                26
+#define TT_OP_ROPE_TABLE          27
+#define TT_OP_SWIGLU_FWD          28
+#define TT_OP_SWIGLU_BWD          29
+#define TT_OP_EMBEDDING_TOKEN_FWD 30
+typedef struct {
+    int64_t pos_off;
+    int inverse;
+    double base;
+} tt_op_rope;
+
 int tt_submit(tt_ctx* ctx, int op, const tt_tile* tiles, int ntiles, const void* scalars, size_t scalars_size);
 
 /* Ordering against streams the context does not own (e.g. a framework's
@@ -988,6 +1069,20 @@ typedef struct {
  * parameters, gradients and moments in pinned host RAM (out-of-core). */
 int tt_gpt2_create(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_gpt2_tiles* tiles,
                    int param_home, tt_gpt2** out);
+/* The LLaMA-style model (the NNTile README's notebook list names LLaMa
+ * next to GPT2; the pith.science review's "Editorial extensions" notes the
+ * same tile tasks assemble other architectures): pre-RMSNorm blocks,
+ * rotary embedding of q and k (base 10000, pairs (i, i + hd/2)), SwiGLU MLP
+ * of width n_inner, no biases, no position table, an untied head. Built
+ * from the same tile tasks as the GPT2 step; the handle is used with every
+ * tt_gpt2_* call below (step, accumulation, loss, row losses, parameters).
+ * cfg->ln_eps is the RMSNorm eps. Parameters, in order: wte [V,d], then per
+ * block attn_norm_g [d], w_qkv [d,3d], w_o [d,d], mlp_norm_g [d], w_gate
+ * [d,I], w_up [d,I], w_down [I,d], then norm_f_g [d], w_head [V,d].
+ * Besides tt_gpt2_create's checks: TT_ERR_SHAPE unless n_embd and the embd
+ * tile are multiples of 4. */
+int tt_llama_create(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_gpt2_tiles* tiles,
+                    int param_home, tt_gpt2** out);
 int tt_gpt2_destroy(tt_gpt2* g);
 int tt_gpt2_num_params(tt_gpt2* g, int* n);
 /* Tensors of parameter `index`: value, gradient, first and second moment

@@ -49,6 +49,8 @@ TT_ADAMW_MAX_TILES = TT_SGD_MAX_TILES = TT_FILL_MAX_TILES = 16
  TT_OP_XENTROPY_LOSS, TT_OP_XENTROPY_GRAD, TT_OP_ADAMW, TT_OP_ADAMW_ADVANCE, TT_OP_SGD, TT_OP_EMBEDDING_FWD,
  TT_OP_EMBEDDING_INDEX, TT_OP_EMBEDDING_BWD, TT_OP_EMBEDDING_POS_BWD, TT_OP_REDUCE_ROWS, TT_OP_SPLIT_TOKENS,
  TT_OP_COPY_IN) = range(1, 24)
+(TT_OP_RMSNORM_FWD, TT_OP_RMSNORM_BWD, TT_OP_ROPE, TT_OP_ROPE_TABLE, TT_OP_SWIGLU_FWD, TT_OP_SWIGLU_BWD,
+ TT_OP_EMBEDDING_TOKEN_FWD) = range(24, 31)
 
 _ERRNAMES = {-1: "TT_ERR_ARG", -2: "TT_ERR_SHAPE", -3: "TT_ERR_OOM", -4: "TT_ERR_HIP", -5: "TT_ERR_STATE",
              -6: "TT_ERR_UNSUPPORTED"}
@@ -111,6 +113,10 @@ class tt_op_copy(C.Structure):
     _fields_ = [("src", C.c_void_p)]
 
 
+class tt_op_rope(C.Structure):
+    _fields_ = [("pos_off", C.c_int64), ("inverse", C.c_int), ("base", C.c_double)]
+
+
 class tt_stats(C.Structure):
     _fields_ = [("tasks", C.c_int64), ("edges", C.c_int64), ("cross_stream_waits", C.c_int64),
                 ("events_recorded", C.c_int64), ("submit_seconds", C.c_double), ("h2d_bytes", C.c_int64),
@@ -168,6 +174,13 @@ SIGNATURES = {
     "tile_layernorm_fwd_multi": (I, [P, I, I64, P, P, P, P, P, P, F]),
     "tile_layernorm_bwd_multi": (I, [P, I, I64, P, P, P, P, P, P, I, P, P, P, SZ]),
     "tile_layernorm_bwd_multi_workspace": (SZ, [I64, I64]),
+    "tile_rmsnorm_fwd": (I, [P, I, I64, P, P, P, P, P, F]),
+    "tile_rmsnorm_bwd": (I, [P, I, I64, P, P, P, P, P, P, I, P, P, SZ]),
+    "tile_rmsnorm_bwd_workspace": (SZ, [I64, I64]),
+    "tile_rope_table": (I, [P, I64, I64, C.c_double, P]),
+    "tile_rope": (I, [P, P, I64, I64, I64, I64, I64, P, I64, I]),
+    "tile_swiglu_fwd": (I, [P, I64, P, P, P]),
+    "tile_swiglu_bwd": (I, [P, I64, P, P, P, P, P]),
     "tile_softmax": (I, [P, I, I64, I64, I64, I64, F, I, P, I64, P, P, I64, I64, P, P, P, I64, F]),
     "tile_xentropy": (I, [P, I, I64, I64, I64, P, P, I64, P, P, P, I, F]),
     "tile_attention_fwd": (I, [P, I64, I64, I64, I64, I64, I64, I64, P, P, P, P, P, P, I, I, F]),
@@ -219,6 +232,7 @@ SIGNATURES = {
     "tt_ctx_profile_every": (I, [P, I]),
     "tt_reset_stats": (I, [P]),
     "tt_gpt2_create": (I, [P, C.POINTER(tt_gpt2_config), C.POINTER(tt_gpt2_tiles), I, PP]),
+    "tt_llama_create": (I, [P, C.POINTER(tt_gpt2_config), C.POINTER(tt_gpt2_tiles), I, PP]),
     "tt_gpt2_destroy": (I, [P]),
     "tt_gpt2_num_params": (I, [P, C.POINTER(I)]),
     "tt_gpt2_param": (I, [P, I, PP, PP, PP, PP]),

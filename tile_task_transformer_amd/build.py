@@ -24,7 +24,7 @@ LIB = os.path.join(HERE, "libtiletask.so")
 ARCH = os.environ.get("TT_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["runtime.cpp", "tasks.cpp", "gpt2.cpp", "gemm.hip", "layernorm.hip", "softmax.hip", "attention.hip", "misc.hip",
-           "probe.hip"]
+           "probe.hip", "rope_swiglu.hip"]
 
 
 def hipcc() -> str:

@@ -16,6 +16,13 @@
 // the token embedding, no dropout, one AdamW group with decay on every
 // parameter.
 //
+// The same file builds the LLaMA-style model (tt_llama_create; the README's
+// notebook list names LLaMa as the second model, and the review's
+// "Editorial extensions" notes that the tile tasks assemble other
+// architectures): pre-RMSNorm blocks, rotary embedding of q and k, a SwiGLU
+// MLP, no biases, no position table and an untied head, with the embedding,
+// head, loss, optimiser and residency of the GPT2 step unchanged.
+//
 // Every task below names the tiles it reads and writes; the executor infers
 // the ordering. Submission order is the program order of the untiled step:
 // embedding, blocks, final LN, head, loss, then the backward in reverse,
@@ -32,6 +39,7 @@ namespace {
 
 struct BlockT {
   tt_tensor *h_in, *ln1, *n1, *q, *k, *v, *o, *lse, *h_mid, *ln2, *n2, *u, *g;
+  tt_tensor* a;  // LLaMA: n2 W_gate (u holds n2 W_up, g the gated product)
 };
 
 }  // namespace
@@ -66,14 +74,22 @@ struct tt_gpt2 {
   int64_t graph_ws_gen = -1;
   int64_t updates = 0;  // AdamW iterations submitted (warm-up schedule)
 
+  bool llama = false;         // LLaMA-style blocks (tt_llama_create)
+  tt_tensor* rope = nullptr;  // LLaMA: rotary cos/sin table [seq, head_dim]
+
   enum { WTE = 0, WPE = 1 };
   int pidx(int layer, int which) const { return 2 + 12 * layer + which; }
   int lnf_g() const { return 2 + 12 * c.n_layer; }
+  // LLaMA parameter indices: wte, 7 per block, norm_f_g, w_head
+  int lidx(int layer, int which) const { return 1 + 7 * layer + which; }
+  int norm_f() const { return 1 + 7 * c.n_layer; }
+  int head_w() const { return llama ? 2 + 7 * c.n_layer : 0; }
 };
 
 namespace {
 
 enum { LN1G, LN1B, WQKV, BQKV, WO, BO, LN2G, LN2B, WFC, BFC, WP, BP };
+enum { ANORM, LQKV, LWO, MNORM, LGATE, LUP, LDOWN };  // LLaMA block parameters
 
 int mk(tt_gpt2* g, tt_tensor** out, const char* name, std::initializer_list<int64_t> shape,
        std::initializer_list<int64_t> tile, int split, int dtype = TT_F32, int home = TT_HOME_DEVICE) {
@@ -337,6 +353,56 @@ int ln_backward(tt_gpt2* g, tt_tensor* dy, tt_tensor* x, tt_tensor* gam, tt_tens
   return submit_op(g->ctx, TT_OP_LAYERNORM_BWD, T.data(), (int)T.size(), &sc, sizeof(sc), "ln_bwd", false);
 }
 
+// y = RMSNorm(x) over the embd tiles of token tile (bi, si): one task
+int rms_forward(tt_gpt2* g, tt_tensor* x, tt_tensor* gam, tt_tensor* rstd, tt_tensor* y, int64_t bi, int64_t si) {
+  std::vector<TileArg> T;
+  for (int64_t e = 0; e < g->NE; ++e) T.push_back({x, L(x, {bi, si, e})});
+  for (int64_t e = 0; e < g->NE; ++e) T.push_back({gam, e});
+  T.push_back({rstd, L(rstd, {bi, si, 0})});
+  for (int64_t e = 0; e < g->NE; ++e) T.push_back({y, L(y, {bi, si, e})});
+  const tt_op_layernorm sc{g->c.ln_eps, 0};
+  return submit_op(g->ctx, TT_OP_RMSNORM_FWD, T.data(), (int)T.size(), &sc, sizeof(sc), "rms_fwd", false);
+}
+
+// dx (+)= RMSNorm_bwd(dy) for token tile (bi, si); dgamma accumulates
+int rms_backward(tt_gpt2* g, tt_tensor* dy, tt_tensor* x, tt_tensor* gam, tt_tensor* rstd, tt_tensor* dx,
+                 int dx_acc, tt_tensor* dgam, int64_t bi, int64_t si) {
+  std::vector<TileArg> T;
+  for (int64_t e = 0; e < g->NE; ++e) T.push_back({dy, L(dy, {bi, si, e})});
+  for (int64_t e = 0; e < g->NE; ++e) T.push_back({x, L(x, {bi, si, e})});
+  for (int64_t e = 0; e < g->NE; ++e) T.push_back({gam, e});
+  T.push_back({rstd, L(rstd, {bi, si, 0})});
+  for (int64_t e = 0; e < g->NE; ++e) T.push_back({dx, L(dx, {bi, si, e})});
+  for (int64_t e = 0; e < g->NE; ++e) T.push_back({dgam, e});
+  const tt_op_layernorm sc{g->c.ln_eps, dx_acc};
+  return submit_op(g->ctx, TT_OP_RMSNORM_BWD, T.data(), (int)T.size(), &sc, sizeof(sc), "rms_bwd", false);
+}
+
+// C = epi(sum_t A_t op(B_t)): one K-sum task (use_ksum) or a chain of
+// accumulating GEMM tasks whose first link adds `res` and last adds `bias`
+int linear(tt_ctx* ctx, const char* label, int tb, TileRef C, const std::vector<TileRef>& As,
+           const std::vector<TileRef>& Bs, int epi = TT_EPI_NONE, TileRef bias = {}, TileRef res = {}) {
+  if (use_ksum(label, C, tb, As[0])) return submit_ksum(ctx, label, tb, C, As, Bs, epi, bias, res);
+  for (size_t t = 0; t < As.size(); ++t) {
+    Gemm q;
+    q.tb = tb;
+    q.A = As[t];
+    q.B = Bs[t];
+    q.C = C;
+    q.beta = t > 0 ? 1.f : 0.f;
+    if (t == 0 && (epi & TT_EPI_RES)) {
+      q.epi |= TT_EPI_RES;
+      q.res = res;
+    }
+    if (t + 1 == As.size() && (epi & TT_EPI_BIAS)) {
+      q.epi |= TT_EPI_BIAS;
+      q.bias = bias;
+    }
+    if (int rc = submit_gemm(ctx, label, q)) return rc;
+  }
+  return TT_OK;
+}
+
 // column sums (bias gradients) of the (X, out) tile pairs: one task
 int colsum_task(tt_ctx* ctx, const std::vector<TileRef>& xs, const std::vector<TileRef>& outs, int beta) {
   std::vector<TileArg> T;
@@ -380,8 +446,8 @@ extern "C" int tt_gpt2_set_replay(tt_gpt2* g, int on) {
   return TT_OK;
 }
 
-extern "C" int tt_gpt2_create(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_gpt2_tiles* tiles, int param_home,
-                              tt_gpt2** out) {
+static int create_model(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_gpt2_tiles* tiles, int param_home,
+                        bool llama, tt_gpt2** out) {
   clear_error();
   if (!ctx || !cfg || !tiles || !out) return fail(TT_ERR_ARG, "tt_gpt2_create: null argument");
   const tt_gpt2_config& c = *cfg;
@@ -401,12 +467,16 @@ extern "C" int tt_gpt2_create(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_g
   if (et > 2048 || vt > 2048) return fail(TT_ERR_UNSUPPORTED, "tt_gpt2_create: embd and vocab tiles must be <= 2048");
   if (param_home != TT_HOME_DEVICE && param_home != TT_HOME_PINNED_HOST)
     return fail(TT_ERR_ARG, "tt_gpt2_create: bad param_home");
+  // the RMSNorm kernels take float4 rows of at most 16384 features
+  if (llama && (c.n_embd % 4 || et % 4 || c.n_embd > 16384))
+    return fail(TT_ERR_SHAPE, "tt_llama_create: n_embd and the embd tile must be multiples of 4, n_embd <= 16384");
 
   std::unique_ptr<tt_gpt2> g(new tt_gpt2());
   g->ctx = ctx;
   g->c = c;
   g->t = t;
   g->param_home = param_home;
+  g->llama = llama;
   g->nb = c.batch / t.batch;
   g->ns = c.seq / t.seq;
   g->ntok = g->nb * g->ns;
@@ -438,6 +508,19 @@ extern "C" int tt_gpt2_create(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_g
   };
   std::vector<Spec> specs;
   specs.push_back({"wte", {V, d}, {vt, et}, 1});
+  if (llama) {
+    for (int l = 0; l < c.n_layer; ++l) {
+      specs.push_back({"attn_norm_g", {d}, {et}, 0});
+      specs.push_back({"w_qkv", {d, 3, H, hd}, {et, 1, ht, hd}, 1});
+      specs.push_back({"w_o", {H, hd, d}, {ht, hd, et}, 2});
+      specs.push_back({"mlp_norm_g", {d}, {et}, 0});
+      specs.push_back({"w_gate", {d, I}, {et, it}, 1});
+      specs.push_back({"w_up", {d, I}, {et, it}, 1});
+      specs.push_back({"w_down", {I, d}, {it, et}, 1});
+    }
+    specs.push_back({"norm_f_g", {d}, {et}, 0});
+    specs.push_back({"w_head", {V, d}, {vt, et}, 1});
+  } else {
   specs.push_back({"wpe", {T, d}, {sq, et}, 1});
   for (int l = 0; l < c.n_layer; ++l) {
     specs.push_back({"ln1_g", {d}, {et}, 0});
@@ -455,6 +538,7 @@ extern "C" int tt_gpt2_create(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_g
   }
   specs.push_back({"lnf_g", {d}, {et}, 0});
   specs.push_back({"lnf_b", {d}, {et}, 0});
+  }
   for (auto& s : specs) {
     tt_tensor* ts[4];
     const char* suffix[4] = {"", ".grad", ".m", ".v"};
@@ -479,9 +563,10 @@ extern "C" int tt_gpt2_create(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_g
   // activations
   G->blk.resize(c.n_layer);
   MK(&(G->blk.empty() ? G->h_last : G->blk[0].h_in), "h0", {B, T, d}, {bt, sq, et}, 2);
+  const int64_t nstat = llama ? 1 : 2;  // (mean, rstd) or rstd per row
   for (int l = 0; l < c.n_layer; ++l) {
     BlockT& b = G->blk[l];
-    MK(&b.ln1, "ln1_stats", {B, T, 2}, {bt, sq, 2}, 2);
+    MK(&b.ln1, "ln1_stats", {B, T, nstat}, {bt, sq, nstat}, 2);
     MK(&b.n1, "n1", {B, T, d}, {bt, sq, et}, 2);
     MK(&b.q, "q", {B, T, H, hd}, {bt, sq, ht, hd}, 2);
     MK(&b.k, "k", {B, T, H, hd}, {bt, sq, ht, hd}, 2);
@@ -489,14 +574,16 @@ extern "C" int tt_gpt2_create(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_g
     MK(&b.o, "o", {B, T, H, hd}, {bt, sq, ht, hd}, 2);
     MK(&b.lse, "attn_lse", {B / bt, T / sq, H / ht, bt * sq * ht}, {1, 1, 1, bt * sq * ht}, 3);
     MK(&b.h_mid, "h_mid", {B, T, d}, {bt, sq, et}, 2);
-    MK(&b.ln2, "ln2_stats", {B, T, 2}, {bt, sq, 2}, 2);
+    MK(&b.ln2, "ln2_stats", {B, T, nstat}, {bt, sq, nstat}, 2);
     MK(&b.n2, "n2", {B, T, d}, {bt, sq, et}, 2);
     MK(&b.u, "u", {B, T, I}, {bt, sq, it}, 2);
-    MK(&b.g, "gelu", {B, T, I}, {bt, sq, it}, 2);
+    MK(&b.g, llama ? "swiglu" : "gelu", {B, T, I}, {bt, sq, it}, 2);
+    if (llama) MK(&b.a, "gate", {B, T, I}, {bt, sq, it}, 2);
     tt_tensor** next = (l + 1 < c.n_layer) ? &G->blk[l + 1].h_in : &G->h_last;
     MK(next, "h", {B, T, d}, {bt, sq, et}, 2);
   }
-  MK(&G->lnf, "lnf_stats", {B, T, 2}, {bt, sq, 2}, 2);
+  MK(&G->lnf, "lnf_stats", {B, T, nstat}, {bt, sq, nstat}, 2);
+  if (llama) MK(&G->rope, "rope_table", {T, hd}, {T, hd}, 1);
   MK(&G->nf, "nf", {B, T, d}, {bt, sq, et}, 2);
   MK(&G->z, "logits", {B, T, V}, {bt, sq, vt}, 2);
   MK(&G->ml, "attn_ml", {B / bt, T / sq, H / ht, bt * sq * ht * 2}, {1, 1, 1, bt * sq * ht * 2}, 3);
@@ -528,6 +615,7 @@ extern "C" int tt_gpt2_create(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_g
   ws = std::max(ws, std::min<int64_t>(16, std::max(G->NE, G->NI)) * tile_reduce_rows_workspace(G->rows, widest));
   // the q/k/v bias gradients: up to 15 head tiles per multi-tile column sum
   ws = std::max(ws, tile_reduce_rows_workspace(G->rows, std::min<int64_t>(15, 3 * G->NH) * ht * hd));
+  if (llama) ws = std::max(ws, tile_rmsnorm_bwd_workspace(G->rows, d));
   // dS of one attention tile pair (the backward's dK/dV kernel hands it to the dQ kernel)
   ws = std::max(ws, tile_attention_bwd_workspace(bt, ht, sq, sq));
   // K slices of the linear layers' long-K sums over token-tile outputs
@@ -548,7 +636,7 @@ extern "C" int tt_gpt2_create(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_g
       };
       batch(3 * G->NH * G->NE, e, hw);
       batch(G->NE * G->NH, hw, e);
-      batch(G->NI * G->NE, e, in);
+      batch(G->NI * G->NE * (llama ? 2 : 1), e, in);  // LLaMA: gate and up weights in one batch
       batch(G->NE * G->NI, in, e);
     }
     ws = std::max(ws, std::min<size_t>(g, (size_t)256 << 20));
@@ -564,8 +652,23 @@ extern "C" int tt_gpt2_create(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_g
         }
     if (hipMemset(G->step->base, 0, 4) != hipSuccess) return fail_clean(fail(TT_ERR_HIP, "hipMemset(step)"));
   }
+  if (llama) {  // the rotary table, once (every rope task reads it)
+    const TileArg T1[1] = {{G->rope, 0}};
+    const tt_op_rope sc{0, 0, 10000.0};
+    if (int rc = submit_op(ctx, TT_OP_ROPE_TABLE, T1, 1, &sc, sizeof(sc), "rope_table", false)) return fail_clean(rc);
+  }
   *out = g.release();
   return TT_OK;
+}
+
+extern "C" int tt_gpt2_create(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_gpt2_tiles* tiles, int param_home,
+                              tt_gpt2** out) {
+  return create_model(ctx, cfg, tiles, param_home, false, out);
+}
+
+extern "C" int tt_llama_create(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_gpt2_tiles* tiles, int param_home,
+                               tt_gpt2** out) {
+  return create_model(ctx, cfg, tiles, param_home, true, out);
 }
 
 extern "C" int tt_gpt2_num_params(tt_gpt2* g, int* n) {
@@ -690,6 +793,273 @@ extern "C" int tt_gpt2_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hp
   return tt_gpt2_step_accum(g, tokens, 1, hp, do_update);
 }
 
+// Causal attention of one block: (query tile, key tile) pairs, key tiles in order
+static int attention_forward(tt_gpt2* g, BlockT& b) {
+  tt_ctx* ctx = g->ctx;
+  const int64_t sq = g->t.seq;
+  const float scale = 1.f / std::sqrt((float)g->hd);
+  for (int64_t bi = 0; bi < g->nb; ++bi)
+    for (int64_t hj = 0; hj < g->NH; ++hj)
+      for (int64_t qi = 0; qi < g->ns; ++qi)
+        for (int64_t ki = 0; ki <= qi; ++ki) {
+          const int64_t lq = L(b.q, {bi, qi, hj, 0}), lk = L(b.k, {bi, ki, hj, 0});
+          const TileArg T[6] = {{b.q, lq}, {b.k, lk}, {b.v, lk}, {b.o, lq}, {g->ml, L(g->ml, {bi, qi, hj, 0})},
+                                {b.lse, L(b.lse, {bi, qi, hj, 0})}};
+          const tt_op_attention sc{qi * sq, ki * sq, ki == 0, ki == qi, 0, 0, scale};
+          TRY(submit_op(ctx, TT_OP_ATTENTION_FWD, T, 6, &sc, sizeof(sc), "attn_fwd", false));
+        }
+  return TT_OK;
+}
+
+// its backward: D = rowsum(dO * O) per query tile, then dQ, dK, dV over the
+// tile pairs (dK, dV accumulating over query tiles, dQ over key tiles)
+static int attention_backward(tt_gpt2* g, BlockT& b) {
+  tt_ctx* ctx = g->ctx;
+  const int64_t sq = g->t.seq;
+  const float scale = 1.f / std::sqrt((float)g->hd);
+  for (int64_t bi = 0; bi < g->nb; ++bi)
+    for (int64_t hj = 0; hj < g->NH; ++hj) {
+      for (int64_t qi = 0; qi < g->ns; ++qi) {
+        const int64_t lq = L(b.o, {bi, qi, hj, 0});
+        const TileArg T[3] = {{b.o, lq}, {g->dO, lq}, {g->Dv, L(g->Dv, {bi, qi, hj, 0})}};
+        const tt_op_attention sc{0, 0, 0, 0, 0, 0, scale};
+        TRY(submit_op(ctx, TT_OP_ATTENTION_PREP, T, 3, &sc, sizeof(sc), "attn_prep", false));
+      }
+      for (int64_t qi = 0; qi < g->ns; ++qi)
+        for (int64_t ki = 0; ki <= qi; ++ki) {
+          const int64_t lq = L(b.q, {bi, qi, hj, 0}), lk = L(b.k, {bi, ki, hj, 0});
+          const int64_t ls = L(b.lse, {bi, qi, hj, 0});
+          const TileArg T[9] = {{b.q, lq},   {b.k, lk},   {b.v, lk},   {g->dO, lq}, {b.lse, ls},
+                                {g->Dv, ls}, {g->dq, lq}, {g->dk, lk}, {g->dv, lk}};
+          const tt_op_attention sc{qi * sq, ki * sq, 0, 0, ki > 0, qi > ki, scale};
+          TRY(submit_op(ctx, TT_OP_ATTENTION_BWD, T, 9, &sc, sizeof(sc), "attn_bwd", false));
+        }
+    }
+  return TT_OK;
+}
+
+// the rotary embedding of every head tile's q and k (or, inverse, of dq and
+// dk) for token tile (bi, si), in place: one task per head tile
+static int rope_tasks(tt_gpt2* g, tt_tensor* q, tt_tensor* k, int64_t bi, int64_t si, int inverse) {
+  for (int64_t hj = 0; hj < g->NH; ++hj) {
+    const int64_t lq = L(q, {bi, si, hj, 0});
+    const TileArg T[3] = {{q, lq}, {k, lq}, {g->rope, 0}};
+    const tt_op_rope sc{si * g->t.seq, inverse, 10000.0};
+    TRY(submit_op(g->ctx, TT_OP_ROPE, T, 3, &sc, sizeof(sc), inverse ? "rope_bwd" : "rope", false));
+  }
+  return TT_OK;
+}
+
+// h_out = h_mid + silu(n2 W_gate) * (n2 W_up) W_down over the token tile's
+// inner tiles, up to 16 (gate, up, out) triples per SwiGLU task
+static int swiglu_tasks(tt_gpt2* g, BlockT& b, tt_tensor* first, int64_t bi, int64_t si, bool bwd) {
+  for (int64_t i0 = 0; i0 < g->NI; i0 += 16) {
+    std::vector<TileArg> T;
+    for (int64_t ij = i0; ij < std::min(g->NI, i0 + 16); ++ij) {
+      if (bwd) {  // (dh, a, u): a and u replaced by their gradients
+        T.push_back({first, L(first, {bi, si, ij})});
+        T.push_back({b.a, L(b.a, {bi, si, ij})});
+        T.push_back({b.u, L(b.u, {bi, si, ij})});
+      } else {    // (a, u, g)
+        T.push_back({b.a, L(b.a, {bi, si, ij})});
+        T.push_back({b.u, L(b.u, {bi, si, ij})});
+        T.push_back({b.g, L(b.g, {bi, si, ij})});
+      }
+    }
+    TRY(submit_op(g->ctx, bwd ? TT_OP_SWIGLU_BWD : TT_OP_SWIGLU_FWD, T.data(), (int)T.size(), nullptr, 0,
+                  bwd ? "swiglu_bwd" : "swiglu", false));
+  }
+  return TT_OK;
+}
+
+// One LLaMA block forward: h_mid = h_in + Attn(rope(RMS1(h_in) W_q), rope(.. W_k), .. W_v) W_o,
+// h_out = h_mid + SwiGLU(RMS2(h_mid)) W_down
+static int llama_block_forward(tt_gpt2* g, int l) {
+  tt_ctx* ctx = g->ctx;
+  BlockT& b = g->blk[l];
+  tt_tensor* hout = (l + 1 < g->c.n_layer) ? g->blk[l + 1].h_in : g->h_last;
+  tt_tensor *an = g->P[g->lidx(l, ANORM)], *wqkv = g->P[g->lidx(l, LQKV)], *wo = g->P[g->lidx(l, LWO)];
+  tt_tensor *mn = g->P[g->lidx(l, MNORM)], *wg = g->P[g->lidx(l, LGATE)], *wu = g->P[g->lidx(l, LUP)];
+  tt_tensor* wd = g->P[g->lidx(l, LDOWN)];
+  const int64_t NE = g->NE, NI = g->NI, NH = g->NH;
+  tt_tensor* qkv[3] = {b.q, b.k, b.v};
+  for (int64_t bi = 0; bi < g->nb; ++bi)
+    for (int64_t si = 0; si < g->ns; ++si) {
+      TRY(rms_forward(g, b.h_in, an, b.ln1, b.n1, bi, si));
+      for (int cq = 0; cq < 3; ++cq)
+        for (int64_t hj = 0; hj < NH; ++hj) {
+          std::vector<TileRef> As, Bs;
+          for (int64_t ek = 0; ek < NE; ++ek) {
+            As.push_back({b.n1, L(b.n1, {bi, si, ek})});
+            Bs.push_back({wqkv, L(wqkv, {ek, cq, hj, 0})});
+          }
+          TRY(linear(ctx, "qkv", 0, {qkv[cq], L(qkv[cq], {bi, si, hj, 0})}, As, Bs));
+        }
+      TRY(rope_tasks(g, b.q, b.k, bi, si, 0));
+    }
+  TRY(attention_forward(g, b));
+  for (int64_t bi = 0; bi < g->nb; ++bi)
+    for (int64_t si = 0; si < g->ns; ++si) {
+      for (int64_t ej = 0; ej < NE; ++ej) {
+        std::vector<TileRef> As, Bs;
+        for (int64_t hk = 0; hk < NH; ++hk) {
+          As.push_back({b.o, L(b.o, {bi, si, hk, 0})});
+          Bs.push_back({wo, L(wo, {hk, 0, ej})});
+        }
+        TRY(linear(ctx, "attn_proj", 0, {b.h_mid, L(b.h_mid, {bi, si, ej})}, As, Bs, TT_EPI_RES, {},
+                   {b.h_in, L(b.h_in, {bi, si, ej})}));
+      }
+      TRY(rms_forward(g, b.h_mid, mn, b.ln2, b.n2, bi, si));
+      for (int64_t ij = 0; ij < NI; ++ij)
+        for (tt_tensor* w : {wg, wu}) {
+          std::vector<TileRef> As, Bs;
+          for (int64_t ek = 0; ek < NE; ++ek) {
+            As.push_back({b.n2, L(b.n2, {bi, si, ek})});
+            Bs.push_back({w, L(w, {ek, ij})});
+          }
+          tt_tensor* out = w == wg ? b.a : b.u;
+          TRY(linear(ctx, "fc", 0, {out, L(out, {bi, si, ij})}, As, Bs));
+        }
+      TRY(swiglu_tasks(g, b, nullptr, bi, si, false));
+      for (int64_t ej = 0; ej < NE; ++ej) {
+        std::vector<TileRef> As, Bs;
+        for (int64_t ik = 0; ik < NI; ++ik) {
+          As.push_back({b.g, L(b.g, {bi, si, ik})});
+          Bs.push_back({wd, L(wd, {ik, ej})});
+        }
+        TRY(linear(ctx, "mlp_proj", 0, {hout, L(hout, {bi, si, ej})}, As, Bs, TT_EPI_RES, {},
+                   {b.h_mid, L(b.h_mid, {bi, si, ej})}));
+      }
+    }
+  return TT_OK;
+}
+
+// Its backward; g->dh holds dL/dh_out on entry and dL/dh_in on return, and
+// the block's weight gradients are written (first token tile of the first
+// minibatch) or accumulated
+static int llama_block_backward(tt_gpt2* g, int l, bool later_mb) {
+  tt_ctx* ctx = g->ctx;
+  BlockT& b = g->blk[l];
+  tt_tensor *an = g->P[g->lidx(l, ANORM)], *wqkv = g->P[g->lidx(l, LQKV)], *wo = g->P[g->lidx(l, LWO)];
+  tt_tensor *mn = g->P[g->lidx(l, MNORM)], *wg = g->P[g->lidx(l, LGATE)], *wu = g->P[g->lidx(l, LUP)];
+  tt_tensor* wd = g->P[g->lidx(l, LDOWN)];
+  tt_tensor *gwqkv = g->G[g->lidx(l, LQKV)], *gwo = g->G[g->lidx(l, LWO)], *gwg = g->G[g->lidx(l, LGATE)];
+  tt_tensor *gwu = g->G[g->lidx(l, LUP)], *gwd = g->G[g->lidx(l, LDOWN)];
+  const int64_t NE = g->NE, NI = g->NI, NH = g->NH;
+  tt_tensor* dqkv[3] = {g->dq, g->dk, g->dv};
+  for (int64_t si = 0; si < g->ns; ++si)
+    for (int64_t bi = 0; bi < g->nb; ++bi) {
+      const int64_t ti = bi + g->nb * si;
+      const float wbeta = (ti > 0 || later_mb) ? 1.f : 0.f;
+      // MLP: h_out = h_mid + g W_down, g = silu(a) * u
+      {
+        std::vector<Gemm> qs;
+        for (int64_t ej = 0; ej < NE; ++ej)
+          for (int64_t ik = 0; ik < NI; ++ik) {
+            Gemm q;
+            q.ta = 1;
+            q.A = {b.g, L(b.g, {bi, si, ik})};
+            q.B = {g->dh, L(g->dh, {bi, si, ej})};
+            q.C = {gwd, L(gwd, {ik, ej})};
+            q.beta = wbeta;
+            qs.push_back(q);
+          }
+        TRY(submit_gemm_batch(ctx, "mlp_proj_dw", qs, true));
+      }
+      for (int64_t ik = 0; ik < NI; ++ik) {
+        std::vector<TileRef> As, Bs;
+        for (int64_t ej = 0; ej < NE; ++ej) {
+          As.push_back({g->dh, L(g->dh, {bi, si, ej})});
+          Bs.push_back({wd, L(wd, {ik, ej})});
+        }
+        TRY(linear(ctx, "mlp_proj_dx", 1, {g->dgu, L(g->dgu, {bi, si, ik})}, As, Bs));
+      }
+      TRY(swiglu_tasks(g, b, g->dgu, bi, si, true));  // a <- da, u <- du
+      {
+        std::vector<Gemm> qs;
+        for (int64_t ik = 0; ik < NI; ++ik)
+          for (int64_t ek = 0; ek < NE; ++ek)
+            for (int w = 0; w < 2; ++w) {
+              tt_tensor *src = w ? b.u : b.a, *dst = w ? gwu : gwg;
+              Gemm q;
+              q.ta = 1;
+              q.A = {b.n2, L(b.n2, {bi, si, ek})};
+              q.B = {src, L(src, {bi, si, ik})};
+              q.C = {dst, L(dst, {ek, ik})};
+              q.beta = wbeta;
+              qs.push_back(q);
+            }
+        TRY(submit_gemm_batch(ctx, "fc_dw", qs, true));
+      }
+      // dn2 = da W_gate^T + du W_up^T: one sum over both weights' inner tiles
+      for (int64_t ek = 0; ek < NE; ++ek) {
+        std::vector<TileRef> As, Bs;
+        for (int w = 0; w < 2; ++w)
+          for (int64_t ik = 0; ik < NI; ++ik) {
+            tt_tensor *src = w ? b.u : b.a, *wt = w ? wu : wg;
+            As.push_back({src, L(src, {bi, si, ik})});
+            Bs.push_back({wt, L(wt, {ek, ik})});
+          }
+        TRY(linear(ctx, "fc_dx", 1, {g->dn, L(g->dn, {bi, si, ek})}, As, Bs));
+      }
+      TRY(rms_backward(g, g->dn, b.h_mid, mn, b.ln2, g->dh, 1, g->G[g->lidx(l, MNORM)], bi, si));
+      // attention projection: h_mid = h_in + O W_o
+      {
+        std::vector<Gemm> qs;
+        for (int64_t ej = 0; ej < NE; ++ej)
+          for (int64_t hk = 0; hk < NH; ++hk) {
+            Gemm q;
+            q.ta = 1;
+            q.A = {b.o, L(b.o, {bi, si, hk, 0})};
+            q.B = {g->dh, L(g->dh, {bi, si, ej})};
+            q.C = {gwo, L(gwo, {hk, 0, ej})};
+            q.beta = wbeta;
+            qs.push_back(q);
+          }
+        TRY(submit_gemm_batch(ctx, "attn_proj_dw", qs, true));
+      }
+      for (int64_t hk = 0; hk < NH; ++hk) {
+        std::vector<TileRef> As, Bs;
+        for (int64_t ej = 0; ej < NE; ++ej) {
+          As.push_back({g->dh, L(g->dh, {bi, si, ej})});
+          Bs.push_back({wo, L(wo, {hk, 0, ej})});
+        }
+        TRY(linear(ctx, "attn_proj_dx", 1, {g->dO, L(g->dO, {bi, si, hk, 0})}, As, Bs));
+      }
+    }
+  TRY(attention_backward(g, b));
+  for (int64_t si = 0; si < g->ns; ++si)
+    for (int64_t bi = 0; bi < g->nb; ++bi) {
+      const int64_t ti = bi + g->nb * si;
+      // gradients of the rotated q and k back through the rotation
+      TRY(rope_tasks(g, g->dq, g->dk, bi, si, 1));
+      std::vector<Gemm> qs;
+      for (int cq = 0; cq < 3; ++cq)
+        for (int64_t hj = 0; hj < NH; ++hj)
+          for (int64_t ek = 0; ek < NE; ++ek) {
+            Gemm q;
+            q.ta = 1;
+            q.A = {b.n1, L(b.n1, {bi, si, ek})};
+            q.B = {dqkv[cq], L(dqkv[cq], {bi, si, hj, 0})};
+            q.C = {gwqkv, L(gwqkv, {ek, cq, hj, 0})};
+            q.beta = (ti > 0 || later_mb) ? 1.f : 0.f;
+            qs.push_back(q);
+          }
+      TRY(submit_gemm_batch(ctx, "qkv_dw", qs, true));
+      for (int64_t ek = 0; ek < NE; ++ek) {
+        std::vector<TileRef> As, Bs;
+        for (int cq = 0; cq < 3; ++cq)
+          for (int64_t hj = 0; hj < NH; ++hj) {
+            As.push_back({dqkv[cq], L(dqkv[cq], {bi, si, hj, 0})});
+            Bs.push_back({wqkv, L(wqkv, {ek, cq, hj, 0})});
+          }
+        TRY(submit_ksum_tb(ctx, "qkv_dx", {g->dn, L(g->dn, {bi, si, ek})}, As, Bs));
+      }
+      TRY(rms_backward(g, g->dn, b.h_in, an, b.ln1, g->dh, 1, g->G[g->lidx(l, ANORM)], bi, si));
+    }
+  return TT_OK;
+}
+
 // One minibatch: forward, loss, backward and (if do_update) AdamW. Minibatch
 // `micro` of `n_micro` accumulates into the gradients and the loss of the
 // earlier ones (micro > 0); the loss is scaled for the mean over all of them.
@@ -733,15 +1103,22 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
   for (int64_t bi = 0; bi < g->nb; ++bi)
     for (int64_t si = 0; si < g->ns; ++si)
       for (int64_t e = 0; e < NE; ++e) {
-        tt_tensor *wte = g->P[0], *wpe = g->P[1];
-        std::vector<TileArg> T = {{g->ids, L(g->ids, {bi, si})}, {wpe, L(wpe, {si, e})}, {h0, L(h0, {bi, si, e})}};
+        tt_tensor* wte = g->P[0];
+        std::vector<TileArg> T = {{g->ids, L(g->ids, {bi, si})}};
+        if (!g->llama) T.push_back({g->P[1], L(g->P[1], {si, e})});  // positions (GPT2)
+        T.push_back({h0, L(h0, {bi, si, e})});
         for (int64_t v = 0; v < NV; ++v) T.push_back({wte, L(wte, {v, e})});
         const tt_op_embedding sc{sq};
-        TRY(submit_op(ctx, TT_OP_EMBEDDING_FWD, T.data(), (int)T.size(), &sc, sizeof(sc), "emb_fwd", false));
+        TRY(submit_op(ctx, g->llama ? TT_OP_EMBEDDING_TOKEN_FWD : TT_OP_EMBEDDING_FWD, T.data(), (int)T.size(), &sc,
+                      sizeof(sc), "emb_fwd", false));
       }
 
   // ---- blocks forward
   for (int l = 0; l < c.n_layer; ++l) {
+    if (g->llama) {
+      TRY(llama_block_forward(g, l));
+      continue;
+    }
     BlockT& b = g->blk[l];
     tt_tensor* hout = (l + 1 < c.n_layer) ? g->blk[l + 1].h_in : g->h_last;
     tt_tensor *ln1g = g->P[g->pidx(l, LN1G)], *ln1b = g->P[g->pidx(l, LN1B)];
@@ -781,17 +1158,7 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
             }
           }
       }
-    // attention: (query tile, key tile) pairs, key tiles in order
-    for (int64_t bi = 0; bi < g->nb; ++bi)
-      for (int64_t hj = 0; hj < NH; ++hj)
-        for (int64_t qi = 0; qi < g->ns; ++qi)
-          for (int64_t ki = 0; ki <= qi; ++ki) {
-            const int64_t lq = L(b.q, {bi, qi, hj, 0}), lk = L(b.k, {bi, ki, hj, 0});
-            const TileArg T[6] = {{b.q, lq}, {b.k, lk}, {b.v, lk}, {b.o, lq}, {g->ml, L(g->ml, {bi, qi, hj, 0})},
-                                  {b.lse, L(b.lse, {bi, qi, hj, 0})}};
-            const tt_op_attention sc{qi * sq, ki * sq, ki == 0, ki == qi, 0, 0, scale};
-            TRY(submit_op(ctx, TT_OP_ATTENTION_FWD, T, 6, &sc, sizeof(sc), "attn_fwd", false));
-          }
+    TRY(attention_forward(g, b));
     for (int64_t bi = 0; bi < g->nb; ++bi)
       for (int64_t si = 0; si < g->ns; ++si) {
         const int64_t ti = bi + g->nb * si;
@@ -885,12 +1252,15 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
       }
   }
 
-  // ---- final LayerNorm, tied head, cross-entropy
-  tt_tensor *lnfg = g->P[g->lnf_g()], *lnfb = g->P[g->lnf_g() + 1], *wte = g->P[0];
+  // ---- final LayerNorm (RMSNorm), head (tied to wte for GPT2), cross-entropy
+  tt_tensor* lnfg = g->P[g->llama ? g->norm_f() : g->lnf_g()];
+  tt_tensor* lnfb = g->llama ? nullptr : g->P[g->lnf_g() + 1];
+  tt_tensor* wte = g->P[g->head_w()];  // the head's weight
   for (int64_t bi = 0; bi < g->nb; ++bi)
     for (int64_t si = 0; si < g->ns; ++si) {
       const int64_t ti = bi + g->nb * si;
-      TRY(ln_forward(g, g->h_last, lnfg, lnfb, g->lnf, g->nf, bi, si));
+      if (g->llama) TRY(rms_forward(g, g->h_last, lnfg, g->lnf, g->nf, bi, si));
+      else TRY(ln_forward(g, g->h_last, lnfg, lnfb, g->lnf, g->nf, bi, si));
       // z_v = nf wte_v^T for every vocab tile v: per embd tile, one batch
       // of equal-shape products (tile_gemm_batch), accumulating over embd
       // tiles; the last embd tile's batch also takes the cross-entropy
@@ -1025,9 +1395,10 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
   }
 
   // ---- backward: head (dz is in place of the logits)
-  // dwte (head part) = sum over token tiles of dz^T nf: per (embd tile,
-  // token tile), one batch of equal-shape products over the vocab tiles
-  tt_tensor* gwte = g->G[0];
+  // dwte (head part; dw_head when untied) = sum over token tiles of dz^T nf:
+  // per (embd tile, token tile), one batch of equal-shape products over the
+  // vocab tiles
+  tt_tensor* gwte = g->G[g->head_w()];
   for (int64_t ek = 0; ek < NE; ++ek)
     for (int64_t si = 0; si < g->ns; ++si)
       for (int64_t bi = 0; bi < g->nb; ++bi) {
@@ -1058,9 +1429,19 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
         const tt_op_gemm sc{0, 0, TT_EPI_NONE, 1.f, 0.f, 1};
         TRY(submit_op(ctx, TT_OP_GEMM_KSUM, T.data(), (int)T.size(), &sc, sizeof(sc), "head_dx", false));
       }
+  if (g->llama) TRY(adamw_of({(size_t)g->head_w()}));  // the untied head's gradient is final
   // zero the LayerNorm and position gradients, which accumulate (over
-  // token tiles, and over minibatches after the first)
-  if (!later_mb) {
+  // token tiles, and over minibatches after the first); LLaMA: the RMSNorm
+  // gains' and the token table's (no head part writes it first)
+  if (!later_mb && g->llama) {
+    std::vector<TileRef> zero;
+    for (int l = 0; l < c.n_layer; ++l)
+      for (int w : {ANORM, MNORM})
+        for (int64_t e = 0; e < NE; ++e) zero.push_back({g->G[g->lidx(l, w)], e});
+    for (int64_t e = 0; e < NE; ++e) zero.push_back({g->G[g->norm_f()], e});
+    for (int64_t lt = 0; lt < g->G[0]->ntiles; ++lt) zero.push_back({g->G[0], lt});
+    TRY(fill_tasks(g, zero, 0.f));
+  } else if (!later_mb) {
     std::vector<TileRef> zero;
     for (int l = 0; l < c.n_layer; ++l)
       for (int w : {LN1G, LN1B, LN2G, LN2B})
@@ -1073,10 +1454,14 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
     TRY(fill_tasks(g, zero, 0.f));
   }
   for (int64_t bi = 0; bi < g->nb; ++bi)
-    for (int64_t si = 0; si < g->ns; ++si)
-      TRY(ln_backward(g, g->dnf, g->h_last, lnfg, g->lnf, g->dh, 0, g->G[g->lnf_g()], g->G[g->lnf_g() + 1], bi,
-                      si));
-  TRY(adamw_of({(size_t)g->lnf_g(), (size_t)g->lnf_g() + 1}));
+    for (int64_t si = 0; si < g->ns; ++si) {
+      if (g->llama) TRY(rms_backward(g, g->dnf, g->h_last, lnfg, g->lnf, g->dh, 0, g->G[g->norm_f()], bi, si));
+      else
+        TRY(ln_backward(g, g->dnf, g->h_last, lnfg, g->lnf, g->dh, 0, g->G[g->lnf_g()], g->G[g->lnf_g() + 1], bi,
+                        si));
+    }
+  if (g->llama) TRY(adamw_of({(size_t)g->norm_f()}));
+  else TRY(adamw_of({(size_t)g->lnf_g(), (size_t)g->lnf_g() + 1}));
 
   // bias gradients of a row of tiles (token tile (bi, si), n feature
   // tiles): up to 16 tiles per task, one pair of launches each
@@ -1094,6 +1479,12 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
 
   // ---- blocks backward
   for (int l = c.n_layer - 1; l >= 0; --l) {
+    if (g->llama) {
+      TRY(llama_block_backward(g, l, later_mb));
+      const size_t p0 = g->lidx(l, 0);
+      TRY(adamw_of({p0 + ANORM, p0 + MNORM, p0 + LQKV, p0 + LWO, p0 + LGATE, p0 + LUP, p0 + LDOWN}));
+      continue;
+    }
     BlockT& b = g->blk[l];
     tt_tensor *ln1g = g->P[g->pidx(l, LN1G)], *wqkv = g->P[g->pidx(l, WQKV)], *wo = g->P[g->pidx(l, WO)];
     tt_tensor *ln2g = g->P[g->pidx(l, LN2G)], *wfc = g->P[g->pidx(l, WFC)], *wp = g->P[g->pidx(l, WP)];
@@ -1225,25 +1616,7 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
           }
         }
       }
-    // attention backward
-    for (int64_t bi = 0; bi < g->nb; ++bi)
-      for (int64_t hj = 0; hj < NH; ++hj) {
-        for (int64_t qi = 0; qi < g->ns; ++qi) {
-          const int64_t lq = L(b.o, {bi, qi, hj, 0});
-          const TileArg T[3] = {{b.o, lq}, {g->dO, lq}, {g->Dv, L(g->Dv, {bi, qi, hj, 0})}};
-          const tt_op_attention sc{0, 0, 0, 0, 0, 0, scale};
-          TRY(submit_op(ctx, TT_OP_ATTENTION_PREP, T, 3, &sc, sizeof(sc), "attn_prep", false));
-        }
-        for (int64_t qi = 0; qi < g->ns; ++qi)
-          for (int64_t ki = 0; ki <= qi; ++ki) {
-            const int64_t lq = L(b.q, {bi, qi, hj, 0}), lk = L(b.k, {bi, ki, hj, 0});
-            const int64_t ls = L(b.lse, {bi, qi, hj, 0});
-            const TileArg T[9] = {{b.q, lq},   {b.k, lk},   {b.v, lk},   {g->dO, lq}, {b.lse, ls},
-                                  {g->Dv, ls}, {g->dq, lq}, {g->dk, lk}, {g->dv, lk}};
-            const tt_op_attention sc{qi * sq, ki * sq, 0, 0, ki > 0, qi > ki, scale};
-            TRY(submit_op(ctx, TT_OP_ATTENTION_BWD, T, 9, &sc, sizeof(sc), "attn_bwd", false));
-          }
-      }
+    TRY(attention_backward(g, b));
     // QKV projection backward
     for (int64_t si = 0; si < g->ns; ++si)
       for (int64_t bi = 0; bi < g->nb; ++bi) {
@@ -1314,14 +1687,15 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
         // in HBM the dwte tiles of one embd column are one contiguous slab:
         // one task and launch over every vocab tile; staged pinned tiles are
         // separate, one task per vocab tile
-        const int64_t per = gwte->home == TT_HOME_DEVICE ? NV : 1;
+        tt_tensor* gtok = g->G[0];
+        const int64_t per = gtok->home == TT_HOME_DEVICE ? NV : 1;
         for (int64_t v0 = 0; v0 < NV; v0 += per) {
           std::vector<TileArg> T(head, head + 3);
-          for (int64_t vj = v0; vj < v0 + per; ++vj) T.push_back({gwte, L(gwte, {vj, ek})});
+          for (int64_t vj = v0; vj < v0 + per; ++vj) T.push_back({gtok, L(gtok, {vj, ek})});
           TRY(submit_op(ctx, TT_OP_EMBEDDING_BWD, T.data(), (int)T.size(), &sc, sizeof(sc), "emb_dw", false));
         }
       }
-  for (int64_t si = 0; si < g->ns; ++si)
+  for (int64_t si = 0; si < g->ns && !g->llama; ++si)
     for (int64_t ek = 0; ek < NE; ++ek)
       for (int64_t bi = 0; bi < g->nb; ++bi) {
         const TileArg T[2] = {{g->dh, L(g->dh, {bi, si, ek})}, {g->G[1], L(g->G[1], {si, ek})}};
@@ -1330,7 +1704,8 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
       }
 
   // ---- AdamW of the embeddings (their gradients are final now)
-  TRY(adamw_of({1, 0}));
+  if (g->llama) TRY(adamw_of({0}));
+  else TRY(adamw_of({1, 0}));
   g->last_tasks = ctx->next_id - t0;
   return ctx->flush();
 }

@@ -736,6 +736,246 @@ extern "C" int tile_layernorm_bwd_multi(void* stream, int count, int64_t rows, c
   return tt::launch_status("tile_layernorm_bwd_multi(colsum)");
 }
 
+// ------------------------------------------------------------------ RMSNorm
+//
+// tile_rmsnorm_fwd / tile_rmsnorm_bwd: the LLaMA block's normalisation,
+// y = x * rstd * g with rstd = 1 / sqrt(mean(x^2) + eps) over a row whose
+// features lie in 1..16 tiles, no shift and no mean. Same geometry as the
+// multi-tile LayerNorm above: a workgroup holds whole rows in registers,
+// row sums combine lanes by a fixed butterfly and waves in wave order
+// (deterministic); the backward writes per-block column partials of dy*n
+// that a second launch sums in block order into dgamma.
+
+namespace {
+
+template <int BT, int VPT>
+__global__ __launch_bounds__(BT) void rms_fwd_multi(int rows, int rows_per_block, LnRowTiles P,
+                                                    float* __restrict__ rstd_out, float eps) {
+  __shared__ float red[2][BT / 64];
+  const float* xp[VPT];
+  float* yp[VPT];
+  int ld[VPT];
+  bool ok[VPT];
+  f32x4 g[VPT];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int col = 4 * ((int)threadIdx.x + k * BT);
+    ok[k] = col < P.total;
+    int w = 0, width = 4, t = 0;
+    if (ok[k]) t = ln_tile(P, col, &w, &width);
+    xp[k] = P.x[t] + w;
+    yp[k] = P.y[t] + w;
+    ld[k] = width;
+    g[k] = ok[k] ? *reinterpret_cast<const f32x4*>(P.g[t] + w) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float inv_n = 1.f / (float)P.total;
+  const int r0 = blockIdx.x * rows_per_block, r1 = min(rows, r0 + rows_per_block);
+  f32x4 v[VPT];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k)
+    v[k] = ok[k] && r0 < r1 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(xp[k] + (int64_t)r0 * ld[k]))
+                            : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int r = r0; r < r1; ++r) {
+    f32x4 nx[VPT];
+    const bool more = r + 1 < r1;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k)
+      nx[k] = ok[k] && more
+                  ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(xp[k] + (int64_t)(r + 1) * ld[k]))
+                  : f32x4{0.f, 0.f, 0.f, 0.f};
+    float s = 0.f, unused = 0.f;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) s += (v[k][0] * v[k][0] + v[k][1] * v[k][1]) + (v[k][2] * v[k][2] + v[k][3] * v[k][3]);
+    block_sum2<BT>(s, unused, red);
+    const float rstd = 1.f / sqrtf(s * inv_n + eps);
+    if (threadIdx.x == 0) rstd_out[r] = rstd;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k)
+      if (ok[k]) {
+        f32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = v[k][i] * rstd * g[k][i];
+        *reinterpret_cast<f32x4*>(yp[k] + (int64_t)r * ld[k]) = o;
+      }
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) v[k] = nx[k];
+  }
+}
+
+// dx (+)= rstd * (dn - n * mean(dn * n)) with n = x * rstd, dn = dy * g; the
+// block's column partials of dy * n go to ws[block][total]
+template <int BT, int VPT>
+__global__ __launch_bounds__(BT) void rms_bwd_multi(int rows, int rows_per_block, LnRowTiles P,
+                                                    const float* __restrict__ rstd_in, int dx_acc,
+                                                    float* __restrict__ ws) {
+  __shared__ float red[2][BT / 64];
+  const float *xp[VPT], *dyp[VPT];
+  float* dxp[VPT];
+  int ld[VPT];
+  bool ok[VPT];
+  f32x4 g[VPT], dg[VPT];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int col = 4 * ((int)threadIdx.x + k * BT);
+    ok[k] = col < P.total;
+    int w = 0, width = 4, t = 0;
+    if (ok[k]) t = ln_tile(P, col, &w, &width);
+    xp[k] = P.x[t] + w;
+    dyp[k] = P.dy[t] + w;
+    dxp[k] = P.y[t] + w;
+    ld[k] = width;
+    g[k] = ok[k] ? *reinterpret_cast<const f32x4*>(P.g[t] + w) : f32x4{0.f, 0.f, 0.f, 0.f};
+    dg[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float inv_n = 1.f / (float)P.total;
+  const int r0 = blockIdx.x * rows_per_block, r1 = min(rows, r0 + rows_per_block);
+  for (int r = r0; r < r1; ++r) {
+    const float rstd = rstd_in[r];
+    f32x4 n[VPT], dn[VPT];
+    float s = 0.f, unused = 0.f;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      f32x4 xv = f32x4{0.f, 0.f, 0.f, 0.f}, dv = xv;
+      if (ok[k]) {
+        xv = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(xp[k] + (int64_t)r * ld[k]));
+        dv = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(dyp[k] + (int64_t)r * ld[k]));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        n[k][i] = xv[i] * rstd;
+        dn[k][i] = dv[i] * g[k][i];
+        s += dn[k][i] * n[k][i];
+        dg[k][i] += dv[i] * n[k][i];
+      }
+    }
+    block_sum2<BT>(s, unused, red);
+    const float a = s * inv_n;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k)
+      if (ok[k]) {
+        float* q = dxp[k] + (int64_t)r * ld[k];
+        f32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = rstd * (dn[k][i] - n[k][i] * a);
+        if (dx_acc) o += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(q));
+        __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(q));
+      }
+  }
+  float* out = ws + (int64_t)blockIdx.x * P.total;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k)
+    if (ok[k]) *reinterpret_cast<f32x4*>(out + 4 * ((int)threadIdx.x + k * BT)) = dg[k];
+}
+
+// dgamma of every tile += the column sums of the block partials (blockIdx.y = tile)
+__global__ __launch_bounds__(1024) void rms_colsum_finish_multi(int nblk, LnRowTiles P, const float* __restrict__ ws) {
+  const int t = blockIdx.y;
+  const int width = t < P.n - 1 ? P.c0 : P.total - (P.n - 1) * P.c0;
+  if ((int)blockIdx.x * 64 >= width) return;
+  colsum_finish_block(nblk, width, ws, (int64_t)P.total, (int64_t)t * P.c0, P.dg[t], 1);
+}
+
+constexpr int kRmsBwdRowsPerBlock = 16;
+
+// like ln_multi_check, one tile allowed
+int rms_check(const char* nm, int count, int64_t rows, const int64_t* cols, LnRowTiles* P) {
+  using tt::fail;
+  if (count < 1 || count > kLnTilesMax) return fail(TT_ERR_ARG, "%s: count must be 1..%d", nm, kLnTilesMax);
+  if (rows < 0 || rows > INT32_MAX) return fail(TT_ERR_ARG, "%s: bad row count", nm);
+  if (!cols) return fail(TT_ERR_ARG, "%s: null cols", nm);
+  int64_t total = 0;
+  for (int t = 0; t < count; ++t) {
+    if (cols[t] < 4 || cols[t] % 4 || (t < count - 1 && cols[t] != cols[0]) || cols[t] > cols[0])
+      return fail(TT_ERR_SHAPE, "%s: tile widths must be multiples of 4, equal but for a narrower last tile", nm);
+    total += cols[t];
+  }
+  if (total > 16384) return fail(TT_ERR_SHAPE, "%s: %lld features exceed 16384", nm, (long long)total);
+  P->n = count;
+  P->c0 = (int)cols[0];
+  P->total = (int)total;
+  return TT_OK;
+}
+
+}  // namespace
+
+extern "C" int tile_rmsnorm_fwd(void* stream, int count, int64_t rows, const int64_t* cols, const float* const* x,
+                                const float* const* gamma, float* rstd, float* const* y, float eps) {
+  using tt::fail;
+  LnRowTiles P{};
+  if (int rc = rms_check("tile_rmsnorm_fwd", count, rows, cols, &P)) return rc;
+  if (rows == 0) return TT_OK;
+  if (!x || !gamma || !y || !rstd) return fail(TT_ERR_ARG, "tile_rmsnorm_fwd: null array");
+  for (int t = 0; t < count; ++t) {
+    if (!tt::aligned16(x[t]) || !tt::aligned16(y[t]) || !tt::aligned16(gamma[t]) || !x[t] || !y[t] || !gamma[t])
+      return fail(TT_ERR_ARG, "tile_rmsnorm_fwd: tile %d is null or not 16-byte aligned", t);
+    P.x[t] = x[t];
+    P.y[t] = y[t];
+    P.g[t] = gamma[t];
+  }
+  int bt, vpt;
+  ln_multi_geometry(P.total, &bt, &vpt);
+  const int r = (int)rows;
+  dim3 grid((unsigned)((r + kLnFwdRowsPerBlock - 1) / kLnFwdRowsPerBlock));
+  hipStream_t s = tt::as_stream(stream);
+#define TT_RMSF(BT, VPT) \
+  hipLaunchKernelGGL((rms_fwd_multi<BT, VPT>), grid, dim3(BT), 0, s, r, kLnFwdRowsPerBlock, P, rstd, eps)
+  if (bt == 256) TT_RMSF(256, 1);
+  else if (bt == 512) TT_RMSF(512, 1);
+  else if (vpt == 1) TT_RMSF(1024, 1);
+  else if (vpt == 2) TT_RMSF(1024, 2);
+  else TT_RMSF(1024, 4);
+#undef TT_RMSF
+  return tt::launch_status("tile_rmsnorm_fwd");
+}
+
+extern "C" size_t tile_rmsnorm_bwd_workspace(int64_t rows, int64_t total) {
+  if (rows < 0 || total < 0) return 0;
+  const int64_t nblk = (rows + kRmsBwdRowsPerBlock - 1) / kRmsBwdRowsPerBlock;
+  return (size_t)(nblk * total * sizeof(float));
+}
+
+extern "C" int tile_rmsnorm_bwd(void* stream, int count, int64_t rows, const int64_t* cols, const float* const* dy,
+                                const float* const* x, const float* const* gamma, const float* rstd,
+                                float* const* dx, int dx_acc, float* const* dgamma, void* workspace,
+                                size_t workspace_bytes) {
+  using tt::fail;
+  LnRowTiles P{};
+  if (int rc = rms_check("tile_rmsnorm_bwd", count, rows, cols, &P)) return rc;
+  if (rows == 0) return TT_OK;
+  if (!dy || !x || !gamma || !dx || !dgamma || !rstd || !workspace)
+    return fail(TT_ERR_ARG, "tile_rmsnorm_bwd: null array or workspace");
+  if (workspace_bytes < tile_rmsnorm_bwd_workspace(rows, P.total) || !tt::aligned16(workspace))
+    return fail(TT_ERR_ARG, "tile_rmsnorm_bwd: workspace too small or misaligned");
+  for (int t = 0; t < count; ++t) {
+    if (!x[t] || !dy[t] || !dx[t] || !gamma[t] || !dgamma[t] || !tt::aligned16(x[t]) || !tt::aligned16(dy[t]) ||
+        !tt::aligned16(dx[t]) || !tt::aligned16(gamma[t]))
+      return fail(TT_ERR_ARG, "tile_rmsnorm_bwd: tile %d is null or not 16-byte aligned", t);
+    P.x[t] = x[t];
+    P.dy[t] = dy[t];
+    P.y[t] = dx[t];
+    P.g[t] = gamma[t];
+    P.dg[t] = dgamma[t];
+  }
+  int bt, vpt;
+  ln_multi_geometry(P.total, &bt, &vpt);
+  const int r = (int)rows;
+  const int nblk = (r + kRmsBwdRowsPerBlock - 1) / kRmsBwdRowsPerBlock;
+  float* ws = (float*)workspace;
+  hipStream_t s = tt::as_stream(stream);
+#define TT_RMSB(BT, VPT) \
+  hipLaunchKernelGGL((rms_bwd_multi<BT, VPT>), dim3(nblk), dim3(BT), 0, s, r, kRmsBwdRowsPerBlock, P, rstd, dx_acc, ws)
+  if (bt == 256) TT_RMSB(256, 1);
+  else if (bt == 512) TT_RMSB(512, 1);
+  else if (vpt == 1) TT_RMSB(1024, 1);
+  else if (vpt == 2) TT_RMSB(1024, 2);
+  else TT_RMSB(1024, 4);
+#undef TT_RMSB
+  if (int rc = tt::launch_status("tile_rmsnorm_bwd")) return rc;
+  hipLaunchKernelGGL(rms_colsum_finish_multi, dim3((unsigned)((P.c0 + 63) / 64), (unsigned)count), dim3(1024), 0, s,
+                     nblk, P, ws);
+  return tt::launch_status("tile_rmsnorm_bwd(colsum)");
+}
+
 // ------------------------------------ LayerNorm backward without allocation
 //
 // tile_layernorm_bwd_noalloc: tile_layernorm_bwd with its column-sum

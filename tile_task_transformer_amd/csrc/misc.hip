@@ -167,7 +167,8 @@ __global__ void emb_fwd(int rows, int cols, const int32_t* __restrict__ ids, int
   } else {
     if (id < v_off || id >= v_off + v_len) return;
     const int64_t pos = pos_off + r % seq_len;
-    o = tt::ld4<VEC>(wte, ld_wte, id - v_off, c, cols) + tt::ld4<VEC>(wpe, ld_wpe, pos, c, cols);
+    o = tt::ld4<VEC>(wte, ld_wte, id - v_off, c, cols);
+    if (wpe) o += tt::ld4<VEC>(wpe, ld_wpe, pos, c, cols);
   }
   tt::st4<VEC>(out, ldo, r, c, cols, o);
 }
@@ -341,11 +342,11 @@ extern "C" int tile_embedding_fwd(void* stream, int64_t rows, int64_t cols, cons
   if (rows < 0 || cols < 0 || seq_len <= 0 || vocab <= 0) return fail(TT_ERR_ARG, "tile_embedding_fwd: bad size");
   if (v_off < 0 || v_len < 0 || v_off + v_len > vocab) return fail(TT_ERR_ARG, "tile_embedding_fwd: bad vocab range");
   if (rows == 0 || cols == 0) return TT_OK;
-  if (!ids || !wte || !wpe || !out || ld_wte < cols || ld_wpe < cols || ldo < cols)
+  if (!ids || !wte || !out || ld_wte < cols || (wpe && ld_wpe < cols) || ldo < cols)
     return fail(TT_ERR_ARG, "tile_embedding_fwd: bad argument");
   if (rows > INT32_MAX || cols > INT32_MAX) return fail(TT_ERR_ARG, "tile_embedding_fwd: size exceeds int32");
-  const bool vec = ld_wte % 4 == 0 && ld_wpe % 4 == 0 && ldo % 4 == 0 && tt::aligned16(wte) && tt::aligned16(wpe) &&
-                   tt::aligned16(out);
+  const bool vec = ld_wte % 4 == 0 && (!wpe || ld_wpe % 4 == 0) && ldo % 4 == 0 && tt::aligned16(wte) &&
+                   tt::aligned16(wpe) && tt::aligned16(out);
   const int64_t work = rows * ((cols + 3) / 4);
   dim3 grid((unsigned)((work + 255) / 256)), block(256);
   hipStream_t s = tt::as_stream(stream);

@@ -866,34 +866,40 @@ bool contiguous_column(const TileArg* W, int nv) {
   return true;
 }
 
-int op_emb_fwd(tt_ctx* ctx, const TileArg* T, int n, const tt_op_embedding& q, const char* label) {
-  const char* nm = "TT_OP_EMBEDDING_FWD";
-  if (n < 4) return fail(TT_ERR_ARG, "%s: tiles ids, wpe, out, wte_0..wte_{n-1}", nm);
+// pos: the tile list has a position-table tile after ids (TT_OP_EMBEDDING_FWD);
+// without it (TT_OP_EMBEDDING_TOKEN_FWD) out = wte[id]
+int op_emb_fwd(tt_ctx* ctx, const TileArg* T, int n, const tt_op_embedding& q, const char* label, bool pos) {
+  const char* nm = pos ? "TT_OP_EMBEDDING_FWD" : "TT_OP_EMBEDDING_TOKEN_FWD";
+  const int np = pos ? 1 : 0;
+  if (n < 3 + np) return fail(TT_ERR_ARG, "%s: tiles ids, %sout, wte_0..wte_{n-1}", nm, pos ? "wpe, " : "");
   if (int rc = need_i32(T[0], nm, "ids")) return rc;
   if (int rc = need_f32(T + 1, n - 1, nm)) return rc;
-  const int nv = n - 3;
-  int64_t rows, cols, pr, pc;
-  matv(T[2], &rows, &cols);
-  matv(T[1], &pr, &pc);
+  const int nv = n - 2 - np;
+  int64_t rows, cols, pr = 0, pc = 0;
+  matv(T[1 + np], &rows, &cols);
+  if (pos) matv(T[1], &pr, &pc);
+  else pr = q.seq_len, pc = cols;
   if (elems(T[0]) != rows || pc != cols || q.seq_len < 1 || q.seq_len > pr || rows % q.seq_len)
     return fail(TT_ERR_SHAPE, "%s: ids %lld, out %lldx%lld, wpe %lldx%lld, seq_len %lld disagree", nm,
                 (long long)elems(T[0]), (long long)rows, (long long)cols, (long long)pr, (long long)pc,
                 (long long)q.seq_len);
   int64_t vocab, vt, v_first;
-  if (int rc = vocab_column(T + 3, nv, cols, nm, true, &vocab, &vt, &v_first)) return rc;
-  std::vector<Access> acc = {acc_of(T[0], TT_R), acc_of(T[1], TT_R), acc_of(T[2], TT_W)};
-  for (int v = 0; v < nv; ++v) acc.push_back(acc_of(T[3 + v], TT_R));
+  if (int rc = vocab_column(T + 2 + np, nv, cols, nm, true, &vocab, &vt, &v_first)) return rc;
+  std::vector<Access> acc = {acc_of(T[0], TT_R), acc_of(T[1 + np], TT_W)};
+  if (pos) acc.push_back(acc_of(T[1], TT_R));
+  for (int v = 0; v < nv; ++v) acc.push_back(acc_of(T[2 + np + v], TT_R));
   std::vector<TileArg> tl(T, T + n);
   const int64_t sl = q.seq_len;
   return ctx->submit(label ? label : "emb_fwd", std::move(acc), [=](hipStream_t s, void*) {
-    const TileArg *ids = &tl[0], *wpe = &tl[1], *out = &tl[2], *W = &tl[3];
+    const TileArg *ids = &tl[0], *out = &tl[1 + np], *W = &tl[2 + np];
+    float* wpe = pos ? Fp(tl[1]) : nullptr;
     if (contiguous_column(W, nv))  // device home: the column is one [vocab, cols] slab
-      return tile_embedding_fwd(s, rows, cols, Ip(*ids), vocab, 0, vocab, Fp(W[0]), cols, Fp(*wpe), cols, sl, 0,
+      return tile_embedding_fwd(s, rows, cols, Ip(*ids), vocab, 0, vocab, Fp(W[0]), cols, wpe, cols, sl, 0,
                                 Fp(*out), cols);
     for (int v = 0; v < nv; ++v) {
       const int64_t v_off = v * vt;
       if (int rc = tile_embedding_fwd(s, rows, cols, Ip(*ids), vocab, v_off, std::min(vt, vocab - v_off), Fp(W[v]),
-                                      cols, Fp(*wpe), cols, sl, 0, Fp(*out), cols))
+                                      cols, wpe, cols, sl, 0, Fp(*out), cols))
         return rc;
     }
     return TT_OK;
@@ -1066,6 +1072,195 @@ int op_fill(tt_ctx* ctx, const TileArg* T, int n, const tt_op_fill& q, const cha
   });
 }
 
+// ------------------------------------------------------- LLaMA block ops
+
+// rows and per-tile widths of an RMSNorm tile list (x_e and the tiles that
+// must match them), checked against the one-pass kernels' limits
+int rms_cols(const char* nm, const TileArg* X, int ne, int64_t* rows, std::vector<int64_t>* cols) {
+  *rows = -1;
+  cols->assign(ne, 0);
+  for (int e = 0; e < ne; ++e) {
+    int64_t r, c;
+    matv(X[e], &r, &c);
+    if (*rows >= 0 && r != *rows) return fail(TT_ERR_SHAPE, "%s: feature tiles have different row counts", nm);
+    *rows = r;
+    (*cols)[e] = c;
+  }
+  int64_t total = 0;
+  for (int e = 0; e < ne; ++e) {
+    const int64_t c = (*cols)[e];
+    if (c < 4 || c % 4 || c > (*cols)[0] || (e + 1 < ne && c != (*cols)[0]))
+      return fail(TT_ERR_SHAPE, "%s: tile widths must be multiples of 4, equal but for a narrower last tile", nm);
+    total += c;
+  }
+  if (total > 16384) return fail(TT_ERR_SHAPE, "%s: %lld features exceed 16384", nm, (long long)total);
+  return TT_OK;
+}
+
+int op_rms_fwd(tt_ctx* ctx, const TileArg* T, int n, const tt_op_layernorm& q, const char* label) {
+  const char* nm = "TT_OP_RMSNORM_FWD";
+  if (n < 4 || (n - 1) % 3 || (n - 1) / 3 > 16) return fail(TT_ERR_ARG, "%s: needs 3n+1 tiles, n <= 16", nm);
+  if (int rc = need_f32(T, n, nm)) return rc;
+  const int ne = (n - 1) / 3;
+  const TileArg *X = T, *Gm = T + ne, *Y = T + 2 * ne + 1;
+  const TileArg rs = T[2 * ne];
+  int64_t rows;
+  std::vector<int64_t> cols;
+  if (int rc = rms_cols(nm, X, ne, &rows, &cols)) return rc;
+  std::vector<Access> acc;
+  for (int e = 0; e < ne; ++e) {
+    int64_t yr, yc;
+    matv(Y[e], &yr, &yc);
+    if (yr != rows || yc != cols[e] || elems(Gm[e]) != cols[e])
+      return fail(TT_ERR_SHAPE, "%s: feature tile %d: shapes of x, gamma, y disagree", nm, e);
+    acc.push_back(acc_of(X[e], TT_R));
+    acc.push_back(acc_of(Gm[e], TT_R));
+    acc.push_back(acc_of(Y[e], TT_W));
+  }
+  if (elems(rs) < rows) return fail(TT_ERR_SHAPE, "%s: rstd tile holds fewer than rows floats", nm);
+  acc.push_back(acc_of(rs, TT_W));
+  std::vector<TileArg> tl(T, T + n);
+  const float eps = q.eps;
+  return ctx->submit(label ? label : "rms_fwd", std::move(acc), [=](hipStream_t s, void*) {
+    std::vector<const float*> xs(ne), gs(ne);
+    std::vector<float*> ys(ne);
+    for (int e = 0; e < ne; ++e) {
+      xs[e] = Fp(tl[e]);
+      gs[e] = Fp(tl[ne + e]);
+      ys[e] = Fp(tl[2 * ne + 1 + e]);
+    }
+    return tile_rmsnorm_fwd(s, ne, rows, cols.data(), xs.data(), gs.data(), Fp(tl[2 * ne]), ys.data(), eps);
+  });
+}
+
+int op_rms_bwd(tt_ctx* ctx, const TileArg* T, int n, const tt_op_layernorm& q, const char* label, bool grow) {
+  const char* nm = "TT_OP_RMSNORM_BWD";
+  if (n < 6 || (n - 1) % 5 || (n - 1) / 5 > 16) return fail(TT_ERR_ARG, "%s: needs 5n+1 tiles, n <= 16", nm);
+  if (int rc = need_f32(T, n, nm)) return rc;
+  const int ne = (n - 1) / 5;
+  const TileArg *DY = T, *X = T + ne, *Gm = T + 2 * ne, *DX = T + 3 * ne + 1, *DG = T + 4 * ne + 1;
+  const TileArg rs = T[3 * ne];
+  int64_t rows;
+  std::vector<int64_t> cols;
+  if (int rc = rms_cols(nm, X, ne, &rows, &cols)) return rc;
+  std::vector<Access> acc;
+  int64_t total = 0;
+  for (int e = 0; e < ne; ++e) {
+    int64_t dyr, dyc, dxr, dxc;
+    matv(DY[e], &dyr, &dyc);
+    matv(DX[e], &dxr, &dxc);
+    if (dyr != rows || dyc != cols[e] || dxr != rows || dxc != cols[e] || elems(Gm[e]) != cols[e] ||
+        elems(DG[e]) != cols[e])
+      return fail(TT_ERR_SHAPE, "%s: feature tile %d: shapes of dy, x, dx, gamma, dgamma disagree", nm, e);
+    total += cols[e];
+    acc.push_back(acc_of(DY[e], TT_R));
+    acc.push_back(acc_of(X[e], TT_R));
+    acc.push_back(acc_of(Gm[e], TT_R));
+    acc.push_back(acc_of(DX[e], q.dx_acc ? TT_RW : TT_W));
+    acc.push_back(acc_of(DG[e], TT_RW));
+  }
+  if (elems(rs) < rows) return fail(TT_ERR_SHAPE, "%s: rstd tile holds fewer than rows floats", nm);
+  acc.push_back(acc_of(rs, TT_R));
+  const size_t need = tile_rmsnorm_bwd_workspace(rows, total);
+  if (grow)
+    if (int rc = ctx->ensure_workspace(need)) return rc;
+  std::vector<TileArg> tl(T, T + n);
+  const int dx_acc = q.dx_acc;
+  return ctx->submit(label ? label : "rms_bwd", std::move(acc), [=](hipStream_t s, void* ws) {
+    std::vector<const float*> dys(ne), xs(ne), gs(ne);
+    std::vector<float*> dxs(ne), dgs(ne);
+    for (int e = 0; e < ne; ++e) {
+      dys[e] = Fp(tl[e]);
+      xs[e] = Fp(tl[ne + e]);
+      gs[e] = Fp(tl[2 * ne + e]);
+      dxs[e] = Fp(tl[3 * ne + 1 + e]);
+      dgs[e] = Fp(tl[4 * ne + 1 + e]);
+    }
+    return tile_rmsnorm_bwd(s, ne, rows, cols.data(), dys.data(), xs.data(), gs.data(), Fp(tl[3 * ne]), dxs.data(),
+                            dx_acc, dgs.data(), ws, ctx->workspace_bytes);
+  });
+}
+
+int op_rope(tt_ctx* ctx, const TileArg* T, int n, const tt_op_rope& q, const char* label) {
+  const char* nm = "TT_OP_ROPE";
+  if (n < 2 || n > 5) return fail(TT_ERR_ARG, "%s: tiles x_0..x_{n-1} (1..4), table", nm);
+  if (int rc = need_f32(T, n, nm)) return rc;
+  int64_t ext[TT_MAX_DIMS];
+  const TileArg& x0 = T[0];
+  if (x0.t->ndim != 4) return fail(TT_ERR_SHAPE, "%s: x tiles must be 4-D [batch, len, heads, hd]", nm);
+  x0.t->extent(x0.lin, ext);
+  const int64_t len = ext[1], heads = ext[2], hd = ext[3], rows = ext[0] * ext[1];
+  std::vector<Access> acc;
+  for (int i = 0; i < n - 1; ++i) {
+    int64_t e2[TT_MAX_DIMS];
+    if (T[i].t->ndim != 4) return fail(TT_ERR_SHAPE, "%s: x tiles must be 4-D", nm);
+    T[i].t->extent(T[i].lin, e2);
+    if (e2[0] != ext[0] || e2[1] != len || e2[2] != heads || e2[3] != hd)
+      return fail(TT_ERR_SHAPE, "%s: x tiles must have equal extents", nm);
+    acc.push_back(acc_of(T[i], TT_RW));
+  }
+  const TileArg tab = T[n - 1];
+  int64_t tr, tc;
+  matv(tab, &tr, &tc);
+  if (tc != hd || q.pos_off < 0 || q.pos_off + len > tr)
+    return fail(TT_ERR_SHAPE, "%s: table %lldx%lld does not cover positions %lld..%lld of head dim %lld", nm,
+                (long long)tr, (long long)tc, (long long)q.pos_off, (long long)(q.pos_off + len - 1), (long long)hd);
+  acc.push_back(acc_of(tab, TT_R));
+  std::vector<TileArg> tl(T, T + n);
+  const int64_t off = q.pos_off;
+  const int inv = q.inverse;
+  return ctx->submit(label ? label : "rope", std::move(acc), [=](hipStream_t s, void*) {
+    for (int i = 0; i < n - 1; ++i)
+      if (int rc = tile_rope(s, Fp(tl[i]), rows, heads, hd, len, off, Fp(tl[n - 1]), tr, inv)) return rc;
+    return TT_OK;
+  });
+}
+
+int op_rope_table(tt_ctx* ctx, const TileArg* T, int n, const tt_op_rope& q, const char* label) {
+  const char* nm = "TT_OP_ROPE_TABLE";
+  if (n != 1) return fail(TT_ERR_ARG, "%s: one tile (the table)", nm);
+  if (int rc = need_f32(T, n, nm)) return rc;
+  int64_t r, c;
+  matv(T[0], &r, &c);
+  if (c != 16 && c != 32 && c != 64 && c != 128) return fail(TT_ERR_SHAPE, "%s: head dim %lld", nm, (long long)c);
+  if (!(q.base > 1.0)) return fail(TT_ERR_ARG, "%s: base must exceed 1", nm);
+  const TileArg t = T[0];
+  const double base = q.base;
+  return ctx->submit(label ? label : "rope_table", {acc_of(t, TT_W)},
+                     [=](hipStream_t s, void*) { return tile_rope_table(s, r, c, base, Fp(t)); });
+}
+
+int op_swiglu(tt_ctx* ctx, const TileArg* T, int n, const char* label, bool bwd) {
+  const char* nm = bwd ? "TT_OP_SWIGLU_BWD" : "TT_OP_SWIGLU_FWD";
+  if (n < 3 || n % 3 || n / 3 > 16) return fail(TT_ERR_ARG, "%s: 1..16 tile triples", nm);
+  if (int rc = need_f32(T, n, nm)) return rc;
+  std::vector<Access> acc;
+  for (int i = 0; i < n; i += 3) {
+    if (elems(T[i]) != elems(T[i + 1]) || elems(T[i]) != elems(T[i + 2]))
+      return fail(TT_ERR_SHAPE, "%s: triple %d: element counts differ", nm, i / 3);
+    if (bwd) {  // dh, a, b: a and b replaced by their gradients
+      acc.push_back(acc_of(T[i], TT_R));
+      acc.push_back(acc_of(T[i + 1], TT_RW));
+      acc.push_back(acc_of(T[i + 2], TT_RW));
+    } else {    // a, b, h
+      acc.push_back(acc_of(T[i], TT_R));
+      acc.push_back(acc_of(T[i + 1], TT_R));
+      acc.push_back(acc_of(T[i + 2], TT_W));
+    }
+  }
+  std::vector<TileArg> tl(T, T + n);
+  return ctx->submit(label ? label : (bwd ? "swiglu_bwd" : "swiglu"), std::move(acc), [=](hipStream_t s, void*) {
+    for (int i = 0; i < n; i += 3) {
+      const int64_t cnt = elems(tl[i]);
+      const int rc = bwd ? tile_swiglu_bwd(s, cnt, Fp(tl[i]), Fp(tl[i + 1]), Fp(tl[i + 2]), Fp(tl[i + 1]),
+                                           Fp(tl[i + 2]))
+                         : tile_swiglu_fwd(s, cnt, Fp(tl[i]), Fp(tl[i + 1]), Fp(tl[i + 2]));
+      if (rc) return rc;
+    }
+    return TT_OK;
+  });
+}
+
 }  // namespace
 
 size_t layernorm_fwd_workspace(int64_t n, int64_t rows) {
@@ -1140,11 +1335,13 @@ int submit_op(tt_ctx* ctx, int op, const TileArg* T, int n, const void* sc, size
       return op_sgd(ctx, T, n, q, label);
     }
     case TT_OP_EMBEDDING_FWD:
+    case TT_OP_EMBEDDING_TOKEN_FWD:
     case TT_OP_EMBEDDING_BWD:
     case TT_OP_EMBEDDING_POS_BWD: {
       tt_op_embedding q;
       if (int rc = scal(sc, size, "TT_OP_EMBEDDING*", &q)) return rc;
-      if (op == TT_OP_EMBEDDING_FWD) return op_emb_fwd(ctx, T, n, q, label);
+      if (op == TT_OP_EMBEDDING_FWD || op == TT_OP_EMBEDDING_TOKEN_FWD)
+        return op_emb_fwd(ctx, T, n, q, label, op == TT_OP_EMBEDDING_FWD);
       if (op == TT_OP_EMBEDDING_BWD) return op_emb_bwd(ctx, T, n, q, label);
       return op_emb_pos_bwd(ctx, T, n, q, label);
     }
@@ -1157,6 +1354,21 @@ int submit_op(tt_ctx* ctx, int op, const TileArg* T, int n, const void* sc, size
     }
     case TT_OP_SPLIT_TOKENS:
       return op_split(ctx, T, n, label);
+    case TT_OP_RMSNORM_FWD:
+    case TT_OP_RMSNORM_BWD: {
+      tt_op_layernorm q;
+      if (int rc = scal(sc, size, "TT_OP_RMSNORM*", &q)) return rc;
+      return op == TT_OP_RMSNORM_FWD ? op_rms_fwd(ctx, T, n, q, label) : op_rms_bwd(ctx, T, n, q, label, grow);
+    }
+    case TT_OP_ROPE:
+    case TT_OP_ROPE_TABLE: {
+      tt_op_rope q;
+      if (int rc = scal(sc, size, "TT_OP_ROPE*", &q)) return rc;
+      return op == TT_OP_ROPE ? op_rope(ctx, T, n, q, label) : op_rope_table(ctx, T, n, q, label);
+    }
+    case TT_OP_SWIGLU_FWD:
+    case TT_OP_SWIGLU_BWD:
+      return op_swiglu(ctx, T, n, label, op == TT_OP_SWIGLU_BWD);
     case TT_OP_COPY_IN: {
       tt_op_copy q;
       if (int rc = scal(sc, size, "TT_OP_COPY_IN", &q)) return rc;

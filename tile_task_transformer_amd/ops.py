@@ -25,7 +25,8 @@ __all__ = [
     "tile_embedding_fwd", "tile_embedding_index", "tile_embedding_bwd", "tile_reduce_rows",
     "tile_reduce_rows_workspace", "tile_reduce_rows_multi", "tile_fill", "tile_fill_multi", "tile_split_tokens",
     "tt_probe_mfma_f32", "tile_layernorm_fwd_multi", "tile_layernorm_bwd_multi",
-    "tile_layernorm_bwd_multi_workspace",
+    "tile_layernorm_bwd_multi_workspace", "tile_rmsnorm_fwd", "tile_rmsnorm_bwd", "tile_rmsnorm_bwd_workspace",
+    "tile_rope_table", "tile_rope", "tile_swiglu_fwd", "tile_swiglu_bwd",
     "TT_EPI_NONE", "TT_EPI_BIAS", "TT_EPI_RES", "TT_EPI_GELU", "TT_EPI_GELU_BWD", "TT_LN_PARTIAL",
     "TT_LN_MERGE", "TT_LN_APPLY", "TT_LN_FUSED", "TT_SM_STATS", "TT_SM_MERGE", "TT_SM_APPLY", "TT_XE_LOSS",
     "TT_XE_GRAD", "TT_XE_STATS", "TT_ATT_PREP", "TT_ATT_GRAD", "TT_EMB_TOKEN", "TT_EMB_POS",
@@ -315,3 +316,43 @@ def tile_layernorm_bwd_multi(stream, rows, cols, dys, xs, gammas, stats, dxs, dx
 
 def tile_layernorm_bwd_multi_workspace(rows, total_cols):
     return lib.tile_layernorm_bwd_multi_workspace(rows, total_cols)
+
+
+def tile_rmsnorm_fwd(stream, rows, cols, xs, gammas, rstd, ys, eps=1e-5):
+    """RMSNorm of a row block over 1..16 feature tiles (the LLaMA block)."""
+    import ctypes as C
+    n = len(xs)
+    c = (C.c_int64 * n)(*[int(v) for v in cols])
+    x, g, y = _arrs(n, xs, gammas, ys)
+    return check(lib.tile_rmsnorm_fwd(stream_handle(stream), n, rows, c, x, g, ptr(rstd), y, eps))
+
+
+def tile_rmsnorm_bwd(stream, rows, cols, dys, xs, gammas, rstd, dxs, dx_acc, dgammas, workspace, workspace_bytes):
+    import ctypes as C
+    n = len(xs)
+    c = (C.c_int64 * n)(*[int(v) for v in cols])
+    dy, x, g, dx, dg = _arrs(n, dys, xs, gammas, dxs, dgammas)
+    return check(lib.tile_rmsnorm_bwd(stream_handle(stream), n, rows, c, dy, x, g, ptr(rstd), dx, dx_acc, dg,
+                                      ptr(workspace), workspace_bytes))
+
+
+def tile_rmsnorm_bwd_workspace(rows, total_cols):
+    return lib.tile_rmsnorm_bwd_workspace(rows, total_cols)
+
+
+def tile_rope_table(stream, seq, hd, base, table):
+    return check(lib.tile_rope_table(stream_handle(stream), seq, hd, float(base), ptr(table)))
+
+
+def tile_rope(stream, x, rows, heads, hd, seq_len, pos_off, table, table_rows, inverse=False):
+    """Rotary embedding of a [rows, heads, hd] q or k tile, in place."""
+    return check(lib.tile_rope(stream_handle(stream), ptr(x), rows, heads, hd, seq_len, pos_off, ptr(table),
+                               table_rows, int(inverse)))
+
+
+def tile_swiglu_fwd(stream, n, a, b, h):
+    return check(lib.tile_swiglu_fwd(stream_handle(stream), n, ptr(a), ptr(b), ptr(h)))
+
+
+def tile_swiglu_bwd(stream, n, dh, a, b, da, db):
+    return check(lib.tile_swiglu_bwd(stream_handle(stream), n, ptr(dh), ptr(a), ptr(b), ptr(da), ptr(db)))

@@ -199,14 +199,19 @@ class GPT2:
     """The GPT2 training step of libtiletask. `shape`/`tiles` are synth.GPT2Shape
     / synth.Tiles-like objects (attribute access)."""
 
-    def __init__(self, ctx: Context, shape, tiles, param_home: int = L.TT_HOME_DEVICE, ln_eps: float = 1e-5):
+    def __init__(self, ctx: Context, shape, tiles, param_home: int = L.TT_HOME_DEVICE, ln_eps: float = 1e-5,
+                 family: str = "gpt2"):
+        """family "gpt2" (tt_gpt2_create) or "llama" (tt_llama_create: the
+        LLaMA-style block; ln_eps is then the RMSNorm eps)."""
         self.ctx = ctx
         self.shape = shape
+        self.family = family
+        create = {"gpt2": lib.tt_gpt2_create, "llama": lib.tt_llama_create}[family]
         cfg = L.tt_gpt2_config(shape.n_layer, shape.vocab, shape.n_embd, shape.n_head, shape.n_inner, shape.seq,
                                shape.batch, ln_eps)
         tl = L.tt_gpt2_tiles(tiles.batch, tiles.seq, tiles.embd, tiles.inner, tiles.head, tiles.vocab)
         h = C.c_void_p()
-        check(lib.tt_gpt2_create(ctx.h, C.byref(cfg), C.byref(tl), param_home, C.byref(h)))
+        check(create(ctx.h, C.byref(cfg), C.byref(tl), param_home, C.byref(h)))
         self.h = h
         n = C.c_int()
         check(lib.tt_gpt2_num_params(self.h, C.byref(n)))
