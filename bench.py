@@ -4,7 +4,9 @@ heads, inner 32768, vocab 50257, seq 1024, batch 4; 3.64 B parameters, all
 state in HBM) with large tiles (batch 4, seq 1024, embd 2048, inner 8192,
 head 16, vocab 2048) -- the largest configuration that fits one GPU. The
 GPT2-small step (12 blocks, d 768, the NNTile README's example tiles) is
-timed after it and reported under "gpt2_small".
+timed after it and reported under "gpt2_small", and the LLaMA-style model
+at the same width and depth (RMSNorm, rotary embedding, SwiGLU width 2048,
+untied head, vocab 32000) under "llama_small".
 
 Prints ONE JSON line:
   value        tokens/s of the whole step (inputs resident in HBM)
@@ -77,24 +79,41 @@ def traffic_bytes(workload: str, label: str):
     return 1024.0 * (t["fetch_kib"] * t["fetch_factor"] + t["write_kib"] * t["write_factor"])
 
 
-def model_flops(s) -> float:
+ALL_WORKLOADS = {**synth.WORKLOADS, **synth.LLAMA_WORKLOADS}
+
+
+def family_of(name: str) -> str:
+    """Block family of a workload: the LLaMA-style ones use RMSNorm, rotary
+    embedding and a SwiGLU MLP (three MLP products instead of two)."""
+    return "llama" if name in synth.LLAMA_WORKLOADS else "gpt2"
+
+
+def specs_of(s, family: str):
+    return synth.llama_param_specs(s) if family == "llama" else synth.param_specs(s)
+
+
+def model_flops(s, family: str = "gpt2") -> float:
     n = s.batch * s.seq
-    per_block = 2 * n * s.n_embd * (3 * s.n_embd + s.n_embd + 2 * s.n_inner)
+    mlp = 3 if family == "llama" else 2  # gate, up, down against input and output layers
+    per_block = 2 * n * s.n_embd * (3 * s.n_embd + s.n_embd + mlp * s.n_inner)
     attn = 2 * 2 * s.batch * s.n_embd * (s.seq * (s.seq + 1) // 2)
     head = 2 * n * s.n_embd * s.vocab
     return 3.0 * (s.n_layer * (per_block + attn) + head)
 
 
-def class_work(s) -> dict:
+def class_work(s, family: str = "gpt2") -> dict:
     """Algorithmic work of each task class over one step: label -> (bound,
     amount, unit). GEMM classes count 2*m*n*k over all their tiles (ragged
     tiles included, so dividing by the launch count gives the exact mean per
     launch); attention counts causal pairs T(T+1)/2, the backward as 5
     products against the forward's 2 (its recompute of P included); memory
-    classes count the bytes each kernel must move at least."""
+    classes count the bytes each kernel must move at least. LLaMA-style
+    steps: "fc" is the SwiGLU gate and up products together, RMSNorm,
+    rotary and SwiGLU passes replace LayerNorm and the bias column sums."""
     n, d, i, v, L = s.batch * s.seq, s.n_embd, s.n_inner, s.vocab, s.n_layer
-    f = {"qkv": 2.0 * n * d * 3 * d * L, "attn_proj": 2.0 * n * d * d * L, "fc": 2.0 * n * d * i * L,
-         "mlp_proj": 2.0 * n * i * d * L, "head": 2.0 * n * d * v}
+    llama = family == "llama"
+    f = {"qkv": 2.0 * n * d * 3 * d * L, "attn_proj": 2.0 * n * d * d * L,
+         "fc": 2.0 * n * d * i * L * (2 if llama else 1), "mlp_proj": 2.0 * n * i * d * L, "head": 2.0 * n * d * v}
     out = {}
     for k, x in f.items():
         for suf in ("", "_dx", "_dw"):
@@ -102,12 +121,19 @@ def class_work(s) -> dict:
     att = 2 * 2 * s.batch * d * (s.seq * (s.seq + 1) // 2) * L
     out["attn_fwd"] = ("mfma", float(att), "flop")
     out["attn_bwd"] = ("mfma", 2.5 * att, "flop")
-    out["ln_fwd"] = ("hbm", 8.0 * n * d * (2 * L + 1), "B")
-    out["ln_bwd"] = ("hbm", 16.0 * n * d * (2 * L + 1), "B")
+    norm = "rms" if llama else "ln"
+    out[norm + "_fwd"] = ("hbm", 8.0 * n * d * (2 * L + 1), "B")
+    out[norm + "_bwd"] = ("hbm", 16.0 * n * d * (2 * L + 1), "B")
     out["ce_stats"] = ("hbm", 4.0 * n * v, "B")
     out["ce_grad"] = ("hbm", 8.0 * n * v, "B")
-    out["colsum"] = ("hbm", 4.0 * n * (3 * d + d + i + d) * L, "B")
-    n_params = sum(int(np.prod(shp)) for _, shp, _ in synth.param_specs(s))
+    if llama:
+        out["rope"] = ("hbm", 16.0 * n * d * L, "B")         # q and k read and written in place
+        out["rope_bwd"] = ("hbm", 16.0 * n * d * L, "B")
+        out["swiglu"] = ("hbm", 12.0 * n * i * L, "B")       # gate, up read; product written
+        out["swiglu_bwd"] = ("hbm", 20.0 * n * i * L, "B")   # dh, gate, up read; two gradients written
+    else:
+        out["colsum"] = ("hbm", 4.0 * n * (3 * d + d + i + d) * L, "B")
+    n_params = sum(int(np.prod(shp)) for _, shp, _ in specs_of(s, family))
     out["adamw"] = ("hbm", 28.0 * n_params, "B")
     return out
 
@@ -117,7 +143,8 @@ def class_work(s) -> dict:
 # to and writes dx; the statistics and column sums only read; the gradient
 # of the logits reads z and writes dz; AdamW reads p, g, m, v and writes p,
 # m, v
-WRITE_SHARE = {"ln_fwd": 0.5, "ln_bwd": 0.25, "ce_stats": 0.0, "ce_grad": 0.5, "colsum": 0.0, "adamw": 3 / 7}
+WRITE_SHARE = {"ln_fwd": 0.5, "ln_bwd": 0.25, "ce_stats": 0.0, "ce_grad": 0.5, "colsum": 0.0, "adamw": 3 / 7,
+               "rms_fwd": 0.5, "rms_bwd": 0.25, "rope": 0.5, "rope_bwd": 0.5, "swiglu": 1 / 3, "swiglu_bwd": 0.4}
 
 
 def hbm_ceiling(probe: dict, write_share: float) -> float:
@@ -132,10 +159,10 @@ def hbm_ceiling(probe: dict, write_share: float) -> float:
 CLASS_LABELS = {"ln_fwd": ("ln_fwd", "ln_part", "ln_merge", "ln_apply"), "ln_bwd": ("ln_bwd", "lnb_part", "lnb_apply")}
 
 
-def class_rooflines(breakdown: dict, s) -> dict:
+def class_rooflines(breakdown: dict, s, family: str = "gpt2") -> dict:
     """Per-class achieved throughput from a serialized profiled step."""
     res = {}
-    for label, (bound, amount, unit) in class_work(s).items():
+    for label, (bound, amount, unit) in class_work(s, family).items():
         parts = [breakdown[x] for x in CLASS_LABELS.get(label, (label,)) if x in breakdown]
         b = {"count": sum(x["count"] for x in parts), "total_ms": sum(x["total_ms"] for x in parts)}
         if not b["count"]:
@@ -540,9 +567,10 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="wide4", choices=sorted(synth.WORKLOADS))
-    ap.add_argument("--also", default="gpt2_small",
-                    help="a second workload timed after the first and reported under its name ('' = none)")
+    ap.add_argument("--workload", default="wide4", choices=sorted(ALL_WORKLOADS))
+    ap.add_argument("--also", default="gpt2_small,llama_small",
+                    help="comma-separated workloads timed after the first, each reported under its name "
+                         "('' = none)")
     ap.add_argument("--streams", type=int, default=0,
                     help="executor streams (0 = measured best per workload: 1; small tiles 4; pinned 1)")
     ap.add_argument("--heavy-gflops", type=float, default=0.0,
@@ -569,7 +597,7 @@ def main(argv=None):
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
         return 2
 
-    w = synth.WORKLOADS[a.workload]
+    w = ALL_WORKLOADS[a.workload]
     if a.streams <= 0:
         # measured on MI355X: many small tasks need concurrency (small tiles:
         # 911 ms on 4 streams, 1018 on 2); GPT2-small's and the wide model's
@@ -592,14 +620,18 @@ def main(argv=None):
     print(f"[bench] probes: {probe}", file=sys.stderr, flush=True)
     out, keep = run(w, a, a.streams, a.breakdown, probe)
     out["probes"] = probe
-    if a.also and a.also != a.workload:
-        w2 = synth.WORKLOADS[a.also]
-        o2, _ = run(w2, a, {"wide4_small_tiles": 4}.get(a.also, 1), "", probe, steps=max(a.steps, 10),
+    for name in [x for x in a.also.split(",") if x and x != a.workload]:
+        w2 = ALL_WORKLOADS[name]
+        o2, _ = run(w2, a, {"wide4_small_tiles": 4}.get(name, 1), "", probe, steps=max(a.steps, 10),
                     warmup=max(a.warmup, 3), want_params=False)
-        out[a.also] = {k: o2[k] for k in ("value", "unit", "ms_per_step", "tflops", "mfma_frac", "tasks_per_step",
-                                          "loss", "roofline")}
-        out[a.also]["config"] = o2["config"]
-    if not a.no_cpu_baseline:
+        out[name] = {k: o2[k] for k in ("value", "unit", "ms_per_step", "tflops", "mfma_frac", "tasks_per_step",
+                                        "loss", "roofline", "largest_class")}
+        out[name]["config"] = o2["config"]
+        if family_of(name) == "llama":
+            out[name]["classes"] = o2["classes"]
+    if not a.no_cpu_baseline and family_of(w.name) != "gpt2":
+        print("[bench] the CPU baseline samples the GPT2 oracle: skipped for this workload", file=sys.stderr)
+    elif not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, keep["params"], keep["tokens"])
         cb = out["cpu_baseline"]
         cb["gpu_speedup"] = round(out["value"] / cb["value"], 1)
@@ -619,15 +651,16 @@ def run(w, a, streams, breakdown_path, probe, steps=None, warmup=None, want_para
     steps = steps or a.steps
     warmup = a.warmup if warmup is None else warmup
     s, t = w.shape, w.tiles
-    specs = synth.param_specs(s)
+    family = family_of(w.name)
+    specs = specs_of(s, family)
     t0 = time.perf_counter()
-    params = synth.init_params(s, seed=0, threads=min(16, len(os.sched_getaffinity(0))))
+    params = synth.init_params(s, seed=0, threads=min(16, len(os.sched_getaffinity(0))), specs=specs)
     tokens = synth.token_stream(s, seed=1)
     home = L.TT_HOME_PINNED_HOST if a.pinned else L.TT_HOME_DEVICE
     ctx = Context(0, n_streams=streams, window=4096, device_budget=int(a.budget_gb * 2 ** 30))
     if a.heavy_gflops > 0:
         ctx.heavy_lane(a.heavy_gflops * 1e9)
-    model = GPT2(ctx, s, t, param_home=home)
+    model = GPT2(ctx, s, t, param_home=home, family=family)
     model.set_params(params, specs)
     if not want_params or a.no_cpu_baseline:
         params = None  # the oracle sample is not needed: free the host copy
@@ -648,7 +681,7 @@ def run(w, a, streams, breakdown_path, probe, steps=None, warmup=None, want_para
     breakdown = ctx.profile_take()
     ctx.profile(None)
     ctx.streams_active(streams)
-    classes = class_rooflines(breakdown, s)
+    classes = class_rooflines(breakdown, s, family)
     if probe:
         # matrix classes against the measured matrix peak; memory classes
         # against the stream probe of their traffic mix
@@ -668,7 +701,7 @@ def run(w, a, streams, breakdown_path, probe, steps=None, warmup=None, want_para
               file=sys.stderr)
     print(f"  serialized total {sum(b['total_ms'] for b in breakdown.values()):.2f} ms", file=sys.stderr,
           flush=True)
-    work = class_work(s)
+    work = class_work(s, family)
     # the dominant class: the largest share of the step's model flops among
     # the matrix-core classes (GEMM and attention alike), ties (the MLP's
     # six products of equal size) broken by name, so that the choice does
@@ -699,7 +732,7 @@ def run(w, a, streams, breakdown_path, probe, steps=None, warmup=None, want_para
 
     ms = 1e3 * elapsed / steps
     tok_s = s.batch * s.seq / (elapsed / steps)
-    tflops = model_flops(s) / (elapsed / steps) / 1e12
+    tflops = model_flops(s, family) / (elapsed / steps) / 1e12
     launches = prof.get("count", 0)
     per_step = classes[dominant]["launches"] if dominant in classes else launches * every / steps
     per_launch = work[dominant][1] / per_step if launches else float("nan")
@@ -710,7 +743,7 @@ def run(w, a, streams, breakdown_path, probe, steps=None, warmup=None, want_para
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
         "warmup": warmup, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": w.name, "global_batch": s.batch, "seq_len": s.seq, "n_layer": s.n_layer,
+        "config": {"workload": w.name, "family": family, "global_batch": s.batch, "seq_len": s.seq, "n_layer": s.n_layer,
                    "n_embd": s.n_embd, "n_inner": s.n_inner, "n_head": s.n_head, "vocab": s.vocab,
                    "tiles": {"batch": t.batch, "seq": t.seq, "embd": t.embd, "inner": t.inner, "head": t.head,
                              "vocab": t.vocab}, "streams": streams, "heavy_gflops": a.heavy_gflops,
@@ -761,7 +794,7 @@ def executor_figures(w, model, ctx, tok, hp, streams, ms, st, steps, busy_steps=
     import tempfile
     ntask = model.task_count()
     with Context(L.TT_DEVICE_DRYRUN, n_streams=streams, window=4096) as dctx:
-        dm = GPT2(dctx, w.shape, w.tiles)
+        dm = GPT2(dctx, w.shape, w.tiles, family=family_of(w.name))
         dm.step(None, **hp)
         t0 = time.perf_counter()
         for _ in range(2):
@@ -770,7 +803,7 @@ def executor_figures(w, model, ctx, tok, hp, streams, ms, st, steps, busy_steps=
         dm.close()
     with tempfile.TemporaryDirectory() as tmp, Context(L.TT_DEVICE_DRYRUN, n_streams=streams, window=4096) as dctx:
         dctx.record(True)
-        dm = GPT2(dctx, w.shape, w.tiles)
+        dm = GPT2(dctx, w.shape, w.tiles, family=family_of(w.name))
         dm.step(None, **hp)
         depth = dag_depth(dctx.dump_dag(os.path.join(tmp, "step.jsonl")))
         dm.close()

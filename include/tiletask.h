@@ -346,6 +346,10 @@ size_t tile_rmsnorm_bwd_workspace(int64_t rows, int64_t total_cols);
 int tile_rope_table(void* stream, int64_t seq, int64_t hd, double base, float* table);
 int tile_rope(void* stream, float* x, int64_t rows, int64_t heads, int64_t hd, int64_t seq_len,
               int64_t pos_off, const float* table, int64_t table_rows, int inverse);
+/* tile_rope_multi -- tile_rope on 1..4 tiles of equal shape in one launch
+ * (a q and a k tile); x is a HOST array of DEVICE pointers. */
+int tile_rope_multi(void* stream, int count, float* const* x, int64_t rows, int64_t heads, int64_t hd,
+                    int64_t seq_len, int64_t pos_off, const float* table, int64_t table_rows, int inverse);
 /* tile_swiglu_fwd / tile_swiglu_bwd -- the LLaMA MLP's gate over n
  * contiguous DEVICE floats: h = silu(a) * b, silu(a) = a / (1 + exp(-a));
  * backward da = dh * b * silu'(a), db = dh * silu(a). da and db may be a

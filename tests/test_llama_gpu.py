@@ -123,6 +123,14 @@ def test_rope_forward_and_transpose(batch, length, heads, hd, pos_off):
     assert_rel(host(t), x.astype(np.float64), 0, 16 * EPS32 * np.abs(x).max(), "round trip")
     with pytest.raises(L.TTError):
         tt.tile_rope(None, dev(x), rows, heads, hd, length, seq - length + 1, tab, seq, 0)
+    # several tiles in one launch: each gets the single-tile result, bit for bit
+    xs = [synth.rand_normal((batch, length, heads, hd), rows + hd + pos_off + j) for j in range(3)]
+    ts = [dev(v) for v in xs]
+    tt.tile_rope_multi(None, ts, rows, heads, hd, length, pos_off, tab, seq, 0)
+    for v, t in zip(xs, ts):
+        one = dev(v)
+        tt.tile_rope(None, one, rows, heads, hd, length, pos_off, tab, seq, 0)
+        assert np.array_equal(host(t), host(one))
 
 
 @pytest.mark.parametrize("n", [4096 + 64, 1001, 3, 0])

@@ -179,6 +179,7 @@ SIGNATURES = {
     "tile_rmsnorm_bwd_workspace": (SZ, [I64, I64]),
     "tile_rope_table": (I, [P, I64, I64, C.c_double, P]),
     "tile_rope": (I, [P, P, I64, I64, I64, I64, I64, P, I64, I]),
+    "tile_rope_multi": (I, [P, I, P, I64, I64, I64, I64, I64, P, I64, I]),
     "tile_swiglu_fwd": (I, [P, I64, P, P, P]),
     "tile_swiglu_bwd": (I, [P, I64, P, P, P, P, P]),
     "tile_softmax": (I, [P, I, I64, I64, I64, I64, F, I, P, I64, P, P, I64, I64, P, P, P, I64, F]),

@@ -875,7 +875,14 @@ __global__ __launch_bounds__(1024) void rms_colsum_finish_multi(int nblk, LnRowT
   colsum_finish_block(nblk, width, ws, (int64_t)P.total, (int64_t)t * P.c0, P.dg[t], 1);
 }
 
+// rows per backward workgroup: up to 16 (fewer column partials to sum), but
+// at least ~1024 workgroups when the rows allow (a 4096-row block of 768
+// features on 16 rows per workgroup makes 256 workgroups, one per CU:
+// 20 % of HBM)
 constexpr int kRmsBwdRowsPerBlock = 16;
+int rms_bwd_rows_per_block(int64_t rows) {
+  return (int)std::max<int64_t>(1, std::min<int64_t>(kRmsBwdRowsPerBlock, rows / 1024));
+}
 
 // like ln_multi_check, one tile allowed
 int rms_check(const char* nm, int count, int64_t rows, const int64_t* cols, LnRowTiles* P) {
@@ -930,7 +937,8 @@ extern "C" int tile_rmsnorm_fwd(void* stream, int count, int64_t rows, const int
 
 extern "C" size_t tile_rmsnorm_bwd_workspace(int64_t rows, int64_t total) {
   if (rows < 0 || total < 0) return 0;
-  const int64_t nblk = (rows + kRmsBwdRowsPerBlock - 1) / kRmsBwdRowsPerBlock;
+  const int rpb = rms_bwd_rows_per_block(rows);
+  const int64_t nblk = (rows + rpb - 1) / rpb;
   return (size_t)(nblk * total * sizeof(float));
 }
 
@@ -959,11 +967,12 @@ extern "C" int tile_rmsnorm_bwd(void* stream, int count, int64_t rows, const int
   int bt, vpt;
   ln_multi_geometry(P.total, &bt, &vpt);
   const int r = (int)rows;
-  const int nblk = (r + kRmsBwdRowsPerBlock - 1) / kRmsBwdRowsPerBlock;
+  const int rpb = rms_bwd_rows_per_block(rows);
+  const int nblk = (r + rpb - 1) / rpb;
   float* ws = (float*)workspace;
   hipStream_t s = tt::as_stream(stream);
 #define TT_RMSB(BT, VPT) \
-  hipLaunchKernelGGL((rms_bwd_multi<BT, VPT>), dim3(nblk), dim3(BT), 0, s, r, kRmsBwdRowsPerBlock, P, rstd, dx_acc, ws)
+  hipLaunchKernelGGL((rms_bwd_multi<BT, VPT>), dim3(nblk), dim3(BT), 0, s, r, rpb, P, rstd, dx_acc, ws)
   if (bt == 256) TT_RMSB(256, 1);
   else if (bt == 512) TT_RMSB(512, 1);
   else if (vpt == 1) TT_RMSB(1024, 1);

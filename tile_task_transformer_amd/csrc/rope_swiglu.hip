@@ -36,12 +36,17 @@ __global__ void rope_table_k(int64_t seq, int half, double base, float* __restri
 
 // one thread per (row, head, 4 consecutive pair indices); INV: the
 // transposed rotation
+struct RopeTiles {
+  float* x[4];
+};
+
 template <bool INV>
-__global__ __launch_bounds__(256) void rope_k(float* __restrict__ x, int64_t rows, int heads, int hd,
-                                              int64_t seq_len, int64_t pos_off, const float* __restrict__ table) {
+__global__ __launch_bounds__(256) void rope_k(RopeTiles X, int64_t rows, int heads, int hd, int64_t seq_len,
+                                              int64_t pos_off, const float* __restrict__ table) {
   const int half = hd >> 1, q4 = half >> 2;
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i >= rows * heads * q4) return;
+  float* __restrict__ x = X.x[blockIdx.y];
   const int j = 4 * (int)(i % q4);
   const int64_t rh = i / q4;
   const int64_t r = rh / heads;
@@ -137,27 +142,48 @@ extern "C" int tile_rope_table(void* stream, int64_t seq, int64_t hd, double bas
   return tt::launch_status("tile_rope_table");
 }
 
-extern "C" int tile_rope(void* stream, float* x, int64_t rows, int64_t heads, int64_t hd, int64_t seq_len,
-                         int64_t pos_off, const float* table, int64_t table_rows, int inverse) {
+namespace {
+
+int rope_launch(void* stream, int count, float* const* x, int64_t rows, int64_t heads, int64_t hd, int64_t seq_len,
+                int64_t pos_off, const float* table, int64_t table_rows, int inverse) {
   using tt::fail;
+  if (count < 1 || count > 4 || !x) return fail(TT_ERR_ARG, "tile_rope: 1..4 tiles");
   if (rows < 0 || heads < 1 || !hd_ok(hd) || seq_len < 1 || pos_off < 0)
     return fail(TT_ERR_ARG, "tile_rope: bad size (rows %lld, heads %lld, hd %lld, seq_len %lld, pos_off %lld)",
                 (long long)rows, (long long)heads, (long long)hd, (long long)seq_len, (long long)pos_off);
   if (rows == 0) return TT_OK;
-  if (!x || !table || !tt::aligned16(x) || !tt::aligned16(table))
-    return fail(TT_ERR_ARG, "tile_rope: x and table must be non-null and 16-byte aligned");
+  RopeTiles X{};
+  for (int t = 0; t < count; ++t) {
+    if (!x[t] || !tt::aligned16(x[t])) return fail(TT_ERR_ARG, "tile_rope: x must be non-null and 16-byte aligned");
+    X.x[t] = x[t];
+  }
+  if (!table || !tt::aligned16(table)) return fail(TT_ERR_ARG, "tile_rope: table must be non-null and 16-byte aligned");
   if (pos_off + std::min(rows, seq_len) > table_rows)
     return fail(TT_ERR_SHAPE, "tile_rope: positions up to %lld exceed the table's %lld rows",
                 (long long)(pos_off + std::min(rows, seq_len)), (long long)table_rows);
   if (rows * heads > INT64_MAX / hd) return fail(TT_ERR_ARG, "tile_rope: size overflows");
   const int64_t work = rows * heads * (hd / 8);
-  dim3 grid((unsigned)((work + 255) / 256)), block(256);
+  dim3 grid((unsigned)((work + 255) / 256), (unsigned)count), block(256);
   hipStream_t s = tt::as_stream(stream);
   if (inverse)
-    hipLaunchKernelGGL(rope_k<true>, grid, block, 0, s, x, rows, (int)heads, (int)hd, seq_len, pos_off, table);
+    hipLaunchKernelGGL(rope_k<true>, grid, block, 0, s, X, rows, (int)heads, (int)hd, seq_len, pos_off, table);
   else
-    hipLaunchKernelGGL(rope_k<false>, grid, block, 0, s, x, rows, (int)heads, (int)hd, seq_len, pos_off, table);
+    hipLaunchKernelGGL(rope_k<false>, grid, block, 0, s, X, rows, (int)heads, (int)hd, seq_len, pos_off, table);
   return tt::launch_status("tile_rope");
+}
+
+}  // namespace
+
+extern "C" int tile_rope(void* stream, float* x, int64_t rows, int64_t heads, int64_t hd, int64_t seq_len,
+                         int64_t pos_off, const float* table, int64_t table_rows, int inverse) {
+  if (!x) return tt::fail(TT_ERR_ARG, "tile_rope: null x");
+  return rope_launch(stream, 1, &x, rows, heads, hd, seq_len, pos_off, table, table_rows, inverse);
+}
+
+extern "C" int tile_rope_multi(void* stream, int count, float* const* x, int64_t rows, int64_t heads, int64_t hd,
+                               int64_t seq_len, int64_t pos_off, const float* table, int64_t table_rows,
+                               int inverse) {
+  return rope_launch(stream, count, x, rows, heads, hd, seq_len, pos_off, table, table_rows, inverse);
 }
 
 extern "C" int tile_swiglu_fwd(void* stream, int64_t n, const float* a, const float* b, float* h) {

@@ -1210,9 +1210,9 @@ int op_rope(tt_ctx* ctx, const TileArg* T, int n, const tt_op_rope& q, const cha
   const int64_t off = q.pos_off;
   const int inv = q.inverse;
   return ctx->submit(label ? label : "rope", std::move(acc), [=](hipStream_t s, void*) {
-    for (int i = 0; i < n - 1; ++i)
-      if (int rc = tile_rope(s, Fp(tl[i]), rows, heads, hd, len, off, Fp(tl[n - 1]), tr, inv)) return rc;
-    return TT_OK;
+    float* xs[4];
+    for (int i = 0; i < n - 1; ++i) xs[i] = Fp(tl[i]);
+    return tile_rope_multi(s, n - 1, xs, rows, heads, hd, len, off, Fp(tl[n - 1]), tr, inv);
   });
 }
 

@@ -26,7 +26,7 @@ __all__ = [
     "tile_reduce_rows_workspace", "tile_reduce_rows_multi", "tile_fill", "tile_fill_multi", "tile_split_tokens",
     "tt_probe_mfma_f32", "tile_layernorm_fwd_multi", "tile_layernorm_bwd_multi",
     "tile_layernorm_bwd_multi_workspace", "tile_rmsnorm_fwd", "tile_rmsnorm_bwd", "tile_rmsnorm_bwd_workspace",
-    "tile_rope_table", "tile_rope", "tile_swiglu_fwd", "tile_swiglu_bwd",
+    "tile_rope_table", "tile_rope", "tile_rope_multi", "tile_swiglu_fwd", "tile_swiglu_bwd",
     "TT_EPI_NONE", "TT_EPI_BIAS", "TT_EPI_RES", "TT_EPI_GELU", "TT_EPI_GELU_BWD", "TT_LN_PARTIAL",
     "TT_LN_MERGE", "TT_LN_APPLY", "TT_LN_FUSED", "TT_SM_STATS", "TT_SM_MERGE", "TT_SM_APPLY", "TT_XE_LOSS",
     "TT_XE_GRAD", "TT_XE_STATS", "TT_ATT_PREP", "TT_ATT_GRAD", "TT_EMB_TOKEN", "TT_EMB_POS",
@@ -348,6 +348,13 @@ def tile_rope(stream, x, rows, heads, hd, seq_len, pos_off, table, table_rows, i
     """Rotary embedding of a [rows, heads, hd] q or k tile, in place."""
     return check(lib.tile_rope(stream_handle(stream), ptr(x), rows, heads, hd, seq_len, pos_off, ptr(table),
                                table_rows, int(inverse)))
+
+
+def tile_rope_multi(stream, xs, rows, heads, hd, seq_len, pos_off, table, table_rows, inverse=False):
+    """tile_rope on 1..4 equal tiles in one launch."""
+    (x,) = _arrs(len(xs), xs)
+    return check(lib.tile_rope_multi(stream_handle(stream), len(xs), x, rows, heads, hd, seq_len, pos_off,
+                                     ptr(table), table_rows, int(inverse)))
 
 
 def tile_swiglu_fwd(stream, n, a, b, h):
