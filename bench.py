@@ -575,6 +575,11 @@ def main(argv=None):
                     help="executor streams (0 = measured best per workload: 1; small tiles 4; pinned 1)")
     ap.add_argument("--heavy-gflops", type=float, default=0.0,
                     help="tasks of at least this many GFLOP run in order on stream 0 (0 = off)")
+    ap.add_argument("--priorities", action="store_true",
+                    help="launch each window by critical-path priority instead of submission order")
+    ap.add_argument("--depth-sweep", default="",
+                    help="instead of the step: time the workload's widths at these block counts (e.g. 1,2,4,8,12) "
+                         "on 1 and 4 streams, 4 with critical-path priorities, and write gpurun_out/depth_sweep.json")
     ap.add_argument("--pinned", action="store_true",
                     help="parameters, gradients and moments live in pinned host RAM (out-of-core residency)")
     ap.add_argument("--budget-gb", type=float, default=0.0, help="device arena for pinned tiles (0 = half of free)")
@@ -615,6 +620,13 @@ def main(argv=None):
         for k, v in res.items():
             print(f"{k:14s} {v['us']:9.1f} us  {v['achieved']:8.1f} {v['unit']:16s} {100 * v['frac']:5.1f}%",
                   file=sys.stderr)
+        return 0
+    if a.depth_sweep:
+        res = depth_sweep(w, [int(x) for x in a.depth_sweep.split(",")])
+        os.makedirs("gpurun_out", exist_ok=True)
+        with open(os.path.join("gpurun_out", "depth_sweep.json"), "w") as f:
+            json.dump(res, f, indent=1)
+        print(json.dumps(res), flush=True)
         return 0
     probe = probes()
     print(f"[bench] probes: {probe}", file=sys.stderr, flush=True)
@@ -660,6 +672,8 @@ def run(w, a, streams, breakdown_path, probe, steps=None, warmup=None, want_para
     ctx = Context(0, n_streams=streams, window=4096, device_budget=int(a.budget_gb * 2 ** 30))
     if a.heavy_gflops > 0:
         ctx.heavy_lane(a.heavy_gflops * 1e9)
+    if a.priorities:
+        ctx.priorities(True)
     model = GPT2(ctx, s, t, param_home=home, family=family)
     model.set_params(params, specs)
     if not want_params or a.no_cpu_baseline:
@@ -747,6 +761,7 @@ def run(w, a, streams, breakdown_path, probe, steps=None, warmup=None, want_para
                    "n_embd": s.n_embd, "n_inner": s.n_inner, "n_head": s.n_head, "vocab": s.vocab,
                    "tiles": {"batch": t.batch, "seq": t.seq, "embd": t.embd, "inner": t.inner, "head": t.head,
                              "vocab": t.vocab}, "streams": streams, "heavy_gflops": a.heavy_gflops,
+                   "priorities": bool(a.priorities),
                    "param_home": "pinned_host" if a.pinned else "device"},
         "tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_FP32_PEAK, 4),
         "mfma_frac_of_probe": round(tflops / probe["mfma_f32_tflops"], 4) if probe else None,
@@ -778,6 +793,62 @@ def run(w, a, streams, breakdown_path, probe, steps=None, warmup=None, want_para
     del tok
     torch.cuda.empty_cache()
     return out, {"params": params, "tokens": tokens}
+
+
+def depth_sweep(w, layers, steps=6, warmup=2):
+    """Step time against depth: the workload's widths and tiles at each block
+    count in `layers`, run with (streams, priorities) = (1, off), (4, off),
+    (4, on); ms per step, ms per block (after the step at zero blocks is
+    subtracted, i.e. the embedding, head, loss and their updates), the GPU
+    idle fraction of one more step and the task graph's longest chain."""
+    import dataclasses
+
+    import torch
+
+    from tile_task_transformer_amd import _lib as L
+    from tile_task_transformer_amd.runtime import Context, GPT2
+    family = family_of(w.name)
+    hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
+    rows = []
+    for n_layer in sorted(set([0] + layers)):
+        s = dataclasses.replace(w.shape, n_layer=n_layer)
+        specs = specs_of(s, family)
+        params = synth.init_params(s, seed=0, threads=min(16, len(os.sched_getaffinity(0))), specs=specs)
+        tok = torch.from_numpy(synth.token_stream(s, seed=1).astype(np.int32)).cuda()
+        for streams, prio in ((1, False), (4, False), (4, True)):
+            ctx = Context(0, n_streams=streams, window=8192)
+            ctx.priorities(prio)
+            model = GPT2(ctx, s, w.tiles, family=family)
+            model.set_params(params, specs)
+            for _ in range(warmup):
+                model.step(tok, **hp)
+            ctx.wait()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                model.step(tok, **hp)
+            ctx.wait()
+            torch.cuda.synchronize()
+            ms = 1e3 * (time.perf_counter() - t0) / steps
+            ctx.profile("*", every=1)
+            model.step(tok, **hp)
+            busy = ctx.profile_busy()
+            ctx.profile_take()
+            ctx.profile(None)
+            rows.append({"n_layer": n_layer, "streams": streams, "priorities": prio, "ms_per_step": round(ms, 3),
+                         "tasks": model.task_count(),
+                         "gpu_idle_frac": round(1 - busy["busy_ms"] / busy["span_ms"], 4) if busy["span_ms"] else None})
+            print(f"[bench] depth {n_layer:2d} streams {streams} priorities {int(prio)}: {ms:8.3f} ms/step, "
+                  f"idle {rows[-1]['gpu_idle_frac']}", file=sys.stderr, flush=True)
+            model.close()
+            ctx.close()
+        del tok
+        torch.cuda.empty_cache()
+    base = {(r["streams"], r["priorities"]): r["ms_per_step"] for r in rows if r["n_layer"] == 0}
+    for r in rows:
+        if r["n_layer"]:
+            r["ms_per_block"] = round((r["ms_per_step"] - base[(r["streams"], r["priorities"])]) / r["n_layer"], 3)
+    return {"workload": w.name, "family": family, "steps": steps, "rows": rows}
 
 
 def executor_figures(w, model, ctx, tok, hp, streams, ms, st, steps, busy_steps=2):

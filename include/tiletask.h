@@ -660,6 +660,18 @@ int tt_ctx_streams_active(tt_ctx* ctx, int n);
  * nothing from sharing the GPU with another one; the light memory-bound
  * tasks still overlap with it. 0 = off (default). Results do not change. */
 int tt_ctx_heavy_lane(tt_ctx* ctx, double min_flops);
+/* Critical-path priorities (whole-iteration scheduling, which the
+ * pith.science review's "Reading between the lines" names as the lever):
+ * with on != 0, each window of submitted tasks is launched as a list
+ * schedule instead of in submission order: among the tasks whose
+ * dependencies have been launched, the one with the costliest chain of
+ * flops to the end of the window goes first (memory-bound tasks count as
+ * 1 MFLOP). The order stays topological and the kernels are the same, so
+ * results do not change; with several streams, the critical path reaches
+ * the GPU first. Contexts with pinned-host tensors keep submission order
+ * (their staging plan follows it). Off by default. Dry-run DAG dumps list
+ * tasks in launch order. */
+int tt_ctx_priorities(tt_ctx* ctx, int on);
 /* Keep (on != 0) or drop the per-task records tt_dump_dag writes; dry-run
  * contexts record by default, device contexts do not. */
 int tt_ctx_record(tt_ctx* ctx, int on);

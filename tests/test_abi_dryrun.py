@@ -285,3 +285,49 @@ def test_out_of_core_wide_model_step_dag(tmp_path):
     assert by["ln_fwd"] == 2 * 8 + 1 and by["ln_bwd"] == 2 * 8 + 1
     assert by["head_dx"] == 8 and by["emb_dw"] == 8 * 25  # pinned table: one task per vocab tile
 
+
+
+def test_priorities_launch_the_critical_path_first(tmp_path):
+    """With critical-path priorities a window is launched as a list
+    schedule: a light task that nothing waits for goes after the heavy chain
+    that was submitted behind it; the order stays topological."""
+    orders = {}
+    for on in (False, True):
+        with Context(L.TT_DEVICE_DRYRUN, n_streams=2) as ctx:
+            ctx.priorities(on)
+            x = ctx.tensor((64, 64), (64, 64))
+            y = ctx.tensor((256, 256), (256, 256))
+            w = ctx.tensor((256, 256), (256, 256))
+            z = ctx.tensor((256, 256), (256, 256))
+            ctx.submit_fill(x, (0, 0), 1.0)                                    # 0: light, no successor
+            ctx.submit_fill(y, (0, 0), 1.0)                                    # 1: light, feeds the GEMM
+            ctx.submit_gemm(0, 0, 1.0, y, (0, 0), w, (0, 0), 0.0, z, (0, 0))  # 2: heavy, after 1
+            dag = ctx.dump_dag(str(tmp_path / f"p{int(on)}.jsonl"))
+        orders[on] = [r["id"] for r in dag]
+    assert orders[False] == [0, 1, 2]
+    assert orders[True] == [1, 2, 0]
+
+
+@pytest.mark.parametrize("tiles", [synth.Tiles(1, 8, 16, 24, 1, 40), synth.Tiles(2, 16, 32, 48, 2, 40)])
+def test_priority_order_of_a_gpt2_step_is_a_race_free_topological_order(tiles, tmp_path):
+    shape = synth.GPT2Shape(2, 100, 64, 4, 96, 32, 2)
+    dags = {}
+    for on in (False, True):
+        with Context(L.TT_DEVICE_DRYRUN, n_streams=4, window=100000) as ctx:
+            ctx.priorities(on)
+            model = GPT2(ctx, shape, tiles)
+            model.step(None)
+            dags[on] = ctx.dump_dag(str(tmp_path / f"s{int(on)}.jsonl"))
+            model.close()
+    base, prio = dags[False], dags[True]
+    assert sorted(r["id"] for r in prio) == [r["id"] for r in base]
+    assert [r["id"] for r in prio] != [r["id"] for r in base]   # the order did change
+    seen = set()
+    for r in prio:
+        assert all(d in seen for d in r["deps"]), r["label"]
+        seen.add(r["id"])
+    # same tasks, same edges, same streams
+    by_id = {r["id"]: r for r in base}
+    for r in prio:
+        assert r["deps"] == by_id[r["id"]]["deps"] and r["stream"] == by_id[r["id"]]["stream"]
+    _check_races(prio)

@@ -126,6 +126,33 @@ def test_tile_shapes_agree_and_steps_are_deterministic():
         assert np.array_equal(a["grads"][name], c["grads"][name]), name
 
 
+def test_priority_launch_order_gives_the_same_bits():
+    """Critical-path priorities reorder launches across 4 streams; every
+    result is bitwise the submission-order run's."""
+    shape = synth.GPT2Shape(2, 256, 64, 4, 256, 32, 2)
+    params = synth.init_params(shape, seed=5)
+    tokens = synth.token_stream(shape, seed=6)
+    tiles = synth.Tiles(1, 8, 16, 64, 1, 48)
+    specs = synth.param_specs(shape)
+    outs = []
+    for prio in (False, True):
+        with Context(0, n_streams=4) as ctx:
+            ctx.priorities(prio)
+            model = GPT2(ctx, shape, tiles)
+            model.set_params(params, specs)
+            tok = torch.from_numpy(tokens.astype(np.int32)).cuda()
+            losses = []
+            for _ in range(2):
+                model.step(tok)
+                losses.append(model.loss())
+            outs.append((losses, model.get(specs, 0), model.get(specs, 1)))
+            model.close()
+    assert outs[0][0] == outs[1][0]
+    for name in outs[0][1]:
+        assert np.array_equal(outs[0][1][name], outs[1][1][name]), name
+        assert np.array_equal(outs[0][2][name], outs[1][2][name]), name
+
+
 def test_gpt2_small_full_size_step_matches_oracle():
     """The GPT2-small workload at its full size and README tiles, checked
     against the full fp64 oracle step."""

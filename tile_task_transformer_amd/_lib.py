@@ -209,6 +209,7 @@ SIGNATURES = {
     "tt_ctx_record": (I, [P, I]),
     "tt_ctx_streams_active": (I, [P, I]),
     "tt_ctx_heavy_lane": (I, [P, C.c_double]),
+    "tt_ctx_priorities": (I, [P, I]),
     "tt_tensor_create": (I, [P, I, C.POINTER(I64), C.POINTER(I64), I, I, PP]),
     "tt_tensor_wrap": (I, [P, I, C.POINTER(I64), C.POINTER(I64), I, P, PP]),
     "tt_tensor_destroy": (I, [P]),

@@ -2,6 +2,7 @@
 #include "runtime.hpp"
 
 #include <algorithm>
+#include <queue>
 #include <cstdlib>
 #include <cstring>
 #include <fstream>
@@ -265,10 +266,14 @@ int tt_ctx::flush() {
     for (int64_t d : task.deps)
       if (d >= window_base && pending[d - window_base].stream != task.stream)
         pending[d - window_base].need_event = true;
-  // 3. launch in submission order
+  // 3. launch in submission order, or (priorities) in a list-schedule order
   if (launched.empty()) launched_base = window_base;
   if (!dryrun && has_pinned) plan_window();
-  for (size_t ti = 0; ti < pending.size(); ++ti) {
+  const std::vector<size_t> order = launch_order();
+  const size_t lbase = launched.size();  // launched[lbase + ti] = pending[ti] (ids are consecutive)
+  launched.resize(lbase + pending.size());
+  for (size_t oi = 0; oi < order.size(); ++oi) {
+    const size_t ti = order[oi];
     tt::Task& task = pending[ti];
     const int s = task.stream;
     cur_task = task.id;
@@ -335,7 +340,7 @@ int tt_ctx::flush() {
         li.event = ev;
       }
     }
-    launched.push_back(li);
+    launched[lbase + ti] = li;
     if (!dryrun && !latched && arena) {
       int rc = clean_ahead(ti);
       if (rc == TT_OK) rc = prefetch(ti);
@@ -349,6 +354,50 @@ int tt_ctx::flush() {
   unplan_window();
   if (latched) return fail(latched, "%s", latched_msg.c_str());
   return TT_OK;
+}
+
+// Launch order of the pending window. Without priorities (or with
+// pinned-host tiles, whose staging plan follows submission order): the
+// submission order. With priorities: a list schedule over the window's
+// graph -- of the tasks whose dependencies in the window have all been
+// launched, the one with the largest bottom level goes next (its cost plus
+// the costliest chain of successors to the end of the window; memory-bound
+// tasks count as 1 MFLOP, about a microsecond of launch and run time), ties
+// by submission order. Every task follows its dependencies, so the order is
+// topological; results do not change (the kernels and their per-tile order
+// are the same), only which independent task reaches its stream first.
+std::vector<size_t> tt_ctx::launch_order() {
+  const size_t n = pending.size();
+  std::vector<size_t> order(n);
+  for (size_t i = 0; i < n; ++i) order[i] = i;
+  if (!priorities || has_pinned || n < 2) return order;
+  std::vector<std::vector<size_t>> succ(n);
+  std::vector<int> indeg(n, 0);
+  for (size_t i = 0; i < n; ++i)
+    for (int64_t d : pending[i].deps)
+      if (d >= window_base) {
+        succ[(size_t)(d - window_base)].push_back(i);
+        indeg[i]++;
+      }
+  std::vector<double> bl(n, 0.0);
+  for (size_t k = n; k-- > 0;) {
+    double m = 0.0;
+    for (size_t j : succ[k]) m = std::max(m, bl[j]);
+    bl[k] = std::max(pending[k].cost, 1e6) + m;
+  }
+  auto lower = [&](size_t a, size_t b) { return bl[a] < bl[b] || (bl[a] == bl[b] && a > b); };
+  std::priority_queue<size_t, std::vector<size_t>, decltype(lower)> ready(lower);
+  for (size_t i = 0; i < n; ++i)
+    if (!indeg[i]) ready.push(i);
+  size_t k = 0;
+  while (!ready.empty()) {
+    const size_t i = ready.top();
+    ready.pop();
+    order[k++] = i;
+    for (size_t j : succ[i])
+      if (--indeg[j] == 0) ready.push(j);
+  }
+  return order;
 }
 
 // ---------------------------------------------------------------- residency
@@ -931,6 +980,13 @@ int tt_ctx_heavy_lane(tt_ctx* c, double min_flops) {
   if (!c || !(min_flops >= 0)) return fail(TT_ERR_ARG, "tt_ctx_heavy_lane: bad argument");
   if (int rc = c->flush()) return rc;
   c->heavy_flops = min_flops;
+  return TT_OK;
+}
+
+int tt_ctx_priorities(tt_ctx* c, int on) {
+  if (!c) return fail(TT_ERR_ARG, "tt_ctx_priorities: null");
+  if (int rc = c->flush()) return rc;
+  c->priorities = on != 0;
   return TT_OK;
 }
 

@@ -130,6 +130,7 @@ struct tt_ctx {
   int n_streams = 1;
   int active_streams = 1;  // tasks go to streams 0..active_streams-1
   double heavy_flops = 0;  // > 0: tasks of at least this cost run in order on stream 0
+  bool priorities = false;  // launch each window by critical-path priority (device homes only)
   int window = 512;
   size_t budget = 0;
   bool record = false;
@@ -230,6 +231,7 @@ struct tt_ctx {
   // ---- internal API
   int submit(const char* label, std::vector<tt::Access> acc, tt::LaunchFn run, double cost = 0.0);
   int flush();
+  std::vector<size_t> launch_order();  // positions in `pending`, in the order they are launched
   int wait_all();
   void forget_launched();  // bookkeeping after a drain: nothing submitted so far is pending
 

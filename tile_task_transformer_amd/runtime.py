@@ -51,6 +51,10 @@ class Context:
         other streams (0 = off)."""
         check(lib.tt_ctx_heavy_lane(self.h, float(min_flops)))
 
+    def priorities(self, on: bool = True):
+        """Launch each window by critical-path priority (device homes only)."""
+        check(lib.tt_ctx_priorities(self.h, int(on)))
+
     def record(self, on: bool = True):
         check(lib.tt_ctx_record(self.h, int(on)))
 
