@@ -735,8 +735,10 @@ static_assert(sizeof(KsumArgs) <= 4096, "kernel arguments over 4 KB");
 // [z * chunk, (z + 1) * chunk) of the concatenated pair list into its own
 // m x n region of P.ws (no epilogue); gemm_split_finish adds the slices in
 // slice order and applies alpha, beta and the epilogue.
+// 256 x 256 blocks (each wave 128 x 128, 256 accumulators per lane) run one
+// workgroup per CU and may use every register of a SIMD
 template <int BM, int BN, int BK, bool TB, bool SPLIT>
-__global__ __launch_bounds__(256, 2) void gemm_ksum_kernel(KsumArgs P) {
+__global__ __launch_bounds__(256, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_ksum_kernel(KsumArgs P) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int A_LD = BK + 4, B_LD = TB ? BK + 4 : BN + 8;  // A K-contiguous; B either way
@@ -949,6 +951,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 // (three): 85.3 against 82.6 % of the fp32 peak for 16 products 8192 x 2048
 // x 4096 with A stored [k][m], 85.1 against 81.2 % for 25 products 4096 x
 // 2048 x 2048 with B stored [n][k]
+// (256 x 128 x 16 blocks, which speed up the long-K sums, do not fit the
+// batch kernel's loop in 256 VGPRs and spill inside it; with one workgroup
+// per CU they measured 77 against 85 % on the wide model's weight gradients)
 enum BatchPlan { kBatchBig, kBatchSmall, kBatchSplit };
 
 template <bool TA, bool TB>
@@ -1049,6 +1054,36 @@ namespace {
 // 83.5 against 82.5 % for four K = 2048 pairs, 87.5 against 86.1 % for four
 // K = 8192 pairs with B stored [n][k]), else 64x64x32. TT_KSUM_BK=16|32
 // overrides the big blocks' BK (tuning).
+// 256 x 128 x 16 blocks (each wave 128 x 64: 8 MFMA tiles against 4, so
+// a quarter fewer LDS reads and global loads per flop; 250-256 VGPRs, two
+// workgroups per CU) for long-K sums of >= 1024 blocks of 128 x 128, i.e.
+// >= 512 of the larger ones: the wide model's MLP input layer (4096 x 8192,
+// K 4 x 2048) 82.8 -> 86.3 % of the fp32 peak, its output layer's input
+// gradient 83.5 -> 84.5 %. Measured alternatives on the same sums: 128 x 256
+// x 16 85.1 / 84.6 %; BK 32 (332-368 VGPRs, one workgroup per CU) 78 / 76 %;
+// 256 x 256 (256 accumulators per lane) spills them to scratch: 32 %.
+// TT_KSUM_HUGE = "BMxBNxBK" (256x128, 128x256 or 256x256 with BK 16 or 32)
+// or "off" overrides (tuning).
+struct HugePlan {
+  int bm = 0, bn = 0, bk = 0;
+};
+HugePlan ksum_huge() {
+  static HugePlan p{256, 128, 16};
+  static bool read = false;
+  if (!read) {
+    read = true;
+    if (const char* e = getenv("TT_KSUM_HUGE")) {
+      int a = 0, b = 0, c = 0;
+      if (sscanf(e, "%dx%dx%d", &a, &b, &c) == 3 && (c == 16 || c == 32) &&
+          ((a == 256 && (b == 128 || b == 256)) || (a == 128 && b == 256)))
+        p = HugePlan{a, b, c};
+      else
+        p = HugePlan{};
+    }
+  }
+  return p;
+}
+
 int ksum_big_bk(int64_t) {
   static int forced = -1;
   if (forced < 0) {
@@ -1128,11 +1163,14 @@ extern "C" int tile_gemm_ksum_ws(void* stream, int count, int transB, int64_t m,
   // 128x128x32 blocks for fewer than 256 with a workspace; else 64x64x32
   const int64_t b128 = (m / 128) * (n / 128);
   const bool big = b128 >= 512;
+  const HugePlan hp = ksum_huge();
+  const bool huge = b128 >= 1024 && hp.bm > 0 && m % hp.bm == 0 && n % hp.bn == 0;
   int64_t total_steps = 0;
   for (int t = 0; t < count; ++t) total_steps += k[t] / 32;
   const bool try_split = !big && workspace && ksum_split_shape(m, n) &&
                          ksum_splits(m, n, total_steps, workspace_bytes) > 1;
-  const int bm = big || try_split ? 128 : 64, bn = bm, bk = big ? ksum_big_bk(b128) : 32;
+  const int bm = huge ? hp.bm : (big || try_split ? 128 : 64), bn = huge ? hp.bn : bm;
+  const int bk = huge ? hp.bk : (big ? ksum_big_bk(b128) : 32);
   auto fits = [&](int t) {  // a pair the branch-free long-K launch can take
     return k[t] % bk == 0 && m % bm == 0 && n % bn == 0 && aligned16(A[t]) && aligned16(B[t]) && lda[t] % 4 == 0 &&
            ldb[t] % 4 == 0 && (int64_t)bm * lda[t] < INT32_MAX && (int64_t)(transB ? bn : bk) * ldb[t] < INT32_MAX;
@@ -1207,7 +1245,20 @@ extern "C" int tile_gemm_ksum_ws(void* stream, int count, int transB, int64_t m,
       if (int rc = tt::launch_status("tile_gemm_ksum(split finish)")) return rc;
     } else {
       const dim3 grid((unsigned)((m / bm) * (n / bn)));
-      if (transB) {
+      if (huge) {
+#define TT_KH(BM_, BN_, BK_)                                                                              \
+  if (bm == BM_ && bn == BN_ && bk == BK_) {                                                              \
+    if (transB) hipLaunchKernelGGL((gemm_ksum_kernel<BM_, BN_, BK_, true, false>), grid, dim3(256), 0, s, P); \
+    else hipLaunchKernelGGL((gemm_ksum_kernel<BM_, BN_, BK_, false, false>), grid, dim3(256), 0, s, P);       \
+  }
+        TT_KH(256, 128, 16)
+        TT_KH(256, 128, 32)
+        TT_KH(128, 256, 16)
+        TT_KH(128, 256, 32)
+        TT_KH(256, 256, 16)
+        TT_KH(256, 256, 32)
+#undef TT_KH
+      } else if (transB) {
         if (big && bk == 32) hipLaunchKernelGGL((gemm_ksum_kernel<128, 128, 32, true, false>), grid, dim3(256), 0, s, P);
         else if (big) hipLaunchKernelGGL((gemm_ksum_kernel<128, 128, 16, true, false>), grid, dim3(256), 0, s, P);
         else if (bm == 128) hipLaunchKernelGGL((gemm_ksum_kernel<128, 128, 32, true, false>), grid, dim3(256), 0, s, P);
