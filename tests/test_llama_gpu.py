@@ -244,6 +244,24 @@ def test_llama_streams_and_pinned_homes_are_bitwise_equal():
                 assert np.array_equal(other[key][name], a[key][name]), (key, name)
 
 
+def test_llama_two_minibatches_make_the_batch_step():
+    """Gradient accumulation for the LLaMA-style step: 2 minibatches of 2
+    windows, then one update, against the oracle's step on all 4 windows."""
+    shape = LT.shape
+    big = synth.GPT2Shape(shape.n_layer, shape.vocab, shape.n_embd, shape.n_head, shape.n_inner, shape.seq,
+                          2 * shape.batch)
+    specs = synth.llama_param_specs(shape)
+    params = synth.init_params(shape, seed=0, specs=specs)
+    tokens = synth.token_stream(big, seed=1)
+    with Context(0, n_streams=4) as ctx:
+        model = GPT2(ctx, shape, synth.Tiles(1, 16, 32, 64, 2, 48), family="llama")
+        model.set_params(params, specs)
+        model.step(torch.from_numpy(tokens.astype(np.int32)).cuda(), n_micro=2)
+        gpu = dict(loss=[model.loss()], grads=model.get(specs, 1), params=model.get(specs, 0))
+        model.close()
+    check_llama_against_oracle(big, gpu, params, tokens, LT)
+
+
 def test_llama_small_full_size_step_matches_oracle():
     """The LLaMA-style model at GPT2-small's width and depth (12 blocks, d
     768, SwiGLU width 2048, vocab 32000, 4 x 1024 tokens, its benchmark
