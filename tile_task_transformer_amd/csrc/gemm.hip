@@ -1191,7 +1191,14 @@ extern "C" int tile_gemm_ksum_ws(void* stream, int count, int transB, int64_t m,
   const int64_t b128 = (m / 128) * (n / 128);
   const bool big = b128 >= 512;
   const HugePlan hp = ksum_huge();
-  const bool huge = b128 >= 1024 && hp.bm > 0 && m % hp.bm == 0 && n % hp.bn == 0;
+  // both plans run two workgroups per CU (512 slots): the larger blocks
+  // only where their last round is as full as the smaller ones' (a 4096 x
+  // 5632 output -- the LLaMA-style wide model's ragged SwiGLU tile -- is
+  // 1408 blocks of 128 x 128, 92 % of 3 rounds, but 704 of 256 x 128, 69 %
+  // of 2: 85 -> 79 % of the fp32 peak), allowing their ~4 % per block
+  auto round_fill = [](int64_t blocks) { return (double)blocks / (double)(((blocks + 511) / 512) * 512); };
+  const bool huge = b128 >= 1024 && hp.bm > 0 && m % hp.bm == 0 && n % hp.bn == 0 &&
+                    1.04 * round_fill((m / hp.bm) * (n / hp.bn)) >= round_fill(b128);
   int64_t total_steps = 0;
   for (int t = 0; t < count; ++t) total_steps += k[t] / 32;
   const bool try_split = !big && workspace && ksum_split_shape(m, n) &&
