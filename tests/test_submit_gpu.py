@@ -34,3 +34,33 @@ def test_user_built_step_matches_oracle(shape, tiles, fused):
         gpu = dict(loss=[m.loss_value()], grads=m.get(m.G), params=m.get(m.P))
         del tok
     check_against_oracle(shape, gpu, params, tokens, w)
+
+
+def test_launch_error_is_latched():
+    """A task whose launch fails (a rotary embedding of head dim 8, which no
+    kernel covers: the submit-time checks pass, the launch refuses it) stops
+    the window: wait reports that error, later submits and copies report the
+    latched state, and destroying the context reports it once more and frees
+    it."""
+    from tile_task_transformer_amd import _lib as L
+    ctx = Context(0, n_streams=2, window=64)
+    a = ctx.tensor([4, 8], [4, 8])
+    b = ctx.tensor([4, 8], [4, 8])
+    x = ctx.tensor([1, 3, 2, 8], [1, 3, 2, 8])
+    table = ctx.tensor([3, 8], [3, 8])
+    for t in (a, b, x, table):
+        t.copy_in(np.zeros(t.shape, np.float32))
+    ctx.submit_fill(a, (0, 0), 1.0)
+    ctx.submit(L.TT_OP_ROPE, [(x, (0, 0, 0, 0)), (table, (0, 0))], L.tt_op_rope(0, 0, 10000.0))
+    ctx.submit_fill(b, (0, 0), 2.0)
+    with pytest.raises(L.TTError) as e:
+        ctx.wait()
+    assert e.value.code == L.TT_ERR_ARG and "tile_rope" in str(e.value)
+    with pytest.raises(L.TTError) as e:
+        ctx.submit_fill(b, (0, 0), 3.0)
+    assert e.value.code == L.TT_ERR_STATE
+    with pytest.raises(L.TTError):
+        a.copy_out()
+    with pytest.raises(L.TTError) as e:
+        ctx.close()
+    assert e.value.code == L.TT_ERR_ARG and ctx.h is None

@@ -131,7 +131,10 @@ int tensor_create(tt_ctx* ctx, int ndim, const int64_t* shape, const int64_t* ts
 
 tt::Launched* tt_ctx::info(int64_t id) {
   if (id < launched_base || id - launched_base >= (int64_t)launched.size()) return nullptr;
-  return &launched[id - launched_base];
+  tt::Launched* li = &launched[id - launched_base];
+  // a window's entries are made before its launches; one whose launch
+  // stopped on an error leaves entries with no stream
+  return li->stream >= 0 ? li : nullptr;
 }
 
 int tt_ctx::acquire_event(int* idx) {
@@ -228,7 +231,23 @@ int tt_ctx::submit(const char* label, std::vector<tt::Access> acc, tt::LaunchFn 
   return rc;
 }
 
+// flush_window, with an error that stops a window part way latched (later
+// submits and waits report it) and the window dropped, so that none of its
+// tasks is launched twice
 int tt_ctx::flush() {
+  const int rc = flush_window();
+  if (rc != TT_OK && !latched) {
+    latched = rc;
+    latched_msg = std::string("launch: ") + tt_last_error();
+  }
+  if (rc != TT_OK && !pending.empty()) {
+    pending.clear();
+    unplan_window();
+  }
+  return rc;
+}
+
+int tt_ctx::flush_window() {
   if (pending.empty()) return latched;
   // 1. stream assignment: continue the chain of a dependency that is still the
   //    tail of its stream, else spread independent work round-robin. With a

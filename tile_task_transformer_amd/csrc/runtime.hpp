@@ -231,6 +231,7 @@ struct tt_ctx {
   // ---- internal API
   int submit(const char* label, std::vector<tt::Access> acc, tt::LaunchFn run, double cost = 0.0);
   int flush();
+  int flush_window();  // flush's body: assign streams, add events, launch the pending window
   std::vector<size_t> launch_order();  // positions in `pending`, in the order they are launched
   int wait_all();
   void forget_launched();  // bookkeeping after a drain: nothing submitted so far is pending

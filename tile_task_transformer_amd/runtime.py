@@ -28,8 +28,9 @@ class Context:
         if self.h:
             for t in self._tensors:
                 t.h = None  # destroyed with the context
-            check(lib.tt_ctx_destroy(self.h))
-            self.h = None
+            # the context is freed even when destroy reports a latched error
+            h, self.h = self.h, None
+            check(lib.tt_ctx_destroy(h))
 
     def __enter__(self):
         return self
@@ -287,5 +288,5 @@ class GPT2:
 
     def close(self):
         if self.h:
-            check(lib.tt_gpt2_destroy(self.h))
-            self.h = None
+            h, self.h = self.h, None
+            check(lib.tt_gpt2_destroy(h))
