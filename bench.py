@@ -60,11 +60,11 @@ HBM_PEAK = 8000.0       # GB/s
 # the counters were taken on (sha256 prefix of the file); else null.
 TRAFFIC = {
     # profiles/gemm_ksum_fc_wide4_traffic.md
-    ("wide4", "fc"): {"source": "tile_task_transformer_amd/csrc/gemm.hip", "sha256": "81d1f38872d6226e",
-                      "fetch_kib": 787760.6, "fetch_factor": 2.0, "write_kib": 262144.0, "write_factor": 1.0},
+    ("wide4", "fc"): {"source": "tile_task_transformer_amd/csrc/gemm.hip", "sha256": "832d171deb162b75",
+                      "fetch_kib": 787708.3, "fetch_factor": 2.0, "write_kib": 262144.0, "write_factor": 1.0},
     # profiles/gemm_batch_head_gpt2_small_traffic.md
-    ("gpt2_small", "head"): {"source": "tile_task_transformer_amd/csrc/gemm.hip", "sha256": "81d1f38872d6226e",
-                             "fetch_kib": 982065.4, "fetch_factor": 2.0, "write_kib": 842558.0, "write_factor": 1.0},
+    ("gpt2_small", "head"): {"source": "tile_task_transformer_amd/csrc/gemm.hip", "sha256": "832d171deb162b75",
+                             "fetch_kib": 983961.5, "fetch_factor": 2.0, "write_kib": 842545.2, "write_factor": 1.0},
 }
 
 
@@ -601,6 +601,9 @@ def main(argv=None):
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
         return 2
+    if a.steps < 1 or a.warmup < 0:
+        print("bench.py: --steps must be at least 1 and --warmup at least 0", file=sys.stderr)
+        return 2
 
     w = ALL_WORKLOADS[a.workload]
     if a.streams <= 0:
@@ -733,12 +736,23 @@ def run(w, a, streams, breakdown_path, probe, steps=None, warmup=None, want_para
     ctx.reset_stats()
     torch.cuda.synchronize()
     ctx.wait()
+    # per-step boundaries: after each step the torch stream waits for every
+    # context stream (the step has flushed already, so this adds one event
+    # record and wait per stream) and records an event, so consecutive events
+    # bracket one step's completion on the GPU
+    cur = torch.cuda.current_stream()
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    for _ in range(steps):
+    ctx.join_stream(cur)
+    bounds[0].record(cur)
+    for i in range(steps):
         model.step(tok, **hp)
+        ctx.join_stream(cur)
+        bounds[i + 1].record(cur)
     ctx.wait()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    step_ms = sorted(bounds[i].elapsed_time(bounds[i + 1]) for i in range(steps))
     loss = model.loss()
     st = ctx.stats()
     prof = ctx.profile_take().get(dominant, {})
@@ -755,7 +769,10 @@ def run(w, a, streams, breakdown_path, probe, steps=None, warmup=None, want_para
     largest = max(classes, key=lambda k: classes[k]["ms"]) if classes else None
     out = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
-        "warmup": warmup, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
+        "warmup": warmup, "ms_per_step": round(ms, 3),
+        "ms_per_step_median": round(step_ms[len(step_ms) // 2] if steps % 2 else
+                                    0.5 * (step_ms[steps // 2 - 1] + step_ms[steps // 2]), 3),
+        "ms_per_step_min": round(step_ms[0], 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "family": family, "global_batch": s.batch, "seq_len": s.seq, "n_layer": s.n_layer,
                    "n_embd": s.n_embd, "n_inner": s.n_inner, "n_head": s.n_head, "vocab": s.vocab,

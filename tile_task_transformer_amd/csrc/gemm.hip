@@ -600,18 +600,44 @@ bool plan_override(Plan* p, int64_t k) {
   return true;
 }
 
+// Whether b128 (>= 512) blocks of 128x128 keep that tile rather than 64x64.
+// A launch lasts as long as its busiest CU, and with b128 blocks over kCUs
+// CUs the last round is partly idle; 64x64 blocks (four times as many) fill
+// their rounds nearly evenly but reuse each loaded element half as often.
+// Measured on MI355X (tile_gemm, A [m][k], B [k][n]): at full rounds 64x64
+// reaches 0.97-0.99 of 128x128's rate for K = 768 and 0.88 for K = 2048 to
+// 8192 (a short K leaves the larger tile's per-block costs less amortised),
+// so 128x128 stays while its rounds are at least that full: 4096 x 2304 x 768
+// (576 blocks, rounds 75 % full) runs at 99 TFLOP/s on 64x64 against 79,
+// 8192 x 2304 x 768 (1152, 90 %) at 113 against 105, 4096 x 2304 x 3072 at
+// 112 against 91-97, while 4096 x 2048 x 8192 (512, full) keeps 124-127 on
+// 128x128 against 112.
+bool rounds_favour_128(int64_t b128, int64_t k) {
+  const int64_t rounds = (b128 + kCUs - 1) / kCUs;
+  const double fill = (double)b128 / (double)(rounds * kCUs);
+  return fill >= (k <= 1024 ? 0.97 : 0.88);
+}
+
 // Block shape and split count: fill at least ~2 workgroups per CU.
 Plan plan_for(int64_t m, int64_t n, int64_t k, size_t ws_bytes) {
   const int64_t want = 512;
   auto blocks = [&](int bm, int bn) { return ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
   // Choices measured per tile-op class on MI355X (isolated launches): 128x128
-  // with BK 16 when it gives >= 2 blocks per CU; split-K only when C is small
-  // (<= 144 such blocks) and K long; otherwise 64x64 blocks, whose larger
-  // block count beats the bigger tile's reuse at these sizes.
+  // with BK 16 when it gives >= 2 blocks per CU and the blocks split evenly
+  // over the CUs; split-K only when C is small (<= 144 such blocks) and K
+  // long; otherwise 64x64 blocks, whose larger block count beats the bigger
+  // tile's reuse at these sizes.
   Plan p{128, 128, 16, 1, (int)k};
-  if (plan_override(&p, k)) return p;
-  if (blocks(128, 128) >= want) return p;
+  if (plan_override(&p, k)) {
+    // an override never splits without the workspace the split needs
+    if (p.splits > 1 && (size_t)p.splits * m * n * sizeof(float) > ws_bytes) {
+      p.splits = 1;
+      p.kchunk = (int)k;
+    }
+    return p;
+  }
   const int64_t b128 = blocks(128, 128);
+  if (b128 >= want) return rounds_favour_128(b128, k) ? p : Plan{64, 64, 32, 1, (int)k};
   if (k >= 2048 && b128 <= 144 && ws_bytes > 0) {
     // split count by CU balance: workgroups run in rounds of one per CU, so
     // b128*s just under a multiple of 256 keeps every CU equally loaded
@@ -1362,7 +1388,11 @@ int batch_run(void* stream, int count, int transA, int transB, const int64_t* m,
   hipStream_t s = tt::as_stream(stream);
   // the plan tile_gemm would pick if the products were one C: split-K over
   // 128x128x32 blocks for few blocks and a long K (with a workspace),
-  // 128x128x32 blocks when there are >= 512 of them, else 64x64x32
+  // 128x128x32 blocks when there are >= 512 of them, else 64x64x32. Unlike
+  // tile_gemm's single products, a batch keeps 128x128 whatever the fill of
+  // its last round: the small-tile wide model's LM head (99 products of
+  // 1024 x 512 x 512, rounds 95 % full) ran at 45 % of the fp32 peak on
+  // 64x64 blocks against 56 % on 128x128
   int64_t b128 = 0;
   for (int t = 0; t < count; ++t)
     if (m[t] > 0 && n[t] > 0) b128 += ((m[t] + 127) / 128) * ((n[t] + 127) / 128);
