@@ -342,7 +342,8 @@ size_t tile_rmsnorm_bwd_workspace(int64_t rows, int64_t total_cols);
  * x length of the tile, row-major, 16-byte aligned); row r has position
  * pos_off + r % seq_len, which must lie below table_rows. inverse != 0
  * applies the transposed rotation (the backward). hd in {16, 32, 64, 128}.
- * TT_ERR_ARG / TT_ERR_SHAPE for bad arguments. */
+ * TT_ERR_ARG / TT_ERR_SHAPE for bad arguments, TT_ERR_ARG also for more
+ * work than one launch covers (2^31 workgroups of 256 threads). */
 int tile_rope_table(void* stream, int64_t seq, int64_t hd, double base, float* table);
 int tile_rope(void* stream, float* x, int64_t rows, int64_t heads, int64_t hd, int64_t seq_len,
               int64_t pos_off, const float* table, int64_t table_rows, int inverse);
@@ -353,7 +354,8 @@ int tile_rope_multi(void* stream, int count, float* const* x, int64_t rows, int6
 /* tile_swiglu_fwd / tile_swiglu_bwd -- the LLaMA MLP's gate over n
  * contiguous DEVICE floats: h = silu(a) * b, silu(a) = a / (1 + exp(-a));
  * backward da = dh * b * silu'(a), db = dh * silu(a). da and db may be a
- * and b themselves (in place). TT_ERR_ARG for n < 0 or null pointers. */
+ * and b themselves (in place). TT_ERR_ARG for n < 0, null pointers or more
+ * elements than one launch covers (2^31 workgroups of 1024). */
 int tile_swiglu_fwd(void* stream, int64_t n, const float* a, const float* b, float* h);
 int tile_swiglu_bwd(void* stream, int64_t n, const float* dh, const float* a, const float* b, float* da,
                     float* db);

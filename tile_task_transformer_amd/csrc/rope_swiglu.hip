@@ -137,6 +137,7 @@ extern "C" int tile_rope_table(void* stream, int64_t seq, int64_t hd, double bas
   if (seq == 0) return TT_OK;
   if (!table) return fail(TT_ERR_ARG, "tile_rope_table: null table");
   const int64_t work = seq * (hd / 2);
+  if ((work + 255) / 256 > INT32_MAX) return fail(TT_ERR_ARG, "tile_rope_table: %lld positions exceed one launch", (long long)seq);
   hipLaunchKernelGGL(rope_table_k, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, tt::as_stream(stream), seq,
                      (int)(hd / 2), base, table);
   return tt::launch_status("tile_rope_table");
@@ -163,6 +164,7 @@ int rope_launch(void* stream, int count, float* const* x, int64_t rows, int64_t 
                 (long long)(pos_off + std::min(rows, seq_len)), (long long)table_rows);
   if (rows * heads > INT64_MAX / hd) return fail(TT_ERR_ARG, "tile_rope: size overflows");
   const int64_t work = rows * heads * (hd / 8);
+  if ((work + 255) / 256 > INT32_MAX) return fail(TT_ERR_ARG, "tile_rope: %lld pairs exceed one launch", (long long)work);
   dim3 grid((unsigned)((work + 255) / 256), (unsigned)count), block(256);
   hipStream_t s = tt::as_stream(stream);
   if (inverse)
@@ -193,6 +195,7 @@ extern "C" int tile_swiglu_fwd(void* stream, int64_t n, const float* a, const fl
   if (!a || !b || !h) return fail(TT_ERR_ARG, "tile_swiglu_fwd: null pointer");
   const bool vec = n % 4 == 0 && tt::aligned16(a) && tt::aligned16(b) && tt::aligned16(h);
   const int64_t work = (n + 3) / 4;
+  if ((work + 255) / 256 > INT32_MAX) return fail(TT_ERR_ARG, "tile_swiglu_fwd: %lld elements exceed one launch", (long long)n);
   dim3 grid((unsigned)((work + 255) / 256)), block(256);
   hipStream_t s = tt::as_stream(stream);
   if (vec) hipLaunchKernelGGL(swiglu_fwd_k<true>, grid, block, 0, s, n, a, b, h);
@@ -209,6 +212,7 @@ extern "C" int tile_swiglu_bwd(void* stream, int64_t n, const float* dh, const f
   const bool vec = n % 4 == 0 && tt::aligned16(dh) && tt::aligned16(a) && tt::aligned16(b) && tt::aligned16(da) &&
                    tt::aligned16(db);
   const int64_t work = (n + 3) / 4;
+  if ((work + 255) / 256 > INT32_MAX) return fail(TT_ERR_ARG, "tile_swiglu_bwd: %lld elements exceed one launch", (long long)n);
   dim3 grid((unsigned)((work + 255) / 256)), block(256);
   hipStream_t s = tt::as_stream(stream);
   if (vec) hipLaunchKernelGGL(swiglu_bwd_k<true>, grid, block, 0, s, n, dh, a, b, da, db);
