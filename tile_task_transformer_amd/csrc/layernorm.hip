@@ -867,12 +867,43 @@ __global__ __launch_bounds__(BT) void rms_bwd_multi(int rows, int rows_per_block
     if (ok[k]) *reinterpret_cast<f32x4*>(out + 4 * ((int)threadIdx.x + k * BT)) = dg[k];
 }
 
-// dgamma of every tile += the column sums of the block partials (blockIdx.y = tile)
+// dgamma of every tile += the column sums of the block partials (blockIdx.y
+// = tile), in a fixed order. One workgroup: 16 columns x 64 row groups
+// (four times the workgroups of colsum_finish_block's 64 x 16: the 768
+// columns of a GPT2-small-wide tile make 48 instead of 12, over 1024
+// partial rows); group g sums rows g, g + 64, ... (four loads in flight),
+// then the 64 group sums are added in group order.
+constexpr int kRmsSumCols = 16;
 __global__ __launch_bounds__(1024) void rms_colsum_finish_multi(int nblk, LnRowTiles P, const float* __restrict__ ws) {
+  __shared__ float red[1024 / kRmsSumCols][kRmsSumCols];
+  constexpr int G = 1024 / kRmsSumCols;
   const int t = blockIdx.y;
   const int width = t < P.n - 1 ? P.c0 : P.total - (P.n - 1) * P.c0;
-  if ((int)blockIdx.x * 64 >= width) return;
-  colsum_finish_block(nblk, width, ws, (int64_t)P.total, (int64_t)t * P.c0, P.dg[t], 1);
+  if ((int)blockIdx.x * kRmsSumCols >= width) return;
+  const int cl = threadIdx.x % kRmsSumCols, grp = threadIdx.x / kRmsSumCols;
+  const int c = blockIdx.x * kRmsSumCols + cl;
+  float sum = 0.f;
+  if (c < width) {
+    const float* src = ws + (int64_t)t * P.c0 + c;
+    const int64_t ld = P.total;
+    int b = grp;
+    for (; b + 3 * G < nblk; b += 4 * G) {
+      const float v0 = src[(int64_t)b * ld], v1 = src[(int64_t)(b + G) * ld];
+      const float v2 = src[(int64_t)(b + 2 * G) * ld], v3 = src[(int64_t)(b + 3 * G) * ld];
+      sum += v0;
+      sum += v1;
+      sum += v2;
+      sum += v3;
+    }
+    for (; b < nblk; b += G) sum += src[(int64_t)b * ld];
+  }
+  red[grp][cl] = sum;
+  __syncthreads();
+  if (grp == 0 && c < width) {
+    float tot = 0.f;
+    for (int i = 0; i < G; ++i) tot += red[i][cl];
+    P.dg[t][c] += tot;
+  }
 }
 
 // rows per backward workgroup: up to 16 (fewer column partials to sum), but
@@ -980,8 +1011,8 @@ extern "C" int tile_rmsnorm_bwd(void* stream, int count, int64_t rows, const int
   else TT_RMSB(1024, 4);
 #undef TT_RMSB
   if (int rc = tt::launch_status("tile_rmsnorm_bwd")) return rc;
-  hipLaunchKernelGGL(rms_colsum_finish_multi, dim3((unsigned)((P.c0 + 63) / 64), (unsigned)count), dim3(1024), 0, s,
-                     nblk, P, ws);
+  hipLaunchKernelGGL(rms_colsum_finish_multi, dim3((unsigned)((P.c0 + kRmsSumCols - 1) / kRmsSumCols), (unsigned)count),
+                     dim3(1024), 0, s, nblk, P, ws);
   return tt::launch_status("tile_rmsnorm_bwd(colsum)");
 }
 
