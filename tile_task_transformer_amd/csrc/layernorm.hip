@@ -229,35 +229,38 @@ __global__ __launch_bounds__(64 * bwd_waves(NV)) void ln_bwd_rows(
 }  // namespace
 
 // Column sums of nblk partial rows -> out[c] (+)= sum_b ws[b*ws_ld + ws_off + c],
-// in a fixed order. One workgroup: 64 columns x 16 row groups; group g sums
-// rows g, g+16, ... (loads issued 4 at a time), then the 16 group sums are
-// added in group order. blockIdx.y = 1 does the same for (ws_off2, out2):
-// LayerNorm's dgamma and dbeta in one launch.
+// in a fixed order. One workgroup: kSumCols (16) columns x 64 row groups;
+// group g sums rows g, g+64, ... (loads issued 4 at a time), then the 64
+// group sums are added in group order. Narrow workgroups give a 768-column
+// sum 48 workgroups instead of the 12 of 64-column ones (the RMSNorm gain
+// gradient over 1024 partial rows: 8.1 -> 5.2 us). blockIdx.y = 1 does the
+// same for (ws_off2, out2): LayerNorm's dgamma and dbeta in one launch.
+constexpr int kSumCols = 16;
 __device__ __forceinline__ void colsum_finish_block(int nblk, int cols, const float* __restrict__ ws, int64_t ws_ld,
                                                     int64_t ws_off, float* __restrict__ out, int accumulate) {
-  __shared__ float red[16][64];
-  const int cl = threadIdx.x & 63, grp = threadIdx.x >> 6;
-  const int c = blockIdx.x * 64 + cl;
+  constexpr int G = 1024 / kSumCols;
+  __shared__ float red[G][kSumCols];
+  const int cl = threadIdx.x % kSumCols, grp = threadIdx.x / kSumCols;
+  const int c = blockIdx.x * kSumCols + cl;
   float s = 0.f;
   if (c < cols) {
     const float* src = ws + ws_off + c;
     int b = grp;
-    for (; b + 48 < nblk; b += 64) {
-      const float v0 = src[(int64_t)b * ws_ld], v1 = src[(int64_t)(b + 16) * ws_ld];
-      const float v2 = src[(int64_t)(b + 32) * ws_ld], v3 = src[(int64_t)(b + 48) * ws_ld];
+    for (; b + 3 * G < nblk; b += 4 * G) {
+      const float v0 = src[(int64_t)b * ws_ld], v1 = src[(int64_t)(b + G) * ws_ld];
+      const float v2 = src[(int64_t)(b + 2 * G) * ws_ld], v3 = src[(int64_t)(b + 3 * G) * ws_ld];
       s += v0;
       s += v1;
       s += v2;
       s += v3;
     }
-    for (; b < nblk; b += 16) s += src[(int64_t)b * ws_ld];
+    for (; b < nblk; b += G) s += src[(int64_t)b * ws_ld];
   }
   red[grp][cl] = s;
   __syncthreads();
   if (grp == 0 && c < cols) {
     float t = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) t += red[i][cl];
+    for (int i = 0; i < G; ++i) t += red[i][cl];
     out[c] = accumulate ? out[c] + t : t;
   }
 }
@@ -405,7 +408,7 @@ extern "C" int tile_layernorm_bwd(void* stream, int phase, int64_t rows, int64_t
 #undef TT_LNB
   if (rc || phase == TT_LN_PARTIAL) return rc;
   const int nblk = (int)((r + bwd_rows_per_block(c) - 1) / bwd_rows_per_block(c));
-  dim3 grid((c + 63) / 64, 2), block(1024);
+  dim3 grid((c + kSumCols - 1) / kSumCols, 2), block(1024);
   hipLaunchKernelGGL(colsum_finish, grid, block, 0, s, nblk, c, ws, (int64_t)2 * c, (int64_t)0, dgamma, 1, (int64_t)c,
                      dbeta);
   return tt::launch_status("tile_layernorm_bwd(colsum)");
@@ -620,7 +623,7 @@ __global__ __launch_bounds__(BT) void ln_bwd_multi(int rows, int rows_per_block,
 __global__ __launch_bounds__(1024) void ln_colsum_finish_multi(int nblk, LnRowTiles P, const float* __restrict__ ws) {
   const int t = blockIdx.y >> 1, which = blockIdx.y & 1;
   const int width = t < P.n - 1 ? P.c0 : P.total - (P.n - 1) * P.c0;
-  if ((int)blockIdx.x * 64 >= width) return;
+  if ((int)blockIdx.x * kSumCols >= width) return;
   colsum_finish_block(nblk, width, ws, (int64_t)2 * P.total, (int64_t)which * P.total + (int64_t)t * P.c0,
                       which ? P.db[t] : P.dg[t], 1);
 }
@@ -731,7 +734,7 @@ extern "C" int tile_layernorm_bwd_multi(void* stream, int count, int64_t rows, c
   else TT_LNB(1024, 4);
 #undef TT_LNB
   if (int rc = tt::launch_status("tile_layernorm_bwd_multi")) return rc;
-  hipLaunchKernelGGL(ln_colsum_finish_multi, dim3((unsigned)((P.c0 + 63) / 64), (unsigned)(2 * count)), dim3(1024), 0,
+  hipLaunchKernelGGL(ln_colsum_finish_multi, dim3((unsigned)((P.c0 + kSumCols - 1) / kSumCols), (unsigned)(2 * count)), dim3(1024), 0,
                      s, nblk, P, ws);
   return tt::launch_status("tile_layernorm_bwd_multi(colsum)");
 }
@@ -867,43 +870,12 @@ __global__ __launch_bounds__(BT) void rms_bwd_multi(int rows, int rows_per_block
     if (ok[k]) *reinterpret_cast<f32x4*>(out + 4 * ((int)threadIdx.x + k * BT)) = dg[k];
 }
 
-// dgamma of every tile += the column sums of the block partials (blockIdx.y
-// = tile), in a fixed order. One workgroup: 16 columns x 64 row groups
-// (four times the workgroups of colsum_finish_block's 64 x 16: the 768
-// columns of a GPT2-small-wide tile make 48 instead of 12, over 1024
-// partial rows); group g sums rows g, g + 64, ... (four loads in flight),
-// then the 64 group sums are added in group order.
-constexpr int kRmsSumCols = 16;
+// dgamma of every tile += the column sums of the block partials (blockIdx.y = tile)
 __global__ __launch_bounds__(1024) void rms_colsum_finish_multi(int nblk, LnRowTiles P, const float* __restrict__ ws) {
-  __shared__ float red[1024 / kRmsSumCols][kRmsSumCols];
-  constexpr int G = 1024 / kRmsSumCols;
   const int t = blockIdx.y;
   const int width = t < P.n - 1 ? P.c0 : P.total - (P.n - 1) * P.c0;
-  if ((int)blockIdx.x * kRmsSumCols >= width) return;
-  const int cl = threadIdx.x % kRmsSumCols, grp = threadIdx.x / kRmsSumCols;
-  const int c = blockIdx.x * kRmsSumCols + cl;
-  float sum = 0.f;
-  if (c < width) {
-    const float* src = ws + (int64_t)t * P.c0 + c;
-    const int64_t ld = P.total;
-    int b = grp;
-    for (; b + 3 * G < nblk; b += 4 * G) {
-      const float v0 = src[(int64_t)b * ld], v1 = src[(int64_t)(b + G) * ld];
-      const float v2 = src[(int64_t)(b + 2 * G) * ld], v3 = src[(int64_t)(b + 3 * G) * ld];
-      sum += v0;
-      sum += v1;
-      sum += v2;
-      sum += v3;
-    }
-    for (; b < nblk; b += G) sum += src[(int64_t)b * ld];
-  }
-  red[grp][cl] = sum;
-  __syncthreads();
-  if (grp == 0 && c < width) {
-    float tot = 0.f;
-    for (int i = 0; i < G; ++i) tot += red[i][cl];
-    P.dg[t][c] += tot;
-  }
+  if ((int)blockIdx.x * kSumCols >= width) return;
+  colsum_finish_block(nblk, width, ws, (int64_t)P.total, (int64_t)t * P.c0, P.dg[t], 1);
 }
 
 // rows per backward workgroup: up to 16 (fewer column partials to sum), but
@@ -1011,7 +983,7 @@ extern "C" int tile_rmsnorm_bwd(void* stream, int count, int64_t rows, const int
   else TT_RMSB(1024, 4);
 #undef TT_RMSB
   if (int rc = tt::launch_status("tile_rmsnorm_bwd")) return rc;
-  hipLaunchKernelGGL(rms_colsum_finish_multi, dim3((unsigned)((P.c0 + kRmsSumCols - 1) / kRmsSumCols), (unsigned)count),
+  hipLaunchKernelGGL(rms_colsum_finish_multi, dim3((unsigned)((P.c0 + kSumCols - 1) / kSumCols), (unsigned)count),
                      dim3(1024), 0, s, nblk, P, ws);
   return tt::launch_status("tile_rmsnorm_bwd(colsum)");
 }
@@ -1139,7 +1111,7 @@ __global__ __launch_bounds__(256) void reduce_rows_stage1_multi(int rows, RowsTi
 __global__ __launch_bounds__(1024) void colsum_finish_multi(int nblk, RowsTiles P, const float* __restrict__ ws,
                                                             int accumulate) {
   const int t = blockIdx.y;
-  if ((int)blockIdx.x * 64 >= P.cols[t]) return;
+  if ((int)blockIdx.x * kSumCols >= P.cols[t]) return;
   colsum_finish_block(nblk, P.cols[t], ws, P.cols[t], P.ws_off[t], P.out[t], accumulate);
 }
 }  // namespace
@@ -1166,7 +1138,7 @@ extern "C" int tile_reduce_rows(void* stream, int64_t rows, int64_t cols, const 
     else hipLaunchKernelGGL(reduce_rows_stage1<false>, grid, block, 0, s, r, c, X, ldx, ws);
     if (int rc = tt::launch_status("tile_reduce_rows")) return rc;
   }
-  hipLaunchKernelGGL(colsum_finish, dim3((c + 63) / 64), dim3(1024), 0, s, nblk, c, ws, (int64_t)c, (int64_t)0, out,
+  hipLaunchKernelGGL(colsum_finish, dim3((c + kSumCols - 1) / kSumCols), dim3(1024), 0, s, nblk, c, ws, (int64_t)c, (int64_t)0, out,
                      beta, (int64_t)0, out);
   return tt::launch_status("tile_reduce_rows(finish)");
 }
@@ -1207,7 +1179,7 @@ extern "C" int tile_reduce_rows_multi(void* stream, int count, int64_t rows, con
     else hipLaunchKernelGGL(reduce_rows_stage1_multi<false>, grid, block, 0, s, r, P, ws);
     if (int rc = tt::launch_status("tile_reduce_rows_multi")) return rc;
   }
-  hipLaunchKernelGGL(colsum_finish_multi, dim3((unsigned)((maxc + 63) / 64), count), dim3(1024), 0, s, nblk, P, ws,
+  hipLaunchKernelGGL(colsum_finish_multi, dim3((unsigned)((maxc + kSumCols - 1) / kSumCols), count), dim3(1024), 0, s, nblk, P, ws,
                      beta);
   return tt::launch_status("tile_reduce_rows_multi(finish)");
 }
