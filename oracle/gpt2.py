@@ -33,6 +33,12 @@ Regularization). Readings taken where the pages are silent:
 
 The arithmetic below is the plain definition of each layer; the only
 library primitive used is numpy's matmul (and exp/log/tanh/sqrt).
+
+Parity unpinned: lr_at between its ends. The README fixes the learning
+rate of iteration 1 (start_lr) and of iteration full_lr_iter onwards (the
+full lr); the linear ramp in between is a reading that no passage or
+closed form fixes, so its interior values are checked only against that
+reading. The ends and the constant schedule are pinned.
 """
 from __future__ import annotations
 
