@@ -646,6 +646,17 @@ typedef struct tt_tensor tt_tensor;
  * (0 = default 512); a larger window gives the stream assignment more
  * look-ahead. One submitting thread per context. */
 int tt_ctx_create(int device, int n_streams, int window, size_t device_budget_bytes, tt_ctx** out);
+/* tt_ctx_create_on_streams -- tt_ctx_create whose tasks run on n_streams
+ * HIP streams the caller owns (a HOST array of hipStream_t handles, e.g.
+ * torch streams): the context does not create, and on destruction does not
+ * destroy, them; they must stay valid until tt_ctx_destroy returns. Work
+ * the caller queues on them interleaves with the tasks in stream order
+ * (use tt_ctx_wait_stream / tt_ctx_join_stream for other streams). The
+ * context still creates its own copy streams for pinned-host tiles.
+ * TT_ERR_ARG for the dry-run device, a null array, a null (legacy
+ * default) stream, or the same stream twice. */
+int tt_ctx_create_on_streams(int device, int n_streams, void* const* streams, int window,
+                             size_t device_budget_bytes, tt_ctx** out);
 int tt_ctx_destroy(tt_ctx* ctx);
 /* hipStream_t of executor stream i (for callers that want to order their own
  * work after the context's). */

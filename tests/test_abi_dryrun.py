@@ -2,6 +2,7 @@
 header declares, argument errors are reported, and the sequential-task-flow
 executor infers exactly the read-after-write, write-after-read and
 write-after-write edges (dry-run contexts launch nothing and need no GPU)."""
+import ctypes as C
 import os
 import re
 
@@ -331,3 +332,13 @@ def test_priority_order_of_a_gpt2_step_is_a_race_free_topological_order(tiles, t
     for r in prio:
         assert r["deps"] == by_id[r["id"]]["deps"] and r["stream"] == by_id[r["id"]]["stream"]
     _check_races(prio)
+
+
+def test_caller_streams_need_a_device():
+    """tt_ctx_create_on_streams refuses the dry-run device and a null stream
+    array before touching any GPU."""
+    with pytest.raises(L.TTError) as e:
+        Context(L.TT_DEVICE_DRYRUN, streams=[1, 2])
+    assert e.value.code == L.TT_ERR_ARG and "needs a device" in str(e.value)
+    h = C.c_void_p()
+    assert L.lib.tt_ctx_create_on_streams(0, 2, None, 0, 0, C.byref(h)) == L.TT_ERR_ARG

@@ -153,6 +153,47 @@ def test_priority_launch_order_gives_the_same_bits():
         assert np.array_equal(outs[0][2][name], outs[1][2][name]), name
 
 
+def test_context_on_caller_streams_gives_the_same_bits():
+    """A context whose tasks run on two torch streams (tt_ctx_create_on_streams)
+    gives bitwise the results of one with its own two streams, leaves the
+    streams usable after it is destroyed, and rejects a repeated or null
+    stream."""
+    from tile_task_transformer_amd import _lib as L
+    shape = synth.GPT2Shape(2, 256, 64, 4, 256, 32, 2)
+    params = synth.init_params(shape, seed=5)
+    tokens = synth.token_stream(shape, seed=6)
+    tiles = synth.Tiles(1, 8, 16, 64, 1, 48)
+    specs = synth.param_specs(shape)
+    mine = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for streams in (None, mine):
+        with Context(0, n_streams=2, streams=streams) as ctx:
+            model = GPT2(ctx, shape, tiles)
+            model.set_params(params, specs)
+            tok = torch.from_numpy(tokens.astype(np.int32)).cuda()
+            losses = []
+            for _ in range(2):
+                model.step(tok)
+                losses.append(model.loss())
+            outs.append((losses, model.get(specs, 0), model.get(specs, 1)))
+            model.close()
+    assert outs[0][0] == outs[1][0]
+    for name in outs[0][1]:
+        assert np.array_equal(outs[0][1][name], outs[1][1][name]), name
+        assert np.array_equal(outs[0][2][name], outs[1][2][name]), name
+    # the borrowed streams outlive the context
+    with torch.cuda.stream(mine[1]):
+        x = torch.arange(1024, device="cuda", dtype=torch.float32) * 2
+    mine[1].synchronize()
+    assert float(x.sum()) == 1023 * 1024
+    with pytest.raises(L.TTError) as e:
+        Context(0, streams=[mine[0], mine[0]])
+    assert e.value.code == L.TT_ERR_ARG
+    with pytest.raises(L.TTError) as e:
+        Context(0, streams=[mine[0], 0])
+    assert e.value.code == L.TT_ERR_ARG
+
+
 def test_gpt2_small_full_size_step_matches_oracle():
     """The GPT2-small workload at its full size and README tiles, checked
     against the full fp64 oracle step."""

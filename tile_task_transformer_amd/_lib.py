@@ -204,6 +204,7 @@ SIGNATURES = {
     "tile_fill_multi": (I, [P, I, P, P, F]),
     "tile_split_tokens": (I, [P, I64, I64, P, P, P]),
     "tt_ctx_create": (I, [I, I, I, SZ, PP]),
+    "tt_ctx_create_on_streams": (I, [I, I, PP, I, SZ, PP]),
     "tt_ctx_destroy": (I, [P]),
     "tt_ctx_stream": (I, [P, I, PP]),
     "tt_ctx_record": (I, [P, I]),

@@ -928,9 +928,12 @@ int tt_ctx::prof_collect() {
 
 // -------------------------------------------------------------------- C ABI
 
-extern "C" {
+namespace {
 
-int tt_ctx_create(int device, int n_streams, int window, size_t device_budget_bytes, tt_ctx** out) {
+// tt_ctx_create with the executor's streams either created here or borrowed
+// from the caller (not null, pairwise distinct, not destroyed here)
+int ctx_create(int device, int n_streams, void* const* borrowed, int window, size_t device_budget_bytes,
+               tt_ctx** out) {
   clear_error();
   if (!out) return fail(TT_ERR_ARG, "tt_ctx_create: out is null");
   if (n_streams < 1 || n_streams > 16) return fail(TT_ERR_ARG, "tt_ctx_create: n_streams must be 1..16");
@@ -952,13 +955,51 @@ int tt_ctx_create(int device, int n_streams, int window, size_t device_budget_by
     if (device < 0) return fail(TT_ERR_ARG, "tt_ctx_create: bad device %d", device);
     TT_HIP_TRY(hipSetDevice(device));
     c->streams.resize(n_streams);
-    for (int s = 0; s < n_streams; ++s)
-      TT_HIP_TRY(hipStreamCreateWithFlags(&c->streams[s], hipStreamNonBlocking));
-    TT_HIP_TRY(hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking));
-    TT_HIP_TRY(hipStreamCreateWithFlags(&c->d2h_stream, hipStreamNonBlocking));
+    for (int s = 0; s < n_streams; ++s) {
+      if (borrowed) {
+        c->streams[s] = static_cast<hipStream_t>(borrowed[s]);
+        continue;
+      }
+      if (hipError_t e = hipStreamCreateWithFlags(&c->streams[s], hipStreamNonBlocking)) {
+        for (int q = 0; q < s; ++q) (void)hipStreamDestroy(c->streams[q]);
+        return fail(TT_ERR_HIP, "tt_ctx_create: hipStreamCreateWithFlags: %s", hipGetErrorString(e));
+      }
+    }
+    c->owns_streams = !borrowed;
+    hipError_t e = hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->d2h_stream, hipStreamNonBlocking);
+    if (e != hipSuccess) {
+      if (c->owns_streams)
+        for (auto st : c->streams) (void)hipStreamDestroy(st);
+      if (c->copy_stream) (void)hipStreamDestroy(c->copy_stream);
+      return fail(TT_ERR_HIP, "tt_ctx_create: hipStreamCreateWithFlags: %s", hipGetErrorString(e));
+    }
   }
   *out = c.release();
   return TT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tt_ctx_create(int device, int n_streams, int window, size_t device_budget_bytes, tt_ctx** out) {
+  return ctx_create(device, n_streams, nullptr, window, device_budget_bytes, out);
+}
+
+int tt_ctx_create_on_streams(int device, int n_streams, void* const* streams, int window,
+                             size_t device_budget_bytes, tt_ctx** out) {
+  clear_error();
+  if (device == TT_DEVICE_DRYRUN) return fail(TT_ERR_ARG, "tt_ctx_create_on_streams: needs a device");
+  if (!streams) return fail(TT_ERR_ARG, "tt_ctx_create_on_streams: null stream array");
+  if (n_streams < 1 || n_streams > 16) return fail(TT_ERR_ARG, "tt_ctx_create: n_streams must be 1..16");
+  for (int i = 0; i < n_streams; ++i) {
+    if (!streams[i])
+      return fail(TT_ERR_ARG, "tt_ctx_create_on_streams: stream %d is the null (legacy default) stream", i);
+    for (int j = 0; j < i; ++j)
+      if (streams[j] == streams[i]) return fail(TT_ERR_ARG, "tt_ctx_create_on_streams: streams %d and %d are one stream", j, i);
+  }
+  return ctx_create(device, n_streams, streams, window, device_budget_bytes, out);
 }
 
 int tt_ctx_destroy(tt_ctx* c) {
@@ -973,7 +1014,8 @@ int tt_ctx_destroy(tt_ctx* c) {
     for (auto e : c->prof_events) (void)hipEventDestroy(e);
     if (c->prof_base) (void)hipEventDestroy(c->prof_base);
     for (auto e : c->ext_events) (void)hipEventDestroy(e);
-    for (auto s : c->streams) (void)hipStreamDestroy(s);
+    if (c->owns_streams)
+      for (auto s : c->streams) (void)hipStreamDestroy(s);
     if (c->copy_stream) (void)hipStreamDestroy(c->copy_stream);
     if (c->d2h_stream) (void)hipStreamDestroy(c->d2h_stream);
     if (c->arena) (void)hipFree(c->arena);

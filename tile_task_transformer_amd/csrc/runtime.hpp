@@ -138,6 +138,7 @@ struct tt_ctx {
   std::string latched_msg;
 
   std::vector<hipStream_t> streams;
+  bool owns_streams = true;            // false: borrowed from the caller (tt_ctx_create_on_streams)
   hipStream_t copy_stream = nullptr;   // residency H2D
   hipStream_t d2h_stream = nullptr;    // residency write-backs (the link is full duplex)
   std::vector<void*> workspace;        // per stream

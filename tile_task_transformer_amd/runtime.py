@@ -16,9 +16,18 @@ class Context:
     """Executor context: `device` = GPU ordinal, or L.TT_DEVICE_DRYRUN to
     record tasks without a GPU."""
 
-    def __init__(self, device: int = 0, n_streams: int = 4, window: int = 0, device_budget: int = 0):
+    def __init__(self, device: int = 0, n_streams: int = 4, window: int = 0, device_budget: int = 0,
+                 streams=None):
+        """streams: optional sequence of n_streams caller-owned streams (torch
+        streams or raw hipStream_t handles) for the tasks
+        (tt_ctx_create_on_streams); they must outlive the context."""
         h = C.c_void_p()
-        check(lib.tt_ctx_create(device, n_streams, window, device_budget, C.byref(h)))
+        if streams is not None:
+            handles = (C.c_void_p * max(1, len(streams)))(*[L.stream_handle(x) for x in streams])
+            check(lib.tt_ctx_create_on_streams(device, len(streams), handles, window, device_budget, C.byref(h)))
+            n_streams = len(streams)
+        else:
+            check(lib.tt_ctx_create(device, n_streams, window, device_budget, C.byref(h)))
         self.h = h
         self.n_streams = n_streams
         self.dryrun = device == L.TT_DEVICE_DRYRUN
