@@ -28,7 +28,7 @@ Prints ONE JSON line:
                workload, scaled to tokens/s of the whole step (see
                cpu_baseline())
 Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload NAME]
-       [--streams S (default: 1; small tiles 4)] [--pinned --budget-gb G]
+       [--streams S (default: 1; small tiles 4)] [--pinned [--grads-in-hbm] --budget-gb G]
 """
 from __future__ import annotations
 
@@ -582,6 +582,8 @@ def main(argv=None):
                          "on 1 and 4 streams, 4 with critical-path priorities, and write gpurun_out/depth_sweep.json")
     ap.add_argument("--pinned", action="store_true",
                     help="parameters, gradients and moments live in pinned host RAM (out-of-core residency)")
+    ap.add_argument("--grads-in-hbm", action="store_true",
+                    help="with --pinned: gradients stay in HBM, only parameters and moments are pinned")
     ap.add_argument("--budget-gb", type=float, default=0.0, help="device arena for pinned tiles (0 = half of free)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", default=os.path.join("gpurun_out", "bench_breakdown.json"),
@@ -603,6 +605,9 @@ def main(argv=None):
         return 2
     if a.steps < 1 or a.warmup < 0:
         print("bench.py: --steps must be at least 1 and --warmup at least 0", file=sys.stderr)
+        return 2
+    if a.grads_in_hbm and not a.pinned:
+        print("bench.py: --grads-in-hbm goes with --pinned", file=sys.stderr)
         return 2
 
     w = ALL_WORKLOADS[a.workload]
@@ -671,7 +676,7 @@ def run(w, a, streams, breakdown_path, probe, steps=None, warmup=None, want_para
     t0 = time.perf_counter()
     params = synth.init_params(s, seed=0, threads=min(16, len(os.sched_getaffinity(0))), specs=specs)
     tokens = synth.token_stream(s, seed=1)
-    home = L.TT_HOME_PINNED_HOST if a.pinned else L.TT_HOME_DEVICE
+    home = (L.TT_HOME_PINNED_STATE if a.grads_in_hbm else L.TT_HOME_PINNED_HOST) if a.pinned else L.TT_HOME_DEVICE
     ctx = Context(0, n_streams=streams, window=4096, device_budget=int(a.budget_gb * 2 ** 30))
     if a.heavy_gflops > 0:
         ctx.heavy_lane(a.heavy_gflops * 1e9)
@@ -752,7 +757,9 @@ def run(w, a, streams, breakdown_path, probe, steps=None, warmup=None, want_para
     ctx.wait()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    step_ms = sorted(bounds[i].elapsed_time(bounds[i + 1]) for i in range(steps))
+    step_ms = [bounds[i].elapsed_time(bounds[i + 1]) for i in range(steps)]
+    print(f"[bench] {w.name}: GPU time of each timed step (ms): {[round(x, 1) for x in step_ms]}", file=sys.stderr)
+    step_ms.sort()
     loss = model.loss()
     st = ctx.stats()
     prof = ctx.profile_take().get(dominant, {})
@@ -779,7 +786,7 @@ def run(w, a, streams, breakdown_path, probe, steps=None, warmup=None, want_para
                    "tiles": {"batch": t.batch, "seq": t.seq, "embd": t.embd, "inner": t.inner, "head": t.head,
                              "vocab": t.vocab}, "streams": streams, "heavy_gflops": a.heavy_gflops,
                    "priorities": bool(a.priorities),
-                   "param_home": "pinned_host" if a.pinned else "device"},
+                   "param_home": ("pinned_state" if a.grads_in_hbm else "pinned_host") if a.pinned else "device"},
         "tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_FP32_PEAK, 4),
         "mfma_frac_of_probe": round(tflops / probe["mfma_f32_tflops"], 4) if probe else None,
         "tasks_per_step": model.task_count(), "loss": round(loss, 5),

@@ -626,6 +626,8 @@ typedef struct tt_tensor tt_tensor;
 #define TT_I32 1
 #define TT_HOME_DEVICE      0   /* tiles live in HBM */
 #define TT_HOME_PINNED_HOST 1   /* tiles live in pinned host RAM, staged on use */
+#define TT_HOME_PINNED_STATE 2  /* tt_gpt2_create / tt_llama_create param_home only: parameters and
+                                   AdamW moments pinned host, gradients in HBM */
 #define TT_DEVICE_DRYRUN   -1   /* tt_ctx_create: no GPU, tasks recorded only */
 
 /* Context: owns n_streams HIP streams (default priority), their events and
@@ -1095,7 +1097,10 @@ typedef struct {
  * w_fc [d,I], b_fc, w_p [I,d], b_p, then lnf_g, lnf_b (GPT2 with a tied
  * head). TT_ERR_SHAPE if seq, head or batch tiles do not divide their axis
  * or n_embd % n_head != 0. param_home = TT_HOME_PINNED_HOST keeps
- * parameters, gradients and moments in pinned host RAM (out-of-core). */
+ * parameters, gradients and moments in pinned host RAM (out-of-core);
+ * TT_HOME_PINNED_STATE keeps parameters and moments there and the
+ * gradients, which are made and consumed within a step, in HBM (no link
+ * traffic for them). */
 int tt_gpt2_create(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_gpt2_tiles* tiles,
                    int param_home, tt_gpt2** out);
 /* The LLaMA-style model (the NNTile README's notebook list names LLaMa

@@ -47,6 +47,40 @@ def test_pinned_host_step_is_bitwise_equal_to_hbm(budget_kib):
     assert st["h2d_bytes"] > 0 and st["evictions"] > 0 and st["d2h_bytes"] > 0, st
 
 
+@pytest.mark.parametrize("family", ["gpt2", "llama"])
+def test_pinned_state_with_gradients_in_hbm_is_bitwise_equal_to_hbm(family):
+    """TT_HOME_PINNED_STATE: parameters and moments pinned, gradients in HBM
+    (they never cross the link); two steps, bitwise the all-in-HBM run."""
+    w = synth.WORKLOADS["tiny"] if family == "gpt2" else synth.LLAMA_WORKLOADS["llama_tiny"]
+    shape, tiles = w.shape, w.tiles
+    specs = synth.param_specs(shape) if family == "gpt2" else synth.llama_param_specs(shape)
+    params = synth.init_params(shape, seed=0, specs=specs)
+    tokens = synth.token_stream(shape, seed=1)
+    outs = []
+    for home, budget in ((L.TT_HOME_DEVICE, 0), (L.TT_HOME_PINNED_HOST, 160 * 1024),
+                         (L.TT_HOME_PINNED_STATE, 160 * 1024)):
+        with Context(0, n_streams=4, device_budget=budget) as ctx:
+            model = GPT2(ctx, shape, tiles, param_home=home, family=family)
+            model.set_params(params, specs)
+            tok = torch.from_numpy(tokens.astype(np.int32)).cuda()
+            losses = []
+            for _ in range(2):
+                model.step(tok)
+                losses.append(model.loss())
+            outs.append(dict(loss=losses, params=model.get(specs, 0), grads=model.get(specs, 1),
+                             m=model.get(specs, 2), v=model.get(specs, 3), stats=ctx.stats()))
+            model.close()
+    ref, pinned, state = outs
+    for got in (pinned, state):
+        assert got["loss"] == ref["loss"]
+        for key in ("params", "grads", "m", "v"):
+            for name in ref[key]:
+                assert np.array_equal(got[key][name], ref[key][name]), (key, name)
+    assert state["stats"]["h2d_bytes"] > 0 and state["stats"]["evictions"] > 0
+    # the gradients no longer cross the link
+    assert state["stats"]["d2h_bytes"] < pinned["stats"]["d2h_bytes"], (state["stats"], pinned["stats"])
+
+
 def test_pinned_step_over_many_small_windows_is_bitwise_equal_to_hbm():
     """A submit window of 32 tasks: the step is launched in many windows, so
     the residency plan (eviction by next use, prefetch) sees only part of

@@ -39,7 +39,7 @@ TT_EMB_TOKEN, TT_EMB_POS = 0, 1
 TT_PROBE_READ, TT_PROBE_WRITE, TT_PROBE_COPY, TT_PROBE_NONTEMPORAL = 0, 1, 2, 4
 TT_MAX_DIMS = 6
 TT_F32, TT_I32 = 0, 1
-TT_HOME_DEVICE, TT_HOME_PINNED_HOST = 0, 1
+TT_HOME_DEVICE, TT_HOME_PINNED_HOST, TT_HOME_PINNED_STATE = 0, 1, 2
 TT_DEVICE_DRYRUN = -1
 TT_R, TT_W, TT_RW = 1, 2, 3
 TT_OPT_ADAMW, TT_OPT_SGD = 0, 1

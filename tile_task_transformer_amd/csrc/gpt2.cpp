@@ -295,7 +295,7 @@ bool head_xstats() {
 int fill_tasks(tt_gpt2* g, const std::vector<TileRef>& tiles, float v) {
   tt_ctx* ctx = g->ctx;
   int64_t max_elems = int64_t(1) << 30;
-  if (g->param_home == TT_HOME_PINNED_HOST && ctx->budget > 0)
+  if (g->param_home != TT_HOME_DEVICE && ctx->budget > 0)
     max_elems = (int64_t)(ctx->budget / (8 * sizeof(float)));
   size_t k = 0;
   while (k < tiles.size()) {
@@ -465,7 +465,7 @@ static int create_model(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_gpt2_ti
     return fail(TT_ERR_UNSUPPORTED, "tt_gpt2_create: head dim %lld not in {16,32,64,128}", (long long)hd);
   const int64_t et = std::min(t.embd, c.n_embd), vt = std::min(t.vocab, c.vocab);
   if (et > 2048 || vt > 2048) return fail(TT_ERR_UNSUPPORTED, "tt_gpt2_create: embd and vocab tiles must be <= 2048");
-  if (param_home != TT_HOME_DEVICE && param_home != TT_HOME_PINNED_HOST)
+  if (param_home != TT_HOME_DEVICE && param_home != TT_HOME_PINNED_HOST && param_home != TT_HOME_PINNED_STATE)
     return fail(TT_ERR_ARG, "tt_gpt2_create: bad param_home");
   // the RMSNorm kernels take float4 rows of at most 16384 features
   if (llama && (c.n_embd % 4 || et % 4 || c.n_embd > 16384))
@@ -544,7 +544,11 @@ static int create_model(tt_ctx* ctx, const tt_gpt2_config* cfg, const tt_gpt2_ti
     const char* suffix[4] = {"", ".grad", ".m", ".v"};
     for (int j = 0; j < 4; ++j) {
       std::string nm = std::string(s.name) + suffix[j];
-      int rc = tensor_create(ctx, (int)s.shape.size(), s.shape.data(), s.tile.data(), TT_F32, ph, s.split,
+      // TT_HOME_PINNED_STATE: parameters and moments pinned, gradients in HBM
+      const int home = ph == TT_HOME_DEVICE ? TT_HOME_DEVICE
+                       : (ph == TT_HOME_PINNED_STATE && j == 1) ? TT_HOME_DEVICE
+                                                                 : TT_HOME_PINNED_HOST;
+      int rc = tensor_create(ctx, (int)s.shape.size(), s.shape.data(), s.tile.data(), TT_F32, home, s.split,
                              nm.c_str(), &ts[j]);
       if (rc) return fail_clean(rc);
       G->owned.push_back(ts[j]);
@@ -1356,7 +1360,7 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
     // with pinned-host homes a task's tiles must fit the device arena (p, g,
     // m and v of every tile): a group then takes at most an eighth of it
     int64_t max_elems = int64_t(16) << 20;
-    if (g->param_home == TT_HOME_PINNED_HOST && ctx->budget > 0)
+    if (g->param_home != TT_HOME_DEVICE && ctx->budget > 0)
       max_elems = std::min<int64_t>(max_elems, (int64_t)(ctx->budget / (8 * 4 * sizeof(float))));
     size_t k = 0;
     while (k < items.size()) {
