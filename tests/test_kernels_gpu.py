@@ -30,7 +30,10 @@ def _op(a, t):
 
 @pytest.mark.parametrize("ta,tb", [(0, 0), (0, 1), (1, 0), (1, 1)])
 @pytest.mark.parametrize("m,n,k", [(257, 130, 70), (128, 128, 16), (300, 513, 337), (1, 1, 1), (64, 200, 1),
-                                   (1100, 700, 256), (4000, 2304, 37)])
+                                   (1100, 700, 256), (4000, 2304, 37),
+                                   # >= 512 blocks of 128x128 whose last round is poorly filled -> 64x64
+                                   # (short and long K), and full rounds that keep 128x128
+                                   (4096, 2304, 768), (4100, 2304, 1030), (4096, 2048, 768)])
 def test_gemm_parity(ta, tb, m, n, k):
     seed = m * 7 + n * 3 + k + 10 * ta + 20 * tb
     a = synth.rand_normal((k, m) if ta else (m, k), seed)
