@@ -193,13 +193,23 @@ def test_gpt2_step_dag_is_race_free(tiles, tmp_path):
     for need in ("emb_fwd", "qkv", "attn_fwd", "attn_proj", "fc", "mlp_proj", "head", "ce_merge",
                  "ce_loss", "ce_grad", "head_dw", "head_dx", "attn_bwd", "adamw", "emb_dw", "emb_dpos"):
         assert need in labels, need
-    # the cross-entropy statistics come from the head's last batch (its
-    # epilogue), not from a separate pass over the logits: every merge reads
-    # partials that a head task wrote
-    assert "ce_stats" not in labels
     label_of = {r["id"]: r["label"] for r in dag}
     merges = [r for r in dag if r["label"] == "ce_merge"]
-    assert merges and all(any(label_of[d] == "head" for d in r["deps"]) for r in merges)
+    ne = -(-shape.n_embd // tiles.embd)
+    nv = -(-shape.vocab // tiles.vocab)
+    ntok = (shape.batch // tiles.batch) * (shape.seq // tiles.seq)
+    heads = sum(1 for r in dag if r["label"] == "head")
+    if ne == 1:
+        # one embd tile: the cross-entropy statistics come from the head's
+        # batched launch (its epilogue), not from a separate pass over the
+        # logits: every merge reads partials that a head task wrote
+        assert "ce_stats" not in labels
+        assert merges and all(any(label_of[d] == "head" for d in r["deps"]) for r in merges)
+    else:
+        # several embd tiles: one long-K head task per (token tile, vocab
+        # tile), then the statistics pass, which the merge reads
+        assert heads == ntok * nv
+        assert merges and all(any(label_of[d] == "ce_stats" for d in r["deps"]) for r in merges)
 
 
 def test_gpt2_accumulating_step_dag_is_race_free(tmp_path):

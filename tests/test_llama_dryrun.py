@@ -44,9 +44,13 @@ def test_llama_step_dag_is_race_free(tiles, tmp_path):
                  "ce_merge", "ce_grad", "head_dw", "head_dx", "mlp_proj_dw", "mlp_proj_dx", "swiglu_bwd", "fc_dw",
                  "fc_dx", "rms_bwd", "attn_bwd", "rope_bwd", "qkv_dw", "qkv_dx", "adamw", "emb_dw"):
         assert need in by, need
-    for absent in ("emb_dpos", "ln_fwd", "ln_bwd", "colsum", "ce_stats"):
+    for absent in ("emb_dpos", "ln_fwd", "ln_bwd", "colsum"):
         assert absent not in by, absent
     nb, ns = SHAPE.batch // tiles.batch, SHAPE.seq // tiles.seq
+    # the head's statistics: fused into its batched launch with one embd
+    # tile, a separate pass after the per-vocab-tile long-K tasks with several
+    ne = -(-SHAPE.n_embd // tiles.embd)
+    assert ("ce_stats" in by) == (ne > 1)
     nh = SHAPE.n_head // tiles.head
     ntok = nb * ns
     assert by["rope"] == by["rope_bwd"] == SHAPE.n_layer * ntok * nh

@@ -278,6 +278,26 @@ bool use_ksum(const char* label, const TileRef& C, int tb, const TileRef& A0) {
   return !(nb >= 512 && nb < 1024 && !tb && ak >= 8192);
 }
 
+// whether the head's forward runs one long-K task per vocab tile (a sum over
+// the embd tiles, then a separate statistics pass over the logits) instead
+// of one batched launch per embd tile accumulating into the logits, the last
+// one with the statistics in its epilogue. With several embd tiles the sums
+// win (measured, each task alone): the wide model's head (4 embd tiles of
+// 2048) 27.7 -> 25.1 ms per step (77 -> 86 % of the fp32 peak), the
+// small-tile model's (16 of 512) 47.3 -> 33.9 ms, whole steps 700 -> 697 and
+// 823 -> 814 ms, the statistics pass costing 0.14-0.22 ms of that. With one
+// embd tile the batch and its fused statistics stay. TT_HEAD_KSUM=0/1 forces
+// either (comparison).
+bool head_ksum(int64_t embd_tiles) {
+  static int forced = -2;
+  if (forced == -2) {
+    const char* e = getenv("TT_HEAD_KSUM");
+    forced = e ? (atoi(e) != 0) : -1;
+  }
+  if (embd_tiles < 2) return false;
+  return forced != 0;
+}
+
 // whether the head's last batch takes the cross-entropy statistics in its
 // epilogue (else a separate pass over the logits); TT_HEAD_XSTATS=0 selects
 // the separate pass (comparison)
@@ -1273,8 +1293,21 @@ static int submit_step(tt_gpt2* g, const int32_t* tokens, const tt_adamw_hparams
       // read again for them
       tt_tensor *z = g->z, *parts = g->ce_parts;
       const int64_t ll = L(g->labels, {bi, si});
-      const bool fused = head_xstats();
-      for (int64_t ek = 0; ek < NE; ++ek) {
+      const bool ksum = head_ksum(NE);
+      const bool fused = head_xstats() && !ksum;
+      if (ksum) {
+        // z_v = sum over the embd tiles of nf_e wte_v,e^T: one long-K task
+        // per vocab tile
+        for (int64_t vj = 0; vj < NV; ++vj) {
+          std::vector<TileRef> As, Bs;
+          for (int64_t ek = 0; ek < NE; ++ek) {
+            As.push_back({g->nf, L(g->nf, {bi, si, ek})});
+            Bs.push_back({wte, L(wte, {vj, ek})});
+          }
+          TRY(submit_ksum(ctx, "head", 1, {g->z, L(g->z, {bi, si, vj})}, As, Bs));
+        }
+      }
+      for (int64_t ek = 0; ek < (ksum ? 0 : NE); ++ek) {
         std::vector<Gemm> qs;
         for (int64_t vj = 0; vj < NV; ++vj) {
           Gemm q;
