@@ -61,10 +61,10 @@ HBM_PEAK = 8000.0       # GB/s
 TRAFFIC = {
     # profiles/gemm_ksum_fc_wide4_traffic.md
     ("wide4", "fc"): {"source": "tile_task_transformer_amd/csrc/gemm.hip", "sha256": "832d171deb162b75",
-                      "fetch_kib": 787708.3, "fetch_factor": 2.0, "write_kib": 262144.0, "write_factor": 1.0},
+                      "fetch_kib": 787728.5, "fetch_factor": 2.0, "write_kib": 262144.0, "write_factor": 1.0},
     # profiles/gemm_batch_head_gpt2_small_traffic.md
     ("gpt2_small", "head"): {"source": "tile_task_transformer_amd/csrc/gemm.hip", "sha256": "832d171deb162b75",
-                             "fetch_kib": 983961.5, "fetch_factor": 2.0, "write_kib": 842545.2, "write_factor": 1.0},
+                             "fetch_kib": 982731.9, "fetch_factor": 2.0, "write_kib": 842550.1, "write_factor": 1.0},
 }
 
 
