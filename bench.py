@@ -579,15 +579,19 @@ def main(argv=None):
                     help="launch each window by critical-path priority instead of submission order")
     ap.add_argument("--depth-sweep", default="",
                     help="instead of the step: time the workload's widths at these block counts (e.g. 1,2,4,8,12) "
-                         "on 1 and 4 streams, 4 with critical-path priorities, and write gpurun_out/depth_sweep.json")
+                         "on 1 and 4 streams, 4 with critical-path priorities, and print the results as JSON "
+                         "(also written to --out-dir/depth_sweep.json)")
+    ap.add_argument("--out-dir", default=os.environ.get("TT_BENCH_OUT", "bench_out"),
+                    help="folder for the per-class breakdown and the depth sweep (default: $TT_BENCH_OUT or bench_out)")
     ap.add_argument("--pinned", action="store_true",
                     help="parameters, gradients and moments live in pinned host RAM (out-of-core residency)")
     ap.add_argument("--grads-in-hbm", action="store_true",
                     help="with --pinned: gradients stay in HBM, only parameters and moments are pinned")
     ap.add_argument("--budget-gb", type=float, default=0.0, help="device arena for pinned tiles (0 = half of free)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--breakdown", default=os.path.join("gpurun_out", "bench_breakdown.json"),
-                    help="per-task-class GPU times of one extra step run on one stream ('' = skip)")
+    ap.add_argument("--breakdown", default=None,
+                    help="file for the per-task-class GPU times of one extra step run on one stream "
+                         "(default: --out-dir/bench_breakdown.json; '' = skip)")
     ap.add_argument("--tile-classes", default="",
                     help="instead of the step: time each tile-op class alone and write this JSON file")
     ap.add_argument("--only", default=None, help="with --tile-classes: just this GEMM class")
@@ -596,6 +600,8 @@ def main(argv=None):
     ap.add_argument("--pmc-summary", nargs="+", default=None,
                     help="instead of running: summarise rocprofv3 counter_collection.csv files")
     a = ap.parse_args(argv)
+    if a.breakdown is None:
+        a.breakdown = os.path.join(a.out_dir, "bench_breakdown.json")
     if a.pmc_summary:
         res = pmc_summary(a.pmc_summary, a.copy_probe_mib)
         print(json.dumps(res, indent=1))
@@ -631,8 +637,8 @@ def main(argv=None):
         return 0
     if a.depth_sweep:
         res = depth_sweep(w, [int(x) for x in a.depth_sweep.split(",")])
-        os.makedirs("gpurun_out", exist_ok=True)
-        with open(os.path.join("gpurun_out", "depth_sweep.json"), "w") as f:
+        os.makedirs(a.out_dir, exist_ok=True)
+        with open(os.path.join(a.out_dir, "depth_sweep.json"), "w") as f:
             json.dump(res, f, indent=1)
         print(json.dumps(res), flush=True)
         return 0
