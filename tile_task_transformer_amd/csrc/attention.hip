@@ -202,12 +202,19 @@ __global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_fwd(AttnGeom g, const
       f32x16 s;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = 0.f;
+      // a wave issuing its products takes priority over the other resident
+      // wave of its SIMD, whose softmax arithmetic fills the gaps (head dim
+      // 64, two waves per SIMD: 0.922 -> 0.89 ms per GPT2-small step; at 128
+      // one wave per SIMD, unchanged; the same in the dK/dV kernel measured
+      // no gain)
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const f32x4 kf = *reinterpret_cast<const f32x4*>(ks + l32 * LD + 8 * kb + 4 * half);
 #pragma unroll
         for (int i = 0; i < 4; ++i) s = mfma(kf[i], qf[kb][i], s);
       }
+      __builtin_amdgcn_s_setprio(0);
       if (kb0 + 31 >= g.k_len || g.k_off + kb0 + 31 > wave_qmin) {  // straddles the diagonal or the end
         // key kl of this block is visible to the lane's query iff kl <= dlim
         const int dlim = (int)max((int64_t)-1, min((int64_t)32, qpos - g.k_off - kb0));
@@ -233,12 +240,14 @@ __global__ __launch_bounds__(kNT, Cfg<HD>::MINW) void attn_fwd(AttnGeom g, const
       psum += __shfl_xor(psum, 32, 64);
       l = l * alpha + psum;
       m = mnew;
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb) {
         oacc[eb] *= alpha;
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[eb] = mfma(vs[kidx(r, half) * LD + eb * 32 + l32], s[r], oacc[eb]);
       }
+      __builtin_amdgcn_s_setprio(0);
     }
     __syncthreads();
     if (more) {
