@@ -650,8 +650,9 @@ typedef struct tt_tensor tt_tensor;
 int tt_ctx_create(int device, int n_streams, int window, size_t device_budget_bytes, tt_ctx** out);
 /* tt_ctx_create_on_streams -- tt_ctx_create whose tasks run on n_streams
  * HIP streams the caller owns (a HOST array of hipStream_t handles, e.g.
- * torch streams): the context does not create, and on destruction does not
- * destroy, them; they must stay valid until tt_ctx_destroy returns. Work
+ * torch streams) of that device: the context does not create, and on
+ * destruction does not destroy, them; they must stay valid until
+ * tt_ctx_destroy returns. Work
  * the caller queues on them interleaves with the tasks in stream order
  * (use tt_ctx_wait_stream / tt_ctx_join_stream for other streams). The
  * context still creates its own copy streams for pinned-host tiles.
