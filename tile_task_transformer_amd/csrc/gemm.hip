@@ -637,7 +637,17 @@ Plan plan_for(int64_t m, int64_t n, int64_t k, size_t ws_bytes) {
     return p;
   }
   const int64_t b128 = blocks(128, 128);
-  if (b128 >= want) return rounds_favour_128(b128, k) ? p : Plan{64, 64, 32, 1, (int)k};
+  if (b128 >= want) {
+    if (!rounds_favour_128(b128, k)) return Plan{64, 64, 32, 1, (int)k};
+    // BK 16 keeps three workgroups per CU, BK 32 two: a block count that is
+    // a multiple of 512 fills whole rounds of two, and there BK 32 wins
+    // (the wide model's MLP output chain links, 4096 x 2048 x 8192: 84.0 ->
+    // 85.1 % of the fp32 peak in the step, the step 697.0 -> 695.3 ms;
+    // 4096 x 2048 x 768: 101 -> 104 TFLOP/s), while 768 blocks fill one
+    // round of three (4096 x 3072 x 768: 103 TFLOP/s at BK 16, 87 at BK 32)
+    if (b128 % 512 == 0) p.bk = 32;
+    return p;
+  }
   if (k >= 2048 && b128 <= 144 && ws_bytes > 0) {
     // split count by CU balance: workgroups run in rounds of one per CU, so
     // b128*s just under a multiple of 256 keeps every CU equally loaded
